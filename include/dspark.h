@@ -1,0 +1,230 @@
+/*
+ * dspark.h — C ABI of the MI355X (gfx950) DSpark draft-and-verify library (libdspark.so).
+ *
+ * One speculative-decoding round of DSpark for a batch of B requests:
+ *   dspark_markov_draft  semi-autoregressive Markov-head draft of gamma tokens per request
+ *   dspark_confidence    confidence head c_k = sigmoid(w . [h_k ; W1[x_{k-1}]] / T_k)
+ *   dspark_plan          survival-ordered greedy planner that maximises Theta = tau * SPS(B)
+ *   dspark_verify        lossless rejection-sampling verify, residual resample, bonus token
+ *
+ * Sources (cited below by tag; each gives the page title and the section or equation):
+ *   [V41]  blog.javazero.top, "DeepSeek-V4.1 模型结构（6）：解码，DSpark"
+ *   [ZDS]  zdszero.github.io, spec_dspark (the DSpark chapter of a speculative-decoding series)
+ *   [AIL]  ailearn.mscapital.top, "DSpark：不让大模型更聪明，而让它「吐字更快」"
+ *   [CSDN] deepseek.csdn.net, DSpark walk-through with equations (1)-(12)
+ *
+ * Conventions shared by every entry point
+ *   - Every array argument is a DEVICE pointer (HIP device memory or memory the device can
+ *     read), row-major and contiguous, allocated and owned by the caller. The library keeps no
+ *     state between calls and allocates no device memory: scratch space comes in through the
+ *     `ws`/`ws_bytes` workspace argument, sized by dspark_workspace_bytes().
+ *   - Every call only enqueues work on `stream` (a hipStream_t; NULL = the null stream) and
+ *     returns without waiting for it. Results are valid once the stream reaches that point.
+ *   - Argument checks run on the host, synchronously, before anything is enqueued; a failed
+ *     check returns its status and enqueues nothing. A launch failure returns DSPARK_ERR_HIP.
+ *     No C++ exception crosses this interface.
+ *   - Pointers must be 16-byte aligned (DSPARK_ERR_ALIGN otherwise); bf16 tensors are passed
+ *     as uint16_t bit patterns.
+ *   - Random draws are never generated inside the library: the caller passes
+ *     uniforms [B][gamma+1][3] fp32 in [0,1), so a round is reproducible bit for bit.
+ *     Component 0 of slot k-1 draws the draft token of position k; component 1 of slot k-1 is
+ *     the accept test of position k; component 2 of slot k-1 draws the token emitted at
+ *     position k (the residual resample after a reject at k, or the bonus at k = l_b + 1).
+ *   - Sampling rule: a draw from a distribution p over token ids with uniform u returns the
+ *     smallest id v whose cumulative probability (ids in ascending order) exceeds u. The pages
+ *     fix only the distribution a draw must follow; this rule makes it reproducible.
+ *   - Results are deterministic: two identical calls give bitwise identical outputs.
+ */
+#ifndef DSPARK_H_
+#define DSPARK_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define DSPARK_API __attribute__((visibility("default")))
+#else
+#define DSPARK_API
+#endif
+
+/* Problem sizes. B requests, gamma draft positions, V vocabulary, r Markov rank, d hidden size
+ * (d is read only by dspark_confidence). Supported: B >= 1, gamma >= 1, V >= 2,
+ * r in {16, 32, 64, 128, 256, 512}, d % 8 == 0, B * gamma <= 8192. */
+typedef struct dspark_dims {
+  int32_t B;
+  int32_t gamma;
+  int32_t V;
+  int32_t r;
+  int32_t d;
+} dspark_dims;
+
+typedef int32_t dspark_status;
+#define DSPARK_OK 0
+#define DSPARK_ERR_NULL 1        /* a required pointer is NULL */
+#define DSPARK_ERR_SHAPE 2       /* a size is out of the supported range */
+#define DSPARK_ERR_ALIGN 3       /* a pointer is not 16-byte aligned */
+#define DSPARK_ERR_WORKSPACE 4   /* ws_bytes < dspark_workspace_bytes(...) */
+#define DSPARK_ERR_SPS 5         /* sps_len <= B * (gamma + 1) */
+#define DSPARK_ERR_HIP 6         /* a HIP launch failed */
+#define DSPARK_ERR_MODE 7        /* unknown plan mode, or LAGGED_TOPK without a ring */
+
+/* Plan modes. [ZDS] "在 SGLang 里": the static mode verifies every drafted token (no planner);
+ * the compact mode plans with the SPS table. */
+#define DSPARK_PLAN_FULL_VERIFY 0 /* l_b = gamma for every request */
+#define DSPARK_PLAN_EARLY_STOP 1  /* Algorithm 1: admit by survival while Theta rises */
+#define DSPARK_PLAN_FULL_PATH 2   /* first maximiser of Theta over the whole admission path */
+#define DSPARK_PLAN_LAGGED_TOPK 3 /* capacity from confidences two rounds back, order now */
+
+/* Operation ids for dspark_workspace_bytes. */
+#define DSPARK_OP_DRAFT 0
+#define DSPARK_OP_CONFIDENCE 1
+#define DSPARK_OP_PLAN 2
+#define DSPARK_OP_VERIFY 3
+
+/* Per-request verify flag bits. */
+#define DSPARK_FLAG_NONFINITE 1u     /* a verified target row has a non-finite log-sum-exp */
+#define DSPARK_FLAG_ZERO_RESIDUAL 2u /* residual mass not positive: token drawn from p_t */
+
+/* Human-readable name of a status code (static storage; never NULL). */
+DSPARK_API const char* dspark_status_string(dspark_status status);
+
+/* Library version string (static storage). */
+DSPARK_API const char* dspark_version(void);
+
+/* Bytes of workspace the operation `op` (DSPARK_OP_*) needs for `dims`; 0 if it needs none,
+ * (size_t)-1 for unsupported dims or op. */
+DSPARK_API size_t dspark_workspace_bytes(dspark_dims dims, int32_t op);
+
+/*
+ * Semi-autoregressive Markov-head draft.
+ * [V41] "Markov head", eqs. (4) and (5) and the serial loop; [CSDN] 4.1-4.2, eq. (4);
+ * [ZDS] "insight 一" (p_k = softmax(U_k + W1[x_{k-1}] W2), then bias position k+1).
+ * For k = 1..gamma: with x_0 = anchor,
+ *   L_k = U_k + W1[x_{k-1}] . W2   (bf16 operands, fp32 accumulation, fp32 logits)
+ *   x_k ~ softmax(L_k)             (inverse-CDF draw with uniforms[b][k-1][0])
+ * The same W1, W2 serve every position; the draft always produces all gamma tokens.
+ *   U         [B][gamma][V] fp32   base logits of the parallel drafter
+ *   W1        [V][r] bf16          Markov embedding table (Embedding(V, r) layout)
+ *   W2t       [V][r] bf16          Markov projection stored token-major: W2t[v][i] = W2[i][v]
+ *                                  (the weight layout of Linear(r, V))
+ *   anchor    [B] int32            x_0, the last token the target emitted
+ *   uniforms  [B][gamma+1][3] fp32
+ *   tokens    [B][gamma] int32     out: drafted tokens x_1..x_gamma
+ *   q_tok     [B][gamma] fp32      out: q_k = p_k(x_k), the draft probability of the token
+ *   lse       [B][gamma] fp64      out: log sum_v exp L_k(v)
+ *   logits_dbg  nullable [B][gamma][V] fp32: out, L_k (costs an extra write of the logits)
+ *   force_tokens nullable [B][gamma] int32: teacher forcing for step-by-step comparison; when
+ *              given, tokens[] still receives each draw, but force_tokens[b][k-1] conditions
+ *              position k+1 and q_tok[b][k-1] is the probability of force_tokens[b][k-1].
+ * Token ids in anchor / force_tokens must lie in [0, V) (not checked on the device).
+ * A row whose logits are not finite yields token 0 and q = lse = NaN.
+ */
+DSPARK_API dspark_status dspark_markov_draft(dspark_dims dims, const float* U, const uint16_t* W1,
+                                             const uint16_t* W2t, const int32_t* anchor,
+                                             const float* uniforms, int32_t* tokens, float* q_tok,
+                                             double* lse, float* logits_dbg,
+                                             const int32_t* force_tokens, void* ws, size_t ws_bytes,
+                                             void* stream);
+
+/*
+ * Confidence head, eq. (7), with the STS temperature applied at inference:
+ *   c_k = sigmoid( (w . [h_k ; W1[x_{k-1}]]) / T_k ),  x_0 = anchor.
+ * [V41] "confidence head", eq. (7) (input holds x_{k-1}, not x_k; no bias term);
+ * [ZDS] "在 SGLang 里" (Linear(h + r, 1), sigmoid(raw / T) with per-position STS temperatures).
+ *   h       [B][gamma][d] bf16   drafter hidden states
+ *   W1      [V][r] bf16          the Markov embedding table
+ *   w       [d + r] bf16         head weights; w[0..d) multiply h_k, w[d..d+r) multiply W1 row
+ *   T       [gamma] fp32         per-position temperature (> 0)
+ *   anchor  [B] int32, tokens [B][gamma] int32 (the drafted tokens)
+ *   conf    [B][gamma] fp32      out
+ * The dot product is accumulated in fp64.
+ */
+DSPARK_API dspark_status dspark_confidence(dspark_dims dims, const uint16_t* h, const uint16_t* W1,
+                                           const uint16_t* w, const float* T,
+                                           const int32_t* anchor, const int32_t* tokens,
+                                           float* conf, void* stream);
+
+/*
+ * Hardware-aware verify planner.
+ * [V41] "调度器" ("目标函数", "贪心就能解", "按置信度截断在什么条件下不改变分布", Appendix A);
+ * [ZDS] "调度" and "在 SGLang 里"; [CSDN] 5.3, 5.4, 8.
+ *   a_{b,j} = prod_{i<=j} c_{b,i} (fp64, sequential),  B_tot = sum_b (1 + l_b),
+ *   tau = sum_b (1 + sum_{j<=l_b} a_{b,j}),            Theta = tau * SPS(B_tot).
+ * Candidates (b, j) are ordered by a descending, ties by b then j ascending; admitting them
+ * one by one along that order traces Theta_i = (B + sum of the first i survivals) * sps[B + i].
+ *   FULL_VERIFY  admit all (conf may be NULL; tau and Theta are then NaN in stats)
+ *   EARLY_STOP   admit while Theta_{i+1} > Theta_i (stop at the first non-increase)
+ *   FULL_PATH    admit the first maximiser of Theta_i over i = 0..B*gamma
+ *   LAGGED_TOPK  K = B + (FULL_PATH count computed on the confidences of round round_index-2,
+ *                read from ring[round_index % 2]); admit the first K - B candidates of this
+ *                round's own order. Rounds 0 and 1 plan with EARLY_STOP. In every round the
+ *                ring slot round_index % 2 is then overwritten with this round's conf.
+ *   conf        [B][gamma] fp32
+ *   sps         [sps_len] fp64, sps[n] = engine steps per second with n verified tokens;
+ *               sps_len must exceed B * (gamma + 1)
+ *   ring        [2][B][gamma] fp32, required for LAGGED_TOPK (NULL otherwise)
+ *   draft_len   [B] int32        out: l_b in [0, gamma]; request b verifies 1 + l_b rows
+ *   row_offsets [B+1] int32      out: exclusive scan of (1 + l_b), the packed row layout
+ *   stats       [4] fp64         out (nullable): {B_tot, tau, Theta, K} at the admitted point
+ *                                (K = B_tot except for LAGGED_TOPK after warm-up)
+ * Runs as a single workgroup; nothing returns to the host.
+ */
+DSPARK_API dspark_status dspark_plan(dspark_dims dims, const float* conf, const double* sps,
+                                     int32_t sps_len, int32_t mode, float* ring,
+                                     int32_t round_index, int32_t* draft_len,
+                                     int32_t* row_offsets, double* stats, void* stream);
+
+/*
+ * Lossless verify.
+ * [V41] "投机解码：让小的先猜，大的一次验一串" and the derivation after it (accept with
+ * min(1, p/q), on reject resample from norm(max(0, p - q)), left to right, the first reject
+ * voids the rest, the bonus from the target when all are accepted, the emitted token is the
+ * next anchor); [AIL] 02 (A/B worked example); [CSDN] 2.1.
+ * Rows of request b: target[row_offsets[b] + j] (j = 0..draft_len[b]) holds the target logits
+ * of position j+1; row draft_len[b] is the bonus position. FULL_VERIFY is the dense layout
+ * row_offsets[b] = b * (gamma + 1).
+ *   Accept test at position k:  uniforms[b][k-1][1] * q_tok[b][k-1] < p_t(x_k)   (fp64)
+ *   First reject at k: next_token ~ max(0, p_t - p_d) / sum, p_d the draft distribution of
+ *   position k recomputed from U, W1, W2t and x_{k-1} (uniforms[b][k-1][2]); all accepted:
+ *   next_token ~ p_t of row draft_len[b] (uniforms[b][draft_len[b]][2]).
+ *   target      [row_offsets[B]][V] fp32 (device-resident; sized for the plan's rows)
+ *   row_offsets [B+1], draft_len [B] int32 (as written by dspark_plan)
+ *   U, W1, W2t, anchor, tokens, q_tok, lse, uniforms: as given to / written by the draft
+ *   accept_len  [B] int32   out: number of drafted tokens accepted (0..draft_len[b]); the
+ *                           round emits tokens[b][0..accept_len) followed by next_token[b]
+ *   next_token  [B] int32   out: the residual or bonus token (the next anchor)
+ *   beta_emit   nullable [B] fp32: out, sum_v min(p_t, p_d) at a residual emission row (the
+ *               acceptance rate of that position, eq. (8)); -1 at a bonus row
+ *   flags       nullable [B] uint32: out, DSPARK_FLAG_* bits
+ */
+DSPARK_API dspark_status dspark_verify(dspark_dims dims, const float* target,
+                                       const int32_t* row_offsets, const int32_t* draft_len,
+                                       const float* U, const uint16_t* W1, const uint16_t* W2t,
+                                       const int32_t* anchor, const int32_t* tokens,
+                                       const float* q_tok, const double* lse,
+                                       const float* uniforms, int32_t* accept_len,
+                                       int32_t* next_token, float* beta_emit, uint32_t* flags,
+                                       void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Kernel timing with HIP events (measurement support; not part of the method).
+ * dspark_profile_begin(capacity) arms up to `capacity` event pairs; while armed, every kernel
+ * launch of the library is bracketed by two events recorded on the launch stream.
+ * dspark_profile_end() waits for the recorded events and returns, per kernel name, the number
+ * of launches and their summed duration in milliseconds (names[i] has static storage), then
+ * disarms. Returns the number of kernel names written (at most max_names), or -1 on error.
+ * Not thread-safe; only for single-threaded benchmarking.
+ */
+DSPARK_API int32_t dspark_profile_begin(int32_t capacity);
+DSPARK_API int32_t dspark_profile_end(const char** names, int32_t* counts, double* total_ms,
+                                      int32_t max_names);
+
+#ifdef __cplusplus
+}  /* extern "C" */
+#endif
+
+#endif /* DSPARK_H_ */

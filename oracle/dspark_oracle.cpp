@@ -1,0 +1,510 @@
+// DSpark draft-and-verify round: plain fp64 CPU oracle.
+//
+// TEST INFRASTRUCTURE ONLY. This file is the slow, obviously-correct reference that the
+// tests, the smoke check and the CPU-baseline leg of the benchmark compare the GPU library
+// against. The GPU library never links, loads or calls it, and it shares no source with the
+// GPU library (no headers, helpers, tables or constants).
+//
+// Sources cited (a reader has these pages):
+//   [V41]     blog.javazero.top, "DeepSeek-V4.1 模型结构（6）：解码，DSpark"
+//   [ZDS]     zdszero.github.io, spec_dspark (DSpark chapter of a speculative-decoding series)
+//   [AIL]     ailearn.mscapital.top, "DSpark：不让大模型更聪明，而让它「吐字更快」"
+//   [CSDN]    deepseek.csdn.net, DSpark walk-through (equations numbered (1)-(12))
+//
+// Every quantity is computed from its plain definition, in double precision, one request at a
+// time, with no blocking, fusion or reordering beyond what the definition states. Where the
+// pages leave a step open, the reading taken is stated at that step.
+//
+// Inputs arrive in the same bit patterns the GPU library gets: fp32 logits, bf16 weights
+// (uint16 bit patterns, widened exactly to double here), fp32 uniforms.
+
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <limits>
+#include <thread>
+#include <vector>
+
+extern "C" {
+
+// Plan modes (numbering is part of the shared interface; see the public header of the library).
+enum { ORACLE_FULL_VERIFY = 0, ORACLE_EARLY_STOP = 1, ORACLE_FULL_PATH = 2, ORACLE_LAGGED_TOPK = 3 };
+
+// Per-request verify flag bits.
+enum { ORACLE_FLAG_NONFINITE = 1u, ORACLE_FLAG_ZERO_RESIDUAL = 2u };
+
+}  // extern "C"
+
+namespace {
+
+double bf16_to_double(uint16_t bits) {
+  uint32_t u = static_cast<uint32_t>(bits) << 16;
+  float f;
+  std::memcpy(&f, &u, sizeof f);
+  return static_cast<double>(f);
+}
+
+// Runs f(i) for i in [0, n) on `threads` worker threads (0 = all hardware threads).
+template <class F>
+void parallel_for(int64_t n, int threads, F f) {
+  if (n <= 0) return;
+  if (threads <= 0) threads = static_cast<int>(std::thread::hardware_concurrency());
+  if (threads <= 0) threads = 1;
+  if (threads > n) threads = static_cast<int>(n);
+  if (threads == 1) {
+    for (int64_t i = 0; i < n; ++i) f(i);
+    return;
+  }
+  std::atomic<int64_t> next(0);
+  std::vector<std::thread> pool;
+  pool.reserve(threads);
+  for (int t = 0; t < threads; ++t)
+    pool.emplace_back([&]() {
+      for (int64_t i = next++; i < n; i = next++) f(i);
+    });
+  for (auto& th : pool) th.join();
+}
+
+// Softmax of fp32 logits in double: p_v = exp(L_v - m) / sum_u exp(L_u - m), m = max L.
+// Returns log-sum-exp = m + log(sum). [V41] "Markov head", eq. (4): every position is one
+// ordinary softmax, so the exact per-token probability q(x_k) is available.
+double softmax_fp64(const float* logits, int V, std::vector<double>& p) {
+  p.assign(V, 0.0);
+  double m = -std::numeric_limits<double>::infinity();
+  for (int v = 0; v < V; ++v) m = std::max(m, static_cast<double>(logits[v]));
+  double z = 0.0;
+  for (int v = 0; v < V; ++v) {
+    p[v] = std::exp(static_cast<double>(logits[v]) - m);
+    z += p[v];
+  }
+  for (int v = 0; v < V; ++v) p[v] /= z;
+  return m + std::log(z);
+}
+
+// Inverse-CDF draw over token ids in ascending order: the first v with CDF(v) > u.
+// Reading: the pages fix only the distribution a draw must follow; this build fixes the rule
+// "ascending token id, strict >, u in [0,1)" so that results are reproducible bit for bit.
+// If rounding leaves no edge above u, the last token with positive probability is taken.
+// *margin receives the distance from u to the nearer edge of the chosen token's interval.
+int32_t inverse_cdf(const std::vector<double>& p, double u, double* margin) {
+  double cdf = 0.0;
+  int32_t last_positive = -1;
+  for (size_t v = 0; v < p.size(); ++v) {
+    const double lo = cdf;
+    cdf += p[v];
+    if (p[v] > 0.0) last_positive = static_cast<int32_t>(v);
+    if (cdf > u) {
+      *margin = std::min(u - lo, cdf - u);
+      return static_cast<int32_t>(v);
+    }
+  }
+  *margin = 0.0;
+  return last_positive >= 0 ? last_positive : 0;
+}
+
+// Markov bias of eq. (5): B(prev, v) = W1[prev] . W2[:, v], with W2 stored token-major
+// (W2t[v][i] = W2[i][v], the layout of a Linear(r, V) weight). [V41] "Markov head", eq. (5);
+// [ZDS] "在 SGLang 里" (markov_w1 = Embedding(V, r), markov_w2 = Linear(r, V)).
+void markov_bias_fp64(const uint16_t* W1, const uint16_t* W2t, int V, int r, int32_t prev,
+                      std::vector<double>& bias) {
+  std::vector<double> e(r);
+  for (int i = 0; i < r; ++i) e[i] = bf16_to_double(W1[static_cast<int64_t>(prev) * r + i]);
+  bias.assign(V, 0.0);
+  for (int v = 0; v < V; ++v) {
+    const uint16_t* col = W2t + static_cast<int64_t>(v) * r;
+    double s = 0.0;
+    for (int i = 0; i < r; ++i) s += e[i] * bf16_to_double(col[i]);
+    bias[v] = s;
+  }
+}
+
+// Draft logits of one position: L_v = fp32(U_v + fp32(B(prev, v))).
+// Reading: the official loop adds the bias in place into the fp32 logits tensor before
+// sampling ([V41] "Markov head", the serial loop: logits[:, i].add_(bias)), so the draft
+// distribution is the softmax of fp32 logits; the bias itself is summed exactly (fp64) and
+// rounded once to fp32.
+void draft_logits(const float* U_row, const uint16_t* W1, const uint16_t* W2t, int V, int r,
+                  int32_t prev, std::vector<float>& L) {
+  std::vector<double> bias;
+  markov_bias_fp64(W1, W2t, V, r, prev, bias);
+  L.assign(V, 0.0f);
+  for (int v = 0; v < V; ++v) {
+    const float b = static_cast<float>(bias[v]);
+    L[v] = U_row[v] + b;  // one fp32 addition, round to nearest
+  }
+}
+
+double logsumexp_fp32_row(const float* row, int V) {
+  double m = -std::numeric_limits<double>::infinity();
+  for (int v = 0; v < V; ++v) m = std::max(m, static_cast<double>(row[v]));
+  double z = 0.0;
+  for (int v = 0; v < V; ++v) z += std::exp(static_cast<double>(row[v]) - m);
+  return m + std::log(z);
+}
+
+// a_{r,j} = prod_{i<=j} c_{r,i}, sequential product in double of the fp32 confidences.
+// [V41] "confidence head": prefix survival a_j; [CSDN] 5.3, a_{r,j} = a_{r,j-1} c_{r,j}.
+void survival(const float* conf, int R, int gamma, std::vector<double>& a) {
+  a.assign(static_cast<size_t>(R) * gamma, 0.0);
+  for (int rq = 0; rq < R; ++rq) {
+    double prod = 1.0;
+    for (int j = 0; j < gamma; ++j) {
+      prod *= static_cast<double>(conf[rq * gamma + j]);
+      a[rq * gamma + j] = prod;
+    }
+  }
+}
+
+struct Candidate {
+  double a;
+  int32_t req, pos;  // pos is 0-based: candidate (req, pos) extends request req to length pos+1
+};
+
+// All (request, position) candidates sorted by survival, descending; ties broken by request
+// then position, ascending (reading: a deterministic tie-break that keeps every request's
+// admitted set a prefix even when c = 1). [V41] "贪心就能解"; [CSDN] 5.3.
+std::vector<Candidate> sorted_candidates(const std::vector<double>& a, int R, int gamma) {
+  std::vector<Candidate> c;
+  c.reserve(static_cast<size_t>(R) * gamma);
+  for (int rq = 0; rq < R; ++rq)
+    for (int j = 0; j < gamma; ++j) c.push_back({a[rq * gamma + j], rq, j});
+  std::sort(c.begin(), c.end(), [](const Candidate& x, const Candidate& y) {
+    if (x.a != y.a) return x.a > y.a;
+    if (x.req != y.req) return x.req < y.req;
+    return x.pos < y.pos;
+  });
+  return c;
+}
+
+// The admission path: theta[i] = tau_i * SPS(R + i), tau_0 = R, tau_i = tau_{i-1} + a_(i).
+// [V41] "目标函数": B = sum(1 + l_r), tau = sum(1 + sum_{j<=l_r} a_{r,j}), Theta = tau SPS(B).
+// Reading: SPS is indexed by the total number of verified tokens B (not by requests).
+void admission_path(const std::vector<Candidate>& cand, int R, const double* sps,
+                    std::vector<double>& tau, std::vector<double>& theta) {
+  const size_t n = cand.size();
+  tau.assign(n + 1, 0.0);
+  theta.assign(n + 1, 0.0);
+  tau[0] = static_cast<double>(R);
+  theta[0] = tau[0] * sps[R];
+  for (size_t i = 1; i <= n; ++i) {
+    tau[i] = tau[i - 1] + cand[i - 1].a;
+    theta[i] = tau[i] * sps[R + i];
+  }
+}
+
+// Algorithm 1: admit in path order while Theta rises; stop at the first candidate whose
+// admission would not raise it (strict >). [V41] "贪心就能解" (once Theta stops rising, stop);
+// [CSDN] 5.3.
+int64_t early_stop_count(const std::vector<double>& theta, double* margin) {
+  const int64_t n = static_cast<int64_t>(theta.size()) - 1;
+  int64_t k = 0;
+  double mg = std::numeric_limits<double>::infinity();
+  while (k < n) {
+    const double rel = std::fabs(theta[k + 1] - theta[k]) / std::fabs(theta[k]);
+    mg = std::min(mg, rel);
+    if (!(theta[k + 1] > theta[k])) break;
+    ++k;
+  }
+  if (margin) *margin = mg;
+  return k;
+}
+
+// Full-path search: the first maximiser of Theta over the whole path. [AIL] 05 (the
+// production variant removes early stop and searches the whole path); [CSDN] 8.
+int64_t full_path_count(const std::vector<double>& theta, double* margin) {
+  int64_t best = 0;
+  for (int64_t i = 1; i < static_cast<int64_t>(theta.size()); ++i)
+    if (theta[i] > theta[best]) best = i;
+  double mg = std::numeric_limits<double>::infinity();
+  for (int64_t i = 0; i < static_cast<int64_t>(theta.size()); ++i)
+    if (i != best) mg = std::min(mg, std::fabs(theta[best] - theta[i]) / std::fabs(theta[best]));
+  if (margin) *margin = mg;
+  return best;
+}
+
+}  // namespace
+
+extern "C" {
+
+// Semi-autoregressive Markov-head draft.
+// [V41] "Markov head" eqs. (4), (5) and the serial loop: the base logits U_k are given; for
+// k = 1..gamma the previous token (x_0 = anchor) selects W1[x_{k-1}], the bias W1[x_{k-1}] W2
+// is added to U_k, and x_k is drawn from the softmax; the same W1, W2 serve every position.
+// [CSDN] 4.1-4.2, eq. (4): local softmax per position, exact q(x_k).
+//
+// Layouts: U [B][gamma][V] fp32; W1, W2t [V][r] bf16 bits; anchor [B]; uniforms
+// [B][gamma+1][3] fp32 (component 0 of slot k-1 draws position k).
+// force_tokens (nullable) [B][gamma]: when given, tokens[] still receives the draw at each
+// position, but the token that conditions the next position and whose probability goes to
+// q[] is force_tokens[b][k-1] (teacher forcing, used to compare step by step).
+// Outputs: tokens [B][gamma], q [B][gamma] = p_k(x_k), lse [B][gamma] = log sum exp L_k,
+// logits (nullable) [B][gamma][V] = L_k, margin (nullable) [B][gamma] = distance of u to the
+// nearer CDF edge of the drawn token.
+// Returns 0, or 2 for a bad shape, 8 for an out-of-range token id.
+int oracle_markov_draft(int B, int gamma, int V, int r, const float* U, const uint16_t* W1,
+                        const uint16_t* W2t, const int32_t* anchor, const float* uniforms,
+                        const int32_t* force_tokens, int32_t* tokens, float* q, double* lse,
+                        float* logits, double* margin, int threads) {
+  if (B < 0 || gamma < 1 || V < 2 || r < 1) return 2;
+  for (int b = 0; b < B; ++b) {
+    if (anchor[b] < 0 || anchor[b] >= V) return 8;
+    if (force_tokens)
+      for (int k = 0; k < gamma; ++k)
+        if (force_tokens[b * gamma + k] < 0 || force_tokens[b * gamma + k] >= V) return 8;
+  }
+  parallel_for(B, threads, [&](int64_t b) {
+    std::vector<float> L;
+    std::vector<double> p;
+    int32_t prev = anchor[b];
+    for (int k = 0; k < gamma; ++k) {
+      const int64_t bk = b * gamma + k;
+      draft_logits(U + bk * V, W1, W2t, V, r, prev, L);
+      const double l = softmax_fp64(L.data(), V, p);
+      const double u = static_cast<double>(uniforms[(b * (gamma + 1) + k) * 3 + 0]);
+      double mg = 0.0;
+      const int32_t x = inverse_cdf(p, u, &mg);
+      tokens[bk] = x;
+      const int32_t cond = force_tokens ? force_tokens[bk] : x;
+      q[bk] = static_cast<float>(p[cond]);
+      lse[bk] = l;
+      if (logits) std::memcpy(logits + bk * V, L.data(), sizeof(float) * V);
+      if (margin) margin[bk] = mg;
+      prev = cond;
+    }
+  });
+  return 0;
+}
+
+// Confidence head, eq. (7), with the STS temperature applied at inference:
+// z = w . [h_k ; W1[x_{k-1}]] (no bias term: eq. (7) has none), c_k = sigmoid(z / T_k).
+// [V41] "confidence head" eq. (7) (the input holds x_{k-1}, not x_k; x_0 = anchor);
+// [ZDS] "在 SGLang 里" (Linear(h + r, 1), sigmoid(raw / T) with the STS temperature).
+// Layouts: h [B][gamma][d] bf16; w [d + r] bf16 (first d entries multiply h_k); T [gamma];
+// tokens [B][gamma] (the drafted tokens; x_{k-1} = tokens[b][k-2] for k >= 2).
+// Outputs: conf [B][gamma] fp32; z_out (nullable) [B][gamma] = the pre-sigmoid value.
+int oracle_confidence(int B, int gamma, int V, int r, int d, const uint16_t* h, const uint16_t* W1,
+                      const uint16_t* w, const float* T, const int32_t* anchor,
+                      const int32_t* tokens, float* conf, double* z_out, int threads) {
+  if (B < 0 || gamma < 1 || V < 2 || r < 1 || d < 1) return 2;
+  for (int b = 0; b < B; ++b) {
+    if (anchor[b] < 0 || anchor[b] >= V) return 8;
+    for (int k = 0; k < gamma; ++k)
+      if (tokens[b * gamma + k] < 0 || tokens[b * gamma + k] >= V) return 8;
+  }
+  parallel_for(static_cast<int64_t>(B) * gamma, threads, [&](int64_t bk) {
+    const int64_t b = bk / gamma, k = bk % gamma;
+    const int32_t prev = (k == 0) ? anchor[b] : tokens[b * gamma + k - 1];
+    double z = 0.0;
+    for (int i = 0; i < d; ++i) z += bf16_to_double(w[i]) * bf16_to_double(h[bk * d + i]);
+    for (int i = 0; i < r; ++i)
+      z += bf16_to_double(w[d + i]) * bf16_to_double(W1[static_cast<int64_t>(prev) * r + i]);
+    const double c = 1.0 / (1.0 + std::exp(-z / static_cast<double>(T[k])));
+    conf[bk] = static_cast<float>(c);
+    if (z_out) z_out[bk] = z;
+  });
+  return 0;
+}
+
+// Hardware-aware verify planner. [V41] "调度器" ("目标函数", "贪心就能解", "按置信度截断在什么
+// 条件下不改变分布"); [ZDS] "调度" and "在 SGLang 里" (lengths 1 + l_r in [1, gamma+1], a flat
+// SPS table degrades to full verify, confidence relayed through a ring with lag 2, no lag
+// without overlap); [CSDN] 5.3, 5.4, 8.
+//
+// Modes: FULL_VERIFY admits everything (l_r = gamma); EARLY_STOP is Algorithm 1;
+// FULL_PATH takes the first maximiser of Theta over the whole path (the retrospective search
+// that is biased when applied to the current round, Appendix A); LAGGED_TOPK takes the
+// capacity K from the confidences of two rounds back (full-path search on those), then admits
+// the top K - R candidates of the current round's own order.
+// Ring (LAGGED_TOPK only) [2][B][gamma]: slot (round % 2) holds round-2's confidences; it is
+// read first, then overwritten with this round's. Reading for the warm-up: rounds 0 and 1
+// have no lagged confidences and use EARLY_STOP (no lag without overlap).
+// Outputs: draft_len [B] (l_r in [0, gamma]); row_offsets [B+1], the exclusive scan of
+// (1 + l_r); stats[4] = {B_tot, tau, Theta, K} at the admitted point (K = capacity for
+// LAGGED_TOPK after warm-up, else B_tot); margin (nullable) = smallest relative Theta gap
+// among the comparisons that decided the admission count; theta_path (nullable) [B*gamma+1]
+// = Theta_i along this round's admission path.
+// sps [sps_len] fp64: sps[n] = steps per second with n verified tokens; sps_len must exceed
+// B * (gamma + 1). Returns 0, 2 (shape), 5 (SPS table too short), 7 (bad mode / missing ring).
+int oracle_plan(int B, int gamma, const float* conf, const double* sps, int sps_len, int mode,
+                float* ring, int round_index, int32_t* draft_len, int32_t* row_offsets,
+                double* stats, double* margin, double* theta_path) {
+  if (B < 1 || gamma < 1) return 2;
+  if (sps_len < B * (gamma + 1) + 1) return 5;
+  if (mode < ORACLE_FULL_VERIFY || mode > ORACLE_LAGGED_TOPK) return 7;
+  if (mode == ORACLE_LAGGED_TOPK && ring == nullptr) return 7;
+  if (mode != ORACLE_FULL_VERIFY && conf == nullptr) return 7;
+
+  const int64_t n = static_cast<int64_t>(B) * gamma;
+  std::vector<double> a, tau, theta;
+  std::vector<Candidate> cand;
+  int64_t admit = 0;
+  double mg = std::numeric_limits<double>::infinity();
+  double capacity = 0.0;
+  bool lagged = false;
+
+  if (mode == ORACLE_FULL_VERIFY) {
+    // Static mode: no planner, every drafted token is verified. Without confidences the
+    // survivals (and so tau and Theta) are unknown and reported as NaN.
+    admit = n;
+    if (conf) {
+      survival(conf, B, gamma, a);
+      cand = sorted_candidates(a, B, gamma);
+    } else {
+      for (int rq = 0; rq < B; ++rq)
+        for (int j = 0; j < gamma; ++j)
+          cand.push_back({std::numeric_limits<double>::quiet_NaN(), rq, j});
+    }
+    admission_path(cand, B, sps, tau, theta);
+  } else {
+    survival(conf, B, gamma, a);
+    cand = sorted_candidates(a, B, gamma);
+    admission_path(cand, B, sps, tau, theta);
+    if (mode == ORACLE_EARLY_STOP || (mode == ORACLE_LAGGED_TOPK && round_index < 2)) {
+      admit = early_stop_count(theta, &mg);
+    } else if (mode == ORACLE_FULL_PATH) {
+      admit = full_path_count(theta, &mg);
+    } else {
+      // Capacity from the confidences of two rounds back: [V41] last paragraph before
+      // "训练"; [CSDN] 8: K from two steps back, order from the current survivals.
+      const float* lag = ring + static_cast<int64_t>(round_index % 2) * n;
+      std::vector<double> a_lag, tau_lag, theta_lag;
+      survival(lag, B, gamma, a_lag);
+      std::vector<Candidate> cand_lag = sorted_candidates(a_lag, B, gamma);
+      admission_path(cand_lag, B, sps, tau_lag, theta_lag);
+      const int64_t k_lag = full_path_count(theta_lag, &mg);
+      admit = std::min<int64_t>(k_lag, n);
+      capacity = static_cast<double>(B) + static_cast<double>(k_lag);
+      lagged = true;
+    }
+  }
+  if (mode == ORACLE_LAGGED_TOPK)
+    std::memcpy(ring + static_cast<int64_t>(round_index % 2) * n, conf, sizeof(float) * n);
+
+  for (int rq = 0; rq < B; ++rq) draft_len[rq] = 0;
+  for (int64_t i = 0; i < admit; ++i) draft_len[cand[i].req] += 1;
+  row_offsets[0] = 0;
+  for (int rq = 0; rq < B; ++rq) row_offsets[rq + 1] = row_offsets[rq] + 1 + draft_len[rq];
+
+  const double b_tot = static_cast<double>(B) + static_cast<double>(admit);
+  if (stats) {
+    stats[0] = b_tot;
+    stats[1] = tau[admit];
+    stats[2] = theta[admit];
+    stats[3] = lagged ? capacity : b_tot;
+  }
+  if (margin) *margin = mg;
+  if (theta_path)
+    for (size_t i = 0; i < theta.size(); ++i) theta_path[i] = theta[i];
+  return 0;
+}
+
+// Lossless verify with the standard rejection rule.
+// [V41] "投机解码：让小的先猜，大的一次验一串" (accept x ~ q with probability min(1, p(x)/q(x));
+// on reject resample from norm(max(0, p - q)); check left to right, the first reject voids the
+// rest; at least one token per round: the bonus from the target when all are accepted, the
+// resample otherwise; that token is the next anchor); [AIL] 02 (worked A/B example, the
+// correction distribution); [CSDN] 2.1.
+//
+// Row layout: the rows of request b are target[row_offsets[b] .. row_offsets[b] + l_b], row j
+// holding the target logits of position j + 1 (row l_b is the bonus position).
+// Accept test at position k (reading, equivalent to u < min(1, p_t/q) with u in [0,1)):
+//   u[b][k-1][1] * q[b][k-1] < p_t(x_k), all in double, q as given (fp32).
+// On the first reject at position k the draft distribution p_d of position k is recomputed
+// from U, W1, W2 and the previous token (same definition as the draft), and the next token is
+// drawn from max(0, p_t - p_d) / sum with u[b][k-1][2]; if that mass is not positive
+// (impossible in exact arithmetic after a reject) the draw falls back to p_t and flag bit 2 is
+// set. When every verified token is accepted, the bonus is drawn from p_t of row l_b with
+// u[b][l_b][2]. A row whose log-sum-exp is not finite sets flag bit 1.
+// Outputs: accept_len [B]; next_token [B]; beta_emit (nullable) [B] = sum_v min(p_t, p_d) at a
+// residual emission row, -1 at a bonus row; flags (nullable) [B]; accept_margin (nullable)
+// [B][gamma] = |u - p_t/q| for each tested position with p_t/q < 1 (+inf otherwise);
+// emit_margin (nullable) [B]; resid_mass (nullable) [B] = sum_v max(0, p_t - p_d) (-1 at bonus).
+int oracle_verify(int B, int gamma, int V, int r, const float* target, const int32_t* row_offsets,
+                  const int32_t* draft_len, const float* U, const uint16_t* W1,
+                  const uint16_t* W2t, const int32_t* anchor, const int32_t* tokens,
+                  const float* q, const float* uniforms, int32_t* accept_len,
+                  int32_t* next_token, float* beta_emit, uint32_t* flags, double* accept_margin,
+                  double* emit_margin, double* resid_mass, int threads) {
+  if (B < 0 || gamma < 1 || V < 2 || r < 1) return 2;
+  for (int b = 0; b < B; ++b) {
+    if (draft_len[b] < 0 || draft_len[b] > gamma) return 2;
+    if (row_offsets[b + 1] - row_offsets[b] != draft_len[b] + 1) return 2;
+    if (anchor[b] < 0 || anchor[b] >= V) return 8;
+    for (int k = 0; k < gamma; ++k)
+      if (tokens[b * gamma + k] < 0 || tokens[b * gamma + k] >= V) return 8;
+  }
+  const double inf = std::numeric_limits<double>::infinity();
+  parallel_for(B, threads, [&](int64_t b) {
+    const int ell = draft_len[b];
+    const int64_t off = row_offsets[b];
+    uint32_t fl = 0;
+    int accepted = 0;
+    int reject_pos = -1;  // 1-based position of the first reject
+    if (accept_margin)
+      for (int k = 0; k < gamma; ++k) accept_margin[b * gamma + k] = inf;
+    for (int k = 1; k <= ell; ++k) {
+      const float* row = target + (off + k - 1) * static_cast<int64_t>(V);
+      const double l = logsumexp_fp32_row(row, V);
+      if (!std::isfinite(l)) fl |= ORACLE_FLAG_NONFINITE;
+      const int32_t x = tokens[b * gamma + k - 1];
+      const double pt = std::exp(static_cast<double>(row[x]) - l);
+      const double u = static_cast<double>(uniforms[(b * (gamma + 1) + (k - 1)) * 3 + 1]);
+      const double qk = static_cast<double>(q[b * gamma + k - 1]);
+      if (accept_margin && pt < qk) accept_margin[b * gamma + k - 1] = std::fabs(u - pt / qk);
+      if (u * qk < pt) {
+        ++accepted;
+      } else {
+        reject_pos = k;
+        break;
+      }
+    }
+    std::vector<double> pt, pd, w;
+    double mg = 0.0;
+    int32_t tok = 0;
+    if (reject_pos < 0) {
+      // Bonus token from the target at position ell + 1.
+      const float* row = target + (off + ell) * static_cast<int64_t>(V);
+      const double l = softmax_fp64(row, V, pt);
+      if (!std::isfinite(l)) fl |= ORACLE_FLAG_NONFINITE;
+      const double u = static_cast<double>(uniforms[(b * (gamma + 1) + ell) * 3 + 2]);
+      tok = inverse_cdf(pt, u, &mg);
+      if (beta_emit) beta_emit[b] = -1.0f;
+      if (resid_mass) resid_mass[b] = -1.0;
+    } else {
+      const int k = reject_pos;
+      const float* row = target + (off + k - 1) * static_cast<int64_t>(V);
+      const double lt = softmax_fp64(row, V, pt);
+      if (!std::isfinite(lt)) fl |= ORACLE_FLAG_NONFINITE;
+      const int32_t prev = (k == 1) ? anchor[b] : tokens[b * gamma + k - 2];
+      std::vector<float> L;
+      draft_logits(U + (b * gamma + k - 1) * static_cast<int64_t>(V), W1, W2t, V, r, prev, L);
+      softmax_fp64(L.data(), V, pd);
+      w.assign(V, 0.0);
+      double mass = 0.0, beta = 0.0;
+      for (int v = 0; v < V; ++v) {
+        w[v] = std::max(0.0, pt[v] - pd[v]);
+        mass += w[v];
+        beta += std::min(pt[v], pd[v]);
+      }
+      const double u = static_cast<double>(uniforms[(b * (gamma + 1) + (k - 1)) * 3 + 2]);
+      if (mass > 0.0 && std::isfinite(mass)) {
+        for (int v = 0; v < V; ++v) w[v] /= mass;
+        tok = inverse_cdf(w, u, &mg);
+      } else {
+        fl |= ORACLE_FLAG_ZERO_RESIDUAL;
+        tok = inverse_cdf(pt, u, &mg);
+      }
+      if (beta_emit) beta_emit[b] = static_cast<float>(beta);
+      if (resid_mass) resid_mass[b] = mass;
+    }
+    accept_len[b] = accepted;
+    next_token[b] = tok;
+    if (flags) flags[b] = fl;
+    if (emit_margin) emit_margin[b] = mg;
+  });
+  return 0;
+}
+
+}  // extern "C"

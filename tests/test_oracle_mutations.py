@@ -1,0 +1,70 @@
+"""The pins must catch plausible mistakes: each case compiles a copy of the oracle with one
+planted mistake (on the CPU, in a temporary directory) and checks that a pin test fails."""
+import ctypes
+import functools
+import os
+import subprocess
+import tempfile
+
+import pytest
+
+import oracle
+import test_oracle_draft_pins as dp
+import test_oracle_plan_pins as pp
+import test_oracle_verify_pins as vp
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "dspark_oracle.cpp")
+
+MUTATIONS = [
+    ("residual sign", "std::max(0.0, pt[v] - pd[v])", "std::max(0.0, pd[v] - pt[v])",
+     [vp.test_ab_worked_example_exact_grid]),
+    ("bias from anchor at every position", "prev = cond;", "prev = anchor[b];",
+     [dp.test_markov_chain_probabilities_closed_form]),
+    ("confidence reads x_k", "(k == 0) ? anchor[b] : tokens[b * gamma + k - 1]",
+     "tokens[b * gamma + k]", [dp.test_confidence_closed_forms]),
+    ("survival order ascending", "if (x.a != y.a) return x.a > y.a;",
+     "if (x.a != y.a) return x.a < y.a;", [pp.test_brute_force_planner_optimality]),
+    ("early stop keeps going on a tie", "if (!(theta[k + 1] > theta[k])) break;",
+     "if (!(theta[k + 1] >= theta[k] - 0.2)) break;", [pp.test_appendix_a_theta_values_and_choices]),
+    ("SPS indexed by admissions", "theta[i] = tau[i] * sps[R + i];", "theta[i] = tau[i] * sps[1 + i];",
+     [pp.test_brute_force_planner_optimality]),
+    ("bonus uses the accept uniform", "uniforms[(b * (gamma + 1) + ell) * 3 + 2]",
+     "uniforms[(b * (gamma + 1) + ell) * 3 + 1]", [vp.test_bonus_only_when_all_accepted_and_flags]),
+    ("accept test inverted ratio", "if (u * qk < pt) {", "if (u * pt < qk) {",
+     [functools.partial(vp.test_chi2_output_marginal_equals_target, 1)]),
+    ("residual recomputed at the next position",
+     "draft_logits(U + (b * gamma + k - 1) * static_cast<int64_t>(V), W1, W2t, V, r, prev, L);",
+     "draft_logits(U + (b * gamma + (k < gamma ? k : k - 1)) * static_cast<int64_t>(V), W1, W2t, V, r, prev, L);",
+     [vp.test_sum_min_identity_on_every_emission_row]),
+    ("temperature multiplies", "std::exp(-z / static_cast<double>(T[k]))",
+     "std::exp(-z * static_cast<double>(T[k]))", [dp.test_confidence_closed_forms]),
+    ("draft inverse CDF from the top", "if (cdf > u) {", "if (cdf > 1.0 - u) {",
+     [dp.test_w2_zero_reduces_to_inverse_cdf_categorical]),
+]
+
+
+@pytest.mark.parametrize("name,old,new,pins", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_planted_mistake_is_caught(name, old, new, pins, monkeypatch):
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor not found once: {old}"
+    with tempfile.TemporaryDirectory() as td:
+        path = os.path.join(td, "m.cpp")
+        lib = os.path.join(td, "libm.so")
+        open(path, "w").write(src.replace(old, new))
+        subprocess.run(["g++", "-O1", "-std=c++17", "-fPIC", "-shared", "-pthread", path, "-o", lib],
+                       check=True)
+        mutated = ctypes.CDLL(lib)
+        for fn in ("oracle_markov_draft", "oracle_confidence", "oracle_plan", "oracle_verify"):
+            getattr(mutated, fn).restype = ctypes.c_int
+        monkeypatch.setattr(oracle, "_lib", mutated)
+        caught = False
+        for pin in pins:
+            try:
+                if pin is pp.test_brute_force_planner_optimality:
+                    for seed in range(40):
+                        pin(seed)
+                else:
+                    pin()
+            except AssertionError:
+                caught = True
+        assert caught, f"planted mistake '{name}' was not caught"
