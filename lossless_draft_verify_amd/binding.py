@@ -1,2 +1,234 @@
-"""Placeholder until the HIP library exists."""
-__all__ = []
+"""Thin ctypes binding of libdspark.so: argument marshalling only.
+
+Every function takes torch tensors that live on the GPU, checks dtype / shape / contiguity,
+and passes raw device pointers and the current HIP stream to the C ABI (include/dspark.h).
+All computation happens in the library's HIP kernels; there is no CPU fallback, and a missing
+library raises at the first call.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "Dims", "DsparkError", "FULL_VERIFY", "EARLY_STOP", "FULL_PATH", "LAGGED_TOPK",
+    "OP_DRAFT", "OP_CONFIDENCE", "OP_PLAN", "OP_VERIFY", "FLAG_NONFINITE", "FLAG_ZERO_RESIDUAL",
+    "library_path", "load_library", "workspace_bytes", "workspace", "markov_draft", "confidence",
+    "plan", "verify", "profile_begin", "profile_end", "version",
+]
+
+FULL_VERIFY, EARLY_STOP, FULL_PATH, LAGGED_TOPK = 0, 1, 2, 3
+OP_DRAFT, OP_CONFIDENCE, OP_PLAN, OP_VERIFY = 0, 1, 2, 3
+FLAG_NONFINITE, FLAG_ZERO_RESIDUAL = 1, 2
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libdspark.so")
+
+
+class DsparkError(RuntimeError):
+    pass
+
+
+class _CDims(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("gamma", ctypes.c_int32), ("V", ctypes.c_int32),
+                ("r", ctypes.c_int32), ("d", ctypes.c_int32)]
+
+
+@dataclass(frozen=True)
+class Dims:
+    B: int
+    gamma: int
+    V: int
+    r: int
+    d: int = 8
+
+    def c(self) -> _CDims:
+        return _CDims(self.B, self.gamma, self.V, self.r, self.d)
+
+
+_P = ctypes.c_void_p
+
+
+def load_library():
+    """Load the in-tree libdspark.so (raises if it has not been built)."""
+    global _LIB
+    if _LIB is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise DsparkError(f"{path} is missing: build it with "
+                              "`python -m lossless_draft_verify_amd.build`")
+        lib = ctypes.CDLL(path)
+        lib.dspark_status_string.restype = ctypes.c_char_p
+        lib.dspark_status_string.argtypes = [ctypes.c_int32]
+        lib.dspark_version.restype = ctypes.c_char_p
+        lib.dspark_workspace_bytes.restype = ctypes.c_size_t
+        lib.dspark_workspace_bytes.argtypes = [_CDims, ctypes.c_int32]
+        lib.dspark_markov_draft.restype = ctypes.c_int32
+        lib.dspark_markov_draft.argtypes = [_CDims] + [_P] * 10 + [_P, ctypes.c_size_t, _P]
+        lib.dspark_confidence.restype = ctypes.c_int32
+        lib.dspark_confidence.argtypes = [_CDims] + [_P] * 7 + [_P]
+        lib.dspark_plan.restype = ctypes.c_int32
+        lib.dspark_plan.argtypes = [_CDims, _P, _P, ctypes.c_int32, ctypes.c_int32, _P,
+                                    ctypes.c_int32, _P, _P, _P, _P]
+        lib.dspark_verify.restype = ctypes.c_int32
+        lib.dspark_verify.argtypes = [_CDims] + [_P] * 15 + [_P, ctypes.c_size_t, _P]
+        lib.dspark_profile_begin.restype = ctypes.c_int32
+        lib.dspark_profile_begin.argtypes = [ctypes.c_int32]
+        lib.dspark_profile_end.restype = ctypes.c_int32
+        lib.dspark_profile_end.argtypes = [ctypes.POINTER(ctypes.c_char_p),
+                                           ctypes.POINTER(ctypes.c_int32),
+                                           ctypes.POINTER(ctypes.c_double), ctypes.c_int32]
+        _LIB = lib
+    return _LIB
+
+
+def version() -> str:
+    return load_library().dspark_version().decode()
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        msg = load_library().dspark_status_string(status).decode()
+        raise DsparkError(f"{what}: {msg} (status {status})")
+
+
+def _ptr(t: Optional[torch.Tensor], dtype=None, shape=None, name="tensor"):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise DsparkError(f"{name} must live on the GPU (got {t.device})")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def workspace_bytes(dims: Dims, op: int) -> int:
+    n = load_library().dspark_workspace_bytes(dims.c(), op)
+    if n == ctypes.c_size_t(-1).value:
+        raise DsparkError(f"unsupported dims {dims} for op {op}")
+    return int(n)
+
+
+def workspace(dims: Dims, op: int, device="cuda") -> torch.Tensor:
+    """A workspace tensor of the size an operation needs (uint8, 256-byte aligned)."""
+    return torch.empty(max(1, workspace_bytes(dims, op)), dtype=torch.uint8, device=device)
+
+
+def markov_draft(dims: Dims, U, W1, W2t, anchor, uniforms, *, tokens=None, q=None, lse=None,
+                 logits_dbg=None, force_tokens=None, ws=None, stream=None):
+    """Markov-head draft (dspark_markov_draft). Returns (tokens, q, lse)."""
+    B, g, V, r = dims.B, dims.gamma, dims.V, dims.r
+    dev = U.device
+    tokens = tokens if tokens is not None else torch.empty((B, g), dtype=torch.int32, device=dev)
+    q = q if q is not None else torch.empty((B, g), dtype=torch.float32, device=dev)
+    lse = lse if lse is not None else torch.empty((B, g), dtype=torch.float64, device=dev)
+    ws = ws if ws is not None else workspace(dims, OP_DRAFT, dev)
+    st = load_library().dspark_markov_draft(
+        dims.c(), _ptr(U, torch.float32, (B, g, V), "U"), _ptr(W1, torch.bfloat16, (V, r), "W1"),
+        _ptr(W2t, torch.bfloat16, (V, r), "W2t"), _ptr(anchor, torch.int32, (B,), "anchor"),
+        _ptr(uniforms, torch.float32, (B, g + 1, 3), "uniforms"),
+        _ptr(tokens, torch.int32, (B, g), "tokens"), _ptr(q, torch.float32, (B, g), "q"),
+        _ptr(lse, torch.float64, (B, g), "lse"),
+        _ptr(logits_dbg, torch.float32, (B, g, V), "logits_dbg"),
+        _ptr(force_tokens, torch.int32, (B, g), "force_tokens"), _ptr(ws, torch.uint8, None, "ws"),
+        ws.numel(), _stream(stream))
+    _check(st, "dspark_markov_draft")
+    return tokens, q, lse
+
+
+def confidence(dims: Dims, h, W1, w, T, anchor, tokens, *, conf=None, stream=None):
+    """Confidence head (dspark_confidence). Returns conf [B][gamma] fp32."""
+    B, g, V, r, d = dims.B, dims.gamma, dims.V, dims.r, dims.d
+    conf = conf if conf is not None else torch.empty((B, g), dtype=torch.float32, device=h.device)
+    st = load_library().dspark_confidence(
+        dims.c(), _ptr(h, torch.bfloat16, (B, g, d), "h"), _ptr(W1, torch.bfloat16, (V, r), "W1"),
+        _ptr(w, torch.bfloat16, (d + r,), "w"), _ptr(T, torch.float32, (g,), "T"),
+        _ptr(anchor, torch.int32, (B,), "anchor"), _ptr(tokens, torch.int32, (B, g), "tokens"),
+        _ptr(conf, torch.float32, (B, g), "conf"), _stream(stream))
+    _check(st, "dspark_confidence")
+    return conf
+
+
+def plan(dims: Dims, conf, sps, mode: int, *, ring=None, round_index: int = 0, draft_len=None,
+         row_offsets=None, stats=None, stream=None):
+    """Verify planner (dspark_plan). Returns (draft_len, row_offsets, stats)."""
+    B, g = dims.B, dims.gamma
+    dev = sps.device
+    draft_len = draft_len if draft_len is not None else torch.empty(B, dtype=torch.int32, device=dev)
+    row_offsets = (row_offsets if row_offsets is not None
+                   else torch.empty(B + 1, dtype=torch.int32, device=dev))
+    stats = stats if stats is not None else torch.empty(4, dtype=torch.float64, device=dev)
+    st = load_library().dspark_plan(
+        dims.c(), _ptr(conf, torch.float32, (B, g), "conf"), _ptr(sps, torch.float64, None, "sps"),
+        int(sps.numel()), int(mode), _ptr(ring, torch.float32, (2, B, g), "ring"),
+        int(round_index), _ptr(draft_len, torch.int32, (B,), "draft_len"),
+        _ptr(row_offsets, torch.int32, (B + 1,), "row_offsets"),
+        _ptr(stats, torch.float64, (4,), "stats"), _stream(stream))
+    _check(st, "dspark_plan")
+    return draft_len, row_offsets, stats
+
+
+def verify(dims: Dims, target, row_offsets, draft_len, U, W1, W2t, anchor, tokens, q, lse,
+           uniforms, *, accept_len=None, next_token=None, beta_emit=None, flags=None, ws=None,
+           stream=None):
+    """Lossless verify (dspark_verify). `target` holds at least row_offsets[B] rows of V
+    logits. Returns (accept_len, next_token, beta_emit, flags)."""
+    B, g, V, r = dims.B, dims.gamma, dims.V, dims.r
+    dev = U.device
+    if target.dim() != 2 or target.shape[1] != V:
+        raise ValueError("target must be [rows][V]")
+    accept_len = accept_len if accept_len is not None else torch.empty(B, dtype=torch.int32, device=dev)
+    next_token = next_token if next_token is not None else torch.empty(B, dtype=torch.int32, device=dev)
+    beta_emit = beta_emit if beta_emit is not None else torch.empty(B, dtype=torch.float32, device=dev)
+    flags = flags if flags is not None else torch.empty(B, dtype=torch.int32, device=dev)
+    ws = ws if ws is not None else workspace(dims, OP_VERIFY, dev)
+    st = load_library().dspark_verify(
+        dims.c(), _ptr(target, torch.float32, None, "target"),
+        _ptr(row_offsets, torch.int32, (B + 1,), "row_offsets"),
+        _ptr(draft_len, torch.int32, (B,), "draft_len"), _ptr(U, torch.float32, (B, g, V), "U"),
+        _ptr(W1, torch.bfloat16, (V, r), "W1"), _ptr(W2t, torch.bfloat16, (V, r), "W2t"),
+        _ptr(anchor, torch.int32, (B,), "anchor"), _ptr(tokens, torch.int32, (B, g), "tokens"),
+        _ptr(q, torch.float32, (B, g), "q"), _ptr(lse, torch.float64, (B, g), "lse"),
+        _ptr(uniforms, torch.float32, (B, g + 1, 3), "uniforms"),
+        _ptr(accept_len, torch.int32, (B,), "accept_len"),
+        _ptr(next_token, torch.int32, (B,), "next_token"),
+        _ptr(beta_emit, torch.float32, (B,), "beta_emit"), _ptr(flags, torch.int32, (B,), "flags"),
+        _ptr(ws, torch.uint8, None, "ws"), ws.numel(), _stream(stream))
+    _check(st, "dspark_verify")
+    return accept_len, next_token, beta_emit, flags
+
+
+def profile_begin(capacity: int = 4096):
+    if load_library().dspark_profile_begin(int(capacity)) != 0:
+        raise DsparkError("dspark_profile_begin failed")
+
+
+def profile_end():
+    """Returns {kernel name: (launches, total milliseconds)}."""
+    n = 16
+    names = (ctypes.c_char_p * n)()
+    counts = (ctypes.c_int32 * n)()
+    ms = (ctypes.c_double * n)()
+    k = load_library().dspark_profile_end(names, counts, ms, n)
+    if k < 0:
+        raise DsparkError("dspark_profile_end failed")
+    return {names[i].decode(): (counts[i], ms[i]) for i in range(k)}

@@ -1,0 +1,317 @@
+// C ABI of libdspark.so: host-side argument checks, workspace layout and launch order.
+// The operations and their sources are documented in include/dspark.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+#include <vector>
+
+#include "dspark.h"
+#include "device.h"
+#include "launch.h"
+
+namespace {
+
+using namespace dspark;
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int ntiles_of(int V) { return (V + kTileTokens - 1) / kTileTokens; }
+int nseg_of(int V) { return (V + kSegTokens - 1) / kSegTokens; }
+
+bool rank_ok(int r) {
+  return r == 16 || r == 32 || r == 64 || r == 128 || r == 256 || r == 512;
+}
+
+// B * (gamma + 1) verified rows index grid dimension y of the target pass (<= 65535); the
+// planner sorts all B * gamma candidates in one workgroup's LDS (<= 8192).
+bool dims_ok(const dspark_dims& d) {
+  if (d.B < 1 || d.gamma < 1 || d.V < 2 || !rank_ok(d.r)) return false;
+  if (static_cast<int64_t>(d.B) * (d.gamma + 1) > 65535) return false;
+  return true;
+}
+bool plan_dims_ok(const dspark_dims& d) {
+  return dims_ok(d) && static_cast<int64_t>(d.B) * d.gamma <= 8192;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// ---- workspace layouts ----------------------------------------------------------------------
+struct DraftWs {
+  float* pmax;
+  float* psum;
+};
+size_t draft_ws(const dspark_dims& d, void* base, DraftWs* out) {
+  const size_t n = static_cast<size_t>(d.B) * ntiles_of(d.V);
+  size_t off = 0;
+  char* b = static_cast<char*>(base);
+  if (out) out->pmax = reinterpret_cast<float*>(b + off);
+  off += align_up(n * sizeof(float));
+  if (out) out->psum = reinterpret_cast<float*>(b + off);
+  off += align_up(n * sizeof(float));
+  return off;
+}
+
+size_t verify_ws(const dspark_dims& d, void* base, VerifyWs* out) {
+  const size_t rows = static_cast<size_t>(d.B) * (d.gamma + 1);
+  const size_t nseg = nseg_of(d.V), nt = ntiles_of(d.V), B = d.B;
+  size_t off = 0;
+  char* b = static_cast<char*>(base);
+  auto take = [&](size_t bytes) {
+    char* p = b + off;
+    off += align_up(bytes);
+    return p;
+  };
+  VerifyWs w;
+  w.seg_max = reinterpret_cast<float*>(take(rows * nseg * sizeof(float)));
+  w.seg_sum = reinterpret_cast<double*>(take(rows * nseg * sizeof(double)));
+  w.ekind = reinterpret_cast<int32_t*>(take(B * sizeof(int32_t)));
+  w.epos = reinterpret_cast<int32_t*>(take(B * sizeof(int32_t)));
+  w.erow = reinterpret_cast<int32_t*>(take(B * sizeof(int32_t)));
+  w.erow_lse = reinterpret_cast<double*>(take(B * sizeof(double)));
+  w.eflags = reinterpret_cast<uint32_t*>(take(B * sizeof(uint32_t)));
+  w.rsum = reinterpret_cast<double*>(take(B * nt * sizeof(double)));
+  w.rmin = reinterpret_cast<double*>(take(B * nt * sizeof(double)));
+  if (out) *out = w;
+  return off;
+}
+
+// ---- kernel timing ----------------------------------------------------------------------------
+enum KernelId {
+  kMarkovStep = 0,
+  kDraftSample,
+  kConfidence,
+  kPlan,
+  kTargetStats,
+  kAccept,
+  kResidualPartials,
+  kEmitSample,
+  kNumKernels
+};
+const char* const kKernelNames[kNumKernels] = {"markov_step",  "draft_sample", "confidence",
+                                               "plan",         "target_stats", "accept",
+                                               "residual_partials", "emit_sample"};
+
+struct Profiler {
+  bool armed = false;
+  int capacity = 0;
+  int used = 0;
+  std::vector<hipEvent_t> events;
+  std::vector<int> ids;
+};
+Profiler g_prof;
+
+template <class F>
+hipError_t timed(KernelId id, hipStream_t s, F launch) {
+  const bool rec = g_prof.armed && g_prof.used < g_prof.capacity;
+  if (rec) (void)hipEventRecord(g_prof.events[2 * g_prof.used], s);
+  const hipError_t e = launch();
+  if (rec) {
+    (void)hipEventRecord(g_prof.events[2 * g_prof.used + 1], s);
+    g_prof.ids[g_prof.used] = id;
+    ++g_prof.used;
+  }
+  return e;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dspark_status_string(dspark_status s) {
+  switch (s) {
+    case DSPARK_OK: return "ok";
+    case DSPARK_ERR_NULL: return "a required pointer is NULL";
+    case DSPARK_ERR_SHAPE: return "a size is out of the supported range";
+    case DSPARK_ERR_ALIGN: return "a pointer is not aligned";
+    case DSPARK_ERR_WORKSPACE: return "workspace too small";
+    case DSPARK_ERR_SPS: return "SPS table shorter than B * (gamma + 1) + 1";
+    case DSPARK_ERR_HIP: return "HIP launch failed";
+    case DSPARK_ERR_MODE: return "unknown plan mode or missing ring";
+    default: return "unknown status";
+  }
+}
+
+const char* dspark_version(void) { return "dspark-gfx950 0.1"; }
+
+size_t dspark_workspace_bytes(dspark_dims dims, int32_t op) {
+  if (!dims_ok(dims)) return static_cast<size_t>(-1);
+  switch (op) {
+    case DSPARK_OP_DRAFT: return draft_ws(dims, nullptr, nullptr);
+    case DSPARK_OP_CONFIDENCE: return 0;
+    case DSPARK_OP_PLAN: return 0;
+    case DSPARK_OP_VERIFY: return verify_ws(dims, nullptr, nullptr);
+    default: return static_cast<size_t>(-1);
+  }
+}
+
+dspark_status dspark_markov_draft(dspark_dims dims, const float* U, const uint16_t* W1,
+                                  const uint16_t* W2t, const int32_t* anchor,
+                                  const float* uniforms, int32_t* tokens, float* q_tok,
+                                  double* lse, float* logits_dbg, const int32_t* force_tokens,
+                                  void* ws, size_t ws_bytes, void* stream) {
+  if (!U || !W1 || !W2t || !anchor || !uniforms || !tokens || !q_tok || !lse || !ws)
+    return DSPARK_ERR_NULL;
+  if (!dims_ok(dims)) return DSPARK_ERR_SHAPE;
+  if (!aligned(U, 16) || !aligned(W1, 16) || !aligned(W2t, 16) || !aligned(anchor, 4) ||
+      !aligned(uniforms, 4) || !aligned(tokens, 4) || !aligned(q_tok, 4) || !aligned(lse, 8) ||
+      (logits_dbg && !aligned(logits_dbg, 4)) || (force_tokens && !aligned(force_tokens, 4)) ||
+      !aligned(ws, kAlign))
+    return DSPARK_ERR_ALIGN;
+  if (ws_bytes < draft_ws(dims, nullptr, nullptr)) return DSPARK_ERR_WORKSPACE;
+  DraftWs w;
+  draft_ws(dims, ws, &w);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int nt = ntiles_of(dims.V);
+  for (int k = 0; k < dims.gamma; ++k) {
+    const int32_t* prev = anchor;
+    int stride = 1;
+    if (k > 0) {
+      prev = (force_tokens ? force_tokens : tokens) + (k - 1);
+      stride = dims.gamma;
+    }
+    StepArgs sa{dims.B, dims.V, dims.gamma, k, nt, U, W1, W2t, prev, stride, w.pmax, w.psum,
+                logits_dbg};
+    if (timed(kMarkovStep, s, [&] { return launch_markov_step(sa, dims.r, s); }) != hipSuccess)
+      return DSPARK_ERR_HIP;
+    SampleArgs pa{dims.B, dims.V, dims.gamma, k, nt, U, W1, W2t, prev, stride, w.pmax, w.psum,
+                  uniforms, force_tokens, tokens, q_tok, lse};
+    if (timed(kDraftSample, s, [&] { return launch_draft_sample(pa, dims.r, s); }) != hipSuccess)
+      return DSPARK_ERR_HIP;
+  }
+  return DSPARK_OK;
+}
+
+dspark_status dspark_confidence(dspark_dims dims, const uint16_t* h, const uint16_t* W1,
+                                const uint16_t* w, const float* T, const int32_t* anchor,
+                                const int32_t* tokens, float* conf, void* stream) {
+  if (!h || !W1 || !w || !T || !anchor || !tokens || !conf) return DSPARK_ERR_NULL;
+  if (!dims_ok(dims) || dims.d < 8 || dims.d % 8 != 0) return DSPARK_ERR_SHAPE;
+  if (!aligned(h, 16) || !aligned(W1, 16) || !aligned(w, 16) || !aligned(T, 4) ||
+      !aligned(anchor, 4) || !aligned(tokens, 4) || !aligned(conf, 4))
+    return DSPARK_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  ConfArgs a{dims.B, dims.gamma, dims.r, dims.d, h, W1, w, T, anchor, tokens, conf};
+  if (timed(kConfidence, s, [&] { return launch_confidence(a, s); }) != hipSuccess)
+    return DSPARK_ERR_HIP;
+  return DSPARK_OK;
+}
+
+dspark_status dspark_plan(dspark_dims dims, const float* conf, const double* sps, int32_t sps_len,
+                          int32_t mode, float* ring, int32_t round_index, int32_t* draft_len,
+                          int32_t* row_offsets, double* stats, void* stream) {
+  if (!sps || !draft_len || !row_offsets) return DSPARK_ERR_NULL;
+  if (mode < DSPARK_PLAN_FULL_VERIFY || mode > DSPARK_PLAN_LAGGED_TOPK) return DSPARK_ERR_MODE;
+  if (mode != DSPARK_PLAN_FULL_VERIFY && !conf) return DSPARK_ERR_NULL;
+  if (mode == DSPARK_PLAN_LAGGED_TOPK && !ring) return DSPARK_ERR_MODE;
+  if (!plan_dims_ok(dims) || round_index < 0) return DSPARK_ERR_SHAPE;
+  if (static_cast<int64_t>(sps_len) < static_cast<int64_t>(dims.B) * (dims.gamma + 1) + 1)
+    return DSPARK_ERR_SPS;
+  if ((conf && !aligned(conf, 4)) || !aligned(sps, 8) || (ring && !aligned(ring, 4)) ||
+      !aligned(draft_len, 4) || !aligned(row_offsets, 4) || (stats && !aligned(stats, 8)))
+    return DSPARK_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  PlanArgs a{dims.B, dims.gamma, sps_len, mode, round_index, conf, sps, ring, draft_len,
+             row_offsets, stats};
+  if (timed(kPlan, s, [&] { return launch_plan(a, s); }) != hipSuccess) return DSPARK_ERR_HIP;
+  return DSPARK_OK;
+}
+
+dspark_status dspark_verify(dspark_dims dims, const float* target, const int32_t* row_offsets,
+                            const int32_t* draft_len, const float* U, const uint16_t* W1,
+                            const uint16_t* W2t, const int32_t* anchor, const int32_t* tokens,
+                            const float* q_tok, const double* lse, const float* uniforms,
+                            int32_t* accept_len, int32_t* next_token, float* beta_emit,
+                            uint32_t* flags, void* ws, size_t ws_bytes, void* stream) {
+  if (!target || !row_offsets || !draft_len || !U || !W1 || !W2t || !anchor || !tokens ||
+      !q_tok || !lse || !uniforms || !accept_len || !next_token || !ws)
+    return DSPARK_ERR_NULL;
+  if (!dims_ok(dims)) return DSPARK_ERR_SHAPE;
+  if (!aligned(target, 16) || !aligned(U, 16) || !aligned(W1, 16) || !aligned(W2t, 16) ||
+      !aligned(row_offsets, 4) || !aligned(draft_len, 4) || !aligned(anchor, 4) ||
+      !aligned(tokens, 4) || !aligned(q_tok, 4) || !aligned(lse, 8) || !aligned(uniforms, 4) ||
+      !aligned(accept_len, 4) || !aligned(next_token, 4) || (beta_emit && !aligned(beta_emit, 4)) ||
+      (flags && !aligned(flags, 4)) || !aligned(ws, kAlign))
+    return DSPARK_ERR_ALIGN;
+  if (ws_bytes < verify_ws(dims, nullptr, nullptr)) return DSPARK_ERR_WORKSPACE;
+  VerifyArgs a;
+  a.B = dims.B;
+  a.V = dims.V;
+  a.gamma = dims.gamma;
+  a.r = dims.r;
+  a.ntiles = ntiles_of(dims.V);
+  a.nseg = nseg_of(dims.V);
+  a.target = target;
+  a.row_offsets = row_offsets;
+  a.draft_len = draft_len;
+  a.U = U;
+  a.W1 = W1;
+  a.W2t = W2t;
+  a.anchor = anchor;
+  a.tokens = tokens;
+  a.q = q_tok;
+  a.lse = lse;
+  a.uniforms = uniforms;
+  a.accept_len = accept_len;
+  a.next_token = next_token;
+  a.beta_emit = beta_emit;
+  a.flags = flags;
+  verify_ws(dims, ws, &a.ws);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (timed(kTargetStats, s, [&] { return launch_target_stats(a, s); }) != hipSuccess)
+    return DSPARK_ERR_HIP;
+  if (timed(kAccept, s, [&] { return launch_accept(a, s); }) != hipSuccess) return DSPARK_ERR_HIP;
+  if (timed(kResidualPartials, s, [&] { return launch_residual_partials(a, s); }) != hipSuccess)
+    return DSPARK_ERR_HIP;
+  if (timed(kEmitSample, s, [&] { return launch_emit_sample(a, s); }) != hipSuccess)
+    return DSPARK_ERR_HIP;
+  return DSPARK_OK;
+}
+
+int32_t dspark_profile_begin(int32_t capacity) {
+  if (capacity < 1 || g_prof.armed) return -1;
+  g_prof.events.assign(2 * static_cast<size_t>(capacity), nullptr);
+  for (auto& e : g_prof.events)
+    if (hipEventCreate(&e) != hipSuccess) return -1;
+  g_prof.ids.assign(capacity, 0);
+  g_prof.capacity = capacity;
+  g_prof.used = 0;
+  g_prof.armed = true;
+  return 0;
+}
+
+int32_t dspark_profile_end(const char** names, int32_t* counts, double* total_ms,
+                           int32_t max_names) {
+  if (!g_prof.armed) return -1;
+  int32_t rc = 0;
+  std::vector<double> ms(kNumKernels, 0.0);
+  std::vector<int> cnt(kNumKernels, 0);
+  if (g_prof.used > 0 && hipEventSynchronize(g_prof.events[2 * g_prof.used - 1]) != hipSuccess)
+    rc = -1;
+  for (int i = 0; rc == 0 && i < g_prof.used; ++i) {
+    float t = 0.0f;
+    if (hipEventElapsedTime(&t, g_prof.events[2 * i], g_prof.events[2 * i + 1]) != hipSuccess) {
+      rc = -1;
+      break;
+    }
+    ms[g_prof.ids[i]] += t;
+    cnt[g_prof.ids[i]] += 1;
+  }
+  for (auto& e : g_prof.events) (void)hipEventDestroy(e);
+  g_prof.events.clear();
+  g_prof.armed = false;
+  g_prof.used = 0;
+  if (rc != 0) return rc;
+  int32_t n = 0;
+  for (int k = 0; k < kNumKernels && n < max_names; ++k) {
+    if (names) names[n] = kKernelNames[k];
+    if (counts) counts[n] = cnt[k];
+    if (total_ms) total_ms[n] = ms[k];
+    ++n;
+  }
+  return n;
+}
+
+}  // extern "C"

@@ -1,0 +1,273 @@
+// Device building blocks for the gfx950 DSpark kernels: MFMA tiles, exact-order reductions and
+// the fp32 exponential used for every softmax term.
+//
+// Determinism: every reduction below combines values in a fixed order, and the HIP sources are
+// compiled with -ffp-contract=off, so the same inputs give the same bits in every kernel that
+// calls these helpers (a sampler can recompute a term exactly as the streaming pass made it).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dspark {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(8 * sizeof(uint16_t)))) uint16_t u16x8_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+
+constexpr int kWave = 64;
+constexpr int kBlock = 256;          // threads per workgroup for the streaming kernels
+constexpr int kTileTokens = 32;      // tokens per MFMA tile = tokens per draft partial
+constexpr int kSegTokens = 4096;     // tokens per target-row segment
+constexpr float kNegInf = -__builtin_inff();
+
+// One 32x32x16 bf16 MFMA step (fp32 accumulate). Lane l holds A[m = l % 32][k = 8 (l / 32) + i]
+// and B[k = 8 (l / 32) + i][n = l % 32], i = 0..7; the result lane l, slot j holds
+// C[m = 8 (j / 4) + 4 (l / 32) + j % 4][n = l % 32]. In the kernels m indexes tokens and n
+// indexes requests: out[token][request] = sum_i W2t[token][i] * E[request][i].
+__device__ __forceinline__ f32x16_t mfma_32x32x16(u16x8_t a, u16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// Token offset (within a 32-token tile) of accumulator slot j in a lane of half `half`.
+__device__ __forceinline__ int tile_token(int j, int half) {
+  return 8 * (j >> 2) + 4 * half + (j & 3);
+}
+
+__device__ __forceinline__ u16x8_t load_u16x8(const uint16_t* p) {
+  return *reinterpret_cast<const u16x8_t*>(p);
+}
+
+__device__ __forceinline__ u16x8_t zero_u16x8() {
+  u16x8_t z = {0, 0, 0, 0, 0, 0, 0, 0};
+  return z;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// exp(x) for x <= 0 in fp32: exp2 of x*log2(e), with the rounding error of that product
+// carried as a first-order correction (2^(y + dy) = 2^y (1 + dy ln 2)). Values below -200 are
+// clamped (the result underflows to 0 either way); NaN propagates.
+__device__ __forceinline__ float exp_term(float x) {
+  const float kLog2eHi = 1.44269502162933349609375f;   // fp32(log2 e)
+  const float kLog2eLo = 1.925963033500011079e-8f;     // log2 e - kLog2eHi
+  const float kLn2 = 0.693147180559945309f;
+  x = (x < -200.0f) ? -200.0f : x;
+  const float y = x * kLog2eHi;
+  const float dy = __builtin_fmaf(x, kLog2eHi, -y) + x * kLog2eLo;
+  const float e = __builtin_amdgcn_exp2f(y);
+  return __builtin_fmaf(e, dy * kLn2, e);
+}
+
+// ---- wave (64-lane) reductions in a fixed butterfly order ------------------------------------
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ int wave_max_int(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+__device__ __forceinline__ int wave_min_int(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = min(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+// Inclusive scan over the 64 lanes (Hillis-Steele, fixed order).
+__device__ __forceinline__ double wave_inclusive_scan(double v, int lane) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const double t = __shfl_up(v, o, kWave);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+__device__ __forceinline__ int wave_inclusive_scan_int(int v, int lane) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int t = __shfl_up(v, o, kWave);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+// ---- block reductions (blockDim.x = NT, a multiple of 64; `red` holds NT/64 slots) -------------
+template <int NT>
+__device__ __forceinline__ float block_max(float v, float* red) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  v = wave_max(v);
+  __syncthreads();
+  if (lane == 0) red[w] = v;
+  __syncthreads();
+  float m = red[0];
+#pragma unroll
+  for (int i = 1; i < NT / 64; ++i) m = fmaxf(m, red[i]);
+  return m;
+}
+template <int NT>
+__device__ __forceinline__ double block_sum(double v, double* red) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  v = wave_sum(v);
+  __syncthreads();
+  if (lane == 0) red[w] = v;
+  __syncthreads();
+  double s = red[0];
+#pragma unroll
+  for (int i = 1; i < NT / 64; ++i) s += red[i];
+  return s;
+}
+template <int NT>
+__device__ __forceinline__ int block_max_int(int v, int* red) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  v = wave_max_int(v);
+  __syncthreads();
+  if (lane == 0) red[w] = v;
+  __syncthreads();
+  int m = red[0];
+#pragma unroll
+  for (int i = 1; i < NT / 64; ++i) m = max(m, red[i]);
+  return m;
+}
+template <int NT>
+__device__ __forceinline__ int block_min_int(int v, int* red) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  v = wave_min_int(v);
+  __syncthreads();
+  if (lane == 0) red[w] = v;
+  __syncthreads();
+  int m = red[0];
+#pragma unroll
+  for (int i = 1; i < NT / 64; ++i) m = min(m, red[i]);
+  return m;
+}
+// Exclusive scan over the block; returns this thread's exclusive prefix, *total the sum.
+template <int NT>
+__device__ __forceinline__ double block_exclusive_scan(double v, double* red, double* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const double inc = wave_inclusive_scan(v, lane);
+  double exc = __shfl_up(inc, 1, kWave);
+  if (lane == 0) exc = 0.0;
+  __syncthreads();
+  if (lane == 63) red[w] = inc;
+  __syncthreads();
+  double before = 0.0, tot = 0.0;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) {
+    if (i < w) before += red[i];
+    tot += red[i];
+  }
+  *total = tot;
+  return before + exc;
+}
+template <int NT>
+__device__ __forceinline__ int block_exclusive_scan_int(int v, int* red, int* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int inc = wave_inclusive_scan_int(v, lane);
+  __syncthreads();
+  if (lane == 63) red[w] = inc;
+  __syncthreads();
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) {
+    if (i < w) before += red[i];
+    tot += red[i];
+  }
+  *total = tot;
+  return before + (inc - v);
+}
+
+// Locate the chunk holding the draw: chunks 0..n-1 carry masses mass(c) >= 0 (ascending token
+// order); the draw is the first chunk whose cumulative mass exceeds u * Z, Z = total mass.
+// Each thread owns a contiguous range of chunks; the owner of the draw is the last thread with
+// positive mass whose exclusive prefix is <= u * Z, and it walks its range in order. If rounding
+// leaves the draw past the owner's range, the owner's last positive chunk is taken with
+// take_last set (the caller then takes that chunk's last positive token).
+struct Located {
+  int chunk;        // -1 if the total mass is not positive and finite
+  int take_last;
+  double before;    // cumulative mass of the chunks before `chunk`
+  double target;    // u * Z
+  double total;     // Z
+};
+
+// target_of(Z) gives the draw's position on the cumulative-mass axis (u * Z for a plain draw).
+template <int NT, class MassFn, class TargetFn>
+__device__ Located locate_chunk_t(int n, TargetFn target_of, MassFn mass, double* red_d,
+                                  int* red_i, Located* shared_out) {
+  const int tid = threadIdx.x;
+  const int per = (n + NT - 1) / NT;
+  const int c0 = min(n, tid * per), c1 = min(n, c0 + per);
+  double S = 0.0;
+  for (int c = c0; c < c1; ++c) S += mass(c);
+  double Z;
+  const double P = block_exclusive_scan<NT>(S, red_d, &Z);
+  const double target = target_of(Z);
+  const bool ok = (Z > 0.0) && (Z < __builtin_inf());
+  const int owner = block_max_int<NT>((ok && S > 0.0 && P <= target) ? tid : -1, red_i);
+  if (tid == owner) {
+    Located r;
+    r.chunk = -1;
+    r.take_last = 0;
+    r.before = 0.0;
+    double cum = P;
+    int last = -1;
+    double last_before = P;
+    for (int c = c0; c < c1; ++c) {
+      const double m = mass(c);
+      if (m > 0.0) {
+        last = c;
+        last_before = cum;
+      }
+      if (cum + m > target) {
+        r.chunk = c;
+        r.before = cum;
+        break;
+      }
+      cum += m;
+    }
+    if (r.chunk < 0) {
+      r.chunk = last;
+      r.before = last_before;
+      r.take_last = 1;
+    }
+    r.target = target;
+    r.total = Z;
+    *shared_out = r;
+  }
+  __syncthreads();
+  Located res;
+  if (owner < 0) {
+    res.chunk = -1;
+    res.take_last = 0;
+    res.before = 0.0;
+    res.target = target;
+    res.total = Z;
+  } else {
+    res = *shared_out;
+  }
+  __syncthreads();
+  return res;
+}
+
+template <int NT, class MassFn>
+__device__ Located locate_chunk(int n, double u, MassFn mass, double* red_d, int* red_i,
+                                Located* shared_out) {
+  return locate_chunk_t<NT>(n, [u](double Z) { return u * Z; }, mass, red_d, red_i, shared_out);
+}
+
+// Mass of a partial (tile max m, fp32 sum s of exp(L - m)) relative to the row max M.
+__device__ __forceinline__ double partial_mass(float m, double s, float M) {
+  return (m == kNegInf) ? 0.0 : exp(static_cast<double>(m) - static_cast<double>(M)) * s;
+}
+
+}  // namespace dspark

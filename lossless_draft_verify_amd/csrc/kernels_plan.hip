@@ -1,0 +1,212 @@
+// Survival-ordered verify planner: one workgroup, everything in LDS.
+//
+// Sources: [V41] blog.javazero.top "DeepSeek-V4.1 模型结构（6）：解码，DSpark", "调度器"
+// ("目标函数": B, tau, Theta; "贪心就能解": sort the survivals, admit one by one, stop once
+// Theta stops rising; the asynchronous production variant in the last paragraph before "训练");
+// [ZDS] zdszero.github.io spec_dspark, "调度" and "在 SGLang 里" (lengths in [1, gamma+1], a
+// flat SPS table degrades to full verify, confidences relayed through a ring, lag 2);
+// [CSDN] deepseek.csdn.net DSpark walk-through, 5.3 and 8.
+//
+// Steps: a_{b,j} = prod c (sequential fp64 per request) -> bitonic sort of (a desc, b, j) ->
+// prefix sums tau_i -> Theta_i = tau_i * sps[B + i] -> admission count by mode -> l_b from
+// the rank of each candidate -> row_offsets. LAGGED_TOPK first runs the full-path search on
+// the ring slot holding the confidences of two rounds back, then overwrites that slot.
+#include <limits.h>
+
+#include "device.h"
+#include "launch.h"
+
+namespace dspark {
+
+namespace {
+
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanMax = 8192;   // B * gamma limit
+
+enum { kFullVerify = 0, kEarlyStop = 1, kFullPath = 2, kLaggedTopK = 3 };
+
+struct PlanSmem {
+  double a[kPlanMax];   // survivals, then prefix sums tau
+  int idx[kPlanMax];    // candidate index b * gamma + j, sorted alongside a
+  double red_d[kPlanThreads / 64];
+  int red_i[kPlanThreads / 64];
+  int n_admit;
+};
+
+__device__ __forceinline__ bool before(double ai, int ii, double aj, int ij) {
+  return (ai > aj) || (ai == aj && ii < ij);
+}
+
+// Fill survivals from conf, sort, and turn a[] into tau_i (a[i] = tau_{i+1}). Returns nothing;
+// results in sm.
+__device__ void sorted_path(PlanSmem& sm, const float* __restrict__ conf, int B, int gamma) {
+  const int tid = threadIdx.x;
+  const int N = B * gamma;
+  int N2 = 1;
+  while (N2 < N) N2 <<= 1;
+  for (int b = tid; b < B; b += kPlanThreads) {
+    double prod = 1.0;
+    for (int j = 0; j < gamma; ++j) {
+      prod *= static_cast<double>(conf[b * gamma + j]);
+      sm.a[b * gamma + j] = prod;
+      sm.idx[b * gamma + j] = b * gamma + j;
+    }
+  }
+  for (int i = N + tid; i < N2; i += kPlanThreads) {
+    sm.a[i] = -__builtin_inf();
+    sm.idx[i] = INT_MAX;
+  }
+  __syncthreads();
+  // Bitonic sort into "before" order.
+  for (int size = 2; size <= N2; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int t = tid; t < N2 / 2; t += kPlanThreads) {
+        const int i = 2 * t - (t & (stride - 1));
+        const int j = i + stride;
+        const bool up = (i & size) == 0;
+        const double ai = sm.a[i], aj = sm.a[j];
+        const int ii = sm.idx[i], ij = sm.idx[j];
+        const bool swap = up ? before(aj, ij, ai, ii) : before(ai, ii, aj, ij);
+        if (swap) {
+          sm.a[i] = aj;
+          sm.a[j] = ai;
+          sm.idx[i] = ij;
+          sm.idx[j] = ii;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  // Inclusive prefix sums of the sorted survivals, plus B: a[i] <- tau_{i+1}.
+  const int per = (N + kPlanThreads - 1) / kPlanThreads;
+  const int i0 = min(N, tid * per), i1 = min(N, i0 + per);
+  double s = 0.0;
+  for (int i = i0; i < i1; ++i) s += sm.a[i];
+  double total;
+  const double before_sum = block_exclusive_scan<kPlanThreads>(s, sm.red_d, &total);
+  double run = static_cast<double>(B) + before_sum;
+  for (int i = i0; i < i1; ++i) {
+    run += sm.a[i];
+    sm.a[i] = run;
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ double tau_at(const PlanSmem& sm, int i, int B) {
+  return i == 0 ? static_cast<double>(B) : sm.a[i - 1];
+}
+
+// Admission count along the current path for EARLY_STOP or FULL_PATH.
+__device__ int admit_count(PlanSmem& sm, const double* __restrict__ sps, int B, int N, int mode) {
+  const int tid = threadIdx.x;
+  if (mode == kEarlyStop) {
+    int first = N;
+    for (int i = tid; i < N; i += kPlanThreads) {
+      const double t0 = tau_at(sm, i, B) * sps[B + i];
+      const double t1 = tau_at(sm, i + 1, B) * sps[B + i + 1];
+      if (!(t1 > t0)) first = min(first, i);
+    }
+    return block_min_int<kPlanThreads>(first, sm.red_i);
+  }
+  // FULL_PATH: first maximiser of Theta_i, i = 0..N.
+  double best = -__builtin_inf();
+  int best_i = INT_MAX;
+  for (int i = tid; i <= N; i += kPlanThreads) {
+    const double th = tau_at(sm, i, B) * sps[B + i];
+    if (th > best) {
+      best = th;
+      best_i = i;
+    }
+  }
+  // block max of Theta, then the smallest index attaining it
+  double w = best;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) w = fmax(w, __shfl_xor(w, o, kWave));
+  __syncthreads();
+  if ((tid & 63) == 0) sm.red_d[tid >> 6] = w;
+  __syncthreads();
+  double gmax = sm.red_d[0];
+  for (int k = 1; k < kPlanThreads / 64; ++k) gmax = fmax(gmax, sm.red_d[k]);
+  return block_min_int<kPlanThreads>(best == gmax ? best_i : INT_MAX, sm.red_i);
+}
+
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs p) {
+  __shared__ PlanSmem sm;
+  const int tid = threadIdx.x;
+  const int B = p.B, gamma = p.gamma, N = B * gamma;
+
+  int n_admit = N;
+  double capacity = -1.0;
+  const bool lagged = (p.mode == kLaggedTopK) && (p.round_index >= 2);
+  if (lagged) {
+    const float* lag = p.ring + static_cast<size_t>(p.round_index % 2) * N;
+    sorted_path(sm, lag, B, gamma);
+    const int k_lag = admit_count(sm, p.sps, B, N, kFullPath);
+    capacity = static_cast<double>(B) + static_cast<double>(k_lag);
+    n_admit = min(k_lag, N);
+    __syncthreads();
+  }
+  const bool have_conf = p.conf != nullptr;
+  if (have_conf) {
+    sorted_path(sm, p.conf, B, gamma);
+    if (p.mode == kEarlyStop || (p.mode == kLaggedTopK && !lagged)) {
+      n_admit = admit_count(sm, p.sps, B, N, kEarlyStop);
+    } else if (p.mode == kFullPath) {
+      n_admit = admit_count(sm, p.sps, B, N, kFullPath);
+    } else if (p.mode == kFullVerify) {
+      n_admit = N;
+    }
+  }
+  if (tid == 0) {
+    const double tau = have_conf ? tau_at(sm, n_admit, B) : __builtin_nan("");
+    if (p.stats) {
+      p.stats[0] = static_cast<double>(B + n_admit);
+      p.stats[1] = tau;
+      p.stats[2] = tau * p.sps[B + n_admit];
+      p.stats[3] = lagged ? capacity : static_cast<double>(B + n_admit);
+    }
+    sm.n_admit = n_admit;
+  }
+  __syncthreads();
+  if (p.mode == kLaggedTopK) {
+    float* slot = p.ring + static_cast<size_t>(p.round_index % 2) * N;
+    for (int i = tid; i < N; i += kPlanThreads) slot[i] = p.conf[i];
+  }
+  // Ranks: candidate (b, j) is admitted iff its sorted position is < n_admit. Reuse a[] as an
+  // int array of positions per candidate.
+  int* rank = reinterpret_cast<int*>(sm.a);
+  if (have_conf) {
+    for (int i = tid; i < N; i += kPlanThreads) rank[sm.idx[i]] = i;
+  } else {
+    for (int i = tid; i < N; i += kPlanThreads) rank[i] = 0;
+  }
+  __syncthreads();
+  // l_b and row offsets (exclusive scan of 1 + l_b over contiguous request ranges).
+  const int per = (B + kPlanThreads - 1) / kPlanThreads;
+  const int b0 = min(B, tid * per), b1 = min(B, b0 + per);
+  int cnt = 0;
+  for (int b = b0; b < b1; ++b) {
+    int l = 0;
+    for (int j = 0; j < gamma; ++j) l += (rank[b * gamma + j] < n_admit) ? 1 : 0;
+    p.draft_len[b] = l;
+    cnt += 1 + l;
+  }
+  int total;
+  int off = block_exclusive_scan_int<kPlanThreads>(cnt, sm.red_i, &total);
+  for (int b = b0; b < b1; ++b) {
+    p.row_offsets[b] = off;
+    int l = 0;
+    for (int j = 0; j < gamma; ++j) l += (rank[b * gamma + j] < n_admit) ? 1 : 0;
+    off += 1 + l;
+  }
+  if (tid == 0) p.row_offsets[B] = total;
+}
+
+}  // namespace
+
+hipError_t launch_plan(const PlanArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace dspark

@@ -1,0 +1,360 @@
+// Lossless verify for gfx950.
+//
+// Sources: [V41] blog.javazero.top "DeepSeek-V4.1 模型结构（6）：解码，DSpark",
+// "投机解码：让小的先猜，大的一次验一串" and the derivation that follows (accept with
+// min(1, p/q); on reject resample from norm(max(0, p - q)); left to right, the first reject
+// voids the rest; at least one token per round, the bonus from the target when all are
+// accepted; that token is the next anchor); [AIL] ailearn.mscapital.top "DSpark：...", 02;
+// [CSDN] deepseek.csdn.net DSpark walk-through, 2.1.
+//
+// Kernels, in stream order (no host synchronisation; grids are sized for the largest plan and
+// read the actual row count from row_offsets[B] on the device):
+//   target_stats       every verified target row, 4096-token segments: segment max and fp64 sum
+//                      of exp(t - segment max)
+//   accept             one wave per request: row log-sum-exp from the segments, left-to-right
+//                      accept test u * q < p_t(x), emission kind / position / row
+//   residual_partials  requests that rejected: the draft logits of the rejected position are
+//                      recomputed with the draft's MFMA sequence (bit-identical), fused with the
+//                      target row into w = max(0, p_t - p_d) and min(p_t, p_d), summed per tile
+//   emit_sample        one workgroup per request: inverse-CDF draw from the residual tiles, or
+//                      from the target row's segments for a bonus (or a zero-mass residual)
+#include "device.h"
+#include "launch.h"
+#include "tiles.h"
+
+namespace dspark {
+
+namespace {
+
+__global__ __launch_bounds__(kBlock) void target_stats_kernel(VerifyArgs p) {
+  __shared__ float red_f[kBlock / 64];
+  __shared__ double red_d[kBlock / 64];
+  const int row = blockIdx.y;
+  if (row >= p.row_offsets[p.B]) return;
+  const int t0 = blockIdx.x * kSegTokens;
+  const float* trow = p.target + static_cast<size_t>(row) * p.V;
+  const bool vec4 = (p.V & 3) == 0;
+  float x[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int v = t0 + 1024 * i + 4 * threadIdx.x;
+    float o[4];
+    load4(trow, v, p.V, vec4, o);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[4 * i + e] = (v + e < p.V) ? o[e] : kNegInf;
+  }
+  float m = max16(x);
+  m = block_max<kBlock>(m, red_f);
+  double s = 0.0;
+  if (m != kNegInf) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) s += static_cast<double>(exp_term(x[j] - m));
+  }
+  s = block_sum<kBlock>(s, red_d);
+  if (threadIdx.x == 0) {
+    p.ws.seg_max[static_cast<size_t>(row) * p.nseg + blockIdx.x] = m;
+    p.ws.seg_sum[static_cast<size_t>(row) * p.nseg + blockIdx.x] = s;
+  }
+}
+
+// log-sum-exp of one target row from its segment partials (whole wave; all lanes get it).
+__device__ double row_lse_wave(const VerifyArgs& p, int row, int lane) {
+  const size_t base = static_cast<size_t>(row) * p.nseg;
+  float m = kNegInf;
+  for (int s = lane; s < p.nseg; s += kWave) m = fmaxf(m, p.ws.seg_max[base + s]);
+  m = wave_max(m);
+  double z = 0.0;
+  for (int s = lane; s < p.nseg; s += kWave) z += partial_mass(p.ws.seg_max[base + s], p.ws.seg_sum[base + s], m);
+  z = wave_sum(z);
+  return static_cast<double>(m) + log(z);
+}
+
+__global__ __launch_bounds__(kBlock) void accept_kernel(VerifyArgs p) {
+  const int lane = threadIdx.x & 63;
+  const int b = blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);
+  if (b >= p.B) return;
+  const int ell = p.draft_len[b];
+  const int off = p.row_offsets[b];
+  uint32_t fl = 0;
+  int accepted = 0, kind = kEmitBonus, epos = ell + 1, erow = off + ell;
+  double else_ = 0.0;
+  bool rejected = false;
+  for (int k = 1; k <= ell; ++k) {
+    const int row = off + k - 1;
+    const double l = row_lse_wave(p, row, lane);
+    if (!isfinite(l)) fl |= 1u;
+    const int32_t x = p.tokens[static_cast<size_t>(b) * p.gamma + k - 1];
+    const double pt = exp(static_cast<double>(p.target[static_cast<size_t>(row) * p.V + x]) - l);
+    const double u = static_cast<double>(p.uniforms[(static_cast<size_t>(b) * (p.gamma + 1) + k - 1) * 3 + 1]);
+    const double qk = static_cast<double>(p.q[static_cast<size_t>(b) * p.gamma + k - 1]);
+    if (u * qk < pt) {
+      ++accepted;
+    } else {
+      kind = kEmitResidual;
+      epos = k;
+      erow = row;
+      else_ = l;
+      rejected = true;
+      break;
+    }
+  }
+  if (!rejected) {
+    else_ = row_lse_wave(p, erow, lane);
+    if (!isfinite(else_)) fl |= 1u;
+  }
+  if (lane == 0) {
+    p.accept_len[b] = accepted;
+    p.ws.ekind[b] = kind;
+    p.ws.epos[b] = epos;
+    p.ws.erow[b] = erow;
+    p.ws.erow_lse[b] = else_;
+    p.ws.eflags[b] = fl;
+  }
+}
+
+// Previous token of emission position j (1-based): the anchor for j = 1.
+__device__ __forceinline__ int32_t emit_prev(const VerifyArgs& p, int b, int j) {
+  return (j == 1) ? p.anchor[b] : p.tokens[static_cast<size_t>(b) * p.gamma + j - 2];
+}
+
+// Residual weight and overlap of one token: w = max(0, p_t - p_d), o = min(p_t, p_d), with
+// NaN behaving as in the comparisons written here (a NaN difference gives w = 0).
+__device__ __forceinline__ void residual_pair(float L, float t, double lse_d, double lse_t,
+                                              double& w, double& o) {
+  const double pd = exp(static_cast<double>(L) - lse_d);
+  const double pt = exp(static_cast<double>(t) - lse_t);
+  const double d = pt - pd;
+  w = (0.0 < d) ? d : 0.0;
+  o = (pd < pt) ? pd : pt;
+}
+
+template <int KS>
+__global__ __launch_bounds__(kBlock, 2) void residual_partials_kernel(VerifyArgs p) {
+  using C = StepCfg<KS>;
+  constexpr int r = C::kR;
+  __shared__ __attribute__((aligned(16))) uint16_t E[C::kBG * C::kLdsRow];
+  __shared__ int list[C::kBG];
+  __shared__ int red_i[kBlock / 64];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, col = lane & 31;
+  const int tok0 = blockIdx.x * (4 * kTileTokens) + wave * kTileTokens;
+  const bool active = tok0 < p.V;
+  const bool vec4 = (p.V & 3) == 0;
+
+  // Residual requests in request order: contiguous request ranges per thread + block scan.
+  const int per = (p.B + kBlock - 1) / kBlock;
+  const int b0 = min(p.B, tid * per), b1 = min(p.B, b0 + per);
+  int cnt = 0;
+  for (int b = b0; b < b1; ++b) cnt += (p.ws.ekind[b] == kEmitResidual) ? 1 : 0;
+  int nres;
+  const int first = block_exclusive_scan_int<kBlock>(cnt, red_i, &nres);
+  if (nres == 0) return;
+
+  u16x8_t a[KS];
+  load_w2_tile<KS>(a, p.W2t, tok0 + col, p.V, half);
+
+  for (int g0 = 0; g0 < nres; g0 += C::kBG) {
+    const int nb = min(C::kBG, nres - g0);
+    int rank = first;
+    for (int b = b0; b < b1; ++b) {
+      if (p.ws.ekind[b] == kEmitResidual) {
+        if (rank >= g0 && rank < g0 + C::kBG) list[rank - g0] = b;
+        ++rank;
+      }
+    }
+    __syncthreads();
+    constexpr int kChunks = r / 8;
+    for (int c = tid; c < C::kBG * kChunks; c += kBlock) {
+      const int i = c / kChunks, q = c % kChunks;
+      u16x8_t v = zero_u16x8();
+      if (i < nb) {
+        const int b = list[i];
+        const int32_t prevtok = emit_prev(p, b, p.ws.epos[b]);
+        v = load_u16x8(p.W1 + static_cast<size_t>(prevtok) * r + q * 8);
+      }
+      *reinterpret_cast<u16x8_t*>(&E[i * C::kLdsRow + q * 8]) = v;
+    }
+    __syncthreads();
+    if (active) {
+      for (int nt = 0; nt * 32 < nb; ++nt) {
+        const uint16_t* erow = &E[(nt * 32 + col) * C::kLdsRow + 8 * half];
+        f32x16_t acc = {};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) acc = mfma_32x32x16(a[s], load_u16x8(erow + 16 * s), acc);
+        const int i = nt * 32 + col;
+        if (i < nb) {
+          const int b = list[i];
+          const int j = p.ws.epos[b];
+          const float* Urow = p.U + (static_cast<size_t>(b) * p.gamma + j - 1) * p.V;
+          const float* trow = p.target + static_cast<size_t>(p.ws.erow[b]) * p.V;
+          const double lse_d = p.lse[static_cast<size_t>(b) * p.gamma + j - 1];
+          const double lse_t = p.ws.erow_lse[b];
+          float L[16];
+          tile_logits(acc, Urow, tok0, p.V, half, vec4, L);
+          double W = 0.0, O = 0.0;
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int v = tok0 + 8 * g + 4 * half;
+            float t[4];
+            load4(trow, v, p.V, vec4, t);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              if (v + e < p.V) {
+                double w, o;
+                residual_pair(L[4 * g + e], t[e], lse_d, lse_t, w, o);
+                W += w;
+                O += o;
+              }
+            }
+          }
+          W = W + __shfl_xor(W, 32, kWave);
+          O = O + __shfl_xor(O, 32, kWave);
+          if (half == 0) {
+            const size_t o = static_cast<size_t>(b) * p.ntiles + tok0 / kTileTokens;
+            p.ws.rsum[o] = W;
+            p.ws.rmin[o] = O;
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <int KS>
+__global__ __launch_bounds__(kBlock) void emit_sample_kernel(VerifyArgs p) {
+  __shared__ double red_d[kBlock / 64];
+  __shared__ float red_f[kBlock / 64];
+  __shared__ int red_i[kBlock / 64];
+  __shared__ Located loc;
+  __shared__ float Ls[kTileTokens];
+  __shared__ int s_tok;
+
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int kind = p.ws.ekind[b];
+  const int j = p.ws.epos[b];
+  const int erow = p.ws.erow[b];
+  uint32_t fl = p.ws.eflags[b];
+  const double u = static_cast<double>(p.uniforms[(static_cast<size_t>(b) * (p.gamma + 1) + j - 1) * 3 + 2]);
+  const float* trow = p.target + static_cast<size_t>(erow) * p.V;
+  bool from_target = (kind == kEmitBonus);
+  int token = 0;
+
+  if (kind == kEmitResidual) {
+    const size_t base = static_cast<size_t>(b) * p.ntiles;
+    double o = 0.0;
+    for (int c = tid; c < p.ntiles; c += kBlock) o += p.ws.rmin[base + c];
+    o = block_sum<kBlock>(o, red_d);
+    if (tid == 0 && p.beta_emit) p.beta_emit[b] = static_cast<float>(o);
+    auto mass = [&](int c) { return p.ws.rsum[base + c]; };
+    const Located L = locate_chunk<kBlock>(p.ntiles, u, mass, red_d, red_i, &loc);
+    if (L.chunk < 0) {
+      fl |= 2u;
+      from_target = true;
+    } else {
+      const int tok0 = L.chunk * kTileTokens;
+      const float* Urow = p.U + (static_cast<size_t>(b) * p.gamma + j - 1) * p.V;
+      if (tid < 64) recompute_tile<KS>(p.W1, p.W2t, Urow, emit_prev(p, b, j), tok0, p.V, Ls);
+      __syncthreads();
+      if (tid == 0) {
+        const double lse_d = p.lse[static_cast<size_t>(b) * p.gamma + j - 1];
+        const double lse_t = p.ws.erow_lse[b];
+        double cum = L.before;
+        int found = -1, last = -1;
+        for (int m = 0; m < kTileTokens && tok0 + m < p.V; ++m) {
+          double w, ov;
+          residual_pair(Ls[m], trow[tok0 + m], lse_d, lse_t, w, ov);
+          if (w > 0.0) last = m;
+          if (!L.take_last) {
+            cum += w;
+            if (cum > L.target) {
+              found = m;
+              break;
+            }
+          }
+        }
+        s_tok = tok0 + (found >= 0 ? found : (last >= 0 ? last : 0));
+      }
+      __syncthreads();
+      token = s_tok;
+    }
+  } else if (tid == 0 && p.beta_emit) {
+    p.beta_emit[b] = -1.0f;
+  }
+
+  if (from_target) {
+    // Draw from p_t of the emission row: segment, then the token inside it.
+    const size_t base = static_cast<size_t>(erow) * p.nseg;
+    float m = kNegInf;
+    for (int s = tid; s < p.nseg; s += kBlock) m = fmaxf(m, p.ws.seg_max[base + s]);
+    const float M = block_max<kBlock>(m, red_f);
+    auto smass = [&](int s) { return partial_mass(p.ws.seg_max[base + s], p.ws.seg_sum[base + s], M); };
+    const Located S = locate_chunk<kBlock>(p.nseg, u, smass, red_d, red_i, &loc);
+    if (S.chunk < 0) {
+      token = 0;
+    } else {
+      const int t0 = S.chunk * kSegTokens;
+      const int n = min(kSegTokens, p.V - t0);
+      const float sm = p.ws.seg_max[base + S.chunk];
+      const double f = exp(static_cast<double>(sm) - static_cast<double>(M));
+      const double tgt = S.take_last ? __builtin_inf() : (S.target - S.before) / f;
+      auto tmass = [&](int c) { return static_cast<double>(exp_term(trow[t0 + c] - sm)); };
+      const Located T = locate_chunk_t<kBlock>(n, [tgt](double) { return tgt; }, tmass, red_d,
+                                               red_i, &loc);
+      token = t0 + (T.chunk >= 0 ? T.chunk : 0);
+    }
+  }
+  if (tid == 0) {
+    p.next_token[b] = token;
+    if (p.flags) p.flags[b] = fl;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_target_stats(const VerifyArgs& a, hipStream_t s) {
+  const int max_rows = a.B * (a.gamma + 1);
+  hipLaunchKernelGGL(target_stats_kernel, dim3(a.nseg, max_rows), dim3(kBlock), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_accept(const VerifyArgs& a, hipStream_t s) {
+  const int grid = (a.B + (kBlock / 64) - 1) / (kBlock / 64);
+  hipLaunchKernelGGL(accept_kernel, dim3(grid), dim3(kBlock), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int KS>
+static hipError_t launch_resid_ks(const VerifyArgs& a, hipStream_t s) {
+  const int grid = (a.V + 4 * kTileTokens - 1) / (4 * kTileTokens);
+  hipLaunchKernelGGL(residual_partials_kernel<KS>, dim3(grid), dim3(kBlock), 0, s, a);
+  return hipGetLastError();
+}
+template <int KS>
+static hipError_t launch_emit_ks(const VerifyArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(emit_sample_kernel<KS>, dim3(a.B), dim3(kBlock), 0, s, a);
+  return hipGetLastError();
+}
+
+#define DSPARK_DISPATCH_KS(r, fn, ...)             \
+  switch (r) {                                     \
+    case 16: return fn<1>(__VA_ARGS__);            \
+    case 32: return fn<2>(__VA_ARGS__);            \
+    case 64: return fn<4>(__VA_ARGS__);            \
+    case 128: return fn<8>(__VA_ARGS__);           \
+    case 256: return fn<16>(__VA_ARGS__);          \
+    case 512: return fn<32>(__VA_ARGS__);          \
+    default: return hipErrorInvalidValue;          \
+  }
+
+hipError_t launch_residual_partials(const VerifyArgs& a, hipStream_t s) {
+  DSPARK_DISPATCH_KS(a.r, launch_resid_ks, a, s)
+}
+hipError_t launch_emit_sample(const VerifyArgs& a, hipStream_t s) {
+  DSPARK_DISPATCH_KS(a.r, launch_emit_ks, a, s)
+}
+
+}  // namespace dspark

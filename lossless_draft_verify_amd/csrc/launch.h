@@ -1,0 +1,103 @@
+// Kernel argument blocks and launchers (internal to libdspark.so).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dspark {
+
+// One draft step k: L = U[:, k] + W1[prev] . W2 -> per-tile partials.
+struct StepArgs {
+  int B, V, gamma, k, ntiles;
+  const float* U;
+  const uint16_t* W1;
+  const uint16_t* W2t;
+  const int32_t* prev;  // conditioning token of request b at prev[b * prev_stride]
+  int prev_stride;
+  float* pmax;          // [B][ntiles] tile max
+  float* psum;          // [B][ntiles] sum exp(L - tile max)
+  float* dbg;           // nullable [B][gamma][V]
+};
+
+struct SampleArgs {
+  int B, V, gamma, k, ntiles;
+  const float* U;
+  const uint16_t* W1;
+  const uint16_t* W2t;
+  const int32_t* prev;
+  int prev_stride;
+  const float* pmax;
+  const float* psum;
+  const float* uniforms;
+  const int32_t* force;  // nullable [B][gamma]
+  int32_t* tokens;
+  float* q;
+  double* lse;
+};
+
+struct ConfArgs {
+  int B, gamma, r, d;
+  const uint16_t* h;
+  const uint16_t* W1;
+  const uint16_t* w;
+  const float* T;
+  const int32_t* anchor;
+  const int32_t* tokens;
+  float* conf;
+};
+
+struct PlanArgs {
+  int B, gamma, sps_len, mode, round_index;
+  const float* conf;   // nullable for FULL_VERIFY
+  const double* sps;
+  float* ring;         // nullable unless LAGGED_TOPK
+  int32_t* draft_len;
+  int32_t* row_offsets;
+  double* stats;       // nullable
+};
+
+// Emission kinds written by the accept scan.
+enum : int32_t { kEmitBonus = 0, kEmitResidual = 1 };
+
+struct VerifyWs {
+  float* seg_max;    // [B*(gamma+1)][nseg]
+  double* seg_sum;   // [B*(gamma+1)][nseg]
+  int32_t* ekind;    // [B]
+  int32_t* epos;     // [B] 1-based position of the emission
+  int32_t* erow;     // [B] packed target row of the emission
+  double* erow_lse;  // [B] log-sum-exp of that target row
+  uint32_t* eflags;  // [B]
+  double* rsum;      // [B][ntiles] residual mass per 32-token tile
+  double* rmin;      // [B][ntiles] sum of min(p_t, p_d) per tile
+};
+
+struct VerifyArgs {
+  int B, V, gamma, r, ntiles, nseg;
+  const float* target;
+  const int32_t* row_offsets;
+  const int32_t* draft_len;
+  const float* U;
+  const uint16_t* W1;
+  const uint16_t* W2t;
+  const int32_t* anchor;
+  const int32_t* tokens;
+  const float* q;
+  const double* lse;
+  const float* uniforms;
+  int32_t* accept_len;
+  int32_t* next_token;
+  float* beta_emit;   // nullable
+  uint32_t* flags;    // nullable
+  VerifyWs ws;
+};
+
+hipError_t launch_markov_step(const StepArgs& a, int r, hipStream_t s);
+hipError_t launch_draft_sample(const SampleArgs& a, int r, hipStream_t s);
+hipError_t launch_confidence(const ConfArgs& a, hipStream_t s);
+hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
+hipError_t launch_target_stats(const VerifyArgs& a, hipStream_t s);
+hipError_t launch_accept(const VerifyArgs& a, hipStream_t s);
+hipError_t launch_residual_partials(const VerifyArgs& a, hipStream_t s);
+hipError_t launch_emit_sample(const VerifyArgs& a, hipStream_t s);
+
+}  // namespace dspark

@@ -1,0 +1,104 @@
+// MFMA tile helpers shared by the draft step, the draft sampler and the residual kernels. All
+// of them form a token tile's logits with the same instruction sequence, so a sampler that
+// recomputes one tile reproduces the streaming pass bit for bit.
+#pragma once
+
+#include "device.h"
+
+namespace dspark {
+
+// E rows in LDS are padded by 8 bf16 so the 32 rows a wave reads with one ds_read_b128 spread
+// over the LDS banks.
+template <int KS>
+struct StepCfg {
+  static constexpr int kR = KS * 16;
+  static constexpr int kBG = (kR <= 256) ? 128 : 64;   // requests per LDS fill
+  static constexpr int kLdsRow = kR + 8;
+};
+
+template <int KS>
+__device__ __forceinline__ void load_w2_tile(u16x8_t (&a)[KS], const uint16_t* __restrict__ W2t,
+                                             int tok, int V, int half) {
+  constexpr int r = KS * 16;
+  if (tok < V) {
+    const uint16_t* p = W2t + static_cast<size_t>(tok) * r + 8 * half;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) a[s] = load_u16x8(p + 16 * s);
+  } else {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) a[s] = zero_u16x8();
+  }
+}
+
+// Load four consecutive fp32 values v..v+3 of a row (those >= V read as 0).
+__device__ __forceinline__ void load4(const float* __restrict__ row, int v, int V, bool vec4,
+                                      float (&o)[4]) {
+  if (vec4 && v + 3 < V) {
+    const float4 t = *reinterpret_cast<const float4*>(row + v);
+    o[0] = t.x;
+    o[1] = t.y;
+    o[2] = t.z;
+    o[3] = t.w;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = (v + i < V) ? row[v + i] : 0.0f;
+  }
+}
+
+// Logits of the 16 accumulator slots a lane holds: L = U + bias (fp32 add), -inf past V.
+__device__ __forceinline__ void tile_logits(const f32x16_t& acc, const float* __restrict__ Urow,
+                                            int tok0, int V, int half, bool vec4, float (&L)[16]) {
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int v = tok0 + 8 * g + 4 * half;
+    float u[4];
+    load4(Urow, v, V, vec4, u);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) L[4 * g + i] = (v + i < V) ? (u[i] + acc[4 * g + i]) : kNegInf;
+  }
+}
+
+// exp(L - m) of the 16 slots, 0 where the tile max is -inf.
+__device__ __forceinline__ void tile_terms(const float (&L)[16], float m, float (&t)[16]) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j) t[j] = (m == kNegInf) ? 0.0f : exp_term(L[j] - m);
+}
+
+__device__ __forceinline__ float sum16(const float (&t)[16]) {
+  const float a = ((t[0] + t[1]) + (t[2] + t[3])) + ((t[4] + t[5]) + (t[6] + t[7]));
+  const float b = ((t[8] + t[9]) + (t[10] + t[11])) + ((t[12] + t[13]) + (t[14] + t[15]));
+  return a + b;
+}
+
+__device__ __forceinline__ float max16(const float (&L)[16]) {
+  float m = L[0];
+#pragma unroll
+  for (int j = 1; j < 16; ++j) m = fmaxf(m, L[j]);
+  return m;
+}
+
+// Recompute the logits of one 32-token tile for one request with exactly the instruction
+// sequence of markov_step_kernel (same k order, same operands; the request sits in every MFMA
+// column, and column placement does not change the result). Called by a whole wave; lanes 0
+// and 32 hold the 32 logits, which are written to Ls[0..32).
+template <int KS>
+__device__ void recompute_tile(const uint16_t* __restrict__ W1, const uint16_t* __restrict__ W2t,
+                               const float* __restrict__ Urow, int32_t prevtok, int tok0, int V,
+                               float* Ls) {
+  constexpr int r = KS * 16;
+  const int lane = threadIdx.x & 63, half = lane >> 5, col = lane & 31;
+  u16x8_t a[KS];
+  load_w2_tile<KS>(a, W2t, tok0 + col, V, half);
+  const uint16_t* erow = W1 + static_cast<size_t>(prevtok) * r + 8 * half;
+  f32x16_t acc = {};
+#pragma unroll
+  for (int s = 0; s < KS; ++s) acc = mfma_32x32x16(a[s], load_u16x8(erow + 16 * s), acc);
+  if (col == 0) {
+    float L[16];
+    tile_logits(acc, Urow, tok0, V, half, (V & 3) == 0, L);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) Ls[tile_token(j, half)] = L[j];
+  }
+}
+
+}  // namespace dspark

@@ -130,7 +130,7 @@ def temperatures(wl: Workload) -> torch.Tensor:
 
 
 def round_inputs(wl: Workload, round_index: int = 0, device="cpu",
-                 with_hidden: Optional[bool] = None) -> Dict[str, torch.Tensor]:
+                 with_hidden: Optional[bool] = None, with_noise: bool = True) -> Dict[str, torch.Tensor]:
     """Per-round tensors: anchor [B], U [B][g][V], U_bonus [B][V], uniforms [B][g+1][3],
     noise [B][g+1][V] (target noise, std per position), and h [B][g][d] when with_hidden."""
     B, g, V = wl.B, wl.gamma, wl.V
@@ -149,11 +149,12 @@ def round_inputs(wl: Workload, round_index: int = 0, device="cpu",
     kk = torch.randint(0, 1 << 24, (B, g + 1, 3), generator=_gen(wl, round_index, _T_UNIF, device),
                        device=device, dtype=torch.int64)
     uniforms = kk.to(torch.float32) * (2.0 ** -24)
-    std = torch.tensor([wl.noise_std(k) for k in range(1, g + 2)], dtype=torch.float32,
-                       device=device).view(1, g + 1, 1)
-    noise = torch.randn((B, g + 1, V), generator=_gen(wl, round_index, _T_NOISE, device),
-                        device=device, dtype=torch.float32) * std
-    out = dict(anchor=anchor, U=U, U_bonus=U_bonus, uniforms=uniforms, noise=noise)
+    out = dict(anchor=anchor, U=U, U_bonus=U_bonus, uniforms=uniforms)
+    if with_noise:
+        std = torch.tensor([wl.noise_std(k) for k in range(1, g + 2)], dtype=torch.float32,
+                           device=device).view(1, g + 1, 1)
+        out["noise"] = torch.randn((B, g + 1, V), generator=_gen(wl, round_index, _T_NOISE, device),
+                                   device=device, dtype=torch.float32) * std
     if with_hidden is None:
         with_hidden = wl.mode != FULL_VERIFY
     if with_hidden:

@@ -1,0 +1,299 @@
+"""GPU <-> oracle parity through the C ABI, per entry point and for whole rounds.
+
+Inputs come from the seeded generators only; the oracle never receives anything the GPU
+computed (GPU calls are fed oracle tokens / plans where a step needs the previous step's
+output)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import lossless_draft_verify_amd as L
+from lossless_draft_verify_amd import workloads as W
+from parity import (LSE_TOL, PLAN_TIE, PROB_TOL, MismatchCounter, bits, compare_draft, dims_of,
+                    gpu_draft, log, np_, oracle_draft)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    if not torch.cuda.is_available():
+        pytest.skip("needs the GPU")
+    L.load_library()
+
+
+def _custom(name, **kw):
+    base = W.WORKLOADS["tiny-b4-v1000-g3"]
+    return W.scaled(base, name=name, **kw)
+
+
+DRAFT_CASES = {
+    "tiny-b4-v1000-g3": W.WORKLOADS["tiny-b4-v1000-g3"],
+    "b32-v32000-g7": W.WORKLOADS["b32-v32000-g7"],
+    # two request groups (130 > 128), ragged 32-request tile, V % 4 != 0 (scalar path), tail tile
+    "b130-v4099-r256-g3": _custom("b130-v4099-r256-g3", seed_id=11, B=130, V=4099, r=256, d=64,
+                                  u_std=3.0, w_std=0.05),
+    "b33-v2051-r64-g4": _custom("b33-v2051-r64-g4", seed_id=12, B=33, V=2051, r=64, gamma=4),
+    "b7-v3000-r512-g2": _custom("b7-v3000-r512-g2", seed_id=13, B=7, V=3000, r=512, gamma=2,
+                                w_std=0.03),
+    "b5-v2-r16-g3": _custom("b5-v2-r16-g3", seed_id=14, B=5, V=2, r=16, gamma=3),
+}
+
+
+@pytest.mark.parametrize("name", list(DRAFT_CASES))
+def test_draft_parity(name):
+    wl = DRAFT_CASES[name]
+    log(f"[draft] {name}")
+    wts = W.weights(wl, DEV)
+    inp = W.round_inputs(wl, 0, DEV, with_hidden=False, with_noise=False)
+    o = oracle_draft(inp, wts, want_logits=True)
+    g = gpu_draft(wl, inp, wts, force=o["tokens"], dbg=True)
+    c = MismatchCounter(f"draft {name}")
+    err = compare_draft(g, o, c)
+    log(f"  logits max err {err:.2e}; {c.report()}")
+    # unforced GPU run: identical to the forced one wherever the draws agree
+    gu = gpu_draft(wl, inp, wts)
+    same = (gu["tokens"] == o["tokens"]).all(axis=1)
+    assert np.array_equal(gu["q"][same], g["q"][same])
+    c.check_rate()
+
+
+def test_draft_logits_recompute_is_bit_exact():
+    """The sampler recomputes one tile with the streaming pass's instruction sequence: forced
+    q must equal exp(L - lse) from the debug logits exactly as recomputed in fp64 here."""
+    wl = DRAFT_CASES["b130-v4099-r256-g3"]
+    wts = W.weights(wl, DEV)
+    inp = W.round_inputs(wl, 0, DEV, with_hidden=False, with_noise=False)
+    g = gpu_draft(wl, inp, wts, dbg=True)
+    Lg = np_(g["logits"]).astype(np.float64)
+    x = g["tokens"]
+    ref = np.exp(np.take_along_axis(Lg, x[..., None], 2)[..., 0] - g["lse"]).astype(np.float32)
+    assert np.array_equal(ref, g["q"])
+
+
+def test_draft_mismatch_rate_headline_vocab():
+    """2 x 10^4 draws at V = 129280 (r = 16 keeps the oracle fast): every mismatch must be a
+    flagged near tie and mismatches must stay under 0.1 % of draws."""
+    wl = W.scaled(W.WORKLOADS["b128-v129280-g5"], name="rate", seed_id=21, B=1024, r=16, d=64,
+                  w_std=0.1)
+    c = MismatchCounter("draft rate V=129280")
+    wts = W.weights(wl, DEV)
+    for rnd in range(4):
+        inp = W.round_inputs(wl, rnd, DEV, with_hidden=False, with_noise=False)
+        o = oracle_draft(inp, wts)
+        g = gpu_draft(wl, inp, wts, force=o["tokens"])
+        compare_draft(g, o, c, logits=False)
+        log(f"  round {rnd}: {c.report()}")
+        del inp
+        torch.cuda.empty_cache()
+    c.check_rate()
+
+
+@pytest.mark.parametrize("name", ["tiny-b4-v1000-g3", "b128-v129280-g5"])
+def test_confidence_parity(name):
+    wl = W.WORKLOADS[name]
+    log(f"[confidence] {name}")
+    wts = W.weights(wl, DEV)
+    inp = W.round_inputs(wl, 0, DEV, with_hidden=True)
+    tokens = torch.randint(0, wl.V, (wl.B, wl.gamma), dtype=torch.int32, device=DEV)
+    T = W.temperatures(wl).to(DEV)
+    o = oracle.confidence(bits(inp["h"]), bits(wts["W1"]), bits(wts["w"]), np_(T), np_(inp["anchor"]),
+                          np_(tokens))
+    c = L.confidence(dims_of(wl), inp["h"], wts["W1"], wts["w"], T, inp["anchor"], tokens)
+    err = np.abs(np_(c) - o["conf"]).max()
+    log(f"  conf max err {err:.2e}")
+    assert err <= PROB_TOL
+
+
+def _plan_case(B, g, sps, seed):
+    gen = torch.Generator().manual_seed(seed)
+    conf = torch.rand((B, g), generator=gen, dtype=torch.float32)
+    kind = seed % 4
+    if kind == 1:
+        conf[torch.rand((B, g), generator=gen) < 0.3] = 1.0
+    elif kind == 2:
+        conf = torch.round(conf * 4) / 4
+    elif kind == 3:
+        conf = 0.5 + 0.5 * conf
+    return conf
+
+
+@pytest.mark.parametrize("B,g,scale,seed", [(4, 3, 0.0, 1), (128, 5, 768.0, 2), (128, 5, 768.0, 3),
+                                            (512, 5, 512.0, 4), (512, 5, 512.0, 5), (37, 7, 30.0, 6),
+                                            (1, 2, 2.0, 7), (1024, 8, 2000.0, 8)])
+def test_plan_parity(B, g, scale, seed):
+    n = B * (g + 1) + 1
+    sps = np.ones(n) if scale == 0 else 1.0 / (1.0 + np.arange(n) / scale)
+    sps_t = torch.tensor(sps, dtype=torch.float64, device=DEV)
+    d = L.Dims(B, g, 8, 16)
+    for mode in (L.FULL_VERIFY, L.EARLY_STOP, L.FULL_PATH):
+        conf = _plan_case(B, g, sps, seed)
+        o = oracle.plan(conf.numpy(), sps, mode)
+        dl, ro, st = L.plan(d, conf.to(DEV), sps_t, mode)
+        if o["margin"] > PLAN_TIE:
+            assert np.array_equal(np_(dl), o["draft_len"]), (mode, np_(dl), o["draft_len"])
+            assert np.array_equal(np_(ro), o["row_offsets"])
+            assert np.allclose(np_(st), o["stats"], rtol=1e-12, atol=0)
+        else:
+            log(f"  flagged planner tie (margin {o['margin']:.1e}), mode {mode}")
+    # lagged capacity over rounds with the device ring
+    ring_o = np.zeros((2, B, g), np.float32)
+    ring_g = torch.zeros((2, B, g), dtype=torch.float32, device=DEV)
+    for t in range(5):
+        conf = _plan_case(B, g, sps, 100 * seed + t)
+        o = oracle.plan(conf.numpy(), sps, L.LAGGED_TOPK, ring=ring_o, round_index=t)
+        dl, ro, st = L.plan(d, conf.to(DEV), sps_t, L.LAGGED_TOPK, ring=ring_g, round_index=t)
+        assert np.array_equal(np_(ring_g), ring_o)
+        if o["margin"] > PLAN_TIE:
+            assert np.array_equal(np_(dl), o["draft_len"]), t
+            assert np.array_equal(np_(ro), o["row_offsets"])
+            assert np.allclose(np_(st), o["stats"], rtol=1e-12, atol=0)
+
+
+def decisive_margin(ov, al_gpu, gamma):
+    """Margin of the accept test that separates the two accept lengths (the first position
+    where the GPU and the oracle could disagree)."""
+    k = np.minimum(np.minimum(al_gpu, ov["accept_len"]), gamma - 1)
+    return ov["accept_margin"][np.arange(len(k)), k]
+
+
+def _oracle_round(wl, inp, wts, mode, conf=None):
+    """Oracle draft (with logits) + plan + target rows; returns everything the round needs."""
+    o = oracle_draft(inp, wts, want_logits=True)
+    if conf is None and mode != W.FULL_VERIFY:
+        T = W.temperatures(wl).numpy()
+        conf = oracle.confidence(bits(inp["h"]), bits(wts["W1"]), bits(wts["w"]), T,
+                                 np_(inp["anchor"]), o["tokens"])["conf"]
+    sps = W.sps_table(wl)
+    if mode == W.FULL_VERIFY and conf is None:
+        p = oracle.plan(None, sps, mode, B=wl.B, gamma=wl.gamma)
+    else:
+        p = oracle.plan(conf, sps, mode)
+    dense = np.concatenate([o["logits"], np_(inp["U_bonus"])[:, None, :]], 1) + np_(inp["noise"])
+    keep = np.arange(wl.gamma + 1)[None, :] <= p["draft_len"][:, None]
+    target = np.ascontiguousarray(dense[keep], dtype=np.float32)
+    return o, conf, p, target
+
+
+VERIFY_CASES = ["tiny-b4-v1000-g3", "b32-v32000-g7", "b130-v4099-r256-g3", "b33-v2051-r64-g4",
+                "b5-v2-r16-g3"]
+
+
+@pytest.mark.parametrize("name", VERIFY_CASES)
+def test_verify_parity(name):
+    wl = DRAFT_CASES.get(name) or W.WORKLOADS[name]
+    log(f"[verify] {name}")
+    wts = W.weights(wl, DEV)
+    inp = W.round_inputs(wl, 0, DEV, with_hidden=False)
+    # ragged verify lengths from a random confidence under a steep SPS
+    rng = np.random.default_rng(wl.seed_id)
+    conf = rng.uniform(0.3, 1.0, (wl.B, wl.gamma)).astype(np.float32)
+    wl_p = W.scaled(wl, sps_kind="hyperbolic", sps_scale=max(1.0, wl.B * 1.5))
+    o, conf, p, target = _oracle_round(wl_p, inp, wts, W.EARLY_STOP, conf=conf)
+    ov = oracle.verify(target, p["row_offsets"], p["draft_len"], np_(inp["U"]), bits(wts["W1"]),
+                       bits(wts["W2t"]), np_(inp["anchor"]), o["tokens"], o["q"], np_(inp["uniforms"]))
+    g = gpu_draft(wl, inp, wts, force=o["tokens"])
+    d = dims_of(wl)
+    T = lambda a, dt=torch.int32: torch.as_tensor(np.ascontiguousarray(a), dtype=dt, device=DEV)
+    al, nt, be, fl = L.verify(d, T(target, torch.float32), T(p["row_offsets"]), T(p["draft_len"]),
+                              inp["U"], wts["W1"], wts["W2t"], inp["anchor"], T(o["tokens"]),
+                              T(o["q"], torch.float32), g["lse_t"], inp["uniforms"])
+    torch.cuda.synchronize()
+    al, nt, be, fl = np_(al), np_(nt), np_(be), np_(fl)
+    acc = MismatchCounter(f"accept {name}")
+    acc.add(al, ov["accept_len"], decisive_margin(ov, al, wl.gamma))
+    same = al == ov["accept_len"]
+    emit = MismatchCounter(f"emit {name}")
+    emit.add(nt[same], ov["next_token"][same], ov["emit_margin"][same])
+    assert np.array_equal(fl[same].astype(np.uint32), ov["flags"][same])
+    assert np.abs(be[same] - ov["beta_emit"][same]).max() <= PROB_TOL
+    log(f"  {acc.report()}; {emit.report()}; residual rows {int((ov['beta_emit'] >= 0).sum())}")
+
+
+@pytest.mark.parametrize("name", ["b128-v129280-g5", "b32-v32000-g7", "b128-v151936-g15"])
+def test_round_full_size(name):
+    """A whole round at the workload's full size, every request checked against the oracle."""
+    wl = W.WORKLOADS[name]
+    log(f"[round] {name}: generating")
+    wts = W.weights(wl, DEV)
+    inp = W.round_inputs(wl, 0, DEV)
+    d = dims_of(wl)
+    log("  oracle round")
+    o, conf_o, p, target = _oracle_round(wl, inp, wts, wl.mode)
+    ov = oracle.verify(target, p["row_offsets"], p["draft_len"], np_(inp["U"]), bits(wts["W1"]),
+                       bits(wts["W2t"]), np_(inp["anchor"]), o["tokens"], o["q"], np_(inp["uniforms"]))
+    log("  gpu round")
+    gu = gpu_draft(wl, inp, wts)                          # the GPU's own draws
+    c = MismatchCounter(f"round draft {name}")
+    c.add(gu["tokens"][:, :1], o["tokens"][:, :1], o["margin"][:, :1])
+    g = gpu_draft(wl, inp, wts, force=o["tokens"], dbg=True)
+    err = compare_draft(g, o, c)
+    log(f"  draft: logits err {err:.2e}; {c.report()}")
+    T = lambda a, dt=torch.int32: torch.as_tensor(np.ascontiguousarray(a), dtype=dt, device=DEV)
+    tok_o = T(o["tokens"])
+    if wl.mode != W.FULL_VERIFY:
+        Tt = W.temperatures(wl).to(DEV)
+        cg = L.confidence(d, inp["h"], wts["W1"], wts["w"], Tt, inp["anchor"], tok_o)
+        assert np.abs(np_(cg) - conf_o).max() <= PROB_TOL
+        # plan on the oracle's confidences (the GPU's agree within 1e-6 but a plan input must be
+        # identical on both sides for an exact comparison)
+        dl, ro, st = L.plan(d, T(conf_o, torch.float32), T(W.sps_table(wl), torch.float64), wl.mode)
+    else:
+        dl, ro, st = L.plan(d, None, T(W.sps_table(wl), torch.float64), wl.mode)
+    if p["margin"] > PLAN_TIE:
+        assert np.array_equal(np_(dl), p["draft_len"])
+        assert np.array_equal(np_(ro), p["row_offsets"])
+    log(f"  plan: B_tot {p['stats'][0]:.0f}, tau {p['stats'][1]:.2f}")
+    al, nt, be, fl = L.verify(d, T(target, torch.float32), ro, dl, inp["U"], wts["W1"], wts["W2t"],
+                              inp["anchor"], tok_o, T(o["q"], torch.float32), g["lse_t"],
+                              inp["uniforms"])
+    torch.cuda.synchronize()
+    al, nt, be = np_(al), np_(nt), np_(be)
+    acc = MismatchCounter("accept")
+    acc.add(al, ov["accept_len"], decisive_margin(ov, al, wl.gamma))
+    same = al == ov["accept_len"]
+    emit = MismatchCounter("emit")
+    emit.add(nt[same], ov["next_token"][same], ov["emit_margin"][same])
+    assert np.abs(be[same] - ov["beta_emit"][same]).max() <= PROB_TOL
+    log(f"  verify: mean accepted {al.mean():.2f}; {acc.report()}; {emit.report()}")
+
+
+def test_determinism_bitwise():
+    wl = W.WORKLOADS["b32-v32000-g7"]
+    wts = W.weights(wl, DEV)
+    inp = W.round_inputs(wl, 0, DEV, with_hidden=False, with_noise=False)
+    a = gpu_draft(wl, inp, wts)
+    b = gpu_draft(wl, inp, wts)
+    for k in ("tokens", "q", "lse"):
+        assert np.array_equal(a[k], b[k])
+
+
+def test_nonfinite_flags_match_oracle():
+    wl = DRAFT_CASES["tiny-b4-v1000-g3"]
+    wts = W.weights(wl, DEV)
+    inp = W.round_inputs(wl, 0, DEV, with_hidden=False)
+    o = oracle_draft(inp, wts, want_logits=True)
+    B, g, V = wl.B, wl.gamma, wl.V
+    dense = np.concatenate([o["logits"], np_(inp["U_bonus"])[:, None, :]], 1) + np_(inp["noise"])
+    dense = np.ascontiguousarray(dense.reshape(-1, V), dtype=np.float32)
+    dense[0 * (g + 1) + 0, 5] = np.nan          # request 0: first verified row
+    dense[1 * (g + 1) + g, :] = -np.inf          # request 1: bonus row all -inf
+    offs = (np.arange(B + 1) * (g + 1)).astype(np.int32)
+    dl = np.full(B, g, np.int32)
+    ov = oracle.verify(dense, offs, dl, np_(inp["U"]), bits(wts["W1"]), bits(wts["W2t"]),
+                       np_(inp["anchor"]), o["tokens"], o["q"], np_(inp["uniforms"]))
+    gd = gpu_draft(wl, inp, wts, force=o["tokens"])
+    T = lambda a, dt=torch.int32: torch.as_tensor(np.ascontiguousarray(a), dtype=dt, device=DEV)
+    al, nt, be, fl = L.verify(dims_of(wl), T(dense, torch.float32), T(offs), T(dl), inp["U"],
+                              wts["W1"], wts["W2t"], inp["anchor"], T(o["tokens"]),
+                              T(o["q"], torch.float32), gd["lse_t"], inp["uniforms"])
+    torch.cuda.synchronize()
+    assert np_(fl)[0] & L.FLAG_NONFINITE and ov["flags"][0] & L.FLAG_NONFINITE
+    assert np.array_equal(np_(al)[:1], ov["accept_len"][:1])
+    assert np.array_equal(np_(nt)[:1], ov["next_token"][:1])
+    if ov["accept_len"][1] == g:
+        assert np_(fl)[1] & L.FLAG_NONFINITE and ov["flags"][1] & L.FLAG_NONFINITE
+        assert np_(nt)[1] == ov["next_token"][1] == 0

@@ -1,0 +1,97 @@
+"""Host-side checks of libdspark.so that need no GPU: every symbol the public header declares is
+exported, workspace sizing, and the synchronous argument checks (a bad argument returns its
+status before anything is enqueued)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import lossless_draft_verify_amd as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dspark.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.library_path()):
+        from lossless_draft_verify_amd import build
+        build.build()
+    return L.load_library()
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"DSPARK_API\s+[\w\s\*]+?\b(dspark_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_four_round_operations():
+    names = _declared()
+    for n in ("dspark_markov_draft", "dspark_confidence", "dspark_plan", "dspark_verify"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", L.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s(dspark_\w+)", out))
+    missing = [n for n in _declared() if n not in exported]
+    assert not missing, missing
+    for n in _declared():
+        getattr(lib, n)
+
+
+def test_workspace_sizes(lib):
+    d = L.Dims(128, 5, 129280, 256, 5120)
+    draft = L.workspace_bytes(d, L.OP_DRAFT)
+    assert draft >= 2 * 128 * (129280 // 32) * 4
+    assert L.workspace_bytes(d, L.OP_CONFIDENCE) == 0
+    assert L.workspace_bytes(d, L.OP_PLAN) == 0
+    assert L.workspace_bytes(d, L.OP_VERIFY) > 0
+    with pytest.raises(L.DsparkError):
+        L.workspace_bytes(L.Dims(128, 5, 129280, 100, 5120), L.OP_DRAFT)   # unsupported rank
+
+
+def _p(v=256):
+    return ctypes.c_void_p(v)
+
+
+def test_argument_checks_without_gpu(lib):
+    d = L.Dims(4, 3, 1000, 16, 64).c()
+    ws_ok = L.workspace_bytes(L.Dims(4, 3, 1000, 16, 64), L.OP_DRAFT)
+    P = _p()
+    # NULL
+    assert lib.dspark_markov_draft(d, None, P, P, P, P, P, P, P, None, None, P, ws_ok, None) == 1
+    # unsupported rank
+    bad = L.Dims(4, 3, 1000, 24, 64).c()
+    assert lib.dspark_markov_draft(bad, P, P, P, P, P, P, P, P, None, None, P, ws_ok, None) == 2
+    # misaligned U
+    assert lib.dspark_markov_draft(d, _p(260), P, P, P, P, P, P, P, None, None, P, ws_ok, None) == 3
+    # workspace too small
+    assert lib.dspark_markov_draft(d, P, P, P, P, P, P, P, P, None, None, P, ws_ok - 1, None) == 4
+    # SPS table too short, bad mode, lagged without ring
+    assert lib.dspark_plan(d, P, P, 4 * 4, 1, None, 0, P, P, None, None) == 5
+    assert lib.dspark_plan(d, P, P, 4 * 4 + 1, 9, None, 0, P, P, None, None) == 7
+    assert lib.dspark_plan(d, P, P, 4 * 4 + 1, 3, None, 0, P, P, None, None) == 7
+    assert lib.dspark_plan(d, None, P, 4 * 4 + 1, 1, None, 0, P, P, None, None) == 1
+    # planner size limit
+    big = L.Dims(2000, 5, 1000, 16, 64).c()
+    assert lib.dspark_plan(big, P, P, 2000 * 6 + 1, 1, None, 0, P, P, None, None) == 2
+    # confidence: d must be a positive multiple of 8
+    odd = L.Dims(4, 3, 1000, 16, 12).c()
+    assert lib.dspark_confidence(odd, P, P, P, P, P, P, P, None) == 2
+    # verify workspace
+    vws = L.workspace_bytes(L.Dims(4, 3, 1000, 16, 64), L.OP_VERIFY)
+    args = [P] * 13 + [None, None, P, vws - 1, None]
+    assert lib.dspark_verify(d, *args) == 4
+    assert lib.dspark_status_string(4) == b"workspace too small"
+
+
+def test_binding_refuses_host_tensors(lib):
+    import torch
+    d = L.Dims(4, 3, 1000, 16, 64)
+    with pytest.raises(L.DsparkError):
+        L.confidence(d, torch.zeros((4, 3, 64), dtype=torch.bfloat16), None, None, None, None, None,
+                     conf=torch.zeros((4, 3)))
