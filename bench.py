@@ -1,0 +1,254 @@
+"""Benchmark one DSpark draft-and-verify round on one MI355X.
+
+A step is one whole round (Markov draft of gamma positions, confidence head, planner, verify)
+over one batch of synthetic inputs already resident in HBM, for the headline workload
+b128-v129280-g5 (B = 128 requests, V = 129280, gamma = 5, r = 256, d = 5120, early-stop planner,
+SPS(n) = 1 / (1 + n / 768)). Three input sets rotate so the working set exceeds the 256 MB
+Infinity Cache. Target logits (the out-of-scope target model) are prepared before timing from
+each set's own draft logits plus noise, laid out in the planner's packed rows.
+
+Prints one JSON line (rank 0). Per-kernel durations come from HIP events recorded around every
+library launch on the launch stream during the timed region.
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import lossless_draft_verify_amd as L  # noqa: E402
+from lossless_draft_verify_amd import workloads as W  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+WORKLOAD = "b128-v129280-g5"
+METRIC = "spec rounds/s at B=128,V=129280,γ=5; achieved HBM GB/s vs peak"
+STEP_SOURCES = ["lossless_draft_verify_amd/csrc/kernels_draft.hip",
+                "lossless_draft_verify_amd/csrc/tiles.h",
+                "lossless_draft_verify_amd/csrc/device.h"]
+
+
+def step_source_sha():
+    h = hashlib.sha256()
+    for p in STEP_SOURCES:
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(launch_units):
+    """HBM bytes per markov_step launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", "markov_step_b128-v129280-g5_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"source_sha:\s*([0-9a-f]+)", text)
+    f = re.search(r"bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m or not f or m.group(1) != step_source_sha():
+        return None
+    return float(f.group(1))
+
+
+class InputSet:
+    def __init__(self, wl, wts, round_index, dev):
+        d = L.Dims(wl.B, wl.gamma, wl.V, wl.r, wl.d)
+        inp = W.round_inputs(wl, round_index, dev, with_hidden=True, with_noise=True)
+        self.anchor, self.U, self.h, self.uniforms = inp["anchor"], inp["U"], inp["h"], inp["uniforms"]
+        self.T = W.temperatures(wl).to(dev)
+        self.sps = torch.tensor(W.sps_table(wl), dtype=torch.float64, device=dev)
+        # Untimed pass: draft with debug logits -> target stand-in = logits + noise; the plan of
+        # this pass fixes the packed row layout (the timed rounds recompute the same plan).
+        logits = torch.empty_like(self.U)
+        tok, q, lse = L.markov_draft(d, self.U, wts["W1"], wts["W2t"], self.anchor, self.uniforms,
+                                     logits_dbg=logits)
+        conf = L.confidence(d, self.h, wts["W1"], wts["w"], self.T, self.anchor, tok)
+        dl, ro, st = L.plan(d, conf, self.sps, wl.mode)
+        dense = W.target_dense(logits, inp["U_bonus"], inp["noise"])
+        del logits, inp
+        self.target = W.pack_rows(dense, dl)
+        del dense
+        torch.cuda.synchronize()
+        self.rows = int(ro[-1].item())
+        self.draft_len = dl.clone()
+
+
+def algorithmic_bytes(wl, rows, n_res):
+    """Bytes the method must move in one round (no caching credit): per draft step the U slice
+    and W2; the hidden states and confidence weights; every verified target row; for rejected
+    requests one more W2 pass plus their U and target rows."""
+    B, V, g, r, d = wl.B, wl.V, wl.gamma, wl.r, wl.d
+    draft = g * (4 * B * V + 2 * r * V)
+    conf = 2 * B * g * d + 2 * (d + r)
+    stats = 4 * rows * V
+    emit = (2 * r * V if n_res > 0 else 0) + n_res * 8 * V
+    return draft + conf + stats + emit
+
+
+def cpu_baseline(wl, wts, s, threads):
+    """The oracle as it stands, timed on the host on one full round of the same workload."""
+    import oracle
+    host = lambda t: t.detach().cpu().numpy()
+    bits = W.bf16_bits
+    U, W1b, W2b = host(s.U), bits(wts["W1"]), bits(wts["W2t"])
+    anchor, unif, h = host(s.anchor), host(s.uniforms), bits(s.h)
+    sps = W.sps_table(wl)
+    t0 = time.perf_counter()
+    o = oracle.markov_draft(U, W1b, W2b, anchor, unif, want_logits=True, threads=threads)
+    c = oracle.confidence(h, W1b, bits(wts["w"]), W.temperatures(wl).numpy(), anchor, o["tokens"],
+                          threads=threads)
+    p = oracle.plan(c["conf"], sps, wl.mode)
+    t1 = time.perf_counter()
+    # target stand-in (not timed): the oracle's own logits + noise, packed by its own plan
+    noise = host(W.round_inputs(wl, 0, "cuda", with_hidden=False)["noise"])
+    ub = host(W.round_inputs(wl, 0, "cuda", with_hidden=False, with_noise=False)["U_bonus"])
+    dense = np.concatenate([o["logits"], ub[:, None, :]], 1) + noise
+    keep = np.arange(wl.gamma + 1)[None, :] <= p["draft_len"][:, None]
+    target = np.ascontiguousarray(dense[keep], dtype=np.float32)
+    del dense, noise
+    t2 = time.perf_counter()
+    oracle.verify(target, p["row_offsets"], p["draft_len"], U, W1b, W2b, anchor, o["tokens"],
+                  o["q"], unif, threads=threads)
+    t3 = time.perf_counter()
+    sec = (t1 - t0) + (t3 - t2)
+    return {"value": 1.0 / sec, "unit": "rounds/s", "cores": threads, "kind": "oracle",
+            "sample": f"one full round of {wl.name} (all {wl.B} requests: draft, confidence, "
+                      f"plan, verify; target construction excluded), {sec:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=60)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--sets", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-events", action="store_true",
+                    help="time without per-launch HIP events (for comparison)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration under rocprof)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build runs on a single MI355X and has no "
+              "multi-GPU path; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    dev = "cuda"
+    wl = W.WORKLOADS[WORKLOAD]
+    d = L.Dims(wl.B, wl.gamma, wl.V, wl.r, wl.d)
+    L.load_library()
+    wts = W.weights(wl, dev)
+    sets = [InputSet(wl, wts, i, dev) for i in range(args.sets)]
+
+    # output and workspace buffers, allocated once
+    B, g = wl.B, wl.gamma
+    ws_d = L.workspace(d, L.OP_DRAFT, dev)
+    ws_v = L.workspace(d, L.OP_VERIFY, dev)
+    tok = torch.empty((B, g), dtype=torch.int32, device=dev)
+    q = torch.empty((B, g), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, g), dtype=torch.float64, device=dev)
+    conf = torch.empty((B, g), dtype=torch.float32, device=dev)
+    dl = torch.empty(B, dtype=torch.int32, device=dev)
+    ro = torch.empty(B + 1, dtype=torch.int32, device=dev)
+    st = torch.empty(4, dtype=torch.float64, device=dev)
+    al = torch.empty(B, dtype=torch.int32, device=dev)
+    nt = torch.empty(B, dtype=torch.int32, device=dev)
+    be = torch.empty(B, dtype=torch.float32, device=dev)
+    fl = torch.empty(B, dtype=torch.int32, device=dev)
+
+    def round_(s):
+        L.markov_draft(d, s.U, wts["W1"], wts["W2t"], s.anchor, s.uniforms, tokens=tok, q=q,
+                       lse=lse, ws=ws_d)
+        L.confidence(d, s.h, wts["W1"], wts["w"], s.T, s.anchor, tok, conf=conf)
+        L.plan(d, conf, s.sps, wl.mode, draft_len=dl, row_offsets=ro, stats=st)
+        L.verify(d, s.target, ro, dl, s.U, wts["W1"], wts["W2t"], s.anchor, tok, q, lse,
+                 s.uniforms, accept_len=al, next_token=nt, beta_emit=be, flags=fl, ws=ws_v)
+
+    # per-set results (identical every time a set is replayed: deterministic)
+    per_set = []
+    for s in sets:
+        round_(s)
+        torch.cuda.synchronize()
+        assert torch.equal(dl, s.draft_len), "the timed plan differs from the preparation pass"
+        n_res = int((be >= 0).sum().item())
+        per_set.append(dict(tokens=int((al + 1).sum().item()), rows=s.rows, n_res=n_res))
+
+    for i in range(args.warmup):
+        round_(sets[i % len(sets)])
+    torch.cuda.synchronize()
+    if not args.no_kernel_events:
+        L.profile_begin(64 * args.steps)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        round_(sets[i % len(sets)])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kern = {} if args.no_kernel_events else L.profile_end()
+
+    rounds_per_s = args.steps / elapsed
+    used = [per_set[i % len(sets)] for i in range(args.steps)]
+    tokens_per_round = float(np.mean([u["tokens"] for u in used]))
+    bytes_per_round = float(np.mean([algorithmic_bytes(wl, u["rows"], u["n_res"]) for u in used]))
+
+    roofline = None
+    kernels = {}
+    for name, (cnt, ms) in kern.items():
+        if cnt:
+            kernels[name] = {"launches": cnt, "avg_us": 1e3 * ms / cnt}
+    if "markov_step" in kernels:
+        step_bytes = 4 * wl.B * wl.V + 2 * wl.r * wl.V        # U slice + W2 per launch
+        avg_s = kernels["markov_step"]["avg_us"] * 1e-6
+        achieved = step_bytes / avg_s / 1e9
+        traffic = traffic_from_profiles(1)
+        roofline = {"kernel": "markov_step", "bound": "hbm", "achieved": round(achieved, 1),
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "traffic": traffic, "algorithmic_bytes_per_launch": step_bytes}
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1.0)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    base = None
+    if not args.no_cpu_baseline:
+        threads = min(16, os.cpu_count() or 1)
+        base = cpu_baseline(wl, wts, sets[0], threads)
+
+    out = {
+        "metric": METRIC,
+        "value": round(rounds_per_s, 2),
+        "unit": "rounds/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(1e3 * elapsed / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 mfma / f32 / f64",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD, "B": wl.B, "V": wl.V, "gamma": wl.gamma, "r": wl.r,
+                   "d": wl.d, "plan": "early_stop", "sps": "1/(1+n/768)", "input_sets": len(sets),
+                   "parallelism": "1 GPU"},
+        "tokens_per_s": round(rounds_per_s * tokens_per_round, 1),
+        "tokens_per_round": tokens_per_round,
+        "round_algorithmic_gbs": round(bytes_per_round * rounds_per_s / 1e9, 1),
+        "round_hbm_frac": round(bytes_per_round * rounds_per_s / 1e9 / HBM_PEAK_GBS, 4),
+        "roofline": roofline,
+        "kernels_us": {k: round(v["avg_us"], 2) for k, v in kernels.items()},
+        "cpu_baseline": base,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
