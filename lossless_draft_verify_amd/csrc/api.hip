@@ -28,7 +28,7 @@ bool rank_ok(int r) {
 // B * (gamma + 1) verified rows index grid dimension y of the target pass (<= 65535); the
 // planner sorts all B * gamma candidates in one workgroup's LDS (<= 8192).
 bool dims_ok(const dspark_dims& d) {
-  if (d.B < 1 || d.gamma < 1 || d.V < 2 || !rank_ok(d.r)) return false;
+  if (d.B < 1 || d.gamma < 1 || d.V < 2 || d.V > kMaxVocab || !rank_ok(d.r)) return false;
   if (static_cast<int64_t>(d.B) * (d.gamma + 1) > 65535) return false;
   return true;
 }
@@ -38,20 +38,28 @@ bool plan_dims_ok(const dspark_dims& d) {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// Compute units of the current device (cached per device id).
+int compute_units() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 // ---- workspace layouts ----------------------------------------------------------------------
 struct DraftWs {
-  float* pmax;
-  float* psum;
+  float2* part;
 };
 size_t draft_ws(const dspark_dims& d, void* base, DraftWs* out) {
   const size_t n = static_cast<size_t>(d.B) * ntiles_of(d.V);
-  size_t off = 0;
-  char* b = static_cast<char*>(base);
-  if (out) out->pmax = reinterpret_cast<float*>(b + off);
-  off += align_up(n * sizeof(float));
-  if (out) out->psum = reinterpret_cast<float*>(b + off);
-  off += align_up(n * sizeof(float));
-  return off;
+  if (out) out->part = static_cast<float2*>(base);
+  return align_up(n * sizeof(float2));
 }
 
 size_t verify_ws(const dspark_dims& d, void* base, VerifyWs* out) {
@@ -165,6 +173,7 @@ dspark_status dspark_markov_draft(dspark_dims dims, const float* U, const uint16
   draft_ws(dims, ws, &w);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int nt = ntiles_of(dims.V);
+  const int cus = compute_units();
   for (int k = 0; k < dims.gamma; ++k) {
     const int32_t* prev = anchor;
     int stride = 1;
@@ -172,11 +181,11 @@ dspark_status dspark_markov_draft(dspark_dims dims, const float* U, const uint16
       prev = (force_tokens ? force_tokens : tokens) + (k - 1);
       stride = dims.gamma;
     }
-    StepArgs sa{dims.B, dims.V, dims.gamma, k, nt, U, W1, W2t, prev, stride, w.pmax, w.psum,
-                logits_dbg};
+    StepArgs sa{dims.B, dims.V, dims.gamma, k, nt, U, W1, W2t, prev, stride, w.part, logits_dbg,
+                cus};
     if (timed(kMarkovStep, s, [&] { return launch_markov_step(sa, dims.r, s); }) != hipSuccess)
       return DSPARK_ERR_HIP;
-    SampleArgs pa{dims.B, dims.V, dims.gamma, k, nt, U, W1, W2t, prev, stride, w.pmax, w.psum,
+    SampleArgs pa{dims.B, dims.V, dims.gamma, k, nt, U, W1, W2t, prev, stride, w.part,
                   uniforms, force_tokens, tokens, q_tok, lse};
     if (timed(kDraftSample, s, [&] { return launch_draft_sample(pa, dims.r, s); }) != hipSuccess)
       return DSPARK_ERR_HIP;

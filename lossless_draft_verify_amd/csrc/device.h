@@ -19,6 +19,7 @@ constexpr int kWave = 64;
 constexpr int kBlock = 256;          // threads per workgroup for the streaming kernels
 constexpr int kTileTokens = 32;      // tokens per MFMA tile = tokens per draft partial
 constexpr int kSegTokens = 4096;     // tokens per target-row segment
+constexpr int kMaxVocab = 1 << 19;   // a sampler stages one row's tile partials in LDS (8 B each)
 constexpr float kNegInf = -__builtin_inff();
 
 // One 32x32x16 bf16 MFMA step (fp32 accumulate). Lane l holds A[m = l % 32][k = 8 (l / 32) + i]
@@ -48,18 +49,18 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
 
-// exp(x) for x <= 0 in fp32: exp2 of x*log2(e), with the rounding error of that product
-// carried as a first-order correction (2^(y + dy) = 2^y (1 + dy ln 2)). Values below -200 are
-// clamped (the result underflows to 0 either way); NaN propagates.
+// exp(x) for x <= 0 in fp32, as exp2(x * log2 e) on the hardware exp2 (about 1 ulp). x is a
+// logit minus its tile maximum, so the terms that carry the probability mass have small |x| and
+// a small rounding error in the product. exp2(-inf) = 0; NaN propagates.
 __device__ __forceinline__ float exp_term(float x) {
-  const float kLog2eHi = 1.44269502162933349609375f;   // fp32(log2 e)
-  const float kLog2eLo = 1.925963033500011079e-8f;     // log2 e - kLog2eHi
-  const float kLn2 = 0.693147180559945309f;
-  x = (x < -200.0f) ? -200.0f : x;
-  const float y = x * kLog2eHi;
-  const float dy = __builtin_fmaf(x, kLog2eHi, -y) + x * kLog2eLo;
-  const float e = __builtin_amdgcn_exp2f(y);
-  return __builtin_fmaf(e, dy * kLn2, e);
+  return __builtin_amdgcn_exp2f(x * 1.44269504088896340736f);
+}
+
+// Workgroup barrier for an LDS hand-off that leaves global loads in flight: __syncthreads()
+// carries a workgroup fence, which waits for every outstanding global load before s_barrier
+// and would serialise a software prefetch issued just before it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // ---- wave (64-lane) reductions in a fixed butterfly order ------------------------------------

@@ -21,74 +21,214 @@ namespace dspark {
 
 namespace {
 
-template <int KS>
-__global__ __launch_bounds__(kBlock, 2) void markov_step_kernel(StepArgs p) {
+// Persistent draft step: one 512-thread workgroup per compute unit walks work items (a
+// 128-token tile of the vocabulary x a group of up to kBG requests). The group's embedding
+// rows sit in LDS; each item's U block is loaded row-contiguously (512 B per request row) and
+// staged through LDS into the MFMA output layout. Wave w computes tokens 32 (w % 4) .. +32 for
+// requests 64 (w / 4) .. +64 of the group (two 32-request MFMA tiles), so each SIMD runs two
+// waves. The next item's U block is loaded right after the current one is staged, and the
+// next W2 tile right after the current MFMAs; LDS hand-offs use lds_barrier(), which leaves
+// those loads in flight.
+constexpr int kStepThreads = 512;
+
+template <int KS, bool VEC4>
+struct StepKernel {
   using C = StepCfg<KS>;
-  constexpr int r = C::kR;
-  __shared__ __attribute__((aligned(16))) uint16_t E[C::kBG * C::kLdsRow];
+  static constexpr int r = C::kR;
+  static constexpr int BG = C::kBG;                   // requests per group (128, or 64 for r=512)
+  static constexpr int kNTW = BG / 64;                // 32-request MFMA tiles per wave
+  static constexpr int kTok = 4 * kTileTokens;        // tokens per item
+  static constexpr int kUrow = kTok + 4;              // padded LDS row of the staged U block
+  static constexpr int kURows = BG / 16;              // U rows per thread (32 threads per row)
+  static constexpr int kPR = r / 8;                   // 16-byte pieces per embedding row
+  static constexpr int kEPieces = (BG * kPR + kStepThreads - 1) / kStepThreads;
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int half = lane >> 5, col = lane & 31;
-  const int tok0 = blockIdx.x * (4 * kTileTokens) + wave * kTileTokens;
-  const bool active = tok0 < p.V;
-  const bool vec4 = (p.V & 3) == 0;
+  const StepArgs& p;
+  uint16_t* E;
+  float* Us;
+  int tid, lane, half, col, ts, bh, ngroups;
 
-  u16x8_t a[KS];
-  load_w2_tile<KS>(a, p.W2t, tok0 + col, p.V, half);
+  __device__ StepKernel(const StepArgs& p_, uint16_t* E_, float* Us_) : p(p_), E(E_), Us(Us_) {
+    tid = threadIdx.x;
+    lane = tid & 63;
+    half = lane >> 5;
+    col = lane & 31;
+    ts = (tid >> 6) & 3;   // token sub-tile of the wave
+    bh = tid >> 8;         // request half of the wave
+    ngroups = (p.B + BG - 1) / BG;
+  }
 
-  for (int bg0 = 0; bg0 < p.B; bg0 += C::kBG) {
-    const int nb = min(C::kBG, p.B - bg0);
-    constexpr int kChunks = r / 8;  // 16-byte pieces per E row
-    for (int c = threadIdx.x; c < C::kBG * kChunks; c += kBlock) {
-      const int i = c / kChunks, q = c % kChunks;
-      u16x8_t v = zero_u16x8();
-      if (i < nb) {
-        const int32_t row = p.prev[static_cast<size_t>(bg0 + i) * p.prev_stride];
-        v = load_u16x8(p.W1 + static_cast<size_t>(row) * r + q * 8);
+  // Request rows past B read row B-1 (never used): no branch in the load sequence.
+  __device__ __forceinline__ void load_u(float4 (&u)[kURows], int it) const {
+    const int tile = it / ngroups, group = it % ngroups;
+    const int v = tile * kTok + 4 * (tid & 31);
+#pragma unroll
+    for (int i = 0; i < kURows; ++i) {
+      const int b = min(group * BG + i * 16 + (tid >> 5), p.B - 1);
+      const float* row = p.U + (static_cast<size_t>(b) * p.gamma + p.k) * p.V;
+      if (VEC4) {
+        u[i] = (v + 3 < p.V) ? *reinterpret_cast<const float4*>(row + v) : make_float4(0.f, 0.f, 0.f, 0.f);
+      } else {
+        float o[4];
+        load4(row, v, p.V, false, o);
+        u[i] = make_float4(o[0], o[1], o[2], o[3]);
       }
-      *reinterpret_cast<u16x8_t*>(&E[i * C::kLdsRow + q * 8]) = v;
     }
-    __syncthreads();
-    if (active) {
-      for (int nt = 0; nt * 32 < nb; ++nt) {
-        const uint16_t* erow = &E[(nt * 32 + col) * C::kLdsRow + 8 * half];
-        f32x16_t acc = {};
+  }
+
+  __device__ __forceinline__ void load_a(u16x8_t (&a)[KS], int it) const {
+    load_w2_tile<KS>(a, p.W2t, (it / ngroups) * kTok + ts * kTileTokens + col, p.V, half);
+  }
+
+  // Embedding rows of one request group into LDS: ids first, then rows.
+  __device__ void load_embeddings(int group) const {
+    // piece c = i * kStepThreads + tid covers row c / kPR, bytes 16 (c % kPR); pieces past the
+    // group (c >= BG * kPR) are clamped to the last one and not stored.
+    int32_t ids[kEPieces];
 #pragma unroll
-        for (int s = 0; s < KS; ++s) acc = mfma_32x32x16(a[s], load_u16x8(erow + 16 * s), acc);
-        const int b = bg0 + nt * 32 + col;
-        if (b < p.B) {
-          const size_t urow = (static_cast<size_t>(b) * p.gamma + p.k) * p.V;
-          float L[16];
-          tile_logits(acc, p.U + urow, tok0, p.V, half, vec4, L);
-          if (p.dbg) {
+    for (int i = 0; i < kEPieces; ++i) {
+      const int c = min(i * kStepThreads + tid, BG * kPR - 1);
+      const int b = min(group * BG + c / kPR, p.B - 1);
+      ids[i] = p.prev[static_cast<size_t>(b) * p.prev_stride];
+    }
+    u16x8_t e[kEPieces];
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              const int v = tok0 + 8 * g + 4 * half;
+    for (int i = 0; i < kEPieces; ++i) {
+      const int c = min(i * kStepThreads + tid, BG * kPR - 1);
+      e[i] = load_u16x8(p.W1 + static_cast<size_t>(ids[i]) * r + (c % kPR) * 8);
+    }
 #pragma unroll
-              for (int i = 0; i < 4; ++i)
-                if (v + i < p.V) p.dbg[urow + v + i] = L[4 * g + i];
-            }
-          }
-          float m = max16(L);
-          m = fmaxf(m, __shfl_xor(m, 32, kWave));
-          float t[16];
-          tile_terms(L, m, t);
-          float s = sum16(t);
-          s = s + __shfl_xor(s, 32, kWave);
-          if (half == 0) {
-            const size_t o = static_cast<size_t>(b) * p.ntiles + tok0 / kTileTokens;
-            p.pmax[o] = m;
-            p.psum[o] = s;
-          }
+    for (int i = 0; i < kEPieces; ++i) {
+      const int c = i * kStepThreads + tid;
+      if (c >= BG * kPR) break;
+      const bool valid = group * BG + c / kPR < p.B;
+      *reinterpret_cast<u16x8_t*>(&E[(c / kPR) * C::kLdsRow + (c % kPR) * 8]) = valid ? e[i] : zero_u16x8();
+    }
+  }
+
+  __device__ __forceinline__ void stage_u(const float4 (&u)[kURows]) const {
+#pragma unroll
+    for (int i = 0; i < kURows; ++i)
+      *reinterpret_cast<float4*>(&Us[(i * 16 + (tid >> 5)) * kUrow + 4 * (tid & 31)]) = u[i];
+  }
+
+  // MFMA (independent chains over the wave's request tiles, embedding reads one k-step ahead).
+  __device__ __forceinline__ void mfma(const u16x8_t (&a)[KS], f32x16_t (&acc)[kNTW]) const {
+    u16x8_t e0[kNTW], e1[kNTW];
+#pragma unroll
+    for (int nt = 0; nt < kNTW; ++nt) {
+      acc[nt] = f32x16_t{};
+      e0[nt] = load_u16x8(&E[((bh * kNTW + nt) * 32 + col) * C::kLdsRow + 8 * half]);
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2) {
+      u16x8_t (&cur)[kNTW] = (s2 & 1) ? e1 : e0;
+      u16x8_t (&nxt)[kNTW] = (s2 & 1) ? e0 : e1;
+      if (s2 + 1 < KS) {
+#pragma unroll
+        for (int nt = 0; nt < kNTW; ++nt)
+          nxt[nt] = load_u16x8(&E[((bh * kNTW + nt) * 32 + col) * C::kLdsRow + 8 * half + 16 * (s2 + 1)]);
+      }
+#pragma unroll
+      for (int nt = 0; nt < kNTW; ++nt) acc[nt] = mfma_32x32x16(a[s2], cur[nt], acc[nt]);
+    }
+  }
+
+  // Epilogue: L = U + bias, tile max, fp32 sum of exp(L - max), one float2 per (request, tile).
+  __device__ __forceinline__ void epilogue(f32x16_t (&acc)[kNTW], int it) const {
+    const int tile = it / ngroups, group = it % ngroups;
+    const int tok0 = tile * kTok + ts * kTileTokens;
+    const bool full = tok0 + kTileTokens <= p.V;
+    float m[kNTW], sm[kNTW];
+#pragma unroll
+    for (int nt = 0; nt < kNTW; ++nt) {
+      const int rt = bh * kNTW + nt;
+      const float* urow = &Us[(rt * 32 + col) * kUrow + ts * kTileTokens + 4 * half];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float4 uu = *reinterpret_cast<const float4*>(urow + 8 * g);
+        acc[nt][4 * g + 0] += uu.x;
+        acc[nt][4 * g + 1] += uu.y;
+        acc[nt][4 * g + 2] += uu.z;
+        acc[nt][4 * g + 3] += uu.w;
+      }
+      if (!full) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (tok0 + tile_token(j, half) >= p.V) acc[nt][j] = kNegInf;
+      }
+      float L[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) L[j] = acc[nt][j];
+      m[nt] = max16(L);
+    }
+#pragma unroll
+    for (int nt = 0; nt < kNTW; ++nt) m[nt] = fmaxf(m[nt], __shfl_xor(m[nt], 32, kWave));
+#pragma unroll
+    for (int nt = 0; nt < kNTW; ++nt) {
+      float t[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) t[j] = exp_term(acc[nt][j] - m[nt]);
+      sm[nt] = (m[nt] == kNegInf) ? 0.0f : sum16(t);
+    }
+#pragma unroll
+    for (int nt = 0; nt < kNTW; ++nt) sm[nt] = sm[nt] + __shfl_xor(sm[nt], 32, kWave);
+#pragma unroll
+    for (int nt = 0; nt < kNTW; ++nt) {
+      const int b = group * BG + (bh * kNTW + nt) * 32 + col;
+      if (b >= p.B) continue;
+      if (half == 0) p.part[static_cast<size_t>(b) * p.ntiles + tok0 / kTileTokens] = make_float2(m[nt], sm[nt]);
+      if (p.dbg) {
+        const size_t drow = (static_cast<size_t>(b) * p.gamma + p.k) * p.V;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int v = tok0 + tile_token(j, half);
+          if (v < p.V) p.dbg[drow + v] = acc[nt][j];
         }
       }
     }
-    __syncthreads();
+  }
+};
+
+template <int KS, bool VEC4>
+__global__ __launch_bounds__(kStepThreads, 1) void markov_step_kernel(StepArgs p) {
+  using K = StepKernel<KS, VEC4>;
+  __shared__ __attribute__((aligned(16))) uint16_t E[K::BG * K::C::kLdsRow];
+  __shared__ __attribute__((aligned(16))) float Us[K::BG * K::kUrow];
+  const K k(p, E, Us);
+  const int nitems = ((p.V + K::kTok - 1) / K::kTok) * k.ngroups;
+  int it = blockIdx.x;
+  if (it >= nitems) return;
+  u16x8_t a[KS];
+  float4 u[K::kURows];
+  f32x16_t acc[K::kNTW];
+  int cur_group = -1;
+  k.load_a(a, it);
+  k.load_u(u, it);
+  for (; it < nitems; it += gridDim.x) {
+    const int group = it % k.ngroups;
+    if (group != cur_group) k.load_embeddings(group);
+    cur_group = group;
+    k.stage_u(u);
+    const int nxt = it + gridDim.x;
+    const bool has_next = nxt < nitems;
+    if (has_next) k.load_u(u, nxt);
+    lds_barrier();
+    const bool active = (it / k.ngroups) * K::kTok + k.ts * kTileTokens < p.V &&
+                        group * K::BG + k.bh * K::kNTW * 32 < p.B;
+    if (active) k.mfma(a, acc);
+    if (has_next) k.load_a(a, nxt);
+    if (active) k.epilogue(acc, it);
+    lds_barrier();
   }
 }
 
+// One workgroup per request: the row's tile partials are staged in LDS (converted in place to
+// fp64 masses relative to the row max), located with a block scan, and the chosen tile is
+// recomputed and walked on wave 0.
 template <int KS>
 __global__ __launch_bounds__(kBlock) void draft_sample_kernel(SampleArgs p) {
+  extern __shared__ double smass[];   // [ntiles]: float2 partials, then fp64 masses in place
   __shared__ double red_d[kBlock / 64];
   __shared__ float red_f[kBlock / 64];
   __shared__ int red_i[kBlock / 64];
@@ -97,22 +237,31 @@ __global__ __launch_bounds__(kBlock) void draft_sample_kernel(SampleArgs p) {
   __shared__ float Lc[kTileTokens];
 
   const int b = blockIdx.x;
-  const int tid = threadIdx.x;
-  const size_t pbase = static_cast<size_t>(b) * p.ntiles;
+  const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5;
+  const int nt = p.ntiles;
+  const float2* part = p.part + static_cast<size_t>(b) * nt;
   const size_t urow = (static_cast<size_t>(b) * p.gamma + p.k) * p.V;
   const int32_t prevtok = p.prev[static_cast<size_t>(b) * p.prev_stride];
   const size_t out = static_cast<size_t>(b) * p.gamma + p.k;
 
-  // Row max over the tile maxima.
-  float m = kNegInf;
-  for (int c = tid; c < p.ntiles; c += kBlock) m = fmaxf(m, p.pmax[pbase + c]);
-  const float M = block_max<kBlock>(m, red_f);
+  u16x8_t e[KS];
+  if (tid < 64) load_e_row<KS>(e, p.W1, prevtok, half);
+  float2* sp = reinterpret_cast<float2*>(smass);
+  for (int c = tid; c < nt; c += kBlock) sp[c] = part[c];
+  __syncthreads();
 
+  const int per = (nt + kBlock - 1) / kBlock;
+  const int c0 = min(nt, tid * per), c1 = min(nt, c0 + per);
+  float m = kNegInf;
+  for (int c = c0; c < c1; ++c) m = fmaxf(m, sp[c].x);
+  const float M = block_max<kBlock>(m, red_f);
+  for (int c = c0; c < c1; ++c) {
+    const float2 v = sp[c];
+    smass[c] = partial_mass(v.x, static_cast<double>(v.y), M);
+  }
+  __syncthreads();
   const double u = static_cast<double>(p.uniforms[(static_cast<size_t>(b) * (p.gamma + 1) + p.k) * 3]);
-  auto mass = [&](int c) {
-    return partial_mass(p.pmax[pbase + c], static_cast<double>(p.psum[pbase + c]), M);
-  };
-  const Located L = locate_chunk<kBlock>(p.ntiles, u, mass, red_d, red_i, &loc);
+  const Located L = locate_chunk<kBlock>(nt, u, [&](int c) { return smass[c]; }, red_d, red_i, &loc);
   const double lse = static_cast<double>(M) + log(L.total);
 
   if (L.chunk < 0) {  // logits not finite: documented fallback
@@ -124,44 +273,34 @@ __global__ __launch_bounds__(kBlock) void draft_sample_kernel(SampleArgs p) {
     return;
   }
   const int tok0 = L.chunk * kTileTokens;
-  if (tid < 64) recompute_tile<KS>(p.W1, p.W2t, p.U + urow, prevtok, tok0, p.V, Ls);
-  __syncthreads();
   int x = 0;
-  __shared__ int s_x;
-  if (tid == 0) {
-    const float tm = p.pmax[pbase + L.chunk];
+  if (tid < 64) {
+    recompute_tile_e<KS>(e, p.W2t, p.U + urow, tok0, p.V, Ls);
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_wave_barrier();
+    const float tm = part[L.chunk].x;
     const double f = exp(static_cast<double>(tm) - static_cast<double>(M));
-    double cum = L.before;
-    int found = -1, last = -1;
-    for (int j = 0; j < kTileTokens && tok0 + j < p.V; ++j) {
-      const float t = exp_term(Ls[j] - tm);
-      if (t > 0.0f) last = j;
-      if (!L.take_last) {
-        cum += f * static_cast<double>(t);
-        if (cum > L.target) {
-          found = j;
-          break;
-        }
-      }
-    }
-    s_x = tok0 + (found >= 0 ? found : (last >= 0 ? last : 0));
+    double w = 0.0;
+    if (lane < kTileTokens && tok0 + lane < p.V) w = f * static_cast<double>(exp_term(Ls[lane] - tm));
+    x = tok0 + walk_tile(w, L.before, L.target, L.take_last != 0);
   }
-  __syncthreads();
-  x = s_x;
   // The token whose probability is reported (and that conditions the next position).
-  const int32_t cond = p.force ? p.force[out] : x;
-  const float* Lsrc = Ls;
-  if (cond / kTileTokens != L.chunk) {
-    if (tid < 64) recompute_tile<KS>(p.W1, p.W2t, p.U + urow, prevtok,
-                                     (cond / kTileTokens) * kTileTokens, p.V, Lc);
-    __syncthreads();
-    Lsrc = Lc;
-  }
-  if (tid == 0) {
-    const float lc = Lsrc[cond % kTileTokens];
-    p.tokens[out] = x;
-    p.q[out] = static_cast<float>(exp(static_cast<double>(lc) - lse));
-    p.lse[out] = lse;
+  if (tid < 64) {
+    const int32_t cond = p.force ? p.force[out] : x;
+    float lc;
+    if (cond / kTileTokens != L.chunk) {
+      recompute_tile_e<KS>(e, p.W2t, p.U + urow, (cond / kTileTokens) * kTileTokens, p.V, Lc);
+      __builtin_amdgcn_s_waitcnt(0);
+      __builtin_amdgcn_wave_barrier();
+      lc = Lc[cond % kTileTokens];
+    } else {
+      lc = Ls[cond % kTileTokens];
+    }
+    if (tid == 0) {
+      p.tokens[out] = x;
+      p.q[out] = static_cast<float>(exp(static_cast<double>(lc) - lse));
+      p.lse[out] = lse;
+    }
   }
 }
 
@@ -198,13 +337,19 @@ __global__ __launch_bounds__(kBlock) void confidence_kernel(ConfArgs p) {
 
 template <int KS>
 static hipError_t launch_step_ks(const StepArgs& a, hipStream_t s) {
-  const int grid = (a.V + 4 * kTileTokens - 1) / (4 * kTileTokens);
-  hipLaunchKernelGGL(markov_step_kernel<KS>, dim3(grid), dim3(kBlock), 0, s, a);
+  const int items = ((a.V + 4 * kTileTokens - 1) / (4 * kTileTokens)) *
+                    ((a.B + StepCfg<KS>::kBG - 1) / StepCfg<KS>::kBG);
+  const int grid = items < a.persistent_wgs ? items : a.persistent_wgs;
+  if ((a.V & 3) == 0)
+    hipLaunchKernelGGL((markov_step_kernel<KS, true>), dim3(grid), dim3(kStepThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((markov_step_kernel<KS, false>), dim3(grid), dim3(kStepThreads), 0, s, a);
   return hipGetLastError();
 }
 template <int KS>
 static hipError_t launch_sample_ks(const SampleArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(draft_sample_kernel<KS>, dim3(a.B), dim3(kBlock), 0, s, a);
+  const size_t lds = static_cast<size_t>(a.ntiles) * sizeof(double);
+  hipLaunchKernelGGL(draft_sample_kernel<KS>, dim3(a.B), dim3(kBlock), lds, s, a);
   return hipGetLastError();
 }
 

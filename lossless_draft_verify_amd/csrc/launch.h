@@ -14,9 +14,9 @@ struct StepArgs {
   const uint16_t* W2t;
   const int32_t* prev;  // conditioning token of request b at prev[b * prev_stride]
   int prev_stride;
-  float* pmax;          // [B][ntiles] tile max
-  float* psum;          // [B][ntiles] sum exp(L - tile max)
+  float2* part;         // [B][ntiles] (tile max, sum exp(L - tile max))
   float* dbg;           // nullable [B][gamma][V]
+  int persistent_wgs;   // workgroups of the persistent step kernel (one per compute unit)
 };
 
 struct SampleArgs {
@@ -26,8 +26,7 @@ struct SampleArgs {
   const uint16_t* W2t;
   const int32_t* prev;
   int prev_stride;
-  const float* pmax;
-  const float* psum;
+  const float2* part;
   const float* uniforms;
   const int32_t* force;  // nullable [B][gamma]
   int32_t* tokens;

@@ -58,12 +58,6 @@ __device__ __forceinline__ void tile_logits(const f32x16_t& acc, const float* __
   }
 }
 
-// exp(L - m) of the 16 slots, 0 where the tile max is -inf.
-__device__ __forceinline__ void tile_terms(const float (&L)[16], float m, float (&t)[16]) {
-#pragma unroll
-  for (int j = 0; j < 16; ++j) t[j] = (m == kNegInf) ? 0.0f : exp_term(L[j] - m);
-}
-
 __device__ __forceinline__ float sum16(const float (&t)[16]) {
   const float a = ((t[0] + t[1]) + (t[2] + t[3])) + ((t[4] + t[5]) + (t[6] + t[7]));
   const float b = ((t[8] + t[9]) + (t[10] + t[11])) + ((t[12] + t[13]) + (t[14] + t[15]));
@@ -99,6 +93,46 @@ __device__ void recompute_tile(const uint16_t* __restrict__ W1, const uint16_t* 
 #pragma unroll
     for (int j = 0; j < 16; ++j) Ls[tile_token(j, half)] = L[j];
   }
+}
+
+// The Markov embedding row of the previous token, in the MFMA B-operand layout of a lane.
+template <int KS>
+__device__ __forceinline__ void load_e_row(u16x8_t (&e)[KS], const uint16_t* __restrict__ W1,
+                                           int32_t prevtok, int half) {
+  constexpr int r = KS * 16;
+  const uint16_t* erow = W1 + static_cast<size_t>(prevtok) * r + 8 * half;
+#pragma unroll
+  for (int s = 0; s < KS; ++s) e[s] = load_u16x8(erow + 16 * s);
+}
+
+// recompute_tile with the embedding row already in registers.
+template <int KS>
+__device__ void recompute_tile_e(const u16x8_t (&e)[KS], const uint16_t* __restrict__ W2t,
+                                 const float* __restrict__ Urow, int tok0, int V, float* Ls) {
+  const int lane = threadIdx.x & 63, half = lane >> 5, col = lane & 31;
+  u16x8_t a[KS];
+  load_w2_tile<KS>(a, W2t, tok0 + col, V, half);
+  f32x16_t acc = {};
+#pragma unroll
+  for (int s = 0; s < KS; ++s) acc = mfma_32x32x16(a[s], e[s], acc);
+  if (col == 0) {
+    float L[16];
+    tile_logits(acc, Urow, tok0, V, half, (V & 3) == 0, L);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) Ls[tile_token(j, half)] = L[j];
+  }
+}
+
+// Walk one tile in ascending token order on one wave: lane j < 32 holds the mass w of token j
+// (0 past the vocabulary). Returns the first j with before + sum_{i<=j} w_i > target, or, if
+// none (rounding) or take_last is set, the last j with w_j > 0 (0 if there is none).
+__device__ __forceinline__ int walk_tile(double w, double before, double target, bool take_last) {
+  const int lane = threadIdx.x & 63;
+  const double cum = before + wave_inclusive_scan(w, lane);
+  const unsigned long long hit = __ballot(!take_last && lane < 32 && cum > target);
+  if (hit) return __ffsll(static_cast<long long>(hit)) - 1;
+  const unsigned long long pos = __ballot(lane < 32 && w > 0.0);
+  return pos ? 63 - __clzll(static_cast<long long>(pos)) : 0;
 }
 
 }  // namespace dspark
