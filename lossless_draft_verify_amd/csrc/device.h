@@ -266,6 +266,10 @@ __device__ Located locate_chunk(int n, double u, MassFn mass, double* red_d, int
   return locate_chunk_t<NT>(n, [u](double Z) { return u * Z; }, mass, red_d, red_i, shared_out);
 }
 
+// LDS slot of entry c in a staging array with one pad slot per 16 entries: a thread's
+// contiguous 16-entry range then starts on a different bank than its neighbours'.
+__host__ __device__ __forceinline__ int padded(int c) { return c + (c >> 4); }
+
 // Mass of a partial (tile max m, fp32 sum s of exp(L - m)) relative to the row max M.
 __device__ __forceinline__ double partial_mass(float m, double s, float M) {
   return (m == kNegInf) ? 0.0 : exp(static_cast<double>(m) - static_cast<double>(M)) * s;

@@ -246,22 +246,36 @@ __global__ __launch_bounds__(kBlock) void draft_sample_kernel(SampleArgs p) {
 
   u16x8_t e[KS];
   if (tid < 64) load_e_row<KS>(e, p.W1, prevtok, half);
+  // Stage the partials: coalesced strided loads (16 in flight per thread), kept as float2 in
+  // padded LDS slots, then converted in place to fp64 masses once the row max is known. The
+  // padding (one slot per 16) spreads a thread's contiguous range over the banks.
   float2* sp = reinterpret_cast<float2*>(smass);
-  for (int c = tid; c < nt; c += kBlock) sp[c] = part[c];
-  __syncthreads();
-
-  const int per = (nt + kBlock - 1) / kBlock;
-  const int c0 = min(nt, tid * per), c1 = min(nt, c0 + per);
+  constexpr int kBatch = 16;
   float m = kNegInf;
-  for (int c = c0; c < c1; ++c) m = fmaxf(m, sp[c].x);
+  for (int c0 = 0; c0 < nt; c0 += kBlock * kBatch) {
+    float2 v[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int c = c0 + i * kBlock + tid;
+      v[i] = part[min(c, nt - 1)];
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int c = c0 + i * kBlock + tid;
+      if (c < nt) {
+        m = fmaxf(m, v[i].x);
+        sp[padded(c)] = v[i];
+      }
+    }
+  }
   const float M = block_max<kBlock>(m, red_f);
-  for (int c = c0; c < c1; ++c) {
-    const float2 v = sp[c];
-    smass[c] = partial_mass(v.x, static_cast<double>(v.y), M);
+  for (int c = tid; c < nt; c += kBlock) {
+    const float2 v = sp[padded(c)];
+    smass[padded(c)] = partial_mass(v.x, static_cast<double>(v.y), M);
   }
   __syncthreads();
   const double u = static_cast<double>(p.uniforms[(static_cast<size_t>(b) * (p.gamma + 1) + p.k) * 3]);
-  const Located L = locate_chunk<kBlock>(nt, u, [&](int c) { return smass[c]; }, red_d, red_i, &loc);
+  const Located L = locate_chunk<kBlock>(nt, u, [&](int c) { return smass[padded(c)]; }, red_d, red_i, &loc);
   const double lse = static_cast<double>(M) + log(L.total);
 
   if (L.chunk < 0) {  // logits not finite: documented fallback
@@ -348,7 +362,7 @@ static hipError_t launch_step_ks(const StepArgs& a, hipStream_t s) {
 }
 template <int KS>
 static hipError_t launch_sample_ks(const SampleArgs& a, hipStream_t s) {
-  const size_t lds = static_cast<size_t>(a.ntiles) * sizeof(double);
+  const size_t lds = static_cast<size_t>(padded(a.ntiles)) * sizeof(double);
   hipLaunchKernelGGL(draft_sample_kernel<KS>, dim3(a.B), dim3(kBlock), lds, s, a);
   return hipGetLastError();
 }

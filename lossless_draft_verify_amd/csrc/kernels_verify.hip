@@ -225,12 +225,12 @@ __global__ __launch_bounds__(kBlock, 2) void residual_partials_kernel(VerifyArgs
 
 template <int KS>
 __global__ __launch_bounds__(kBlock) void emit_sample_kernel(VerifyArgs p) {
+  extern __shared__ double stage[];   // padded: residual tile masses, or one segment's terms
   __shared__ double red_d[kBlock / 64];
   __shared__ float red_f[kBlock / 64];
   __shared__ int red_i[kBlock / 64];
   __shared__ Located loc;
   __shared__ float Ls[kTileTokens];
-  __shared__ int s_tok;
 
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
@@ -244,42 +244,52 @@ __global__ __launch_bounds__(kBlock) void emit_sample_kernel(VerifyArgs p) {
   int token = 0;
 
   if (kind == kEmitResidual) {
+    // Residual tile masses into LDS (16 loads in flight per thread) and their overlap sum.
     const size_t base = static_cast<size_t>(b) * p.ntiles;
+    const int nt = p.ntiles;
+    constexpr int kBatch = 16;
     double o = 0.0;
-    for (int c = tid; c < p.ntiles; c += kBlock) o += p.ws.rmin[base + c];
+    for (int c0 = 0; c0 < nt; c0 += kBlock * kBatch) {
+      double w[kBatch], ov[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        const int c = min(c0 + i * kBlock + tid, nt - 1);
+        w[i] = p.ws.rsum[base + c];
+        ov[i] = p.ws.rmin[base + c];
+      }
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        const int c = c0 + i * kBlock + tid;
+        if (c < nt) {
+          stage[padded(c)] = w[i];
+          o += ov[i];
+        }
+      }
+    }
     o = block_sum<kBlock>(o, red_d);
     if (tid == 0 && p.beta_emit) p.beta_emit[b] = static_cast<float>(o);
-    auto mass = [&](int c) { return p.ws.rsum[base + c]; };
-    const Located L = locate_chunk<kBlock>(p.ntiles, u, mass, red_d, red_i, &loc);
+    const Located L = locate_chunk<kBlock>(nt, u, [&](int c) { return stage[padded(c)]; }, red_d,
+                                           red_i, &loc);
     if (L.chunk < 0) {
       fl |= 2u;
       from_target = true;
     } else {
       const int tok0 = L.chunk * kTileTokens;
-      const float* Urow = p.U + (static_cast<size_t>(b) * p.gamma + j - 1) * p.V;
-      if (tid < 64) recompute_tile<KS>(p.W1, p.W2t, Urow, emit_prev(p, b, j), tok0, p.V, Ls);
-      __syncthreads();
-      if (tid == 0) {
-        const double lse_d = p.lse[static_cast<size_t>(b) * p.gamma + j - 1];
-        const double lse_t = p.ws.erow_lse[b];
-        double cum = L.before;
-        int found = -1, last = -1;
-        for (int m = 0; m < kTileTokens && tok0 + m < p.V; ++m) {
-          double w, ov;
-          residual_pair(Ls[m], trow[tok0 + m], lse_d, lse_t, w, ov);
-          if (w > 0.0) last = m;
-          if (!L.take_last) {
-            cum += w;
-            if (cum > L.target) {
-              found = m;
-              break;
-            }
-          }
+      if (tid < 64) {
+        const int lane = tid;
+        const float* Urow = p.U + (static_cast<size_t>(b) * p.gamma + j - 1) * p.V;
+        const float tv = (lane < kTileTokens && tok0 + lane < p.V) ? trow[tok0 + lane] : 0.0f;
+        recompute_tile<KS>(p.W1, p.W2t, Urow, emit_prev(p, b, j), tok0, p.V, Ls);
+        __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_wave_barrier();
+        double w = 0.0;
+        if (lane < kTileTokens && tok0 + lane < p.V) {
+          double ov;
+          residual_pair(Ls[lane], tv, p.lse[static_cast<size_t>(b) * p.gamma + j - 1],
+                        p.ws.erow_lse[b], w, ov);
         }
-        s_tok = tok0 + (found >= 0 ? found : (last >= 0 ? last : 0));
+        token = tok0 + walk_tile(w, L.before, L.target, L.take_last != 0);
       }
-      __syncthreads();
-      token = s_tok;
     }
   } else if (tid == 0 && p.beta_emit) {
     p.beta_emit[b] = -1.0f;
@@ -299,10 +309,27 @@ __global__ __launch_bounds__(kBlock) void emit_sample_kernel(VerifyArgs p) {
       const int t0 = S.chunk * kSegTokens;
       const int n = min(kSegTokens, p.V - t0);
       const float sm = p.ws.seg_max[base + S.chunk];
+      const bool vec4 = (p.V & 3) == 0;
+      float x[16];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float o4[4];
+        load4(trow, t0 + 1024 * i + 4 * tid, p.V, vec4, o4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[4 * i + e] = o4[e];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int c = 1024 * i + 4 * tid + e;
+          if (c < n) stage[padded(c)] = static_cast<double>(exp_term(x[4 * i + e] - sm));
+        }
+      __syncthreads();
       const double f = exp(static_cast<double>(sm) - static_cast<double>(M));
       const double tgt = S.take_last ? __builtin_inf() : (S.target - S.before) / f;
-      auto tmass = [&](int c) { return static_cast<double>(exp_term(trow[t0 + c] - sm)); };
-      const Located T = locate_chunk_t<kBlock>(n, [tgt](double) { return tgt; }, tmass, red_d,
+      const Located T = locate_chunk_t<kBlock>(n, [tgt](double) { return tgt; },
+                                               [&](int c) { return stage[padded(c)]; }, red_d,
                                                red_i, &loc);
       token = t0 + (T.chunk >= 0 ? T.chunk : 0);
     }
@@ -335,7 +362,8 @@ static hipError_t launch_resid_ks(const VerifyArgs& a, hipStream_t s) {
 }
 template <int KS>
 static hipError_t launch_emit_ks(const VerifyArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(emit_sample_kernel<KS>, dim3(a.B), dim3(kBlock), 0, s, a);
+  const int slots = padded(a.ntiles > kSegTokens ? a.ntiles : kSegTokens);
+  hipLaunchKernelGGL(emit_sample_kernel<KS>, dim3(a.B), dim3(kBlock), slots * sizeof(double), s, a);
   return hipGetLastError();
 }
 

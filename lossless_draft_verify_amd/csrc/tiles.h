@@ -71,30 +71,6 @@ __device__ __forceinline__ float max16(const float (&L)[16]) {
   return m;
 }
 
-// Recompute the logits of one 32-token tile for one request with exactly the instruction
-// sequence of markov_step_kernel (same k order, same operands; the request sits in every MFMA
-// column, and column placement does not change the result). Called by a whole wave; lanes 0
-// and 32 hold the 32 logits, which are written to Ls[0..32).
-template <int KS>
-__device__ void recompute_tile(const uint16_t* __restrict__ W1, const uint16_t* __restrict__ W2t,
-                               const float* __restrict__ Urow, int32_t prevtok, int tok0, int V,
-                               float* Ls) {
-  constexpr int r = KS * 16;
-  const int lane = threadIdx.x & 63, half = lane >> 5, col = lane & 31;
-  u16x8_t a[KS];
-  load_w2_tile<KS>(a, W2t, tok0 + col, V, half);
-  const uint16_t* erow = W1 + static_cast<size_t>(prevtok) * r + 8 * half;
-  f32x16_t acc = {};
-#pragma unroll
-  for (int s = 0; s < KS; ++s) acc = mfma_32x32x16(a[s], load_u16x8(erow + 16 * s), acc);
-  if (col == 0) {
-    float L[16];
-    tile_logits(acc, Urow, tok0, V, half, (V & 3) == 0, L);
-#pragma unroll
-    for (int j = 0; j < 16; ++j) Ls[tile_token(j, half)] = L[j];
-  }
-}
-
 // The Markov embedding row of the previous token, in the MFMA B-operand layout of a lane.
 template <int KS>
 __device__ __forceinline__ void load_e_row(u16x8_t (&e)[KS], const uint16_t* __restrict__ W1,
@@ -105,22 +81,46 @@ __device__ __forceinline__ void load_e_row(u16x8_t (&e)[KS], const uint16_t* __r
   for (int s = 0; s < KS; ++s) e[s] = load_u16x8(erow + 16 * s);
 }
 
-// recompute_tile with the embedding row already in registers.
+// Recompute the logits of one 32-token tile for one request with exactly the instruction
+// sequence of the streaming draft step (same k order, same operands; the request sits in every
+// MFMA column, and column placement does not change the result). Called by a whole wave; the
+// tile's U values are loaded together with the W2 tile. Lanes 0 and 32 hold the 32 logits,
+// which are written to Ls[0..32).
 template <int KS>
 __device__ void recompute_tile_e(const u16x8_t (&e)[KS], const uint16_t* __restrict__ W2t,
                                  const float* __restrict__ Urow, int tok0, int V, float* Ls) {
   const int lane = threadIdx.x & 63, half = lane >> 5, col = lane & 31;
   u16x8_t a[KS];
   load_w2_tile<KS>(a, W2t, tok0 + col, V, half);
+  float u[16];
+  const bool vec4 = (V & 3) == 0;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    float o[4];
+    load4(Urow, tok0 + 8 * g + 4 * half, V, vec4, o);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) u[4 * g + i] = o[i];
+  }
   f32x16_t acc = {};
 #pragma unroll
   for (int s = 0; s < KS; ++s) acc = mfma_32x32x16(a[s], e[s], acc);
   if (col == 0) {
-    float L[16];
-    tile_logits(acc, Urow, tok0, V, half, (V & 3) == 0, L);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) Ls[tile_token(j, half)] = L[j];
+    for (int j = 0; j < 16; ++j) {
+      const int v = tok0 + tile_token(j, half);
+      Ls[tile_token(j, half)] = (v < V) ? (u[j] + acc[j]) : kNegInf;
+    }
   }
+}
+
+// recompute_tile_e with the embedding row of `prevtok` loaded here.
+template <int KS>
+__device__ void recompute_tile(const uint16_t* __restrict__ W1, const uint16_t* __restrict__ W2t,
+                               const float* __restrict__ Urow, int32_t prevtok, int tok0, int V,
+                               float* Ls) {
+  u16x8_t e[KS];
+  load_e_row<KS>(e, W1, prevtok, (threadIdx.x & 63) >> 5);
+  recompute_tile_e<KS>(e, W2t, Urow, tok0, V, Ls);
 }
 
 // Walk one tile in ascending token order on one wave: lane j < 32 holds the mass w of token j
