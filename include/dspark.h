@@ -52,7 +52,7 @@ extern "C" {
 #endif
 
 /* Problem sizes. B requests, gamma draft positions, V vocabulary, r Markov rank, d hidden size
- * (d is read only by dspark_confidence). Supported: B >= 1, gamma >= 1, V >= 2,
+ * (d is read only by dspark_confidence). Supported: B >= 1, 1 <= gamma <= 255, 2 <= V <= 2^19,
  * r in {16, 32, 64, 128, 256, 512}, d % 8 == 0, B * (gamma + 1) <= 65535, and for
  * dspark_plan B * gamma <= 8192. */
 typedef struct dspark_dims {

@@ -28,7 +28,8 @@ bool rank_ok(int r) {
 // B * (gamma + 1) verified rows index grid dimension y of the target pass (<= 65535); the
 // planner sorts all B * gamma candidates in one workgroup's LDS (<= 8192).
 bool dims_ok(const dspark_dims& d) {
-  if (d.B < 1 || d.gamma < 1 || d.V < 2 || d.V > kMaxVocab || !rank_ok(d.r)) return false;
+  if (d.B < 1 || d.gamma < 1 || d.gamma > kMaxGamma || d.V < 2 || d.V > kMaxVocab || !rank_ok(d.r))
+    return false;
   if (static_cast<int64_t>(d.B) * (d.gamma + 1) > 65535) return false;
   return true;
 }

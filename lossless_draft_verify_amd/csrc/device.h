@@ -19,6 +19,7 @@ constexpr int kWave = 64;
 constexpr int kBlock = 256;          // threads per workgroup for the streaming kernels
 constexpr int kTileTokens = 32;      // tokens per MFMA tile = tokens per draft partial
 constexpr int kSegTokens = 4096;     // tokens per target-row segment
+constexpr int kMaxGamma = 255;       // draft positions per request (accept scan LDS)
 constexpr int kMaxVocab = 1 << 19;   // a sampler stages one row's tile partials in LDS (8 B each)
 constexpr float kNegInf = -__builtin_inff();
 

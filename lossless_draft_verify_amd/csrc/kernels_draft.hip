@@ -325,20 +325,27 @@ __global__ __launch_bounds__(kBlock) void confidence_kernel(ConfArgs p) {
   if (idx >= p.B * p.gamma) return;
   const int b = idx / p.gamma, k = idx % p.gamma;
   const int32_t prevtok = (k == 0) ? p.anchor[b] : p.tokens[static_cast<size_t>(b) * p.gamma + k - 1];
+  // Loads in batches of 8 pieces per lane (all in flight before the products), fp64 sum.
   double acc = 0.0;
   const uint16_t* hrow = p.h + static_cast<size_t>(idx) * p.d;
-  for (int i = lane * 8; i < p.d; i += 64 * 8) {
-    const u16x8_t hv = load_u16x8(hrow + i), wv = load_u16x8(p.w + i);
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      acc += static_cast<double>(bf16_to_f32(hv[e]) * bf16_to_f32(wv[e]));  // exact product
-  }
   const uint16_t* erow = p.W1 + static_cast<size_t>(prevtok) * p.r;
-  for (int i = lane * 8; i < p.r; i += 64 * 8) {
-    const u16x8_t ev = load_u16x8(erow + i), wv = load_u16x8(p.w + p.d + i);
+  const int n = p.d + p.r;               // pieces of 8: d/8 from h, r/8 from the embedding row
+  constexpr int kBatch = 8;
+  for (int i0 = lane * 8; i0 < n; i0 += 64 * 8 * kBatch) {
+    u16x8_t xv[kBatch], wv[kBatch];
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      acc += static_cast<double>(bf16_to_f32(ev[e]) * bf16_to_f32(wv[e]));
+    for (int q = 0; q < kBatch; ++q) {
+      const int i = min(i0 + q * 64 * 8, n - 8);
+      xv[q] = (i < p.d) ? load_u16x8(hrow + i) : load_u16x8(erow + (i - p.d));
+      wv[q] = load_u16x8(p.w + i);
+    }
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) {
+      if (i0 + q * 64 * 8 >= n) break;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        acc += static_cast<double>(bf16_to_f32(xv[q][e]) * bf16_to_f32(wv[q][e]));  // exact product
+    }
   }
   const double z = wave_sum(acc);
   if (lane == 0) {

@@ -42,7 +42,7 @@ __device__ __forceinline__ bool before(double ai, int ii, double aj, int ij) {
 __device__ void sorted_path(PlanSmem& sm, const float* __restrict__ conf, int B, int gamma) {
   const int tid = threadIdx.x;
   const int N = B * gamma;
-  int N2 = 1;
+  int N2 = kWave;                       // whole waves: the shuffle stages need full waves
   while (N2 < N) N2 <<= 1;
   for (int b = tid; b < B; b += kPlanThreads) {
     double prod = 1.0;
@@ -57,9 +57,12 @@ __device__ void sorted_path(PlanSmem& sm, const float* __restrict__ conf, int B,
     sm.idx[i] = INT_MAX;
   }
   __syncthreads();
-  // Bitonic sort into "before" order.
+  // Bitonic sort into "before" order. Stages with a stride of 64 or more exchange through LDS;
+  // the remaining stages of each merge stay inside a wave and use lane shuffles (element i
+  // lives in lane i % 64), so each merge costs one barrier for all of its short strides.
   for (int size = 2; size <= N2; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+    int stride = size >> 1;
+    for (; stride >= kWave; stride >>= 1) {
       for (int t = tid; t < N2 / 2; t += kPlanThreads) {
         const int i = 2 * t - (t & (stride - 1));
         const int j = i + stride;
@@ -76,6 +79,27 @@ __device__ void sorted_path(PlanSmem& sm, const float* __restrict__ conf, int B,
       }
       __syncthreads();
     }
+    for (int base = 0; base < N2; base += kPlanThreads) {
+      const int i = base + tid;
+      if (i < N2) {   // uniform per wave: N2 and base are multiples of 64
+        double a = sm.a[i];
+        int ix = sm.idx[i];
+        const bool up = (i & size) == 0;
+        for (int st = stride; st > 0; st >>= 1) {
+          const double pa = __shfl_xor(a, st, kWave);
+          const int pi = __shfl_xor(ix, st, kWave);
+          const bool lower = (i & st) == 0;
+          const bool other_first = before(pa, pi, a, ix);
+          if ((lower == up) ? other_first : !other_first) {
+            a = pa;
+            ix = pi;
+          }
+        }
+        sm.a[i] = a;
+        sm.idx[i] = ix;
+      }
+    }
+    __syncthreads();
   }
   // Inclusive prefix sums of the sorted survivals, plus B: a[i] <- tau_{i+1}.
   const int per = (N + kPlanThreads - 1) / kPlanThreads;

@@ -57,57 +57,77 @@ __global__ __launch_bounds__(kBlock) void target_stats_kernel(VerifyArgs p) {
   }
 }
 
-// log-sum-exp of one target row from its segment partials (whole wave; all lanes get it).
-__device__ double row_lse_wave(const VerifyArgs& p, int row, int lane) {
-  const size_t base = static_cast<size_t>(row) * p.nseg;
-  float m = kNegInf;
-  for (int s = lane; s < p.nseg; s += kWave) m = fmaxf(m, p.ws.seg_max[base + s]);
-  m = wave_max(m);
-  double z = 0.0;
-  for (int s = lane; s < p.nseg; s += kWave) z += partial_mass(p.ws.seg_max[base + s], p.ws.seg_sum[base + s], m);
-  z = wave_sum(z);
-  return static_cast<double>(m) + log(z);
-}
+// One wave per request. The log-sum-exp of all its verified rows and the accept-test inputs of
+// all its positions are loaded together (no dependent chain per position); lane k then tests
+// position k + 1 and the first failing lane, found with a ballot, is the first reject.
+constexpr int kAcceptRows = 16;    // rows reduced per batch (one batch when gamma < 16)
 
 __global__ __launch_bounds__(kBlock) void accept_kernel(VerifyArgs p) {
-  const int lane = threadIdx.x & 63;
-  const int b = blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);
+  __shared__ double lse_s[kBlock / 64][kMaxGamma + 1];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int b = blockIdx.x * (kBlock / 64) + w;
   if (b >= p.B) return;
   const int ell = p.draft_len[b];
   const int off = p.row_offsets[b];
   uint32_t fl = 0;
-  int accepted = 0, kind = kEmitBonus, epos = ell + 1, erow = off + ell;
-  double else_ = 0.0;
-  bool rejected = false;
-  for (int k = 1; k <= ell; ++k) {
-    const int row = off + k - 1;
-    const double l = row_lse_wave(p, row, lane);
-    if (!isfinite(l)) fl |= 1u;
-    const int32_t x = p.tokens[static_cast<size_t>(b) * p.gamma + k - 1];
-    const double pt = exp(static_cast<double>(p.target[static_cast<size_t>(row) * p.V + x]) - l);
-    const double u = static_cast<double>(p.uniforms[(static_cast<size_t>(b) * (p.gamma + 1) + k - 1) * 3 + 1]);
-    const double qk = static_cast<double>(p.q[static_cast<size_t>(b) * p.gamma + k - 1]);
-    if (u * qk < pt) {
-      ++accepted;
-    } else {
-      kind = kEmitResidual;
-      epos = k;
-      erow = row;
-      else_ = l;
-      rejected = true;
+  // 1. log-sum-exp of rows off .. off + ell (segments: lane + 64 i, i < 2, nseg <= 128).
+  for (int r0 = 0; r0 <= ell; r0 += kAcceptRows) {
+    float mx[kAcceptRows][2];
+    double sg[kAcceptRows][2];
+#pragma unroll
+    for (int r = 0; r < kAcceptRows; ++r)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int sgi = lane + 64 * i;
+        const bool valid = (r0 + r <= ell) && sgi < p.nseg;
+        const size_t o = static_cast<size_t>(off + min(r0 + r, ell)) * p.nseg + min(sgi, p.nseg - 1);
+        const float m0 = p.ws.seg_max[o];
+        const double s0 = p.ws.seg_sum[o];
+        mx[r][i] = valid ? m0 : kNegInf;
+        sg[r][i] = valid ? s0 : 0.0;
+      }
+#pragma unroll
+    for (int r = 0; r < kAcceptRows; ++r) {
+      if (r0 + r > ell) break;
+      const float M = wave_max(fmaxf(mx[r][0], mx[r][1]));
+      const double z = wave_sum(partial_mass(mx[r][0], sg[r][0], M) + partial_mass(mx[r][1], sg[r][1], M));
+      if (lane == 0) lse_s[w][r0 + r] = static_cast<double>(M) + log(z);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_wave_barrier();
+  // 2. accept tests, 64 positions per batch: lane k tests position k0 + k + 1.
+  int accepted = ell;
+  for (int k0 = 0; k0 < ell; k0 += 64) {
+    const int k = k0 + lane;
+    bool ok = true;
+    if (k < ell) {
+      const int row = off + k;
+      const int32_t x = p.tokens[static_cast<size_t>(b) * p.gamma + k];
+      const double l = lse_s[w][k];
+      const double pt = exp(static_cast<double>(p.target[static_cast<size_t>(row) * p.V + x]) - l);
+      const double u = static_cast<double>(p.uniforms[(static_cast<size_t>(b) * (p.gamma + 1) + k) * 3 + 1]);
+      const double qk = static_cast<double>(p.q[static_cast<size_t>(b) * p.gamma + k]);
+      ok = u * qk < pt;
+    }
+    const unsigned long long fail = __ballot(!ok);
+    if (fail) {
+      accepted = k0 + __ffsll(static_cast<long long>(fail)) - 1;
       break;
     }
   }
-  if (!rejected) {
-    else_ = row_lse_wave(p, erow, lane);
-    if (!isfinite(else_)) fl |= 1u;
-  }
+  // Rows tested before the first reject, and the emission row, feed the non-finite flag.
+  const bool rejected = accepted < ell;
+  const int last = rejected ? accepted : ell;    // 0-based row of the emission
+  for (int k = lane; k <= last; k += 64)
+    if (!isfinite(lse_s[w][k])) fl |= 1u;
+  fl = (__ballot(fl != 0u) != 0ull) ? 1u : 0u;
   if (lane == 0) {
     p.accept_len[b] = accepted;
-    p.ws.ekind[b] = kind;
-    p.ws.epos[b] = epos;
-    p.ws.erow[b] = erow;
-    p.ws.erow_lse[b] = else_;
+    p.ws.ekind[b] = rejected ? kEmitResidual : kEmitBonus;
+    p.ws.epos[b] = last + 1;
+    p.ws.erow[b] = off + last;
+    p.ws.erow_lse[b] = lse_s[w][last];
     p.ws.eflags[b] = fl;
   }
 }
