@@ -23,8 +23,10 @@
  *   - Argument checks run on the host, synchronously, before anything is enqueued; a failed
  *     check returns its status and enqueues nothing. A launch failure returns DSPARK_ERR_HIP.
  *     No C++ exception crosses this interface.
- *   - Pointers must be 16-byte aligned (DSPARK_ERR_ALIGN otherwise); bf16 tensors are passed
- *     as uint16_t bit patterns.
+ *   - Alignment (DSPARK_ERR_ALIGN otherwise): the bulk tensors that kernels read in 16-byte
+ *     vectors (U, target, W1, W2t, h, w) must be 16-byte aligned, the workspace 256-byte
+ *     aligned, and every other array aligned to its element size. bf16 tensors are passed as
+ *     uint16_t bit patterns.
  *   - Random draws are never generated inside the library: the caller passes
  *     uniforms [B][gamma+1][3] fp32 in [0,1), so a round is reproducible bit for bit.
  *     Component 0 of slot k-1 draws the draft token of position k; component 1 of slot k-1 is
