@@ -223,6 +223,202 @@ __global__ __launch_bounds__(kStepThreads, 1) void markov_step_kernel(StepArgs p
   }
 }
 
+// ---- Pipelined draft step: tiles copied into LDS by LDS-DMA loads ----------------------------
+//
+// One 256-thread workgroup per compute unit, on a persistent grid whose size is a multiple of
+// the number of 128-request groups, so every workgroup keeps one group for the whole launch.
+// Wave w owns requests 32w .. 32w+31 of the group and holds their embedding rows in registers
+// (the MFMA B operand) throughout. A work item is one 32-token tile: its 32 W2t rows and the
+// group's U block (128 request rows x 32 tokens, fp32) are copied from HBM into one of kStages
+// LDS stages by global_load_lds_dwordx4, which writes LDS directly and holds no registers, so
+// kStages - 1 items stay in flight while one is computed. Each wave then reads the W2 tile from
+// LDS as the MFMA A operand and its own U rows for the epilogue. Both blocks are XOR-swizzled
+// in 16-byte chunks (chunk c of row t is stored at c ^ (t & 7)), so the 32 rows one ds_read_b128
+// touches fall on distinct banks.
+//
+// The copies are awaited explicitly: s_waitcnt vmcnt(n) with n the number of copies this wave
+// issued after the awaited item, then s_barrier for the other waves' copies. No global store is
+// issued inside the pipelined loop (the partials collect in LDS and are written when the buffer
+// is full, followed by a full drain, and after the loop), so the vector-memory counter only
+// ever holds copies, in issue order.
+constexpr int kDmaThreads = 256;
+constexpr int kDmaGroup = 128;   // requests per group: 4 waves x 32
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Copy 16 bytes per lane from global memory into LDS at byte address lds + 16 * lane (lds
+// wave-uniform). Written as inline asm so that the compiler does not see an LDS-DMA write: it
+// tracks those only coarsely and would put a full vmcnt(0) wait (every copy in flight) before
+// each LDS read it cannot tell apart from the copies. The kernel orders copies and reads itself:
+// wait_copies<n>() + s_barrier before a stage is read, lds_barrier() before it is overwritten;
+// the "memory" clobbers keep the compiler's LDS reads between those points.
+__device__ __forceinline__ void copy16_to_lds(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds)
+               : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void*)p));
+}
+
+template <int N>
+__device__ __forceinline__ void wait_copies() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+
+template <int KS>
+struct DmaStep {
+  static constexpr int r = 16 * KS;
+  static constexpr int kW2Chunks = 2 * KS;                          // 16-byte chunks per row
+  static constexpr int kW2Bytes = kTileTokens * kW2Chunks * 16;     // 32 W2t rows
+  static constexpr int kUChunks = kTileTokens / 4;                  // 8 per U row segment
+  static constexpr int kUBytes = kDmaGroup * kUChunks * 16;         // 16 KB
+  static constexpr int kStageBytes = kW2Bytes + kUBytes;
+  static constexpr int kStages = (KS >= 32) ? 3 : 4;
+  static constexpr int kPartItems = (KS >= 32) ? 8 : 16;           // items of partials in LDS
+  static constexpr int kW2Copies = kW2Bytes / 1024 / 4;             // copies per wave per item
+  static constexpr int kUCopies = kUBytes / 1024 / 4;
+  static constexpr int kCopies = kW2Copies + kUCopies;
+  static_assert(KS >= 4, "the W2 tile needs at least one 1 KB copy per wave");
+  static_assert((kStages - 1) * kCopies <= 63, "vmcnt range");
+};
+
+template <int KS>
+__global__ __launch_bounds__(kDmaThreads, 1) void markov_step_dma_kernel(StepArgs p) {
+  using D = DmaStep<KS>;
+  __shared__ __attribute__((aligned(1024))) unsigned char stage[D::kStages * D::kStageBytes];
+  __shared__ float2 pbuf[D::kPartItems * kDmaGroup];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5, col = lane & 31;
+  const int ngroups = (p.B + kDmaGroup - 1) / kDmaGroup;
+  const int group = blockIdx.x % ngroups;
+  const int tile0 = blockIdx.x / ngroups, tstep = gridDim.x / ngroups;
+  const int n = (tile0 < p.ntiles) ? (p.ntiles - tile0 + tstep - 1) / tstep : 0;
+  if (n == 0) return;
+  const int row_own = 32 * wave + col;                  // request row within the group
+  const bool wave_active = group * kDmaGroup + 32 * wave < p.B;
+
+  // Embedding rows of this lane's request (rows past B repeat row B-1 and are never stored).
+  u16x8_t e[KS];
+  {
+    const int b = min(group * kDmaGroup + row_own, p.B - 1);
+    load_e_row<KS>(e, p.W1, p.prev[static_cast<size_t>(b) * p.prev_stride], half);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) asm volatile("" ::"v"(e[s]));   // complete before the copies
+  }
+
+  // Per-lane LDS offsets of the A-operand chunks (k-steps s = 4i + t use a_off[t] + 128 i)
+  // and of this lane's four U chunks.
+  const uint32_t stage_addr = lds_addr(stage);
+  uint32_t a_off[4], u_off[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    a_off[t] = 16 * (col * D::kW2Chunks + ((2 * t + half) ^ (col & 7)));
+    u_off[t] = D::kW2Bytes + 16 * (row_own * D::kUChunks + ((2 * t + half) ^ (row_own & 7)));
+  }
+
+  // This wave's share of item j's copies into stage j % kStages. Rows past V or B are clamped
+  // to the last valid one (all addresses stay inside the tensors); the epilogue masks them.
+  auto issue = [&](int j) {
+    const int tok0 = (tile0 + j * tstep) * kTileTokens;
+    const uint32_t base = stage_addr + (j % D::kStages) * D::kStageBytes;
+#pragma unroll
+    for (int i = 0; i < D::kW2Copies; ++i) {
+      const int q = wave * D::kW2Copies + i;
+      const int slot = 64 * q + lane;
+      const int row = slot / D::kW2Chunks;
+      const int c = (slot % D::kW2Chunks) ^ (row & 7);
+      const int tok = min(tok0 + row, p.V - 1);
+      copy16_to_lds(p.W2t + static_cast<size_t>(tok) * D::r + 8 * c, base + 1024 * q);
+    }
+#pragma unroll
+    for (int i = 0; i < D::kUCopies; ++i) {
+      const int q = wave * D::kUCopies + i;
+      const int slot = 64 * q + lane;
+      const int row = slot / D::kUChunks;
+      const int c = (slot % D::kUChunks) ^ (row & 7);
+      const int b = min(group * kDmaGroup + row, p.B - 1);
+      const int v = min(tok0 + 4 * c, p.V - 4);
+      copy16_to_lds(p.U + (static_cast<size_t>(b) * p.gamma + p.k) * p.V + v,
+                    base + D::kW2Bytes + 1024 * q);
+    }
+  };
+
+  // Partials of items j0 .. j1-1 held by this wave, to global memory.
+  auto flush = [&](int j0, int j1) {
+    const int cnt = (j1 - j0) * 32;
+    for (int x = lane; x < cnt; x += 64) {
+      const int j = j0 + x / 32, row = 32 * wave + x % 32;
+      const int b = group * kDmaGroup + row;
+      if (b < p.B)
+        p.part[static_cast<size_t>(b) * p.ntiles + tile0 + j * tstep] =
+            pbuf[(j % D::kPartItems) * kDmaGroup + row];
+    }
+  };
+
+  const int pre = min(D::kStages - 1, n);
+  for (int j = 0; j < pre; ++j) issue(j);
+  int flushed = 0;
+  for (int j = 0; j < n; ++j) {
+    if (j + D::kStages - 1 < n) issue(j + D::kStages - 1);
+    const int ahead = min(D::kStages - 1, n - 1 - j);
+    if (ahead >= 3) wait_copies<3 * D::kCopies>();
+    else if (ahead == 2) wait_copies<2 * D::kCopies>();
+    else if (ahead == 1) wait_copies<D::kCopies>();
+    else wait_copies<0>();
+    asm volatile("s_barrier" ::: "memory");
+
+    if (wave_active) {
+      const unsigned char* base = stage + (j % D::kStages) * D::kStageBytes;
+      // A operand: chunk 2s + half of W2t row `col`; U: chunks 2g + half of request row_own.
+      u16x8_t a[KS];
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        a[s] = *reinterpret_cast<const u16x8_t*>(base + 128 * (s >> 2) + a_off[s & 3]);
+      float4 uu[4];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) uu[g] = *reinterpret_cast<const float4*>(base + u_off[g]);
+      f32x16_t acc = {};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) acc = mfma_32x32x16(a[s], e[s], acc);
+      // Epilogue: L = U + bias, tile max, fp32 sum of exp(L - max) (the order of the
+      // non-pipelined step kernel, so both give the same partials bit for bit).
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        acc[4 * g + 0] += uu[g].x;
+        acc[4 * g + 1] += uu[g].y;
+        acc[4 * g + 2] += uu[g].z;
+        acc[4 * g + 3] += uu[g].w;
+      }
+      const int tok0 = (tile0 + j * tstep) * kTileTokens;
+      if (tok0 + kTileTokens > p.V) {
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj)
+          if (tok0 + tile_token(jj, half) >= p.V) acc[jj] = kNegInf;
+      }
+      float L[16];
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) L[jj] = acc[jj];
+      float m = max16(L);
+      m = fmaxf(m, __shfl_xor(m, 32, kWave));
+      float t[16];
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) t[jj] = exp_term(L[jj] - m);
+      float sm = (m == kNegInf) ? 0.0f : sum16(t);
+      sm = sm + __shfl_xor(sm, 32, kWave);
+      if (half == 0) pbuf[(j % D::kPartItems) * kDmaGroup + row_own] = make_float2(m, sm);
+    }
+    lds_barrier();   // stage j % kStages is free for item j + kStages
+    if ((j + 1) % D::kPartItems == 0 && j + 1 < n) {
+      flush(flushed, j + 1);
+      flushed = j + 1;
+      wait_copies<0>();   // the stores join the counter: drain it so later counts hold copies only
+    }
+  }
+  flush(flushed, n);
+}
+
 // One workgroup per request: the row's tile partials are staged in LDS (converted in place to
 // fp64 masses relative to the row max), located with a block scan, and the chosen tile is
 // recomputed and walked on wave 0.
@@ -357,7 +553,22 @@ __global__ __launch_bounds__(kBlock) void confidence_kernel(ConfArgs p) {
 }  // namespace
 
 template <int KS>
+static hipError_t launch_step_dma(const StepArgs& a, hipStream_t s) {
+  const int ngroups = (a.B + kDmaGroup - 1) / kDmaGroup;
+  const int per = a.persistent_wgs / ngroups;
+  const int grid = (per > 0 ? per : 1) * ngroups;
+  hipLaunchKernelGGL(markov_step_dma_kernel<KS>, dim3(grid), dim3(kDmaThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int KS>
 static hipError_t launch_step_ks(const StepArgs& a, hipStream_t s) {
+  // The pipelined kernel copies 16-byte U chunks (rows 16-byte aligned: V % 4 == 0) and at
+  // least one 1 KB W2 copy per wave (r >= 64); the debug-logits output would put global stores
+  // inside its copy pipeline, so that request takes the register-prefetch kernel.
+  if constexpr (KS >= 4) {
+    if (a.dbg == nullptr && (a.V & 3) == 0) return launch_step_dma<KS>(a, s);
+  }
   const int items = ((a.V + 4 * kTileTokens - 1) / (4 * kTileTokens)) *
                     ((a.B + StepCfg<KS>::kBG - 1) / StepCfg<KS>::kBG);
   const int grid = items < a.persistent_wgs ? items : a.persistent_wgs;

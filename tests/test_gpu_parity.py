@@ -40,7 +40,22 @@ DRAFT_CASES = {
     "b7-v3000-r512-g2": _custom("b7-v3000-r512-g2", seed_id=13, B=7, V=3000, r=512, gamma=2,
                                 w_std=0.03),
     "b5-v2-r16-g3": _custom("b5-v2-r16-g3", seed_id=14, B=5, V=2, r=16, gamma=3),
+    # cases the pipelined (LDS-copy) step kernel takes (V % 4 == 0, r >= 64): two groups with a
+    # ragged second one, a 4-token tail tile, r = 64 / 128, and a batch below one wave's 32
+    "b130-v4100-r128-g3": _custom("b130-v4100-r128-g3", seed_id=15, B=130, V=4100, r=128,
+                                  u_std=3.0, w_std=0.05),
+    "b33-v2052-r64-g4": _custom("b33-v2052-r64-g4", seed_id=16, B=33, V=2052, r=64, gamma=4),
+    "b20-v8192-r256-g2": _custom("b20-v8192-r256-g2", seed_id=17, B=20, V=8192, r=256, gamma=2,
+                                 u_std=3.0, w_std=0.05),
 }
+
+
+def _forced_without_debug_matches(wl, inp, wts, g, force):
+    """The step kernel without a debug output (the pipelined one wherever it applies) must give
+    the same draws, q and lse, bit for bit, as the debug-output run g under the same forcing."""
+    gn = gpu_draft(wl, inp, wts, force=force)
+    for k in ("tokens", "q", "lse"):
+        assert np.array_equal(gn[k], g[k]), k
 
 
 @pytest.mark.parametrize("name", list(DRAFT_CASES))
@@ -54,6 +69,7 @@ def test_draft_parity(name):
     c = MismatchCounter(f"draft {name}")
     err = compare_draft(g, o, c)
     log(f"  logits max err {err:.2e}; {c.report()}")
+    _forced_without_debug_matches(wl, inp, wts, g, o["tokens"])
     # unforced GPU run: identical to the forced one wherever the draws agree
     gu = gpu_draft(wl, inp, wts)
     same = (gu["tokens"] == o["tokens"]).all(axis=1)
@@ -231,6 +247,7 @@ def test_round_full_size(name):
     c.add(gu["tokens"][:, :1], o["tokens"][:, :1], o["margin"][:, :1])
     g = gpu_draft(wl, inp, wts, force=o["tokens"], dbg=True)
     err = compare_draft(g, o, c)
+    _forced_without_debug_matches(wl, inp, wts, g, o["tokens"])
     log(f"  draft: logits err {err:.2e}; {c.report()}")
     T = lambda a, dt=torch.int32: torch.as_tensor(np.ascontiguousarray(a), dtype=dt, device=DEV)
     tok_o = T(o["tokens"])
