@@ -225,24 +225,25 @@ __global__ __launch_bounds__(kStepThreads, 1) void markov_step_kernel(StepArgs p
 
 // ---- Pipelined draft step: tiles copied into LDS by LDS-DMA loads ----------------------------
 //
-// One 256-thread workgroup per compute unit, on a persistent grid whose size is a multiple of
+// One 512-thread workgroup per compute unit, on a persistent grid whose size is a multiple of
 // the number of 128-request groups, so every workgroup keeps one group for the whole launch.
-// Wave w owns requests 32w .. 32w+31 of the group and holds their embedding rows in registers
-// (the MFMA B operand) throughout. A work item is one 32-token tile: its 32 W2t rows and the
-// group's U block (128 request rows x 32 tokens, fp32) are copied from HBM into one of kStages
-// LDS stages by global_load_lds_dwordx4, which writes LDS directly and holds no registers, so
-// kStages - 1 items stay in flight while one is computed. Each wave then reads the W2 tile from
-// LDS as the MFMA A operand and its own U rows for the epilogue. Both blocks are XOR-swizzled
-// in 16-byte chunks (chunk c of row t is stored at c ^ (t & 7)), so the 32 rows one ds_read_b128
-// touches fall on distinct banks.
+// A work item is 64 tokens (two 32-token tiles): its 64 W2t rows and the group's U block
+// (128 request rows x 64 tokens, fp32) are copied from HBM into one of two LDS stages by
+// global_load_lds_dwordx4, which writes LDS directly and holds no registers, so the next item
+// is in flight while one is computed. Wave w computes tile w / 4 of the item for requests
+// 32 (w % 4) .. +32, whose embedding rows (the MFMA B operand) it holds in registers for the
+// whole launch; each SIMD runs two waves. Both LDS blocks are XOR-swizzled in 16-byte chunks
+// (chunk c of row t is stored at c ^ (t & 15)), so the rows one ds_read_b128 touches fall on
+// distinct banks.
 //
 // The copies are awaited explicitly: s_waitcnt vmcnt(n) with n the number of copies this wave
 // issued after the awaited item, then s_barrier for the other waves' copies. No global store is
 // issued inside the pipelined loop (the partials collect in LDS and are written when the buffer
 // is full, followed by a full drain, and after the loop), so the vector-memory counter only
 // ever holds copies, in issue order.
-constexpr int kDmaThreads = 256;
-constexpr int kDmaGroup = 128;   // requests per group: 4 waves x 32
+constexpr int kDmaThreads = 512;
+constexpr int kDmaGroup = 128;   // requests per group: 4 waves x 32 per tile
+constexpr int kDmaTiles = 2;     // 32-token tiles per item
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -265,21 +266,31 @@ __device__ __forceinline__ void wait_copies() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Value of lane l ^ 32 (v_permlane32_swap exchanges the two half-waves).
+__device__ __forceinline__ float other_half(float x, int half) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(half ? r[0] : r[1]);
+}
 
 template <int KS>
 struct DmaStep {
   static constexpr int r = 16 * KS;
+  static constexpr int kTok = kDmaTiles * kTileTokens;              // 64 tokens per item
   static constexpr int kW2Chunks = 2 * KS;                          // 16-byte chunks per row
-  static constexpr int kW2Bytes = kTileTokens * kW2Chunks * 16;     // 32 W2t rows
-  static constexpr int kUChunks = kTileTokens / 4;                  // 8 per U row segment
-  static constexpr int kUBytes = kDmaGroup * kUChunks * 16;         // 16 KB
+  static constexpr int kW2Bytes = kTok * kW2Chunks * 16;            // 64 W2t rows
+  static constexpr int kUChunks = kTok / 4;                         // 16 per U row segment
+  static constexpr int kUBytes = kDmaGroup * kUChunks * 16;         // 32 KB
   static constexpr int kStageBytes = kW2Bytes + kUBytes;
-  static constexpr int kStages = (KS >= 32) ? 3 : 4;
-  static constexpr int kPartItems = (KS >= 32) ? 8 : 16;           // items of partials in LDS
-  static constexpr int kW2Copies = kW2Bytes / 1024 / 4;             // copies per wave per item
-  static constexpr int kUCopies = kUBytes / 1024 / 4;
+  static constexpr int kStages = 2;
+  static constexpr int kPartItems = 8;                              // items of partials in LDS
+  static constexpr int kWaves = kDmaThreads / 64;
+  static constexpr int kW2Copies = kW2Bytes / 1024 / kWaves;        // copies per wave per item
+  static constexpr int kUCopies = kUBytes / 1024 / kWaves;
   static constexpr int kCopies = kW2Copies + kUCopies;
-  static_assert(KS >= 4, "the W2 tile needs at least one 1 KB copy per wave");
+  static constexpr int kW2Swz = (kW2Chunks >= 16) ? 15 : kW2Chunks - 1;   // W2 swizzle mask
+  static constexpr int kAOffs = (KS < 8) ? KS : 8;                   // distinct lane offsets
+  static_assert(KS >= 4 && KS <= 16, "one to four 1 KB W2 copies per wave per item");
   static_assert((kStages - 1) * kCopies <= 63, "vmcnt range");
 };
 
@@ -287,48 +298,51 @@ template <int KS>
 __global__ __launch_bounds__(kDmaThreads, 1) void markov_step_dma_kernel(StepArgs p) {
   using D = DmaStep<KS>;
   __shared__ __attribute__((aligned(1024))) unsigned char stage[D::kStages * D::kStageBytes];
-  __shared__ float2 pbuf[D::kPartItems * kDmaGroup];
+  __shared__ float2 pbuf[D::kPartItems * kDmaTiles * kDmaGroup];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, col = lane & 31;
+  const int sub = wave >> 2, rq = wave & 3;             // tile within the item, request quarter
+  // Workgroup w of a group takes a contiguous range of items, so that the partials of one
+  // request that it produces are contiguous in memory (full-line writes).
   const int ngroups = (p.B + kDmaGroup - 1) / kDmaGroup;
   const int group = blockIdx.x % ngroups;
-  const int tile0 = blockIdx.x / ngroups, tstep = gridDim.x / ngroups;
-  const int n = (tile0 < p.ntiles) ? (p.ntiles - tile0 + tstep - 1) / tstep : 0;
-  if (n == 0) return;
-  const int row_own = 32 * wave + col;                  // request row within the group
-  const bool wave_active = group * kDmaGroup + 32 * wave < p.B;
+  const int wg = blockIdx.x / ngroups, nwg = gridDim.x / ngroups;
+  const int nitems = (p.V + D::kTok - 1) / D::kTok;
+  const int item_lo = static_cast<int>(static_cast<int64_t>(nitems) * wg / nwg);
+  const int n = static_cast<int>(static_cast<int64_t>(nitems) * (wg + 1) / nwg) - item_lo;
+  if (n <= 0) return;
+  const int row_own = 32 * rq + col;                    // request row within the group
+  const bool wave_active = group * kDmaGroup + 32 * rq < p.B;
+  const int32_t prevtok =
+      p.prev[static_cast<size_t>(min(group * kDmaGroup + row_own, p.B - 1)) * p.prev_stride];
 
-  // Embedding rows of this lane's request (rows past B repeat row B-1 and are never stored).
-  u16x8_t e[KS];
-  {
-    const int b = min(group * kDmaGroup + row_own, p.B - 1);
-    load_e_row<KS>(e, p.W1, p.prev[static_cast<size_t>(b) * p.prev_stride], half);
-#pragma unroll
-    for (int s = 0; s < KS; ++s) asm volatile("" ::"v"(e[s]));   // complete before the copies
-  }
-
-  // Per-lane LDS offsets of the A-operand chunks (k-steps s = 4i + t use a_off[t] + 128 i)
-  // and of this lane's four U chunks.
+  // Per-lane LDS offsets: k-step s of the A operand (W2t row 32 sub + col, chunk 2s + half) is
+  // at a_off[s % 8] + 256 (s / 8); U chunk 8 sub + 2g + half of row row_own at u_off[g].
   const uint32_t stage_addr = lds_addr(stage);
-  uint32_t a_off[4], u_off[4];
+  uint32_t a_off[D::kAOffs], u_off[4];
+  {
+    const int wrow = 32 * sub + col;
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    a_off[t] = 16 * (col * D::kW2Chunks + ((2 * t + half) ^ (col & 7)));
-    u_off[t] = D::kW2Bytes + 16 * (row_own * D::kUChunks + ((2 * t + half) ^ (row_own & 7)));
+    for (int t = 0; t < D::kAOffs; ++t)
+      a_off[t] = 16 * (wrow * D::kW2Chunks + ((2 * t + half) ^ (wrow & D::kW2Swz)));
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      u_off[g] = D::kW2Bytes +
+                 16 * (row_own * D::kUChunks + ((8 * sub + 2 * g + half) ^ (row_own & 15)));
   }
 
   // This wave's share of item j's copies into stage j % kStages. Rows past V or B are clamped
   // to the last valid one (all addresses stay inside the tensors); the epilogue masks them.
   auto issue = [&](int j) {
-    const int tok0 = (tile0 + j * tstep) * kTileTokens;
+    const int tok0 = (item_lo + j) * D::kTok;
     const uint32_t base = stage_addr + (j % D::kStages) * D::kStageBytes;
 #pragma unroll
     for (int i = 0; i < D::kW2Copies; ++i) {
       const int q = wave * D::kW2Copies + i;
       const int slot = 64 * q + lane;
       const int row = slot / D::kW2Chunks;
-      const int c = (slot % D::kW2Chunks) ^ (row & 7);
+      const int c = (slot % D::kW2Chunks) ^ (row & D::kW2Swz);
       const int tok = min(tok0 + row, p.V - 1);
       copy16_to_lds(p.W2t + static_cast<size_t>(tok) * D::r + 8 * c, base + 1024 * q);
     }
@@ -337,7 +351,7 @@ __global__ __launch_bounds__(kDmaThreads, 1) void markov_step_dma_kernel(StepArg
       const int q = wave * D::kUCopies + i;
       const int slot = 64 * q + lane;
       const int row = slot / D::kUChunks;
-      const int c = (slot % D::kUChunks) ^ (row & 7);
+      const int c = (slot % D::kUChunks) ^ (row & 15);
       const int b = min(group * kDmaGroup + row, p.B - 1);
       const int v = min(tok0 + 4 * c, p.V - 4);
       copy16_to_lds(p.U + (static_cast<size_t>(b) * p.gamma + p.k) * p.V + v,
@@ -345,37 +359,45 @@ __global__ __launch_bounds__(kDmaThreads, 1) void markov_step_dma_kernel(StepArg
     }
   };
 
-  // Partials of items j0 .. j1-1 held by this wave, to global memory.
+  // Partials of items j0 .. j1-1 (after a barrier), to global memory by the whole workgroup:
+  // consecutive threads take consecutive tiles of one request, so the stores fill whole lines.
   auto flush = [&](int j0, int j1) {
-    const int cnt = (j1 - j0) * 32;
-    for (int x = lane; x < cnt; x += 64) {
-      const int j = j0 + x / 32, row = 32 * wave + x % 32;
+    const int per = (j1 - j0) * kDmaTiles;
+    for (int x = tid; x < kDmaGroup * per; x += kDmaThreads) {
+      const int row = x / per, tt = x % per;
+      const int j = j0 + tt / kDmaTiles;
       const int b = group * kDmaGroup + row;
-      if (b < p.B)
-        p.part[static_cast<size_t>(b) * p.ntiles + tile0 + j * tstep] =
-            pbuf[(j % D::kPartItems) * kDmaGroup + row];
+      const int tile = (item_lo + j0) * kDmaTiles + tt;
+      if (b < p.B && tile < p.ntiles)
+        p.part[static_cast<size_t>(b) * p.ntiles + tile] =
+            pbuf[((j % D::kPartItems) * kDmaTiles + tt % kDmaTiles) * kDmaGroup + row];
     }
   };
 
-  const int pre = min(D::kStages - 1, n);
-  for (int j = 0; j < pre; ++j) issue(j);
+  // The first item's copies go out before the embedding rows are gathered (the gather waits
+  // for the request's previous token), so the two latencies overlap.
+  issue(0);
+  u16x8_t e[KS];
+  load_e_row<KS>(e, p.W1, prevtok, half);
+#pragma unroll
+  for (int s = 0; s < KS; ++s) asm volatile("" ::"v"(e[s]));   // rows in registers from here
   int flushed = 0;
   for (int j = 0; j < n; ++j) {
-    if (j + D::kStages - 1 < n) issue(j + D::kStages - 1);
-    const int ahead = min(D::kStages - 1, n - 1 - j);
-    if (ahead >= 3) wait_copies<3 * D::kCopies>();
-    else if (ahead == 2) wait_copies<2 * D::kCopies>();
-    else if (ahead == 1) wait_copies<D::kCopies>();
-    else wait_copies<0>();
+    if (j + 1 < n) {
+      issue(j + 1);
+      wait_copies<D::kCopies>();
+    } else {
+      wait_copies<0>();
+    }
     asm volatile("s_barrier" ::: "memory");
 
-    if (wave_active) {
+    const int tok0 = (item_lo + j) * D::kTok + sub * kTileTokens;
+    if (wave_active && tok0 < p.V) {
       const unsigned char* base = stage + (j % D::kStages) * D::kStageBytes;
-      // A operand: chunk 2s + half of W2t row `col`; U: chunks 2g + half of request row_own.
       u16x8_t a[KS];
 #pragma unroll
       for (int s = 0; s < KS; ++s)
-        a[s] = *reinterpret_cast<const u16x8_t*>(base + 128 * (s >> 2) + a_off[s & 3]);
+        a[s] = *reinterpret_cast<const u16x8_t*>(base + 256 * (s >> 3) + a_off[s % D::kAOffs]);
       float4 uu[4];
 #pragma unroll
       for (int g = 0; g < 4; ++g) uu[g] = *reinterpret_cast<const float4*>(base + u_off[g]);
@@ -383,7 +405,7 @@ __global__ __launch_bounds__(kDmaThreads, 1) void markov_step_dma_kernel(StepArg
 #pragma unroll
       for (int s = 0; s < KS; ++s) acc = mfma_32x32x16(a[s], e[s], acc);
       // Epilogue: L = U + bias, tile max, fp32 sum of exp(L - max) (the order of the
-      // non-pipelined step kernel, so both give the same partials bit for bit).
+      // register-prefetch step kernel, so both give the same partials bit for bit).
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         acc[4 * g + 0] += uu[g].x;
@@ -391,7 +413,6 @@ __global__ __launch_bounds__(kDmaThreads, 1) void markov_step_dma_kernel(StepArg
         acc[4 * g + 2] += uu[g].z;
         acc[4 * g + 3] += uu[g].w;
       }
-      const int tok0 = (tile0 + j * tstep) * kTileTokens;
       if (tok0 + kTileTokens > p.V) {
 #pragma unroll
         for (int jj = 0; jj < 16; ++jj)
@@ -401,13 +422,14 @@ __global__ __launch_bounds__(kDmaThreads, 1) void markov_step_dma_kernel(StepArg
 #pragma unroll
       for (int jj = 0; jj < 16; ++jj) L[jj] = acc[jj];
       float m = max16(L);
-      m = fmaxf(m, __shfl_xor(m, 32, kWave));
+      m = fmaxf(m, other_half(m, half));
       float t[16];
 #pragma unroll
       for (int jj = 0; jj < 16; ++jj) t[jj] = exp_term(L[jj] - m);
       float sm = (m == kNegInf) ? 0.0f : sum16(t);
-      sm = sm + __shfl_xor(sm, 32, kWave);
-      if (half == 0) pbuf[(j % D::kPartItems) * kDmaGroup + row_own] = make_float2(m, sm);
+      sm = sm + other_half(sm, half);
+      if (half == 0)
+        pbuf[((j % D::kPartItems) * kDmaTiles + sub) * kDmaGroup + row_own] = make_float2(m, sm);
     }
     lds_barrier();   // stage j % kStages is free for item j + kStages
     if ((j + 1) % D::kPartItems == 0 && j + 1 < n) {
@@ -563,10 +585,11 @@ static hipError_t launch_step_dma(const StepArgs& a, hipStream_t s) {
 
 template <int KS>
 static hipError_t launch_step_ks(const StepArgs& a, hipStream_t s) {
-  // The pipelined kernel copies 16-byte U chunks (rows 16-byte aligned: V % 4 == 0) and at
-  // least one 1 KB W2 copy per wave (r >= 64); the debug-logits output would put global stores
-  // inside its copy pipeline, so that request takes the register-prefetch kernel.
-  if constexpr (KS >= 4) {
+  // The pipelined kernel copies 16-byte U chunks (rows 16-byte aligned: V % 4 == 0), one to four
+  // 1 KB W2 copies per wave (64 <= r <= 256; two r = 512 stages would not fit in LDS), and the
+  // debug-logits output would put global stores inside its copy pipeline: other requests take
+  // the register-prefetch kernel.
+  if constexpr (KS >= 4 && KS <= 16) {
     if (a.dbg == nullptr && (a.V & 3) == 0) return launch_step_dma<KS>(a, s);
   }
   const int items = ((a.V + 4 * kTileTokens - 1) / (4 * kTileTokens)) *
