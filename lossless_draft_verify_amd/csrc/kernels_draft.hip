@@ -288,6 +288,8 @@ struct DmaStep {
   static constexpr int kW2Copies = kW2Bytes / 1024 / kWaves;        // copies per wave per item
   static constexpr int kUCopies = kUBytes / 1024 / kWaves;
   static constexpr int kCopies = kW2Copies + kUCopies;
+  static constexpr int kECopies = kDmaGroup * kW2Chunks * 16 / 1024 / kWaves;   // embedding rows
+  static_assert(kDmaGroup * kW2Chunks * 16 <= kStageBytes, "embedding rows fit in one stage");
   static constexpr int kW2Swz = (kW2Chunks >= 16) ? 15 : kW2Chunks - 1;   // W2 swizzle mask
   static constexpr int kAOffs = (KS < 8) ? KS : 8;                   // distinct lane offsets
   static_assert(KS >= 4 && KS <= 16, "one to four 1 KB W2 copies per wave per item");
@@ -299,6 +301,7 @@ __global__ __launch_bounds__(kDmaThreads, 1) void markov_step_dma_kernel(StepArg
   using D = DmaStep<KS>;
   __shared__ __attribute__((aligned(1024))) unsigned char stage[D::kStages * D::kStageBytes];
   __shared__ float2 pbuf[D::kPartItems * kDmaTiles * kDmaGroup];
+  __shared__ __attribute__((aligned(256))) int32_t pid[kDmaGroup];   // previous tokens
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, col = lane & 31;
@@ -314,8 +317,6 @@ __global__ __launch_bounds__(kDmaThreads, 1) void markov_step_dma_kernel(StepArg
   if (n <= 0) return;
   const int row_own = 32 * rq + col;                    // request row within the group
   const bool wave_active = group * kDmaGroup + 32 * rq < p.B;
-  const int32_t prevtok =
-      p.prev[static_cast<size_t>(min(group * kDmaGroup + row_own, p.B - 1)) * p.prev_stride];
 
   // Per-lane LDS offsets: k-step s of the A operand (W2t row 32 sub + col, chunk 2s + half) is
   // at a_off[s % 8] + 256 (s / 8); U chunk 8 sub + 2g + half of row row_own at u_off[g].
@@ -374,13 +375,40 @@ __global__ __launch_bounds__(kDmaThreads, 1) void markov_step_dma_kernel(StepArg
     }
   };
 
-  // The first item's copies go out before the embedding rows are gathered (the gather waits
-  // for the request's previous token), so the two latencies overlap.
-  issue(0);
-  u16x8_t e[KS];
-  load_e_row<KS>(e, p.W1, prevtok, half);
+  // Prologue, all copies: the group's previous tokens into LDS; then the embedding rows
+  // W1[prev] (each row once per workgroup, swizzled like W2t) into stage 1, with item 0 behind
+  // them into stage 0; each wave reads its rows into registers and releases stage 1.
+  if (wave < kDmaGroup / 64) {
+    const int b = min(group * kDmaGroup + 64 * wave + lane, p.B - 1);
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
+                 ::"v"(p.prev + static_cast<size_t>(b) * p.prev_stride),
+                 "s"(lds_addr(pid) + 256 * wave) : "memory", "m0");
+  }
+  wait_copies<0>();
+  asm volatile("s_barrier" ::: "memory");
+  {
+    const uint32_t ebase = stage_addr + D::kStageBytes;
 #pragma unroll
-  for (int s = 0; s < KS; ++s) asm volatile("" ::"v"(e[s]));   // rows in registers from here
+    for (int i = 0; i < D::kECopies; ++i) {
+      const int q = wave * D::kECopies + i;
+      const int slot = 64 * q + lane;
+      const int row = slot / D::kW2Chunks;
+      const int c = (slot % D::kW2Chunks) ^ (row & D::kW2Swz);
+      copy16_to_lds(p.W1 + static_cast<size_t>(pid[row]) * D::r + 8 * c, ebase + 1024 * q);
+    }
+  }
+  issue(0);
+  wait_copies<D::kCopies>();                  // the embedding rows (item 0 may be in flight)
+  asm volatile("s_barrier" ::: "memory");
+  u16x8_t e[KS];
+  {
+    const unsigned char* eb = stage + D::kStageBytes;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      e[s] = *reinterpret_cast<const u16x8_t*>(
+          eb + 16 * (row_own * D::kW2Chunks + ((2 * s + half) ^ (row_own & D::kW2Swz))));
+  }
+  lds_barrier();                              // stage 1 is free for item 1
   int flushed = 0;
   for (int j = 0; j < n; ++j) {
     if (j + 1 < n) {
