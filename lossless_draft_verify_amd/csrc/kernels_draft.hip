@@ -469,15 +469,29 @@ __global__ __launch_bounds__(kDmaThreads, 1) void markov_step_dma_kernel(StepArg
   flush(flushed, n);
 }
 
-// One workgroup per request: the row's tile partials are staged in LDS (converted in place to
-// fp64 masses relative to the row max), located with a block scan, and the chosen tile is
-// recomputed and walked on wave 0.
+// One 1024-thread workgroup per request. Thread t holds a contiguous range of at most 16 tile
+// partials (V <= 2^19) in registers: the row max comes from a block reduction, the tile masses
+// exp(m - M) * s (fp32 exponential, fp64 product) from registers, and a block scan of the
+// per-thread sums finds the thread whose range holds u * Z; that thread walks its own
+// registers to the tile. Wave 0 then recomputes the tile's logits and walks them to the token.
+// r = 512 takes 512 threads: its 32-step tile recompute needs more than 128 registers a lane.
 template <int KS>
-__global__ __launch_bounds__(kBlock) void draft_sample_kernel(SampleArgs p) {
-  extern __shared__ double smass[];   // [ntiles]: float2 partials, then fp64 masses in place
-  __shared__ double red_d[kBlock / 64];
-  __shared__ float red_f[kBlock / 64];
-  __shared__ int red_i[kBlock / 64];
+struct SampleCfg {
+  static constexpr int kThreads = (KS >= 32) ? 512 : 1024;
+  static constexpr int kPer = kMaxVocab / kTileTokens / kThreads;   // tiles per thread, at most
+};
+
+__device__ __forceinline__ double tile_mass(float m, float s, float M) {
+  return (m == kNegInf) ? 0.0 : static_cast<double>(exp_term(m - M)) * static_cast<double>(s);
+}
+
+template <int KS>
+__global__ __launch_bounds__(SampleCfg<KS>::kThreads) void draft_sample_kernel(SampleArgs p) {
+  constexpr int kSampleThreads = SampleCfg<KS>::kThreads;
+  constexpr int kSamplePer = SampleCfg<KS>::kPer;
+  __shared__ double red_d[kSampleThreads / 64];
+  __shared__ float red_f[kSampleThreads / 64];
+  __shared__ int red_i[kSampleThreads / 64];
   __shared__ Located loc;
   __shared__ float Ls[kTileTokens];
   __shared__ float Lc[kTileTokens];
@@ -487,44 +501,71 @@ __global__ __launch_bounds__(kBlock) void draft_sample_kernel(SampleArgs p) {
   const int nt = p.ntiles;
   const float2* part = p.part + static_cast<size_t>(b) * nt;
   const size_t urow = (static_cast<size_t>(b) * p.gamma + p.k) * p.V;
-  const int32_t prevtok = p.prev[static_cast<size_t>(b) * p.prev_stride];
   const size_t out = static_cast<size_t>(b) * p.gamma + p.k;
 
-  u16x8_t e[KS];
-  if (tid < 64) load_e_row<KS>(e, p.W1, prevtok, half);
-  // Stage the partials: coalesced strided loads (16 in flight per thread), kept as float2 in
-  // padded LDS slots, then converted in place to fp64 masses once the row max is known. The
-  // padding (one slot per 16) spreads a thread's contiguous range over the banks.
-  float2* sp = reinterpret_cast<float2*>(smass);
-  constexpr int kBatch = 16;
+  // The embedding row W1[prev] goes to LDS by an LDS-DMA copy issued first, so it costs no
+  // registers while the partials are processed (the tile recompute reads it back).
+  __shared__ __attribute__((aligned(16))) uint16_t Es[16 * KS];
+  {
+    const int32_t prevtok = p.prev[static_cast<size_t>(b) * p.prev_stride];
+    if (tid < 2 * KS)
+      copy16_to_lds(p.W1 + static_cast<size_t>(prevtok) * (16 * KS) + 8 * tid, lds_addr(Es));
+  }
+  const int per = (nt + kSampleThreads - 1) / kSampleThreads;   // uniform, <= kSamplePer
+  const int c0 = min(nt, tid * per), c1 = min(nt, c0 + per);
+  float2 v[kSamplePer];
   float m = kNegInf;
-  for (int c0 = 0; c0 < nt; c0 += kBlock * kBatch) {
-    float2 v[kBatch];
 #pragma unroll
-    for (int i = 0; i < kBatch; ++i) {
-      const int c = c0 + i * kBlock + tid;
-      v[i] = part[min(c, nt - 1)];
-    }
+  for (int i = 0; i < kSamplePer; ++i) {
+    v[i] = make_float2(kNegInf, 0.0f);
+    if (i < per && c0 + i < c1) v[i] = part[c0 + i];
+    m = fmaxf(m, v[i].x);
+  }
+  const float M = block_max<kSampleThreads>(m, red_f);
+  double S = 0.0;
 #pragma unroll
-    for (int i = 0; i < kBatch; ++i) {
-      const int c = c0 + i * kBlock + tid;
-      if (c < nt) {
-        m = fmaxf(m, v[i].x);
-        sp[padded(c)] = v[i];
+  for (int i = 0; i < kSamplePer; ++i)
+    if (i < per) S += tile_mass(v[i].x, v[i].y, M);
+  double Z;
+  const double P = block_exclusive_scan<kSampleThreads>(S, red_d, &Z);
+  const double target =
+      static_cast<double>(p.uniforms[(static_cast<size_t>(b) * (p.gamma + 1) + p.k) * 3]) * Z;
+  const bool ok = (Z > 0.0) && (Z < __builtin_inf());
+  // Owner: the last thread with positive mass whose exclusive prefix is <= u * Z. It walks its
+  // range in order; if rounding leaves the draw past it, its last positive tile is taken.
+  const int owner = block_max_int<kSampleThreads>((ok && S > 0.0 && P <= target) ? tid : -1, red_i);
+  if (tid == owner) {
+    Located r;
+    r.chunk = -1;
+    r.take_last = 0;
+    r.before = 0.0;
+    double cum = P, last_before = P;
+    int last = -1;
+#pragma unroll
+    for (int i = 0; i < kSamplePer; ++i) {
+      if (i < per && r.chunk < 0) {
+        const double mi = tile_mass(v[i].x, v[i].y, M);
+        if (mi > 0.0) {
+          last = c0 + i;
+          last_before = cum;
+        }
+        if (cum + mi > target) {
+          r.chunk = c0 + i;
+          r.before = cum;
+        }
+        cum += mi;
       }
     }
-  }
-  const float M = block_max<kBlock>(m, red_f);
-  for (int c = tid; c < nt; c += kBlock) {
-    const float2 v = sp[padded(c)];
-    smass[padded(c)] = partial_mass(v.x, static_cast<double>(v.y), M);
+    if (r.chunk < 0) {
+      r.chunk = last;
+      r.before = last_before;
+      r.take_last = 1;
+    }
+    loc = r;
   }
   __syncthreads();
-  const double u = static_cast<double>(p.uniforms[(static_cast<size_t>(b) * (p.gamma + 1) + p.k) * 3]);
-  const Located L = locate_chunk<kBlock>(nt, u, [&](int c) { return smass[padded(c)]; }, red_d, red_i, &loc);
-  const double lse = static_cast<double>(M) + log(L.total);
-
-  if (L.chunk < 0) {  // logits not finite: documented fallback
+  const double lse = static_cast<double>(M) + log(Z);
+  if (owner < 0) {  // logits not finite: documented fallback
     if (tid == 0) {
       p.tokens[out] = 0;
       p.q[out] = __builtin_nanf("");
@@ -532,35 +573,33 @@ __global__ __launch_bounds__(kBlock) void draft_sample_kernel(SampleArgs p) {
     }
     return;
   }
+  const Located L = loc;
+  if (tid >= 64) return;
+  wait_copies<0>();   // the embedding row copy (long done: the partials were loaded after it)
   const int tok0 = L.chunk * kTileTokens;
-  int x = 0;
-  if (tid < 64) {
-    recompute_tile_e<KS>(e, p.W2t, p.U + urow, tok0, p.V, Ls);
+  recompute_tile_lds<KS>(Es, p.W2t, p.U + urow, tok0, p.V, Ls);
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_wave_barrier();
+  const float tm = part[L.chunk].x;
+  const double f = static_cast<double>(exp_term(tm - M));
+  double w = 0.0;
+  if (lane < kTileTokens && tok0 + lane < p.V) w = f * static_cast<double>(exp_term(Ls[lane] - tm));
+  const int x = tok0 + walk_tile(w, L.before, target, L.take_last != 0);
+  // The token whose probability is reported (and that conditions the next position).
+  const int32_t cond = p.force ? p.force[out] : x;
+  float lc;
+  if (cond / kTileTokens != L.chunk) {
+    recompute_tile_lds<KS>(Es, p.W2t, p.U + urow, (cond / kTileTokens) * kTileTokens, p.V, Lc);
     __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_wave_barrier();
-    const float tm = part[L.chunk].x;
-    const double f = exp(static_cast<double>(tm) - static_cast<double>(M));
-    double w = 0.0;
-    if (lane < kTileTokens && tok0 + lane < p.V) w = f * static_cast<double>(exp_term(Ls[lane] - tm));
-    x = tok0 + walk_tile(w, L.before, L.target, L.take_last != 0);
+    lc = Lc[cond % kTileTokens];
+  } else {
+    lc = Ls[cond % kTileTokens];
   }
-  // The token whose probability is reported (and that conditions the next position).
-  if (tid < 64) {
-    const int32_t cond = p.force ? p.force[out] : x;
-    float lc;
-    if (cond / kTileTokens != L.chunk) {
-      recompute_tile_e<KS>(e, p.W2t, p.U + urow, (cond / kTileTokens) * kTileTokens, p.V, Lc);
-      __builtin_amdgcn_s_waitcnt(0);
-      __builtin_amdgcn_wave_barrier();
-      lc = Lc[cond % kTileTokens];
-    } else {
-      lc = Ls[cond % kTileTokens];
-    }
-    if (tid == 0) {
-      p.tokens[out] = x;
-      p.q[out] = static_cast<float>(exp(static_cast<double>(lc) - lse));
-      p.lse[out] = lse;
-    }
+  if (tid == 0) {
+    p.tokens[out] = x;
+    p.q[out] = static_cast<float>(exp(static_cast<double>(lc) - lse));
+    p.lse[out] = lse;
   }
 }
 
@@ -631,8 +670,7 @@ static hipError_t launch_step_ks(const StepArgs& a, hipStream_t s) {
 }
 template <int KS>
 static hipError_t launch_sample_ks(const SampleArgs& a, hipStream_t s) {
-  const size_t lds = static_cast<size_t>(padded(a.ntiles)) * sizeof(double);
-  hipLaunchKernelGGL(draft_sample_kernel<KS>, dim3(a.B), dim3(kBlock), lds, s, a);
+  hipLaunchKernelGGL(draft_sample_kernel<KS>, dim3(a.B), dim3(SampleCfg<KS>::kThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -113,6 +113,36 @@ __device__ void recompute_tile_e(const u16x8_t (&e)[KS], const uint16_t* __restr
   }
 }
 
+// recompute_tile_e with the embedding row read from LDS (Es: r bf16) one k-step at a time, for
+// callers that keep the row in LDS rather than in registers.
+template <int KS>
+__device__ void recompute_tile_lds(const uint16_t* Es, const uint16_t* __restrict__ W2t,
+                                   const float* __restrict__ Urow, int tok0, int V, float* Ls) {
+  const int lane = threadIdx.x & 63, half = lane >> 5, col = lane & 31;
+  u16x8_t a[KS];
+  load_w2_tile<KS>(a, W2t, tok0 + col, V, half);
+  float u[16];
+  const bool vec4 = (V & 3) == 0;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    float o[4];
+    load4(Urow, tok0 + 8 * g + 4 * half, V, vec4, o);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) u[4 * g + i] = o[i];
+  }
+  f32x16_t acc = {};
+#pragma unroll
+  for (int s = 0; s < KS; ++s)
+    acc = mfma_32x32x16(a[s], *reinterpret_cast<const u16x8_t*>(Es + 16 * s + 8 * half), acc);
+  if (col == 0) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int v = tok0 + tile_token(j, half);
+      Ls[tile_token(j, half)] = (v < V) ? (u[j] + acc[j]) : kNegInf;
+    }
+  }
+}
+
 // recompute_tile_e with the embedding row of `prevtok` loaded here.
 template <int KS>
 __device__ void recompute_tile(const uint16_t* __restrict__ W1, const uint16_t* __restrict__ W2t,
