@@ -471,8 +471,8 @@ __global__ __launch_bounds__(kDmaThreads, 1) void markov_step_dma_kernel(StepArg
 
 // One 1024-thread workgroup per request. Thread t holds a contiguous range of at most 16 tile
 // partials (V <= 2^19) in registers: the row max comes from a block reduction, the tile masses
-// exp(m - M) * s (fp32 exponential, fp64 product) from registers, and a block scan of the
-// per-thread sums finds the thread whose range holds u * Z; that thread walks its own
+// exp(m - M) * s (fp32 exponential, fp64 product) from registers, and wave 0 scans the
+// per-thread sums to find the thread whose range holds u * Z; that thread walks its own
 // registers to the tile. Wave 0 then recomputes the tile's logits and walks them to the token.
 // r = 512 takes 512 threads: its 32-step tile recompute needs more than 128 registers a lane.
 template <int KS>
@@ -489,9 +489,10 @@ template <int KS>
 __global__ __launch_bounds__(SampleCfg<KS>::kThreads) void draft_sample_kernel(SampleArgs p) {
   constexpr int kSampleThreads = SampleCfg<KS>::kThreads;
   constexpr int kSamplePer = SampleCfg<KS>::kPer;
-  __shared__ double red_d[kSampleThreads / 64];
   __shared__ float red_f[kSampleThreads / 64];
-  __shared__ int red_i[kSampleThreads / 64];
+  __shared__ double ssum[kSampleThreads];
+  __shared__ int sh_owner;
+  __shared__ double sh_before, sh_target, sh_Z;
   __shared__ Located loc;
   __shared__ float Ls[kTileTokens];
   __shared__ float Lc[kTileTokens];
@@ -526,20 +527,58 @@ __global__ __launch_bounds__(SampleCfg<KS>::kThreads) void draft_sample_kernel(S
 #pragma unroll
   for (int i = 0; i < kSamplePer; ++i)
     if (i < per) S += tile_mass(v[i].x, v[i].y, M);
-  double Z;
-  const double P = block_exclusive_scan<kSampleThreads>(S, red_d, &Z);
-  const double target =
-      static_cast<double>(p.uniforms[(static_cast<size_t>(b) * (p.gamma + 1) + p.k) * 3]) * Z;
-  const bool ok = (Z > 0.0) && (Z < __builtin_inf());
-  // Owner: the last thread with positive mass whose exclusive prefix is <= u * Z. It walks its
-  // range in order; if rounding leaves the draw past it, its last positive tile is taken.
-  const int owner = block_max_int<kSampleThreads>((ok && S > 0.0 && P <= target) ? tid : -1, red_i);
+  ssum[tid] = S;
+  __syncthreads();
+  // Wave 0 finds the owner: the last thread with positive mass whose exclusive prefix is
+  // <= u * Z. Lane l sums threads kG l .. kG l + kG-1 in order, a wave scan gives the group
+  // prefixes and Z, the last group holding such a thread is located by ballot, and its kG
+  // sums are walked in order.
+  if (tid < 64) {
+    constexpr int kG = kSampleThreads / 64;
+    double gs = 0.0;
+#pragma unroll
+    for (int i = 0; i < kG; ++i) gs += ssum[kG * lane + i];
+    const double inc = wave_inclusive_scan(gs, lane);
+    double exc = __shfl_up(inc, 1, kWave);
+    if (lane == 0) exc = 0.0;
+    const double Z = __shfl(inc, kWave - 1, kWave);
+    const double target =
+        static_cast<double>(p.uniforms[(static_cast<size_t>(b) * (p.gamma + 1) + p.k) * 3]) * Z;
+    const bool ok = (Z > 0.0) && (Z < __builtin_inf());
+    const unsigned long long cand = __ballot(ok && gs > 0.0 && exc <= target);
+    int own = -1;
+    double before = 0.0;
+    if (cand) {
+      const int g = 63 - __clzll(static_cast<long long>(cand));
+      double cum = __shfl(exc, g, kWave);
+#pragma unroll
+      for (int i = 0; i < kG; ++i) {
+        const double si = ssum[kG * g + i];
+        if (si > 0.0 && cum <= target) {
+          own = kG * g + i;
+          before = cum;
+        }
+        cum += si;
+      }
+    }
+    if (lane == 0) {
+      sh_owner = own;
+      sh_before = before;
+      sh_target = target;
+      sh_Z = Z;
+    }
+  }
+  __syncthreads();
+  const int owner = sh_owner;
+  const double target = sh_target, Z = sh_Z;
+  // The owner walks its range in order; if rounding leaves the draw past it, its last positive
+  // tile is taken.
   if (tid == owner) {
     Located r;
     r.chunk = -1;
     r.take_last = 0;
     r.before = 0.0;
-    double cum = P, last_before = P;
+    double cum = sh_before, last_before = sh_before;
     int last = -1;
 #pragma unroll
     for (int i = 0; i < kSamplePer; ++i) {
