@@ -64,6 +64,37 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Value held by lane l ^ S (S = 1, 2, 4, 8, 16, 32) without going through LDS: DPP quad
+// permutes for 1 and 2, DPP row shifts for 4 and 8, and the gfx950 row-pair / half-wave swaps
+// for 16 and 32.
+template <int S>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t x) {
+  const int lane = threadIdx.x & 63;
+  if constexpr (S == 1) {
+    return __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+  } else if constexpr (S == 2) {
+    return __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+  } else if constexpr (S == 4 || S == 8) {
+    const uint32_t up = __builtin_amdgcn_mov_dpp(x, 0x100 + S, 0xF, 0xF, false);   // row_shl:S
+    const uint32_t dn = __builtin_amdgcn_mov_dpp(x, 0x110 + S, 0xF, 0xF, false);   // row_shr:S
+    return (lane & S) ? dn : up;
+  } else if constexpr (S == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    return (lane & 16) ? r[0] : r[1];
+  } else {
+    static_assert(S == 32, "lane_xor: S in 1..32");
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return (lane & 32) ? r[0] : r[1];
+  }
+}
+template <int S>
+__device__ __forceinline__ double lane_xor(double x) {
+  const uint64_t u = static_cast<uint64_t>(__double_as_longlong(x));
+  const uint32_t lo = lane_xor<S>(static_cast<uint32_t>(u));
+  const uint32_t hi = lane_xor<S>(static_cast<uint32_t>(u >> 32));
+  return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+}
+
 // ---- wave (64-lane) reductions in a fixed butterfly order ------------------------------------
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

@@ -7,7 +7,7 @@
 // flat SPS table degrades to full verify, confidences relayed through a ring, lag 2);
 // [CSDN] deepseek.csdn.net DSpark walk-through, 5.3 and 8.
 //
-// Steps: a_{b,j} = prod c (sequential fp64 per request) -> bitonic sort of (a desc, b, j) ->
+// Steps: a_{b,j} = prod c (sequential fp64 per request) -> merge sort of (a desc, b, j) ->
 // prefix sums tau_i -> Theta_i = tau_i * sps[B + i] -> admission count by mode -> l_b from
 // the rank of each candidate -> row_offsets. LAGGED_TOPK first runs the full-path search on
 // the ring slot holding the confidences of two rounds back, then overwrites that slot.
@@ -33,17 +33,35 @@ struct PlanSmem {
   int n_admit;
 };
 
+// "Before" order of candidates: survival descending, then candidate index ascending.
 __device__ __forceinline__ bool before(double ai, int ii, double aj, int ij) {
   return (ai > aj) || (ai == aj && ii < ij);
 }
 
-// Fill survivals from conf, sort, and turn a[] into tau_i (a[i] = tau_{i+1}). Returns nothing;
-// results in sm.
+// One compare-exchange of a bitonic stage with partner lane l ^ S (within the wave); `up`
+// selects the direction of the bitonic sequence the lane belongs to.
+template <int S>
+__device__ __forceinline__ void exchange(double& a, int& ix, int l, bool up) {
+  const double pa = lane_xor<S>(a);
+  const int pi = static_cast<int>(lane_xor<S>(static_cast<uint32_t>(ix)));
+  const bool lower = (l & S) == 0;
+  const bool other_first = before(pa, pi, a, ix);
+  if ((lower == up) ? other_first : !other_first) {
+    a = pa;
+    ix = pi;
+  }
+}
+
+// Fill survivals from conf, sort, and turn a[] into tau_i (a[i] = tau_{i+1}). Results in sm.
+//
+// The sort: every 64-element chunk is sorted inside one wave (bitonic, no LDS traffic), then
+// merge levels double the runs. A merge level places every element directly: its position is
+// its rank in its own run plus the number of elements of the partner run that come before it,
+// found by binary search (the left run holds the lower indices, so on equal survivals the left
+// element goes first).
 __device__ void sorted_path(PlanSmem& sm, const float* __restrict__ conf, int B, int gamma) {
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int N = B * gamma;
-  int N2 = kWave;                       // whole waves: the shuffle stages need full waves
-  while (N2 < N) N2 <<= 1;
   for (int b = tid; b < B; b += kPlanThreads) {
     double prod = 1.0;
     for (int j = 0; j < gamma; ++j) {
@@ -52,51 +70,61 @@ __device__ void sorted_path(PlanSmem& sm, const float* __restrict__ conf, int B,
       sm.idx[b * gamma + j] = b * gamma + j;
     }
   }
-  for (int i = N + tid; i < N2; i += kPlanThreads) {
-    sm.a[i] = -__builtin_inf();
-    sm.idx[i] = INT_MAX;
+  __syncthreads();
+  // Runs of 64: each wave sorts 64-element chunks in registers with a bitonic network whose
+  // exchanges go through DPP / lane swaps (positions past N hold -inf and sort last).
+  for (int c = wave; c * kWave < N; c += kPlanThreads / kWave) {
+    const int i = c * kWave + lane;
+    double a = (i < N) ? sm.a[i] : -__builtin_inf();
+    int ix = (i < N) ? sm.idx[i] : INT_MAX;
+#pragma unroll
+    for (int size = 2; size <= kWave; size <<= 1) {
+      const bool up = (lane & size) == 0 || size == kWave;
+      if (size >= 64) exchange<32>(a, ix, lane, up);
+      if (size >= 32) exchange<16>(a, ix, lane, up);
+      if (size >= 16) exchange<8>(a, ix, lane, up);
+      if (size >= 8) exchange<4>(a, ix, lane, up);
+      if (size >= 4) exchange<2>(a, ix, lane, up);
+      exchange<1>(a, ix, lane, up);
+    }
+    if (i < N) {
+      sm.a[i] = a;
+      sm.idx[i] = ix;
+    }
   }
   __syncthreads();
-  // Bitonic sort into "before" order. Stages with a stride of 64 or more exchange through LDS;
-  // the remaining stages of each merge stay inside a wave and use lane shuffles (element i
-  // lives in lane i % 64), so each merge costs one barrier for all of its short strides.
-  for (int size = 2; size <= N2; size <<= 1) {
-    int stride = size >> 1;
-    for (; stride >= kWave; stride >>= 1) {
-      for (int t = tid; t < N2 / 2; t += kPlanThreads) {
-        const int i = 2 * t - (t & (stride - 1));
-        const int j = i + stride;
-        const bool up = (i & size) == 0;
-        const double ai = sm.a[i], aj = sm.a[j];
-        const int ii = sm.idx[i], ij = sm.idx[j];
-        const bool swap = up ? before(aj, ij, ai, ii) : before(ai, ii, aj, ij);
-        if (swap) {
-          sm.a[i] = aj;
-          sm.a[j] = ai;
-          sm.idx[i] = ij;
-          sm.idx[j] = ii;
+  constexpr int kPer = kPlanMax / kPlanThreads;
+  for (int run = kWave; run < N; run *= 2) {
+    double ka[kPer];
+    int ki[kPer], pos[kPer];
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      const int p = tid + q * kPlanThreads;
+      pos[q] = -1;
+      if (p < N) {
+        ka[q] = sm.a[p];
+        ki[q] = sm.idx[p];
+        const int base = (p / (2 * run)) * (2 * run);
+        const bool left = p - base < run;
+        const int own = left ? p - base : p - base - run;
+        const int o0 = left ? base + run : base;
+        const int olen = left ? max(0, min(run, N - base - run)) : run;
+        int lo = 0, hi = olen;
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          const double y = sm.a[o0 + mid];
+          if (left ? (y > ka[q]) : (y >= ka[q])) lo = mid + 1;
+          else hi = mid;
         }
+        pos[q] = base + own + lo;
       }
-      __syncthreads();
     }
-    for (int base = 0; base < N2; base += kPlanThreads) {
-      const int i = base + tid;
-      if (i < N2) {   // uniform per wave: N2 and base are multiples of 64
-        double a = sm.a[i];
-        int ix = sm.idx[i];
-        const bool up = (i & size) == 0;
-        for (int st = stride; st > 0; st >>= 1) {
-          const double pa = __shfl_xor(a, st, kWave);
-          const int pi = __shfl_xor(ix, st, kWave);
-          const bool lower = (i & st) == 0;
-          const bool other_first = before(pa, pi, a, ix);
-          if ((lower == up) ? other_first : !other_first) {
-            a = pa;
-            ix = pi;
-          }
-        }
-        sm.a[i] = a;
-        sm.idx[i] = ix;
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      if (pos[q] >= 0) {
+        sm.a[pos[q]] = ka[q];
+        sm.idx[pos[q]] = ki[q];
       }
     }
     __syncthreads();
