@@ -33,7 +33,8 @@ WORKLOAD = "b128-v129280-g5"
 METRIC = "spec rounds/s at B=128,V=129280,γ=5; achieved HBM GB/s vs peak"
 STEP_SOURCES = ["lossless_draft_verify_amd/csrc/kernels_draft.hip",
                 "lossless_draft_verify_amd/csrc/tiles.h",
-                "lossless_draft_verify_amd/csrc/device.h"]
+                "lossless_draft_verify_amd/csrc/device.h",
+                "lossless_draft_verify_amd/csrc/dma.h"]
 
 
 def step_source_sha():

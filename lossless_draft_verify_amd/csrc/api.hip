@@ -83,6 +83,8 @@ size_t verify_ws(const dspark_dims& d, void* base, VerifyWs* out) {
   w.eflags = reinterpret_cast<uint32_t*>(take(B * sizeof(uint32_t)));
   w.rsum = reinterpret_cast<double*>(take(B * nt * sizeof(double)));
   w.rmin = reinterpret_cast<double*>(take(B * nt * sizeof(double)));
+  w.rcount = reinterpret_cast<int32_t*>(take(sizeof(int32_t)));
+  w.rrec = reinterpret_cast<ResRec*>(take(B * sizeof(ResRec)));
   if (out) *out = w;
   return off;
 }
@@ -268,6 +270,7 @@ dspark_status dspark_verify(dspark_dims dims, const float* target, const int32_t
   a.next_token = next_token;
   a.beta_emit = beta_emit;
   a.flags = flags;
+  a.persistent_wgs = compute_units();
   verify_ws(dims, ws, &a.ws);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (timed(kTargetStats, s, [&] { return launch_target_stats(a, s); }) != hipSuccess)

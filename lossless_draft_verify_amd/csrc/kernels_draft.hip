@@ -15,6 +15,7 @@
 //                (bit-identical), and walks them in fp64 to the drawn token.
 #include "device.h"
 #include "launch.h"
+#include "dma.h"
 #include "tiles.h"
 
 namespace dspark {
@@ -245,34 +246,6 @@ constexpr int kDmaThreads = 512;
 constexpr int kDmaGroup = 128;   // requests per group: 4 waves x 32 per tile
 constexpr int kDmaTiles = 2;     // 32-token tiles per item
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Copy 16 bytes per lane from global memory into LDS at byte address lds + 16 * lane (lds
-// wave-uniform). Written as inline asm so that the compiler does not see an LDS-DMA write: it
-// tracks those only coarsely and would put a full vmcnt(0) wait (every copy in flight) before
-// each LDS read it cannot tell apart from the copies. The kernel orders copies and reads itself:
-// wait_copies<n>() + s_barrier before a stage is read, lds_barrier() before it is overwritten;
-// the "memory" clobbers keep the compiler's LDS reads between those points.
-__device__ __forceinline__ void copy16_to_lds(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds)
-               : "memory", "m0");
-}
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void*)p));
-}
-
-template <int N>
-__device__ __forceinline__ void wait_copies() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-// Value of lane l ^ 32 (v_permlane32_swap exchanges the two half-waves).
-__device__ __forceinline__ float other_half(float x, int half) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                  false);
-  return __uint_as_float(half ? r[0] : r[1]);
-}
-
 template <int KS>
 struct DmaStep {
   static constexpr int r = 16 * KS;
@@ -380,9 +353,7 @@ __global__ __launch_bounds__(kDmaThreads, 1) void markov_step_dma_kernel(StepArg
   // them into stage 0; each wave reads its rows into registers and releases stage 1.
   if (wave < kDmaGroup / 64) {
     const int b = min(group * kDmaGroup + 64 * wave + lane, p.B - 1);
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
-                 ::"v"(p.prev + static_cast<size_t>(b) * p.prev_stride),
-                 "s"(lds_addr(pid) + 256 * wave) : "memory", "m0");
+    copy4_to_lds(p.prev + static_cast<size_t>(b) * p.prev_stride, lds_addr(pid) + 256 * wave);
   }
   wait_copies<0>();
   asm volatile("s_barrier" ::: "memory");

@@ -20,6 +20,7 @@
 //                      from the target row's segments for a bonus (or a zero-mass residual)
 #include "device.h"
 #include "launch.h"
+#include "dma.h"
 #include "tiles.h"
 
 namespace dspark {
@@ -30,6 +31,7 @@ __global__ __launch_bounds__(kBlock) void target_stats_kernel(VerifyArgs p) {
   __shared__ float red_f[kBlock / 64];
   __shared__ double red_d[kBlock / 64];
   const int row = blockIdx.y;
+  if (blockIdx.x == 0 && row == 0 && threadIdx.x == 0) *p.ws.rcount = 0;   // for accept
   if (row >= p.row_offsets[p.B]) return;
   const int t0 = blockIdx.x * kSegTokens;
   const float* trow = p.target + static_cast<size_t>(row) * p.V;
@@ -123,6 +125,16 @@ __global__ __launch_bounds__(kBlock) void accept_kernel(VerifyArgs p) {
     if (!isfinite(lse_s[w][k])) fl |= 1u;
   fl = (__ballot(fl != 0u) != 0ull) ? 1u : 0u;
   if (lane == 0) {
+    if (rejected) {
+      ResRec r;
+      r.b = b;
+      r.j = last + 1;
+      r.erow = off + last;
+      r.prev = (last == 0) ? p.anchor[b] : p.tokens[static_cast<size_t>(b) * p.gamma + last - 1];
+      r.lse_d = p.lse[static_cast<size_t>(b) * p.gamma + last];
+      r.lse_t = lse_s[w][last];
+      p.ws.rrec[atomicAdd(p.ws.rcount, 1)] = r;
+    }
     p.accept_len[b] = accepted;
     p.ws.ekind[b] = rejected ? kEmitResidual : kEmitBonus;
     p.ws.epos[b] = last + 1;
@@ -241,6 +253,208 @@ __global__ __launch_bounds__(kBlock, 2) void residual_partials_kernel(VerifyArgs
     }
     __syncthreads();
   }
+}
+
+// ---- Pipelined residual pass --------------------------------------------------------------
+//
+// The structure of the pipelined draft step, for the requests that rejected: a persistent grid
+// whose workgroups split the residual list into groups of 64 (records written by the accept
+// scan) and the vocabulary into contiguous ranges of 64-token items. Per item, the 64 W2t rows,
+// the group's U row segments (draft position j) and target row segments are copied into one of
+// two LDS stages; wave (sub, rq) recomputes the logits of tile `sub` for requests 32 rq .. +32
+// with the draft's MFMA sequence (bit-identical logits) and reduces w = max(0, p_t - p_d) and
+// min(p_t, p_d) over the tile in fp64.
+constexpr int kResThreads = 256;
+constexpr int kResGroup = 64;
+constexpr int kResTiles = 2;
+
+template <int KS>
+struct ResStep {
+  static constexpr int r = 16 * KS;
+  static constexpr int kTok = kResTiles * kTileTokens;              // 64 tokens per item
+  static constexpr int kW2Chunks = 2 * KS;
+  static constexpr int kW2Bytes = kTok * kW2Chunks * 16;
+  static constexpr int kRowChunks = kTok / 4;                       // 16 per row segment
+  static constexpr int kRowBytes = kResGroup * kRowChunks * 16;     // 16 KB
+  static constexpr int kStageBytes = kW2Bytes + 2 * kRowBytes;      // W2t | U rows | target rows
+  static constexpr int kStages = 2;
+  static constexpr int kPartItems = 8;
+  static constexpr int kWaves = kResThreads / 64;
+  static constexpr int kW2Copies = kW2Bytes / 1024 / kWaves;
+  static constexpr int kRowCopies = kRowBytes / 1024 / kWaves;
+  static constexpr int kCopies = kW2Copies + 2 * kRowCopies;
+  static constexpr int kECopies = kResGroup * kW2Chunks * 16 / 1024 / kWaves;
+  static constexpr int kW2Swz = (kW2Chunks >= 16) ? 15 : kW2Chunks - 1;
+  static constexpr int kAOffs = (KS < 8) ? KS : 8;
+  static_assert(KS >= 4 && KS <= 16, "one to four 1 KB W2 copies per wave per item");
+  static_assert(kCopies <= 63, "vmcnt range");
+  static_assert(kResGroup * kW2Chunks * 16 <= kStageBytes, "embedding rows fit in one stage");
+};
+
+template <int KS>
+__global__ __launch_bounds__(kResThreads, 1) void residual_dma_kernel(VerifyArgs p) {
+  using D = ResStep<KS>;
+  __shared__ __attribute__((aligned(1024))) unsigned char stage[D::kStages * D::kStageBytes];
+  __shared__ double2 pbuf[D::kPartItems * kResTiles * kResGroup];   // (sum w, sum min)
+  __shared__ ResRec rec[kResGroup];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5, col = lane & 31;
+  const int sub = wave >> 1, rq = wave & 1;
+  const int nres = *p.ws.rcount;
+  if (nres <= 0) return;
+  const int ngroups = (nres + kResGroup - 1) / kResGroup;   // <= gridDim.x (launch sizing)
+  const int nwg = gridDim.x / ngroups;
+  if (static_cast<int>(blockIdx.x) >= nwg * ngroups) return;
+  const int group = blockIdx.x % ngroups, wg = blockIdx.x / ngroups;
+  const int gcount = min(kResGroup, nres - group * kResGroup);
+  const int nitems = (p.V + D::kTok - 1) / D::kTok;
+  const int item_lo = static_cast<int>(static_cast<int64_t>(nitems) * wg / nwg);
+  const int n = static_cast<int>(static_cast<int64_t>(nitems) * (wg + 1) / nwg) - item_lo;
+  if (n <= 0) return;
+  if (tid < kResGroup) rec[tid] = p.ws.rrec[group * kResGroup + min(tid, gcount - 1)];
+  __syncthreads();
+  const int row_own = 32 * rq + col;
+  const bool wave_active = 32 * rq < gcount;
+
+  const uint32_t stage_addr = lds_addr(stage);
+  uint32_t a_off[D::kAOffs], u_off[4];
+  {
+    const int wrow = 32 * sub + col;
+#pragma unroll
+    for (int t = 0; t < D::kAOffs; ++t)
+      a_off[t] = 16 * (wrow * D::kW2Chunks + ((2 * t + half) ^ (wrow & D::kW2Swz)));
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      u_off[g] = D::kW2Bytes +
+                 16 * (row_own * D::kRowChunks + ((8 * sub + 2 * g + half) ^ (row_own & 15)));
+  }
+
+  // This wave's share of item j's copies. Positions past V are clamped (masked later).
+  auto issue = [&](int j) {
+    const int tok0 = (item_lo + j) * D::kTok;
+    const uint32_t base = stage_addr + (j % D::kStages) * D::kStageBytes;
+#pragma unroll
+    for (int i = 0; i < D::kW2Copies; ++i) {
+      const int q = wave * D::kW2Copies + i;
+      const int slot = 64 * q + lane;
+      const int row = slot / D::kW2Chunks;
+      const int c = (slot % D::kW2Chunks) ^ (row & D::kW2Swz);
+      const int tok = min(tok0 + row, p.V - 1);
+      copy16_to_lds(p.W2t + static_cast<size_t>(tok) * D::r + 8 * c, base + 1024 * q);
+    }
+#pragma unroll
+    for (int i = 0; i < D::kRowCopies; ++i) {
+      const int q = wave * D::kRowCopies + i;
+      const int slot = 64 * q + lane;
+      const int row = slot / D::kRowChunks;
+      const int c = (slot % D::kRowChunks) ^ (row & 15);
+      const int v = min(tok0 + 4 * c, p.V - 4);
+      const ResRec& R = rec[row];
+      copy16_to_lds(p.U + (static_cast<size_t>(R.b) * p.gamma + R.j - 1) * p.V + v,
+                    base + D::kW2Bytes + 1024 * q);
+      copy16_to_lds(p.target + static_cast<size_t>(R.erow) * p.V + v,
+                    base + D::kW2Bytes + D::kRowBytes + 1024 * q);
+    }
+  };
+
+  // Tile sums of items j0 .. j1-1 (after a barrier) to rsum / rmin: consecutive threads take
+  // consecutive tiles of one request.
+  auto flush = [&](int j0, int j1) {
+    const int per = (j1 - j0) * kResTiles;
+    for (int x = tid; x < gcount * per; x += kResThreads) {
+      const int row = x / per, tt = x % per;
+      const int j = j0 + tt / kResTiles;
+      const int tile = (item_lo + j0) * kResTiles + tt;
+      if (tile < p.ntiles) {
+        const double2 v = pbuf[((j % D::kPartItems) * kResTiles + tt % kResTiles) * kResGroup + row];
+        const size_t o = static_cast<size_t>(rec[row].b) * p.ntiles + tile;
+        p.ws.rsum[o] = v.x;
+        p.ws.rmin[o] = v.y;
+      }
+    }
+  };
+
+  // Prologue: embedding rows W1[prev] of the group into stage 1, item 0 into stage 0.
+  {
+    const uint32_t ebase = stage_addr + D::kStageBytes;
+#pragma unroll
+    for (int i = 0; i < D::kECopies; ++i) {
+      const int q = wave * D::kECopies + i;
+      const int slot = 64 * q + lane;
+      const int row = slot / D::kW2Chunks;
+      const int c = (slot % D::kW2Chunks) ^ (row & D::kW2Swz);
+      copy16_to_lds(p.W1 + static_cast<size_t>(rec[row].prev) * D::r + 8 * c, ebase + 1024 * q);
+    }
+  }
+  issue(0);
+  wait_copies<D::kCopies>();
+  asm volatile("s_barrier" ::: "memory");
+  u16x8_t e[KS];
+  {
+    const unsigned char* eb = stage + D::kStageBytes;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      e[s] = *reinterpret_cast<const u16x8_t*>(
+          eb + 16 * (row_own * D::kW2Chunks + ((2 * s + half) ^ (row_own & D::kW2Swz))));
+  }
+  const double lse_d = rec[row_own].lse_d, lse_t = rec[row_own].lse_t;
+  lds_barrier();
+  int flushed = 0;
+  for (int j = 0; j < n; ++j) {
+    if (j + 1 < n) {
+      issue(j + 1);
+      wait_copies<D::kCopies>();
+    } else {
+      wait_copies<0>();
+    }
+    asm volatile("s_barrier" ::: "memory");
+    const int tok0 = (item_lo + j) * D::kTok + sub * kTileTokens;
+    if (wave_active && tok0 < p.V) {
+      const unsigned char* base = stage + (j % D::kStages) * D::kStageBytes;
+      u16x8_t a[KS];
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        a[s] = *reinterpret_cast<const u16x8_t*>(base + 256 * (s >> 3) + a_off[s % D::kAOffs]);
+      float4 uu[4], tt[4];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        uu[g] = *reinterpret_cast<const float4*>(base + u_off[g]);
+        tt[g] = *reinterpret_cast<const float4*>(base + u_off[g] + D::kRowBytes);
+      }
+      f32x16_t acc = {};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) acc = mfma_32x32x16(a[s], e[s], acc);
+      // Same terms and summation order as the register-load residual kernel.
+      double W = 0.0, O = 0.0;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int v = tok0 + 8 * g + 4 * half;
+        const float u4[4] = {uu[g].x, uu[g].y, uu[g].z, uu[g].w};
+        const float t4[4] = {tt[g].x, tt[g].y, tt[g].z, tt[g].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (v + i < p.V) {
+            double w, o;
+            residual_pair(u4[i] + acc[4 * g + i], t4[i], lse_d, lse_t, w, o);
+            W += w;
+            O += o;
+          }
+        }
+      }
+      W = W + other_half(W, half);
+      O = O + other_half(O, half);
+      if (half == 0 && row_own < gcount)
+        pbuf[((j % D::kPartItems) * kResTiles + sub) * kResGroup + row_own] = make_double2(W, O);
+    }
+    lds_barrier();
+    if ((j + 1) % D::kPartItems == 0 && j + 1 < n) {
+      flush(flushed, j + 1);
+      flushed = j + 1;
+      wait_copies<0>();   // the stores join the counter: drain it so later counts hold copies only
+    }
+  }
+  flush(flushed, n);
 }
 
 template <int KS>
@@ -376,6 +590,16 @@ hipError_t launch_accept(const VerifyArgs& a, hipStream_t s) {
 
 template <int KS>
 static hipError_t launch_resid_ks(const VerifyArgs& a, hipStream_t s) {
+  // The pipelined pass copies 16-byte row chunks (V % 4 == 0) and 1-4 KB of W2t per wave
+  // (64 <= r <= 256); other shapes take the register-load kernel.
+  if constexpr (KS >= 4 && KS <= 16) {
+    if ((a.V & 3) == 0) {
+      const int groups = (a.B + kResGroup - 1) / kResGroup;
+      const int grid = a.persistent_wgs > groups ? a.persistent_wgs : groups;
+      hipLaunchKernelGGL(residual_dma_kernel<KS>, dim3(grid), dim3(kResThreads), 0, s, a);
+      return hipGetLastError();
+    }
+  }
   const int grid = (a.V + 4 * kTileTokens - 1) / (4 * kTileTokens);
   hipLaunchKernelGGL(residual_partials_kernel<KS>, dim3(grid), dim3(kBlock), 0, s, a);
   return hipGetLastError();

@@ -58,6 +58,17 @@ struct PlanArgs {
 // Emission kinds written by the accept scan.
 enum : int32_t { kEmitBonus = 0, kEmitResidual = 1 };
 
+// One residual emission, appended by the accept scan (in no particular order: the kernels that
+// read the list give every request the same result whatever its slot).
+struct ResRec {
+  int32_t b;       // request
+  int32_t j;       // 1-based emission position (the first rejected draft position)
+  int32_t erow;    // packed target row of position j
+  int32_t prev;    // token before position j (the anchor for j = 1)
+  double lse_d;    // log-sum-exp of the draft logits of position j
+  double lse_t;    // log-sum-exp of the target row
+};
+
 struct VerifyWs {
   float* seg_max;    // [B*(gamma+1)][nseg]
   double* seg_sum;   // [B*(gamma+1)][nseg]
@@ -68,6 +79,8 @@ struct VerifyWs {
   uint32_t* eflags;  // [B]
   double* rsum;      // [B][ntiles] residual mass per 32-token tile
   double* rmin;      // [B][ntiles] sum of min(p_t, p_d) per tile
+  int32_t* rcount;   // [1] residual emissions (zeroed by the target pass, counted by accept)
+  ResRec* rrec;      // [B] their records
 };
 
 struct VerifyArgs {
@@ -87,6 +100,7 @@ struct VerifyArgs {
   int32_t* next_token;
   float* beta_emit;   // nullable
   uint32_t* flags;    // nullable
+  int persistent_wgs; // workgroups of the pipelined residual kernel (one per compute unit)
   VerifyWs ws;
 };
 
