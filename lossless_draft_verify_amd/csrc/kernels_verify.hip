@@ -261,10 +261,11 @@ __global__ __launch_bounds__(kBlock, 2) void residual_partials_kernel(VerifyArgs
 // whose workgroups split the residual list into groups of 64 (records written by the accept
 // scan) and the vocabulary into contiguous ranges of 64-token items. Per item, the 64 W2t rows,
 // the group's U row segments (draft position j) and target row segments are copied into one of
-// two LDS stages; wave (sub, rq) recomputes the logits of tile `sub` for requests 32 rq .. +32
-// with the draft's MFMA sequence (bit-identical logits) and reduces w = max(0, p_t - p_d) and
-// min(p_t, p_d) over the tile in fp64.
-constexpr int kResThreads = 256;
+// two LDS stages; waves (sub, rq, part) recompute the logits of tile `sub` for requests
+// 32 rq .. +32 with the draft's MFMA sequence (bit-identical logits; the two waves of a pair
+// compute the same tile) and reduce w = max(0, p_t - p_d) and min(p_t, p_d) in fp64 over half of
+// the tile each (the fp64 exponentials dominate, so eight waves share them).
+constexpr int kResThreads = 512;
 constexpr int kResGroup = 64;
 constexpr int kResTiles = 2;
 
@@ -278,7 +279,7 @@ struct ResStep {
   static constexpr int kRowBytes = kResGroup * kRowChunks * 16;     // 16 KB
   static constexpr int kStageBytes = kW2Bytes + 2 * kRowBytes;      // W2t | U rows | target rows
   static constexpr int kStages = 2;
-  static constexpr int kPartItems = 8;
+  static constexpr int kPartItems = 4;
   static constexpr int kWaves = kResThreads / 64;
   static constexpr int kW2Copies = kW2Bytes / 1024 / kWaves;
   static constexpr int kRowCopies = kRowBytes / 1024 / kWaves;
@@ -286,8 +287,8 @@ struct ResStep {
   static constexpr int kECopies = kResGroup * kW2Chunks * 16 / 1024 / kWaves;
   static constexpr int kW2Swz = (kW2Chunks >= 16) ? 15 : kW2Chunks - 1;
   static constexpr int kAOffs = (KS < 8) ? KS : 8;
-  static_assert(KS >= 4 && KS <= 16, "one to four 1 KB W2 copies per wave per item");
-  static_assert(kCopies <= 63, "vmcnt range");
+  static_assert(KS >= 8 && KS <= 16, "one or two 1 KB W2 copies per wave per item");
+  static_assert(kRowCopies >= 1 && kCopies <= 63, "copy counts");
   static_assert(kResGroup * kW2Chunks * 16 <= kStageBytes, "embedding rows fit in one stage");
 };
 
@@ -295,12 +296,12 @@ template <int KS>
 __global__ __launch_bounds__(kResThreads, 1) void residual_dma_kernel(VerifyArgs p) {
   using D = ResStep<KS>;
   __shared__ __attribute__((aligned(1024))) unsigned char stage[D::kStages * D::kStageBytes];
-  __shared__ double2 pbuf[D::kPartItems * kResTiles * kResGroup];   // (sum w, sum min)
+  __shared__ double2 pbuf[D::kPartItems * kResTiles * 2 * kResGroup];   // (sum w, sum min)
   __shared__ ResRec rec[kResGroup];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, col = lane & 31;
-  const int sub = wave >> 1, rq = wave & 1;
+  const int sub = (wave >> 1) & 1, rq = wave & 1, part = wave >> 2;
   const int nres = *p.ws.rcount;
   if (nres <= 0) return;
   const int ngroups = (nres + kResGroup - 1) / kResGroup;   // <= gridDim.x (launch sizing)
@@ -318,16 +319,18 @@ __global__ __launch_bounds__(kResThreads, 1) void residual_dma_kernel(VerifyArgs
   const bool wave_active = 32 * rq < gcount;
 
   const uint32_t stage_addr = lds_addr(stage);
-  uint32_t a_off[D::kAOffs], u_off[4];
+  uint32_t a_off[D::kAOffs], u_off[2];
   {
     const int wrow = 32 * sub + col;
 #pragma unroll
     for (int t = 0; t < D::kAOffs; ++t)
       a_off[t] = 16 * (wrow * D::kW2Chunks + ((2 * t + half) ^ (wrow & D::kW2Swz)));
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
-      u_off[g] = D::kW2Bytes +
+    for (int h = 0; h < 2; ++h) {
+      const int g = 2 * part + h;
+      u_off[h] = D::kW2Bytes +
                  16 * (row_own * D::kRowChunks + ((8 * sub + 2 * g + half) ^ (row_own & 15)));
+    }
   }
 
   // This wave's share of item j's copies. Positions past V are clamped (masked later).
@@ -367,10 +370,11 @@ __global__ __launch_bounds__(kResThreads, 1) void residual_dma_kernel(VerifyArgs
       const int j = j0 + tt / kResTiles;
       const int tile = (item_lo + j0) * kResTiles + tt;
       if (tile < p.ntiles) {
-        const double2 v = pbuf[((j % D::kPartItems) * kResTiles + tt % kResTiles) * kResGroup + row];
+        const int slot = ((j % D::kPartItems) * kResTiles + tt % kResTiles) * 2;
+        const double2 v0 = pbuf[slot * kResGroup + row], v1 = pbuf[(slot + 1) * kResGroup + row];
         const size_t o = static_cast<size_t>(rec[row].b) * p.ntiles + tile;
-        p.ws.rsum[o] = v.x;
-        p.ws.rmin[o] = v.y;
+        p.ws.rsum[o] = v0.x + v1.x;
+        p.ws.rmin[o] = v0.y + v1.y;
       }
     }
   };
@@ -416,22 +420,23 @@ __global__ __launch_bounds__(kResThreads, 1) void residual_dma_kernel(VerifyArgs
 #pragma unroll
       for (int s = 0; s < KS; ++s)
         a[s] = *reinterpret_cast<const u16x8_t*>(base + 256 * (s >> 3) + a_off[s % D::kAOffs]);
-      float4 uu[4], tt[4];
+      float4 uu[2], tt[2];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        uu[g] = *reinterpret_cast<const float4*>(base + u_off[g]);
-        tt[g] = *reinterpret_cast<const float4*>(base + u_off[g] + D::kRowBytes);
+      for (int h = 0; h < 2; ++h) {
+        uu[h] = *reinterpret_cast<const float4*>(base + u_off[h]);
+        tt[h] = *reinterpret_cast<const float4*>(base + u_off[h] + D::kRowBytes);
       }
       f32x16_t acc = {};
 #pragma unroll
       for (int s = 0; s < KS; ++s) acc = mfma_32x32x16(a[s], e[s], acc);
-      // Same terms and summation order as the register-load residual kernel.
+      // This wave's half of the tile (accumulator slot groups 2 part, 2 part + 1), in token order.
       double W = 0.0, O = 0.0;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
+      for (int h = 0; h < 2; ++h) {
+        const int g = 2 * part + h;
         const int v = tok0 + 8 * g + 4 * half;
-        const float u4[4] = {uu[g].x, uu[g].y, uu[g].z, uu[g].w};
-        const float t4[4] = {tt[g].x, tt[g].y, tt[g].z, tt[g].w};
+        const float u4[4] = {uu[h].x, uu[h].y, uu[h].z, uu[h].w};
+        const float t4[4] = {tt[h].x, tt[h].y, tt[h].z, tt[h].w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           if (v + i < p.V) {
@@ -445,7 +450,8 @@ __global__ __launch_bounds__(kResThreads, 1) void residual_dma_kernel(VerifyArgs
       W = W + other_half(W, half);
       O = O + other_half(O, half);
       if (half == 0 && row_own < gcount)
-        pbuf[((j % D::kPartItems) * kResTiles + sub) * kResGroup + row_own] = make_double2(W, O);
+        pbuf[(((j % D::kPartItems) * kResTiles + sub) * 2 + part) * kResGroup + row_own] =
+            make_double2(W, O);
     }
     lds_barrier();
     if ((j + 1) % D::kPartItems == 0 && j + 1 < n) {
@@ -590,9 +596,9 @@ hipError_t launch_accept(const VerifyArgs& a, hipStream_t s) {
 
 template <int KS>
 static hipError_t launch_resid_ks(const VerifyArgs& a, hipStream_t s) {
-  // The pipelined pass copies 16-byte row chunks (V % 4 == 0) and 1-4 KB of W2t per wave
-  // (64 <= r <= 256); other shapes take the register-load kernel.
-  if constexpr (KS >= 4 && KS <= 16) {
+  // The pipelined pass copies 16-byte row chunks (V % 4 == 0) and 1-2 KB of W2t per wave
+  // (128 <= r <= 256); other shapes take the register-load kernel.
+  if constexpr (KS >= 8 && KS <= 16) {
     if ((a.V & 3) == 0) {
       const int groups = (a.B + kResGroup - 1) / kResGroup;
       const int grid = a.persistent_wgs > groups ? a.persistent_wgs : groups;
