@@ -95,6 +95,25 @@ __device__ __forceinline__ double lane_xor(double x) {
   return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
 }
 
+// Wave max / fp64 sum through lane_xor (no LDS traffic), butterfly 32, 16, ..., 1; every lane
+// ends with the same value (the pairwise sums only swap operands between partner lanes).
+__device__ __forceinline__ float wave_max_x(float v) {
+  v = fmaxf(v, __uint_as_float(lane_xor<32>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(lane_xor<16>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(lane_xor<8>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(lane_xor<4>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(lane_xor<2>(__float_as_uint(v))));
+  return fmaxf(v, __uint_as_float(lane_xor<1>(__float_as_uint(v))));
+}
+__device__ __forceinline__ double wave_sum_x(double v) {
+  v += lane_xor<32>(v);
+  v += lane_xor<16>(v);
+  v += lane_xor<8>(v);
+  v += lane_xor<4>(v);
+  v += lane_xor<2>(v);
+  return v + lane_xor<1>(v);
+}
+
 // ---- wave (64-lane) reductions in a fixed butterfly order ------------------------------------
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

@@ -27,35 +27,62 @@ namespace dspark {
 
 namespace {
 
-__global__ __launch_bounds__(kBlock) void target_stats_kernel(VerifyArgs p) {
-  __shared__ float red_f[kBlock / 64];
-  __shared__ double red_d[kBlock / 64];
-  const int row = blockIdx.y;
-  if (blockIdx.x == 0 && row == 0 && threadIdx.x == 0) *p.ws.rcount = 0;   // for accept
-  if (row >= p.row_offsets[p.B]) return;
-  const int t0 = blockIdx.x * kSegTokens;
-  const float* trow = p.target + static_cast<size_t>(row) * p.V;
-  const bool vec4 = (p.V & 3) == 0;
-  float x[16];
+// Target row statistics, one 256-thread block per (row, 4096-token segment) work item on a
+// grid-stride loop over the rows the plan produced (read on the device). Each thread holds 16
+// values; the next item's loads are issued before the current item is reduced, and the block
+// reductions use LDS-only barriers, so those loads stay in flight through them.
+constexpr int kStatsBlocksPerCU = 8;
+
+__device__ __forceinline__ void load_segment(const float* __restrict__ trow, int t0, int V,
+                                             bool vec4, float (&x)[16]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int v = t0 + 1024 * i + 4 * threadIdx.x;
     float o[4];
-    load4(trow, v, p.V, vec4, o);
+    load4(trow, v, V, vec4, o);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) x[4 * i + e] = (v + e < p.V) ? o[e] : kNegInf;
+    for (int e = 0; e < 4; ++e) x[4 * i + e] = (v + e < V) ? o[e] : kNegInf;
   }
-  float m = max16(x);
-  m = block_max<kBlock>(m, red_f);
-  double s = 0.0;
-  if (m != kNegInf) {
+}
+
+__global__ __launch_bounds__(kBlock) void target_stats_kernel(VerifyArgs p) {
+  __shared__ float red_f[kBlock / 64];
+  __shared__ double red_d[kBlock / 64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *p.ws.rcount = 0;   // residual list (for accept)
+  const int nitems = p.row_offsets[p.B] * p.nseg;
+  const bool vec4 = (p.V & 3) == 0;
+  int it = blockIdx.x;
+  if (it >= nitems) return;
+  float x[16], y[16];
+  load_segment(p.target + static_cast<size_t>(it / p.nseg) * p.V, (it % p.nseg) * kSegTokens, p.V,
+               vec4, x);
+  for (; it < nitems; it += gridDim.x) {
+    const int nxt = it + gridDim.x;
+    if (nxt < nitems)
+      load_segment(p.target + static_cast<size_t>(nxt / p.nseg) * p.V, (nxt % p.nseg) * kSegTokens,
+                   p.V, vec4, y);
+    float m = max16(x);
+    m = wave_max_x(m);
+    lds_barrier();
+    if (lane == 0) red_f[w] = m;
+    lds_barrier();
+    m = fmaxf(fmaxf(red_f[0], red_f[1]), fmaxf(red_f[2], red_f[3]));
+    double s = 0.0;
+    if (m != kNegInf) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) s += static_cast<double>(exp_term(x[j] - m));
-  }
-  s = block_sum<kBlock>(s, red_d);
-  if (threadIdx.x == 0) {
-    p.ws.seg_max[static_cast<size_t>(row) * p.nseg + blockIdx.x] = m;
-    p.ws.seg_sum[static_cast<size_t>(row) * p.nseg + blockIdx.x] = s;
+      for (int j = 0; j < 16; ++j) s += static_cast<double>(exp_term(x[j] - m));
+    }
+    s = wave_sum_x(s);
+    if (lane == 0) red_d[w] = s;
+    lds_barrier();
+    if (threadIdx.x == 0) {
+      const size_t o = static_cast<size_t>(it / p.nseg) * p.nseg + it % p.nseg;
+      p.ws.seg_max[o] = m;
+      p.ws.seg_sum[o] = (red_d[0] + red_d[1]) + (red_d[2] + red_d[3]);
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) x[j] = y[j];
   }
 }
 
@@ -583,8 +610,8 @@ __global__ __launch_bounds__(kBlock) void emit_sample_kernel(VerifyArgs p) {
 }  // namespace
 
 hipError_t launch_target_stats(const VerifyArgs& a, hipStream_t s) {
-  const int max_rows = a.B * (a.gamma + 1);
-  hipLaunchKernelGGL(target_stats_kernel, dim3(a.nseg, max_rows), dim3(kBlock), 0, s, a);
+  hipLaunchKernelGGL(target_stats_kernel, dim3(a.persistent_wgs * kStatsBlocksPerCU), dim3(kBlock),
+                     0, s, a);
   return hipGetLastError();
 }
 
