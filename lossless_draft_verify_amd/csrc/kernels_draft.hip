@@ -613,39 +613,47 @@ __global__ __launch_bounds__(SampleCfg<KS>::kThreads) void draft_sample_kernel(S
   }
 }
 
-// Confidence head: one wave per (request, position).
+// Confidence head: one 256-thread block per (request, position). The hidden-state pieces go
+// out before the previous token is known; the embedding-row pieces follow it. Products in fp64,
+// summed per thread in piece order, then across the block in a fixed order.
 __global__ __launch_bounds__(kBlock) void confidence_kernel(ConfArgs p) {
-  const int lane = threadIdx.x & 63;
-  const int idx = blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);
-  if (idx >= p.B * p.gamma) return;
+  __shared__ double red[kBlock / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int idx = blockIdx.x;
   const int b = idx / p.gamma, k = idx % p.gamma;
-  const int32_t prevtok = (k == 0) ? p.anchor[b] : p.tokens[static_cast<size_t>(b) * p.gamma + k - 1];
-  // Loads in batches of 8 pieces per lane (all in flight before the products), fp64 sum.
-  double acc = 0.0;
   const uint16_t* hrow = p.h + static_cast<size_t>(idx) * p.d;
-  const uint16_t* erow = p.W1 + static_cast<size_t>(prevtok) * p.r;
-  const int n = p.d + p.r;               // pieces of 8: d/8 from h, r/8 from the embedding row
-  constexpr int kBatch = 8;
-  for (int i0 = lane * 8; i0 < n; i0 += 64 * 8 * kBatch) {
-    u16x8_t xv[kBatch], wv[kBatch];
+  constexpr int kBatch = 4;   // pieces of 8 per thread per batch: 8192 elements per batch
+  double acc = 0.0;
+  const int nh = p.d / 8;     // hidden-state pieces
+  for (int c0 = 0; c0 < nh; c0 += kBlock * kBatch) {
+    u16x8_t xv[kBatch], ww[kBatch];
 #pragma unroll
     for (int q = 0; q < kBatch; ++q) {
-      const int i = min(i0 + q * 64 * 8, n - 8);
-      xv[q] = (i < p.d) ? load_u16x8(hrow + i) : load_u16x8(erow + (i - p.d));
-      wv[q] = load_u16x8(p.w + i);
+      const int c = min(c0 + q * kBlock + tid, nh - 1);
+      xv[q] = load_u16x8(hrow + 8 * c);
+      ww[q] = load_u16x8(p.w + 8 * c);
     }
 #pragma unroll
     for (int q = 0; q < kBatch; ++q) {
-      if (i0 + q * 64 * 8 >= n) break;
+      if (c0 + q * kBlock + tid >= nh) break;
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        acc += static_cast<double>(bf16_to_f32(xv[q][e]) * bf16_to_f32(wv[q][e]));  // exact product
+        acc += static_cast<double>(bf16_to_f32(xv[q][e]) * bf16_to_f32(ww[q][e]));   // exact
     }
   }
-  const double z = wave_sum(acc);
-  if (lane == 0) {
-    const double c = 1.0 / (1.0 + exp(-z / static_cast<double>(p.T[k])));
-    p.conf[idx] = static_cast<float>(c);
+  const int32_t prevtok = (k == 0) ? p.anchor[b] : p.tokens[static_cast<size_t>(b) * p.gamma + k - 1];
+  for (int c = tid; c < p.r / 8; c += kBlock) {
+    const u16x8_t ev = load_u16x8(p.W1 + static_cast<size_t>(prevtok) * p.r + 8 * c);
+    const u16x8_t we = load_u16x8(p.w + p.d + 8 * c);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc += static_cast<double>(bf16_to_f32(ev[e]) * bf16_to_f32(we[e]));
+  }
+  acc = wave_sum_x(acc);
+  if (lane == 0) red[wv] = acc;
+  __syncthreads();
+  if (tid == 0) {
+    const double z = (red[0] + red[1]) + (red[2] + red[3]);
+    p.conf[idx] = static_cast<float>(1.0 / (1.0 + exp(-z / static_cast<double>(p.T[k]))));
   }
 }
 
@@ -702,9 +710,7 @@ hipError_t launch_draft_sample(const SampleArgs& a, int r, hipStream_t s) {
   DSPARK_DISPATCH_KS(r, launch_sample_ks, a, s)
 }
 hipError_t launch_confidence(const ConfArgs& a, hipStream_t s) {
-  const int waves = a.B * a.gamma;
-  const int grid = (waves + (kBlock / 64) - 1) / (kBlock / 64);
-  hipLaunchKernelGGL(confidence_kernel, dim3(grid), dim3(kBlock), 0, s, a);
+  hipLaunchKernelGGL(confidence_kernel, dim3(a.B * a.gamma), dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }
 
