@@ -99,6 +99,20 @@ __global__ __launch_bounds__(kBlock) void accept_kernel(VerifyArgs p) {
   const int ell = p.draft_len[b];
   const int off = p.row_offsets[b];
   uint32_t fl = 0;
+  // 0. The accept-test inputs of the first 64 positions go out first (the target value of a
+  //    drafted token needs only the token and the row offset).
+  float tx0 = 0.0f, u0 = 0.0f, q0 = 0.0f;
+  int32_t x0 = 0;
+  double lsed0 = 0.0;
+  const int32_t anc = p.anchor[b];
+  if (lane < ell) {
+    const int32_t x = p.tokens[static_cast<size_t>(b) * p.gamma + lane];
+    x0 = x;
+    lsed0 = p.lse[static_cast<size_t>(b) * p.gamma + lane];
+    tx0 = p.target[static_cast<size_t>(off + lane) * p.V + x];
+    u0 = p.uniforms[(static_cast<size_t>(b) * (p.gamma + 1) + lane) * 3 + 1];
+    q0 = p.q[static_cast<size_t>(b) * p.gamma + lane];
+  }
   // 1. log-sum-exp of rows off .. off + ell (segments: lane + 64 i, i < 2, nseg <= 128).
   for (int r0 = 0; r0 <= ell; r0 += kAcceptRows) {
     float mx[kAcceptRows][2];
@@ -118,8 +132,8 @@ __global__ __launch_bounds__(kBlock) void accept_kernel(VerifyArgs p) {
 #pragma unroll
     for (int r = 0; r < kAcceptRows; ++r) {
       if (r0 + r > ell) break;
-      const float M = wave_max(fmaxf(mx[r][0], mx[r][1]));
-      const double z = wave_sum(partial_mass(mx[r][0], sg[r][0], M) + partial_mass(mx[r][1], sg[r][1], M));
+      const float M = wave_max_x(fmaxf(mx[r][0], mx[r][1]));
+      const double z = wave_sum_x(partial_mass(mx[r][0], sg[r][0], M) + partial_mass(mx[r][1], sg[r][1], M));
       if (lane == 0) lse_s[w][r0 + r] = static_cast<double>(M) + log(z);
     }
   }
@@ -131,13 +145,16 @@ __global__ __launch_bounds__(kBlock) void accept_kernel(VerifyArgs p) {
     const int k = k0 + lane;
     bool ok = true;
     if (k < ell) {
-      const int row = off + k;
-      const int32_t x = p.tokens[static_cast<size_t>(b) * p.gamma + k];
-      const double l = lse_s[w][k];
-      const double pt = exp(static_cast<double>(p.target[static_cast<size_t>(row) * p.V + x]) - l);
-      const double u = static_cast<double>(p.uniforms[(static_cast<size_t>(b) * (p.gamma + 1) + k) * 3 + 1]);
-      const double qk = static_cast<double>(p.q[static_cast<size_t>(b) * p.gamma + k]);
-      ok = u * qk < pt;
+      float tx = tx0, uk = u0, qk = q0;
+      if (k0 > 0) {
+        const int row = off + k;
+        const int32_t x = p.tokens[static_cast<size_t>(b) * p.gamma + k];
+        tx = p.target[static_cast<size_t>(row) * p.V + x];
+        uk = p.uniforms[(static_cast<size_t>(b) * (p.gamma + 1) + k) * 3 + 1];
+        qk = p.q[static_cast<size_t>(b) * p.gamma + k];
+      }
+      const double pt = exp(static_cast<double>(tx) - lse_s[w][k]);
+      ok = static_cast<double>(uk) * static_cast<double>(qk) < pt;
     }
     const unsigned long long fail = __ballot(!ok);
     if (fail) {
@@ -151,14 +168,25 @@ __global__ __launch_bounds__(kBlock) void accept_kernel(VerifyArgs p) {
   for (int k = lane; k <= last; k += 64)
     if (!isfinite(lse_s[w][k])) fl |= 1u;
   fl = (__ballot(fl != 0u) != 0ull) ? 1u : 0u;
+  // Inputs of the residual record: positions 0..63 come from the registers loaded in step 0,
+  // later ones from memory.
+  int32_t prev_x = anc;
+  double lse_d = 0.0;
+  if (rejected) {
+    const int32_t xs = __shfl(x0, (last + 63) & 63, kWave);
+    const double ls = __shfl(lsed0, last & 63, kWave);
+    prev_x = (last == 0) ? anc
+             : (last - 1 < 64 ? xs : p.tokens[static_cast<size_t>(b) * p.gamma + last - 1]);
+    lse_d = (last < 64) ? ls : p.lse[static_cast<size_t>(b) * p.gamma + last];
+  }
   if (lane == 0) {
     if (rejected) {
       ResRec r;
       r.b = b;
       r.j = last + 1;
       r.erow = off + last;
-      r.prev = (last == 0) ? p.anchor[b] : p.tokens[static_cast<size_t>(b) * p.gamma + last - 1];
-      r.lse_d = p.lse[static_cast<size_t>(b) * p.gamma + last];
+      r.prev = prev_x;
+      r.lse_d = lse_d;
       r.lse_t = lse_s[w][last];
       p.ws.rrec[atomicAdd(p.ws.rcount, 1)] = r;
     }
