@@ -95,9 +95,31 @@ __device__ __forceinline__ double lane_xor(double x) {
   return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
 }
 
-// Wave max / fp64 sum through lane_xor (no LDS traffic), butterfly 32, 16, ..., 1; every lane
-// ends with the same value (the pairwise sums only swap operands between partner lanes).
-__device__ __forceinline__ float wave_max_x(float v) {
+// Lane l - S of the same 16-lane row, 0 for the first S lanes of each row (DPP row_shr with
+// zero fill).
+template <int S>
+__device__ __forceinline__ uint32_t row_shr_zero(uint32_t x) {
+  return __builtin_amdgcn_update_dpp(0u, x, 0x110 + S, 0xF, 0xF, true);
+}
+template <int S>
+__device__ __forceinline__ double row_shr_zero(double x) {
+  const uint64_t u = static_cast<uint64_t>(__double_as_longlong(x));
+  const uint32_t lo = row_shr_zero<S>(static_cast<uint32_t>(u));
+  const uint32_t hi = row_shr_zero<S>(static_cast<uint32_t>(u >> 32));
+  return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+}
+// Value of lane l (uniform l) in every lane.
+__device__ __forceinline__ double read_lane(double x, int l) {
+  const uint64_t u = static_cast<uint64_t>(__double_as_longlong(x));
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(u), l);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(u >> 32), l);
+  return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+}
+__device__ __forceinline__ int read_lane(int x, int l) { return __builtin_amdgcn_readlane(x, l); }
+
+// ---- wave (64-lane) reductions: butterfly 32, 16, ..., 1 through lane_xor (no LDS traffic);
+// every lane ends with the same value (the pairwise sums only swap operands between partners).
+__device__ __forceinline__ float wave_max(float v) {
   v = fmaxf(v, __uint_as_float(lane_xor<32>(__float_as_uint(v))));
   v = fmaxf(v, __uint_as_float(lane_xor<16>(__float_as_uint(v))));
   v = fmaxf(v, __uint_as_float(lane_xor<8>(__float_as_uint(v))));
@@ -105,7 +127,15 @@ __device__ __forceinline__ float wave_max_x(float v) {
   v = fmaxf(v, __uint_as_float(lane_xor<2>(__float_as_uint(v))));
   return fmaxf(v, __uint_as_float(lane_xor<1>(__float_as_uint(v))));
 }
-__device__ __forceinline__ double wave_sum_x(double v) {
+__device__ __forceinline__ double wave_max(double v) {
+  v = fmax(v, lane_xor<32>(v));
+  v = fmax(v, lane_xor<16>(v));
+  v = fmax(v, lane_xor<8>(v));
+  v = fmax(v, lane_xor<4>(v));
+  v = fmax(v, lane_xor<2>(v));
+  return fmax(v, lane_xor<1>(v));
+}
+__device__ __forceinline__ double wave_sum(double v) {
   v += lane_xor<32>(v);
   v += lane_xor<16>(v);
   v += lane_xor<8>(v);
@@ -113,44 +143,51 @@ __device__ __forceinline__ double wave_sum_x(double v) {
   v += lane_xor<2>(v);
   return v + lane_xor<1>(v);
 }
-
-// ---- wave (64-lane) reductions in a fixed butterfly order ------------------------------------
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
-}
-__device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
-}
 __device__ __forceinline__ int wave_max_int(int v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o, kWave));
-  return v;
+  v = max(v, static_cast<int>(lane_xor<32>(static_cast<uint32_t>(v))));
+  v = max(v, static_cast<int>(lane_xor<16>(static_cast<uint32_t>(v))));
+  v = max(v, static_cast<int>(lane_xor<8>(static_cast<uint32_t>(v))));
+  v = max(v, static_cast<int>(lane_xor<4>(static_cast<uint32_t>(v))));
+  v = max(v, static_cast<int>(lane_xor<2>(static_cast<uint32_t>(v))));
+  return max(v, static_cast<int>(lane_xor<1>(static_cast<uint32_t>(v))));
 }
 __device__ __forceinline__ int wave_min_int(int v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = min(v, __shfl_xor(v, o, kWave));
-  return v;
+  v = min(v, static_cast<int>(lane_xor<32>(static_cast<uint32_t>(v))));
+  v = min(v, static_cast<int>(lane_xor<16>(static_cast<uint32_t>(v))));
+  v = min(v, static_cast<int>(lane_xor<8>(static_cast<uint32_t>(v))));
+  v = min(v, static_cast<int>(lane_xor<4>(static_cast<uint32_t>(v))));
+  v = min(v, static_cast<int>(lane_xor<2>(static_cast<uint32_t>(v))));
+  return min(v, static_cast<int>(lane_xor<1>(static_cast<uint32_t>(v))));
 }
-// Inclusive scan over the 64 lanes (Hillis-Steele, fixed order).
+// Inclusive scan over the 64 lanes in a fixed order: a Kogge-Stone scan inside each 16-lane row
+// (DPP row shifts by 1, 2, 4, 8), then row r adds the totals of rows 0 .. r-1, summed from row
+// 0 upwards. All 64 lanes must be active.
 __device__ __forceinline__ double wave_inclusive_scan(double v, int lane) {
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const double t = __shfl_up(v, o, kWave);
-    if (lane >= o) v += t;
-  }
-  return v;
+  v += row_shr_zero<1>(v);
+  v += row_shr_zero<2>(v);
+  v += row_shr_zero<4>(v);
+  v += row_shr_zero<8>(v);
+  const double r0 = read_lane(v, 15), r1 = read_lane(v, 31), r2 = read_lane(v, 47);
+  const double r01 = r0 + r1, r012 = r01 + r2;
+  const int row = lane >> 4;
+  return row == 0 ? v : v + (row == 1 ? r0 : (row == 2 ? r01 : r012));
 }
 __device__ __forceinline__ int wave_inclusive_scan_int(int v, int lane) {
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int t = __shfl_up(v, o, kWave);
-    if (lane >= o) v += t;
-  }
-  return v;
+  v += static_cast<int>(row_shr_zero<1>(static_cast<uint32_t>(v)));
+  v += static_cast<int>(row_shr_zero<2>(static_cast<uint32_t>(v)));
+  v += static_cast<int>(row_shr_zero<4>(static_cast<uint32_t>(v)));
+  v += static_cast<int>(row_shr_zero<8>(static_cast<uint32_t>(v)));
+  const int r0 = read_lane(v, 15), r1 = read_lane(v, 31), r2 = read_lane(v, 47);
+  const int row = lane >> 4;
+  return v + (row == 0 ? 0 : (row == 1 ? r0 : (row == 2 ? r0 + r1 : r0 + r1 + r2)));
+}
+// Exclusive prefix from the inclusive scan `inc`: lane l - 1's value, 0 in lane 0.
+__device__ __forceinline__ double wave_exclusive_of(double inc, int lane) {
+  const double sh = row_shr_zero<1>(inc);
+  const double p0 = read_lane(inc, 15), p1 = read_lane(inc, 31), p2 = read_lane(inc, 47);
+  const int row = lane >> 4;
+  if ((lane & 15) != 0) return sh;
+  return row == 0 ? 0.0 : (row == 1 ? p0 : (row == 2 ? p1 : p2));
 }
 
 // ---- block reductions (blockDim.x = NT, a multiple of 64; `red` holds NT/64 slots) -------------
@@ -207,8 +244,7 @@ template <int NT>
 __device__ __forceinline__ double block_exclusive_scan(double v, double* red, double* total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const double inc = wave_inclusive_scan(v, lane);
-  double exc = __shfl_up(inc, 1, kWave);
-  if (lane == 0) exc = 0.0;
+  const double exc = wave_exclusive_of(inc, lane);
   __syncthreads();
   if (lane == 63) red[w] = inc;
   __syncthreads();

@@ -164,7 +164,7 @@ struct StepKernel {
       m[nt] = max16(L);
     }
 #pragma unroll
-    for (int nt = 0; nt < kNTW; ++nt) m[nt] = fmaxf(m[nt], __shfl_xor(m[nt], 32, kWave));
+    for (int nt = 0; nt < kNTW; ++nt) m[nt] = fmaxf(m[nt], __uint_as_float(lane_xor<32>(__float_as_uint(m[nt]))));
 #pragma unroll
     for (int nt = 0; nt < kNTW; ++nt) {
       float t[16];
@@ -173,7 +173,7 @@ struct StepKernel {
       sm[nt] = (m[nt] == kNegInf) ? 0.0f : sum16(t);
     }
 #pragma unroll
-    for (int nt = 0; nt < kNTW; ++nt) sm[nt] = sm[nt] + __shfl_xor(sm[nt], 32, kWave);
+    for (int nt = 0; nt < kNTW; ++nt) sm[nt] = sm[nt] + __uint_as_float(lane_xor<32>(__float_as_uint(sm[nt])));
 #pragma unroll
     for (int nt = 0; nt < kNTW; ++nt) {
       const int b = group * BG + (bh * kNTW + nt) * 32 + col;
@@ -510,9 +510,8 @@ __global__ __launch_bounds__(SampleCfg<KS>::kThreads) void draft_sample_kernel(S
 #pragma unroll
     for (int i = 0; i < kG; ++i) gs += ssum[kG * lane + i];
     const double inc = wave_inclusive_scan(gs, lane);
-    double exc = __shfl_up(inc, 1, kWave);
-    if (lane == 0) exc = 0.0;
-    const double Z = __shfl(inc, kWave - 1, kWave);
+    const double exc = wave_exclusive_of(inc, lane);
+    const double Z = read_lane(inc, kWave - 1);
     const double target =
         static_cast<double>(p.uniforms[(static_cast<size_t>(b) * (p.gamma + 1) + p.k) * 3]) * Z;
     const bool ok = (Z > 0.0) && (Z < __builtin_inf());
@@ -521,7 +520,7 @@ __global__ __launch_bounds__(SampleCfg<KS>::kThreads) void draft_sample_kernel(S
     double before = 0.0;
     if (cand) {
       const int g = 63 - __clzll(static_cast<long long>(cand));
-      double cum = __shfl(exc, g, kWave);
+      double cum = read_lane(exc, g);
 #pragma unroll
       for (int i = 0; i < kG; ++i) {
         const double si = ssum[kG * g + i];
@@ -648,7 +647,7 @@ __global__ __launch_bounds__(kBlock) void confidence_kernel(ConfArgs p) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc += static_cast<double>(bf16_to_f32(ev[e]) * bf16_to_f32(we[e]));
   }
-  acc = wave_sum_x(acc);
+  acc = wave_sum(acc);
   if (lane == 0) red[wv] = acc;
   __syncthreads();
   if (tid == 0) {

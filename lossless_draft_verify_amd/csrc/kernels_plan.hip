@@ -52,22 +52,50 @@ __device__ __forceinline__ void exchange(double& a, int& ix, int l, bool up) {
   }
 }
 
-// Fill survivals from conf, sort, and turn a[] into tau_i (a[i] = tau_{i+1}). Results in sm.
+constexpr int kPer = kPlanMax / kPlanThreads;   // candidates per thread
+
+// The global inputs of candidate i = tid, issued together at kernel entry so that their
+// latencies overlap each other and the sort (candidates past the first 1024, if any, are read
+// where they are used): its confidence, its lag-slot value, and sps[B + i], sps[B + i + 1] for
+// the admission tests.
+struct PlanInputs {
+  float c, lag;
+  double s0, s1;
+};
+
+__device__ __forceinline__ void load_inputs(PlanInputs& in, const PlanArgs& p, bool lagged) {
+  const int i = threadIdx.x, N = p.B * p.gamma;
+  const float* lag = p.ring + static_cast<size_t>(p.round_index % 2) * N;
+  in.c = (p.conf != nullptr && i < N) ? p.conf[i] : 0.0f;
+  in.lag = (lagged && i < N) ? lag[i] : 0.0f;
+  in.s0 = (i <= N) ? p.sps[p.B + i] : 0.0;
+  in.s1 = (i < N) ? p.sps[p.B + i + 1] : 0.0;
+}
+
+// Fill survivals from the confidences src (c0 = src[tid], already loaded), sort, and turn a[] into
+// tau_i (a[i] = tau_{i+1}). Results in sm.
 //
 // The sort: every 64-element chunk is sorted inside one wave (bitonic, no LDS traffic), then
 // merge levels double the runs. A merge level places every element directly: its position is
 // its rank in its own run plus the number of elements of the partner run that come before it,
-// found by binary search (the left run holds the lower indices, so on equal survivals the left
-// element goes first).
-__device__ void sorted_path(PlanSmem& sm, const float* __restrict__ conf, int B, int gamma) {
+// found by a fixed-step binary search. The left run holds the lower candidate indices, so an
+// element of the right run comes before a left element x iff it is > x, and a left element
+// comes before a right element x iff it is >= x.
+__device__ void sorted_path(PlanSmem& sm, const float* __restrict__ src, float c0, int B,
+                            int gamma) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int N = B * gamma;
+  for (int i = tid; i < N; i += kPlanThreads) {
+    sm.a[i] = static_cast<double>(i == tid ? c0 : src[i]);
+    sm.idx[i] = i;
+  }
+  __syncthreads();
+  // a_{b,j}: running product along each request's path, in place (one thread per request).
   for (int b = tid; b < B; b += kPlanThreads) {
     double prod = 1.0;
     for (int j = 0; j < gamma; ++j) {
-      prod *= static_cast<double>(conf[b * gamma + j]);
+      prod *= sm.a[b * gamma + j];
       sm.a[b * gamma + j] = prod;
-      sm.idx[b * gamma + j] = b * gamma + j;
     }
   }
   __syncthreads();
@@ -93,7 +121,6 @@ __device__ void sorted_path(PlanSmem& sm, const float* __restrict__ conf, int B,
     }
   }
   __syncthreads();
-  constexpr int kPer = kPlanMax / kPlanThreads;
   for (int run = kWave; run < N; run *= 2) {
     double ka[kPer];
     int ki[kPer], pos[kPer];
@@ -109,13 +136,17 @@ __device__ void sorted_path(PlanSmem& sm, const float* __restrict__ conf, int B,
         const int own = left ? p - base : p - base - run;
         const int o0 = left ? base + run : base;
         const int olen = left ? max(0, min(run, N - base - run)) : run;
-        int lo = 0, hi = olen;
-        while (lo < hi) {
-          const int mid = (lo + hi) >> 1;
-          const double y = sm.a[o0 + mid];
-          if (left ? (y > ka[q]) : (y >= ka[q])) lo = mid + 1;
-          else hi = mid;
-        }
+        // Count of partner elements before ka[q]: fixed-step binary lifting over the run
+        // length (every lane takes the same steps; reads are clamped to valid addresses).
+        int lo = 0;
+        auto probe = [&](int at, int add) {
+          const double y = sm.a[min(o0 + min(at, olen - 1), N - 1)];
+          const int hit = static_cast<int>(at < olen) &
+                          (static_cast<int>(y > ka[q]) | (static_cast<int>(!left) & static_cast<int>(y == ka[q])));
+          lo += hit * add;
+        };
+        for (int step = run / 2; step >= 1; step >>= 1) probe(lo + step - 1, step);
+        probe(lo, 1);
         pos[q] = base + own + lo;
       }
     }
@@ -149,13 +180,14 @@ __device__ __forceinline__ double tau_at(const PlanSmem& sm, int i, int B) {
 }
 
 // Admission count along the current path for EARLY_STOP or FULL_PATH.
-__device__ int admit_count(PlanSmem& sm, const double* __restrict__ sps, int B, int N, int mode) {
+__device__ int admit_count(PlanSmem& sm, const PlanInputs& in, const double* __restrict__ sps,
+                           int B, int N, int mode) {
   const int tid = threadIdx.x;
   if (mode == kEarlyStop) {
     int first = N;
     for (int i = tid; i < N; i += kPlanThreads) {
-      const double t0 = tau_at(sm, i, B) * sps[B + i];
-      const double t1 = tau_at(sm, i + 1, B) * sps[B + i + 1];
+      const double t0 = tau_at(sm, i, B) * (i == tid ? in.s0 : sps[B + i]);
+      const double t1 = tau_at(sm, i + 1, B) * (i == tid ? in.s1 : sps[B + i + 1]);
       if (!(t1 > t0)) first = min(first, i);
     }
     return block_min_int<kPlanThreads>(first, sm.red_i);
@@ -164,16 +196,14 @@ __device__ int admit_count(PlanSmem& sm, const double* __restrict__ sps, int B, 
   double best = -__builtin_inf();
   int best_i = INT_MAX;
   for (int i = tid; i <= N; i += kPlanThreads) {
-    const double th = tau_at(sm, i, B) * sps[B + i];
+    const double th = tau_at(sm, i, B) * (i == tid ? in.s0 : sps[B + i]);
     if (th > best) {
       best = th;
       best_i = i;
     }
   }
   // block max of Theta, then the smallest index attaining it
-  double w = best;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) w = fmax(w, __shfl_xor(w, o, kWave));
+  double w = wave_max(best);
   __syncthreads();
   if ((tid & 63) == 0) sm.red_d[tid >> 6] = w;
   __syncthreads();
@@ -190,21 +220,22 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs p) {
   int n_admit = N;
   double capacity = -1.0;
   const bool lagged = (p.mode == kLaggedTopK) && (p.round_index >= 2);
+  PlanInputs in;
+  load_inputs(in, p, lagged);
   if (lagged) {
-    const float* lag = p.ring + static_cast<size_t>(p.round_index % 2) * N;
-    sorted_path(sm, lag, B, gamma);
-    const int k_lag = admit_count(sm, p.sps, B, N, kFullPath);
+    sorted_path(sm, p.ring + static_cast<size_t>(p.round_index % 2) * N, in.lag, B, gamma);
+    const int k_lag = admit_count(sm, in, p.sps, B, N, kFullPath);
     capacity = static_cast<double>(B) + static_cast<double>(k_lag);
     n_admit = min(k_lag, N);
     __syncthreads();
   }
   const bool have_conf = p.conf != nullptr;
   if (have_conf) {
-    sorted_path(sm, p.conf, B, gamma);
+    sorted_path(sm, p.conf, in.c, B, gamma);
     if (p.mode == kEarlyStop || (p.mode == kLaggedTopK && !lagged)) {
-      n_admit = admit_count(sm, p.sps, B, N, kEarlyStop);
+      n_admit = admit_count(sm, in, p.sps, B, N, kEarlyStop);
     } else if (p.mode == kFullPath) {
-      n_admit = admit_count(sm, p.sps, B, N, kFullPath);
+      n_admit = admit_count(sm, in, p.sps, B, N, kFullPath);
     } else if (p.mode == kFullVerify) {
       n_admit = N;
     }
@@ -222,7 +253,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs p) {
   __syncthreads();
   if (p.mode == kLaggedTopK) {
     float* slot = p.ring + static_cast<size_t>(p.round_index % 2) * N;
-    for (int i = tid; i < N; i += kPlanThreads) slot[i] = p.conf[i];
+    for (int i = tid; i < N; i += kPlanThreads) slot[i] = (i == tid) ? in.c : p.conf[i];
   }
   // Ranks: candidate (b, j) is admitted iff its sorted position is < n_admit. Reuse a[] as an
   // int array of positions per candidate.

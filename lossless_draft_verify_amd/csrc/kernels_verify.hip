@@ -63,7 +63,7 @@ __global__ __launch_bounds__(kBlock) void target_stats_kernel(VerifyArgs p) {
       load_segment(p.target + static_cast<size_t>(nxt / p.nseg) * p.V, (nxt % p.nseg) * kSegTokens,
                    p.V, vec4, y);
     float m = max16(x);
-    m = wave_max_x(m);
+    m = wave_max(m);
     lds_barrier();
     if (lane == 0) red_f[w] = m;
     lds_barrier();
@@ -73,7 +73,7 @@ __global__ __launch_bounds__(kBlock) void target_stats_kernel(VerifyArgs p) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) s += static_cast<double>(exp_term(x[j] - m));
     }
-    s = wave_sum_x(s);
+    s = wave_sum(s);
     if (lane == 0) red_d[w] = s;
     lds_barrier();
     if (threadIdx.x == 0) {
@@ -132,8 +132,8 @@ __global__ __launch_bounds__(kBlock) void accept_kernel(VerifyArgs p) {
 #pragma unroll
     for (int r = 0; r < kAcceptRows; ++r) {
       if (r0 + r > ell) break;
-      const float M = wave_max_x(fmaxf(mx[r][0], mx[r][1]));
-      const double z = wave_sum_x(partial_mass(mx[r][0], sg[r][0], M) + partial_mass(mx[r][1], sg[r][1], M));
+      const float M = wave_max(fmaxf(mx[r][0], mx[r][1]));
+      const double z = wave_sum(partial_mass(mx[r][0], sg[r][0], M) + partial_mass(mx[r][1], sg[r][1], M));
       if (lane == 0) lse_s[w][r0 + r] = static_cast<double>(M) + log(z);
     }
   }
@@ -173,8 +173,8 @@ __global__ __launch_bounds__(kBlock) void accept_kernel(VerifyArgs p) {
   int32_t prev_x = anc;
   double lse_d = 0.0;
   if (rejected) {
-    const int32_t xs = __shfl(x0, (last + 63) & 63, kWave);
-    const double ls = __shfl(lsed0, last & 63, kWave);
+    const int32_t xs = read_lane(static_cast<int>(x0), (last + 63) & 63);   // last: wave-uniform
+    const double ls = read_lane(lsed0, last & 63);
     prev_x = (last == 0) ? anc
              : (last - 1 < 64 ? xs : p.tokens[static_cast<size_t>(b) * p.gamma + last - 1]);
     lse_d = (last < 64) ? ls : p.lse[static_cast<size_t>(b) * p.gamma + last];
@@ -296,8 +296,8 @@ __global__ __launch_bounds__(kBlock, 2) void residual_partials_kernel(VerifyArgs
               }
             }
           }
-          W = W + __shfl_xor(W, 32, kWave);
-          O = O + __shfl_xor(O, 32, kWave);
+          W = W + lane_xor<32>(W);
+          O = O + lane_xor<32>(O);
           if (half == 0) {
             const size_t o = static_cast<size_t>(b) * p.ntiles + tok0 / kTileTokens;
             p.ws.rsum[o] = W;
