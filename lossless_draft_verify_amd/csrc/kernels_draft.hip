@@ -13,6 +13,8 @@
 //   draft_sample one workgroup per request: combines the tile partials in fp64, finds the tile
 //                that holds u * Z, recomputes that tile's 32 logits with the same MFMA sequence
 //                (bit-identical), and walks them in fp64 to the drawn token.
+#include <type_traits>
+
 #include "device.h"
 #include "launch.h"
 #include "dma.h"
@@ -441,10 +443,12 @@ __global__ __launch_bounds__(kDmaThreads, 1) void markov_step_dma_kernel(StepArg
 }
 
 // One 1024-thread workgroup per request. Thread t holds a contiguous range of at most 16 tile
-// partials (V <= 2^19) in registers: the row max comes from a block reduction, the tile masses
-// exp(m - M) * s (fp32 exponential, fp64 product) from registers, and wave 0 scans the
-// per-thread sums to find the thread whose range holds u * Z; that thread walks its own
-// registers to the tile. Wave 0 then recomputes the tile's logits and walks them to the token.
+// partials (V <= 2^19) in registers: the row max comes from a block reduction, and each thread
+// writes its tile masses exp(m - M) * s (fp32 exponential, fp64 product) to LDS with their sum.
+// Wave 0 then locates the draw u * Z in three levels, each a wave scan and a ballot: the group
+// of threads, the thread, and the tile (the last candidate with positive mass whose exclusive
+// prefix is <= u * Z at the first two levels, the first tile whose inclusive prefix passes it at
+// the last). Wave 0 recomputes that tile's logits and walks them to the token.
 // r = 512 takes 512 threads: its 32-step tile recompute needs more than 128 registers a lane.
 template <int KS>
 struct SampleCfg {
@@ -462,9 +466,7 @@ __global__ __launch_bounds__(SampleCfg<KS>::kThreads) void draft_sample_kernel(S
   constexpr int kSamplePer = SampleCfg<KS>::kPer;
   __shared__ float red_f[kSampleThreads / 64];
   __shared__ double ssum[kSampleThreads];
-  __shared__ int sh_owner;
-  __shared__ double sh_before, sh_target, sh_Z;
-  __shared__ Located loc;
+  extern __shared__ double mass[];   // [ntiles], dynamic
   __shared__ float Ls[kTileTokens];
   __shared__ float Lc[kTileTokens];
 
@@ -475,106 +477,65 @@ __global__ __launch_bounds__(SampleCfg<KS>::kThreads) void draft_sample_kernel(S
   const size_t urow = (static_cast<size_t>(b) * p.gamma + p.k) * p.V;
   const size_t out = static_cast<size_t>(b) * p.gamma + p.k;
 
-  // The embedding row W1[prev] goes to LDS by an LDS-DMA copy issued first, so it costs no
-  // registers while the partials are processed (the tile recompute reads it back).
-  __shared__ __attribute__((aligned(16))) uint16_t Es[16 * KS];
-  {
-    const int32_t prevtok = p.prev[static_cast<size_t>(b) * p.prev_stride];
-    if (tid < 2 * KS)
-      copy16_to_lds(p.W1 + static_cast<size_t>(prevtok) * (16 * KS) + 8 * tid, lds_addr(Es));
-  }
+  // The partials' loads go out first, unconditionally (index clamped into the row), the count
+  // picked by a uniform branch. The embedding row W1[prev] then goes to LDS by an LDS-DMA copy,
+  // so it costs no registers while the partials are processed (the tile recompute reads it
+  // back); the previous token is loaded before the partials, so both latencies overlap. The
+  // validity of each partial is applied only after the copy is issued.
   const int per = (nt + kSampleThreads - 1) / kSampleThreads;   // uniform, <= kSamplePer
   const int c0 = min(nt, tid * per), c1 = min(nt, c0 + per);
+  const int32_t prevtok = p.prev[static_cast<size_t>(b) * p.prev_stride];
+  __shared__ __attribute__((aligned(16))) uint16_t Es[16 * KS];
   float2 v[kSamplePer];
+  auto load_parts = [&](auto n_c) {
+    constexpr int n = decltype(n_c)::value;
+    float2 t[n];
+#pragma unroll
+    for (int i = 0; i < n; ++i) t[i] = part[min(c0 + i, nt - 1)];
+    if (tid < 2 * KS)
+      copy16_to_lds(p.W1 + static_cast<size_t>(prevtok) * (16 * KS) + 8 * tid, lds_addr(Es));
+#pragma unroll
+    for (int i = 0; i < kSamplePer; ++i)
+      v[i] = (i < n && i < per && c0 + i < c1) ? t[min(i, n - 1)] : make_float2(kNegInf, 0.0f);
+  };
+  if (per <= 4) {
+    load_parts(std::integral_constant<int, 4>{});
+  } else if (per <= 8) {
+    load_parts(std::integral_constant<int, 8>{});
+  } else {
+    load_parts(std::integral_constant<int, kSamplePer>{});
+  }
   float m = kNegInf;
 #pragma unroll
-  for (int i = 0; i < kSamplePer; ++i) {
-    v[i] = make_float2(kNegInf, 0.0f);
-    if (i < per && c0 + i < c1) v[i] = part[c0 + i];
-    m = fmaxf(m, v[i].x);
-  }
+  for (int i = 0; i < kSamplePer; ++i) m = fmaxf(m, v[i].x);
   const float M = block_max<kSampleThreads>(m, red_f);
   double S = 0.0;
 #pragma unroll
-  for (int i = 0; i < kSamplePer; ++i)
-    if (i < per) S += tile_mass(v[i].x, v[i].y, M);
+  for (int i = 0; i < kSamplePer; ++i) {
+    if (i < per && c0 + i < c1) {
+      const double mi = tile_mass(v[i].x, v[i].y, M);
+      mass[c0 + i] = mi;
+      S += mi;
+    }
+  }
   ssum[tid] = S;
   __syncthreads();
-  // Wave 0 finds the owner: the last thread with positive mass whose exclusive prefix is
-  // <= u * Z. Lane l sums threads kG l .. kG l + kG-1 in order, a wave scan gives the group
-  // prefixes and Z, the last group holding such a thread is located by ballot, and its kG
-  // sums are walked in order.
-  if (tid < 64) {
-    constexpr int kG = kSampleThreads / 64;
-    double gs = 0.0;
+  if (tid >= 64) return;
+  // Level 1: lane l sums threads kG l .. kG l + kG - 1 in order; the last group holding a
+  // candidate thread is the last lane with positive sum whose exclusive prefix is <= u * Z.
+  constexpr int kG = kSampleThreads / 64;
+  double gs = 0.0;
 #pragma unroll
-    for (int i = 0; i < kG; ++i) gs += ssum[kG * lane + i];
-    const double inc = wave_inclusive_scan(gs, lane);
-    const double exc = wave_exclusive_of(inc, lane);
-    const double Z = read_lane(inc, kWave - 1);
-    const double target =
-        static_cast<double>(p.uniforms[(static_cast<size_t>(b) * (p.gamma + 1) + p.k) * 3]) * Z;
-    const bool ok = (Z > 0.0) && (Z < __builtin_inf());
-    const unsigned long long cand = __ballot(ok && gs > 0.0 && exc <= target);
-    int own = -1;
-    double before = 0.0;
-    if (cand) {
-      const int g = 63 - __clzll(static_cast<long long>(cand));
-      double cum = read_lane(exc, g);
-#pragma unroll
-      for (int i = 0; i < kG; ++i) {
-        const double si = ssum[kG * g + i];
-        if (si > 0.0 && cum <= target) {
-          own = kG * g + i;
-          before = cum;
-        }
-        cum += si;
-      }
-    }
-    if (lane == 0) {
-      sh_owner = own;
-      sh_before = before;
-      sh_target = target;
-      sh_Z = Z;
-    }
-  }
-  __syncthreads();
-  const int owner = sh_owner;
-  const double target = sh_target, Z = sh_Z;
-  // The owner walks its range in order; if rounding leaves the draw past it, its last positive
-  // tile is taken.
-  if (tid == owner) {
-    Located r;
-    r.chunk = -1;
-    r.take_last = 0;
-    r.before = 0.0;
-    double cum = sh_before, last_before = sh_before;
-    int last = -1;
-#pragma unroll
-    for (int i = 0; i < kSamplePer; ++i) {
-      if (i < per && r.chunk < 0) {
-        const double mi = tile_mass(v[i].x, v[i].y, M);
-        if (mi > 0.0) {
-          last = c0 + i;
-          last_before = cum;
-        }
-        if (cum + mi > target) {
-          r.chunk = c0 + i;
-          r.before = cum;
-        }
-        cum += mi;
-      }
-    }
-    if (r.chunk < 0) {
-      r.chunk = last;
-      r.before = last_before;
-      r.take_last = 1;
-    }
-    loc = r;
-  }
-  __syncthreads();
+  for (int i = 0; i < kG; ++i) gs += ssum[kG * lane + i];
+  const double inc = wave_inclusive_scan(gs, lane);
+  const double exc = wave_exclusive_of(inc, lane);
+  const double Z = read_lane(inc, kWave - 1);
+  const double target =
+      static_cast<double>(p.uniforms[(static_cast<size_t>(b) * (p.gamma + 1) + p.k) * 3]) * Z;
+  const bool ok = (Z > 0.0) && (Z < __builtin_inf());
+  const unsigned long long cand = __ballot(ok && gs > 0.0 && exc <= target);
   const double lse = static_cast<double>(M) + log(Z);
-  if (owner < 0) {  // logits not finite: documented fallback
+  if (!cand) {  // logits not finite: documented fallback
     if (tid == 0) {
       p.tokens[out] = 0;
       p.q[out] = __builtin_nanf("");
@@ -582,14 +543,41 @@ __global__ __launch_bounds__(SampleCfg<KS>::kThreads) void draft_sample_kernel(S
     }
     return;
   }
-  const Located L = loc;
-  if (tid >= 64) return;
-  wait_copies<0>();   // the embedding row copy (long done: the partials were loaded after it)
+  const int g = 63 - __clzll(static_cast<long long>(cand));
+  // Level 2: the threads of group g on lanes 0 .. kG-1 (the group's first thread with positive
+  // mass has prefix read_lane(exc, g) <= u * Z, so there is always a candidate).
+  const double gbase = read_lane(exc, g);
+  const double si = (lane < kG) ? ssum[kG * g + lane] : 0.0;
+  const double tpre = gbase + wave_exclusive_of(wave_inclusive_scan(si, lane), lane);
+  const unsigned long long cand2 = __ballot(lane < kG && si > 0.0 && tpre <= target);
+  const int i2 = 63 - __clzll(static_cast<long long>(cand2));
+  const int t = kG * g + i2;
+  const double tbase = read_lane(tpre, i2);
+  // Level 3: the tiles of thread t on lanes 0 .. n-1 (n <= kSamplePer <= 64): the first whose
+  // inclusive prefix passes u * Z, else (rounding) its last tile with positive mass.
+  const int tc0 = min(nt, t * per), tn = min(nt, tc0 + per) - tc0;
+  const double mi = (lane < tn) ? mass[tc0 + lane] : 0.0;
+  const double mpre = tbase + wave_exclusive_of(wave_inclusive_scan(mi, lane), lane);
+  const unsigned long long hit = __ballot(lane < tn && mpre + mi > target);
+  Located L;
+  if (hit) {
+    const int i3 = __ffsll(static_cast<long long>(hit)) - 1;
+    L.chunk = tc0 + i3;
+    L.before = read_lane(mpre, i3);
+    L.take_last = 0;
+  } else {
+    const unsigned long long pos = __ballot(lane < tn && mi > 0.0);
+    const int i3 = 63 - __clzll(static_cast<long long>(pos));   // thread t has positive mass
+    L.chunk = tc0 + i3;
+    L.before = read_lane(mpre, i3);
+    L.take_last = 1;
+  }
+  const float tm = part[L.chunk].x;   // goes out with the tile's loads
+  wait_copies<0>();   // the embedding row copy (issued with the partials' loads)
   const int tok0 = L.chunk * kTileTokens;
   recompute_tile_lds<KS>(Es, p.W2t, p.U + urow, tok0, p.V, Ls);
   __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_wave_barrier();
-  const float tm = part[L.chunk].x;
   const double f = static_cast<double>(exp_term(tm - M));
   double w = 0.0;
   if (lane < kTileTokens && tok0 + lane < p.V) w = f * static_cast<double>(exp_term(Ls[lane] - tm));
@@ -687,7 +675,8 @@ static hipError_t launch_step_ks(const StepArgs& a, hipStream_t s) {
 }
 template <int KS>
 static hipError_t launch_sample_ks(const SampleArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(draft_sample_kernel<KS>, dim3(a.B), dim3(SampleCfg<KS>::kThreads), 0, s, a);
+  hipLaunchKernelGGL(draft_sample_kernel<KS>, dim3(a.B), dim3(SampleCfg<KS>::kThreads),
+                     static_cast<size_t>(a.ntiles) * sizeof(double), s, a);
   return hipGetLastError();
 }
 

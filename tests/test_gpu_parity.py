@@ -47,6 +47,9 @@ DRAFT_CASES = {
     "b33-v2052-r64-g4": _custom("b33-v2052-r64-g4", seed_id=16, B=33, V=2052, r=64, gamma=4),
     "b20-v8192-r256-g2": _custom("b20-v8192-r256-g2", seed_id=17, B=20, V=8192, r=256, gamma=2,
                                  u_std=3.0, w_std=0.05),
+    # the largest vocabulary the library takes (2^19): 16 tiles per sampler thread, the
+    # sampler's per-tile masses filling 128 KiB of LDS
+    "b3-v524288-r64-g2": _custom("b3-v524288-r64-g2", seed_id=18, B=3, V=1 << 19, r=64, gamma=2),
 }
 
 
