@@ -485,6 +485,7 @@ __global__ __launch_bounds__(SampleCfg<KS>::kThreads) void draft_sample_kernel(S
   const int per = (nt + kSampleThreads - 1) / kSampleThreads;   // uniform, <= kSamplePer
   const int c0 = min(nt, tid * per), c1 = min(nt, c0 + per);
   const int32_t prevtok = p.prev[static_cast<size_t>(b) * p.prev_stride];
+  const int32_t forced = p.force ? p.force[out] : 0;   // the token to condition on, if forced
   __shared__ __attribute__((aligned(16))) uint16_t Es[16 * KS];
   float2 v[kSamplePer];
   auto load_parts = [&](auto n_c) {
@@ -579,23 +580,28 @@ __global__ __launch_bounds__(SampleCfg<KS>::kThreads) void draft_sample_kernel(S
   __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_wave_barrier();
   const double f = static_cast<double>(exp_term(tm - M));
-  double w = 0.0;
-  if (lane < kTileTokens && tok0 + lane < p.V) w = f * static_cast<double>(exp_term(Ls[lane] - tm));
+  // Lane j's token mass for the walk and its probability exp(L_j - lse) (independent of the
+  // walk, so the two overlap; the reported one is read from its lane afterwards).
+  double w = 0.0, qj = 0.0;
+  if (lane < kTileTokens && tok0 + lane < p.V) {
+    w = f * static_cast<double>(exp_term(Ls[lane] - tm));
+    qj = exp(static_cast<double>(Ls[lane]) - lse);
+  }
   const int x = tok0 + walk_tile(w, L.before, target, L.take_last != 0);
   // The token whose probability is reported (and that conditions the next position).
-  const int32_t cond = p.force ? p.force[out] : x;
-  float lc;
+  const int32_t cond = p.force ? forced : x;
+  double qc;
   if (cond / kTileTokens != L.chunk) {
     recompute_tile_lds<KS>(Es, p.W2t, p.U + urow, (cond / kTileTokens) * kTileTokens, p.V, Lc);
     __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_wave_barrier();
-    lc = Lc[cond % kTileTokens];
+    qc = exp(static_cast<double>(Lc[cond % kTileTokens]) - lse);
   } else {
-    lc = Ls[cond % kTileTokens];
+    qc = read_lane(qj, cond % kTileTokens);
   }
   if (tid == 0) {
     p.tokens[out] = x;
-    p.q[out] = static_cast<float>(exp(static_cast<double>(lc) - lse));
+    p.q[out] = static_cast<float>(qc);
     p.lse[out] = lse;
   }
 }
