@@ -18,6 +18,12 @@ __device__ __forceinline__ void copy16_to_lds(const void* src, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds)
                : "memory", "m0");
 }
+// Same, with the non-temporal hint, for operands read once per round (U slices, target rows):
+// they then displace less of what is re-read every step (the W2 columns).
+__device__ __forceinline__ void copy16_to_lds_nt(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(src), "s"(lds)
+               : "memory", "m0");
+}
 // Same, 4 bytes per lane, to lds + 4 * lane.
 __device__ __forceinline__ void copy4_to_lds(const void* src, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(lds)
@@ -30,6 +36,21 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 template <int N>
 __device__ __forceinline__ void wait_copies() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// wait_copies<Base + Step * k>() for a wave-uniform k in [0, K] (the count of copies a wave
+// issued per stage when it varies at run time).
+template <int Base, int Step, int K>
+__device__ __forceinline__ void wait_copies_upto(int k) {
+  if constexpr (K > 0) {
+    if (k >= K) {
+      wait_copies<Base + Step * K>();
+      return;
+    }
+    wait_copies_upto<Base, Step, K - 1>(k);
+  } else {
+    wait_copies<Base>();
+  }
 }
 
 // Value of lane l ^ 32 (v_permlane32_swap exchanges the two half-waves).

@@ -330,8 +330,8 @@ __global__ __launch_bounds__(kDmaThreads, 1) void markov_step_dma_kernel(StepArg
       const int c = (slot % D::kUChunks) ^ (row & 15);
       const int b = min(group * kDmaGroup + row, p.B - 1);
       const int v = min(tok0 + 4 * c, p.V - 4);
-      copy16_to_lds(p.U + (static_cast<size_t>(b) * p.gamma + p.k) * p.V + v,
-                    base + D::kW2Bytes + 1024 * q);
+      copy16_to_lds_nt(p.U + (static_cast<size_t>(b) * p.gamma + p.k) * p.V + v,
+                       base + D::kW2Bytes + 1024 * q);
     }
   };
 

@@ -33,13 +33,24 @@ namespace {
 // reductions use LDS-only barriers, so those loads stay in flight through them.
 constexpr int kStatsBlocksPerCU = 8;
 
+// The row is read once per round: non-temporal loads, so that it displaces less of the W2
+// columns the residual pass reads next.
 __device__ __forceinline__ void load_segment(const float* __restrict__ trow, int t0, int V,
                                              bool vec4, float (&x)[16]) {
+  typedef float nt_f4 __attribute__((ext_vector_type(4)));
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int v = t0 + 1024 * i + 4 * threadIdx.x;
     float o[4];
-    load4(trow, v, V, vec4, o);
+    if (vec4 && v + 3 < V) {
+      const nt_f4 t = __builtin_nontemporal_load(reinterpret_cast<const nt_f4*>(trow + v));
+      o[0] = t.x;
+      o[1] = t.y;
+      o[2] = t.z;
+      o[3] = t.w;
+    } else {
+      load4(trow, v, V, vec4, o);
+    }
 #pragma unroll
     for (int e = 0; e < 4; ++e) x[4 * i + e] = (v + e < V) ? o[e] : kNegInf;
   }
@@ -372,6 +383,17 @@ __global__ __launch_bounds__(kResThreads, 1) void residual_dma_kernel(VerifyArgs
   __syncthreads();
   const int row_own = 32 * rq + col;
   const bool wave_active = 32 * rq < gcount;
+  // Copies of request rows are issued only for rows below gcount (a 1 KB copy covers
+  // 1024 / (16 kRowChunks) rows; a wave's copies cover consecutive rows, so its valid ones are a
+  // prefix): nrow_w row copies per kind and ne_w embedding-row copies for this wave. The waits
+  // use this wave's exact count of copies per item.
+  constexpr int kRowsPerCopy = 1024 / (16 * D::kRowChunks);
+  constexpr int kERowsPerCopy = 1024 / (16 * D::kW2Chunks);
+  const int nrow_w = min(D::kRowCopies, max(0, (gcount - kRowsPerCopy * D::kRowCopies * wave +
+                                                kRowsPerCopy - 1) / kRowsPerCopy));
+  const int ne_w = min(D::kECopies, max(0, (gcount - kERowsPerCopy * D::kECopies * wave +
+                                            kERowsPerCopy - 1) / kERowsPerCopy));
+  auto wait_item = [&]() { wait_copies_upto<D::kW2Copies, 2, D::kRowCopies>(nrow_w); };
 
   const uint32_t stage_addr = lds_addr(stage);
   uint32_t a_off[D::kAOffs], u_off[2];
@@ -403,16 +425,17 @@ __global__ __launch_bounds__(kResThreads, 1) void residual_dma_kernel(VerifyArgs
     }
 #pragma unroll
     for (int i = 0; i < D::kRowCopies; ++i) {
+      if (i >= nrow_w) break;   // wave-uniform: copies past the group's rows are not issued
       const int q = wave * D::kRowCopies + i;
       const int slot = 64 * q + lane;
       const int row = slot / D::kRowChunks;
       const int c = (slot % D::kRowChunks) ^ (row & 15);
       const int v = min(tok0 + 4 * c, p.V - 4);
       const ResRec& R = rec[row];
-      copy16_to_lds(p.U + (static_cast<size_t>(R.b) * p.gamma + R.j - 1) * p.V + v,
-                    base + D::kW2Bytes + 1024 * q);
-      copy16_to_lds(p.target + static_cast<size_t>(R.erow) * p.V + v,
-                    base + D::kW2Bytes + D::kRowBytes + 1024 * q);
+      copy16_to_lds_nt(p.U + (static_cast<size_t>(R.b) * p.gamma + R.j - 1) * p.V + v,
+                       base + D::kW2Bytes + 1024 * q);
+      copy16_to_lds_nt(p.target + static_cast<size_t>(R.erow) * p.V + v,
+                       base + D::kW2Bytes + D::kRowBytes + 1024 * q);
     }
   };
 
@@ -439,6 +462,7 @@ __global__ __launch_bounds__(kResThreads, 1) void residual_dma_kernel(VerifyArgs
     const uint32_t ebase = stage_addr + D::kStageBytes;
 #pragma unroll
     for (int i = 0; i < D::kECopies; ++i) {
+      if (i >= ne_w) break;   // wave-uniform
       const int q = wave * D::kECopies + i;
       const int slot = 64 * q + lane;
       const int row = slot / D::kW2Chunks;
@@ -447,7 +471,7 @@ __global__ __launch_bounds__(kResThreads, 1) void residual_dma_kernel(VerifyArgs
     }
   }
   issue(0);
-  wait_copies<D::kCopies>();
+  wait_item();   // the embedding rows (issued first) have landed
   asm volatile("s_barrier" ::: "memory");
   u16x8_t e[KS];
   {
@@ -463,7 +487,7 @@ __global__ __launch_bounds__(kResThreads, 1) void residual_dma_kernel(VerifyArgs
   for (int j = 0; j < n; ++j) {
     if (j + 1 < n) {
       issue(j + 1);
-      wait_copies<D::kCopies>();
+      wait_item();   // outstanding: at most item j + 1's copies
     } else {
       wait_copies<0>();
     }
