@@ -10,6 +10,7 @@ import torch
 import oracle
 import lossless_draft_verify_amd as L
 from lossless_draft_verify_amd import workloads as W
+from oracle_chain import OracleChain
 from parity import (LSE_TOL, PLAN_TIE, PROB_TOL, MismatchCounter, bits, compare_draft, dims_of,
                     gpu_draft, log, np_, oracle_draft)
 
@@ -279,6 +280,153 @@ def test_round_full_size(name):
     emit.add(nt[same], ov["next_token"][same], ov["emit_margin"][same])
     assert np.abs(be[same] - ov["beta_emit"][same]).max() <= PROB_TOL
     log(f"  verify: mean accepted {al.mean():.2f}; {acc.report()}; {emit.report()}")
+
+
+def _T(a, dt=torch.int32):
+    return torch.as_tensor(np.ascontiguousarray(a), dtype=dt, device=DEV)
+
+
+def test_lagged_chain_parity():
+    """Twenty chained rounds of the lagged planner at a scaled high-load shape (two request
+    groups, the second ragged; a vocabulary tail): the oracle drives the chain (next anchor =
+    its emitted token), and every round each entry point gets the oracle's inputs and is compared
+    with it, the device confidence ring included."""
+    wl = W.scaled(W.WORKLOADS["b512-v129280-g5-lagged"], name="chain-b160-v4100-g5", seed_id=32,
+                  B=160, V=4100, d=256, sps_scale=160.0)
+    log(f"[chain] {wl.name}: oracle chain of {wl.rounds} rounds")
+    wts_cpu = W.weights(wl)
+    wts = {k: v.to(DEV) for k, v in wts_cpu.items()}
+    chain = OracleChain(wl, wts_cpu)
+    recs, _ = chain.run(chain.initial_state(), wl.rounds)
+    d = dims_of(wl)
+    ring_g = torch.zeros((2, wl.B, wl.gamma), dtype=torch.float32, device=DEV)
+    sps_t = _T(W.sps_table(wl), torch.float64)
+    temps = W.temperatures(wl).to(DEV)
+    cd, ca, ce = (MismatchCounter("chain draft"), MismatchCounter("chain accept"),
+                  MismatchCounter("chain emit"))
+    for rec in recs:
+        inp = {k: v.to(DEV) for k, v in rec["inp"].items()}
+        inp["anchor"] = _T(rec["anchor"])
+        o, p, ov = rec["draft"], rec["plan"], rec["verify"]
+        gu = gpu_draft(wl, inp, wts)
+        cd.add(gu["tokens"][:, :1], o["tokens"][:, :1], o["margin"][:, :1])
+        g = gpu_draft(wl, inp, wts, force=o["tokens"], dbg=True)
+        compare_draft(g, o, cd)
+        tok = _T(o["tokens"])
+        cg = L.confidence(d, inp["h"], wts["W1"], wts["w"], temps, inp["anchor"], tok)
+        assert np.abs(np_(cg) - rec["conf"]).max() <= PROB_TOL
+        dl, ro, st = L.plan(d, _T(rec["conf"], torch.float32), sps_t, L.LAGGED_TOPK, ring=ring_g,
+                            round_index=rec["t"])
+        torch.cuda.synchronize()
+        assert np.array_equal(np_(ring_g), rec["ring_after"]), rec["t"]
+        if p["margin"] > PLAN_TIE:
+            assert np.array_equal(np_(dl), p["draft_len"]), rec["t"]
+            assert np.array_equal(np_(ro), p["row_offsets"]), rec["t"]
+            assert np.allclose(np_(st), p["stats"], rtol=1e-12, atol=0), rec["t"]
+        al, nt, be, fl = L.verify(d, _T(rec["target"], torch.float32), _T(p["row_offsets"]),
+                                  _T(p["draft_len"]), inp["U"], wts["W1"], wts["W2t"],
+                                  inp["anchor"], tok, _T(o["q"], torch.float32), g["lse_t"],
+                                  inp["uniforms"])
+        torch.cuda.synchronize()
+        al, nt, be, fl = np_(al), np_(nt), np_(be), np_(fl)
+        ca.add(al, ov["accept_len"], decisive_margin(ov, al, wl.gamma))
+        same = al == ov["accept_len"]
+        ce.add(nt[same], ov["next_token"][same], ov["emit_margin"][same])
+        assert np.array_equal(fl[same].astype(np.uint32), ov["flags"][same])
+        assert np.abs(be[same] - ov["beta_emit"][same]).max() <= PROB_TOL
+        log(f"  round {rec['t']}: B_tot {p['stats'][0]:.0f}, capacity {p['stats'][3]:.0f}, "
+            f"mean accepted {al.mean():.2f}")
+    for c in (cd, ca, ce):
+        c.check_rate()
+    log(f"  {cd.report()}; {ca.report()}; {ce.report()}")
+
+
+def _admission(conf, sps, B, gamma, mode):
+    """Admission count along the survival order (numpy, from the definition): running fp64
+    products per request, order by (-a, candidate index), tau_i = B + the first i survivals,
+    Theta_i = tau_i * sps[B + i]; early stop at the first non-increase, full path at the first
+    maximum. Returns (count, order, relative margin of the deciding comparison)."""
+    a = np.cumprod(conf.astype(np.float64), axis=1).reshape(-1)
+    n = a.size
+    order = np.lexsort((np.arange(n), -a))
+    tau = B + np.concatenate([[0.0], np.cumsum(a[order])])
+    theta = tau * sps[B:B + n + 1]
+    if mode == L.EARLY_STOP:
+        stop = np.nonzero(~(theta[1:] > theta[:-1]))[0]
+        count = int(stop[0]) if stop.size else n
+        k = min(count, n - 1)   # comparisons 0 .. k decided the count
+        gaps = np.abs(theta[1:k + 2] - theta[:k + 1]) / theta[:k + 1]
+        return count, order, float(gaps.min()) if gaps.size else np.inf
+    count = int(np.argmax(theta))
+    rest = np.delete(theta, count)
+    margin = (theta[count] - rest.max()) / theta[count] if rest.size else np.inf
+    return count, order, float(margin)
+
+
+def test_lagged_chain_full_size():
+    """The high-load workload at full size (B = 512, V = 129280) for its 20 chained rounds, in
+    the launch configuration the bench uses, driven by the GPU's own draws (next anchor = the
+    emitted token). Checked by properties that hold at any size: the ring holds each round's
+    confidences for the round two later; the lengths follow the lagged-capacity definition
+    recomputed from the confidences (numpy); the packed offsets, the accept lengths, the emitted
+    tokens and the beta values are consistent."""
+    wl = W.WORKLOADS["b512-v129280-g5-lagged"]
+    log(f"[chain] {wl.name}: {wl.rounds} rounds on the GPU")
+    wts = W.weights(wl, DEV)
+    d = dims_of(wl)
+    B, g, V = wl.B, wl.gamma, wl.V
+    sps = W.sps_table(wl)
+    sps_t, temps = _T(sps, torch.float64), W.temperatures(wl).to(DEV)
+    ring = torch.zeros((2, B, g), dtype=torch.float32, device=DEV)
+    confs, anchor = [], None
+    checked = 0
+    for t in range(wl.rounds):
+        inp = W.round_inputs(wl, t, DEV)
+        if anchor is not None:
+            inp["anchor"] = anchor
+        logits = torch.empty_like(inp["U"])
+        tok, q, lse = L.markov_draft(d, inp["U"], wts["W1"], wts["W2t"], inp["anchor"],
+                                     inp["uniforms"], logits_dbg=logits)
+        conf = L.confidence(d, inp["h"], wts["W1"], wts["w"], temps, inp["anchor"], tok)
+        before = np_(ring).copy()
+        dl, ro, st = L.plan(d, conf, sps_t, L.LAGGED_TOPK, ring=ring, round_index=t)
+        torch.cuda.synchronize()
+        c, dl_h, ro_h, st_h, after = np_(conf), np_(dl), np_(ro), np_(st), np_(ring)
+        confs.append(c)
+        assert np.array_equal(after[t % 2], c) and np.array_equal(after[1 - t % 2], before[1 - t % 2])
+        if t >= 2:
+            assert np.array_equal(before[t % 2], confs[t - 2])
+            k_lag, _, m_lag = _admission(confs[t - 2], sps, B, g, L.FULL_PATH)
+            _, order, _ = _admission(c, sps, B, g, L.FULL_PATH)
+            n = min(k_lag, B * g)
+            if m_lag > PLAN_TIE:
+                assert st_h[3] == B + k_lag
+                assert np.array_equal(dl_h, np.bincount(order[:n] // g, minlength=B)), t
+                checked += 1
+        else:
+            n, order, m = _admission(c, sps, B, g, L.EARLY_STOP)
+            if m > PLAN_TIE:
+                assert np.array_equal(dl_h, np.bincount(order[:n] // g, minlength=B)), t
+                checked += 1
+        assert st_h[0] == B + dl_h.sum()
+        assert np.array_equal(ro_h, np.concatenate([[0], np.cumsum(1 + dl_h)]))
+        target = W.pack_rows(W.target_dense(logits, inp["U_bonus"], inp["noise"]), dl)
+        del logits
+        al, nt, be, fl = L.verify(d, target, ro, dl, inp["U"], wts["W1"], wts["W2t"],
+                                  inp["anchor"], tok, q, lse, inp["uniforms"])
+        torch.cuda.synchronize()
+        al_h, nt_h, be_h, fl_h = np_(al), np_(nt), np_(be), np_(fl)
+        assert ((al_h >= 0) & (al_h <= dl_h)).all()
+        assert ((nt_h >= 0) & (nt_h < V)).all()
+        assert (fl_h == 0).all()
+        bonus = al_h == dl_h
+        assert (be_h[bonus] == -1.0).all()
+        assert ((be_h[~bonus] >= 0.0) & (be_h[~bonus] <= 1.0)).all()
+        anchor = nt.to(torch.int32).contiguous()
+        log(f"  round {t}: B_tot {st_h[0]:.0f}, capacity {st_h[3]:.0f}, mean accepted "
+            f"{al_h.mean():.2f}, bonus {bonus.mean():.2f}")
+        del inp, target
+    assert checked >= wl.rounds - 2
 
 
 def test_determinism_bitwise():
