@@ -347,6 +347,60 @@ __device__ Located locate_chunk_t(int n, TargetFn target_of, MassFn mass, double
   return res;
 }
 
+// The same draw located by one wave, for blocks whose NT threads each own a contiguous range of
+// `per` chunks (thread t: chunks t per .. t per + per - 1, clipped to n; per <= 64) and have
+// written the sum of their range, added in chunk order, to ssum[t]; mass(c) must be readable by
+// every lane (LDS). Three levels, each a wave scan and a ballot: the group of NT / 64 threads,
+// the thread (the last with positive mass whose exclusive prefix is <= the target), and the
+// chunk (the first whose inclusive prefix passes the target, else, when rounding leaves the draw
+// past the thread's range, its last positive chunk with take_last set). The prefix of a thread
+// is its group's prefix plus the sums before it in the group; the first positive thread of the
+// chosen group has exactly its group's prefix, so the second level always finds one. All 64
+// lanes of the wave must be active; every lane gets the result.
+template <int NT, class MassFn, class TargetFn>
+__device__ Located wave_locate(const double* ssum, int n, int per, TargetFn target_of,
+                               MassFn mass) {
+  constexpr int kG = NT / 64;
+  const int lane = threadIdx.x & 63;
+  double gs = 0.0;
+#pragma unroll
+  for (int i = 0; i < kG; ++i) gs += ssum[kG * lane + i];
+  const double inc = wave_inclusive_scan(gs, lane);
+  const double exc = wave_exclusive_of(inc, lane);
+  Located r;
+  r.total = read_lane(inc, kWave - 1);
+  r.target = target_of(r.total);
+  r.chunk = -1;
+  r.take_last = 0;
+  r.before = 0.0;
+  const bool ok = (r.total > 0.0) && (r.total < __builtin_inf());
+  const unsigned long long cand = __ballot(ok && gs > 0.0 && exc <= r.target);
+  if (!cand) return r;
+  const int g = 63 - __clzll(static_cast<long long>(cand));
+  const double gbase = read_lane(exc, g);
+  const double si = (lane < kG) ? ssum[kG * g + lane] : 0.0;
+  const double tpre = gbase + wave_exclusive_of(wave_inclusive_scan(si, lane), lane);
+  const unsigned long long cand2 = __ballot(lane < kG && si > 0.0 && tpre <= r.target);
+  const int i2 = 63 - __clzll(static_cast<long long>(cand2));
+  const int t = kG * g + i2;
+  const double tbase = read_lane(tpre, i2);
+  const int tc0 = min(n, t * per), tn = min(n, tc0 + per) - tc0;
+  const double mi = (lane < tn) ? mass(tc0 + lane) : 0.0;
+  const double mpre = tbase + wave_exclusive_of(wave_inclusive_scan(mi, lane), lane);
+  const unsigned long long hit = __ballot(lane < tn && mpre + mi > r.target);
+  int i3;
+  if (hit) {
+    i3 = __ffsll(static_cast<long long>(hit)) - 1;
+  } else {
+    const unsigned long long pos = __ballot(lane < tn && mi > 0.0);   // thread t has positive mass
+    i3 = 63 - __clzll(static_cast<long long>(pos));
+    r.take_last = 1;
+  }
+  r.chunk = tc0 + i3;
+  r.before = read_lane(mpre, i3);
+  return r;
+}
+
 template <int NT, class MassFn>
 __device__ Located locate_chunk(int n, double u, MassFn mass, double* red_d, int* red_i,
                                 Located* shared_out) {

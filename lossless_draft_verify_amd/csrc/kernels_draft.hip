@@ -522,56 +522,19 @@ __global__ __launch_bounds__(SampleCfg<KS>::kThreads) void draft_sample_kernel(S
   ssum[tid] = S;
   __syncthreads();
   if (tid >= 64) return;
-  // Level 1: lane l sums threads kG l .. kG l + kG - 1 in order; the last group holding a
-  // candidate thread is the last lane with positive sum whose exclusive prefix is <= u * Z.
-  constexpr int kG = kSampleThreads / 64;
-  double gs = 0.0;
-#pragma unroll
-  for (int i = 0; i < kG; ++i) gs += ssum[kG * lane + i];
-  const double inc = wave_inclusive_scan(gs, lane);
-  const double exc = wave_exclusive_of(inc, lane);
-  const double Z = read_lane(inc, kWave - 1);
-  const double target =
-      static_cast<double>(p.uniforms[(static_cast<size_t>(b) * (p.gamma + 1) + p.k) * 3]) * Z;
-  const bool ok = (Z > 0.0) && (Z < __builtin_inf());
-  const unsigned long long cand = __ballot(ok && gs > 0.0 && exc <= target);
-  const double lse = static_cast<double>(M) + log(Z);
-  if (!cand) {  // logits not finite: documented fallback
+  const double u =
+      static_cast<double>(p.uniforms[(static_cast<size_t>(b) * (p.gamma + 1) + p.k) * 3]);
+  const Located L = wave_locate<kSampleThreads>(
+      ssum, nt, per, [u](double Z) { return u * Z; }, [&](int c) { return mass[c]; });
+  const double target = L.target;
+  const double lse = static_cast<double>(M) + log(L.total);
+  if (L.chunk < 0) {  // logits not finite: documented fallback
     if (tid == 0) {
       p.tokens[out] = 0;
       p.q[out] = __builtin_nanf("");
       p.lse[out] = __builtin_nan("");
     }
     return;
-  }
-  const int g = 63 - __clzll(static_cast<long long>(cand));
-  // Level 2: the threads of group g on lanes 0 .. kG-1 (the group's first thread with positive
-  // mass has prefix read_lane(exc, g) <= u * Z, so there is always a candidate).
-  const double gbase = read_lane(exc, g);
-  const double si = (lane < kG) ? ssum[kG * g + lane] : 0.0;
-  const double tpre = gbase + wave_exclusive_of(wave_inclusive_scan(si, lane), lane);
-  const unsigned long long cand2 = __ballot(lane < kG && si > 0.0 && tpre <= target);
-  const int i2 = 63 - __clzll(static_cast<long long>(cand2));
-  const int t = kG * g + i2;
-  const double tbase = read_lane(tpre, i2);
-  // Level 3: the tiles of thread t on lanes 0 .. n-1 (n <= kSamplePer <= 64): the first whose
-  // inclusive prefix passes u * Z, else (rounding) its last tile with positive mass.
-  const int tc0 = min(nt, t * per), tn = min(nt, tc0 + per) - tc0;
-  const double mi = (lane < tn) ? mass[tc0 + lane] : 0.0;
-  const double mpre = tbase + wave_exclusive_of(wave_inclusive_scan(mi, lane), lane);
-  const unsigned long long hit = __ballot(lane < tn && mpre + mi > target);
-  Located L;
-  if (hit) {
-    const int i3 = __ffsll(static_cast<long long>(hit)) - 1;
-    L.chunk = tc0 + i3;
-    L.before = read_lane(mpre, i3);
-    L.take_last = 0;
-  } else {
-    const unsigned long long pos = __ballot(lane < tn && mi > 0.0);
-    const int i3 = 63 - __clzll(static_cast<long long>(pos));   // thread t has positive mass
-    L.chunk = tc0 + i3;
-    L.before = read_lane(mpre, i3);
-    L.take_last = 1;
   }
   const float tm = part[L.chunk].x;   // goes out with the tile's loads
   wait_copies<0>();   // the embedding row copy (issued with the partials' loads)

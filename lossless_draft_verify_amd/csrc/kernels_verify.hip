@@ -545,14 +545,15 @@ __global__ __launch_bounds__(kResThreads, 1) void residual_dma_kernel(VerifyArgs
 template <int KS>
 __global__ __launch_bounds__(kBlock) void emit_sample_kernel(VerifyArgs p) {
   extern __shared__ double stage[];   // padded: residual tile masses, or one segment's terms
-  __shared__ double red_d[kBlock / 64];
-  __shared__ float red_f[kBlock / 64];
-  __shared__ int red_i[kBlock / 64];
+  __shared__ double ssum[kBlock];     // per-thread sums over contiguous ranges (wave-0 search)
+  __shared__ double osum[kBlock];     // per-thread overlap sums (beta)
   __shared__ Located loc;
+  __shared__ float seg_m, row_m;     // the chosen segment's max, the row's largest segment max
   __shared__ float Ls[kTileTokens];
+  __shared__ __attribute__((aligned(16))) uint16_t Es[16 * KS];
 
   const int b = blockIdx.x;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int kind = p.ws.ekind[b];
   const int j = p.ws.epos[b];
   const int erow = p.ws.erow[b];
@@ -563,9 +564,11 @@ __global__ __launch_bounds__(kBlock) void emit_sample_kernel(VerifyArgs p) {
   int token = 0;
 
   if (kind == kEmitResidual) {
-    // Residual tile masses into LDS (16 loads in flight per thread) and their overlap sum.
+    // Residual tile masses into LDS (16 loads in flight per thread) with the overlap partials;
+    // the embedding row of the position's previous token is copied into LDS behind them.
     const size_t base = static_cast<size_t>(b) * p.ntiles;
     const int nt = p.ntiles;
+    const int32_t prevtok = emit_prev(p, b, j);
     constexpr int kBatch = 16;
     double o = 0.0;
     for (int c0 = 0; c0 < nt; c0 += kBlock * kBatch) {
@@ -576,6 +579,8 @@ __global__ __launch_bounds__(kBlock) void emit_sample_kernel(VerifyArgs p) {
         w[i] = p.ws.rsum[base + c];
         ov[i] = p.ws.rmin[base + c];
       }
+      if (c0 == 0 && tid < 2 * KS)
+        copy16_to_lds(p.W1 + static_cast<size_t>(prevtok) * (16 * KS) + 8 * tid, lds_addr(Es));
 #pragma unroll
       for (int i = 0; i < kBatch; ++i) {
         const int c = c0 + i * kBlock + tid;
@@ -585,71 +590,113 @@ __global__ __launch_bounds__(kBlock) void emit_sample_kernel(VerifyArgs p) {
         }
       }
     }
-    o = block_sum<kBlock>(o, red_d);
-    if (tid == 0 && p.beta_emit) p.beta_emit[b] = static_cast<float>(o);
-    const Located L = locate_chunk<kBlock>(nt, u, [&](int c) { return stage[padded(c)]; }, red_d,
-                                           red_i, &loc);
+    __syncthreads();
+    const int per = (nt + kBlock - 1) / kBlock;   // <= 64 (V <= 2^19)
+    const int c0 = min(nt, tid * per), c1 = min(nt, c0 + per);
+    double S = 0.0;
+    for (int c = c0; c < c1; ++c) S += stage[padded(c)];
+    ssum[tid] = S;
+    osum[tid] = o;
+    __syncthreads();
+    if (tid < 64) {
+      double og = 0.0;
+#pragma unroll
+      for (int i = 0; i < kBlock / 64; ++i) og += osum[(kBlock / 64) * lane + i];
+      og = wave_sum(og);
+      if (tid == 0 && p.beta_emit) p.beta_emit[b] = static_cast<float>(og);
+      const Located L = wave_locate<kBlock>(
+          ssum, nt, per, [u](double Z) { return u * Z; }, [&](int c) { return stage[padded(c)]; });
+      if (tid == 0) loc = L;
+    }
+    __syncthreads();
+    const Located L = loc;
     if (L.chunk < 0) {
       fl |= 2u;
       from_target = true;
     } else {
+      if (tid >= 64) return;
       const int tok0 = L.chunk * kTileTokens;
-      if (tid < 64) {
-        const int lane = tid;
-        const float* Urow = p.U + (static_cast<size_t>(b) * p.gamma + j - 1) * p.V;
-        const float tv = (lane < kTileTokens && tok0 + lane < p.V) ? trow[tok0 + lane] : 0.0f;
-        recompute_tile<KS>(p.W1, p.W2t, Urow, emit_prev(p, b, j), tok0, p.V, Ls);
-        __builtin_amdgcn_s_waitcnt(0);
-        __builtin_amdgcn_wave_barrier();
-        double w = 0.0;
-        if (lane < kTileTokens && tok0 + lane < p.V) {
-          double ov;
-          residual_pair(Ls[lane], tv, p.lse[static_cast<size_t>(b) * p.gamma + j - 1],
-                        p.ws.erow_lse[b], w, ov);
-        }
-        token = tok0 + walk_tile(w, L.before, L.target, L.take_last != 0);
+      const float* Urow = p.U + (static_cast<size_t>(b) * p.gamma + j - 1) * p.V;
+      const float tv = (lane < kTileTokens && tok0 + lane < p.V) ? trow[tok0 + lane] : 0.0f;
+      wait_copies<0>();   // the embedding row
+      recompute_tile_lds<KS>(Es, p.W2t, Urow, tok0, p.V, Ls);
+      __builtin_amdgcn_s_waitcnt(0);
+      __builtin_amdgcn_wave_barrier();
+      double w = 0.0;
+      if (lane < kTileTokens && tok0 + lane < p.V) {
+        double ov;
+        residual_pair(Ls[lane], tv, p.lse[static_cast<size_t>(b) * p.gamma + j - 1],
+                      p.ws.erow_lse[b], w, ov);
       }
+      token = tok0 + walk_tile(w, L.before, L.target, L.take_last != 0);
     }
   } else if (tid == 0 && p.beta_emit) {
     p.beta_emit[b] = -1.0f;
   }
 
   if (from_target) {
-    // Draw from p_t of the emission row: segment, then the token inside it.
+    // Draw from p_t of the emission row. Wave 0 picks the segment: lane l owns segments 2l,
+    // 2l + 1 (nseg <= 128), masses relative to the row's largest segment max.
     const size_t base = static_cast<size_t>(erow) * p.nseg;
-    float m = kNegInf;
-    for (int s = tid; s < p.nseg; s += kBlock) m = fmaxf(m, p.ws.seg_max[base + s]);
-    const float M = block_max<kBlock>(m, red_f);
-    auto smass = [&](int s) { return partial_mass(p.ws.seg_max[base + s], p.ws.seg_sum[base + s], M); };
-    const Located S = locate_chunk<kBlock>(p.nseg, u, smass, red_d, red_i, &loc);
+    if (tid < 64) {
+      float m[2];
+      double sg[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int s = 2 * lane + i;
+        m[i] = (s < p.nseg) ? p.ws.seg_max[base + s] : kNegInf;
+        sg[i] = (s < p.nseg) ? p.ws.seg_sum[base + s] : 0.0;
+      }
+      const float M = wave_max(fmaxf(m[0], m[1]));
+      double S = 0.0;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const double ms = partial_mass(m[i], sg[i], M);
+        stage[2 * lane + i] = ms;
+        S += ms;
+      }
+      ssum[lane] = S;
+      __builtin_amdgcn_s_waitcnt(0);   // this wave's LDS writes, read back by other lanes
+      __builtin_amdgcn_wave_barrier();
+      const Located Sg = wave_locate<64>(
+          ssum, p.nseg, 2, [u](double Z) { return u * Z; }, [&](int c) { return stage[c]; });
+      if (tid == 0) {
+        loc = Sg;
+        row_m = M;
+      }
+      if (Sg.chunk >= 0 && lane == (Sg.chunk >> 1)) seg_m = m[Sg.chunk & 1];
+    }
+    __syncthreads();
+    const Located S = loc;
     if (S.chunk < 0) {
       token = 0;
     } else {
+      // The segment's 4096 terms exp(t - segment max): thread t takes tokens 16 t .. 16 t + 15.
       const int t0 = S.chunk * kSegTokens;
       const int n = min(kSegTokens, p.V - t0);
-      const float sm = p.ws.seg_max[base + S.chunk];
+      const float sm = seg_m;
       const bool vec4 = (p.V & 3) == 0;
-      float x[16];
+      double Sum = 0.0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float o4[4];
-        load4(trow, t0 + 1024 * i + 4 * tid, p.V, vec4, o4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) x[4 * i + e] = o4[e];
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
+        float x4[4];
+        load4(trow, t0 + 16 * tid + 4 * i, p.V, vec4, x4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int c = 1024 * i + 4 * tid + e;
-          if (c < n) stage[padded(c)] = static_cast<double>(exp_term(x[4 * i + e] - sm));
+          const int c = 16 * tid + 4 * i + e;
+          const double ms = (c < n) ? static_cast<double>(exp_term(x4[e] - sm)) : 0.0;
+          stage[padded(c)] = ms;
+          Sum += ms;
         }
+      }
+      ssum[tid] = Sum;
       __syncthreads();
-      const double f = exp(static_cast<double>(sm) - static_cast<double>(M));
+      if (tid >= 64) return;
+      const double f = exp(static_cast<double>(sm) - static_cast<double>(row_m));
       const double tgt = S.take_last ? __builtin_inf() : (S.target - S.before) / f;
-      const Located T = locate_chunk_t<kBlock>(n, [tgt](double) { return tgt; },
-                                               [&](int c) { return stage[padded(c)]; }, red_d,
-                                               red_i, &loc);
+      const Located T = wave_locate<kBlock>(
+          ssum, n, kSegTokens / kBlock, [tgt](double) { return tgt; },
+          [&](int c) { return stage[padded(c)]; });
       token = t0 + (T.chunk >= 0 ? T.chunk : 0);
     }
   }
