@@ -110,42 +110,83 @@ __global__ __launch_bounds__(kBlock) void accept_kernel(VerifyArgs p) {
   const int ell = p.draft_len[b];
   const int off = p.row_offsets[b];
   uint32_t fl = 0;
-  // 0. The accept-test inputs of the first 64 positions go out first (the target value of a
-  //    drafted token needs only the token and the row offset).
+  // 0. Everything that needs only (ell, off) goes out first: the accept-test inputs of the first
+  //    64 positions and, for nseg <= 32, the segment statistics of every verified row; the
+  //    target value of a drafted token waits for the token.
   float tx0 = 0.0f, u0 = 0.0f, q0 = 0.0f;
   int32_t x0 = 0;
   double lsed0 = 0.0;
   const int32_t anc = p.anchor[b];
   if (lane < ell) {
-    const int32_t x = p.tokens[static_cast<size_t>(b) * p.gamma + lane];
-    x0 = x;
+    x0 = p.tokens[static_cast<size_t>(b) * p.gamma + lane];
     lsed0 = p.lse[static_cast<size_t>(b) * p.gamma + lane];
-    tx0 = p.target[static_cast<size_t>(off + lane) * p.V + x];
     u0 = p.uniforms[(static_cast<size_t>(b) * (p.gamma + 1) + lane) * 3 + 1];
     q0 = p.q[static_cast<size_t>(b) * p.gamma + lane];
   }
-  // 1. log-sum-exp of rows off .. off + ell (segments: lane + 64 i, i < 2, nseg <= 128).
-  for (int r0 = 0; r0 <= ell; r0 += kAcceptRows) {
-    float mx[kAcceptRows][2];
-    double sg[kAcceptRows][2];
+  if (p.nseg <= 32) {
+    // Rows in pairs: lanes 0..31 take row 2 pr, lanes 32..63 row 2 pr + 1, lane & 31 a segment.
+    // A 32-lane butterfly reduces both rows at once, adding the same values in the same order
+    // as a 64-lane one over one row (whose other lanes would add exact zeros).
+    const int half = lane >> 5, sgi = lane & 31;
+    for (int r0 = 0; r0 <= ell; r0 += kAcceptRows) {
+      float mx[kAcceptRows / 2];
+      double sg[kAcceptRows / 2];
 #pragma unroll
-    for (int r = 0; r < kAcceptRows; ++r)
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int sgi = lane + 64 * i;
-        const bool valid = (r0 + r <= ell) && sgi < p.nseg;
-        const size_t o = static_cast<size_t>(off + min(r0 + r, ell)) * p.nseg + min(sgi, p.nseg - 1);
+      for (int pr = 0; pr < kAcceptRows / 2; ++pr) {
+        const int row = r0 + 2 * pr + half;
+        const bool valid = row <= ell && sgi < p.nseg;
+        const size_t o =
+            static_cast<size_t>(off + min(row, ell)) * p.nseg + min(sgi, p.nseg - 1);
         const float m0 = p.ws.seg_max[o];
         const double s0 = p.ws.seg_sum[o];
-        mx[r][i] = valid ? m0 : kNegInf;
-        sg[r][i] = valid ? s0 : 0.0;
+        mx[pr] = valid ? m0 : kNegInf;
+        sg[pr] = valid ? s0 : 0.0;
       }
+      if (r0 == 0 && lane < ell) tx0 = p.target[static_cast<size_t>(off + lane) * p.V + x0];
 #pragma unroll
-    for (int r = 0; r < kAcceptRows; ++r) {
-      if (r0 + r > ell) break;
-      const float M = wave_max(fmaxf(mx[r][0], mx[r][1]));
-      const double z = wave_sum(partial_mass(mx[r][0], sg[r][0], M) + partial_mass(mx[r][1], sg[r][1], M));
-      if (lane == 0) lse_s[w][r0 + r] = static_cast<double>(M) + log(z);
+      for (int pr = 0; pr < kAcceptRows / 2; ++pr) {
+        if (r0 + 2 * pr > ell) break;
+        float M = mx[pr];
+        M = fmaxf(M, __uint_as_float(lane_xor<16>(__float_as_uint(M))));
+        M = fmaxf(M, __uint_as_float(lane_xor<8>(__float_as_uint(M))));
+        M = fmaxf(M, __uint_as_float(lane_xor<4>(__float_as_uint(M))));
+        M = fmaxf(M, __uint_as_float(lane_xor<2>(__float_as_uint(M))));
+        M = fmaxf(M, __uint_as_float(lane_xor<1>(__float_as_uint(M))));
+        double z = partial_mass(mx[pr], sg[pr], M);
+        z += lane_xor<16>(z);
+        z += lane_xor<8>(z);
+        z += lane_xor<4>(z);
+        z += lane_xor<2>(z);
+        z += lane_xor<1>(z);
+        const int row = r0 + 2 * pr + half;
+        if (sgi == 0 && row <= ell) lse_s[w][row] = static_cast<double>(M) + log(z);
+      }
+    }
+  } else {
+    if (lane < ell) tx0 = p.target[static_cast<size_t>(off + lane) * p.V + x0];
+    // 1. log-sum-exp of rows off .. off + ell (segments: lane + 64 i, i < 2, nseg <= 128).
+    for (int r0 = 0; r0 <= ell; r0 += kAcceptRows) {
+      float mx[kAcceptRows][2];
+      double sg[kAcceptRows][2];
+#pragma unroll
+      for (int r = 0; r < kAcceptRows; ++r)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int sgi = lane + 64 * i;
+          const bool valid = (r0 + r <= ell) && sgi < p.nseg;
+          const size_t o = static_cast<size_t>(off + min(r0 + r, ell)) * p.nseg + min(sgi, p.nseg - 1);
+          const float m0 = p.ws.seg_max[o];
+          const double s0 = p.ws.seg_sum[o];
+          mx[r][i] = valid ? m0 : kNegInf;
+          sg[r][i] = valid ? s0 : 0.0;
+        }
+#pragma unroll
+      for (int r = 0; r < kAcceptRows; ++r) {
+        if (r0 + r > ell) break;
+        const float M = wave_max(fmaxf(mx[r][0], mx[r][1]));
+        const double z = wave_sum(partial_mass(mx[r][0], sg[r][0], M) + partial_mass(mx[r][1], sg[r][1], M));
+        if (lane == 0) lse_s[w][r0 + r] = static_cast<double>(M) + log(z);
+      }
     }
   }
   __builtin_amdgcn_s_waitcnt(0);

@@ -233,6 +233,34 @@ def test_verify_parity(name):
     log(f"  {acc.report()}; {emit.report()}; residual rows {int((ov['beta_emit'] >= 0).sum())}")
 
 
+def test_verify_long_block():
+    """Full verify of a 20-token block (21 rows a request, more than one batch of the accept
+    scan's per-row reductions) at a vocabulary of fewer than 32 segments."""
+    wl = _custom("b9-v3000-r64-g20", seed_id=19, B=9, V=3000, r=64, gamma=20, noise_std=lambda k: 0.05)
+    log(f"[verify] {wl.name}")
+    wts = W.weights(wl, DEV)
+    inp = W.round_inputs(wl, 0, DEV, with_hidden=False)
+    o, conf, p, target = _oracle_round(wl, inp, wts, W.FULL_VERIFY)
+    assert (p["draft_len"] == wl.gamma).all()
+    ov = oracle.verify(target, p["row_offsets"], p["draft_len"], np_(inp["U"]), bits(wts["W1"]),
+                       bits(wts["W2t"]), np_(inp["anchor"]), o["tokens"], o["q"], np_(inp["uniforms"]))
+    g = gpu_draft(wl, inp, wts, force=o["tokens"])
+    al, nt, be, fl = L.verify(dims_of(wl), _T(target, torch.float32), _T(p["row_offsets"]),
+                              _T(p["draft_len"]), inp["U"], wts["W1"], wts["W2t"], inp["anchor"],
+                              _T(o["tokens"]), _T(o["q"], torch.float32), g["lse_t"],
+                              inp["uniforms"])
+    torch.cuda.synchronize()
+    al, nt, be = np_(al), np_(nt), np_(be)
+    acc = MismatchCounter("accept long block")
+    acc.add(al, ov["accept_len"], decisive_margin(ov, al, wl.gamma))
+    same = al == ov["accept_len"]
+    emit = MismatchCounter("emit long block")
+    emit.add(nt[same], ov["next_token"][same], ov["emit_margin"][same])
+    assert np.abs(be[same] - ov["beta_emit"][same]).max() <= PROB_TOL
+    assert ov["accept_len"].max() >= 16, "some request should accept into the second batch of rows"
+    log(f"  accepted {ov['accept_len'].tolist()}; {acc.report()}")
+
+
 @pytest.mark.parametrize("name", ["b128-v129280-g5", "b32-v32000-g7", "b128-v151936-g15"])
 def test_round_full_size(name):
     """A whole round at the workload's full size, every request checked against the oracle."""
