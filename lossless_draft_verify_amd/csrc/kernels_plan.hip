@@ -72,21 +72,25 @@ __device__ __forceinline__ void load_inputs(PlanInputs& in, const PlanArgs& p, b
   in.s1 = (i < N) ? p.sps[p.B + i + 1] : 0.0;
 }
 
-// Fill survivals from the confidences src (c0 = src[tid], already loaded), sort, and turn a[] into
-// tau_i (a[i] = tau_{i+1}). Results in sm.
+// Fill survivals from the confidences src (c0 = src[tid], already loaded), sort, and turn a[]
+// into tau_i (a[i] = tau_{i+1}). Results in sm.
 //
-// The sort: every 64-element chunk is sorted inside one wave (bitonic, no LDS traffic), then
-// merge levels double the runs. A merge level places every element directly: its position is
-// its rank in its own run plus the number of elements of the partner run that come before it,
-// found by a fixed-step binary search. The left run holds the lower candidate indices, so an
-// element of the right run comes before a left element x iff it is > x, and a left element
-// comes before a right element x iff it is >= x.
+// The sort runs over Np = N rounded up to a power of two (at least 64): entries N .. Np-1 hold
+// -inf with the highest candidate indices, so they sort last and every run below is full. Every
+// 64-element chunk is sorted inside one wave (bitonic, no LDS traffic), then merge levels double
+// the runs. A merge level places every element directly: its position is its rank in its own run
+// plus the number of elements of the partner run that come before it. The left run holds the
+// lower candidate indices, so for x in the left run a right element comes first iff it is > x,
+// and for x in the right run a left element comes first iff it is >= x, that is > the next
+// double below x: one threshold per element, one comparison per probe of a fixed-step base-4
+// search. A padding element comes after every real one and after the padding of lower index.
 __device__ void sorted_path(PlanSmem& sm, const float* __restrict__ src, float c0, int B,
                             int gamma) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int N = B * gamma;
-  for (int i = tid; i < N; i += kPlanThreads) {
-    sm.a[i] = static_cast<double>(i == tid ? c0 : src[i]);
+  const int Np = (N <= kWave) ? kWave : (1 << (32 - __clz(N - 1)));
+  for (int i = tid; i < Np; i += kPlanThreads) {
+    sm.a[i] = (i < N) ? static_cast<double>(i == tid ? c0 : src[i]) : -__builtin_inf();
     sm.idx[i] = i;
   }
   __syncthreads();
@@ -100,11 +104,11 @@ __device__ void sorted_path(PlanSmem& sm, const float* __restrict__ src, float c
   }
   __syncthreads();
   // Runs of 64: each wave sorts 64-element chunks in registers with a bitonic network whose
-  // exchanges go through DPP / lane swaps (positions past N hold -inf and sort last).
-  for (int c = wave; c * kWave < N; c += kPlanThreads / kWave) {
+  // exchanges go through DPP / lane swaps.
+  for (int c = wave; c * kWave < Np; c += kPlanThreads / kWave) {
     const int i = c * kWave + lane;
-    double a = (i < N) ? sm.a[i] : -__builtin_inf();
-    int ix = (i < N) ? sm.idx[i] : INT_MAX;
+    double a = sm.a[i];
+    int ix = sm.idx[i];
 #pragma unroll
     for (int size = 2; size <= kWave; size <<= 1) {
       const bool up = (lane & size) == 0 || size == kWave;
@@ -115,39 +119,49 @@ __device__ void sorted_path(PlanSmem& sm, const float* __restrict__ src, float c
       if (size >= 4) exchange<2>(a, ix, lane, up);
       exchange<1>(a, ix, lane, up);
     }
-    if (i < N) {
-      sm.a[i] = a;
-      sm.idx[i] = ix;
-    }
+    sm.a[i] = a;
+    sm.idx[i] = ix;
   }
   __syncthreads();
-  for (int run = kWave; run < N; run *= 2) {
+  for (int run = kWave; run < Np; run *= 2) {
     double ka[kPer];
     int ki[kPer], pos[kPer];
 #pragma unroll
     for (int q = 0; q < kPer; ++q) {
       const int p = tid + q * kPlanThreads;
       pos[q] = -1;
-      if (p < N) {
+      if (p < Np) {
         ka[q] = sm.a[p];
         ki[q] = sm.idx[p];
-        const int base = (p / (2 * run)) * (2 * run);
+        const int base = p & ~(2 * run - 1);
         const bool left = p - base < run;
         const int own = left ? p - base : p - base - run;
         const int o0 = left ? base + run : base;
-        const int olen = left ? max(0, min(run, N - base - run)) : run;
-        // Count of partner elements before ka[q]: fixed-step binary lifting over the run
-        // length (every lane takes the same steps; reads are clamped to valid addresses).
-        int lo = 0;
-        auto probe = [&](int at, int add) {
-          const double y = sm.a[min(o0 + min(at, olen - 1), N - 1)];
-          const int hit = static_cast<int>(at < olen) &
-                          (static_cast<int>(y > ka[q]) | (static_cast<int>(!left) & static_cast<int>(y == ka[q])));
-          lo += hit * add;
-        };
-        for (int step = run / 2; step >= 1; step >>= 1) probe(lo + step - 1, step);
-        probe(lo, 1);
-        pos[q] = base + own + lo;
+        int cnt;
+        if (ki[q] >= N) {
+          const int real = min(max(N - o0, 0), run);
+          cnt = left ? real : run;
+        } else {
+          const double thr = left ? ka[q] : nextafter(ka[q], -__builtin_inf());
+          const double* r = sm.a + o0;
+          // Base-4 lifting: three independent probes a step (one binary step first when the run
+          // length is an odd power of two), then the last position.
+          int lo = 0, len = run;
+          if (__builtin_ctz(run) & 1) {
+            lo += (r[len / 2 - 1] > thr) ? len / 2 : 0;
+            len /= 2;
+          }
+          for (; len >= 4; len >>= 2) {
+            const int qq = len >> 2;
+            const int n1 = (r[lo + qq - 1] > thr) ? 1 : 0;
+            const int n2 = (r[lo + 2 * qq - 1] > thr) ? 1 : 0;
+            const int n3 = (r[lo + 3 * qq - 1] > thr) ? 1 : 0;
+            lo += qq * (n1 + n2 + n3);
+          }
+          lo += (r[lo] > thr) ? 1 : 0;
+          cnt = lo;
+        }
+        pos[q] = base + own + cnt;
       }
     }
     __syncthreads();
