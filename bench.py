@@ -29,6 +29,7 @@ import lossless_draft_verify_amd as L  # noqa: E402
 from lossless_draft_verify_amd import workloads as W  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 MFMA, no sparsity
 WORKLOAD = "b128-v129280-g5"
 METRIC = "spec rounds/s at B=128,V=129280,γ=5; achieved HBM GB/s vs peak"
 STEP_SOURCES = ["lossless_draft_verify_amd/csrc/kernels_draft.hip",
@@ -135,6 +136,8 @@ def main():
                     help="skip the kernel-timing pass (no per-kernel durations or roofline)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration under rocprof)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time eager launches only (no hipGraph capture of the round)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build runs on a single MI355X and has no "
@@ -179,7 +182,8 @@ def main():
         torch.cuda.synchronize()
         assert torch.equal(dl, s.draft_len), "the timed plan differs from the preparation pass"
         n_res = int((be >= 0).sum().item())
-        per_set.append(dict(tokens=int((al + 1).sum().item()), rows=s.rows, n_res=n_res))
+        per_set.append(dict(tokens=int((al + 1).sum().item()), rows=s.rows, n_res=n_res,
+                            out=[t.clone() for t in (tok, dl, al, nt, be)]))
 
     for i in range(args.warmup):
         round_(sets[i % len(sets)])
@@ -190,6 +194,31 @@ def main():
         round_(sets[i % len(sets)])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    # Graph region: each input set's round captured once as a hipGraph (every launch has its
+    # shapes on the device, so one capture replays any planned lengths), every replay checked
+    # against the eager results, then K replays timed the same way (reported beside `value`).
+    elapsed_graph = None
+    if not args.no_graph:
+        graphs = []
+        for s in sets:
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                round_(s)
+            graphs.append(gr)
+        for rep in range(2):
+            for gr, ps in zip(graphs, per_set):
+                gr.replay()
+                torch.cuda.synchronize()
+                for a, b in zip((tok, dl, al, nt, be), ps["out"]):
+                    assert torch.equal(a, b), "a graph replay differs from the eager round"
+        for i in range(args.warmup):
+            graphs[i % len(graphs)].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            graphs[i % len(graphs)].replay()
+        torch.cuda.synchronize()
+        elapsed_graph = time.perf_counter() - t0
     # Kernel-timing region: the same K rounds again, with a HIP event pair recorded around every
     # library launch on its stream (the events add gaps between kernels, so this region does not
     # set `value`; it gives each kernel's average duration).
@@ -204,12 +233,16 @@ def main():
         elapsed_ev = time.perf_counter() - t1
         kern = L.profile_end()
 
-    rounds_per_s = args.steps / elapsed
+    # `value` is the eager rate: replaying the captured round measured slower than launching it
+    # (the launches already run back to back), so the graph rate is reported beside it.
+    timed = elapsed
+    rounds_per_s = args.steps / timed
     used = [per_set[i % len(sets)] for i in range(args.steps)]
     tokens_per_round = float(np.mean([u["tokens"] for u in used]))
     bytes_per_round = float(np.mean([algorithmic_bytes(wl, u["rows"], u["n_res"]) for u in used]))
 
     roofline = None
+    mfma = None
     kernels = {}
     for name, (cnt, ms) in kern.items():
         if cnt:
@@ -224,6 +257,9 @@ def main():
                     "traffic": traffic, "traffic_unit": "bytes per launch",
                     "algorithmic_bytes_per_launch": step_bytes,
                     "avg_launch_us": round(kernels["markov_step"]["avg_us"], 3)}
+        flops = 2.0 * wl.B * wl.r * wl.V                        # the W2 contraction per launch
+        mfma = {"kernel": "markov_step", "tflops": round(flops / avg_s / 1e12, 1),
+                "peak": MFMA_BF16_PEAK_TFLOPS, "frac": round(flops / avg_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
 
     if args.copy_calibration:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
@@ -245,7 +281,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(1e3 * elapsed / args.steps, 4),
+        "ms_per_step": round(1e3 * timed / args.steps, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -253,12 +289,15 @@ def main():
         "data": "synthetic",
         "config": {"workload": WORKLOAD, "B": wl.B, "V": wl.V, "gamma": wl.gamma, "r": wl.r,
                    "d": wl.d, "plan": "early_stop", "sps": "1/(1+n/768)", "input_sets": len(sets),
-                   "parallelism": "1 GPU"},
+                   "parallelism": "1 GPU", "launch": "eager"},
+        "graph_rounds_per_s": (round(args.steps / elapsed_graph, 2)
+                               if elapsed_graph is not None else None),
         "tokens_per_s": round(rounds_per_s * tokens_per_round, 1),
         "tokens_per_round": tokens_per_round,
         "round_algorithmic_gbs": round(bytes_per_round * rounds_per_s / 1e9, 1),
         "round_hbm_frac": round(bytes_per_round * rounds_per_s / 1e9 / HBM_PEAK_GBS, 4),
         "roofline": roofline,
+        "mfma": mfma,
         "kernels_us": {k: round(v["avg_us"], 2) for k, v in kernels.items()},
         "ms_per_step_with_kernel_events": (round(1e3 * elapsed_ev / args.steps, 4)
                                            if elapsed_ev else None),

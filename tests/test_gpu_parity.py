@@ -457,6 +457,70 @@ def test_lagged_chain_full_size():
     assert checked >= wl.rounds - 2
 
 
+def test_graph_replay_matches_eager():
+    """A whole round (draft, confidence, plan, verify) captured once as a hipGraph and replayed
+    several times, with unrelated eager work and synchronisations between the replays and the
+    outputs overwritten before each one: every replay must reproduce the eager round bit for
+    bit (all shapes the kernels need live on the device, and no call records a memset)."""
+    wl = W.scaled(W.WORKLOADS["b128-v129280-g5"], name="graph-b64-v8192-g5", seed_id=40, B=64,
+                  V=8192, d=256, sps_scale=64.0)
+    wts = W.weights(wl, DEV)
+    inp = W.round_inputs(wl, 0, DEV)
+    d = dims_of(wl)
+    B, g = wl.B, wl.gamma
+    temps = W.temperatures(wl).to(DEV)
+    sps = _T(W.sps_table(wl), torch.float64)
+    logits = torch.empty_like(inp["U"])
+    t0, _, _ = L.markov_draft(d, inp["U"], wts["W1"], wts["W2t"], inp["anchor"], inp["uniforms"],
+                              logits_dbg=logits)
+    c0 = L.confidence(d, inp["h"], wts["W1"], wts["w"], temps, inp["anchor"], t0)
+    dl0, _, _ = L.plan(d, c0, sps, wl.mode)
+    target = W.pack_rows(W.target_dense(logits, inp["U_bonus"], inp["noise"]), dl0)
+    del logits
+    ws_d, ws_v = L.workspace(d, L.OP_DRAFT, DEV), L.workspace(d, L.OP_VERIFY, DEV)
+    out = dict(tok=torch.empty((B, g), dtype=torch.int32, device=DEV),
+               q=torch.empty((B, g), dtype=torch.float32, device=DEV),
+               lse=torch.empty((B, g), dtype=torch.float64, device=DEV),
+               conf=torch.empty((B, g), dtype=torch.float32, device=DEV),
+               dl=torch.empty(B, dtype=torch.int32, device=DEV),
+               ro=torch.empty(B + 1, dtype=torch.int32, device=DEV),
+               st=torch.empty(4, dtype=torch.float64, device=DEV),
+               al=torch.empty(B, dtype=torch.int32, device=DEV),
+               nt=torch.empty(B, dtype=torch.int32, device=DEV),
+               be=torch.empty(B, dtype=torch.float32, device=DEV),
+               fl=torch.empty(B, dtype=torch.int32, device=DEV))
+
+    def round_():
+        o = out
+        L.markov_draft(d, inp["U"], wts["W1"], wts["W2t"], inp["anchor"], inp["uniforms"],
+                       tokens=o["tok"], q=o["q"], lse=o["lse"], ws=ws_d)
+        L.confidence(d, inp["h"], wts["W1"], wts["w"], temps, inp["anchor"], o["tok"], conf=o["conf"])
+        L.plan(d, o["conf"], sps, wl.mode, draft_len=o["dl"], row_offsets=o["ro"], stats=o["st"])
+        L.verify(d, target, o["ro"], o["dl"], inp["U"], wts["W1"], wts["W2t"], inp["anchor"],
+                 o["tok"], o["q"], o["lse"], inp["uniforms"], accept_len=o["al"],
+                 next_token=o["nt"], beta_emit=o["be"], flags=o["fl"], ws=ws_v)
+
+    round_()
+    torch.cuda.synchronize()
+    eager = {k: v.clone() for k, v in out.items()}
+    assert torch.equal(eager["dl"], dl0)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        round_()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        junk = torch.randn(1 << 20, device=DEV)
+        _ = float(junk.square().sum().item())          # eager work between the replays
+        for v in out.values():
+            v.fill_(-7)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for k, v in out.items():
+            assert torch.equal(v, eager[k]), (rep, k)
+    log(f"  graph replays match the eager round (B_tot {eager['st'][0].item():.0f})")
+
+
 def test_determinism_bitwise():
     wl = W.WORKLOADS["b32-v32000-g7"]
     wts = W.weights(wl, DEV)
