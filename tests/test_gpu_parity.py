@@ -173,6 +173,52 @@ def test_plan_parity(B, g, scale, seed):
             assert np.allclose(np_(st), o["stats"], rtol=1e-12, atol=0)
 
 
+def _bucketed_sps(n, bucket, step, saw, rng):
+    """Steps per second when the step time grows by `step` per bucket of verified tokens (a
+    piecewise-constant, non-smooth table), optionally with a rise inside each bucket (sawtooth):
+    Theta then has several local maxima along the admission path."""
+    x = np.arange(n, dtype=np.float64)
+    sps = 1.0 / (1.0 + np.floor(x / bucket) * step)
+    if saw:
+        sps = sps * (1.0 + rng.uniform(0.05, 0.3) * ((x % bucket) / bucket))
+    return sps
+
+
+@pytest.mark.parametrize("B,g,bucket,saw,seed", [(128, 5, 32, False, 61), (128, 5, 32, True, 62),
+                                                 (512, 5, 64, True, 63), (37, 7, 8, True, 64)])
+def test_plan_parity_bucketed_sps(B, g, bucket, saw, seed):
+    """Planner parity under non-unimodal SPS tables (batch-bucketed step times, sawtooth): early
+    stop halts at the first local maximum of Theta, full path finds the global one, and the
+    lagged capacity takes the full-path count of the slot two rounds back."""
+    rng = np.random.default_rng(seed)
+    n = B * (g + 1) + 1
+    sps = _bucketed_sps(n, bucket, rng.uniform(0.1, 0.5), saw, rng)
+    sps_t = torch.tensor(sps, dtype=torch.float64, device=DEV)
+    d = L.Dims(B, g, 8, 16)
+    for mode in (L.EARLY_STOP, L.FULL_PATH):
+        conf = _plan_case(B, g, sps, seed)
+        o = oracle.plan(conf.numpy(), sps, mode)
+        dl, ro, st = L.plan(d, conf.to(DEV), sps_t, mode)
+        if o["margin"] > PLAN_TIE:
+            assert np.array_equal(np_(dl), o["draft_len"]), mode
+            assert np.array_equal(np_(ro), o["row_offsets"])
+            assert np.allclose(np_(st), o["stats"], rtol=1e-12, atol=0)
+    e = oracle.plan(_plan_case(B, g, sps, seed).numpy(), sps, L.EARLY_STOP)["draft_len"].sum()
+    f = oracle.plan(_plan_case(B, g, sps, seed).numpy(), sps, L.FULL_PATH)["draft_len"].sum()
+    ring_o = np.zeros((2, B, g), np.float32)
+    ring_g = torch.zeros((2, B, g), dtype=torch.float32, device=DEV)
+    for t in range(6):
+        conf = _plan_case(B, g, sps, 100 * seed + t)
+        o = oracle.plan(conf.numpy(), sps, L.LAGGED_TOPK, ring=ring_o, round_index=t)
+        dl, ro, st = L.plan(d, conf.to(DEV), sps_t, L.LAGGED_TOPK, ring=ring_g, round_index=t)
+        assert np.array_equal(np_(ring_g), ring_o)
+        if o["margin"] > PLAN_TIE:
+            assert np.array_equal(np_(dl), o["draft_len"]), t
+            assert np.array_equal(np_(ro), o["row_offsets"])
+            assert np.allclose(np_(st), o["stats"], rtol=1e-12, atol=0)
+    log(f"  B={B} bucket={bucket} saw={saw}: early stop admits {e}, full path {f}")
+
+
 def decisive_margin(ov, al_gpu, gamma):
     """Margin of the accept test that separates the two accept lengths (the first position
     where the GPU and the oracle could disagree)."""
