@@ -128,8 +128,8 @@ def cpu_baseline(wl, wts, s, threads):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=60)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--sets", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-events", action="store_true",
@@ -194,6 +194,17 @@ def main():
         round_(sets[i % len(sets)])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    # Round-time distribution: the same K rounds with an event pair at each round boundary
+    # only (no events between a round's launches).
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    ev[0].record()
+    for i in range(args.steps):
+        round_(sets[i % len(sets)])
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    per_round_us = np.array([1e3 * ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)])
+    round_us = {k: round(float(np.percentile(per_round_us, q)), 2)
+                for k, q in (("p10", 10), ("p50", 50), ("p90", 90))}
     # Graph region: each input set's round captured once as a hipGraph (every launch has its
     # shapes on the device, so one capture replays any planned lengths), every replay checked
     # against the eager results, then K replays timed the same way (reported beside `value`).
@@ -290,6 +301,7 @@ def main():
         "config": {"workload": WORKLOAD, "B": wl.B, "V": wl.V, "gamma": wl.gamma, "r": wl.r,
                    "d": wl.d, "plan": "early_stop", "sps": "1/(1+n/768)", "input_sets": len(sets),
                    "parallelism": "1 GPU", "launch": "eager"},
+        "round_us": round_us,
         "graph_rounds_per_s": (round(args.steps / elapsed_graph, 2)
                                if elapsed_graph is not None else None),
         "tokens_per_s": round(rounds_per_s * tokens_per_round, 1),
