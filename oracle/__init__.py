@@ -43,7 +43,8 @@ def _load():
         if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
             build(force=True)
         _lib = ctypes.CDLL(_LIB_PATH)
-        for name in ("oracle_markov_draft", "oracle_confidence", "oracle_plan", "oracle_verify"):
+        for name in ("oracle_markov_draft", "oracle_markov_draft_opts", "oracle_confidence",
+                     "oracle_plan", "oracle_verify", "oracle_verify_opts"):
             getattr(_lib, name).restype = ctypes.c_int
     return _lib
 
@@ -71,9 +72,12 @@ def _check(rc, what):
         raise ValueError(f"{what} rejected its arguments (code {rc})")
 
 
-def markov_draft(U, W1, W2t, anchor, uniforms, force_tokens=None, want_logits=False, threads=0):
+def markov_draft(U, W1, W2t, anchor, uniforms, force_tokens=None, want_logits=False, threads=0,
+                 temperature=1.0, greedy=False):
     """Markov-head draft. U [B][g][V] f32, W1/W2t [V][r] bf16 bits, anchor [B] i32,
-    uniforms [B][g+1][3] f32. Returns dict(tokens, q, lse, margin[, logits])."""
+    uniforms [B][g+1][3] f32; temperature > 0 (logits scaled by fp32(1/temperature)) or greedy.
+    Returns dict(tokens, q, lse, margin[, logits]); for greedy, margin is the gap between the
+    two largest logits."""
     lib = _load()
     U = _c(U, np.float32)
     B, g, V = U.shape
@@ -86,9 +90,11 @@ def markov_draft(U, W1, W2t, anchor, uniforms, force_tokens=None, want_logits=Fa
     out = dict(tokens=np.zeros((B, g), np.int32), q=np.zeros((B, g), np.float32),
                lse=np.zeros((B, g), np.float64), margin=np.zeros((B, g), np.float64))
     logits = np.zeros((B, g, V), np.float32) if want_logits else None
-    rc = lib.oracle_markov_draft(B, g, V, r, _ptr(U), _ptr(W1), _ptr(W2t), _ptr(anchor),
-                                 _ptr(uniforms), _ptr(force), _ptr(out["tokens"]), _ptr(out["q"]),
-                                 _ptr(out["lse"]), _ptr(logits), _ptr(out["margin"]), int(threads))
+    rc = lib.oracle_markov_draft_opts(B, g, V, r, _ptr(U), _ptr(W1), _ptr(W2t), _ptr(anchor),
+                                      _ptr(uniforms), _ptr(force), ctypes.c_float(temperature),
+                                      int(bool(greedy)), _ptr(out["tokens"]), _ptr(out["q"]),
+                                      _ptr(out["lse"]), _ptr(logits), _ptr(out["margin"]),
+                                      int(threads))
     _check(rc, "oracle_markov_draft")
     if want_logits:
         out["logits"] = logits
@@ -138,8 +144,10 @@ def plan(conf, sps, mode, B=None, gamma=None, ring=None, round_index=0):
                 theta_path=theta)
 
 
-def verify(target, row_offsets, draft_len, U, W1, W2t, anchor, tokens, q, uniforms, threads=0):
-    """Lossless verify. target [row_offsets[B]][V] f32 (packed rows).
+def verify(target, row_offsets, draft_len, U, W1, W2t, anchor, tokens, q, uniforms, threads=0,
+           temperature=1.0, greedy=False):
+    """Lossless verify. target [row_offsets[B]][V] f32 (packed rows); temperature / greedy
+    describe the draft distribution (as for markov_draft).
     Returns dict(accept_len, next_token, beta_emit, flags, accept_margin, emit_margin,
     resid_mass)."""
     lib = _load()
@@ -155,10 +163,11 @@ def verify(target, row_offsets, draft_len, U, W1, W2t, anchor, tokens, q, unifor
                beta_emit=np.zeros(B, np.float32), flags=np.zeros(B, np.uint32),
                accept_margin=np.zeros((B, g), np.float64), emit_margin=np.zeros(B, np.float64),
                resid_mass=np.zeros(B, np.float64))
-    rc = lib.oracle_verify(B, g, V, r, _ptr(target), _ptr(row_offsets), _ptr(draft_len), _ptr(U),
-                           _ptr(W1), _ptr(W2t), _ptr(_c(anchor, np.int32)),
+    rc = lib.oracle_verify_opts(B, g, V, r, _ptr(target), _ptr(row_offsets), _ptr(draft_len),
+                           _ptr(U), _ptr(W1), _ptr(W2t), _ptr(_c(anchor, np.int32)),
                            _ptr(_c(tokens, np.int32)), _ptr(_c(q, np.float32)),
-                           _ptr(_c(uniforms, np.float32)), _ptr(out["accept_len"]),
+                           _ptr(_c(uniforms, np.float32)), ctypes.c_float(temperature),
+                           int(bool(greedy)), _ptr(out["accept_len"]),
                            _ptr(out["next_token"]), _ptr(out["beta_emit"]), _ptr(out["flags"]),
                            _ptr(out["accept_margin"]), _ptr(out["emit_margin"]),
                            _ptr(out["resid_mass"]), int(threads))

@@ -136,6 +136,31 @@ void draft_logits(const float* U_row, const uint16_t* W1, const uint16_t* W2t, i
   }
 }
 
+// Draft temperature: the official loop samples each position with a temperature ([V41] "Markov
+// head", the serial loop: sample(logits, temperature)). Reading: the fp32 logits are multiplied,
+// in fp32, by beta = fp32(1 / tau) before the softmax; tau = 1 (beta = 1) leaves them unchanged.
+float temperature_beta(float tau) { return static_cast<float>(1.0 / static_cast<double>(tau)); }
+
+void scale_logits(std::vector<float>& L, float beta) {
+  if (beta == 1.0f) return;
+  for (float& x : L) x = x * beta;  // one fp32 multiplication, round to nearest
+}
+
+// Greedy draft (the deployed recipe drafts greedily: [V41] / [AIL] V4 recipe,
+// draft_sample_method "greedy"): the token with the largest logit, the smallest id among equal
+// maxima; the draft distribution is the point mass on it. *gap receives the distance from the
+// largest logit to the largest logit of any other token (0 on a tie).
+int32_t greedy_token(const std::vector<float>& L, double* gap) {
+  int32_t best = 0;
+  for (size_t v = 1; v < L.size(); ++v)
+    if (L[v] > L[best]) best = static_cast<int32_t>(v);
+  double second = -std::numeric_limits<double>::infinity();
+  for (size_t v = 0; v < L.size(); ++v)
+    if (static_cast<int32_t>(v) != best) second = std::max(second, static_cast<double>(L[v]));
+  *gap = static_cast<double>(L[best]) - second;
+  return best;
+}
+
 double logsumexp_fp32_row(const float* row, int V) {
   double m = -std::numeric_limits<double>::infinity();
   for (int v = 0; v < V; ++v) m = std::max(m, static_cast<double>(row[v]));
@@ -243,11 +268,18 @@ extern "C" {
 // logits (nullable) [B][gamma][V] = L_k, margin (nullable) [B][gamma] = distance of u to the
 // nearer CDF edge of the drawn token.
 // Returns 0, or 2 for a bad shape, 8 for an out-of-range token id.
-int oracle_markov_draft(int B, int gamma, int V, int r, const float* U, const uint16_t* W1,
-                        const uint16_t* W2t, const int32_t* anchor, const float* uniforms,
-                        const int32_t* force_tokens, int32_t* tokens, float* q, double* lse,
-                        float* logits, double* margin, int threads) {
+// With draft options: temperature tau > 0 draws from softmax(beta L), beta = fp32(1 / tau), and
+// q / lse refer to that distribution; greedy != 0 drafts the first maximal logit, q = 1 (0 for a
+// forced token that is not it), lse = the largest logit, and margin receives the gap between the
+// two largest logits instead.
+int oracle_markov_draft_opts(int B, int gamma, int V, int r, const float* U, const uint16_t* W1,
+                             const uint16_t* W2t, const int32_t* anchor, const float* uniforms,
+                             const int32_t* force_tokens, float temperature, int greedy,
+                             int32_t* tokens, float* q, double* lse, float* logits, double* margin,
+                             int threads) {
   if (B < 0 || gamma < 1 || V < 2 || r < 1) return 2;
+  if (!greedy && !(temperature > 0.0f && std::isfinite(temperature))) return 2;
+  const float beta = greedy ? 1.0f : temperature_beta(temperature);
   for (int b = 0; b < B; ++b) {
     if (anchor[b] < 0 || anchor[b] >= V) return 8;
     if (force_tokens)
@@ -261,20 +293,37 @@ int oracle_markov_draft(int B, int gamma, int V, int r, const float* U, const ui
     for (int k = 0; k < gamma; ++k) {
       const int64_t bk = b * gamma + k;
       draft_logits(U + bk * V, W1, W2t, V, r, prev, L);
-      const double l = softmax_fp64(L.data(), V, p);
-      const double u = static_cast<double>(uniforms[(b * (gamma + 1) + k) * 3 + 0]);
-      double mg = 0.0;
-      const int32_t x = inverse_cdf(p, u, &mg);
-      tokens[bk] = x;
-      const int32_t cond = force_tokens ? force_tokens[bk] : x;
-      q[bk] = static_cast<float>(p[cond]);
-      lse[bk] = l;
       if (logits) std::memcpy(logits + bk * V, L.data(), sizeof(float) * V);
+      double mg = 0.0;
+      int32_t x, cond;
+      if (greedy) {
+        x = greedy_token(L, &mg);
+        cond = force_tokens ? force_tokens[bk] : x;
+        q[bk] = (cond == x) ? 1.0f : 0.0f;
+        lse[bk] = static_cast<double>(L[x]);
+      } else {
+        scale_logits(L, beta);
+        const double l = softmax_fp64(L.data(), V, p);
+        const double u = static_cast<double>(uniforms[(b * (gamma + 1) + k) * 3 + 0]);
+        x = inverse_cdf(p, u, &mg);
+        cond = force_tokens ? force_tokens[bk] : x;
+        q[bk] = static_cast<float>(p[cond]);
+        lse[bk] = l;
+      }
+      tokens[bk] = x;
       if (margin) margin[bk] = mg;
       prev = cond;
     }
   });
   return 0;
+}
+
+int oracle_markov_draft(int B, int gamma, int V, int r, const float* U, const uint16_t* W1,
+                        const uint16_t* W2t, const int32_t* anchor, const float* uniforms,
+                        const int32_t* force_tokens, int32_t* tokens, float* q, double* lse,
+                        float* logits, double* margin, int threads) {
+  return oracle_markov_draft_opts(B, gamma, V, r, U, W1, W2t, anchor, uniforms, force_tokens, 1.0f,
+                                  0, tokens, q, lse, logits, margin, threads);
 }
 
 // Confidence head, eq. (7), with the STS temperature applied at inference:
@@ -421,13 +470,19 @@ int oracle_plan(int B, int gamma, const float* conf, const double* sps, int sps_
 // residual emission row, -1 at a bonus row; flags (nullable) [B]; accept_margin (nullable)
 // [B][gamma] = |u - p_t/q| for each tested position with p_t/q < 1 (+inf otherwise);
 // emit_margin (nullable) [B]; resid_mass (nullable) [B] = sum_v max(0, p_t - p_d) (-1 at bonus).
-int oracle_verify(int B, int gamma, int V, int r, const float* target, const int32_t* row_offsets,
-                  const int32_t* draft_len, const float* U, const uint16_t* W1,
-                  const uint16_t* W2t, const int32_t* anchor, const int32_t* tokens,
-                  const float* q, const float* uniforms, int32_t* accept_len,
-                  int32_t* next_token, float* beta_emit, uint32_t* flags, double* accept_margin,
-                  double* emit_margin, double* resid_mass, int threads) {
+// With draft options (as for the draft): the draft distribution p_d whose residual is drawn from
+// is softmax(beta L) at temperature tau, or, for a greedy draft, the point mass on the drafted
+// token (q = 1 in the accept test).
+int oracle_verify_opts(int B, int gamma, int V, int r, const float* target,
+                       const int32_t* row_offsets, const int32_t* draft_len, const float* U,
+                       const uint16_t* W1, const uint16_t* W2t, const int32_t* anchor,
+                       const int32_t* tokens, const float* q, const float* uniforms,
+                       float temperature, int greedy, int32_t* accept_len, int32_t* next_token,
+                       float* beta_emit, uint32_t* flags, double* accept_margin,
+                       double* emit_margin, double* resid_mass, int threads) {
   if (B < 0 || gamma < 1 || V < 2 || r < 1) return 2;
+  if (!greedy && !(temperature > 0.0f && std::isfinite(temperature))) return 2;
+  const float beta = greedy ? 1.0f : temperature_beta(temperature);
   for (int b = 0; b < B; ++b) {
     if (draft_len[b] < 0 || draft_len[b] > gamma) return 2;
     if (row_offsets[b + 1] - row_offsets[b] != draft_len[b] + 1) return 2;
@@ -477,10 +532,16 @@ int oracle_verify(int B, int gamma, int V, int r, const float* target, const int
       const float* row = target + (off + k - 1) * static_cast<int64_t>(V);
       const double lt = softmax_fp64(row, V, pt);
       if (!std::isfinite(lt)) fl |= ORACLE_FLAG_NONFINITE;
-      const int32_t prev = (k == 1) ? anchor[b] : tokens[b * gamma + k - 2];
-      std::vector<float> L;
-      draft_logits(U + (b * gamma + k - 1) * static_cast<int64_t>(V), W1, W2t, V, r, prev, L);
-      softmax_fp64(L.data(), V, pd);
+      if (greedy) {
+        pd.assign(V, 0.0);
+        pd[tokens[b * gamma + k - 1]] = 1.0;
+      } else {
+        const int32_t prev = (k == 1) ? anchor[b] : tokens[b * gamma + k - 2];
+        std::vector<float> L;
+        draft_logits(U + (b * gamma + k - 1) * static_cast<int64_t>(V), W1, W2t, V, r, prev, L);
+        scale_logits(L, beta);
+        softmax_fp64(L.data(), V, pd);
+      }
       w.assign(V, 0.0);
       double mass = 0.0, beta = 0.0;
       for (int v = 0; v < V; ++v) {
@@ -505,6 +566,17 @@ int oracle_verify(int B, int gamma, int V, int r, const float* target, const int
     if (emit_margin) emit_margin[b] = mg;
   });
   return 0;
+}
+
+int oracle_verify(int B, int gamma, int V, int r, const float* target, const int32_t* row_offsets,
+                  const int32_t* draft_len, const float* U, const uint16_t* W1,
+                  const uint16_t* W2t, const int32_t* anchor, const int32_t* tokens,
+                  const float* q, const float* uniforms, int32_t* accept_len,
+                  int32_t* next_token, float* beta_emit, uint32_t* flags, double* accept_margin,
+                  double* emit_margin, double* resid_mass, int threads) {
+  return oracle_verify_opts(B, gamma, V, r, target, row_offsets, draft_len, U, W1, W2t, anchor,
+                            tokens, q, uniforms, 1.0f, 0, accept_len, next_token, beta_emit, flags,
+                            accept_margin, emit_margin, resid_mass, threads);
 }
 
 }  // extern "C"

@@ -9,6 +9,7 @@ import tempfile
 import pytest
 
 import oracle
+import test_oracle_draft_options_pins as op
 import test_oracle_draft_pins as dp
 import test_oracle_plan_pins as pp
 import test_oracle_verify_pins as vp
@@ -40,6 +41,15 @@ MUTATIONS = [
      "std::exp(-z * static_cast<double>(T[k]))", [dp.test_confidence_closed_forms]),
     ("draft inverse CDF from the top", "if (cdf > u) {", "if (cdf > 1.0 - u) {",
      [dp.test_w2_zero_reduces_to_inverse_cdf_categorical]),
+    ("draft temperature multiplies", "return static_cast<float>(1.0 / static_cast<double>(tau));",
+     "return tau;", [op.test_temperature_limits_uniform_and_argmax]),
+    ("greedy takes the last maximum", "if (L[v] > L[best]) best", "if (L[v] >= L[best]) best",
+     [op.test_greedy_draft_closed_form_and_ties]),
+    ("greedy residual keeps the drafted token", "pd[tokens[b * gamma + k - 1]] = 1.0;",
+     "pd[0] = 1.0;", [op.test_greedy_verify_is_lossless_exact_grid]),
+    ("tempered residual left unscaled", "        scale_logits(L, beta);\n        softmax_fp64(L.data(), V, pd);",
+     "        softmax_fp64(L.data(), V, pd);",
+     [functools.partial(op.test_tempered_verify_is_lossless_exact_grid, 0.5)]),
 ]
 
 
