@@ -60,7 +60,7 @@ def traffic_from_profiles(launch_units):
 
 
 class InputSet:
-    def __init__(self, wl, wts, round_index, dev):
+    def __init__(self, wl, wts, round_index, dev, opts):
         d = L.Dims(wl.B, wl.gamma, wl.V, wl.r, wl.d)
         inp = W.round_inputs(wl, round_index, dev, with_hidden=True, with_noise=True)
         self.anchor, self.U, self.h, self.uniforms = inp["anchor"], inp["U"], inp["h"], inp["uniforms"]
@@ -70,7 +70,7 @@ class InputSet:
         # this pass fixes the packed row layout (the timed rounds recompute the same plan).
         logits = torch.empty_like(self.U)
         tok, q, lse = L.markov_draft(d, self.U, wts["W1"], wts["W2t"], self.anchor, self.uniforms,
-                                     logits_dbg=logits)
+                                     logits_dbg=logits, **opts)
         conf = L.confidence(d, self.h, wts["W1"], wts["w"], self.T, self.anchor, tok)
         dl, ro, st = L.plan(d, conf, self.sps, wl.mode)
         dense = W.target_dense(logits, inp["U_bonus"], inp["noise"])
@@ -82,19 +82,23 @@ class InputSet:
         self.draft_len = dl.clone()
 
 
-def algorithmic_bytes(wl, rows, n_res):
+def algorithmic_bytes(wl, rows, n_res, greedy=False):
     """Bytes the method must move in one round (no caching credit): per draft step the U slice
     and W2; the hidden states and confidence weights; every verified target row; for rejected
-    requests one more W2 pass plus their U and target rows."""
+    requests one more W2 pass plus their U and target rows (a greedy draft's residual needs only
+    the target rows: its draft distribution is a point mass)."""
     B, V, g, r, d = wl.B, wl.V, wl.gamma, wl.r, wl.d
     draft = g * (4 * B * V + 2 * r * V)
     conf = 2 * B * g * d + 2 * (d + r)
     stats = 4 * rows * V
-    emit = (2 * r * V if n_res > 0 else 0) + n_res * 8 * V
+    if greedy:
+        emit = n_res * 4 * V
+    else:
+        emit = (2 * r * V if n_res > 0 else 0) + n_res * 8 * V
     return draft + conf + stats + emit
 
 
-def cpu_baseline(wl, wts, s, threads):
+def cpu_baseline(wl, wts, s, threads, opts):
     """The oracle as it stands, timed on the host on one full round of the same workload."""
     import oracle
     host = lambda t: t.detach().cpu().numpy()
@@ -103,7 +107,7 @@ def cpu_baseline(wl, wts, s, threads):
     anchor, unif, h = host(s.anchor), host(s.uniforms), bits(s.h)
     sps = W.sps_table(wl)
     t0 = time.perf_counter()
-    o = oracle.markov_draft(U, W1b, W2b, anchor, unif, want_logits=True, threads=threads)
+    o = oracle.markov_draft(U, W1b, W2b, anchor, unif, want_logits=True, threads=threads, **opts)
     c = oracle.confidence(h, W1b, bits(wts["w"]), W.temperatures(wl).numpy(), anchor, o["tokens"],
                           threads=threads)
     p = oracle.plan(c["conf"], sps, wl.mode)
@@ -117,7 +121,7 @@ def cpu_baseline(wl, wts, s, threads):
     del dense, noise
     t2 = time.perf_counter()
     oracle.verify(target, p["row_offsets"], p["draft_len"], U, W1b, W2b, anchor, o["tokens"],
-                  o["q"], unif, threads=threads)
+                  o["q"], unif, threads=threads, **opts)
     t3 = time.perf_counter()
     sec = (t1 - t0) + (t3 - t2)
     return {"value": 1.0 / sec, "unit": "rounds/s", "cores": threads, "kind": "oracle",
@@ -138,7 +142,16 @@ def main():
                     help="also run a plain 1 GiB device copy (counter calibration under rocprof)")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches only (no hipGraph capture of the round)")
+    ap.add_argument("--temperature", type=float, default=1.0,
+                    help="draft sampling temperature (the drafted distribution softmax(L / tau))")
+    ap.add_argument("--greedy", action="store_true",
+                    help="greedy draft (first maximal logit; the verify's residual is p_t "
+                         "without the drafted token)")
     args = ap.parse_args()
+    if not args.greedy and not (args.temperature > 0 and np.isfinite(args.temperature)):
+        print("--temperature must be positive and finite", file=sys.stderr)
+        sys.exit(2)
+    opts = {"temperature": args.temperature, "greedy": args.greedy}
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build runs on a single MI355X and has no "
               "multi-GPU path; run with --gpus 1", file=sys.stderr)
@@ -149,7 +162,7 @@ def main():
     d = L.Dims(wl.B, wl.gamma, wl.V, wl.r, wl.d)
     L.load_library()
     wts = W.weights(wl, dev)
-    sets = [InputSet(wl, wts, i, dev) for i in range(args.sets)]
+    sets = [InputSet(wl, wts, i, dev, opts) for i in range(args.sets)]
 
     # output and workspace buffers, allocated once
     B, g = wl.B, wl.gamma
@@ -169,11 +182,12 @@ def main():
 
     def round_(s):
         L.markov_draft(d, s.U, wts["W1"], wts["W2t"], s.anchor, s.uniforms, tokens=tok, q=q,
-                       lse=lse, ws=ws_d)
+                       lse=lse, ws=ws_d, **opts)
         L.confidence(d, s.h, wts["W1"], wts["w"], s.T, s.anchor, tok, conf=conf)
         L.plan(d, conf, s.sps, wl.mode, draft_len=dl, row_offsets=ro, stats=st)
         L.verify(d, s.target, ro, dl, s.U, wts["W1"], wts["W2t"], s.anchor, tok, q, lse,
-                 s.uniforms, accept_len=al, next_token=nt, beta_emit=be, flags=fl, ws=ws_v)
+                 s.uniforms, accept_len=al, next_token=nt, beta_emit=be, flags=fl, ws=ws_v,
+                 **opts)
 
     # per-set results (identical every time a set is replayed: deterministic)
     per_set = []
@@ -250,7 +264,8 @@ def main():
     rounds_per_s = args.steps / timed
     used = [per_set[i % len(sets)] for i in range(args.steps)]
     tokens_per_round = float(np.mean([u["tokens"] for u in used]))
-    bytes_per_round = float(np.mean([algorithmic_bytes(wl, u["rows"], u["n_res"]) for u in used]))
+    bytes_per_round = float(np.mean([algorithmic_bytes(wl, u["rows"], u["n_res"], args.greedy)
+                                     for u in used]))
 
     roofline = None
     mfma = None
@@ -283,7 +298,7 @@ def main():
     base = None
     if not args.no_cpu_baseline:
         threads = min(16, os.cpu_count() or 1)
-        base = cpu_baseline(wl, wts, sets[0], threads)
+        base = cpu_baseline(wl, wts, sets[0], threads, opts)
 
     out = {
         "metric": METRIC,
@@ -300,7 +315,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": WORKLOAD, "B": wl.B, "V": wl.V, "gamma": wl.gamma, "r": wl.r,
                    "d": wl.d, "plan": "early_stop", "sps": "1/(1+n/768)", "input_sets": len(sets),
-                   "parallelism": "1 GPU", "launch": "eager"},
+                   "parallelism": "1 GPU", "launch": "eager",
+                   "draft": ("greedy" if args.greedy
+                             else f"sampled at temperature {args.temperature:g}")},
         "round_us": round_us,
         "graph_rounds_per_s": (round(args.steps / elapsed_graph, 2)
                                if elapsed_graph is not None else None),

@@ -6,6 +6,7 @@
  *   dspark_confidence    confidence head c_k = sigmoid(w . [h_k ; W1[x_{k-1}]] / T_k)
  *   dspark_plan          survival-ordered greedy planner that maximises Theta = tau * SPS(B)
  *   dspark_verify        lossless rejection-sampling verify, residual resample, bonus token
+ *   dspark_markov_draft_opts, dspark_verify_opts   the same with a draft temperature or greedy
  *
  * Sources (cited below by tag; each gives the page title and the section or equation):
  *   [V41]  blog.javazero.top, "DeepSeek-V4.1 模型结构（6）：解码，DSpark"
@@ -74,6 +75,7 @@ typedef int32_t dspark_status;
 #define DSPARK_ERR_SPS 5         /* sps_len <= B * (gamma + 1) */
 #define DSPARK_ERR_HIP 6         /* a HIP launch failed */
 #define DSPARK_ERR_MODE 7        /* unknown plan mode, or LAGGED_TOPK without a ring */
+#define DSPARK_ERR_OPTS 8        /* draft options out of range (temperature not positive, finite) */
 
 /* Plan modes. [ZDS] "在 SGLang 里": the static mode verifies every drafted token (no planner);
  * the compact mode plans with the SPS table. */
@@ -132,6 +134,35 @@ DSPARK_API dspark_status dspark_markov_draft(dspark_dims dims, const float* U, c
                                              double* lse, float* logits_dbg,
                                              const int32_t* force_tokens, void* ws, size_t ws_bytes,
                                              void* stream);
+
+/*
+ * Draft sampling options. [V41] "Markov head", the serial loop (each position is sampled with a
+ * temperature); [V41] / [AIL] the deployed recipe drafts greedily (draft_sample_method "greedy").
+ *   temperature  > 0 and finite: the fp32 logits L_k are multiplied, in fp32, by
+ *                beta = fp32(1 / temperature) and x_k ~ softmax(beta L_k); q_tok and lse refer to
+ *                that distribution (temperature 1 is the plain draft, bit for bit).
+ *   greedy       nonzero: x_k is the first token with the largest logit L_k (the temperature is
+ *                ignored); q_tok = 1 (the point mass; 0 for a forced token other than x_k) and
+ *                lse = max_v L_k(v). With non-finite logits the greedy token is unspecified.
+ */
+typedef struct dspark_draft_opts {
+  float temperature;
+  int32_t greedy;
+} dspark_draft_opts;
+
+/*
+ * dspark_markov_draft with draft options (opts NULL: temperature 1, sampling). logits_dbg
+ * receives L_k before the temperature. Returns DSPARK_ERR_OPTS for a temperature that is not
+ * positive and finite (when greedy is 0); the other arguments and checks are those of
+ * dspark_markov_draft.
+ */
+DSPARK_API dspark_status dspark_markov_draft_opts(dspark_dims dims, const float* U,
+                                                  const uint16_t* W1, const uint16_t* W2t,
+                                                  const int32_t* anchor, const float* uniforms,
+                                                  int32_t* tokens, float* q_tok, double* lse,
+                                                  float* logits_dbg, const int32_t* force_tokens,
+                                                  void* ws, size_t ws_bytes,
+                                                  const dspark_draft_opts* opts, void* stream);
 
 /*
  * Confidence head, eq. (7), with the STS temperature applied at inference:
@@ -212,6 +243,25 @@ DSPARK_API dspark_status dspark_verify(dspark_dims dims, const float* target,
                                        const float* uniforms, int32_t* accept_len,
                                        int32_t* next_token, float* beta_emit, uint32_t* flags,
                                        void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * dspark_verify for a draft made with options (opts NULL: temperature 1, sampling). The accept
+ * test is unchanged (q_tok is the draft probability the options produced: 1 for a greedy
+ * draft, which is accepted iff u < p_t(x)); after a reject at position j the residual is
+ * max(0, p_t - p_d) with p_d = softmax(beta L_j) at the draft temperature, or the point mass
+ * on x_j for a greedy draft (so the correction draws from p_t without x_j). lse must be the
+ * draft's output under the same options. [V41] "投机解码…" (the accept / resample rule holds for
+ * any draft distribution, a point mass included). Returns DSPARK_ERR_OPTS as the draft does.
+ */
+DSPARK_API dspark_status dspark_verify_opts(dspark_dims dims, const float* target,
+                                            const int32_t* row_offsets, const int32_t* draft_len,
+                                            const float* U, const uint16_t* W1, const uint16_t* W2t,
+                                            const int32_t* anchor, const int32_t* tokens,
+                                            const float* q_tok, const double* lse,
+                                            const float* uniforms, int32_t* accept_len,
+                                            int32_t* next_token, float* beta_emit, uint32_t* flags,
+                                            void* ws, size_t ws_bytes,
+                                            const dspark_draft_opts* opts, void* stream);
 
 /*
  * Kernel timing with HIP events (measurement support; not part of the method).

@@ -42,6 +42,17 @@ class _CDims(ctypes.Structure):
                 ("r", ctypes.c_int32), ("d", ctypes.c_int32)]
 
 
+class _CDraftOpts(ctypes.Structure):
+    _fields_ = [("temperature", ctypes.c_float), ("greedy", ctypes.c_int32)]
+
+
+def _opts(temperature: float, greedy: bool):
+    """Draft options for the *_opts entry points (None: temperature 1, sampling)."""
+    if not greedy and float(temperature) == 1.0:
+        return None
+    return ctypes.byref(_CDraftOpts(float(temperature), 1 if greedy else 0))
+
+
 @dataclass(frozen=True)
 class Dims:
     B: int
@@ -73,6 +84,9 @@ def load_library():
         lib.dspark_workspace_bytes.argtypes = [_CDims, ctypes.c_int32]
         lib.dspark_markov_draft.restype = ctypes.c_int32
         lib.dspark_markov_draft.argtypes = [_CDims] + [_P] * 10 + [_P, ctypes.c_size_t, _P]
+        lib.dspark_markov_draft_opts.restype = ctypes.c_int32
+        lib.dspark_markov_draft_opts.argtypes = ([_CDims] + [_P] * 10 +
+                                                 [_P, ctypes.c_size_t, _P, _P])
         lib.dspark_confidence.restype = ctypes.c_int32
         lib.dspark_confidence.argtypes = [_CDims] + [_P] * 7 + [_P]
         lib.dspark_plan.restype = ctypes.c_int32
@@ -80,6 +94,8 @@ def load_library():
                                     ctypes.c_int32, _P, _P, _P, _P]
         lib.dspark_verify.restype = ctypes.c_int32
         lib.dspark_verify.argtypes = [_CDims] + [_P] * 15 + [_P, ctypes.c_size_t, _P]
+        lib.dspark_verify_opts.restype = ctypes.c_int32
+        lib.dspark_verify_opts.argtypes = [_CDims] + [_P] * 15 + [_P, ctypes.c_size_t, _P, _P]
         lib.dspark_profile_begin.restype = ctypes.c_int32
         lib.dspark_profile_begin.argtypes = [ctypes.c_int32]
         lib.dspark_profile_end.restype = ctypes.c_int32
@@ -134,15 +150,17 @@ def workspace(dims: Dims, op: int, device="cuda") -> torch.Tensor:
 
 
 def markov_draft(dims: Dims, U, W1, W2t, anchor, uniforms, *, tokens=None, q=None, lse=None,
-                 logits_dbg=None, force_tokens=None, ws=None, stream=None):
-    """Markov-head draft (dspark_markov_draft). Returns (tokens, q, lse)."""
+                 logits_dbg=None, force_tokens=None, ws=None, temperature: float = 1.0,
+                 greedy: bool = False, stream=None):
+    """Markov-head draft (dspark_markov_draft_opts): sampled at `temperature`, or greedy.
+    Returns (tokens, q, lse)."""
     B, g, V, r = dims.B, dims.gamma, dims.V, dims.r
     dev = U.device
     tokens = tokens if tokens is not None else torch.empty((B, g), dtype=torch.int32, device=dev)
     q = q if q is not None else torch.empty((B, g), dtype=torch.float32, device=dev)
     lse = lse if lse is not None else torch.empty((B, g), dtype=torch.float64, device=dev)
     ws = ws if ws is not None else workspace(dims, OP_DRAFT, dev)
-    st = load_library().dspark_markov_draft(
+    st = load_library().dspark_markov_draft_opts(
         dims.c(), _ptr(U, torch.float32, (B, g, V), "U"), _ptr(W1, torch.bfloat16, (V, r), "W1"),
         _ptr(W2t, torch.bfloat16, (V, r), "W2t"), _ptr(anchor, torch.int32, (B,), "anchor"),
         _ptr(uniforms, torch.float32, (B, g + 1, 3), "uniforms"),
@@ -150,8 +168,8 @@ def markov_draft(dims: Dims, U, W1, W2t, anchor, uniforms, *, tokens=None, q=Non
         _ptr(lse, torch.float64, (B, g), "lse"),
         _ptr(logits_dbg, torch.float32, (B, g, V), "logits_dbg"),
         _ptr(force_tokens, torch.int32, (B, g), "force_tokens"), _ptr(ws, torch.uint8, None, "ws"),
-        ws.numel(), _stream(stream))
-    _check(st, "dspark_markov_draft")
+        ws.numel(), _opts(temperature, greedy), _stream(stream))
+    _check(st, "dspark_markov_draft_opts")
     return tokens, q, lse
 
 
@@ -189,9 +207,10 @@ def plan(dims: Dims, conf, sps, mode: int, *, ring=None, round_index: int = 0, d
 
 def verify(dims: Dims, target, row_offsets, draft_len, U, W1, W2t, anchor, tokens, q, lse,
            uniforms, *, accept_len=None, next_token=None, beta_emit=None, flags=None, ws=None,
-           stream=None):
-    """Lossless verify (dspark_verify). `target` holds at least row_offsets[B] rows of V
-    logits. Returns (accept_len, next_token, beta_emit, flags)."""
+           temperature: float = 1.0, greedy: bool = False, stream=None):
+    """Lossless verify (dspark_verify_opts) of a draft made at `temperature` (or greedy).
+    `target` holds at least row_offsets[B] rows of V logits.
+    Returns (accept_len, next_token, beta_emit, flags)."""
     B, g, V, r = dims.B, dims.gamma, dims.V, dims.r
     dev = U.device
     if target.dim() != 2 or target.shape[1] != V:
@@ -201,7 +220,7 @@ def verify(dims: Dims, target, row_offsets, draft_len, U, W1, W2t, anchor, token
     beta_emit = beta_emit if beta_emit is not None else torch.empty(B, dtype=torch.float32, device=dev)
     flags = flags if flags is not None else torch.empty(B, dtype=torch.int32, device=dev)
     ws = ws if ws is not None else workspace(dims, OP_VERIFY, dev)
-    st = load_library().dspark_verify(
+    st = load_library().dspark_verify_opts(
         dims.c(), _ptr(target, torch.float32, None, "target"),
         _ptr(row_offsets, torch.int32, (B + 1,), "row_offsets"),
         _ptr(draft_len, torch.int32, (B,), "draft_len"), _ptr(U, torch.float32, (B, g, V), "U"),
@@ -212,8 +231,8 @@ def verify(dims: Dims, target, row_offsets, draft_len, U, W1, W2t, anchor, token
         _ptr(accept_len, torch.int32, (B,), "accept_len"),
         _ptr(next_token, torch.int32, (B,), "next_token"),
         _ptr(beta_emit, torch.float32, (B,), "beta_emit"), _ptr(flags, torch.int32, (B,), "flags"),
-        _ptr(ws, torch.uint8, None, "ws"), ws.numel(), _stream(stream))
-    _check(st, "dspark_verify")
+        _ptr(ws, torch.uint8, None, "ws"), ws.numel(), _opts(temperature, greedy), _stream(stream))
+    _check(st, "dspark_verify_opts")
     return accept_len, next_token, beta_emit, flags
 
 

@@ -2,6 +2,7 @@
 // The operations and their sources are documented in include/dspark.h.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdint>
 #include <cstring>
 #include <vector>
@@ -40,6 +41,22 @@ bool plan_dims_ok(const dspark_dims& d) {
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 // Compute units of the current device (cached per device id).
+// Draft options: beta = fp32(1 / temperature) (1 for greedy or no options). False when the
+// temperature is not positive and finite.
+bool draft_options(const dspark_draft_opts* opts, float* beta, int* greedy) {
+  *beta = 1.0f;
+  *greedy = 0;
+  if (!opts) return true;
+  if (opts->greedy) {
+    *greedy = 1;
+    return true;
+  }
+  const float t = opts->temperature;
+  if (!(t > 0.0f) || !std::isfinite(t)) return false;
+  *beta = static_cast<float>(1.0 / static_cast<double>(t));
+  return true;
+}
+
 int compute_units() {
   static int cached[64] = {0};
   int dev = 0;
@@ -141,6 +158,7 @@ const char* dspark_status_string(dspark_status s) {
     case DSPARK_ERR_SPS: return "SPS table shorter than B * (gamma + 1) + 1";
     case DSPARK_ERR_HIP: return "HIP launch failed";
     case DSPARK_ERR_MODE: return "unknown plan mode or missing ring";
+    case DSPARK_ERR_OPTS: return "draft temperature not positive and finite";
     default: return "unknown status";
   }
 }
@@ -158,13 +176,17 @@ size_t dspark_workspace_bytes(dspark_dims dims, int32_t op) {
   }
 }
 
-dspark_status dspark_markov_draft(dspark_dims dims, const float* U, const uint16_t* W1,
-                                  const uint16_t* W2t, const int32_t* anchor,
-                                  const float* uniforms, int32_t* tokens, float* q_tok,
-                                  double* lse, float* logits_dbg, const int32_t* force_tokens,
-                                  void* ws, size_t ws_bytes, void* stream) {
+dspark_status dspark_markov_draft_opts(dspark_dims dims, const float* U, const uint16_t* W1,
+                                       const uint16_t* W2t, const int32_t* anchor,
+                                       const float* uniforms, int32_t* tokens, float* q_tok,
+                                       double* lse, float* logits_dbg,
+                                       const int32_t* force_tokens, void* ws, size_t ws_bytes,
+                                       const dspark_draft_opts* opts, void* stream) {
   if (!U || !W1 || !W2t || !anchor || !uniforms || !tokens || !q_tok || !lse || !ws)
     return DSPARK_ERR_NULL;
+  float beta = 1.0f;
+  int greedy = 0;
+  if (!draft_options(opts, &beta, &greedy)) return DSPARK_ERR_OPTS;
   if (!dims_ok(dims)) return DSPARK_ERR_SHAPE;
   if (!aligned(U, 16) || !aligned(W1, 16) || !aligned(W2t, 16) || !aligned(anchor, 4) ||
       !aligned(uniforms, 4) || !aligned(tokens, 4) || !aligned(q_tok, 4) || !aligned(lse, 8) ||
@@ -185,15 +207,24 @@ dspark_status dspark_markov_draft(dspark_dims dims, const float* U, const uint16
       stride = dims.gamma;
     }
     StepArgs sa{dims.B, dims.V, dims.gamma, k, nt, U, W1, W2t, prev, stride, w.part, logits_dbg,
-                cus};
+                cus, beta};
     if (timed(kMarkovStep, s, [&] { return launch_markov_step(sa, dims.r, s); }) != hipSuccess)
       return DSPARK_ERR_HIP;
     SampleArgs pa{dims.B, dims.V, dims.gamma, k, nt, U, W1, W2t, prev, stride, w.part,
-                  uniforms, force_tokens, tokens, q_tok, lse};
+                  uniforms, force_tokens, tokens, q_tok, lse, beta, greedy};
     if (timed(kDraftSample, s, [&] { return launch_draft_sample(pa, dims.r, s); }) != hipSuccess)
       return DSPARK_ERR_HIP;
   }
   return DSPARK_OK;
+}
+
+dspark_status dspark_markov_draft(dspark_dims dims, const float* U, const uint16_t* W1,
+                                  const uint16_t* W2t, const int32_t* anchor,
+                                  const float* uniforms, int32_t* tokens, float* q_tok,
+                                  double* lse, float* logits_dbg, const int32_t* force_tokens,
+                                  void* ws, size_t ws_bytes, void* stream) {
+  return dspark_markov_draft_opts(dims, U, W1, W2t, anchor, uniforms, tokens, q_tok, lse,
+                                  logits_dbg, force_tokens, ws, ws_bytes, nullptr, stream);
 }
 
 dspark_status dspark_confidence(dspark_dims dims, const uint16_t* h, const uint16_t* W1,
@@ -231,15 +262,19 @@ dspark_status dspark_plan(dspark_dims dims, const float* conf, const double* sps
   return DSPARK_OK;
 }
 
-dspark_status dspark_verify(dspark_dims dims, const float* target, const int32_t* row_offsets,
-                            const int32_t* draft_len, const float* U, const uint16_t* W1,
-                            const uint16_t* W2t, const int32_t* anchor, const int32_t* tokens,
-                            const float* q_tok, const double* lse, const float* uniforms,
-                            int32_t* accept_len, int32_t* next_token, float* beta_emit,
-                            uint32_t* flags, void* ws, size_t ws_bytes, void* stream) {
+dspark_status dspark_verify_opts(dspark_dims dims, const float* target,
+                                 const int32_t* row_offsets, const int32_t* draft_len,
+                                 const float* U, const uint16_t* W1, const uint16_t* W2t,
+                                 const int32_t* anchor, const int32_t* tokens, const float* q_tok,
+                                 const double* lse, const float* uniforms, int32_t* accept_len,
+                                 int32_t* next_token, float* beta_emit, uint32_t* flags, void* ws,
+                                 size_t ws_bytes, const dspark_draft_opts* opts, void* stream) {
   if (!target || !row_offsets || !draft_len || !U || !W1 || !W2t || !anchor || !tokens ||
       !q_tok || !lse || !uniforms || !accept_len || !next_token || !ws)
     return DSPARK_ERR_NULL;
+  float beta = 1.0f;
+  int greedy = 0;
+  if (!draft_options(opts, &beta, &greedy)) return DSPARK_ERR_OPTS;
   if (!dims_ok(dims)) return DSPARK_ERR_SHAPE;
   if (!aligned(target, 16) || !aligned(U, 16) || !aligned(W1, 16) || !aligned(W2t, 16) ||
       !aligned(row_offsets, 4) || !aligned(draft_len, 4) || !aligned(anchor, 4) ||
@@ -271,6 +306,8 @@ dspark_status dspark_verify(dspark_dims dims, const float* target, const int32_t
   a.beta_emit = beta_emit;
   a.flags = flags;
   a.persistent_wgs = compute_units();
+  a.beta = beta;
+  a.greedy = greedy;
   verify_ws(dims, ws, &a.ws);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (timed(kTargetStats, s, [&] { return launch_target_stats(a, s); }) != hipSuccess)
@@ -281,6 +318,17 @@ dspark_status dspark_verify(dspark_dims dims, const float* target, const int32_t
   if (timed(kEmitSample, s, [&] { return launch_emit_sample(a, s); }) != hipSuccess)
     return DSPARK_ERR_HIP;
   return DSPARK_OK;
+}
+
+dspark_status dspark_verify(dspark_dims dims, const float* target, const int32_t* row_offsets,
+                            const int32_t* draft_len, const float* U, const uint16_t* W1,
+                            const uint16_t* W2t, const int32_t* anchor, const int32_t* tokens,
+                            const float* q_tok, const double* lse, const float* uniforms,
+                            int32_t* accept_len, int32_t* next_token, float* beta_emit,
+                            uint32_t* flags, void* ws, size_t ws_bytes, void* stream) {
+  return dspark_verify_opts(dims, target, row_offsets, draft_len, U, W1, W2t, anchor, tokens,
+                            q_tok, lse, uniforms, accept_len, next_token, beta_emit, flags, ws,
+                            ws_bytes, nullptr, stream);
 }
 
 int32_t dspark_profile_begin(int32_t capacity) {

@@ -137,7 +137,8 @@ struct StepKernel {
     }
   }
 
-  // Epilogue: L = U + bias, tile max, fp32 sum of exp(L - max), one float2 per (request, tile).
+  // Epilogue: L = U + bias (written out as the debug logits when asked), scaled by the draft
+  // temperature, tile max, fp32 sum of exp(x - max), one float2 per (request, tile).
   __device__ __forceinline__ void epilogue(f32x16_t (&acc)[kNTW], int it) const {
     const int tile = it / ngroups, group = it % ngroups;
     const int tok0 = tile * kTok + ts * kTileTokens;
@@ -160,6 +161,17 @@ struct StepKernel {
         for (int j = 0; j < 16; ++j)
           if (tok0 + tile_token(j, half) >= p.V) acc[nt][j] = kNegInf;
       }
+      const int b = group * BG + rt * 32 + col;
+      if (p.dbg && b < p.B) {   // the logits L themselves, before the temperature
+        const size_t drow = (static_cast<size_t>(b) * p.gamma + p.k) * p.V;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int v = tok0 + tile_token(j, half);
+          if (v < p.V) p.dbg[drow + v] = acc[nt][j];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[nt][j] *= p.beta;
       float L[16];
 #pragma unroll
       for (int j = 0; j < 16; ++j) L[j] = acc[nt][j];
@@ -181,14 +193,6 @@ struct StepKernel {
       const int b = group * BG + (bh * kNTW + nt) * 32 + col;
       if (b >= p.B) continue;
       if (half == 0) p.part[static_cast<size_t>(b) * p.ntiles + tok0 / kTileTokens] = make_float2(m[nt], sm[nt]);
-      if (p.dbg) {
-        const size_t drow = (static_cast<size_t>(b) * p.gamma + p.k) * p.V;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int v = tok0 + tile_token(j, half);
-          if (v < p.V) p.dbg[drow + v] = acc[nt][j];
-        }
-      }
     }
   }
 };
@@ -419,9 +423,9 @@ __global__ __launch_bounds__(kDmaThreads, 1) void markov_step_dma_kernel(StepArg
         for (int jj = 0; jj < 16; ++jj)
           if (tok0 + tile_token(jj, half) >= p.V) acc[jj] = kNegInf;
       }
-      float L[16];
+      float L[16];   // the draft temperature scales the logits (beta = 1: unchanged)
 #pragma unroll
-      for (int jj = 0; jj < 16; ++jj) L[jj] = acc[jj];
+      for (int jj = 0; jj < 16; ++jj) L[jj] = acc[jj] * p.beta;
       float m = max16(L);
       m = fmaxf(m, other_half(m, half));
       float t[16];
@@ -448,7 +452,9 @@ __global__ __launch_bounds__(kDmaThreads, 1) void markov_step_dma_kernel(StepArg
 // Wave 0 then locates the draw u * Z in three levels, each a wave scan and a ballot: the group
 // of threads, the thread, and the tile (the last candidate with positive mass whose exclusive
 // prefix is <= u * Z at the first two levels, the first tile whose inclusive prefix passes it at
-// the last). Wave 0 recomputes that tile's logits and walks them to the token.
+// the last). Wave 0 recomputes that tile's logits and walks them to the token. The logits are
+// scaled by the draft temperature as in the step kernel; a greedy draft instead takes the first
+// maximal logit (the first tile whose max is the row max, then its first lane holding it).
 // r = 512 takes 512 threads: its 32-step tile recompute needs more than 128 registers a lane.
 template <int KS>
 struct SampleCfg {
@@ -465,6 +471,7 @@ __global__ __launch_bounds__(SampleCfg<KS>::kThreads) void draft_sample_kernel(S
   constexpr int kSampleThreads = SampleCfg<KS>::kThreads;
   constexpr int kSamplePer = SampleCfg<KS>::kPer;
   __shared__ float red_f[kSampleThreads / 64];
+  __shared__ int red_i[kSampleThreads / 64];
   __shared__ double ssum[kSampleThreads];
   extern __shared__ double mass[];   // [ntiles], dynamic
   __shared__ float Ls[kTileTokens];
@@ -510,24 +517,43 @@ __global__ __launch_bounds__(SampleCfg<KS>::kThreads) void draft_sample_kernel(S
 #pragma unroll
   for (int i = 0; i < kSamplePer; ++i) m = fmaxf(m, v[i].x);
   const float M = block_max<kSampleThreads>(m, red_f);
-  double S = 0.0;
+  int gtile = 0x7fffffff;
+  if (p.greedy) {
+    // Greedy draft (the partials hold unscaled logits): the first tile whose max is the row max.
+    int first = 0x7fffffff;
 #pragma unroll
-  for (int i = 0; i < kSamplePer; ++i) {
-    if (i < per && c0 + i < c1) {
-      const double mi = tile_mass(v[i].x, v[i].y, M);
-      mass[c0 + i] = mi;
-      S += mi;
+    for (int i = 0; i < kSamplePer; ++i)
+      if (i < per && c0 + i < c1 && v[i].x == M) first = min(first, c0 + i);
+    gtile = block_min_int<kSampleThreads>(first, red_i);
+  } else {
+    double S = 0.0;
+#pragma unroll
+    for (int i = 0; i < kSamplePer; ++i) {
+      if (i < per && c0 + i < c1) {
+        const double mi = tile_mass(v[i].x, v[i].y, M);
+        mass[c0 + i] = mi;
+        S += mi;
+      }
     }
+    ssum[tid] = S;
+    __syncthreads();
   }
-  ssum[tid] = S;
-  __syncthreads();
   if (tid >= 64) return;
-  const double u =
-      static_cast<double>(p.uniforms[(static_cast<size_t>(b) * (p.gamma + 1) + p.k) * 3]);
-  const Located L = wave_locate<kSampleThreads>(
-      ssum, nt, per, [u](double Z) { return u * Z; }, [&](int c) { return mass[c]; });
-  const double target = L.target;
-  const double lse = static_cast<double>(M) + log(L.total);
+  Located L;
+  double lse;
+  if (p.greedy) {
+    L.chunk = (gtile == 0x7fffffff) ? -1 : gtile;
+    L.before = 0.0;
+    L.target = 0.0;
+    L.take_last = 0;
+    lse = static_cast<double>(M);
+  } else {
+    const double u =
+        static_cast<double>(p.uniforms[(static_cast<size_t>(b) * (p.gamma + 1) + p.k) * 3]);
+    L = wave_locate<kSampleThreads>(
+        ssum, nt, per, [u](double Z) { return u * Z; }, [&](int c) { return mass[c]; });
+    lse = static_cast<double>(M) + log(L.total);
+  }
   if (L.chunk < 0) {  // logits not finite: documented fallback
     if (tid == 0) {
       p.tokens[out] = 0;
@@ -542,25 +568,36 @@ __global__ __launch_bounds__(SampleCfg<KS>::kThreads) void draft_sample_kernel(S
   recompute_tile_lds<KS>(Es, p.W2t, p.U + urow, tok0, p.V, Ls);
   __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_wave_barrier();
-  const double f = static_cast<double>(exp_term(tm - M));
-  // Lane j's token mass for the walk and its probability exp(L_j - lse) (independent of the
-  // walk, so the two overlap; the reported one is read from its lane afterwards).
-  double w = 0.0, qj = 0.0;
-  if (lane < kTileTokens && tok0 + lane < p.V) {
-    w = f * static_cast<double>(exp_term(Ls[lane] - tm));
-    qj = exp(static_cast<double>(Ls[lane]) - lse);
-  }
-  const int x = tok0 + walk_tile(w, L.before, target, L.take_last != 0);
-  // The token whose probability is reported (and that conditions the next position).
-  const int32_t cond = p.force ? forced : x;
+  int x;
   double qc;
-  if (cond / kTileTokens != L.chunk) {
-    recompute_tile_lds<KS>(Es, p.W2t, p.U + urow, (cond / kTileTokens) * kTileTokens, p.V, Lc);
-    __builtin_amdgcn_s_waitcnt(0);
-    __builtin_amdgcn_wave_barrier();
-    qc = exp(static_cast<double>(Lc[cond % kTileTokens]) - lse);
+  if (p.greedy) {
+    // The first token of the tile holding the row max in the bit-identical recompute; the draft
+    // distribution is the point mass on it.
+    const unsigned long long hit =
+        __ballot(lane < kTileTokens && tok0 + lane < p.V && Ls[lane] == M);
+    x = tok0 + (hit ? __ffsll(static_cast<long long>(hit)) - 1 : 0);
+    qc = ((p.force ? forced : x) == x) ? 1.0 : 0.0;
   } else {
-    qc = read_lane(qj, cond % kTileTokens);
+    const double f = static_cast<double>(exp_term(tm - M));
+    // Lane j's token mass for the walk and its probability exp(x_j - lse) (independent of the
+    // walk, so the two overlap; the reported one is read from its lane afterwards).
+    double w = 0.0, qj = 0.0;
+    if (lane < kTileTokens && tok0 + lane < p.V) {
+      const float xl = Ls[lane] * p.beta;   // as the step kernel scaled it
+      w = f * static_cast<double>(exp_term(xl - tm));
+      qj = exp(static_cast<double>(xl) - lse);
+    }
+    x = tok0 + walk_tile(w, L.before, L.target, L.take_last != 0);
+    // The token whose probability is reported (and that conditions the next position).
+    const int32_t cond = p.force ? forced : x;
+    if (cond / kTileTokens != L.chunk) {
+      recompute_tile_lds<KS>(Es, p.W2t, p.U + urow, (cond / kTileTokens) * kTileTokens, p.V, Lc);
+      __builtin_amdgcn_s_waitcnt(0);
+      __builtin_amdgcn_wave_barrier();
+      qc = exp(static_cast<double>(Lc[cond % kTileTokens] * p.beta) - lse);
+    } else {
+      qc = read_lane(qj, cond % kTileTokens);
+    }
   }
   if (tid == 0) {
     p.tokens[out] = x;

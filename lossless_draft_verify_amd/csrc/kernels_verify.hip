@@ -222,13 +222,15 @@ __global__ __launch_bounds__(kBlock) void accept_kernel(VerifyArgs p) {
   fl = (__ballot(fl != 0u) != 0ull) ? 1u : 0u;
   // Inputs of the residual record: positions 0..63 come from the registers loaded in step 0,
   // later ones from memory.
-  int32_t prev_x = anc;
+  int32_t prev_x = anc, xtok = 0;
   double lse_d = 0.0;
   if (rejected) {
     const int32_t xs = read_lane(static_cast<int>(x0), (last + 63) & 63);   // last: wave-uniform
+    const int32_t xr = read_lane(static_cast<int>(x0), last & 63);
     const double ls = read_lane(lsed0, last & 63);
     prev_x = (last == 0) ? anc
              : (last - 1 < 64 ? xs : p.tokens[static_cast<size_t>(b) * p.gamma + last - 1]);
+    xtok = (last < 64) ? xr : p.tokens[static_cast<size_t>(b) * p.gamma + last];
     lse_d = (last < 64) ? ls : p.lse[static_cast<size_t>(b) * p.gamma + last];
   }
   if (lane == 0) {
@@ -238,6 +240,7 @@ __global__ __launch_bounds__(kBlock) void accept_kernel(VerifyArgs p) {
       r.j = last + 1;
       r.erow = off + last;
       r.prev = prev_x;
+      r.tok = xtok;
       r.lse_d = lse_d;
       r.lse_t = lse_s[w][last];
       p.ws.rrec[atomicAdd(p.ws.rcount, 1)] = r;
@@ -256,18 +259,35 @@ __device__ __forceinline__ int32_t emit_prev(const VerifyArgs& p, int b, int j) 
   return (j == 1) ? p.anchor[b] : p.tokens[static_cast<size_t>(b) * p.gamma + j - 2];
 }
 
+// Draft probability of one token: softmax(beta L) of the position (lse_d its log-sum-exp, beta
+// the draft temperature's multiplier, applied in fp32 as in the draft), or, for a greedy draft,
+// the point mass on the drafted token.
+__device__ __forceinline__ double draft_prob(float L, float beta, double lse_d, bool greedy,
+                                             bool drafted) {
+  return greedy ? (drafted ? 1.0 : 0.0) : exp(static_cast<double>(L * beta) - lse_d);
+}
+// The same with the kind of draft fixed at compile time (the residual passes, where a run-time
+// select per token is measurable; a greedy pass never reads the draft logits).
+template <bool Greedy>
+__device__ __forceinline__ double draft_prob_t(float L, float beta, double lse_d, bool drafted) {
+  if constexpr (Greedy) {
+    return drafted ? 1.0 : 0.0;
+  } else {
+    return exp(static_cast<double>(L * beta) - lse_d);
+  }
+}
+
 // Residual weight and overlap of one token: w = max(0, p_t - p_d), o = min(p_t, p_d), with
 // NaN behaving as in the comparisons written here (a NaN difference gives w = 0).
-__device__ __forceinline__ void residual_pair(float L, float t, double lse_d, double lse_t,
-                                              double& w, double& o) {
-  const double pd = exp(static_cast<double>(L) - lse_d);
+__device__ __forceinline__ void residual_pair(double pd, float t, double lse_t, double& w,
+                                              double& o) {
   const double pt = exp(static_cast<double>(t) - lse_t);
   const double d = pt - pd;
   w = (0.0 < d) ? d : 0.0;
   o = (pd < pt) ? pd : pt;
 }
 
-template <int KS>
+template <int KS, bool Greedy>
 __global__ __launch_bounds__(kBlock, 2) void residual_partials_kernel(VerifyArgs p) {
   using C = StepCfg<KS>;
   constexpr int r = C::kR;
@@ -330,6 +350,7 @@ __global__ __launch_bounds__(kBlock, 2) void residual_partials_kernel(VerifyArgs
           const float* trow = p.target + static_cast<size_t>(p.ws.erow[b]) * p.V;
           const double lse_d = p.lse[static_cast<size_t>(b) * p.gamma + j - 1];
           const double lse_t = p.ws.erow_lse[b];
+          const int32_t xtok = p.tokens[static_cast<size_t>(b) * p.gamma + j - 1];
           float L[16];
           tile_logits(acc, Urow, tok0, p.V, half, vec4, L);
           double W = 0.0, O = 0.0;
@@ -342,7 +363,8 @@ __global__ __launch_bounds__(kBlock, 2) void residual_partials_kernel(VerifyArgs
             for (int e = 0; e < 4; ++e) {
               if (v + e < p.V) {
                 double w, o;
-                residual_pair(L[4 * g + e], t[e], lse_d, lse_t, w, o);
+                residual_pair(draft_prob_t<Greedy>(L[4 * g + e], p.beta, lse_d, v + e == xtok),
+                              t[e], lse_t, w, o);
                 W += w;
                 O += o;
               }
@@ -399,7 +421,7 @@ struct ResStep {
   static_assert(kResGroup * kW2Chunks * 16 <= kStageBytes, "embedding rows fit in one stage");
 };
 
-template <int KS>
+template <int KS, bool Greedy>
 __global__ __launch_bounds__(kResThreads, 1) void residual_dma_kernel(VerifyArgs p) {
   using D = ResStep<KS>;
   __shared__ __attribute__((aligned(1024))) unsigned char stage[D::kStages * D::kStageBytes];
@@ -523,6 +545,7 @@ __global__ __launch_bounds__(kResThreads, 1) void residual_dma_kernel(VerifyArgs
           eb + 16 * (row_own * D::kW2Chunks + ((2 * s + half) ^ (row_own & D::kW2Swz))));
   }
   const double lse_d = rec[row_own].lse_d, lse_t = rec[row_own].lse_t;
+  const int32_t xtok = rec[row_own].tok;
   lds_barrier();
   int flushed = 0;
   for (int j = 0; j < n; ++j) {
@@ -561,7 +584,9 @@ __global__ __launch_bounds__(kResThreads, 1) void residual_dma_kernel(VerifyArgs
         for (int i = 0; i < 4; ++i) {
           if (v + i < p.V) {
             double w, o;
-            residual_pair(u4[i] + acc[4 * g + i], t4[i], lse_d, lse_t, w, o);
+            residual_pair(draft_prob_t<Greedy>(u4[i] + acc[4 * g + i], p.beta, lse_d,
+                                               v + i == xtok),
+                          t4[i], lse_t, w, o);
             W += w;
             O += o;
           }
@@ -666,8 +691,10 @@ __global__ __launch_bounds__(kBlock) void emit_sample_kernel(VerifyArgs p) {
       double w = 0.0;
       if (lane < kTileTokens && tok0 + lane < p.V) {
         double ov;
-        residual_pair(Ls[lane], tv, p.lse[static_cast<size_t>(b) * p.gamma + j - 1],
-                      p.ws.erow_lse[b], w, ov);
+        const int32_t xtok = p.tokens[static_cast<size_t>(b) * p.gamma + j - 1];
+        residual_pair(draft_prob(Ls[lane], p.beta, p.lse[static_cast<size_t>(b) * p.gamma + j - 1],
+                                 p.greedy, tok0 + lane == xtok),
+                      tv, p.ws.erow_lse[b], w, ov);
       }
       token = tok0 + walk_tile(w, L.before, L.target, L.take_last != 0);
     }
@@ -761,21 +788,26 @@ hipError_t launch_accept(const VerifyArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int KS>
-static hipError_t launch_resid_ks(const VerifyArgs& a, hipStream_t s) {
+template <int KS, bool Greedy>
+static hipError_t launch_resid_kind(const VerifyArgs& a, hipStream_t s) {
   // The pipelined pass copies 16-byte row chunks (V % 4 == 0) and 1-2 KB of W2t per wave
   // (128 <= r <= 256); other shapes take the register-load kernel.
   if constexpr (KS >= 8 && KS <= 16) {
     if ((a.V & 3) == 0) {
       const int groups = (a.B + kResGroup - 1) / kResGroup;
       const int grid = a.persistent_wgs > groups ? a.persistent_wgs : groups;
-      hipLaunchKernelGGL(residual_dma_kernel<KS>, dim3(grid), dim3(kResThreads), 0, s, a);
+      hipLaunchKernelGGL((residual_dma_kernel<KS, Greedy>), dim3(grid), dim3(kResThreads), 0, s,
+                         a);
       return hipGetLastError();
     }
   }
   const int grid = (a.V + 4 * kTileTokens - 1) / (4 * kTileTokens);
-  hipLaunchKernelGGL(residual_partials_kernel<KS>, dim3(grid), dim3(kBlock), 0, s, a);
+  hipLaunchKernelGGL((residual_partials_kernel<KS, Greedy>), dim3(grid), dim3(kBlock), 0, s, a);
   return hipGetLastError();
+}
+template <int KS>
+static hipError_t launch_resid_ks(const VerifyArgs& a, hipStream_t s) {
+  return a.greedy ? launch_resid_kind<KS, true>(a, s) : launch_resid_kind<KS, false>(a, s);
 }
 template <int KS>
 static hipError_t launch_emit_ks(const VerifyArgs& a, hipStream_t s) {

@@ -15,8 +15,9 @@ struct StepArgs {
   const int32_t* prev;  // conditioning token of request b at prev[b * prev_stride]
   int prev_stride;
   float2* part;         // [B][ntiles] (tile max, sum exp(L - tile max))
-  float* dbg;           // nullable [B][gamma][V]
+  float* dbg;           // nullable [B][gamma][V] (the logits L, before the temperature)
   int persistent_wgs;   // workgroups of the persistent step kernel (one per compute unit)
+  float beta;           // logits are scaled by beta = fp32(1 / temperature) (1: unscaled)
 };
 
 struct SampleArgs {
@@ -32,6 +33,8 @@ struct SampleArgs {
   int32_t* tokens;
   float* q;
   double* lse;
+  float beta;   // as in StepArgs
+  int greedy;   // draft the first maximal logit (point-mass q)
 };
 
 struct ConfArgs {
@@ -65,6 +68,7 @@ struct ResRec {
   int32_t j;       // 1-based emission position (the first rejected draft position)
   int32_t erow;    // packed target row of position j
   int32_t prev;    // token before position j (the anchor for j = 1)
+  int32_t tok;     // the drafted token of position j (the point mass of a greedy draft)
   double lse_d;    // log-sum-exp of the draft logits of position j
   double lse_t;    // log-sum-exp of the target row
 };
@@ -101,6 +105,8 @@ struct VerifyArgs {
   float* beta_emit;   // nullable
   uint32_t* flags;    // nullable
   int persistent_wgs; // workgroups of the pipelined residual kernel (one per compute unit)
+  float beta;         // the draft distribution: softmax(beta L), beta = fp32(1 / temperature)
+  int greedy;         // or the point mass on the drafted token (greedy drafts)
   VerifyWs ws;
 };
 

@@ -72,21 +72,23 @@ class MismatchCounter:
                 f"({100 * self.rate():.3f} %), flagged {100 * self.flagged / max(1, self.draws):.1f} %")
 
 
-def gpu_draft(wl, inp, wts, force=None, dbg=False, B=None):
+def gpu_draft(wl, inp, wts, force=None, dbg=False, B=None, temperature=1.0, greedy=False):
     d = dims_of(wl, B)
     dev = inp["U"].device
     logits = torch.empty_like(inp["U"]) if dbg else None
     f = None if force is None else torch.as_tensor(force, dtype=torch.int32, device=dev).contiguous()
     t, q, lse = L.markov_draft(d, inp["U"], wts["W1"], wts["W2t"], inp["anchor"], inp["uniforms"],
-                               logits_dbg=logits, force_tokens=f)
+                               logits_dbg=logits, force_tokens=f, temperature=temperature,
+                               greedy=greedy)
     torch.cuda.synchronize()
     return dict(tokens=np_(t), q=np_(q), lse=np_(lse), logits=None if logits is None else logits,
                 tokens_t=t, q_t=q, lse_t=lse)
 
 
-def oracle_draft(inp, wts, force=None, want_logits=False):
+def oracle_draft(inp, wts, force=None, want_logits=False, temperature=1.0, greedy=False):
     return oracle.markov_draft(np_(inp["U"]), bits(wts["W1"]), bits(wts["W2t"]), np_(inp["anchor"]),
-                               np_(inp["uniforms"]), force_tokens=force, want_logits=want_logits)
+                               np_(inp["uniforms"]), force_tokens=force, want_logits=want_logits,
+                               temperature=temperature, greedy=greedy)
 
 
 def compare_draft(g, o, counter, logits=True):

@@ -89,6 +89,26 @@ def test_argument_checks_without_gpu(lib):
     assert lib.dspark_status_string(4) == b"workspace too small"
 
 
+def test_draft_option_checks_without_gpu(lib):
+    """A temperature that is not positive and finite is refused (status 8) by the draft and the
+    verify; a greedy draft ignores the temperature, so its call goes on to the next check."""
+    dims = L.Dims(4, 3, 1000, 16, 64)
+    d, P = dims.c(), _p()
+    ws_ok = L.workspace_bytes(dims, L.OP_DRAFT)
+    vws = L.workspace_bytes(dims, L.OP_VERIFY)
+    opts = L.binding._CDraftOpts
+    for t in (0.0, -1.0, float("inf"), float("nan")):
+        o = ctypes.byref(opts(t, 0))
+        assert lib.dspark_markov_draft_opts(d, P, P, P, P, P, P, P, P, None, None, P, ws_ok, o,
+                                            None) == 8
+        assert lib.dspark_verify_opts(d, *([P] * 13), None, None, P, vws, o, None) == 8
+    g = ctypes.byref(opts(0.0, 1))
+    assert lib.dspark_markov_draft_opts(d, P, P, P, P, P, P, P, P, None, None, P, ws_ok - 1, g,
+                                        None) == 4
+    assert lib.dspark_verify_opts(d, *([P] * 13), None, None, P, vws - 1, g, None) == 4
+    assert lib.dspark_status_string(8) == b"draft temperature not positive and finite"
+
+
 def test_binding_refuses_host_tensors(lib):
     import torch
     d = L.Dims(4, 3, 1000, 16, 64)
