@@ -44,7 +44,8 @@ def _load():
             build(force=True)
         _lib = ctypes.CDLL(_LIB_PATH)
         for name in ("oracle_markov_draft", "oracle_markov_draft_opts", "oracle_confidence",
-                     "oracle_plan", "oracle_verify", "oracle_verify_opts"):
+                     "oracle_plan", "oracle_verify", "oracle_verify_opts", "oracle_rnn_draft",
+                     "oracle_rnn_verify"):
             getattr(_lib, name).restype = ctypes.c_int
     return _lib
 
@@ -172,4 +173,68 @@ def verify(target, row_offsets, draft_len, U, W1, W2t, anchor, tokens, q, unifor
                            _ptr(out["accept_margin"]), _ptr(out["emit_margin"]),
                            _ptr(out["resid_mass"]), int(threads))
     _check(rc, "oracle_verify")
+    return out
+
+
+def rnn_draft(U, W1, W2t, Wgco, h, anchor, uniforms, force_tokens=None, want_logits=False,
+              threads=0, temperature=1.0, greedy=False):
+    """RNN-head draft, eq. (6). U [B][g][V] f32; W1/W2t [V][r], Wgco [3r][2r+d] (rows W_g, W_c,
+    W_o) and h [B][g][d] as bf16 bits; anchor, uniforms, options as for markov_draft.
+    Returns dict(tokens, q, lse, margin, e[, logits]) with e [B][g][r] f64 = tanh(W_o z_k)."""
+    lib = _load()
+    U = _c(U, np.float32)
+    B, g, V = U.shape
+    W1, W2t, Wgco, h = _bits(W1), _bits(W2t), _bits(Wgco), _bits(h)
+    r = W1.shape[1]
+    d = h.shape[2]
+    assert W1.shape == (V, r) and W2t.shape == (V, r) and h.shape == (B, g, d)
+    assert Wgco.shape == (3 * r, 2 * r + d)
+    anchor = _c(anchor, np.int32)
+    uniforms = _c(uniforms, np.float32)
+    assert uniforms.shape == (B, g + 1, 3)
+    force = None if force_tokens is None else _c(force_tokens, np.int32)
+    out = dict(tokens=np.zeros((B, g), np.int32), q=np.zeros((B, g), np.float32),
+               lse=np.zeros((B, g), np.float64), margin=np.zeros((B, g), np.float64),
+               e=np.zeros((B, g, r), np.float64))
+    logits = np.zeros((B, g, V), np.float32) if want_logits else None
+    rc = lib.oracle_rnn_draft(B, g, V, r, d, _ptr(U), _ptr(W1), _ptr(W2t), _ptr(Wgco), _ptr(h),
+                              _ptr(anchor), _ptr(uniforms), _ptr(force), ctypes.c_float(temperature),
+                              int(bool(greedy)), _ptr(out["tokens"]), _ptr(out["q"]),
+                              _ptr(out["lse"]), _ptr(logits), _ptr(out["margin"]), _ptr(out["e"]),
+                              int(threads))
+    _check(rc, "oracle_rnn_draft")
+    if want_logits:
+        out["logits"] = logits
+    return out
+
+
+def rnn_verify(target, row_offsets, draft_len, U, W1, W2t, Wgco, h, anchor, tokens, q, uniforms,
+               threads=0, temperature=1.0, greedy=False):
+    """Lossless verify of an RNN-head draft (p_d recomputed from eq. (6) along the drafted
+    tokens). Arguments and result as for verify, plus Wgco and h as for rnn_draft."""
+    lib = _load()
+    U = _c(U, np.float32)
+    B, g, V = U.shape
+    W1, W2t, Wgco, h = _bits(W1), _bits(W2t), _bits(Wgco), _bits(h)
+    r = W1.shape[1]
+    d = h.shape[2]
+    assert Wgco.shape == (3 * r, 2 * r + d) and h.shape == (B, g, d)
+    target = _c(target, np.float32)
+    row_offsets = _c(row_offsets, np.int32)
+    draft_len = _c(draft_len, np.int32)
+    assert target.shape == (int(row_offsets[B]), V)
+    out = dict(accept_len=np.zeros(B, np.int32), next_token=np.zeros(B, np.int32),
+               beta_emit=np.zeros(B, np.float32), flags=np.zeros(B, np.uint32),
+               accept_margin=np.zeros((B, g), np.float64), emit_margin=np.zeros(B, np.float64),
+               resid_mass=np.zeros(B, np.float64))
+    rc = lib.oracle_rnn_verify(B, g, V, r, d, _ptr(target), _ptr(row_offsets), _ptr(draft_len),
+                               _ptr(U), _ptr(W1), _ptr(W2t), _ptr(Wgco), _ptr(h),
+                               _ptr(_c(anchor, np.int32)), _ptr(_c(tokens, np.int32)),
+                               _ptr(_c(q, np.float32)), _ptr(_c(uniforms, np.float32)),
+                               ctypes.c_float(temperature), int(bool(greedy)),
+                               _ptr(out["accept_len"]), _ptr(out["next_token"]),
+                               _ptr(out["beta_emit"]), _ptr(out["flags"]),
+                               _ptr(out["accept_margin"]), _ptr(out["emit_margin"]),
+                               _ptr(out["resid_mass"]), int(threads))
+    _check(rc, "oracle_rnn_verify")
     return out

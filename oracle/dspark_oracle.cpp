@@ -161,6 +161,55 @@ int32_t greedy_token(const std::vector<float>& L, double* gap) {
   return best;
 }
 
+// RNN head, eq. (6) ([CSDN] 4.2 "两种串行头"; [AIL] "RNN 头（可选）"; [V41] "Markov head", the
+// smaller-RNN alternative the paper tried): a recurrent state summarises the block's prefix.
+// Step k concatenates z_k = [s_{k-1}; W1[x_{k-1}]; h_k] and applies a GRU-like gated update
+//   s_k = sigma(W_g z_k) * s_{k-1} + (1 - sigma(W_g z_k)) * tanh(W_c z_k)   (elementwise),
+// and the bias of position k is B_k = W2^T tanh(W_o z_k), i.e. B_k(v) = sum_j W2[j][v] e_k[j]
+// with e_k = tanh(W_o z_k).
+// Readings (the pages fix none of these): the state has r components, the rank of W1 and W2, so
+// that e_k feeds W2 directly; s_0 = 0 at the start of every block (the state covers the prefix
+// inside the block, whose first conditioning token is the anchor); eq. (6) has no bias terms;
+// W_g, W_c and W_o are stacked by rows into one bf16 matrix Wgco [3r][2r + d] (rows 0..r-1 W_g,
+// r..2r-1 W_c, 2r..3r-1 W_o) whose columns follow z's order (state, embedding, hidden state);
+// h_k is the backbone hidden state of position k, the one the confidence head reads. All of it
+// in fp64; the bias is rounded once to fp32 and added to the fp32 U as for the Markov head.
+void rnn_update(const uint16_t* Wgco, const uint16_t* W1, const uint16_t* h_row, int r, int d,
+                int32_t x_prev, const std::vector<double>& s_prev, std::vector<double>& s_next,
+                std::vector<double>& e) {
+  const int nz = 2 * r + d;
+  std::vector<double> z(nz);
+  for (int i = 0; i < r; ++i) z[i] = s_prev[i];
+  for (int i = 0; i < r; ++i) z[r + i] = bf16_to_double(W1[static_cast<int64_t>(x_prev) * r + i]);
+  for (int i = 0; i < d; ++i) z[2 * r + i] = bf16_to_double(h_row[i]);
+  auto row_dot = [&](int row) {
+    const uint16_t* w = Wgco + static_cast<int64_t>(row) * nz;
+    double a = 0.0;
+    for (int i = 0; i < nz; ++i) a += bf16_to_double(w[i]) * z[i];
+    return a;
+  };
+  s_next.assign(r, 0.0);
+  e.assign(r, 0.0);
+  for (int j = 0; j < r; ++j) {
+    const double gate = 1.0 / (1.0 + std::exp(-row_dot(j)));
+    const double cand = std::tanh(row_dot(r + j));
+    s_next[j] = gate * s_prev[j] + (1.0 - gate) * cand;
+    e[j] = std::tanh(row_dot(2 * r + j));
+  }
+}
+
+// Draft logits of one position under the RNN head: L_v = fp32(U_v + fp32(sum_j W2[j][v] e[j])).
+void rnn_draft_logits(const float* U_row, const uint16_t* W2t, int V, int r,
+                      const std::vector<double>& e, std::vector<float>& Lr) {
+  Lr.assign(V, 0.0f);
+  for (int v = 0; v < V; ++v) {
+    const uint16_t* col = W2t + static_cast<int64_t>(v) * r;
+    double bias = 0.0;
+    for (int j = 0; j < r; ++j) bias += bf16_to_double(col[j]) * e[j];
+    Lr[v] = U_row[v] + static_cast<float>(bias);
+  }
+}
+
 double logsumexp_fp32_row(const float* row, int V) {
   double m = -std::numeric_limits<double>::infinity();
   for (int v = 0; v < V; ++v) m = std::max(m, static_cast<double>(row[v]));
@@ -473,23 +522,19 @@ int oracle_plan(int B, int gamma, const float* conf, const double* sps, int sps_
 // With draft options (as for the draft): the draft distribution p_d whose residual is drawn from
 // is softmax(beta L) at temperature tau, or, for a greedy draft, the point mass on the drafted
 // token (q = 1 in the accept test).
-int oracle_verify_opts(int B, int gamma, int V, int r, const float* target,
-                       const int32_t* row_offsets, const int32_t* draft_len, const float* U,
-                       const uint16_t* W1, const uint16_t* W2t, const int32_t* anchor,
-                       const int32_t* tokens, const float* q, const float* uniforms,
-                       float temperature, int greedy, int32_t* accept_len, int32_t* next_token,
-                       float* beta_emit, uint32_t* flags, double* accept_margin,
-                       double* emit_margin, double* resid_mass, int threads) {
-  if (B < 0 || gamma < 1 || V < 2 || r < 1) return 2;
-  if (!greedy && !(temperature > 0.0f && std::isfinite(temperature))) return 2;
-  const float beta = greedy ? 1.0f : temperature_beta(temperature);
-  for (int b = 0; b < B; ++b) {
-    if (draft_len[b] < 0 || draft_len[b] > gamma) return 2;
-    if (row_offsets[b + 1] - row_offsets[b] != draft_len[b] + 1) return 2;
-    if (anchor[b] < 0 || anchor[b] >= V) return 8;
-    for (int k = 0; k < gamma; ++k)
-      if (tokens[b * gamma + k] < 0 || tokens[b * gamma + k] >= V) return 8;
-  }
+}  // extern "C"
+
+namespace {
+
+// The verify of one batch, given the draft distribution of a rejected position: draft_pd(b, k,
+// pd) fills p_d of request b at its 1-based position k (the draft head's own definition). The
+// accept test, the residual, the bonus and the flags are those stated above.
+template <class DraftPd>
+void verify_core(int B, int gamma, int V, const float* target, const int32_t* row_offsets,
+                 const int32_t* draft_len, const int32_t* tokens, const float* q,
+                 const float* uniforms, int greedy, DraftPd draft_pd, int32_t* accept_len,
+                 int32_t* next_token, float* beta_emit, uint32_t* flags, double* accept_margin,
+                 double* emit_margin, double* resid_mass, int threads) {
   const double inf = std::numeric_limits<double>::infinity();
   parallel_for(B, threads, [&](int64_t b) {
     const int ell = draft_len[b];
@@ -536,11 +581,7 @@ int oracle_verify_opts(int B, int gamma, int V, int r, const float* target,
         pd.assign(V, 0.0);
         pd[tokens[b * gamma + k - 1]] = 1.0;
       } else {
-        const int32_t prev = (k == 1) ? anchor[b] : tokens[b * gamma + k - 2];
-        std::vector<float> L;
-        draft_logits(U + (b * gamma + k - 1) * static_cast<int64_t>(V), W1, W2t, V, r, prev, L);
-        scale_logits(L, beta);
-        softmax_fp64(L.data(), V, pd);
+        draft_pd(b, k, pd);
       }
       w.assign(V, 0.0);
       double mass = 0.0, beta = 0.0;
@@ -565,6 +606,40 @@ int oracle_verify_opts(int B, int gamma, int V, int r, const float* target,
     if (flags) flags[b] = fl;
     if (emit_margin) emit_margin[b] = mg;
   });
+}
+
+}  // namespace
+
+extern "C" {
+
+int oracle_verify_opts(int B, int gamma, int V, int r, const float* target,
+                       const int32_t* row_offsets, const int32_t* draft_len, const float* U,
+                       const uint16_t* W1, const uint16_t* W2t, const int32_t* anchor,
+                       const int32_t* tokens, const float* q, const float* uniforms,
+                       float temperature, int greedy, int32_t* accept_len, int32_t* next_token,
+                       float* beta_emit, uint32_t* flags, double* accept_margin,
+                       double* emit_margin, double* resid_mass, int threads) {
+  if (B < 0 || gamma < 1 || V < 2 || r < 1) return 2;
+  if (!greedy && !(temperature > 0.0f && std::isfinite(temperature))) return 2;
+  const float beta = greedy ? 1.0f : temperature_beta(temperature);
+  for (int b = 0; b < B; ++b) {
+    if (draft_len[b] < 0 || draft_len[b] > gamma) return 2;
+    if (row_offsets[b + 1] - row_offsets[b] != draft_len[b] + 1) return 2;
+    if (anchor[b] < 0 || anchor[b] >= V) return 8;
+    for (int k = 0; k < gamma; ++k)
+      if (tokens[b * gamma + k] < 0 || tokens[b * gamma + k] >= V) return 8;
+  }
+  // Markov head: p_d of position k from U, W1, W2 and the previous token.
+  auto markov_pd = [&](int64_t b, int k, std::vector<double>& pd) {
+    const int32_t prev = (k == 1) ? anchor[b] : tokens[b * gamma + k - 2];
+    std::vector<float> L;
+    draft_logits(U + (b * gamma + k - 1) * static_cast<int64_t>(V), W1, W2t, V, r, prev, L);
+    scale_logits(L, beta);
+    softmax_fp64(L.data(), V, pd);
+  };
+  verify_core(B, gamma, V, target, row_offsets, draft_len, tokens, q, uniforms, greedy, markov_pd,
+              accept_len, next_token, beta_emit, flags, accept_margin, emit_margin, resid_mass,
+              threads);
   return 0;
 }
 
@@ -577,6 +652,104 @@ int oracle_verify(int B, int gamma, int V, int r, const float* target, const int
   return oracle_verify_opts(B, gamma, V, r, target, row_offsets, draft_len, U, W1, W2t, anchor,
                             tokens, q, uniforms, 1.0f, 0, accept_len, next_token, beta_emit, flags,
                             accept_margin, emit_margin, resid_mass, threads);
+}
+
+// RNN-head draft, eqs. (4) and (6): per request, s_0 = 0 and x_0 = the anchor; at position k
+// the state update of eq. (6) on z_k = [s_{k-1}; W1[x_{k-1}]; h_k] gives s_k and e_k =
+// tanh(W_o z_k); L_k = fp32(U_k + fp32(W2^T e_k)); x_k is drawn as in the Markov draft (same
+// uniforms, temperature, greedy rule and forcing); the conditioning token x_k (drawn or forced)
+// feeds position k + 1. h [B][gamma][d] bf16 bits; Wgco [3r][2r + d] bf16 bits (see
+// rnn_update). Outputs as oracle_markov_draft_opts, plus e_out (nullable) [B][gamma][r] =
+// e_k in fp64.
+int oracle_rnn_draft(int B, int gamma, int V, int r, int d, const float* U, const uint16_t* W1,
+                     const uint16_t* W2t, const uint16_t* Wgco, const uint16_t* h,
+                     const int32_t* anchor, const float* uniforms, const int32_t* force_tokens,
+                     float temperature, int greedy, int32_t* tokens, float* q, double* lse,
+                     float* logits, double* margin, double* e_out, int threads) {
+  if (B < 0 || gamma < 1 || V < 2 || r < 1 || d < 0) return 2;
+  if (!greedy && !(temperature > 0.0f && std::isfinite(temperature))) return 2;
+  const float beta = greedy ? 1.0f : temperature_beta(temperature);
+  for (int b = 0; b < B; ++b) {
+    if (anchor[b] < 0 || anchor[b] >= V) return 8;
+    if (force_tokens)
+      for (int k = 0; k < gamma; ++k)
+        if (force_tokens[b * gamma + k] < 0 || force_tokens[b * gamma + k] >= V) return 8;
+  }
+  parallel_for(B, threads, [&](int64_t b) {
+    std::vector<double> state(r, 0.0), next_state, e, p;
+    std::vector<float> Lr;
+    int32_t x_prev = anchor[b];
+    for (int k = 0; k < gamma; ++k) {
+      const int64_t bk = b * gamma + k;
+      rnn_update(Wgco, W1, h + bk * static_cast<int64_t>(d), r, d, x_prev, state, next_state, e);
+      state.swap(next_state);
+      if (e_out)
+        for (int j = 0; j < r; ++j) e_out[bk * r + j] = e[j];
+      rnn_draft_logits(U + bk * V, W2t, V, r, e, Lr);
+      if (logits) std::memcpy(logits + bk * V, Lr.data(), sizeof(float) * V);
+      double mg = 0.0;
+      int32_t x, x_cond;
+      if (greedy) {
+        x = greedy_token(Lr, &mg);
+        x_cond = force_tokens ? force_tokens[bk] : x;
+        q[bk] = (x_cond == x) ? 1.0f : 0.0f;
+        lse[bk] = static_cast<double>(Lr[x]);
+      } else {
+        scale_logits(Lr, beta);
+        const double l = softmax_fp64(Lr.data(), V, p);
+        const double u = static_cast<double>(uniforms[(b * (gamma + 1) + k) * 3 + 0]);
+        x = inverse_cdf(p, u, &mg);
+        x_cond = force_tokens ? force_tokens[bk] : x;
+        q[bk] = static_cast<float>(p[x_cond]);
+        lse[bk] = l;
+      }
+      tokens[bk] = x;
+      if (margin) margin[bk] = mg;
+      x_prev = x_cond;
+    }
+  });
+  return 0;
+}
+
+// Verify of an RNN-head draft: as oracle_verify_opts, with p_d of the rejected position k
+// recomputed from eq. (6) by running the state from s_0 = 0 along the anchor and the drafted
+// tokens x_1 .. x_{k-1}.
+int oracle_rnn_verify(int B, int gamma, int V, int r, int d, const float* target,
+                      const int32_t* row_offsets, const int32_t* draft_len, const float* U,
+                      const uint16_t* W1, const uint16_t* W2t, const uint16_t* Wgco,
+                      const uint16_t* h, const int32_t* anchor, const int32_t* tokens,
+                      const float* q, const float* uniforms, float temperature, int greedy,
+                      int32_t* accept_len, int32_t* next_token, float* beta_emit, uint32_t* flags,
+                      double* accept_margin, double* emit_margin, double* resid_mass,
+                      int threads) {
+  if (B < 0 || gamma < 1 || V < 2 || r < 1 || d < 0) return 2;
+  if (!greedy && !(temperature > 0.0f && std::isfinite(temperature))) return 2;
+  const float beta = greedy ? 1.0f : temperature_beta(temperature);
+  for (int b = 0; b < B; ++b) {
+    if (draft_len[b] < 0 || draft_len[b] > gamma) return 2;
+    if (row_offsets[b + 1] - row_offsets[b] != draft_len[b] + 1) return 2;
+    if (anchor[b] < 0 || anchor[b] >= V) return 8;
+    for (int k = 0; k < gamma; ++k)
+      if (tokens[b * gamma + k] < 0 || tokens[b * gamma + k] >= V) return 8;
+  }
+  auto rnn_pd = [&](int64_t b, int k, std::vector<double>& pd) {
+    std::vector<double> state(r, 0.0), next_state, e;
+    int32_t x_prev = anchor[b];
+    for (int i = 1; i <= k; ++i) {
+      const int64_t bi = b * gamma + i - 1;
+      rnn_update(Wgco, W1, h + bi * static_cast<int64_t>(d), r, d, x_prev, state, next_state, e);
+      state.swap(next_state);
+      x_prev = tokens[bi];
+    }
+    std::vector<float> Lr;
+    rnn_draft_logits(U + (b * gamma + k - 1) * static_cast<int64_t>(V), W2t, V, r, e, Lr);
+    scale_logits(Lr, beta);
+    softmax_fp64(Lr.data(), V, pd);
+  };
+  verify_core(B, gamma, V, target, row_offsets, draft_len, tokens, q, uniforms, greedy, rnn_pd,
+              accept_len, next_token, beta_emit, flags, accept_margin, emit_margin, resid_mass,
+              threads);
+  return 0;
 }
 
 }  // extern "C"

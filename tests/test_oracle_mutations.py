@@ -12,6 +12,7 @@ import oracle
 import test_oracle_draft_options_pins as op
 import test_oracle_draft_pins as dp
 import test_oracle_plan_pins as pp
+import test_oracle_rnn_pins as rp
 import test_oracle_verify_pins as vp
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "dspark_oracle.cpp")
@@ -47,9 +48,27 @@ MUTATIONS = [
      [op.test_greedy_draft_closed_form_and_ties]),
     ("greedy residual keeps the drafted token", "pd[tokens[b * gamma + k - 1]] = 1.0;",
      "pd[0] = 1.0;", [op.test_greedy_verify_is_lossless_exact_grid]),
-    ("tempered residual left unscaled", "        scale_logits(L, beta);\n        softmax_fp64(L.data(), V, pd);",
-     "        softmax_fp64(L.data(), V, pd);",
+    ("tempered residual left unscaled", "    scale_logits(L, beta);\n    softmax_fp64(L.data(), V, pd);",
+     "    softmax_fp64(L.data(), V, pd);",
      [functools.partial(op.test_tempered_verify_is_lossless_exact_grid, 0.5)]),
+    ("rnn gate roles swapped", "s_next[j] = gate * s_prev[j] + (1.0 - gate) * cand;",
+     "s_next[j] = (1.0 - gate) * s_prev[j] + gate * cand;",
+     [functools.partial(rp.test_saturated_gates, 1.0)]),
+    ("rnn bias read from the candidate rows", "e[j] = std::tanh(row_dot(2 * r + j));",
+     "e[j] = std::tanh(row_dot(r + j));", [rp.test_output_path_is_a_tanh_embedding_chain]),
+    ("rnn draft conditions every step on the anchor", "x_prev = x_cond;", "x_prev = anchor[b];",
+     [rp.test_output_path_is_a_tanh_embedding_chain]),
+    ("rnn state not carried between draft steps",
+     "rnn_update(Wgco, W1, h + bk * static_cast<int64_t>(d), r, d, x_prev, state, next_state, e);\n      state.swap(next_state);",
+     "rnn_update(Wgco, W1, h + bk * static_cast<int64_t>(d), r, d, x_prev, state, next_state, e);",
+     [rp.test_state_path_half_gate_closed_form]),
+    ("rnn verify reruns the state along the anchor", "x_prev = tokens[bi];", "x_prev = anchor[b];",
+     [functools.partial(rp.test_verify_recomputes_the_draft_distribution_along_the_drafted_tokens,
+                        "embedding")]),
+    ("rnn hidden block read at the embedding offset",
+     "for (int i = 0; i < d; ++i) z[2 * r + i] = bf16_to_double(h_row[i]);",
+     "for (int i = 0; i < d && i < r; ++i) z[r + i] = bf16_to_double(h_row[i]);",
+     [rp.test_state_path_half_gate_closed_form]),
 ]
 
 
