@@ -7,6 +7,7 @@
  *   dspark_plan          survival-ordered greedy planner that maximises Theta = tau * SPS(B)
  *   dspark_verify        lossless rejection-sampling verify, residual resample, bonus token
  *   dspark_markov_draft_opts, dspark_verify_opts   the same with a draft temperature or greedy
+ *   dspark_rnn_draft, dspark_rnn_verify   the draft and verify with the RNN head of eq. (6)
  *
  * Sources (cited below by tag; each gives the page title and the section or equation):
  *   [V41]  blog.javazero.top, "DeepSeek-V4.1 模型结构（6）：解码，DSpark"
@@ -89,6 +90,8 @@ typedef int32_t dspark_status;
 #define DSPARK_OP_CONFIDENCE 1
 #define DSPARK_OP_PLAN 2
 #define DSPARK_OP_VERIFY 3
+#define DSPARK_OP_RNN_DRAFT 4
+#define DSPARK_OP_RNN_VERIFY 5
 
 /* Per-request verify flag bits. */
 #define DSPARK_FLAG_NONFINITE 1u     /* a verified target row has a non-finite log-sum-exp */
@@ -262,6 +265,52 @@ DSPARK_API dspark_status dspark_verify_opts(dspark_dims dims, const float* targe
                                             int32_t* next_token, float* beta_emit, uint32_t* flags,
                                             void* ws, size_t ws_bytes,
                                             const dspark_draft_opts* opts, void* stream);
+
+/*
+ * Draft with the RNN head instead of the Markov head. [CSDN] 4.2, eq. (6); [AIL] "RNN 头（可选）";
+ * [V41] "Markov head" (the paper's small-RNN alternative): a recurrent state s summarises the
+ * block's prefix. Per request s_0 = 0 and x_0 = anchor[b]; at position k (1-based)
+ *   z_k = [s_{k-1}; W1[x_{k-1}]; h_k],
+ *   s_k = sigmoid(W_g z_k) * s_{k-1} + (1 - sigmoid(W_g z_k)) * tanh(W_c z_k)   (elementwise),
+ *   e_k = tanh(W_o z_k),   B_k = W2^T e_k,   p_k = softmax(U_k + B_k),
+ * and x_k is drawn, forced and reported as in dspark_markov_draft_opts (same uniforms, options,
+ * q_tok, lse, logits_dbg). The state has r components and eq. (6) has no bias terms.
+ *   Wgco      bf16 [3r][2r + d]: rows 0..r-1 W_g, r..2r-1 W_c, 2r..3r-1 W_o; columns in z's
+ *             order: state (r), embedding (r), hidden state (d).
+ *   h         bf16 [B][gamma][d]: the backbone hidden states h_k (those of the confidence head).
+ *   e_rows    out, fp32 [B][gamma][r]: e_k = tanh(W_o z_k), the bias vectors; the verify of the
+ *             round takes them (dspark_rnn_verify).
+ * Precision: pre-activations in fp64 (the hidden block as bf16 MFMA products summed in fp32
+ * over 128 products, then in fp64); e_k rounded to fp32, and the bias contraction takes it as
+ * three bf16 terms whose sum is that fp32 value, with fp32 accumulation.
+ * Requires r <= 256 and d a positive multiple of 8 (else DSPARK_ERR_SHAPE); workspace:
+ * dspark_workspace_bytes(dims, DSPARK_OP_RNN_DRAFT). Other checks and errors as in
+ * dspark_markov_draft_opts.
+ */
+DSPARK_API dspark_status dspark_rnn_draft(dspark_dims dims, const float* U, const uint16_t* W1,
+                                          const uint16_t* W2t, const uint16_t* Wgco,
+                                          const uint16_t* h, const int32_t* anchor,
+                                          const float* uniforms, int32_t* tokens, float* q_tok,
+                                          double* lse, float* e_rows, float* logits_dbg,
+                                          const int32_t* force_tokens, void* ws, size_t ws_bytes,
+                                          const dspark_draft_opts* opts, void* stream);
+
+/*
+ * Verify of an RNN-head draft: as dspark_verify_opts, with the draft distribution of a rejected
+ * position j recomputed from the draft's bias vector e_j (e_rows, fp32 [B][gamma][r], as
+ * dspark_rnn_draft wrote it, taken as the same three bf16 terms): p_d = softmax(beta (U_j + W2^T
+ * e_j)). No embedding table or anchor is needed. Requires r <= 256 and d as for the draft;
+ * workspace: dspark_workspace_bytes(dims, DSPARK_OP_RNN_VERIFY).
+ */
+DSPARK_API dspark_status dspark_rnn_verify(dspark_dims dims, const float* target,
+                                           const int32_t* row_offsets, const int32_t* draft_len,
+                                           const float* U, const uint16_t* W2t,
+                                           const float* e_rows, const int32_t* tokens,
+                                           const float* q_tok, const double* lse,
+                                           const float* uniforms, int32_t* accept_len,
+                                           int32_t* next_token, float* beta_emit, uint32_t* flags,
+                                           void* ws, size_t ws_bytes,
+                                           const dspark_draft_opts* opts, void* stream);
 
 /*
  * Kernel timing with HIP events (measurement support; not part of the method).

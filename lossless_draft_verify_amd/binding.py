@@ -16,13 +16,14 @@ import torch
 
 __all__ = [
     "Dims", "DsparkError", "FULL_VERIFY", "EARLY_STOP", "FULL_PATH", "LAGGED_TOPK",
-    "OP_DRAFT", "OP_CONFIDENCE", "OP_PLAN", "OP_VERIFY", "FLAG_NONFINITE", "FLAG_ZERO_RESIDUAL",
-    "library_path", "load_library", "workspace_bytes", "workspace", "markov_draft", "confidence",
-    "plan", "verify", "profile_begin", "profile_end", "version",
+    "OP_DRAFT", "OP_CONFIDENCE", "OP_PLAN", "OP_VERIFY", "OP_RNN_DRAFT", "OP_RNN_VERIFY",
+    "FLAG_NONFINITE", "FLAG_ZERO_RESIDUAL", "library_path", "load_library", "workspace_bytes",
+    "workspace", "markov_draft", "confidence", "plan", "verify", "rnn_draft", "rnn_verify",
+    "profile_begin", "profile_end", "version",
 ]
 
 FULL_VERIFY, EARLY_STOP, FULL_PATH, LAGGED_TOPK = 0, 1, 2, 3
-OP_DRAFT, OP_CONFIDENCE, OP_PLAN, OP_VERIFY = 0, 1, 2, 3
+OP_DRAFT, OP_CONFIDENCE, OP_PLAN, OP_VERIFY, OP_RNN_DRAFT, OP_RNN_VERIFY = 0, 1, 2, 3, 4, 5
 FLAG_NONFINITE, FLAG_ZERO_RESIDUAL = 1, 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -96,6 +97,10 @@ def load_library():
         lib.dspark_verify.argtypes = [_CDims] + [_P] * 15 + [_P, ctypes.c_size_t, _P]
         lib.dspark_verify_opts.restype = ctypes.c_int32
         lib.dspark_verify_opts.argtypes = [_CDims] + [_P] * 15 + [_P, ctypes.c_size_t, _P, _P]
+        lib.dspark_rnn_draft.restype = ctypes.c_int32
+        lib.dspark_rnn_draft.argtypes = [_CDims] + [_P] * 13 + [_P, ctypes.c_size_t, _P, _P]
+        lib.dspark_rnn_verify.restype = ctypes.c_int32
+        lib.dspark_rnn_verify.argtypes = [_CDims] + [_P] * 14 + [_P, ctypes.c_size_t, _P, _P]
         lib.dspark_profile_begin.restype = ctypes.c_int32
         lib.dspark_profile_begin.argtypes = [ctypes.c_int32]
         lib.dspark_profile_end.restype = ctypes.c_int32
@@ -251,3 +256,61 @@ def profile_end():
     if k < 0:
         raise DsparkError("dspark_profile_end failed")
     return {names[i].decode(): (counts[i], ms[i]) for i in range(k)}
+
+
+def rnn_draft(dims: Dims, U, W1, W2t, Wgco, h, anchor, uniforms, *, tokens=None, q=None, lse=None,
+              e_rows=None, logits_dbg=None, force_tokens=None, ws=None, temperature: float = 1.0,
+              greedy: bool = False, stream=None):
+    """Draft with the RNN head (dspark_rnn_draft). Wgco [3r][2r+d] bf16 (rows W_g, W_c, W_o),
+    h [B][gamma][d] bf16. Returns (tokens, q, lse, e_rows) with e_rows [B][gamma][r] fp32."""
+    B, g, V, r, d = dims.B, dims.gamma, dims.V, dims.r, dims.d
+    dev = U.device
+    tokens = tokens if tokens is not None else torch.empty((B, g), dtype=torch.int32, device=dev)
+    q = q if q is not None else torch.empty((B, g), dtype=torch.float32, device=dev)
+    lse = lse if lse is not None else torch.empty((B, g), dtype=torch.float64, device=dev)
+    e_rows = e_rows if e_rows is not None else torch.empty((B, g, r), dtype=torch.float32, device=dev)
+    ws = ws if ws is not None else workspace(dims, OP_RNN_DRAFT, dev)
+    st = load_library().dspark_rnn_draft(
+        dims.c(), _ptr(U, torch.float32, (B, g, V), "U"), _ptr(W1, torch.bfloat16, (V, r), "W1"),
+        _ptr(W2t, torch.bfloat16, (V, r), "W2t"),
+        _ptr(Wgco, torch.bfloat16, (3 * r, 2 * r + d), "Wgco"),
+        _ptr(h, torch.bfloat16, (B, g, d), "h"), _ptr(anchor, torch.int32, (B,), "anchor"),
+        _ptr(uniforms, torch.float32, (B, g + 1, 3), "uniforms"),
+        _ptr(tokens, torch.int32, (B, g), "tokens"), _ptr(q, torch.float32, (B, g), "q"),
+        _ptr(lse, torch.float64, (B, g), "lse"), _ptr(e_rows, torch.float32, (B, g, r), "e_rows"),
+        _ptr(logits_dbg, torch.float32, (B, g, V), "logits_dbg"),
+        _ptr(force_tokens, torch.int32, (B, g), "force_tokens"), _ptr(ws, torch.uint8, None, "ws"),
+        ws.numel(), _opts(temperature, greedy), _stream(stream))
+    _check(st, "dspark_rnn_draft")
+    return tokens, q, lse, e_rows
+
+
+def rnn_verify(dims: Dims, target, row_offsets, draft_len, U, W2t, e_rows, tokens, q, lse,
+               uniforms, *, accept_len=None, next_token=None, beta_emit=None, flags=None, ws=None,
+               temperature: float = 1.0, greedy: bool = False, stream=None):
+    """Lossless verify of an RNN-head draft (dspark_rnn_verify): the draft distribution of a
+    rejected position comes from its bias vector e_rows[b][j]. Returns (accept_len, next_token,
+    beta_emit, flags)."""
+    B, g, V, r = dims.B, dims.gamma, dims.V, dims.r
+    dev = U.device
+    if target.dim() != 2 or target.shape[1] != V:
+        raise ValueError("target must be [rows][V]")
+    accept_len = accept_len if accept_len is not None else torch.empty(B, dtype=torch.int32, device=dev)
+    next_token = next_token if next_token is not None else torch.empty(B, dtype=torch.int32, device=dev)
+    beta_emit = beta_emit if beta_emit is not None else torch.empty(B, dtype=torch.float32, device=dev)
+    flags = flags if flags is not None else torch.empty(B, dtype=torch.int32, device=dev)
+    ws = ws if ws is not None else workspace(dims, OP_RNN_VERIFY, dev)
+    st = load_library().dspark_rnn_verify(
+        dims.c(), _ptr(target, torch.float32, None, "target"),
+        _ptr(row_offsets, torch.int32, (B + 1,), "row_offsets"),
+        _ptr(draft_len, torch.int32, (B,), "draft_len"), _ptr(U, torch.float32, (B, g, V), "U"),
+        _ptr(W2t, torch.bfloat16, (V, r), "W2t"), _ptr(e_rows, torch.float32, (B, g, r), "e_rows"),
+        _ptr(tokens, torch.int32, (B, g), "tokens"), _ptr(q, torch.float32, (B, g), "q"),
+        _ptr(lse, torch.float64, (B, g), "lse"),
+        _ptr(uniforms, torch.float32, (B, g + 1, 3), "uniforms"),
+        _ptr(accept_len, torch.int32, (B,), "accept_len"),
+        _ptr(next_token, torch.int32, (B,), "next_token"),
+        _ptr(beta_emit, torch.float32, (B,), "beta_emit"), _ptr(flags, torch.int32, (B,), "flags"),
+        _ptr(ws, torch.uint8, None, "ws"), ws.numel(), _opts(temperature, greedy), _stream(stream))
+    _check(st, "dspark_rnn_verify")
+    return accept_len, next_token, beta_emit, flags

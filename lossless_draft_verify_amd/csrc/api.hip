@@ -10,6 +10,7 @@
 #include "dspark.h"
 #include "device.h"
 #include "launch.h"
+#include "tiles.h"
 
 namespace {
 
@@ -80,6 +81,36 @@ size_t draft_ws(const dspark_dims& d, void* base, DraftWs* out) {
   return align_up(n * sizeof(float2));
 }
 
+// RNN-head draft: the step partials, then P [2][B gamma][3r] fp64 (split-K parts of the hidden
+// block), the state ping-pong [2][B][r] fp64 and the bias rows E [B gamma][3r] bf16.
+struct RnnDraftWs {
+  DraftWs draft;
+  double* P;
+  double* s[2];
+  uint16_t* E;
+};
+size_t rnn_draft_ws(const dspark_dims& d, void* base, RnnDraftWs* out) {
+  const size_t M = static_cast<size_t>(d.B) * d.gamma;
+  char* b = static_cast<char*>(base);
+  size_t off = draft_ws(d, base, out ? &out->draft : nullptr);
+  auto take = [&](size_t bytes) {
+    char* p = b ? b + off : nullptr;
+    off += align_up(bytes);
+    return p;
+  };
+  char* P = take(2 * M * 3 * d.r * sizeof(double));
+  char* s0 = take(static_cast<size_t>(d.B) * d.r * sizeof(double));
+  char* s1 = take(static_cast<size_t>(d.B) * d.r * sizeof(double));
+  char* E = take(M * kRnnTerms * d.r * sizeof(uint16_t));
+  if (out) {
+    out->P = reinterpret_cast<double*>(P);
+    out->s[0] = reinterpret_cast<double*>(s0);
+    out->s[1] = reinterpret_cast<double*>(s1);
+    out->E = reinterpret_cast<uint16_t*>(E);
+  }
+  return off;
+}
+
 size_t verify_ws(const dspark_dims& d, void* base, VerifyWs* out) {
   const size_t rows = static_cast<size_t>(d.B) * (d.gamma + 1);
   const size_t nseg = nseg_of(d.V), nt = ntiles_of(d.V), B = d.B;
@@ -106,6 +137,17 @@ size_t verify_ws(const dspark_dims& d, void* base, VerifyWs* out) {
   return off;
 }
 
+// Verify of an RNN-head draft: the verify workspace, then the bias rows E [B gamma][3r] bf16.
+size_t rnn_verify_ws(const dspark_dims& d, void* base, VerifyWs* out, uint16_t** E) {
+  const size_t off = verify_ws(d, base, out);
+  if (E) *E = reinterpret_cast<uint16_t*>(static_cast<char*>(base) + off);
+  return off + align_up(static_cast<size_t>(d.B) * d.gamma * kRnnTerms * d.r * sizeof(uint16_t));
+}
+
+// The RNN head needs the hidden states (d a positive multiple of 8) and r <= 256 (the three
+// bf16 terms of a bias row fill at most two 1 KB copies of one wave).
+bool rnn_dims_ok(const dspark_dims& d) { return dims_ok(d) && d.r <= 256 && d.d >= 8 && d.d % 8 == 0; }
+
 // ---- kernel timing ----------------------------------------------------------------------------
 enum KernelId {
   kMarkovStep = 0,
@@ -116,11 +158,15 @@ enum KernelId {
   kAccept,
   kResidualPartials,
   kEmitSample,
+  kRnnPre,
+  kRnnState,
+  kSplitBias,
   kNumKernels
 };
 const char* const kKernelNames[kNumKernels] = {"markov_step",  "draft_sample", "confidence",
                                                "plan",         "target_stats", "accept",
-                                               "residual_partials", "emit_sample"};
+                                               "residual_partials", "emit_sample",
+                                               "rnn_pre",      "rnn_state",    "split_bias"};
 
 struct Profiler {
   bool armed = false;
@@ -142,6 +188,71 @@ hipError_t timed(KernelId id, hipStream_t s, F launch) {
     ++g_prof.used;
   }
   return e;
+}
+
+// The serial draft loop shared by the two heads: per position the bias step (bias rows from
+// W1[prev], or from E after the RNN state step) and the sampler.
+struct RnnDraftInputs {
+  const uint16_t* Wgco;
+  const uint16_t* h;
+  float* e_rows;
+  RnnDraftWs w;
+};
+
+dspark_status draft_loop(const dspark_dims& dims, const float* U, const uint16_t* W1,
+                         const uint16_t* W2t, const int32_t* anchor, const float* uniforms,
+                         int32_t* tokens, float* q_tok, double* lse, float* logits_dbg,
+                         const int32_t* force_tokens, float2* part, float beta, int greedy,
+                         const RnnDraftInputs* rnn, hipStream_t s) {
+  const int nt = ntiles_of(dims.V);
+  const int cus = compute_units();
+  if (rnn) {
+    RnnPreArgs pa{dims.B * dims.gamma, dims.r, dims.d, rnn->h, rnn->Wgco, rnn->w.P};
+    if (timed(kRnnPre, s, [&] { return launch_rnn_pre(pa, s); }) != hipSuccess)
+      return DSPARK_ERR_HIP;
+  }
+  for (int k = 0; k < dims.gamma; ++k) {
+    const int32_t* prev = anchor;
+    int stride = 1;
+    if (k > 0) {
+      prev = (force_tokens ? force_tokens : tokens) + (k - 1);
+      stride = dims.gamma;
+    }
+    if (rnn) {
+      RnnStateArgs ra{dims.B,        dims.gamma,       k,          dims.r,
+                      dims.d,        rnn->w.P,         rnn->Wgco,  W1,
+                      prev,          stride,           k > 0 ? rnn->w.s[(k + 1) & 1] : nullptr,
+                      rnn->w.s[k & 1], rnn->e_rows,    rnn->w.E};
+      if (timed(kRnnState, s, [&] { return launch_rnn_state(ra, s); }) != hipSuccess)
+        return DSPARK_ERR_HIP;
+    }
+    StepArgs sa{dims.B, dims.V, dims.gamma, k, nt, U, W1, W2t, prev, stride, part, logits_dbg,
+                cus, beta};
+    SampleArgs pa{dims.B, dims.V, dims.gamma, k, nt, U, W1, W2t, prev, stride, part,
+                  uniforms, force_tokens, tokens, q_tok, lse, beta, greedy};
+    if (rnn) {
+      sa.e_terms = pa.e_terms = kRnnTerms;
+      sa.E = pa.E = rnn->w.E;
+    }
+    if (timed(kMarkovStep, s, [&] { return launch_markov_step(sa, dims.r, s); }) != hipSuccess)
+      return DSPARK_ERR_HIP;
+    if (timed(kDraftSample, s, [&] { return launch_draft_sample(pa, dims.r, s); }) != hipSuccess)
+      return DSPARK_ERR_HIP;
+  }
+  return DSPARK_OK;
+}
+
+// The four verify passes, shared by the two heads (bias rows from W1[prev], or E).
+dspark_status verify_passes(const dspark_dims& dims, VerifyArgs& a, hipStream_t s) {
+  if (timed(kTargetStats, s, [&] { return launch_target_stats(a, s); }) != hipSuccess)
+    return DSPARK_ERR_HIP;
+  if (timed(kAccept, s, [&] { return launch_accept(a, s); }) != hipSuccess) return DSPARK_ERR_HIP;
+  if (timed(kResidualPartials, s, [&] { return launch_residual_partials(a, s); }) != hipSuccess)
+    return DSPARK_ERR_HIP;
+  if (timed(kEmitSample, s, [&] { return launch_emit_sample(a, s); }) != hipSuccess)
+    return DSPARK_ERR_HIP;
+  (void)dims;
+  return DSPARK_OK;
 }
 
 }  // namespace
@@ -172,6 +283,11 @@ size_t dspark_workspace_bytes(dspark_dims dims, int32_t op) {
     case DSPARK_OP_CONFIDENCE: return 0;
     case DSPARK_OP_PLAN: return 0;
     case DSPARK_OP_VERIFY: return verify_ws(dims, nullptr, nullptr);
+    case DSPARK_OP_RNN_DRAFT:
+      return rnn_dims_ok(dims) ? rnn_draft_ws(dims, nullptr, nullptr) : static_cast<size_t>(-1);
+    case DSPARK_OP_RNN_VERIFY:
+      return rnn_dims_ok(dims) ? rnn_verify_ws(dims, nullptr, nullptr, nullptr)
+                               : static_cast<size_t>(-1);
     default: return static_cast<size_t>(-1);
   }
 }
@@ -196,26 +312,35 @@ dspark_status dspark_markov_draft_opts(dspark_dims dims, const float* U, const u
   if (ws_bytes < draft_ws(dims, nullptr, nullptr)) return DSPARK_ERR_WORKSPACE;
   DraftWs w;
   draft_ws(dims, ws, &w);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const int nt = ntiles_of(dims.V);
-  const int cus = compute_units();
-  for (int k = 0; k < dims.gamma; ++k) {
-    const int32_t* prev = anchor;
-    int stride = 1;
-    if (k > 0) {
-      prev = (force_tokens ? force_tokens : tokens) + (k - 1);
-      stride = dims.gamma;
-    }
-    StepArgs sa{dims.B, dims.V, dims.gamma, k, nt, U, W1, W2t, prev, stride, w.part, logits_dbg,
-                cus, beta};
-    if (timed(kMarkovStep, s, [&] { return launch_markov_step(sa, dims.r, s); }) != hipSuccess)
-      return DSPARK_ERR_HIP;
-    SampleArgs pa{dims.B, dims.V, dims.gamma, k, nt, U, W1, W2t, prev, stride, w.part,
-                  uniforms, force_tokens, tokens, q_tok, lse, beta, greedy};
-    if (timed(kDraftSample, s, [&] { return launch_draft_sample(pa, dims.r, s); }) != hipSuccess)
-      return DSPARK_ERR_HIP;
-  }
-  return DSPARK_OK;
+  return draft_loop(dims, U, W1, W2t, anchor, uniforms, tokens, q_tok, lse, logits_dbg,
+                    force_tokens, w.part, beta, greedy, nullptr, static_cast<hipStream_t>(stream));
+}
+
+dspark_status dspark_rnn_draft(dspark_dims dims, const float* U, const uint16_t* W1,
+                               const uint16_t* W2t, const uint16_t* Wgco, const uint16_t* h,
+                               const int32_t* anchor, const float* uniforms, int32_t* tokens,
+                               float* q_tok, double* lse, float* e_rows, float* logits_dbg,
+                               const int32_t* force_tokens, void* ws, size_t ws_bytes,
+                               const dspark_draft_opts* opts, void* stream) {
+  if (!U || !W1 || !W2t || !Wgco || !h || !anchor || !uniforms || !tokens || !q_tok || !lse ||
+      !e_rows || !ws)
+    return DSPARK_ERR_NULL;
+  float beta = 1.0f;
+  int greedy = 0;
+  if (!draft_options(opts, &beta, &greedy)) return DSPARK_ERR_OPTS;
+  if (!rnn_dims_ok(dims)) return DSPARK_ERR_SHAPE;
+  if (!aligned(U, 16) || !aligned(W1, 16) || !aligned(W2t, 16) || !aligned(Wgco, 16) ||
+      !aligned(h, 16) || !aligned(anchor, 4) || !aligned(uniforms, 4) || !aligned(tokens, 4) ||
+      !aligned(q_tok, 4) || !aligned(lse, 8) || !aligned(e_rows, 4) ||
+      (logits_dbg && !aligned(logits_dbg, 4)) || (force_tokens && !aligned(force_tokens, 4)) ||
+      !aligned(ws, kAlign))
+    return DSPARK_ERR_ALIGN;
+  if (ws_bytes < rnn_draft_ws(dims, nullptr, nullptr)) return DSPARK_ERR_WORKSPACE;
+  RnnDraftInputs rnn{Wgco, h, e_rows, {}};
+  rnn_draft_ws(dims, ws, &rnn.w);
+  return draft_loop(dims, U, W1, W2t, anchor, uniforms, tokens, q_tok, lse, logits_dbg,
+                    force_tokens, rnn.w.draft.part, beta, greedy, &rnn,
+                    static_cast<hipStream_t>(stream));
 }
 
 dspark_status dspark_markov_draft(dspark_dims dims, const float* U, const uint16_t* W1,
@@ -309,15 +434,63 @@ dspark_status dspark_verify_opts(dspark_dims dims, const float* target,
   a.beta = beta;
   a.greedy = greedy;
   verify_ws(dims, ws, &a.ws);
+  return verify_passes(dims, a, static_cast<hipStream_t>(stream));
+}
+
+dspark_status dspark_rnn_verify(dspark_dims dims, const float* target, const int32_t* row_offsets,
+                                const int32_t* draft_len, const float* U, const uint16_t* W2t,
+                                const float* e_rows, const int32_t* tokens, const float* q_tok,
+                                const double* lse, const float* uniforms, int32_t* accept_len,
+                                int32_t* next_token, float* beta_emit, uint32_t* flags, void* ws,
+                                size_t ws_bytes, const dspark_draft_opts* opts, void* stream) {
+  if (!target || !row_offsets || !draft_len || !U || !W2t || !e_rows || !tokens || !q_tok ||
+      !lse || !uniforms || !accept_len || !next_token || !ws)
+    return DSPARK_ERR_NULL;
+  float beta = 1.0f;
+  int greedy = 0;
+  if (!draft_options(opts, &beta, &greedy)) return DSPARK_ERR_OPTS;
+  if (!rnn_dims_ok(dims)) return DSPARK_ERR_SHAPE;
+  if (!aligned(target, 16) || !aligned(U, 16) || !aligned(W2t, 16) || !aligned(e_rows, 4) ||
+      !aligned(row_offsets, 4) || !aligned(draft_len, 4) || !aligned(tokens, 4) ||
+      !aligned(q_tok, 4) || !aligned(lse, 8) || !aligned(uniforms, 4) ||
+      !aligned(accept_len, 4) || !aligned(next_token, 4) || (beta_emit && !aligned(beta_emit, 4)) ||
+      (flags && !aligned(flags, 4)) || !aligned(ws, kAlign))
+    return DSPARK_ERR_ALIGN;
+  if (ws_bytes < rnn_verify_ws(dims, nullptr, nullptr, nullptr)) return DSPARK_ERR_WORKSPACE;
+  VerifyArgs a;
+  a.B = dims.B;
+  a.V = dims.V;
+  a.gamma = dims.gamma;
+  a.r = dims.r;
+  a.ntiles = ntiles_of(dims.V);
+  a.nseg = nseg_of(dims.V);
+  a.target = target;
+  a.row_offsets = row_offsets;
+  a.draft_len = draft_len;
+  a.U = U;
+  a.W1 = nullptr;
+  a.W2t = W2t;
+  a.anchor = nullptr;
+  a.tokens = tokens;
+  a.q = q_tok;
+  a.lse = lse;
+  a.uniforms = uniforms;
+  a.accept_len = accept_len;
+  a.next_token = next_token;
+  a.beta_emit = beta_emit;
+  a.flags = flags;
+  a.persistent_wgs = compute_units();
+  a.beta = beta;
+  a.greedy = greedy;
+  uint16_t* E = nullptr;
+  rnn_verify_ws(dims, ws, &a.ws, &E);
+  a.e_terms = kRnnTerms;
+  a.E = E;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (timed(kTargetStats, s, [&] { return launch_target_stats(a, s); }) != hipSuccess)
+  SplitArgs sp{dims.B * dims.gamma, dims.r, e_rows, E};
+  if (timed(kSplitBias, s, [&] { return launch_split_bias(sp, s); }) != hipSuccess)
     return DSPARK_ERR_HIP;
-  if (timed(kAccept, s, [&] { return launch_accept(a, s); }) != hipSuccess) return DSPARK_ERR_HIP;
-  if (timed(kResidualPartials, s, [&] { return launch_residual_partials(a, s); }) != hipSuccess)
-    return DSPARK_ERR_HIP;
-  if (timed(kEmitSample, s, [&] { return launch_emit_sample(a, s); }) != hipSuccess)
-    return DSPARK_ERR_HIP;
-  return DSPARK_OK;
+  return verify_passes(dims, a, s);
 }
 
 dspark_status dspark_verify(dspark_dims dims, const float* target, const int32_t* row_offsets,

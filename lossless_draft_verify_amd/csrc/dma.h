@@ -33,6 +33,17 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void*)p));
 }
 
+// Copy a row of N 16-byte pieces from global memory to LDS (bytes lds .. lds + 16 N) with the
+// lanes of one wave: lane l copies piece l, and piece 64 + l when N > 64.
+template <int N>
+__device__ __forceinline__ void copy_row_to_lds(const uint16_t* src, uint32_t lds, int lane) {
+  static_assert(N <= 128, "at most two copies per lane");
+  if (lane < N) copy16_to_lds(src + 8 * lane, lds);
+  if constexpr (N > 64) {
+    if (lane < N - 64) copy16_to_lds(src + 8 * (64 + lane), lds + 1024);
+  }
+}
+
 template <int N>
 __device__ __forceinline__ void wait_copies() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");

@@ -34,16 +34,16 @@ namespace {
 // those loads in flight.
 constexpr int kStepThreads = 512;
 
-template <int KS, bool VEC4>
+template <int KS, bool VEC4, int NT>
 struct StepKernel {
-  using C = StepCfg<KS>;
-  static constexpr int r = C::kR;
+  using C = StepCfg<KS * NT>;                         // LDS rows hold NT r bf16 (the bias row)
+  static constexpr int r = 16 * KS;                   // rank: W2 columns
   static constexpr int BG = C::kBG;                   // requests per group (128, or 64 for r=512)
   static constexpr int kNTW = BG / 64;                // 32-request MFMA tiles per wave
   static constexpr int kTok = 4 * kTileTokens;        // tokens per item
   static constexpr int kUrow = kTok + 4;              // padded LDS row of the staged U block
   static constexpr int kURows = BG / 16;              // U rows per thread (32 threads per row)
-  static constexpr int kPR = r / 8;                   // 16-byte pieces per embedding row
+  static constexpr int kPR = NT * r / 8;              // 16-byte pieces per bias row
   static constexpr int kEPieces = (BG * kPR + kStepThreads - 1) / kStepThreads;
 
   const StepArgs& p;
@@ -83,7 +83,7 @@ struct StepKernel {
     load_w2_tile<KS>(a, p.W2t, (it / ngroups) * kTok + ts * kTileTokens + col, p.V, half);
   }
 
-  // Embedding rows of one request group into LDS: ids first, then rows.
+  // Bias rows of one request group into LDS (Markov: token ids first, then rows).
   __device__ void load_embeddings(int group) const {
     // piece c = i * kStepThreads + tid covers row c / kPR, bytes 16 (c % kPR); pieces past the
     // group (c >= BG * kPR) are clamped to the last one and not stored.
@@ -92,13 +92,14 @@ struct StepKernel {
     for (int i = 0; i < kEPieces; ++i) {
       const int c = min(i * kStepThreads + tid, BG * kPR - 1);
       const int b = min(group * BG + c / kPR, p.B - 1);
-      ids[i] = p.prev[static_cast<size_t>(b) * p.prev_stride];
+      ids[i] = (NT == 1) ? p.prev[static_cast<size_t>(b) * p.prev_stride] : b;
     }
     u16x8_t e[kEPieces];
 #pragma unroll
     for (int i = 0; i < kEPieces; ++i) {
       const int c = min(i * kStepThreads + tid, BG * kPR - 1);
-      e[i] = load_u16x8(p.W1 + static_cast<size_t>(ids[i]) * r + (c % kPR) * 8);
+      const int64_t pos = static_cast<int64_t>(ids[i]) * p.gamma + p.k;
+      e[i] = load_u16x8(bias_row<NT>(p.W1, p.E, r, ids[i], pos) + (c % kPR) * 8);
     }
 #pragma unroll
     for (int i = 0; i < kEPieces; ++i) {
@@ -124,16 +125,16 @@ struct StepKernel {
       e0[nt] = load_u16x8(&E[((bh * kNTW + nt) * 32 + col) * C::kLdsRow + 8 * half]);
     }
 #pragma unroll
-    for (int s2 = 0; s2 < KS; ++s2) {
+    for (int s2 = 0; s2 < NT * KS; ++s2) {
       u16x8_t (&cur)[kNTW] = (s2 & 1) ? e1 : e0;
       u16x8_t (&nxt)[kNTW] = (s2 & 1) ? e0 : e1;
-      if (s2 + 1 < KS) {
+      if (s2 + 1 < NT * KS) {
 #pragma unroll
         for (int nt = 0; nt < kNTW; ++nt)
           nxt[nt] = load_u16x8(&E[((bh * kNTW + nt) * 32 + col) * C::kLdsRow + 8 * half + 16 * (s2 + 1)]);
       }
 #pragma unroll
-      for (int nt = 0; nt < kNTW; ++nt) acc[nt] = mfma_32x32x16(a[s2], cur[nt], acc[nt]);
+      for (int nt = 0; nt < kNTW; ++nt) acc[nt] = mfma_32x32x16(a[s2 % KS], cur[nt], acc[nt]);
     }
   }
 
@@ -197,9 +198,9 @@ struct StepKernel {
   }
 };
 
-template <int KS, bool VEC4>
+template <int KS, bool VEC4, int NT>
 __global__ __launch_bounds__(kStepThreads, 1) void markov_step_kernel(StepArgs p) {
-  using K = StepKernel<KS, VEC4>;
+  using K = StepKernel<KS, VEC4, NT>;
   __shared__ __attribute__((aligned(16))) uint16_t E[K::BG * K::C::kLdsRow];
   __shared__ __attribute__((aligned(16))) float Us[K::BG * K::kUrow];
   const K k(p, E, Us);
@@ -275,7 +276,7 @@ struct DmaStep {
   static_assert((kStages - 1) * kCopies <= 63, "vmcnt range");
 };
 
-template <int KS>
+template <int KS, int NT>
 __global__ __launch_bounds__(kDmaThreads, 1) void markov_step_dma_kernel(StepArgs p) {
   using D = DmaStep<KS>;
   __shared__ __attribute__((aligned(1024))) unsigned char stage[D::kStages * D::kStageBytes];
@@ -354,38 +355,50 @@ __global__ __launch_bounds__(kDmaThreads, 1) void markov_step_dma_kernel(StepArg
     }
   };
 
-  // Prologue, all copies: the group's previous tokens into LDS; then the embedding rows
-  // W1[prev] (each row once per workgroup, swizzled like W2t) into stage 1, with item 0 behind
-  // them into stage 0; each wave reads its rows into registers and releases stage 1.
-  if (wave < kDmaGroup / 64) {
-    const int b = min(group * kDmaGroup + 64 * wave + lane, p.B - 1);
-    copy4_to_lds(p.prev + static_cast<size_t>(b) * p.prev_stride, lds_addr(pid) + 256 * wave);
-  }
-  wait_copies<0>();
-  asm volatile("s_barrier" ::: "memory");
-  {
-    const uint32_t ebase = stage_addr + D::kStageBytes;
-#pragma unroll
-    for (int i = 0; i < D::kECopies; ++i) {
-      const int q = wave * D::kECopies + i;
-      const int slot = 64 * q + lane;
-      const int row = slot / D::kW2Chunks;
-      const int c = (slot % D::kW2Chunks) ^ (row & D::kW2Swz);
-      copy16_to_lds(p.W1 + static_cast<size_t>(pid[row]) * D::r + 8 * c, ebase + 1024 * q);
+  // Prologue. Markov head, all copies: the group's previous tokens into LDS; then the
+  // embedding rows W1[prev] (each row once per workgroup, swizzled like W2t) into stage 1, with
+  // item 0 behind them into stage 0; each wave reads its rows into registers and releases
+  // stage 1. RNN head: each lane loads its request's bias row (both terms) straight into
+  // registers, and those loads are drained before the copy pipeline starts.
+  u16x8_t e[NT * KS];
+  if constexpr (NT == 1) {
+    if (wave < kDmaGroup / 64) {
+      const int b = min(group * kDmaGroup + 64 * wave + lane, p.B - 1);
+      copy4_to_lds(p.prev + static_cast<size_t>(b) * p.prev_stride, lds_addr(pid) + 256 * wave);
     }
-  }
-  issue(0);
-  wait_copies<D::kCopies>();                  // the embedding rows (item 0 may be in flight)
-  asm volatile("s_barrier" ::: "memory");
-  u16x8_t e[KS];
-  {
-    const unsigned char* eb = stage + D::kStageBytes;
+    wait_copies<0>();
+    asm volatile("s_barrier" ::: "memory");
+    {
+      const uint32_t ebase = stage_addr + D::kStageBytes;
 #pragma unroll
-    for (int s = 0; s < KS; ++s)
-      e[s] = *reinterpret_cast<const u16x8_t*>(
-          eb + 16 * (row_own * D::kW2Chunks + ((2 * s + half) ^ (row_own & D::kW2Swz))));
+      for (int i = 0; i < D::kECopies; ++i) {
+        const int q = wave * D::kECopies + i;
+        const int slot = 64 * q + lane;
+        const int row = slot / D::kW2Chunks;
+        const int c = (slot % D::kW2Chunks) ^ (row & D::kW2Swz);
+        copy16_to_lds(p.W1 + static_cast<size_t>(pid[row]) * D::r + 8 * c, ebase + 1024 * q);
+      }
+    }
+    issue(0);
+    wait_copies<D::kCopies>();                  // the embedding rows (item 0 may be in flight)
+    asm volatile("s_barrier" ::: "memory");
+    {
+      const unsigned char* eb = stage + D::kStageBytes;
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        e[s] = *reinterpret_cast<const u16x8_t*>(
+            eb + 16 * (row_own * D::kW2Chunks + ((2 * s + half) ^ (row_own & D::kW2Swz))));
+    }
+    lds_barrier();                              // stage 1 is free for item 1
+  } else {
+    const int b = min(group * kDmaGroup + row_own, p.B - 1);
+    const uint16_t* erow =
+        bias_row<NT>(p.W1, p.E, D::r, 0, static_cast<int64_t>(b) * p.gamma + p.k) + 8 * half;
+#pragma unroll
+    for (int s = 0; s < NT * KS; ++s) e[s] = load_u16x8(erow + 16 * s);
+    __builtin_amdgcn_s_waitcnt(0);
+    issue(0);
   }
-  lds_barrier();                              // stage 1 is free for item 1
   int flushed = 0;
   for (int j = 0; j < n; ++j) {
     if (j + 1 < n) {
@@ -408,7 +421,7 @@ __global__ __launch_bounds__(kDmaThreads, 1) void markov_step_dma_kernel(StepArg
       for (int g = 0; g < 4; ++g) uu[g] = *reinterpret_cast<const float4*>(base + u_off[g]);
       f32x16_t acc = {};
 #pragma unroll
-      for (int s = 0; s < KS; ++s) acc = mfma_32x32x16(a[s], e[s], acc);
+      for (int s = 0; s < NT * KS; ++s) acc = mfma_32x32x16(a[s % KS], e[s], acc);
       // Epilogue: L = U + bias, tile max, fp32 sum of exp(L - max) (the order of the
       // register-prefetch step kernel, so both give the same partials bit for bit).
 #pragma unroll
@@ -466,7 +479,7 @@ __device__ __forceinline__ double tile_mass(float m, float s, float M) {
   return (m == kNegInf) ? 0.0 : static_cast<double>(exp_term(m - M)) * static_cast<double>(s);
 }
 
-template <int KS>
+template <int KS, int NT>
 __global__ __launch_bounds__(SampleCfg<KS>::kThreads) void draft_sample_kernel(SampleArgs p) {
   constexpr int kSampleThreads = SampleCfg<KS>::kThreads;
   constexpr int kSamplePer = SampleCfg<KS>::kPer;
@@ -493,15 +506,16 @@ __global__ __launch_bounds__(SampleCfg<KS>::kThreads) void draft_sample_kernel(S
   const int c0 = min(nt, tid * per), c1 = min(nt, c0 + per);
   const int32_t prevtok = p.prev[static_cast<size_t>(b) * p.prev_stride];
   const int32_t forced = p.force ? p.force[out] : 0;   // the token to condition on, if forced
-  __shared__ __attribute__((aligned(16))) uint16_t Es[16 * KS];
+  __shared__ __attribute__((aligned(16))) uint16_t Es[16 * KS * NT];
   float2 v[kSamplePer];
   auto load_parts = [&](auto n_c) {
     constexpr int n = decltype(n_c)::value;
     float2 t[n];
 #pragma unroll
     for (int i = 0; i < n; ++i) t[i] = part[min(c0 + i, nt - 1)];
-    if (tid < 2 * KS)
-      copy16_to_lds(p.W1 + static_cast<size_t>(prevtok) * (16 * KS) + 8 * tid, lds_addr(Es));
+    if (tid < 64)
+      copy_row_to_lds<2 * KS * NT>(
+          bias_row<NT>(p.W1, p.E, 16 * KS, prevtok, static_cast<int64_t>(out)), lds_addr(Es), tid);
 #pragma unroll
     for (int i = 0; i < kSamplePer; ++i)
       v[i] = (i < n && i < per && c0 + i < c1) ? t[min(i, n - 1)] : make_float2(kNegInf, 0.0f);
@@ -565,7 +579,7 @@ __global__ __launch_bounds__(SampleCfg<KS>::kThreads) void draft_sample_kernel(S
   const float tm = part[L.chunk].x;   // goes out with the tile's loads
   wait_copies<0>();   // the embedding row copy (issued with the partials' loads)
   const int tok0 = L.chunk * kTileTokens;
-  recompute_tile_lds<KS>(Es, p.W2t, p.U + urow, tok0, p.V, Ls);
+  recompute_tile_lds<KS, NT>(Es, p.W2t, p.U + urow, tok0, p.V, Ls);
   __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_wave_barrier();
   int x;
@@ -591,7 +605,8 @@ __global__ __launch_bounds__(SampleCfg<KS>::kThreads) void draft_sample_kernel(S
     // The token whose probability is reported (and that conditions the next position).
     const int32_t cond = p.force ? forced : x;
     if (cond / kTileTokens != L.chunk) {
-      recompute_tile_lds<KS>(Es, p.W2t, p.U + urow, (cond / kTileTokens) * kTileTokens, p.V, Lc);
+      recompute_tile_lds<KS, NT>(Es, p.W2t, p.U + urow, (cond / kTileTokens) * kTileTokens, p.V,
+                                 Lc);
       __builtin_amdgcn_s_waitcnt(0);
       __builtin_amdgcn_wave_barrier();
       qc = exp(static_cast<double>(Lc[cond % kTileTokens] * p.beta) - lse);
@@ -652,38 +667,68 @@ __global__ __launch_bounds__(kBlock) void confidence_kernel(ConfArgs p) {
 
 }  // namespace
 
-template <int KS>
+template <int KS, int NT>
 static hipError_t launch_step_dma(const StepArgs& a, hipStream_t s) {
   const int ngroups = (a.B + kDmaGroup - 1) / kDmaGroup;
   const int per = a.persistent_wgs / ngroups;
   const int grid = (per > 0 ? per : 1) * ngroups;
-  hipLaunchKernelGGL(markov_step_dma_kernel<KS>, dim3(grid), dim3(kDmaThreads), 0, s, a);
+  hipLaunchKernelGGL((markov_step_dma_kernel<KS, NT>), dim3(grid), dim3(kDmaThreads), 0, s, a);
   return hipGetLastError();
 }
 
-template <int KS>
-static hipError_t launch_step_ks(const StepArgs& a, hipStream_t s) {
+template <int KS, int NT>
+static hipError_t launch_step_prefetch(const StepArgs& a, hipStream_t s) {
+  const int items = ((a.V + 4 * kTileTokens - 1) / (4 * kTileTokens)) *
+                    ((a.B + StepCfg<KS * NT>::kBG - 1) / StepCfg<KS * NT>::kBG);
+  const int grid = items < a.persistent_wgs ? items : a.persistent_wgs;
+  if ((a.V & 3) == 0)
+    hipLaunchKernelGGL((markov_step_kernel<KS, true, NT>), dim3(grid), dim3(kStepThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((markov_step_kernel<KS, false, NT>), dim3(grid), dim3(kStepThreads), 0, s,
+                       a);
+  return hipGetLastError();
+}
+
+template <int KS, int NT>
+static hipError_t launch_step_kind(const StepArgs& a, hipStream_t s) {
   // The pipelined kernel copies 16-byte U chunks (rows 16-byte aligned: V % 4 == 0), one to four
   // 1 KB W2 copies per wave (64 <= r <= 256; two r = 512 stages would not fit in LDS), and the
   // debug-logits output would put global stores inside its copy pipeline: other requests take
   // the register-prefetch kernel.
   if constexpr (KS >= 4 && KS <= 16) {
-    if (a.dbg == nullptr && (a.V & 3) == 0) return launch_step_dma<KS>(a, s);
+    if (a.dbg == nullptr && (a.V & 3) == 0) return launch_step_dma<KS, NT>(a, s);
   }
-  const int items = ((a.V + 4 * kTileTokens - 1) / (4 * kTileTokens)) *
-                    ((a.B + StepCfg<KS>::kBG - 1) / StepCfg<KS>::kBG);
-  const int grid = items < a.persistent_wgs ? items : a.persistent_wgs;
-  if ((a.V & 3) == 0)
-    hipLaunchKernelGGL((markov_step_kernel<KS, true>), dim3(grid), dim3(kStepThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL((markov_step_kernel<KS, false>), dim3(grid), dim3(kStepThreads), 0, s, a);
-  return hipGetLastError();
+  return launch_step_prefetch<KS, NT>(a, s);
+}
+// Bias rows of three bf16 terms (the RNN head) are built for r <= 256; the pipelined step holds
+// them in registers up to r = 128 (at r = 256 they take the register-prefetch kernel, whose
+// LDS holds them).
+template <int KS>
+static hipError_t launch_step_ks(const StepArgs& a, hipStream_t s) {
+  if (a.e_terms == 1) return launch_step_kind<KS, 1>(a, s);
+  if constexpr (KS <= 8) {
+    if (a.e_terms == kRnnTerms) return launch_step_kind<KS, kRnnTerms>(a, s);
+  } else if constexpr (KS == 16) {
+    if (a.e_terms == kRnnTerms) return launch_step_prefetch<KS, kRnnTerms>(a, s);
+  }
+  return hipErrorInvalidValue;
 }
 template <int KS>
 static hipError_t launch_sample_ks(const SampleArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(draft_sample_kernel<KS>, dim3(a.B), dim3(SampleCfg<KS>::kThreads),
-                     static_cast<size_t>(a.ntiles) * sizeof(double), s, a);
-  return hipGetLastError();
+  const size_t lds = static_cast<size_t>(a.ntiles) * sizeof(double);
+  if (a.e_terms == 1) {
+    hipLaunchKernelGGL((draft_sample_kernel<KS, 1>), dim3(a.B), dim3(SampleCfg<KS>::kThreads), lds,
+                       s, a);
+    return hipGetLastError();
+  }
+  if constexpr (KS <= 16) {
+    if (a.e_terms == kRnnTerms) {
+      hipLaunchKernelGGL((draft_sample_kernel<KS, kRnnTerms>), dim3(a.B),
+                         dim3(SampleCfg<KS>::kThreads), lds, s, a);
+      return hipGetLastError();
+    }
+  }
+  return hipErrorInvalidValue;
 }
 
 #define DSPARK_DISPATCH_KS(r, fn, ...)             \

@@ -116,7 +116,7 @@ __global__ __launch_bounds__(kBlock) void accept_kernel(VerifyArgs p) {
   float tx0 = 0.0f, u0 = 0.0f, q0 = 0.0f;
   int32_t x0 = 0;
   double lsed0 = 0.0;
-  const int32_t anc = p.anchor[b];
+  const int32_t anc = p.anchor ? p.anchor[b] : 0;   // no anchor for an RNN-head draft
   if (lane < ell) {
     x0 = p.tokens[static_cast<size_t>(b) * p.gamma + lane];
     lsed0 = p.lse[static_cast<size_t>(b) * p.gamma + lane];
@@ -287,10 +287,10 @@ __device__ __forceinline__ void residual_pair(double pd, float t, double lse_t, 
   o = (pd < pt) ? pd : pt;
 }
 
-template <int KS, bool Greedy>
+template <int KS, bool Greedy, int NT>
 __global__ __launch_bounds__(kBlock, 2) void residual_partials_kernel(VerifyArgs p) {
-  using C = StepCfg<KS>;
-  constexpr int r = C::kR;
+  using C = StepCfg<KS * NT>;   // LDS rows hold the NT r bf16 of a bias row
+  constexpr int r = 16 * KS;
   __shared__ __attribute__((aligned(16))) uint16_t E[C::kBG * C::kLdsRow];
   __shared__ int list[C::kBG];
   __shared__ int red_i[kBlock / 64];
@@ -324,14 +324,16 @@ __global__ __launch_bounds__(kBlock, 2) void residual_partials_kernel(VerifyArgs
       }
     }
     __syncthreads();
-    constexpr int kChunks = r / 8;
+    constexpr int kChunks = NT * r / 8;
     for (int c = tid; c < C::kBG * kChunks; c += kBlock) {
       const int i = c / kChunks, q = c % kChunks;
       u16x8_t v = zero_u16x8();
       if (i < nb) {
         const int b = list[i];
-        const int32_t prevtok = emit_prev(p, b, p.ws.epos[b]);
-        v = load_u16x8(p.W1 + static_cast<size_t>(prevtok) * r + q * 8);
+        const int j = p.ws.epos[b];
+        const int32_t prevtok = (NT == 1) ? emit_prev(p, b, j) : 0;
+        const int64_t pos = static_cast<int64_t>(b) * p.gamma + j - 1;
+        v = load_u16x8(bias_row<NT>(p.W1, p.E, r, prevtok, pos) + q * 8);
       }
       *reinterpret_cast<u16x8_t*>(&E[i * C::kLdsRow + q * 8]) = v;
     }
@@ -341,7 +343,8 @@ __global__ __launch_bounds__(kBlock, 2) void residual_partials_kernel(VerifyArgs
         const uint16_t* erow = &E[(nt * 32 + col) * C::kLdsRow + 8 * half];
         f32x16_t acc = {};
 #pragma unroll
-        for (int s = 0; s < KS; ++s) acc = mfma_32x32x16(a[s], load_u16x8(erow + 16 * s), acc);
+        for (int s = 0; s < NT * KS; ++s)
+          acc = mfma_32x32x16(a[s % KS], load_u16x8(erow + 16 * s), acc);
         const int i = nt * 32 + col;
         if (i < nb) {
           const int b = list[i];
@@ -421,7 +424,7 @@ struct ResStep {
   static_assert(kResGroup * kW2Chunks * 16 <= kStageBytes, "embedding rows fit in one stage");
 };
 
-template <int KS, bool Greedy>
+template <int KS, bool Greedy, int NT>
 __global__ __launch_bounds__(kResThreads, 1) void residual_dma_kernel(VerifyArgs p) {
   using D = ResStep<KS>;
   __shared__ __attribute__((aligned(1024))) unsigned char stage[D::kStages * D::kStageBytes];
@@ -454,8 +457,9 @@ __global__ __launch_bounds__(kResThreads, 1) void residual_dma_kernel(VerifyArgs
   constexpr int kERowsPerCopy = 1024 / (16 * D::kW2Chunks);
   const int nrow_w = min(D::kRowCopies, max(0, (gcount - kRowsPerCopy * D::kRowCopies * wave +
                                                 kRowsPerCopy - 1) / kRowsPerCopy));
-  const int ne_w = min(D::kECopies, max(0, (gcount - kERowsPerCopy * D::kECopies * wave +
-                                            kERowsPerCopy - 1) / kERowsPerCopy));
+  const int ne_w = (NT == 1) ? min(D::kECopies, max(0, (gcount - kERowsPerCopy * D::kECopies * wave +
+                                                        kERowsPerCopy - 1) / kERowsPerCopy))
+                             : 0;
   auto wait_item = [&]() { wait_copies_upto<D::kW2Copies, 2, D::kRowCopies>(nrow_w); };
 
   const uint32_t stage_addr = lds_addr(stage);
@@ -520,7 +524,18 @@ __global__ __launch_bounds__(kResThreads, 1) void residual_dma_kernel(VerifyArgs
     }
   };
 
-  // Prologue: embedding rows W1[prev] of the group into stage 1, item 0 into stage 0.
+  // Prologue. Markov head: embedding rows W1[prev] of the group into stage 1, item 0 into
+  // stage 0. RNN head: each lane loads its request's bias row (both terms) into registers,
+  // drained before the copies start.
+  u16x8_t e[NT * KS];
+  if constexpr (NT > 1) {
+    const ResRec& R = rec[row_own];
+    const uint16_t* erow =
+        bias_row<NT>(p.W1, p.E, D::r, 0, static_cast<int64_t>(R.b) * p.gamma + R.j - 1) + 8 * half;
+#pragma unroll
+    for (int s = 0; s < NT * KS; ++s) e[s] = load_u16x8(erow + 16 * s);
+    __builtin_amdgcn_s_waitcnt(0);
+  }
   {
     const uint32_t ebase = stage_addr + D::kStageBytes;
 #pragma unroll
@@ -536,8 +551,7 @@ __global__ __launch_bounds__(kResThreads, 1) void residual_dma_kernel(VerifyArgs
   issue(0);
   wait_item();   // the embedding rows (issued first) have landed
   asm volatile("s_barrier" ::: "memory");
-  u16x8_t e[KS];
-  {
+  if constexpr (NT == 1) {
     const unsigned char* eb = stage + D::kStageBytes;
 #pragma unroll
     for (int s = 0; s < KS; ++s)
@@ -571,7 +585,7 @@ __global__ __launch_bounds__(kResThreads, 1) void residual_dma_kernel(VerifyArgs
       }
       f32x16_t acc = {};
 #pragma unroll
-      for (int s = 0; s < KS; ++s) acc = mfma_32x32x16(a[s], e[s], acc);
+      for (int s = 0; s < NT * KS; ++s) acc = mfma_32x32x16(a[s % KS], e[s], acc);
       // This wave's half of the tile (accumulator slot groups 2 part, 2 part + 1), in token order.
       double W = 0.0, O = 0.0;
 #pragma unroll
@@ -608,7 +622,7 @@ __global__ __launch_bounds__(kResThreads, 1) void residual_dma_kernel(VerifyArgs
   flush(flushed, n);
 }
 
-template <int KS>
+template <int KS, int NT>
 __global__ __launch_bounds__(kBlock) void emit_sample_kernel(VerifyArgs p) {
   extern __shared__ double stage[];   // padded: residual tile masses, or one segment's terms
   __shared__ double ssum[kBlock];     // per-thread sums over contiguous ranges (wave-0 search)
@@ -616,7 +630,7 @@ __global__ __launch_bounds__(kBlock) void emit_sample_kernel(VerifyArgs p) {
   __shared__ Located loc;
   __shared__ float seg_m, row_m;     // the chosen segment's max, the row's largest segment max
   __shared__ float Ls[kTileTokens];
-  __shared__ __attribute__((aligned(16))) uint16_t Es[16 * KS];
+  __shared__ __attribute__((aligned(16))) uint16_t Es[16 * KS * NT];
 
   const int b = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -634,7 +648,7 @@ __global__ __launch_bounds__(kBlock) void emit_sample_kernel(VerifyArgs p) {
     // the embedding row of the position's previous token is copied into LDS behind them.
     const size_t base = static_cast<size_t>(b) * p.ntiles;
     const int nt = p.ntiles;
-    const int32_t prevtok = emit_prev(p, b, j);
+    const int32_t prevtok = (NT == 1) ? emit_prev(p, b, j) : 0;
     constexpr int kBatch = 16;
     double o = 0.0;
     for (int c0 = 0; c0 < nt; c0 += kBlock * kBatch) {
@@ -645,8 +659,10 @@ __global__ __launch_bounds__(kBlock) void emit_sample_kernel(VerifyArgs p) {
         w[i] = p.ws.rsum[base + c];
         ov[i] = p.ws.rmin[base + c];
       }
-      if (c0 == 0 && tid < 2 * KS)
-        copy16_to_lds(p.W1 + static_cast<size_t>(prevtok) * (16 * KS) + 8 * tid, lds_addr(Es));
+      if (c0 == 0 && tid < 64)
+        copy_row_to_lds<2 * KS * NT>(
+            bias_row<NT>(p.W1, p.E, 16 * KS, prevtok, static_cast<int64_t>(b) * p.gamma + j - 1),
+            lds_addr(Es), tid);
 #pragma unroll
       for (int i = 0; i < kBatch; ++i) {
         const int c = c0 + i * kBlock + tid;
@@ -685,7 +701,7 @@ __global__ __launch_bounds__(kBlock) void emit_sample_kernel(VerifyArgs p) {
       const float* Urow = p.U + (static_cast<size_t>(b) * p.gamma + j - 1) * p.V;
       const float tv = (lane < kTileTokens && tok0 + lane < p.V) ? trow[tok0 + lane] : 0.0f;
       wait_copies<0>();   // the embedding row
-      recompute_tile_lds<KS>(Es, p.W2t, Urow, tok0, p.V, Ls);
+      recompute_tile_lds<KS, NT>(Es, p.W2t, Urow, tok0, p.V, Ls);
       __builtin_amdgcn_s_waitcnt(0);
       __builtin_amdgcn_wave_barrier();
       double w = 0.0;
@@ -788,32 +804,53 @@ hipError_t launch_accept(const VerifyArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int KS, bool Greedy>
+template <int KS, bool Greedy, int NT>
 static hipError_t launch_resid_kind(const VerifyArgs& a, hipStream_t s) {
   // The pipelined pass copies 16-byte row chunks (V % 4 == 0) and 1-2 KB of W2t per wave
-  // (128 <= r <= 256); other shapes take the register-load kernel.
-  if constexpr (KS >= 8 && KS <= 16) {
+  // (128 <= r <= 256) and holds a wave's bias rows in registers (the three terms of the RNN
+  // head only up to r = 128); other shapes take the register-load kernel.
+  if constexpr (KS >= 8 && KS <= 16 && (NT == 1 || KS <= 8)) {
     if ((a.V & 3) == 0) {
       const int groups = (a.B + kResGroup - 1) / kResGroup;
       const int grid = a.persistent_wgs > groups ? a.persistent_wgs : groups;
-      hipLaunchKernelGGL((residual_dma_kernel<KS, Greedy>), dim3(grid), dim3(kResThreads), 0, s,
-                         a);
+      hipLaunchKernelGGL((residual_dma_kernel<KS, Greedy, NT>), dim3(grid), dim3(kResThreads), 0,
+                         s, a);
       return hipGetLastError();
     }
   }
   const int grid = (a.V + 4 * kTileTokens - 1) / (4 * kTileTokens);
-  hipLaunchKernelGGL((residual_partials_kernel<KS, Greedy>), dim3(grid), dim3(kBlock), 0, s, a);
+  hipLaunchKernelGGL((residual_partials_kernel<KS, Greedy, NT>), dim3(grid), dim3(kBlock), 0, s,
+                     a);
   return hipGetLastError();
 }
+template <int KS, int NT>
+static hipError_t launch_resid_terms(const VerifyArgs& a, hipStream_t s) {
+  return a.greedy ? launch_resid_kind<KS, true, NT>(a, s) : launch_resid_kind<KS, false, NT>(a, s);
+}
+// Bias rows of three bf16 terms (the RNN head) are built for r <= 256.
 template <int KS>
 static hipError_t launch_resid_ks(const VerifyArgs& a, hipStream_t s) {
-  return a.greedy ? launch_resid_kind<KS, true>(a, s) : launch_resid_kind<KS, false>(a, s);
+  if (a.e_terms == 1) return launch_resid_terms<KS, 1>(a, s);
+  if constexpr (KS <= 16) {
+    if (a.e_terms == kRnnTerms) return launch_resid_terms<KS, kRnnTerms>(a, s);
+  }
+  return hipErrorInvalidValue;
 }
 template <int KS>
 static hipError_t launch_emit_ks(const VerifyArgs& a, hipStream_t s) {
   const int slots = padded(a.ntiles > kSegTokens ? a.ntiles : kSegTokens);
-  hipLaunchKernelGGL(emit_sample_kernel<KS>, dim3(a.B), dim3(kBlock), slots * sizeof(double), s, a);
-  return hipGetLastError();
+  const size_t lds = static_cast<size_t>(slots) * sizeof(double);
+  if (a.e_terms == 1) {
+    hipLaunchKernelGGL((emit_sample_kernel<KS, 1>), dim3(a.B), dim3(kBlock), lds, s, a);
+    return hipGetLastError();
+  }
+  if constexpr (KS <= 16) {
+    if (a.e_terms == kRnnTerms) {
+      hipLaunchKernelGGL((emit_sample_kernel<KS, kRnnTerms>), dim3(a.B), dim3(kBlock), lds, s, a);
+      return hipGetLastError();
+    }
+  }
+  return hipErrorInvalidValue;
 }
 
 #define DSPARK_DISPATCH_KS(r, fn, ...)             \

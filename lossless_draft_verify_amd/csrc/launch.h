@@ -18,6 +18,10 @@ struct StepArgs {
   float* dbg;           // nullable [B][gamma][V] (the logits L, before the temperature)
   int persistent_wgs;   // workgroups of the persistent step kernel (one per compute unit)
   float beta;           // logits are scaled by beta = fp32(1 / temperature) (1: unscaled)
+  // Bias rows: 1 = the Markov embedding row W1[prev]; 3 = the RNN head's bias vector of
+  // (b, k) as three bf16 terms, E [B][gamma][3r] (prev unused).
+  int e_terms = 1;
+  const uint16_t* E = nullptr;
 };
 
 struct SampleArgs {
@@ -35,6 +39,8 @@ struct SampleArgs {
   double* lse;
   float beta;   // as in StepArgs
   int greedy;   // draft the first maximal logit (point-mass q)
+  int e_terms = 1;               // as in StepArgs
+  const uint16_t* E = nullptr;
 };
 
 struct ConfArgs {
@@ -108,6 +114,41 @@ struct VerifyArgs {
   float beta;         // the draft distribution: softmax(beta L), beta = fp32(1 / temperature)
   int greedy;         // or the point mass on the drafted token (greedy drafts)
   VerifyWs ws;
+  int e_terms = 1;               // bias rows as in StepArgs (3: E [B][gamma][3r], in ws)
+  const uint16_t* E = nullptr;
+};
+
+// RNN head, eq. (6). P [M][3r] (fp64) = the hidden-state block of Wgco applied to every h_k
+// (M = B gamma rows (b, k)); computed once per round, off the serial chain.
+struct RnnPreArgs {
+  int M, r, d;
+  const uint16_t* h;      // [M][d] bf16
+  const uint16_t* Wgco;   // [3r][2r + d] bf16: rows W_g, W_c, W_o; columns state | embedding | hidden
+  double* P;              // [M][3r]
+};
+
+// One step of the RNN state: pre-activations a = P[b][k] + Wgco[:, state] s_{k-1} +
+// Wgco[:, embedding] W1[x_{k-1}] (fp64), s_k, e_k = tanh(a_o); e_k as fp32 and as three bf16
+// terms (the bias rows of the step kernel).
+struct RnnStateArgs {
+  int B, gamma, k, r, d;
+  const double* P;
+  const uint16_t* Wgco;
+  const uint16_t* W1;
+  const int32_t* prev;    // conditioning token of request b at prev[b * prev_stride]
+  int prev_stride;
+  const double* s_in;     // [B][r] s_{k-1} (ignored at k = 0: s_0 = 0)
+  double* s_out;          // [B][r] s_k
+  float* e_out;           // [B][gamma][r] e_k (fp32)
+  uint16_t* E;            // [B][gamma][3r] bf16 terms of e_k
+};
+
+// The bf16 terms of given fp32 bias vectors (the verify of an RNN-head draft): E [n][3r] from
+// e [n][r], the same split the state step writes.
+struct SplitArgs {
+  int n, r;
+  const float* e;
+  uint16_t* E;
 };
 
 hipError_t launch_markov_step(const StepArgs& a, int r, hipStream_t s);
@@ -118,5 +159,8 @@ hipError_t launch_target_stats(const VerifyArgs& a, hipStream_t s);
 hipError_t launch_accept(const VerifyArgs& a, hipStream_t s);
 hipError_t launch_residual_partials(const VerifyArgs& a, hipStream_t s);
 hipError_t launch_emit_sample(const VerifyArgs& a, hipStream_t s);
+hipError_t launch_rnn_pre(const RnnPreArgs& a, hipStream_t s);
+hipError_t launch_rnn_state(const RnnStateArgs& a, hipStream_t s);
+hipError_t launch_split_bias(const SplitArgs& a, hipStream_t s);
 
 }  // namespace dspark

@@ -71,51 +71,31 @@ __device__ __forceinline__ float max16(const float (&L)[16]) {
   return m;
 }
 
-// The Markov embedding row of the previous token, in the MFMA B-operand layout of a lane.
-template <int KS>
-__device__ __forceinline__ void load_e_row(u16x8_t (&e)[KS], const uint16_t* __restrict__ W1,
-                                           int32_t prevtok, int half) {
-  constexpr int r = KS * 16;
-  const uint16_t* erow = W1 + static_cast<size_t>(prevtok) * r + 8 * half;
-#pragma unroll
-  for (int s = 0; s < KS; ++s) e[s] = load_u16x8(erow + 16 * s);
+// The B-operand row of the bias contraction for one (request, position): the Markov
+// embedding row W1[prev] (NT = 1, r bf16), or the RNN head's bias vector e of that position held
+// as NT bf16 terms [t_1 | t_2 | t_3] (NT = kRnnTerms = 3, rows of 3r bf16 at E + pos * 3r):
+// t_1 = RN(e), t_2 = RN(e - t_1), t_3 = RN(e - t_1 - t_2), whose sum carries the fp32 e to its
+// 24 bits. The contraction runs over the NT terms in order, each over the r columns of W2, so
+// every caller forms the same fp32 sums.
+constexpr int kRnnTerms = 3;
+
+template <int NT>
+__device__ __forceinline__ const uint16_t* bias_row(const uint16_t* W1, const uint16_t* E, int r,
+                                                    int32_t prev, int64_t pos) {
+  if constexpr (NT == 1) {
+    return W1 + static_cast<size_t>(prev) * r;
+  } else {
+    return E + static_cast<size_t>(pos) * (NT * r);
+  }
 }
 
 // Recompute the logits of one 32-token tile for one request with exactly the instruction
-// sequence of the streaming draft step (same k order, same operands; the request sits in every
-// MFMA column, and column placement does not change the result). Called by a whole wave; the
-// tile's U values are loaded together with the W2 tile. Lanes 0 and 32 hold the 32 logits,
-// which are written to Ls[0..32).
-template <int KS>
-__device__ void recompute_tile_e(const u16x8_t (&e)[KS], const uint16_t* __restrict__ W2t,
-                                 const float* __restrict__ Urow, int tok0, int V, float* Ls) {
-  const int lane = threadIdx.x & 63, half = lane >> 5, col = lane & 31;
-  u16x8_t a[KS];
-  load_w2_tile<KS>(a, W2t, tok0 + col, V, half);
-  float u[16];
-  const bool vec4 = (V & 3) == 0;
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    float o[4];
-    load4(Urow, tok0 + 8 * g + 4 * half, V, vec4, o);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) u[4 * g + i] = o[i];
-  }
-  f32x16_t acc = {};
-#pragma unroll
-  for (int s = 0; s < KS; ++s) acc = mfma_32x32x16(a[s], e[s], acc);
-  if (col == 0) {
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int v = tok0 + tile_token(j, half);
-      Ls[tile_token(j, half)] = (v < V) ? (u[j] + acc[j]) : kNegInf;
-    }
-  }
-}
-
-// recompute_tile_e with the embedding row read from LDS (Es: r bf16) one k-step at a time, for
-// callers that keep the row in LDS rather than in registers.
-template <int KS>
+// sequence of the streaming draft step (same k order: the NT terms in turn, each over the r
+// columns; same operands; the request sits in every MFMA column, and column placement does not
+// change the result). Called by a whole wave; the bias row (NT r bf16) is read from LDS one
+// k-step at a time, and the tile's U values are loaded together with the W2 tile. Lanes 0 and 32
+// hold the 32 logits, which are written to Ls[0..32).
+template <int KS, int NT = 1>
 __device__ void recompute_tile_lds(const uint16_t* Es, const uint16_t* __restrict__ W2t,
                                    const float* __restrict__ Urow, int tok0, int V, float* Ls) {
   const int lane = threadIdx.x & 63, half = lane >> 5, col = lane & 31;
@@ -132,8 +112,8 @@ __device__ void recompute_tile_lds(const uint16_t* Es, const uint16_t* __restric
   }
   f32x16_t acc = {};
 #pragma unroll
-  for (int s = 0; s < KS; ++s)
-    acc = mfma_32x32x16(a[s], *reinterpret_cast<const u16x8_t*>(Es + 16 * s + 8 * half), acc);
+  for (int s = 0; s < NT * KS; ++s)
+    acc = mfma_32x32x16(a[s % KS], *reinterpret_cast<const u16x8_t*>(Es + 16 * s + 8 * half), acc);
   if (col == 0) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
@@ -141,16 +121,6 @@ __device__ void recompute_tile_lds(const uint16_t* Es, const uint16_t* __restric
       Ls[tile_token(j, half)] = (v < V) ? (u[j] + acc[j]) : kNegInf;
     }
   }
-}
-
-// recompute_tile_e with the embedding row of `prevtok` loaded here.
-template <int KS>
-__device__ void recompute_tile(const uint16_t* __restrict__ W1, const uint16_t* __restrict__ W2t,
-                               const float* __restrict__ Urow, int32_t prevtok, int tok0, int V,
-                               float* Ls) {
-  u16x8_t e[KS];
-  load_e_row<KS>(e, W1, prevtok, (threadIdx.x & 63) >> 5);
-  recompute_tile_e<KS>(e, W2t, Urow, tok0, V, Ls);
 }
 
 // Walk one tile in ascending token order on one wave: lane j < 32 holds the mass w of token j

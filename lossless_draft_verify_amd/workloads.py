@@ -28,7 +28,7 @@ import numpy as np
 import torch
 
 # tensor ids for seeding
-_T_ANCHOR, _T_U, _T_PEAKS, _T_W1, _T_W2, _T_H, _T_W, _T_UNIF, _T_NOISE, _T_UBONUS = range(10)
+_T_ANCHOR, _T_U, _T_PEAKS, _T_W1, _T_W2, _T_H, _T_W, _T_UNIF, _T_NOISE, _T_UBONUS, _T_WGCO = range(11)
 _WEIGHTS_ROUND = 1 << 20
 
 FULL_VERIFY, EARLY_STOP, FULL_PATH, LAGGED_TOPK = 0, 1, 2, 3
@@ -116,6 +116,19 @@ def weights(wl: Workload, device="cpu") -> Dict[str, torch.Tensor]:
     w = _normal((wl.d + wl.r,), 1.0 / np.sqrt(wl.d + wl.r), _gen(wl, R, _T_W, device),
                 device).to(torch.bfloat16)
     return dict(W1=W1, W2t=W2t, w=w)
+
+
+def rnn_weights(wl: Workload, device="cpu") -> torch.Tensor:
+    """RNN-head weights Wgco [3r][2r+d] bf16: rows W_g, W_c, W_o; columns in the order of
+    z = [state; embedding; hidden]. Each column block is scaled so that it adds unit variance to
+    a pre-activation: state block N(0, 1/sqrt(r)), embedding block N(0, 1/(w_std sqrt(r))),
+    hidden block N(0, 1/sqrt(d))."""
+    r, d = wl.r, wl.d
+    W = _normal((3 * r, 2 * r + d), 1.0, _gen(wl, _WEIGHTS_ROUND, _T_WGCO, device), device)
+    scale = torch.cat([torch.full((r,), 1.0 / np.sqrt(r)),
+                       torch.full((r,), 1.0 / (wl.w_std * np.sqrt(r))),
+                       torch.full((d,), 1.0 / np.sqrt(d))]).to(device)
+    return (W * scale[None, :]).to(torch.bfloat16)
 
 
 def sps_table(wl: Workload) -> np.ndarray:

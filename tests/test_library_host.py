@@ -109,6 +109,26 @@ def test_draft_option_checks_without_gpu(lib):
     assert lib.dspark_status_string(8) == b"draft temperature not positive and finite"
 
 
+def test_rnn_head_checks_without_gpu(lib):
+    """The RNN head: workspace sizes, r <= 256 and d a positive multiple of 8, NULL checks."""
+    dims = L.Dims(4, 3, 1000, 16, 64)
+    d, P = dims.c(), _p()
+    n = L.workspace_bytes(dims, L.OP_RNN_DRAFT)
+    assert n >= L.workspace_bytes(dims, L.OP_DRAFT) + 2 * 12 * 48 * 8 + 2 * 4 * 16 * 8 + 12 * 48 * 2
+    v = L.workspace_bytes(dims, L.OP_RNN_VERIFY)
+    assert v >= L.workspace_bytes(dims, L.OP_VERIFY) + 12 * 48 * 2
+    for bad in (L.Dims(4, 3, 1000, 512, 64), L.Dims(4, 3, 1000, 16, 12), L.Dims(4, 3, 1000, 16, 0)):
+        with pytest.raises(L.DsparkError):
+            L.workspace_bytes(bad, L.OP_RNN_DRAFT)
+        assert lib.dspark_rnn_draft(bad.c(), *([P] * 11), None, None, P, n, None, None) == 2
+    # NULL Wgco; a workspace one byte short
+    assert lib.dspark_rnn_draft(d, P, P, P, None, *([P] * 7), None, None, P, n, None, None) == 1
+    assert lib.dspark_rnn_draft(d, *([P] * 11), None, None, P, n - 1, None, None) == 4
+    assert lib.dspark_rnn_verify(d, *([P] * 12), None, None, P, v - 1, None, None) == 4
+    assert lib.dspark_rnn_verify(d, *([P] * 5), None, *([P] * 6), None, None, P, v, None,
+                                 None) == 1
+
+
 def test_binding_refuses_host_tensors(lib):
     import torch
     d = L.Dims(4, 3, 1000, 16, 64)
