@@ -60,7 +60,7 @@ def traffic_from_profiles(launch_units):
 
 
 class InputSet:
-    def __init__(self, wl, wts, round_index, dev, opts):
+    def __init__(self, wl, wts, round_index, dev, opts, head="markov"):
         d = L.Dims(wl.B, wl.gamma, wl.V, wl.r, wl.d)
         inp = W.round_inputs(wl, round_index, dev, with_hidden=True, with_noise=True)
         self.anchor, self.U, self.h, self.uniforms = inp["anchor"], inp["U"], inp["h"], inp["uniforms"]
@@ -69,8 +69,12 @@ class InputSet:
         # Untimed pass: draft with debug logits -> target stand-in = logits + noise; the plan of
         # this pass fixes the packed row layout (the timed rounds recompute the same plan).
         logits = torch.empty_like(self.U)
-        tok, q, lse = L.markov_draft(d, self.U, wts["W1"], wts["W2t"], self.anchor, self.uniforms,
-                                     logits_dbg=logits, **opts)
+        if head == "rnn":
+            tok, q, lse, _ = L.rnn_draft(d, self.U, wts["W1"], wts["W2t"], wts["Wgco"], self.h,
+                                         self.anchor, self.uniforms, logits_dbg=logits, **opts)
+        else:
+            tok, q, lse = L.markov_draft(d, self.U, wts["W1"], wts["W2t"], self.anchor,
+                                         self.uniforms, logits_dbg=logits, **opts)
         conf = L.confidence(d, self.h, wts["W1"], wts["w"], self.T, self.anchor, tok)
         dl, ro, st = L.plan(d, conf, self.sps, wl.mode)
         dense = W.target_dense(logits, inp["U_bonus"], inp["noise"])
@@ -82,13 +86,17 @@ class InputSet:
         self.draft_len = dl.clone()
 
 
-def algorithmic_bytes(wl, rows, n_res, greedy=False):
+def algorithmic_bytes(wl, rows, n_res, greedy=False, head="markov"):
     """Bytes the method must move in one round (no caching credit): per draft step the U slice
     and W2; the hidden states and confidence weights; every verified target row; for rejected
     requests one more W2 pass plus their U and target rows (a greedy draft's residual needs only
-    the target rows: its draft distribution is a point mass)."""
+    the target rows: its draft distribution is a point mass). The RNN head adds the hidden
+    states and the hidden block of Wgco once, the state and embedding blocks of Wgco per step,
+    and the fp32 bias vectors written by the draft and read by the verify."""
     B, V, g, r, d = wl.B, wl.V, wl.gamma, wl.r, wl.d
     draft = g * (4 * B * V + 2 * r * V)
+    if head == "rnn":
+        draft += 2 * B * g * d + 2 * 3 * r * d + g * 2 * 3 * r * 2 * r + 2 * 4 * B * g * r
     conf = 2 * B * g * d + 2 * (d + r)
     stats = 4 * rows * V
     if greedy:
@@ -98,7 +106,7 @@ def algorithmic_bytes(wl, rows, n_res, greedy=False):
     return draft + conf + stats + emit
 
 
-def cpu_baseline(wl, wts, s, threads, opts):
+def cpu_baseline(wl, wts, s, threads, opts, head="markov"):
     """The oracle as it stands, timed on the host on one full round of the same workload."""
     import oracle
     host = lambda t: t.detach().cpu().numpy()
@@ -107,7 +115,13 @@ def cpu_baseline(wl, wts, s, threads, opts):
     anchor, unif, h = host(s.anchor), host(s.uniforms), bits(s.h)
     sps = W.sps_table(wl)
     t0 = time.perf_counter()
-    o = oracle.markov_draft(U, W1b, W2b, anchor, unif, want_logits=True, threads=threads, **opts)
+    if head == "rnn":
+        Wg = bits(wts["Wgco"])
+        o = oracle.rnn_draft(U, W1b, W2b, Wg, h, anchor, unif, want_logits=True, threads=threads,
+                             **opts)
+    else:
+        o = oracle.markov_draft(U, W1b, W2b, anchor, unif, want_logits=True, threads=threads,
+                                **opts)
     c = oracle.confidence(h, W1b, bits(wts["w"]), W.temperatures(wl).numpy(), anchor, o["tokens"],
                           threads=threads)
     p = oracle.plan(c["conf"], sps, wl.mode)
@@ -120,12 +134,17 @@ def cpu_baseline(wl, wts, s, threads, opts):
     target = np.ascontiguousarray(dense[keep], dtype=np.float32)
     del dense, noise
     t2 = time.perf_counter()
-    oracle.verify(target, p["row_offsets"], p["draft_len"], U, W1b, W2b, anchor, o["tokens"],
-                  o["q"], unif, threads=threads, **opts)
+    if head == "rnn":
+        oracle.rnn_verify(target, p["row_offsets"], p["draft_len"], U, W1b, W2b, Wg, h, anchor,
+                          o["tokens"], o["q"], unif, threads=threads, **opts)
+    else:
+        oracle.verify(target, p["row_offsets"], p["draft_len"], U, W1b, W2b, anchor, o["tokens"],
+                      o["q"], unif, threads=threads, **opts)
     t3 = time.perf_counter()
     sec = (t1 - t0) + (t3 - t2)
     return {"value": 1.0 / sec, "unit": "rounds/s", "cores": threads, "kind": "oracle",
-            "sample": f"one full round of {wl.name} (all {wl.B} requests: draft, confidence, "
+            "sample": f"one full round of {wl.name} (all {wl.B} requests: {head}-head draft, "
+                      f"confidence, "
                       f"plan, verify; target construction excluded), {sec:.2f} s"}
 
 
@@ -144,6 +163,8 @@ def main():
                     help="time eager launches only (no hipGraph capture of the round)")
     ap.add_argument("--temperature", type=float, default=1.0,
                     help="draft sampling temperature (the drafted distribution softmax(L / tau))")
+    ap.add_argument("--head", choices=["markov", "rnn"], default="markov",
+                    help="serial draft head: the Markov head (eq. 5) or the RNN head (eq. 6)")
     ap.add_argument("--greedy", action="store_true",
                     help="greedy draft (first maximal logit; the verify's residual is p_t "
                          "without the drafted token)")
@@ -162,12 +183,16 @@ def main():
     d = L.Dims(wl.B, wl.gamma, wl.V, wl.r, wl.d)
     L.load_library()
     wts = W.weights(wl, dev)
-    sets = [InputSet(wl, wts, i, dev, opts) for i in range(args.sets)]
+    if args.head == "rnn":
+        wts["Wgco"] = W.rnn_weights(wl, dev)
+    sets = [InputSet(wl, wts, i, dev, opts, args.head) for i in range(args.sets)]
 
     # output and workspace buffers, allocated once
     B, g = wl.B, wl.gamma
-    ws_d = L.workspace(d, L.OP_DRAFT, dev)
-    ws_v = L.workspace(d, L.OP_VERIFY, dev)
+    rnn = args.head == "rnn"
+    ws_d = L.workspace(d, L.OP_RNN_DRAFT if rnn else L.OP_DRAFT, dev)
+    ws_v = L.workspace(d, L.OP_RNN_VERIFY if rnn else L.OP_VERIFY, dev)
+    e_rows = torch.empty((wl.B, wl.gamma, wl.r), dtype=torch.float32, device=dev) if rnn else None
     tok = torch.empty((B, g), dtype=torch.int32, device=dev)
     q = torch.empty((B, g), dtype=torch.float32, device=dev)
     lse = torch.empty((B, g), dtype=torch.float64, device=dev)
@@ -180,7 +205,7 @@ def main():
     be = torch.empty(B, dtype=torch.float32, device=dev)
     fl = torch.empty(B, dtype=torch.int32, device=dev)
 
-    def round_(s):
+    def round_markov(s):
         L.markov_draft(d, s.U, wts["W1"], wts["W2t"], s.anchor, s.uniforms, tokens=tok, q=q,
                        lse=lse, ws=ws_d, **opts)
         L.confidence(d, s.h, wts["W1"], wts["w"], s.T, s.anchor, tok, conf=conf)
@@ -188,6 +213,16 @@ def main():
         L.verify(d, s.target, ro, dl, s.U, wts["W1"], wts["W2t"], s.anchor, tok, q, lse,
                  s.uniforms, accept_len=al, next_token=nt, beta_emit=be, flags=fl, ws=ws_v,
                  **opts)
+
+    def round_rnn(s):
+        L.rnn_draft(d, s.U, wts["W1"], wts["W2t"], wts["Wgco"], s.h, s.anchor, s.uniforms,
+                    tokens=tok, q=q, lse=lse, e_rows=e_rows, ws=ws_d, **opts)
+        L.confidence(d, s.h, wts["W1"], wts["w"], s.T, s.anchor, tok, conf=conf)
+        L.plan(d, conf, s.sps, wl.mode, draft_len=dl, row_offsets=ro, stats=st)
+        L.rnn_verify(d, s.target, ro, dl, s.U, wts["W2t"], e_rows, tok, q, lse, s.uniforms,
+                     accept_len=al, next_token=nt, beta_emit=be, flags=fl, ws=ws_v, **opts)
+
+    round_ = round_rnn if args.head == "rnn" else round_markov
 
     # per-set results (identical every time a set is replayed: deterministic)
     per_set = []
@@ -264,8 +299,8 @@ def main():
     rounds_per_s = args.steps / timed
     used = [per_set[i % len(sets)] for i in range(args.steps)]
     tokens_per_round = float(np.mean([u["tokens"] for u in used]))
-    bytes_per_round = float(np.mean([algorithmic_bytes(wl, u["rows"], u["n_res"], args.greedy)
-                                     for u in used]))
+    bytes_per_round = float(np.mean([algorithmic_bytes(wl, u["rows"], u["n_res"], args.greedy,
+                                                       args.head) for u in used]))
 
     roofline = None
     mfma = None
@@ -277,15 +312,19 @@ def main():
         step_bytes = 4 * wl.B * wl.V + 2 * wl.r * wl.V        # U slice + W2 per launch
         avg_s = kernels["markov_step"]["avg_us"] * 1e-6
         achieved = step_bytes / avg_s / 1e9
-        traffic = traffic_from_profiles(1)
+        # the committed counters were taken on the Markov head's step kernel
+        traffic = traffic_from_profiles(1) if args.head == "markov" else None
         roofline = {"kernel": "markov_step", "bound": "hbm", "achieved": round(achieved, 1),
                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                     "traffic": traffic, "traffic_unit": "bytes per launch",
                     "algorithmic_bytes_per_launch": step_bytes,
                     "avg_launch_us": round(kernels["markov_step"]["avg_us"], 3)}
-        flops = 2.0 * wl.B * wl.r * wl.V                        # the W2 contraction per launch
+        # the W2 contraction per launch; the RNN head's bias vector enters it as three bf16 terms
+        terms = 3 if args.head == "rnn" else 1
+        flops = 2.0 * wl.B * wl.r * wl.V * terms
         mfma = {"kernel": "markov_step", "tflops": round(flops / avg_s / 1e12, 1),
-                "peak": MFMA_BF16_PEAK_TFLOPS, "frac": round(flops / avg_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+                "peak": MFMA_BF16_PEAK_TFLOPS, "frac": round(flops / avg_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                "bias_terms": terms}
 
     if args.copy_calibration:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
@@ -298,7 +337,7 @@ def main():
     base = None
     if not args.no_cpu_baseline:
         threads = min(16, os.cpu_count() or 1)
-        base = cpu_baseline(wl, wts, sets[0], threads, opts)
+        base = cpu_baseline(wl, wts, sets[0], threads, opts, args.head)
 
     out = {
         "metric": METRIC,
@@ -317,7 +356,8 @@ def main():
                    "d": wl.d, "plan": "early_stop", "sps": "1/(1+n/768)", "input_sets": len(sets),
                    "parallelism": "1 GPU", "launch": "eager",
                    "draft": ("greedy" if args.greedy
-                             else f"sampled at temperature {args.temperature:g}")},
+                             else f"sampled at temperature {args.temperature:g}"),
+                   "head": args.head},
         "round_us": round_us,
         "graph_rounds_per_s": (round(args.steps / elapsed_graph, 2)
                                if elapsed_graph is not None else None),

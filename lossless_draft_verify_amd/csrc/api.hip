@@ -81,11 +81,11 @@ size_t draft_ws(const dspark_dims& d, void* base, DraftWs* out) {
   return align_up(n * sizeof(float2));
 }
 
-// RNN-head draft: the step partials, then P [2][B gamma][3r] fp64 (split-K parts of the hidden
-// block), the state ping-pong [2][B][r] fp64 and the bias rows E [B gamma][3r] bf16.
+// RNN-head draft: the step partials, then P [kRnnPreSplits][B gamma][3r] fp32 (slices of the
+// hidden block), the state ping-pong [2][B][r] fp64 and the bias rows E [B gamma][3r] bf16.
 struct RnnDraftWs {
   DraftWs draft;
-  double* P;
+  float* P;
   double* s[2];
   uint16_t* E;
 };
@@ -98,12 +98,12 @@ size_t rnn_draft_ws(const dspark_dims& d, void* base, RnnDraftWs* out) {
     off += align_up(bytes);
     return p;
   };
-  char* P = take(2 * M * 3 * d.r * sizeof(double));
+  char* P = take(static_cast<size_t>(kRnnPreSplits) * M * 3 * d.r * sizeof(float));
   char* s0 = take(static_cast<size_t>(d.B) * d.r * sizeof(double));
   char* s1 = take(static_cast<size_t>(d.B) * d.r * sizeof(double));
   char* E = take(M * kRnnTerms * d.r * sizeof(uint16_t));
   if (out) {
-    out->P = reinterpret_cast<double*>(P);
+    out->P = reinterpret_cast<float*>(P);
     out->s[0] = reinterpret_cast<double*>(s0);
     out->s[1] = reinterpret_cast<double*>(s1);
     out->E = reinterpret_cast<uint16_t*>(E);

@@ -8,7 +8,8 @@
 //
 // Three kernels:
 //   rnn_pre     the hidden-state block of Wgco applied to every h_k of the round (one bf16 MFMA
-//               GEMM, B gamma x d x 3r, off the serial chain): P[split][B gamma][3r] in fp64.
+//               GEMM, B gamma x d x 3r, off the serial chain): P[slice][B gamma][3r], the sums
+//               over kRnnPreSplits slices of the hidden dimension (fp64 sums stored as fp32).
 //   rnn_state   one step: pre-activations P + Wgco[:, state] s_{k-1} + Wgco[:, emb] W1[x_{k-1}]
 //               in fp64, the gates, s_k, and e_k = tanh(a_o), written as fp32 and as three bf16
 //               terms (t1 = RN(e), t2 = RN(e - t1), t3 = RN(e - t1 - t2)) that the bias
@@ -17,6 +18,7 @@
 #include <hip/hip_runtime.h>
 
 #include "device.h"
+#include "dma.h"
 #include "launch.h"
 #include "tiles.h"
 
@@ -26,70 +28,108 @@ namespace {
 // ---- rnn_pre: P = h . Wgco[:, hidden]^T ------------------------------------------------------
 //
 // A 256-thread workgroup computes a 64 (outputs n) x 64 (rows m = b gamma + k) tile over one
-// half of the hidden dimension; wave w takes the 32 x 32 sub-tile (n: w & 1, m: w >> 1). The A
-// operand is 8 consecutive bf16 of a Wgco row (output n = lane % 32), the B operand 8 of an h
-// row (m = lane % 32), both 16-byte loads straight from global memory (the two waves sharing an
-// operand meet in L1). Every 8 k-steps the fp32 MFMA sums are added into fp64 accumulators, so
-// the fp32 part of the error covers 128 products at a time.
+// of kRnnPreSplits slices of the hidden dimension; wave w takes the 32 x 32 sub-tile
+// (n: w & 1, m: w >> 1). The slice is walked in chunks of 128 columns: the chunk's 64 Wgco rows
+// and 64 h rows (256 B each) are copied into one of two LDS stages by LDS-DMA loads (whole 1 KB
+// lines per instruction, the next chunk in flight while one is computed), XOR-swizzled in
+// 16-byte pieces (piece c of row t at c ^ (t & 15)) so the 32 rows one ds_read_b128 touches fall
+// on distinct banks. After every chunk (8 k-steps, 128 products) the fp32 MFMA sums are added
+// into fp64 accumulators; each slice's sum is stored as fp32 (one rounding, about 6e-8
+// relative) and the state step adds the slices in fp64. Columns past d read as zero.
 constexpr int kPreThreads = 256;
-constexpr int kPreSplits = 2;
-constexpr int kPreBatch = 8;   // k-steps per fp32 chunk
-
-__device__ __forceinline__ u16x8_t load_or_zero(const uint16_t* row, int k, int d) {
-  return (k < d) ? load_u16x8(row + k) : zero_u16x8();   // d % 8 == 0: chunks are whole
-}
+constexpr int kPreChunk = 128;                        // columns per stage
+constexpr int kPreRowBytes = kPreChunk * 2;           // 256 B: 16 pieces of 16 B
+constexpr int kPreOperandBytes = 64 * kPreRowBytes;   // 16 KB per operand per stage
+constexpr int kPreStageBytes = 2 * kPreOperandBytes;
+constexpr int kPreCopies = kPreStageBytes / 1024 / (kPreThreads / 64);   // 8 per wave per chunk
 
 __global__ __launch_bounds__(kPreThreads) void rnn_pre_kernel(RnnPreArgs p) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ __attribute__((aligned(1024))) unsigned char stage[2 * kPreStageBytes];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, col = lane & 31;
   const int N = 3 * p.r, nz = 2 * p.r + p.d;
   const int ntn = (N + 63) / 64, ntm = (p.M + 63) / 64;
   const int tile = blockIdx.x % (ntn * ntm), split = blockIdx.x / (ntn * ntm);
-  const int n0 = (tile % ntn) * 64 + 32 * (wave & 1);
-  const int m0 = (tile / ntn) * 64 + 32 * (wave >> 1);
-  // This split's k range, in whole 16-column steps.
-  const int steps = (p.d + 15) / 16;
-  const int s_lo = steps * split / kPreSplits, s_hi = steps * (split + 1) / kPreSplits;
-  const uint16_t* arow = p.Wgco + static_cast<size_t>(min(n0 + col, N - 1)) * nz + 2 * p.r;
-  const uint16_t* brow = p.h + static_cast<size_t>(min(m0 + col, p.M - 1)) * p.d;
+  const int nb = (tile % ntn) * 64, mb = (tile / ntn) * 64;
+  const int nchunks = (p.d + kPreChunk - 1) / kPreChunk;
+  const int c_lo = nchunks * split / kRnnPreSplits, c_hi = nchunks * (split + 1) / kRnnPreSplits;
+  const uint32_t stage_addr = lds_addr(stage);
+
+  // This wave's copies of chunk c into stage st: instruction q covers 4 rows (64 pieces);
+  // q < 16 fill the Wgco rows, the rest the h rows. Sources past d are clamped inside the row.
+  auto issue = [&](int c, int st) {
+#pragma unroll
+    for (int i = 0; i < kPreCopies; ++i) {
+      const int q = wave * kPreCopies + i;
+      const int qq = q & 15;
+      const int slot = 64 * qq + lane;
+      const int row = slot >> 4;
+      const int piece = (slot & 15) ^ (row & 15);
+      const int k = min(c * kPreChunk + 8 * piece, p.d - 8);
+      const uint16_t* src =
+          (q < 16) ? p.Wgco + static_cast<size_t>(min(nb + row, N - 1)) * nz + 2 * p.r + k
+                   : p.h + static_cast<size_t>(min(mb + row, p.M - 1)) * p.d + k;
+      copy16_to_lds(src, stage_addr + st * kPreStageBytes + (q >> 4) * kPreOperandBytes +
+                             1024 * qq);
+    }
+  };
+
+  const int arow = 32 * (wave & 1) + col, brow = 32 * (wave >> 1) + col;
   double acc64[16];
 #pragma unroll
   for (int j = 0; j < 16; ++j) acc64[j] = 0.0;
-  for (int s0 = s_lo; s0 < s_hi; s0 += kPreBatch) {
-    u16x8_t a[kPreBatch], b[kPreBatch];
-#pragma unroll
-    for (int i = 0; i < kPreBatch; ++i) {
-      const int k = 16 * (s0 + i) + 8 * half;
-      const bool in = s0 + i < s_hi;
-      a[i] = in ? load_or_zero(arow, k, p.d) : zero_u16x8();
-      b[i] = in ? load_or_zero(brow, k, p.d) : zero_u16x8();
+  if (c_lo < c_hi) issue(c_lo, 0);
+  for (int c = c_lo; c < c_hi; ++c) {
+    if (c + 1 < c_hi) {
+      issue(c + 1, (c + 1 - c_lo) & 1);
+      wait_copies<kPreCopies>();
+    } else {
+      wait_copies<0>();
     }
+    asm volatile("s_barrier" ::: "memory");
+    const unsigned char* base = stage + ((c - c_lo) & 1) * kPreStageBytes;
     f32x16_t acc = {};
 #pragma unroll
-    for (int i = 0; i < kPreBatch; ++i) acc = mfma_32x32x16(a[i], b[i], acc);
+    for (int s = 0; s < kPreChunk / 16; ++s) {
+      const int piece = 2 * s + half;
+      const bool in = c * kPreChunk + 8 * piece < p.d;
+      const u16x8_t a = *reinterpret_cast<const u16x8_t*>(
+          base + arow * kPreRowBytes + 16 * (piece ^ (arow & 15)));
+      const u16x8_t b = *reinterpret_cast<const u16x8_t*>(
+          base + kPreOperandBytes + brow * kPreRowBytes + 16 * (piece ^ (brow & 15)));
+      acc = mfma_32x32x16(in ? a : zero_u16x8(), b, acc);
+    }
 #pragma unroll
     for (int j = 0; j < 16; ++j) acc64[j] += static_cast<double>(acc[j]);
+    lds_barrier();   // the stage is free for chunk c + 2
   }
-  const int m = m0 + col;
+  const int m = mb + 32 * (wave >> 1) + col;
   if (m < p.M) {
-    double* out = p.P + (static_cast<size_t>(split) * p.M + m) * N;
+    float* out = p.P + (static_cast<size_t>(split) * p.M + m) * N;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const int n = n0 + tile_token(j, half);
-      if (n < N) out[n] = acc64[j];
+      const int n = nb + 32 * (wave & 1) + tile_token(j, half);
+      if (n < N) out[n] = static_cast<float>(acc64[j]);
     }
   }
 }
 
 // ---- rnn_state: one step of eq. (6) ----------------------------------------------------------
 //
-// Workgroup (request b, block of 64 state indices j); its four waves split the 2r columns of
-// z's state and embedding blocks into quarters. Thread (j, quarter) forms the three partial
-// dot products of rows j, r + j, 2r + j (W_g, W_c, W_o) over its quarter in fp64, z read from
-// LDS (every lane of a wave reads the same element: a broadcast); the quarters are summed in
-// fixed order with the two split-K parts of P.
+// Workgroup (block of 32 state indices j, block of 4 requests); its four waves split the 2r
+// columns of z's state and embedding blocks into quarters. Each wave first copies its quarter of
+// the 96 weight rows it needs (rows j, r + j, 2r + j: W_g, W_c, W_o) into its own LDS region by
+// LDS-DMA loads, all in flight at once (swizzled in 16-byte pieces like the other staged
+// tiles); lane (j, request pair) then forms the six partial dot products with its two requests'
+// z in fp64 (z from LDS, read by 32 lanes at once: broadcasts). Each weight element is read from
+// L2 by 32 request blocks instead of 128 requests. The quarters are summed in fixed order in LDS
+// with the slices of P, then wave 0 applies the gates.
 constexpr int kStateThreads = 256;
-constexpr int kStateJ = 64;
+constexpr int kStateJ = 32;
+constexpr int kStateB = 4;
+constexpr int kStateRows = 3 * kStateJ;                       // 96 weight rows per workgroup
+constexpr int kStateWaveBytes = kStateRows * (2 * 256 / 4) * 2;   // a quarter at r = 256: 24 KB
 
 __device__ __forceinline__ double bf16_to_f64(uint16_t v) {
   return static_cast<double>(__uint_as_float(static_cast<uint32_t>(v) << 16));
@@ -119,61 +159,114 @@ __device__ __forceinline__ void split_terms(float e, uint16_t* row, int r) {
 }
 
 __global__ __launch_bounds__(kStateThreads) void rnn_state_kernel(RnnStateArgs p) {
-  extern __shared__ double zs[];              // [2r]: s_{k-1} | W1[x_{k-1}]
-  __shared__ double part[3][3][kStateJ];      // quarters 1..3 of the three dot products
-  const int tid = threadIdx.x, jl = tid & 63, quarter = tid >> 6;
+  extern __shared__ double zs[];                    // [kStateB][2r]: s_{k-1} | W1[x_{k-1}]
+  __shared__ double part[3][6][64];                 // quarters 1..3: (row, request) x lane
+  __shared__ __attribute__((aligned(1024))) unsigned char wst[4 * kStateWaveBytes];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int quarter = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = p.r, nz = 2 * r + p.d;
   const int nj = (r + kStateJ - 1) / kStateJ;
-  const int b = blockIdx.x / nj, j0 = (blockIdx.x % nj) * kStateJ;
-  const int32_t x = p.prev[static_cast<size_t>(b) * p.prev_stride];
-  for (int i = tid; i < 2 * r; i += kStateThreads) {
-    zs[i] = (i < r) ? (p.s_in ? p.s_in[static_cast<size_t>(b) * r + i] : 0.0)
-                    : bf16_to_f64(p.W1[static_cast<size_t>(x) * r + (i - r)]);
+  const int j0 = (blockIdx.x % nj) * kStateJ, b0 = (blockIdx.x / nj) * kStateB;
+  const int q = (2 * r) / 4, i0 = quarter * q;       // 2r is a multiple of 32
+  const int cpr = q / 8;                             // 16-byte pieces per row: 1, 2, 4, 8 or 16
+  const int swz = cpr - 1;
+  // This wave's weight rows (t < 96: block t / 32 of W_g, W_c, W_o, state index t % 32) into
+  // its LDS region, all copies in flight at once.
+  const uint32_t wbase = lds_addr(wst) + quarter * kStateWaveBytes;
+  const int npieces = kStateRows * cpr;
+  for (int t = 0; t * 64 < npieces; ++t) {
+    const int slot = 64 * t + lane;
+    if (slot < npieces) {
+      const int row = slot / cpr;
+      const int piece = (slot % cpr) ^ (row & swz);
+      const int jr = min(j0 + row % kStateJ, r - 1);
+      copy16_to_lds(p.Wgco + static_cast<size_t>((row / kStateJ) * r + jr) * nz + i0 + 8 * piece,
+                    wbase + 1024 * t);
+    }
   }
+  // z of the block's requests: their previous tokens first, then every value's load in flight
+  // at once (at most kStateB * 2 * 256 / kStateThreads = 8 per thread) before the LDS stores.
+  __shared__ int32_t xs[kStateB];
+  if (tid < kStateB)
+    xs[tid] = p.prev[static_cast<size_t>(min(b0 + tid, p.B - 1)) * p.prev_stride];
   __syncthreads();
+  constexpr int kZPer = kStateB * 2 * 256 / kStateThreads;
+  double zv[kZPer];
+#pragma unroll
+  for (int u = 0; u < kZPer; ++u) {
+    const int i = tid + u * kStateThreads;
+    const int rb = min(i / (2 * r), kStateB - 1), c = i % (2 * r);
+    const int b = min(b0 + rb, p.B - 1);
+    const double sv = (p.s_in && c < r) ? p.s_in[static_cast<size_t>(b) * r + c] : 0.0;
+    const double ev = bf16_to_f64(p.W1[static_cast<size_t>(xs[rb]) * r + (c < r ? 0 : c - r)]);
+    zv[u] = (c < r) ? sv : ev;
+  }
+#pragma unroll
+  for (int u = 0; u < kZPer; ++u) {
+    const int i = tid + u * kStateThreads;
+    if (i < kStateB * 2 * r) zs[i] = zv[u];
+  }
+  wait_copies<0>();
+  __syncthreads();
+  const int jl = lane & 31, rp = lane >> 5;          // state index, request pair
   const int j = j0 + jl;
-  const int jc = min(j, r - 1);               // rows past r are computed on row r - 1, not stored
-  const int q = (2 * r) / 4, i0 = quarter * q;   // 2r is a multiple of 8
-  const uint16_t* wg = p.Wgco + static_cast<size_t>(jc) * nz;
-  const uint16_t* wc = p.Wgco + static_cast<size_t>(r + jc) * nz;
-  const uint16_t* wo = p.Wgco + static_cast<size_t>(2 * r + jc) * nz;
-  double ag = 0.0, ac = 0.0, ao = 0.0;
-  for (int i = i0; i < i0 + q; i += 8) {
-    const u16x8_t vg = load_u16x8(wg + i), vc = load_u16x8(wc + i), vo = load_u16x8(wo + i);
+  const unsigned char* wl = wst + quarter * kStateWaveBytes;
+  const double* z0 = zs + (2 * rp) * (2 * r) + i0;
+  const double* z1 = z0 + 2 * r;
+  double acc[6] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0};   // (g, c, o) x (request 2rp, 2rp + 1)
+  for (int pc = 0; pc < cpr; ++pc) {
+    u16x8_t w3[3];
+#pragma unroll
+    for (int m3 = 0; m3 < 3; ++m3) {
+      const int row = m3 * kStateJ + jl;
+      w3[m3] = *reinterpret_cast<const u16x8_t*>(wl + 16 * (row * cpr + (pc ^ (row & swz))));
+    }
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      const double z = zs[i + t];
-      ag += bf16_to_f64(vg[t]) * z;
-      ac += bf16_to_f64(vc[t]) * z;
-      ao += bf16_to_f64(vo[t]) * z;
+      const double za = z0[8 * pc + t], zb = z1[8 * pc + t];
+      const double g = bf16_to_f64(w3[0][t]), c = bf16_to_f64(w3[1][t]), o = bf16_to_f64(w3[2][t]);
+      // explicit fused multiply-adds (the build does not contract): one rounding per term
+      acc[0] = fma(g, za, acc[0]);
+      acc[1] = fma(c, za, acc[1]);
+      acc[2] = fma(o, za, acc[2]);
+      acc[3] = fma(g, zb, acc[3]);
+      acc[4] = fma(c, zb, acc[4]);
+      acc[5] = fma(o, zb, acc[5]);
     }
   }
   if (quarter > 0) {
-    part[quarter - 1][0][jl] = ag;
-    part[quarter - 1][1][jl] = ac;
-    part[quarter - 1][2][jl] = ao;
+#pragma unroll
+    for (int t = 0; t < 6; ++t) part[quarter - 1][t][lane] = acc[t];
   }
   __syncthreads();
   if (quarter != 0 || j >= r) return;
 #pragma unroll
-  for (int t = 0; t < 3; ++t) {
-    ag += part[t][0][jl];
-    ac += part[t][1][jl];
-    ao += part[t][2][jl];
+  for (int w = 0; w < 3; ++w) {
+#pragma unroll
+    for (int t = 0; t < 6; ++t) acc[t] += part[w][t][lane];
   }
-  const size_t m = static_cast<size_t>(b) * p.gamma + p.k;
   const int N = 3 * r;
-  const double* P0 = p.P + m * N;
-  const double* P1 = p.P + (static_cast<size_t>(p.B) * p.gamma + m) * N;
-  ag += P0[j] + P1[j];
-  ac += P0[r + j] + P1[r + j];
-  ao += P0[2 * r + j] + P1[2 * r + j];
-  const double gate = 1.0 / (1.0 + exp(-ag));
-  const double s_prev = zs[j];
-  p.s_out[static_cast<size_t>(b) * r + j] = gate * s_prev + (1.0 - gate) * tanh(ac);
-  const float e = static_cast<float>(tanh(ao));
-  p.e_out[m * r + j] = e;
-  split_terms(e, p.E + m * (kRnnTerms * r) + j, r);
+  const size_t M = static_cast<size_t>(p.B) * p.gamma;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int b = b0 + 2 * rp + h;
+    if (b >= p.B) continue;
+    const size_t m = static_cast<size_t>(b) * p.gamma + p.k;
+    double ag = acc[3 * h], ac = acc[3 * h + 1], ao = acc[3 * h + 2];
+#pragma unroll
+    for (int sp = 0; sp < kRnnPreSplits; ++sp) {
+      const float* P = p.P + (sp * M + m) * N;
+      ag += static_cast<double>(P[j]);
+      ac += static_cast<double>(P[r + j]);
+      ao += static_cast<double>(P[2 * r + j]);
+    }
+    const double gate = 1.0 / (1.0 + exp(-ag));
+    const double s_prev = zs[(2 * rp + h) * (2 * r) + j];
+    p.s_out[static_cast<size_t>(b) * r + j] = gate * s_prev + (1.0 - gate) * tanh(ac);
+    const float e = static_cast<float>(tanh(ao));
+    p.e_out[m * r + j] = e;
+    split_terms(e, p.E + m * (kRnnTerms * r) + j, r);
+  }
 }
 
 __global__ __launch_bounds__(256) void split_bias_kernel(SplitArgs p) {
@@ -188,14 +281,15 @@ __global__ __launch_bounds__(256) void split_bias_kernel(SplitArgs p) {
 
 hipError_t launch_rnn_pre(const RnnPreArgs& a, hipStream_t s) {
   const int ntn = (3 * a.r + 63) / 64, ntm = (a.M + 63) / 64;
-  hipLaunchKernelGGL(rnn_pre_kernel, dim3(ntn * ntm * kPreSplits), dim3(kPreThreads), 0, s, a);
+  hipLaunchKernelGGL(rnn_pre_kernel, dim3(ntn * ntm * kRnnPreSplits), dim3(kPreThreads), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_rnn_state(const RnnStateArgs& a, hipStream_t s) {
   const int nj = (a.r + kStateJ - 1) / kStateJ;
-  hipLaunchKernelGGL(rnn_state_kernel, dim3(a.B * nj), dim3(kStateThreads),
-                     static_cast<size_t>(2 * a.r) * sizeof(double), s, a);
+  const int nb = (a.B + kStateB - 1) / kStateB;
+  hipLaunchKernelGGL(rnn_state_kernel, dim3(nj * nb), dim3(kStateThreads),
+                     static_cast<size_t>(kStateB * 2 * a.r) * sizeof(double), s, a);
   return hipGetLastError();
 }
 

@@ -118,13 +118,15 @@ struct VerifyArgs {
   const uint16_t* E = nullptr;
 };
 
-// RNN head, eq. (6). P [M][3r] (fp64) = the hidden-state block of Wgco applied to every h_k
-// (M = B gamma rows (b, k)); computed once per round, off the serial chain.
+// RNN head, eq. (6). P [kRnnPreSplits][M][3r] = the hidden-state block of Wgco applied to every
+// h_k (M = B gamma rows (b, k)), one part per slice of the hidden dimension (summed in fp64,
+// stored as fp32); computed once per round, off the serial chain.
+constexpr int kRnnPreSplits = 8;
 struct RnnPreArgs {
   int M, r, d;
   const uint16_t* h;      // [M][d] bf16
   const uint16_t* Wgco;   // [3r][2r + d] bf16: rows W_g, W_c, W_o; columns state | embedding | hidden
-  double* P;              // [M][3r]
+  float* P;               // [kRnnPreSplits][M][3r]
 };
 
 // One step of the RNN state: pre-activations a = P[b][k] + Wgco[:, state] s_{k-1} +
@@ -132,7 +134,7 @@ struct RnnPreArgs {
 // terms (the bias rows of the step kernel).
 struct RnnStateArgs {
   int B, gamma, k, r, d;
-  const double* P;
+  const float* P;         // [kRnnPreSplits][M][3r] (rnn_pre)
   const uint16_t* Wgco;
   const uint16_t* W1;
   const int32_t* prev;    // conditioning token of request b at prev[b * prev_stride]

@@ -114,7 +114,7 @@ def test_rnn_head_checks_without_gpu(lib):
     dims = L.Dims(4, 3, 1000, 16, 64)
     d, P = dims.c(), _p()
     n = L.workspace_bytes(dims, L.OP_RNN_DRAFT)
-    assert n >= L.workspace_bytes(dims, L.OP_DRAFT) + 2 * 12 * 48 * 8 + 2 * 4 * 16 * 8 + 12 * 48 * 2
+    assert n >= L.workspace_bytes(dims, L.OP_DRAFT) + 8 * 12 * 48 * 4 + 2 * 4 * 16 * 8 + 12 * 48 * 2
     v = L.workspace_bytes(dims, L.OP_RNN_VERIFY)
     assert v >= L.workspace_bytes(dims, L.OP_VERIFY) + 12 * 48 * 2
     for bad in (L.Dims(4, 3, 1000, 512, 64), L.Dims(4, 3, 1000, 16, 12), L.Dims(4, 3, 1000, 16, 0)):
