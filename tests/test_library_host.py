@@ -135,3 +135,47 @@ def test_binding_refuses_host_tensors(lib):
     with pytest.raises(L.DsparkError):
         L.confidence(d, torch.zeros((4, 3, 64), dtype=torch.bfloat16), None, None, None, None, None,
                      conf=torch.zeros((4, 3)))
+
+
+def _c_kind(param):
+    """The ctypes kind a C parameter needs: pointer, int32, size_t or the dims struct."""
+    t = param.rsplit(" ", 1)[0] if not param.endswith("*") else param
+    if "*" in param:
+        return "ptr"
+    if t.startswith("dspark_dims"):
+        return "dims"
+    if t.startswith("size_t"):
+        return "size_t"
+    if t.startswith("int32_t") or t.startswith("dspark_status"):
+        return "int32"
+    raise AssertionError(f"unmapped C parameter {param!r}")
+
+
+def _py_kind(t):
+    if t is L.binding._CDims:
+        return "dims"
+    if t is ctypes.c_size_t:
+        return "size_t"
+    if t is ctypes.c_int32:
+        return "int32"
+    if t is ctypes.c_void_p or (isinstance(t, type) and issubclass(t, ctypes._Pointer)):
+        return "ptr"
+    raise AssertionError(f"unmapped ctypes type {t!r}")
+
+
+def test_binding_signatures_match_the_header(lib):
+    """Every function the binding declares has the header's parameter count and kinds, so a
+    marshalled call can never shift its arguments."""
+    text = open(HEADER).read()
+    decls = dict(re.findall(r"DSPARK_API\s+[\w\s\*]+?\b(dspark_\w+)\s*\(([^)]*)\)\s*;", text))
+    checked = 0
+    for name, params in decls.items():
+        fn = getattr(lib, name)
+        if getattr(fn, "argtypes", None) is None:
+            continue
+        c_params = [p.strip() for p in params.split(",") if p.strip() and p.strip() != "void"]
+        assert len(fn.argtypes) == len(c_params), (name, len(fn.argtypes), len(c_params))
+        for c, py in zip(c_params, fn.argtypes):
+            assert _c_kind(c) == _py_kind(py), (name, c, py)
+        checked += 1
+    assert checked >= 12
