@@ -315,7 +315,8 @@ DSPARK_API dspark_status dspark_rnn_verify(dspark_dims dims, const float* target
 /*
  * Kernel timing with HIP events (measurement support; not part of the method).
  * dspark_profile_begin(capacity) arms up to `capacity` event pairs; while armed, every kernel
- * launch of the library is bracketed by two events recorded on the launch stream.
+ * launch of the library records a pair with its dispatch on the launch stream (the start and
+ * stop events of hipExtLaunchKernel, taken around the kernel by the command processor).
  * dspark_profile_end() waits for the recorded events and returns, per kernel name, the number
  * of launches and their summed duration in milliseconds (names[i] has static storage), then
  * disarms. Returns the number of kernel names written (at most max_names), or -1 on error.

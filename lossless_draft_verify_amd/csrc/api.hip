@@ -12,6 +12,13 @@
 #include "launch.h"
 #include "tiles.h"
 
+namespace dspark {
+LaunchTiming& launch_timing() {
+  thread_local LaunchTiming t;
+  return t;
+}
+}  // namespace dspark
+
 namespace {
 
 using namespace dspark;
@@ -177,13 +184,20 @@ struct Profiler {
 };
 Profiler g_prof;
 
+// While the profiler is armed, the launch made by `launch` records the next event pair with
+// its dispatch (launch_kernel); if it launched nothing, the pair is recorded back to back.
 template <class F>
 hipError_t timed(KernelId id, hipStream_t s, F launch) {
   const bool rec = g_prof.armed && g_prof.used < g_prof.capacity;
-  if (rec) (void)hipEventRecord(g_prof.events[2 * g_prof.used], s);
+  LaunchTiming& t = launch_timing();
+  if (rec) t = LaunchTiming{g_prof.events[2 * g_prof.used], g_prof.events[2 * g_prof.used + 1]};
   const hipError_t e = launch();
   if (rec) {
-    (void)hipEventRecord(g_prof.events[2 * g_prof.used + 1], s);
+    if (t.start) {
+      (void)hipEventRecord(t.start, s);
+      (void)hipEventRecord(t.stop, s);
+      t = LaunchTiming{};
+    }
     g_prof.ids[g_prof.used] = id;
     ++g_prof.used;
   }

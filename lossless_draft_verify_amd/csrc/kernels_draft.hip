@@ -672,7 +672,7 @@ static hipError_t launch_step_dma(const StepArgs& a, hipStream_t s) {
   const int ngroups = (a.B + kDmaGroup - 1) / kDmaGroup;
   const int per = a.persistent_wgs / ngroups;
   const int grid = (per > 0 ? per : 1) * ngroups;
-  hipLaunchKernelGGL((markov_step_dma_kernel<KS, NT>), dim3(grid), dim3(kDmaThreads), 0, s, a);
+  launch_kernel(markov_step_dma_kernel<KS, NT>, dim3(grid), dim3(kDmaThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -682,9 +682,9 @@ static hipError_t launch_step_prefetch(const StepArgs& a, hipStream_t s) {
                     ((a.B + StepCfg<KS * NT>::kBG - 1) / StepCfg<KS * NT>::kBG);
   const int grid = items < a.persistent_wgs ? items : a.persistent_wgs;
   if ((a.V & 3) == 0)
-    hipLaunchKernelGGL((markov_step_kernel<KS, true, NT>), dim3(grid), dim3(kStepThreads), 0, s, a);
+    launch_kernel(markov_step_kernel<KS, true, NT>, dim3(grid), dim3(kStepThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((markov_step_kernel<KS, false, NT>), dim3(grid), dim3(kStepThreads), 0, s,
+    launch_kernel(markov_step_kernel<KS, false, NT>, dim3(grid), dim3(kStepThreads), 0, s,
                        a);
   return hipGetLastError();
 }
@@ -717,13 +717,13 @@ template <int KS>
 static hipError_t launch_sample_ks(const SampleArgs& a, hipStream_t s) {
   const size_t lds = static_cast<size_t>(a.ntiles) * sizeof(double);
   if (a.e_terms == 1) {
-    hipLaunchKernelGGL((draft_sample_kernel<KS, 1>), dim3(a.B), dim3(SampleCfg<KS>::kThreads), lds,
+    launch_kernel(draft_sample_kernel<KS, 1>, dim3(a.B), dim3(SampleCfg<KS>::kThreads), lds,
                        s, a);
     return hipGetLastError();
   }
   if constexpr (KS <= 16) {
     if (a.e_terms == kRnnTerms) {
-      hipLaunchKernelGGL((draft_sample_kernel<KS, kRnnTerms>), dim3(a.B),
+      launch_kernel(draft_sample_kernel<KS, kRnnTerms>, dim3(a.B),
                          dim3(SampleCfg<KS>::kThreads), lds, s, a);
       return hipGetLastError();
     }
@@ -749,7 +749,7 @@ hipError_t launch_draft_sample(const SampleArgs& a, int r, hipStream_t s) {
   DSPARK_DISPATCH_KS(r, launch_sample_ks, a, s)
 }
 hipError_t launch_confidence(const ConfArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(confidence_kernel, dim3(a.B * a.gamma), dim3(kBlock), 0, s, a);
+  launch_kernel(confidence_kernel, dim3(a.B * a.gamma), dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }
 

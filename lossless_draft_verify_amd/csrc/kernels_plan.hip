@@ -302,7 +302,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs p) {
 }  // namespace
 
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, a);
+  launch_kernel(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, a);
   return hipGetLastError();
 }
 

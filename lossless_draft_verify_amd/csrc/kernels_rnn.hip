@@ -281,14 +281,14 @@ __global__ __launch_bounds__(256) void split_bias_kernel(SplitArgs p) {
 
 hipError_t launch_rnn_pre(const RnnPreArgs& a, hipStream_t s) {
   const int ntn = (3 * a.r + 63) / 64, ntm = (a.M + 63) / 64;
-  hipLaunchKernelGGL(rnn_pre_kernel, dim3(ntn * ntm * kRnnPreSplits), dim3(kPreThreads), 0, s, a);
+  launch_kernel(rnn_pre_kernel, dim3(ntn * ntm * kRnnPreSplits), dim3(kPreThreads), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_rnn_state(const RnnStateArgs& a, hipStream_t s) {
   const int nj = (a.r + kStateJ - 1) / kStateJ;
   const int nb = (a.B + kStateB - 1) / kStateB;
-  hipLaunchKernelGGL(rnn_state_kernel, dim3(nj * nb), dim3(kStateThreads),
+  launch_kernel(rnn_state_kernel, dim3(nj * nb), dim3(kStateThreads),
                      static_cast<size_t>(kStateB * 2 * a.r) * sizeof(double), s, a);
   return hipGetLastError();
 }
@@ -296,7 +296,7 @@ hipError_t launch_rnn_state(const RnnStateArgs& a, hipStream_t s) {
 hipError_t launch_split_bias(const SplitArgs& a, hipStream_t s) {
   const size_t n = static_cast<size_t>(a.n) * a.r;
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(split_bias_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0,
+  launch_kernel(split_bias_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0,
                      s, a);
   return hipGetLastError();
 }

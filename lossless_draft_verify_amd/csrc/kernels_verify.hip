@@ -793,14 +793,14 @@ __global__ __launch_bounds__(kBlock) void emit_sample_kernel(VerifyArgs p) {
 }  // namespace
 
 hipError_t launch_target_stats(const VerifyArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(target_stats_kernel, dim3(a.persistent_wgs * kStatsBlocksPerCU), dim3(kBlock),
+  launch_kernel(target_stats_kernel, dim3(a.persistent_wgs * kStatsBlocksPerCU), dim3(kBlock),
                      0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_accept(const VerifyArgs& a, hipStream_t s) {
   const int grid = (a.B + (kBlock / 64) - 1) / (kBlock / 64);
-  hipLaunchKernelGGL(accept_kernel, dim3(grid), dim3(kBlock), 0, s, a);
+  launch_kernel(accept_kernel, dim3(grid), dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }
 
@@ -813,13 +813,13 @@ static hipError_t launch_resid_kind(const VerifyArgs& a, hipStream_t s) {
     if ((a.V & 3) == 0) {
       const int groups = (a.B + kResGroup - 1) / kResGroup;
       const int grid = a.persistent_wgs > groups ? a.persistent_wgs : groups;
-      hipLaunchKernelGGL((residual_dma_kernel<KS, Greedy, NT>), dim3(grid), dim3(kResThreads), 0,
+      launch_kernel(residual_dma_kernel<KS, Greedy, NT>, dim3(grid), dim3(kResThreads), 0,
                          s, a);
       return hipGetLastError();
     }
   }
   const int grid = (a.V + 4 * kTileTokens - 1) / (4 * kTileTokens);
-  hipLaunchKernelGGL((residual_partials_kernel<KS, Greedy, NT>), dim3(grid), dim3(kBlock), 0, s,
+  launch_kernel(residual_partials_kernel<KS, Greedy, NT>, dim3(grid), dim3(kBlock), 0, s,
                      a);
   return hipGetLastError();
 }
@@ -841,12 +841,12 @@ static hipError_t launch_emit_ks(const VerifyArgs& a, hipStream_t s) {
   const int slots = padded(a.ntiles > kSegTokens ? a.ntiles : kSegTokens);
   const size_t lds = static_cast<size_t>(slots) * sizeof(double);
   if (a.e_terms == 1) {
-    hipLaunchKernelGGL((emit_sample_kernel<KS, 1>), dim3(a.B), dim3(kBlock), lds, s, a);
+    launch_kernel(emit_sample_kernel<KS, 1>, dim3(a.B), dim3(kBlock), lds, s, a);
     return hipGetLastError();
   }
   if constexpr (KS <= 16) {
     if (a.e_terms == kRnnTerms) {
-      hipLaunchKernelGGL((emit_sample_kernel<KS, kRnnTerms>), dim3(a.B), dim3(kBlock), lds, s, a);
+      launch_kernel(emit_sample_kernel<KS, kRnnTerms>, dim3(a.B), dim3(kBlock), lds, s, a);
       return hipGetLastError();
     }
   }

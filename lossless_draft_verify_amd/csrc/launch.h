@@ -1,6 +1,7 @@
 // Kernel argument blocks and launchers (internal to libdspark.so).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -152,6 +153,28 @@ struct SplitArgs {
   const float* e;
   uint16_t* E;
 };
+
+// Kernel timing: the event pair the next launch records with its dispatch (hipExtLaunchKernel
+// start and stop events, taken by the command processor around the kernel itself), or none.
+struct LaunchTiming {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+LaunchTiming& launch_timing();   // per host thread
+
+// Every kernel of the library is launched through here.
+template <typename... KArgs, typename... Args>
+inline void launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t shmem,
+                          hipStream_t s, Args... args) {
+  LaunchTiming& t = launch_timing();
+  if (t.start) {
+    hipExtLaunchKernelGGL(kernel, grid, block, static_cast<uint32_t>(shmem), s, t.start, t.stop, 0,
+                          args...);
+    t = LaunchTiming{};
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, shmem, s, args...);
+  }
+}
 
 hipError_t launch_markov_step(const StepArgs& a, int r, hipStream_t s);
 hipError_t launch_draft_sample(const SampleArgs& a, int r, hipStream_t s);
