@@ -211,3 +211,78 @@ def test_rnn_round_full_size(opt):
     assert np.abs(be[same] - ov["beta_emit"][same]).max() <= PROB_TOL
     log(f"  logits err {err:.2e}, e err {e_err:.2e}; {c.report()}; mean accepted {al.mean():.2f}; "
         f"{acc.report()}; {emit.report()}")
+
+
+def _rnn_round_setup(seed_id):
+    wl = W.scaled(W.WORKLOADS["b128-v129280-g5"], name="rnn-graph", seed_id=seed_id, B=64,
+                  V=8192, d=256, sps_scale=64.0)
+    wts, inp = _inputs(wl)
+    d = dims_of(wl)
+    temps = W.temperatures(wl).to(DEV)
+    sps = _T(W.sps_table(wl), torch.float64)
+    logits = torch.empty_like(inp["U"])
+    t0, _, _, _ = L.rnn_draft(d, inp["U"], wts["W1"], wts["W2t"], wts["Wgco"], inp["h"],
+                              inp["anchor"], inp["uniforms"], logits_dbg=logits)
+    c0 = L.confidence(d, inp["h"], wts["W1"], wts["w"], temps, inp["anchor"], t0)
+    dl0, _, _ = L.plan(d, c0, sps, wl.mode)
+    target = W.pack_rows(W.target_dense(logits, inp["U_bonus"], inp["noise"]), dl0)
+    del logits
+    B, g = wl.B, wl.gamma
+    out = dict(tok=torch.empty((B, g), dtype=torch.int32, device=DEV),
+               q=torch.empty((B, g), dtype=torch.float32, device=DEV),
+               lse=torch.empty((B, g), dtype=torch.float64, device=DEV),
+               e=torch.empty((B, g, wl.r), dtype=torch.float32, device=DEV),
+               conf=torch.empty((B, g), dtype=torch.float32, device=DEV),
+               dl=torch.empty(B, dtype=torch.int32, device=DEV),
+               ro=torch.empty(B + 1, dtype=torch.int32, device=DEV),
+               st=torch.empty(4, dtype=torch.float64, device=DEV),
+               al=torch.empty(B, dtype=torch.int32, device=DEV),
+               nt=torch.empty(B, dtype=torch.int32, device=DEV),
+               be=torch.empty(B, dtype=torch.float32, device=DEV),
+               fl=torch.empty(B, dtype=torch.int32, device=DEV))
+    ws_d, ws_v = L.workspace(d, L.OP_RNN_DRAFT, DEV), L.workspace(d, L.OP_RNN_VERIFY, DEV)
+
+    def round_():
+        o = out
+        L.rnn_draft(d, inp["U"], wts["W1"], wts["W2t"], wts["Wgco"], inp["h"], inp["anchor"],
+                    inp["uniforms"], tokens=o["tok"], q=o["q"], lse=o["lse"], e_rows=o["e"],
+                    ws=ws_d)
+        L.confidence(d, inp["h"], wts["W1"], wts["w"], temps, inp["anchor"], o["tok"],
+                     conf=o["conf"])
+        L.plan(d, o["conf"], sps, wl.mode, draft_len=o["dl"], row_offsets=o["ro"],
+               stats=o["st"])
+        L.rnn_verify(d, target, o["ro"], o["dl"], inp["U"], wts["W2t"], o["e"], o["tok"],
+                     o["q"], o["lse"], inp["uniforms"], accept_len=o["al"], next_token=o["nt"],
+                     beta_emit=o["be"], flags=o["fl"], ws=ws_v)
+
+    return out, round_, dl0
+
+
+def test_rnn_round_graph_replays_and_determinism():
+    """An RNN-head round (its pre-GEMM, state steps and three-term bias rows included) gives the
+    same bits on a second eager run, and captured once as a hipGraph reproduces them on every
+    replay, with eager work between the replays and the outputs overwritten before each."""
+    out, round_, dl0 = _rnn_round_setup(91)
+    round_()
+    torch.cuda.synchronize()
+    eager = {k: v.clone() for k, v in out.items()}
+    assert torch.equal(eager["dl"], dl0)
+    round_()
+    torch.cuda.synchronize()
+    for k, v in out.items():
+        assert torch.equal(v, eager[k]), ("second eager run", k)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        round_()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        junk = torch.randn(1 << 20, device=DEV)
+        _ = float(junk.square().sum().item())
+        for v in out.values():
+            v.fill_(-7)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for k, v in out.items():
+            assert torch.equal(v, eager[k]), (rep, k)
+    log(f"  rnn round: eager runs and four graph replays equal (B_tot {eager['st'][0].item():.0f})")
