@@ -204,18 +204,6 @@ __device__ __forceinline__ float block_max(float v, float* red) {
   return m;
 }
 template <int NT>
-__device__ __forceinline__ double block_sum(double v, double* red) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  v = wave_sum(v);
-  __syncthreads();
-  if (lane == 0) red[w] = v;
-  __syncthreads();
-  double s = red[0];
-#pragma unroll
-  for (int i = 1; i < NT / 64; ++i) s += red[i];
-  return s;
-}
-template <int NT>
 __device__ __forceinline__ int block_max_int(int v, int* red) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   v = wave_max_int(v);
@@ -274,12 +262,10 @@ __device__ __forceinline__ int block_exclusive_scan_int(int v, int* red, int* to
   return before + (inc - v);
 }
 
-// Locate the chunk holding the draw: chunks 0..n-1 carry masses mass(c) >= 0 (ascending token
-// order); the draw is the first chunk whose cumulative mass exceeds u * Z, Z = total mass.
-// Each thread owns a contiguous range of chunks; the owner of the draw is the last thread with
-// positive mass whose exclusive prefix is <= u * Z, and it walks its range in order. If rounding
-// leaves the draw past the owner's range, the owner's last positive chunk is taken with
-// take_last set (the caller then takes that chunk's last positive token).
+// The chunk holding a draw: chunks 0..n-1 carry masses mass(c) >= 0 (ascending token order);
+// the draw is the first chunk whose cumulative mass exceeds the target (u * Z, Z = total mass).
+// If rounding leaves the draw past the last positive chunk of the range that should hold it,
+// that chunk is taken with take_last set (the caller then takes its last positive token).
 struct Located {
   int chunk;        // -1 if the total mass is not positive and finite
   int take_last;
@@ -288,66 +274,7 @@ struct Located {
   double total;     // Z
 };
 
-// target_of(Z) gives the draw's position on the cumulative-mass axis (u * Z for a plain draw).
-template <int NT, class MassFn, class TargetFn>
-__device__ Located locate_chunk_t(int n, TargetFn target_of, MassFn mass, double* red_d,
-                                  int* red_i, Located* shared_out) {
-  const int tid = threadIdx.x;
-  const int per = (n + NT - 1) / NT;
-  const int c0 = min(n, tid * per), c1 = min(n, c0 + per);
-  double S = 0.0;
-  for (int c = c0; c < c1; ++c) S += mass(c);
-  double Z;
-  const double P = block_exclusive_scan<NT>(S, red_d, &Z);
-  const double target = target_of(Z);
-  const bool ok = (Z > 0.0) && (Z < __builtin_inf());
-  const int owner = block_max_int<NT>((ok && S > 0.0 && P <= target) ? tid : -1, red_i);
-  if (tid == owner) {
-    Located r;
-    r.chunk = -1;
-    r.take_last = 0;
-    r.before = 0.0;
-    double cum = P;
-    int last = -1;
-    double last_before = P;
-    for (int c = c0; c < c1; ++c) {
-      const double m = mass(c);
-      if (m > 0.0) {
-        last = c;
-        last_before = cum;
-      }
-      if (cum + m > target) {
-        r.chunk = c;
-        r.before = cum;
-        break;
-      }
-      cum += m;
-    }
-    if (r.chunk < 0) {
-      r.chunk = last;
-      r.before = last_before;
-      r.take_last = 1;
-    }
-    r.target = target;
-    r.total = Z;
-    *shared_out = r;
-  }
-  __syncthreads();
-  Located res;
-  if (owner < 0) {
-    res.chunk = -1;
-    res.take_last = 0;
-    res.before = 0.0;
-    res.target = target;
-    res.total = Z;
-  } else {
-    res = *shared_out;
-  }
-  __syncthreads();
-  return res;
-}
-
-// The same draw located by one wave, for blocks whose NT threads each own a contiguous range of
+// A draw located by one wave, for blocks whose NT threads each own a contiguous range of
 // `per` chunks (thread t: chunks t per .. t per + per - 1, clipped to n; per <= 64) and have
 // written the sum of their range, added in chunk order, to ssum[t]; mass(c) must be readable by
 // every lane (LDS). Three levels, each a wave scan and a ballot: the group of NT / 64 threads,
@@ -399,12 +326,6 @@ __device__ Located wave_locate(const double* ssum, int n, int per, TargetFn targ
   r.chunk = tc0 + i3;
   r.before = read_lane(mpre, i3);
   return r;
-}
-
-template <int NT, class MassFn>
-__device__ Located locate_chunk(int n, double u, MassFn mass, double* red_d, int* red_i,
-                                Located* shared_out) {
-  return locate_chunk_t<NT>(n, [u](double Z) { return u * Z; }, mass, red_d, red_i, shared_out);
 }
 
 // LDS slot of entry c in a staging array with one pad slot per 16 entries: a thread's
