@@ -603,3 +603,54 @@ def test_nonfinite_flags_match_oracle():
     if ov["accept_len"][1] == g:
         assert np_(fl)[1] & L.FLAG_NONFINITE and ov["flags"][1] & L.FLAG_NONFINITE
         assert np_(nt)[1] == ov["next_token"][1] == 0
+
+
+def _verify_against_oracle(wl, name, noise_scale=1.0):
+    """Full verify of every drafted token against the oracle on the oracle's own draft; returns
+    the oracle's and the GPU's accept lengths."""
+    log(f"[verify edge] {name}")
+    wts = W.weights(wl, DEV)
+    inp = W.round_inputs(wl, 0, DEV, with_hidden=False)
+    inp["noise"] = inp["noise"] * noise_scale
+    o, conf, p, target = _oracle_round(wl, inp, wts, W.FULL_VERIFY)
+    ov = oracle.verify(target, p["row_offsets"], p["draft_len"], np_(inp["U"]), bits(wts["W1"]),
+                       bits(wts["W2t"]), np_(inp["anchor"]), o["tokens"], o["q"],
+                       np_(inp["uniforms"]))
+    g = gpu_draft(wl, inp, wts, force=o["tokens"])
+    al, nt, be, fl = L.verify(dims_of(wl), _T(target, torch.float32), _T(p["row_offsets"]),
+                              _T(p["draft_len"]), inp["U"], wts["W1"], wts["W2t"], inp["anchor"],
+                              _T(o["tokens"]), _T(o["q"], torch.float32), g["lse_t"],
+                              inp["uniforms"])
+    torch.cuda.synchronize()
+    al, nt, be, fl = np_(al), np_(nt), np_(be), np_(fl)
+    acc = MismatchCounter(f"accept {name}")
+    acc.add(al, ov["accept_len"], decisive_margin(ov, al, wl.gamma))
+    same = al == ov["accept_len"]
+    emit = MismatchCounter(f"emit {name}")
+    emit.add(nt[same], ov["next_token"][same], ov["emit_margin"][same])
+    assert np.array_equal(fl[same].astype(np.uint32), ov["flags"][same])
+    assert np.abs(be[same] - ov["beta_emit"][same]).max() <= PROB_TOL
+    log(f"  accepted {ov['accept_len'].tolist()[:8]}...; {acc.report()}; {emit.report()}")
+    return ov["accept_len"], al
+
+
+def test_verify_largest_vocabulary():
+    """The largest vocabulary the library takes (2^19 tokens, 128 target segments a row)."""
+    _verify_against_oracle(DRAFT_CASES["b3-v524288-r64-g2"], "b3-v524288-r64-g2")
+
+
+def test_verify_longest_block():
+    """The longest block (gamma 255: 256 rows a request, four 64-row batches of the accept
+    scan), with a low-noise target so that long runs are accepted."""
+    wl = _custom("b2-v1000-r16-g255", seed_id=92, B=2, V=1000, r=16, gamma=255,
+                 noise_std=lambda k: 0.02)
+    acc, _ = _verify_against_oracle(wl, "b2-v1000-g255")
+    assert acc.max() >= 64, "a request should accept into the second batch of rows"
+
+
+def test_verify_target_equal_to_draft():
+    """Target = draft logits exactly (no noise): p_t = p_d, so every test passes unless the
+    fp32 rounding of q puts u q at p_t (probability ~1e-7), and every request takes the bonus."""
+    wl = _custom("b64-v4000-r64-g6-exact", seed_id=93, B=64, V=4000, r=64, gamma=6)
+    acc, al = _verify_against_oracle(wl, "b64-v4000-g6 exact target", noise_scale=0.0)
+    assert (acc == wl.gamma).mean() >= 0.99 and np.array_equal(acc, al)
