@@ -277,6 +277,15 @@ __device__ __forceinline__ double draft_prob_t(float L, float beta, double lse_d
   }
 }
 
+// a or b by a wave-uniform byte selector: v_perm_b32 takes bytes 0-3 of (b, a) from a for
+// 0x03020100 and from b for 0x07060504. A byte permute, so that the choice between two elements
+// of a register array stays one instruction: a select there would be folded into a run-time
+// register index.
+constexpr uint32_t kPickA = 0x03020100u, kPickB = 0x07060504u;
+__device__ __forceinline__ float pick(float a, float b, uint32_t sel) {
+  return __uint_as_float(__builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), sel));
+}
+
 // Residual weight and overlap of one token: w = max(0, p_t - p_d), o = min(p_t, p_d), with
 // NaN behaving as in the comparisons written here (a NaN difference gives w = 0).
 __device__ __forceinline__ void residual_pair(double pd, float t, double lse_t, double& w,
@@ -434,6 +443,7 @@ __global__ __launch_bounds__(kResThreads, 1) void residual_dma_kernel(VerifyArgs
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, col = lane & 31;
   const int sub = (wave >> 1) & 1, rq = wave & 1, part = wave >> 2;
+  const uint32_t part_sel = part ? kPickB : kPickA;
   const int nres = *p.ws.rcount;
   if (nres <= 0) return;
   const int ngroups = (nres + kResGroup - 1) / kResGroup;   // <= gridDim.x (launch sizing)
@@ -587,25 +597,35 @@ __global__ __launch_bounds__(kResThreads, 1) void residual_dma_kernel(VerifyArgs
 #pragma unroll
       for (int s = 0; s < NT * KS; ++s) acc = mfma_32x32x16(a[s % KS], e[s], acc);
       // This wave's half of the tile (accumulator slot groups 2 part, 2 part + 1), in token order.
+      // Its eight slots are taken by byte permutes (a select here becomes a register-indexing
+      // sequence per term), and only a tile that reaches past V checks its tokens.
+      float Lh[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) Lh[q] = pick(acc[q], acc[8 + q], part_sel);
       double W = 0.0, O = 0.0;
+      auto half_tile = [&](auto checked) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int g = 2 * part + h;
-        const int v = tok0 + 8 * g + 4 * half;
-        const float u4[4] = {uu[h].x, uu[h].y, uu[h].z, uu[h].w};
-        const float t4[4] = {tt[h].x, tt[h].y, tt[h].z, tt[h].w};
+        for (int h = 0; h < 2; ++h) {
+          const int v = tok0 + 8 * (2 * part + h) + 4 * half;
+          const float u4[4] = {uu[h].x, uu[h].y, uu[h].z, uu[h].w};
+          const float t4[4] = {tt[h].x, tt[h].y, tt[h].z, tt[h].w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (v + i < p.V) {
-            double w, o;
-            residual_pair(draft_prob_t<Greedy>(u4[i] + acc[4 * g + i], p.beta, lse_d,
-                                               v + i == xtok),
-                          t4[i], lse_t, w, o);
-            W += w;
-            O += o;
+          for (int i = 0; i < 4; ++i) {
+            if (!decltype(checked)::value || v + i < p.V) {
+              double w, o;
+              residual_pair(draft_prob_t<Greedy>(u4[i] + Lh[4 * h + i], p.beta, lse_d,
+                                                 v + i == xtok),
+                            t4[i], lse_t, w, o);
+              W += w;
+              O += o;
+            }
           }
         }
-      }
+      };
+      if (tok0 + kTileTokens <= p.V)
+        half_tile(std::false_type{});
+      else
+        half_tile(std::true_type{});
       W = W + other_half(W, half);
       O = O + other_half(O, half);
       if (half == 0 && row_own < gcount)
