@@ -8,6 +8,8 @@
  *   dspark_verify        lossless rejection-sampling verify, residual resample, bonus token
  *   dspark_markov_draft_opts, dspark_verify_opts   the same with a draft temperature or greedy
  *   dspark_rnn_draft, dspark_rnn_verify   the draft and verify with the RNN head of eq. (6)
+ *   dspark_markov_draft_plan   draft, confidence and plan of a round in one call, the plan
+ *                        computed beside the last position's draft step
  *
  * Sources (cited below by tag; each gives the page title and the section or equation):
  *   [V41]  blog.javazero.top, "DeepSeek-V4.1 模型结构（6）：解码，DSpark"
@@ -58,7 +60,7 @@ extern "C" {
 /* Problem sizes. B requests, gamma draft positions, V vocabulary, r Markov rank, d hidden size
  * (d is read only by dspark_confidence). Supported: B >= 1, 1 <= gamma <= 255, 2 <= V <= 2^19,
  * r in {16, 32, 64, 128, 256, 512}, d % 8 == 0, B * (gamma + 1) <= 65535, and for
- * dspark_plan B * gamma <= 8192. */
+ * dspark_plan and dspark_markov_draft_plan B * gamma <= 8192. */
 typedef struct dspark_dims {
   int32_t B;
   int32_t gamma;
@@ -214,6 +216,30 @@ DSPARK_API dspark_status dspark_plan(dspark_dims dims, const float* conf, const 
                                      int32_t sps_len, int32_t mode, float* ring,
                                      int32_t round_index, int32_t* draft_len,
                                      int32_t* row_offsets, double* stats, void* stream);
+
+/*
+ * The draft side of one round in a single call: the Markov-head draft (as
+ * dspark_markov_draft_opts without logits_dbg or force_tokens), the confidence head (as
+ * dspark_confidence) and the planner (as dspark_plan), with the same arguments, checks and
+ * outputs as those three calls made one after the other. Passages: those of the three calls;
+ * the planner depends only on the confidences, which depend only on x_0 .. x_{gamma-1}
+ * ([V41] "confidence head", eq. (7)), so it is computed while the last position is drafted.
+ * Order on the stream: draft positions 1 .. gamma-1, the confidence head, then the last
+ * position's step with the planner on one extra workgroup of the same launch (for r in
+ * {64, 128, 256}, V % 4 == 0 and B * gamma <= 4096; other shapes launch the planner and the
+ * step one after the other), then the last position's sampler. The results are bit-identical to
+ * the three separate calls.
+ *   ws, ws_bytes   the draft workspace (dspark_workspace_bytes(dims, DSPARK_OP_DRAFT))
+ *   opts           nullable; temperature / greedy as in dspark_markov_draft_opts
+ * Returns the first failing check of the three calls (nothing is launched then).
+ */
+DSPARK_API dspark_status dspark_markov_draft_plan(
+    dspark_dims dims, const float* U, const uint16_t* W1, const uint16_t* W2t,
+    const int32_t* anchor, const float* uniforms, const uint16_t* h, const uint16_t* w,
+    const float* T, const double* sps, int32_t sps_len, int32_t mode, float* ring,
+    int32_t round_index, int32_t* tokens, float* q_tok, double* lse, float* conf,
+    int32_t* draft_len, int32_t* row_offsets, double* stats, void* ws, size_t ws_bytes,
+    const dspark_draft_opts* opts, void* stream);
 
 /*
  * Lossless verify.

@@ -213,11 +213,20 @@ struct RnnDraftInputs {
   RnnDraftWs w;
 };
 
+// The confidence head and the plan of a round, when the draft call also makes them: they need
+// only the tokens before the last position, so they are launched before the last step, and the
+// plan runs on one workgroup of that step's launch where the shape allows.
+struct RoundPlan {
+  ConfArgs conf;
+  PlanArgs plan;
+};
+
 dspark_status draft_loop(const dspark_dims& dims, const float* U, const uint16_t* W1,
                          const uint16_t* W2t, const int32_t* anchor, const float* uniforms,
                          int32_t* tokens, float* q_tok, double* lse, float* logits_dbg,
                          const int32_t* force_tokens, float2* part, float beta, int greedy,
-                         const RnnDraftInputs* rnn, hipStream_t s) {
+                         const RnnDraftInputs* rnn, hipStream_t s,
+                         const RoundPlan* round_plan = nullptr) {
   const int nt = ntiles_of(dims.V);
   const int cus = compute_units();
   if (rnn) {
@@ -248,8 +257,26 @@ dspark_status draft_loop(const dspark_dims& dims, const float* U, const uint16_t
       sa.e_terms = pa.e_terms = kRnnTerms;
       sa.E = pa.E = rnn->w.E;
     }
-    if (timed(kMarkovStep, s, [&] { return launch_markov_step(sa, dims.r, s); }) != hipSuccess)
+    if (round_plan && k == dims.gamma - 1) {
+      if (timed(kConfidence, s, [&] { return launch_confidence(round_plan->conf, s); }) !=
+          hipSuccess)
+        return DSPARK_ERR_HIP;
+      if (markov_step_plan_fits(sa, dims.r, dims.B, dims.gamma)) {
+        if (timed(kMarkovStep, s, [&] {
+              return launch_markov_step_plan(sa, round_plan->plan, dims.r, s);
+            }) != hipSuccess)
+          return DSPARK_ERR_HIP;
+      } else {
+        if (timed(kPlan, s, [&] { return launch_plan(round_plan->plan, s); }) != hipSuccess)
+          return DSPARK_ERR_HIP;
+        if (timed(kMarkovStep, s, [&] { return launch_markov_step(sa, dims.r, s); }) !=
+            hipSuccess)
+          return DSPARK_ERR_HIP;
+      }
+    } else if (timed(kMarkovStep, s, [&] { return launch_markov_step(sa, dims.r, s); }) !=
+               hipSuccess) {
       return DSPARK_ERR_HIP;
+    }
     if (timed(kDraftSample, s, [&] { return launch_draft_sample(pa, dims.r, s); }) != hipSuccess)
       return DSPARK_ERR_HIP;
   }
@@ -266,6 +293,36 @@ dspark_status verify_passes(const dspark_dims& dims, VerifyArgs& a, hipStream_t 
   if (timed(kEmitSample, s, [&] { return launch_emit_sample(a, s); }) != hipSuccess)
     return DSPARK_ERR_HIP;
   (void)dims;
+  return DSPARK_OK;
+}
+
+// Argument checks of the confidence head and of the planner (shared by their own entry points
+// and the draft call that also makes them).
+dspark_status check_confidence(const dspark_dims& dims, const uint16_t* h, const uint16_t* W1,
+                               const uint16_t* w, const float* T, const int32_t* anchor,
+                               const int32_t* tokens, const float* conf) {
+  if (!h || !W1 || !w || !T || !anchor || !tokens || !conf) return DSPARK_ERR_NULL;
+  if (!dims_ok(dims) || dims.d < 8 || dims.d % 8 != 0) return DSPARK_ERR_SHAPE;
+  if (!aligned(h, 16) || !aligned(W1, 16) || !aligned(w, 16) || !aligned(T, 4) ||
+      !aligned(anchor, 4) || !aligned(tokens, 4) || !aligned(conf, 4))
+    return DSPARK_ERR_ALIGN;
+  return DSPARK_OK;
+}
+
+dspark_status check_plan(const dspark_dims& dims, const float* conf, const double* sps,
+                         int32_t sps_len, int32_t mode, const float* ring, int32_t round_index,
+                         const int32_t* draft_len, const int32_t* row_offsets,
+                         const double* stats) {
+  if (!sps || !draft_len || !row_offsets) return DSPARK_ERR_NULL;
+  if (mode < DSPARK_PLAN_FULL_VERIFY || mode > DSPARK_PLAN_LAGGED_TOPK) return DSPARK_ERR_MODE;
+  if (mode != DSPARK_PLAN_FULL_VERIFY && !conf) return DSPARK_ERR_NULL;
+  if (mode == DSPARK_PLAN_LAGGED_TOPK && !ring) return DSPARK_ERR_MODE;
+  if (!plan_dims_ok(dims) || round_index < 0) return DSPARK_ERR_SHAPE;
+  if (static_cast<int64_t>(sps_len) < static_cast<int64_t>(dims.B) * (dims.gamma + 1) + 1)
+    return DSPARK_ERR_SPS;
+  if ((conf && !aligned(conf, 4)) || !aligned(sps, 8) || (ring && !aligned(ring, 4)) ||
+      !aligned(draft_len, 4) || !aligned(row_offsets, 4) || (stats && !aligned(stats, 8)))
+    return DSPARK_ERR_ALIGN;
   return DSPARK_OK;
 }
 
@@ -369,11 +426,8 @@ dspark_status dspark_markov_draft(dspark_dims dims, const float* U, const uint16
 dspark_status dspark_confidence(dspark_dims dims, const uint16_t* h, const uint16_t* W1,
                                 const uint16_t* w, const float* T, const int32_t* anchor,
                                 const int32_t* tokens, float* conf, void* stream) {
-  if (!h || !W1 || !w || !T || !anchor || !tokens || !conf) return DSPARK_ERR_NULL;
-  if (!dims_ok(dims) || dims.d < 8 || dims.d % 8 != 0) return DSPARK_ERR_SHAPE;
-  if (!aligned(h, 16) || !aligned(W1, 16) || !aligned(w, 16) || !aligned(T, 4) ||
-      !aligned(anchor, 4) || !aligned(tokens, 4) || !aligned(conf, 4))
-    return DSPARK_ERR_ALIGN;
+  const dspark_status st = check_confidence(dims, h, W1, w, T, anchor, tokens, conf);
+  if (st != DSPARK_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   ConfArgs a{dims.B, dims.gamma, dims.r, dims.d, h, W1, w, T, anchor, tokens, conf};
   if (timed(kConfidence, s, [&] { return launch_confidence(a, s); }) != hipSuccess)
@@ -384,21 +438,45 @@ dspark_status dspark_confidence(dspark_dims dims, const uint16_t* h, const uint1
 dspark_status dspark_plan(dspark_dims dims, const float* conf, const double* sps, int32_t sps_len,
                           int32_t mode, float* ring, int32_t round_index, int32_t* draft_len,
                           int32_t* row_offsets, double* stats, void* stream) {
-  if (!sps || !draft_len || !row_offsets) return DSPARK_ERR_NULL;
-  if (mode < DSPARK_PLAN_FULL_VERIFY || mode > DSPARK_PLAN_LAGGED_TOPK) return DSPARK_ERR_MODE;
-  if (mode != DSPARK_PLAN_FULL_VERIFY && !conf) return DSPARK_ERR_NULL;
-  if (mode == DSPARK_PLAN_LAGGED_TOPK && !ring) return DSPARK_ERR_MODE;
-  if (!plan_dims_ok(dims) || round_index < 0) return DSPARK_ERR_SHAPE;
-  if (static_cast<int64_t>(sps_len) < static_cast<int64_t>(dims.B) * (dims.gamma + 1) + 1)
-    return DSPARK_ERR_SPS;
-  if ((conf && !aligned(conf, 4)) || !aligned(sps, 8) || (ring && !aligned(ring, 4)) ||
-      !aligned(draft_len, 4) || !aligned(row_offsets, 4) || (stats && !aligned(stats, 8)))
-    return DSPARK_ERR_ALIGN;
+  const dspark_status st =
+      check_plan(dims, conf, sps, sps_len, mode, ring, round_index, draft_len, row_offsets, stats);
+  if (st != DSPARK_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   PlanArgs a{dims.B, dims.gamma, sps_len, mode, round_index, conf, sps, ring, draft_len,
              row_offsets, stats};
   if (timed(kPlan, s, [&] { return launch_plan(a, s); }) != hipSuccess) return DSPARK_ERR_HIP;
   return DSPARK_OK;
+}
+
+dspark_status dspark_markov_draft_plan(dspark_dims dims, const float* U, const uint16_t* W1,
+                                       const uint16_t* W2t, const int32_t* anchor,
+                                       const float* uniforms, const uint16_t* h,
+                                       const uint16_t* w, const float* T, const double* sps,
+                                       int32_t sps_len, int32_t mode, float* ring,
+                                       int32_t round_index, int32_t* tokens, float* q_tok,
+                                       double* lse, float* conf, int32_t* draft_len,
+                                       int32_t* row_offsets, double* stats, void* ws,
+                                       size_t ws_bytes, const dspark_draft_opts* opts,
+                                       void* stream) {
+  if (!U || !W2t || !uniforms || !q_tok || !lse || !ws) return DSPARK_ERR_NULL;
+  dspark_status st = check_confidence(dims, h, W1, w, T, anchor, tokens, conf);
+  if (st != DSPARK_OK) return st;
+  st = check_plan(dims, conf, sps, sps_len, mode, ring, round_index, draft_len, row_offsets, stats);
+  if (st != DSPARK_OK) return st;
+  float beta = 1.0f;
+  int greedy = 0;
+  if (!draft_options(opts, &beta, &greedy)) return DSPARK_ERR_OPTS;
+  if (!aligned(U, 16) || !aligned(W2t, 16) || !aligned(uniforms, 4) || !aligned(q_tok, 4) ||
+      !aligned(lse, 8) || !aligned(ws, kAlign))
+    return DSPARK_ERR_ALIGN;
+  if (ws_bytes < draft_ws(dims, nullptr, nullptr)) return DSPARK_ERR_WORKSPACE;
+  DraftWs dw;
+  draft_ws(dims, ws, &dw);
+  const RoundPlan rp{{dims.B, dims.gamma, dims.r, dims.d, h, W1, w, T, anchor, tokens, conf},
+                     {dims.B, dims.gamma, sps_len, mode, round_index, conf, sps, ring, draft_len,
+                      row_offsets, stats}};
+  return draft_loop(dims, U, W1, W2t, anchor, uniforms, tokens, q_tok, lse, nullptr, nullptr,
+                    dw.part, beta, greedy, nullptr, static_cast<hipStream_t>(stream), &rp);
 }
 
 dspark_status dspark_verify_opts(dspark_dims dims, const float* target,

@@ -19,6 +19,7 @@
 #include "launch.h"
 #include "dma.h"
 #include "tiles.h"
+#include "plan.h"
 
 namespace dspark {
 
@@ -276,12 +277,24 @@ struct DmaStep {
   static_assert((kStages - 1) * kCopies <= 63, "vmcnt range");
 };
 
-template <int KS, int NT>
-__global__ __launch_bounds__(kDmaThreads, 1) void markov_step_dma_kernel(StepArgs p) {
+// LDS of the pipelined step: the copy stages, the partials of kPartItems items, and the
+// group's previous tokens.
+template <int KS>
+struct DmaLds {
   using D = DmaStep<KS>;
-  __shared__ __attribute__((aligned(1024))) unsigned char stage[D::kStages * D::kStageBytes];
-  __shared__ float2 pbuf[D::kPartItems * kDmaTiles * kDmaGroup];
-  __shared__ __attribute__((aligned(256))) int32_t pid[kDmaGroup];   // previous tokens
+  __attribute__((aligned(1024))) unsigned char stage[D::kStages * D::kStageBytes];
+  float2 pbuf[D::kPartItems * kDmaTiles * kDmaGroup];
+  __attribute__((aligned(256))) int32_t pid[kDmaGroup];
+};
+
+// The pipelined step as run by workgroup `bid` of `nblk` step workgroups.
+template <int KS, int NT>
+__device__ __forceinline__ void markov_step_dma(const StepArgs& p, unsigned bid, unsigned nblk,
+                                                DmaLds<KS>& lds) {
+  using D = DmaStep<KS>;
+  unsigned char* stage = lds.stage;
+  float2* pbuf = lds.pbuf;
+  int32_t* pid = lds.pid;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, col = lane & 31;
@@ -289,8 +302,8 @@ __global__ __launch_bounds__(kDmaThreads, 1) void markov_step_dma_kernel(StepArg
   // Workgroup w of a group takes a contiguous range of items, so that the partials of one
   // request that it produces are contiguous in memory (full-line writes).
   const int ngroups = (p.B + kDmaGroup - 1) / kDmaGroup;
-  const int group = blockIdx.x % ngroups;
-  const int wg = blockIdx.x / ngroups, nwg = gridDim.x / ngroups;
+  const int group = bid % ngroups;
+  const int wg = bid / ngroups, nwg = nblk / ngroups;
   const int nitems = (p.V + D::kTok - 1) / D::kTok;
   const int item_lo = static_cast<int>(static_cast<int64_t>(nitems) * wg / nwg);
   const int n = static_cast<int>(static_cast<int64_t>(nitems) * (wg + 1) / nwg) - item_lo;
@@ -457,6 +470,29 @@ __global__ __launch_bounds__(kDmaThreads, 1) void markov_step_dma_kernel(StepArg
     }
   }
   flush(flushed, n);
+}
+
+template <int KS, int NT>
+__global__ __launch_bounds__(kDmaThreads, 1) void markov_step_dma_kernel(StepArgs p) {
+  __shared__ DmaLds<KS> lds;
+  markov_step_dma<KS, NT>(p, blockIdx.x, gridDim.x, lds);
+}
+
+// The last draft position's step with the verify planner beside it: workgroup 0 plans (its LDS
+// holds the planner's arrays in place of the copy stages), the others run the step. The plan
+// needs only the confidences, which need only the tokens before the last position, so it costs
+// the round no time of its own; no workgroup waits for another.
+constexpr int kFusedPlanMax = 4096;   // B * gamma limit of the fused planner
+
+template <int KS>
+__global__ __launch_bounds__(kDmaThreads, 1) void markov_step_plan_kernel(StepArgs p, PlanArgs pa) {
+  __shared__ DmaLds<KS> lds;
+  static_assert(sizeof(plan::Smem<kFusedPlanMax>) <= sizeof(lds.stage), "planner fits the stages");
+  if (blockIdx.x == 0) {
+    plan::run<kDmaThreads>(pa, *reinterpret_cast<plan::Smem<kFusedPlanMax>*>(lds.stage));
+    return;
+  }
+  markov_step_dma<KS, 1>(p, blockIdx.x - 1, gridDim.x - 1, lds);
 }
 
 // One 1024-thread workgroup per request. Thread t holds a contiguous range of at most 16 tile
@@ -676,6 +712,15 @@ static hipError_t launch_step_dma(const StepArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int KS>
+static hipError_t launch_step_plan(const StepArgs& a, const PlanArgs& pa, hipStream_t s) {
+  const int ngroups = (a.B + kDmaGroup - 1) / kDmaGroup;
+  const int per = (a.persistent_wgs - 1) / ngroups;
+  const int grid = 1 + (per > 0 ? per : 1) * ngroups;
+  launch_kernel(markov_step_plan_kernel<KS>, dim3(grid), dim3(kDmaThreads), 0, s, a, pa);
+  return hipGetLastError();
+}
+
 template <int KS, int NT>
 static hipError_t launch_step_prefetch(const StepArgs& a, hipStream_t s) {
   const int items = ((a.V + 4 * kTileTokens - 1) / (4 * kTileTokens)) *
@@ -744,6 +789,19 @@ static hipError_t launch_sample_ks(const SampleArgs& a, hipStream_t s) {
 
 hipError_t launch_markov_step(const StepArgs& a, int r, hipStream_t s) {
   DSPARK_DISPATCH_KS(r, launch_step_ks, a, s)
+}
+bool markov_step_plan_fits(const StepArgs& a, int r, int B, int gamma) {
+  return (r == 64 || r == 128 || r == 256) && a.e_terms == 1 && a.dbg == nullptr &&
+         (a.V & 3) == 0 && static_cast<int64_t>(B) * gamma <= kFusedPlanMax &&
+         a.persistent_wgs > (B + kDmaGroup - 1) / kDmaGroup;
+}
+hipError_t launch_markov_step_plan(const StepArgs& a, const PlanArgs& pa, int r, hipStream_t s) {
+  switch (r) {
+    case 64: return launch_step_plan<4>(a, pa, s);
+    case 128: return launch_step_plan<8>(a, pa, s);
+    case 256: return launch_step_plan<16>(a, pa, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 hipError_t launch_draft_sample(const SampleArgs& a, int r, hipStream_t s) {
   DSPARK_DISPATCH_KS(r, launch_sample_ks, a, s)

@@ -180,6 +180,10 @@ hipError_t launch_markov_step(const StepArgs& a, int r, hipStream_t s);
 hipError_t launch_draft_sample(const SampleArgs& a, int r, hipStream_t s);
 hipError_t launch_confidence(const ConfArgs& a, hipStream_t s);
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
+// The last position's draft step with the planner beside it (one launch); fits() says
+// whether this shape can take it (else the step and the plan are launched one after the other).
+bool markov_step_plan_fits(const StepArgs& a, int r, int B, int gamma);
+hipError_t launch_markov_step_plan(const StepArgs& a, const PlanArgs& pa, int r, hipStream_t s);
 hipError_t launch_target_stats(const VerifyArgs& a, hipStream_t s);
 hipError_t launch_accept(const VerifyArgs& a, hipStream_t s);
 hipError_t launch_residual_partials(const VerifyArgs& a, hipStream_t s);

@@ -163,6 +163,32 @@ def _py_kind(t):
     raise AssertionError(f"unmapped ctypes type {t!r}")
 
 
+def test_draft_plan_checks_without_gpu(lib):
+    """dspark_markov_draft_plan refuses what the draft, confidence and plan calls refuse, with
+    the same statuses, before anything is enqueued."""
+    dims = L.Dims(4, 3, 1000, 16, 64)
+    d, P = dims.c(), _p()
+    ws = L.workspace_bytes(dims, L.OP_DRAFT)
+    sl = 4 * 4 + 1
+
+    def call(dd=d, U=P, h=P, sps_len=sl, mode=1, ring=None, conf=P, ws_bytes=ws, opts=None):
+        return lib.dspark_markov_draft_plan(dd, U, P, P, P, P, h, P, P, P, sps_len, mode, ring, 0,
+                                            P, P, P, conf, P, P, None, P, ws_bytes, opts, None)
+
+    assert call(U=None) == 1                       # draft input
+    assert call(h=None) == 1                       # confidence input
+    assert call(conf=None) == 1                    # the confidences are an output here
+    assert call(dd=L.Dims(4, 3, 1000, 16, 12).c()) == 2   # d not a multiple of 8
+    assert call(dd=L.Dims(2000, 5, 1000, 16, 64).c(), sps_len=2000 * 6 + 1) == 2   # plan size
+    assert call(sps_len=sl - 1) == 5
+    assert call(mode=9) == 7
+    assert call(mode=3) == 7                       # LAGGED_TOPK without a ring
+    assert call(U=_p(260)) == 3
+    assert call(ws_bytes=ws - 1) == 4
+    bad_t = ctypes.byref(L.binding._CDraftOpts(0.0, 0))
+    assert call(opts=bad_t) == 8
+
+
 def test_binding_signatures_match_the_header(lib):
     """Every function the binding declares has the header's parameter count and kinds, so a
     marshalled call can never shift its arguments."""
