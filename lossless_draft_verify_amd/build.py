@@ -16,7 +16,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdspark.so")
 
-SOURCES = ["api.hip", "kernels_draft.hip", "kernels_plan.hip", "kernels_verify.hip", "kernels_rnn.hip"]
+SOURCES = ["api.hip", "kernels_draft.hip", "kernels_confidence.hip", "kernels_plan.hip",
+           "kernels_verify.hip", "kernels_rnn.hip"]
 
 # -ffp-contract=off: every kernel forms its floating-point results with the same operations, so
 # a sampler that recomputes a tile gets the streaming pass's bits. The packed-fp32 feature is

@@ -1,9 +1,9 @@
-// Markov-head draft and confidence head for gfx950.
+// Markov-head draft for gfx950.
 //
 // Sources: [V41] blog.javazero.top "DeepSeek-V4.1 模型结构（6）：解码，DSpark", "Markov head"
-// (eqs. (4), (5), the serial loop) and "confidence head" (eq. (7)); [ZDS] zdszero.github.io
-// spec_dspark, "在 SGLang 里" (sigmoid(raw / T) with per-position STS temperatures);
-// [CSDN] deepseek.csdn.net DSpark walk-through, 4.1-4.2.
+// (eqs. (4), (5), the serial loop); [ZDS] zdszero.github.io spec_dspark, "insight 一";
+// [CSDN] deepseek.csdn.net DSpark walk-through, 4.1-4.2. The last position's step can carry the
+// verify planner (plan.h) on one extra workgroup.
 //
 // One draft step k (the serial dependency: step k+1 needs every request's x_k):
 //   markov_step  streams W2t and the U slice of position k once, forms
@@ -657,50 +657,6 @@ __global__ __launch_bounds__(SampleCfg<KS>::kThreads) void draft_sample_kernel(S
   }
 }
 
-// Confidence head: one 256-thread block per (request, position). The hidden-state pieces go
-// out before the previous token is known; the embedding-row pieces follow it. Products in fp64,
-// summed per thread in piece order, then across the block in a fixed order.
-__global__ __launch_bounds__(kBlock) void confidence_kernel(ConfArgs p) {
-  __shared__ double red[kBlock / 64];
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int idx = blockIdx.x;
-  const int b = idx / p.gamma, k = idx % p.gamma;
-  const uint16_t* hrow = p.h + static_cast<size_t>(idx) * p.d;
-  constexpr int kBatch = 4;   // pieces of 8 per thread per batch: 8192 elements per batch
-  double acc = 0.0;
-  const int nh = p.d / 8;     // hidden-state pieces
-  for (int c0 = 0; c0 < nh; c0 += kBlock * kBatch) {
-    u16x8_t xv[kBatch], ww[kBatch];
-#pragma unroll
-    for (int q = 0; q < kBatch; ++q) {
-      const int c = min(c0 + q * kBlock + tid, nh - 1);
-      xv[q] = load_u16x8(hrow + 8 * c);
-      ww[q] = load_u16x8(p.w + 8 * c);
-    }
-#pragma unroll
-    for (int q = 0; q < kBatch; ++q) {
-      if (c0 + q * kBlock + tid >= nh) break;
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        acc += static_cast<double>(bf16_to_f32(xv[q][e]) * bf16_to_f32(ww[q][e]));   // exact
-    }
-  }
-  const int32_t prevtok = (k == 0) ? p.anchor[b] : p.tokens[static_cast<size_t>(b) * p.gamma + k - 1];
-  for (int c = tid; c < p.r / 8; c += kBlock) {
-    const u16x8_t ev = load_u16x8(p.W1 + static_cast<size_t>(prevtok) * p.r + 8 * c);
-    const u16x8_t we = load_u16x8(p.w + p.d + 8 * c);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc += static_cast<double>(bf16_to_f32(ev[e]) * bf16_to_f32(we[e]));
-  }
-  acc = wave_sum(acc);
-  if (lane == 0) red[wv] = acc;
-  __syncthreads();
-  if (tid == 0) {
-    const double z = (red[0] + red[1]) + (red[2] + red[3]);
-    p.conf[idx] = static_cast<float>(1.0 / (1.0 + exp(-z / static_cast<double>(p.T[k]))));
-  }
-}
-
 }  // namespace
 
 template <int KS, int NT>
@@ -805,10 +761,6 @@ hipError_t launch_markov_step_plan(const StepArgs& a, const PlanArgs& pa, int r,
 }
 hipError_t launch_draft_sample(const SampleArgs& a, int r, hipStream_t s) {
   DSPARK_DISPATCH_KS(r, launch_sample_ks, a, s)
-}
-hipError_t launch_confidence(const ConfArgs& a, hipStream_t s) {
-  launch_kernel(confidence_kernel, dim3(a.B * a.gamma), dim3(kBlock), 0, s, a);
-  return hipGetLastError();
 }
 
 }  // namespace dspark
