@@ -112,9 +112,23 @@ def test_draft_mismatch_rate_headline_vocab():
     c.check_rate()
 
 
-@pytest.mark.parametrize("name", ["tiny-b4-v1000-g3", "b128-v129280-g5"])
+CONF_CASES = {
+    "tiny-b4-v1000-g3": W.WORKLOADS["tiny-b4-v1000-g3"],
+    "b128-v129280-g5": W.WORKLOADS["b128-v129280-g5"],
+    # hidden sizes past one batch of loads (8192 elements): one piece in the second batch, and
+    # two full batches; r = 512 puts an embedding-row piece on every lane of wave 0
+    "b6-d8200-r512-g3": _custom("b6-d8200-r512-g3", seed_id=51, B=6, V=3000, r=512, d=8200,
+                                gamma=3),
+    "b5-d16384-r64-g2": _custom("b5-d16384-r64-g2", seed_id=52, B=5, V=2048, r=64, d=16384,
+                                gamma=2),
+    # the smallest hidden state: one piece, on thread 0 only
+    "b7-d8-r16-g4": _custom("b7-d8-r16-g4", seed_id=53, B=7, V=1000, r=16, d=8, gamma=4),
+}
+
+
+@pytest.mark.parametrize("name", list(CONF_CASES))
 def test_confidence_parity(name):
-    wl = W.WORKLOADS[name]
+    wl = CONF_CASES[name]
     log(f"[confidence] {name}")
     wts = W.weights(wl, DEV)
     inp = W.round_inputs(wl, 0, DEV, with_hidden=True)
