@@ -254,9 +254,12 @@ constexpr int kDmaThreads = 512;
 constexpr int kDmaGroup = 128;   // requests per group: 4 waves x 32 per tile
 constexpr int kDmaTiles = 2;     // 32-token tiles per item
 
-template <int KS>
+// TPW: 32-token tiles each wave computes per item (1: eight waves; 2: four waves, each taking
+// both tiles of its request quarter).
+template <int KS, int TPW = 1>
 struct DmaStep {
   static constexpr int r = 16 * KS;
+  static constexpr int kThreads = kDmaThreads / TPW;
   static constexpr int kTok = kDmaTiles * kTileTokens;              // 64 tokens per item
   static constexpr int kW2Chunks = 2 * KS;                          // 16-byte chunks per row
   static constexpr int kW2Bytes = kTok * kW2Chunks * 16;            // 64 W2t rows
@@ -265,7 +268,7 @@ struct DmaStep {
   static constexpr int kStageBytes = kW2Bytes + kUBytes;
   static constexpr int kStages = 2;
   static constexpr int kPartItems = 8;                              // items of partials in LDS
-  static constexpr int kWaves = kDmaThreads / 64;
+  static constexpr int kWaves = kThreads / 64;
   static constexpr int kW2Copies = kW2Bytes / 1024 / kWaves;        // copies per wave per item
   static constexpr int kUCopies = kUBytes / 1024 / kWaves;
   static constexpr int kCopies = kW2Copies + kUCopies;
@@ -288,17 +291,17 @@ struct DmaLds {
 };
 
 // The pipelined step as run by workgroup `bid` of `nblk` step workgroups.
-template <int KS, int NT>
+template <int KS, int NT, int TPW = 1>
 __device__ __forceinline__ void markov_step_dma(const StepArgs& p, unsigned bid, unsigned nblk,
                                                 DmaLds<KS>& lds) {
-  using D = DmaStep<KS>;
+  using D = DmaStep<KS, TPW>;
   unsigned char* stage = lds.stage;
   float2* pbuf = lds.pbuf;
   int32_t* pid = lds.pid;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, col = lane & 31;
-  const int sub = wave >> 2, rq = wave & 3;             // tile within the item, request quarter
+  const int sub = wave >> 2, rq = wave & 3;   // (first) tile within the item, request quarter
   // Workgroup w of a group takes a contiguous range of items, so that the partials of one
   // request that it produces are contiguous in memory (full-line writes).
   const int ngroups = (p.B + kDmaGroup - 1) / kDmaGroup;
@@ -312,18 +315,22 @@ __device__ __forceinline__ void markov_step_dma(const StepArgs& p, unsigned bid,
   const bool wave_active = group * kDmaGroup + 32 * rq < p.B;
 
   // Per-lane LDS offsets: k-step s of the A operand (W2t row 32 sub + col, chunk 2s + half) is
-  // at a_off[s % 8] + 256 (s / 8); U chunk 8 sub + 2g + half of row row_own at u_off[g].
+  // at a_off[s % 8] + 256 (s / 8), plus kTileA for the wave's second tile (the swizzle depends
+  // only on col); U chunk 8 tile + 2g + half of row row_own at u_off[tile - sub][g].
   const uint32_t stage_addr = lds_addr(stage);
-  uint32_t a_off[D::kAOffs], u_off[4];
+  constexpr uint32_t kTileA = 16 * kTileTokens * D::kW2Chunks;
+  uint32_t a_off[D::kAOffs], u_off[TPW][4];
   {
     const int wrow = 32 * sub + col;
 #pragma unroll
     for (int t = 0; t < D::kAOffs; ++t)
       a_off[t] = 16 * (wrow * D::kW2Chunks + ((2 * t + half) ^ (wrow & D::kW2Swz)));
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
-      u_off[g] = D::kW2Bytes +
-                 16 * (row_own * D::kUChunks + ((8 * sub + 2 * g + half) ^ (row_own & 15)));
+    for (int sb = 0; sb < TPW; ++sb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        u_off[sb][g] = D::kW2Bytes + 16 * (row_own * D::kUChunks +
+                                           ((8 * (sub + sb) + 2 * g + half) ^ (row_own & 15)));
   }
 
   // This wave's share of item j's copies into stage j % kStages. Rows past V or B are clamped
@@ -357,7 +364,7 @@ __device__ __forceinline__ void markov_step_dma(const StepArgs& p, unsigned bid,
   // consecutive threads take consecutive tiles of one request, so the stores fill whole lines.
   auto flush = [&](int j0, int j1) {
     const int per = (j1 - j0) * kDmaTiles;
-    for (int x = tid; x < kDmaGroup * per; x += kDmaThreads) {
+    for (int x = tid; x < kDmaGroup * per; x += D::kThreads) {
       const int row = x / per, tt = x % per;
       const int j = j0 + tt / kDmaTiles;
       const int b = group * kDmaGroup + row;
@@ -422,45 +429,95 @@ __device__ __forceinline__ void markov_step_dma(const StepArgs& p, unsigned bid,
     }
     asm volatile("s_barrier" ::: "memory");
 
-    const int tok0 = (item_lo + j) * D::kTok + sub * kTileTokens;
-    if (wave_active && tok0 < p.V) {
-      const unsigned char* base = stage + (j % D::kStages) * D::kStageBytes;
-      u16x8_t a[KS];
-#pragma unroll
-      for (int s = 0; s < KS; ++s)
-        a[s] = *reinterpret_cast<const u16x8_t*>(base + 256 * (s >> 3) + a_off[s % D::kAOffs]);
-      float4 uu[4];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) uu[g] = *reinterpret_cast<const float4*>(base + u_off[g]);
-      f32x16_t acc = {};
-#pragma unroll
-      for (int s = 0; s < NT * KS; ++s) acc = mfma_32x32x16(a[s % KS], e[s], acc);
-      // Epilogue: L = U + bias, tile max, fp32 sum of exp(L - max) (the order of the
-      // register-prefetch step kernel, so both give the same partials bit for bit).
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        acc[4 * g + 0] += uu[g].x;
-        acc[4 * g + 1] += uu[g].y;
-        acc[4 * g + 2] += uu[g].z;
-        acc[4 * g + 3] += uu[g].w;
+    if constexpr (TPW == 1) {
+      const int tok0 = (item_lo + j) * D::kTok + sub * kTileTokens;
+      if (wave_active && tok0 < p.V) {
+        const unsigned char* base = stage + (j % D::kStages) * D::kStageBytes;
+        u16x8_t a[KS];
+  #pragma unroll
+        for (int s = 0; s < KS; ++s)
+          a[s] = *reinterpret_cast<const u16x8_t*>(base + 256 * (s >> 3) + a_off[s % D::kAOffs]);
+        float4 uu[4];
+  #pragma unroll
+        for (int g = 0; g < 4; ++g) uu[g] = *reinterpret_cast<const float4*>(base + u_off[0][g]);
+        f32x16_t acc = {};
+  #pragma unroll
+        for (int s = 0; s < NT * KS; ++s) acc = mfma_32x32x16(a[s % KS], e[s], acc);
+        // Epilogue: L = U + bias, tile max, fp32 sum of exp(L - max) (the order of the
+        // register-prefetch step kernel, so both give the same partials bit for bit).
+  #pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          acc[4 * g + 0] += uu[g].x;
+          acc[4 * g + 1] += uu[g].y;
+          acc[4 * g + 2] += uu[g].z;
+          acc[4 * g + 3] += uu[g].w;
+        }
+        if (tok0 + kTileTokens > p.V) {
+  #pragma unroll
+          for (int jj = 0; jj < 16; ++jj)
+            if (tok0 + tile_token(jj, half) >= p.V) acc[jj] = kNegInf;
+        }
+        float L[16];   // the draft temperature scales the logits (beta = 1: unchanged)
+  #pragma unroll
+        for (int jj = 0; jj < 16; ++jj) L[jj] = acc[jj] * p.beta;
+        float m = max16(L);
+        m = fmaxf(m, other_half(m, half));
+        float t[16];
+  #pragma unroll
+        for (int jj = 0; jj < 16; ++jj) t[jj] = exp_term(L[jj] - m);
+        float sm = (m == kNegInf) ? 0.0f : sum16(t);
+        sm = sm + other_half(sm, half);
+        if (half == 0)
+          pbuf[((j % D::kPartItems) * kDmaTiles + sub) * kDmaGroup + row_own] = make_float2(m, sm);
       }
-      if (tok0 + kTileTokens > p.V) {
+    } else {
+      // Four waves: this wave's request quarter over each tile of the item in turn.
 #pragma unroll
-        for (int jj = 0; jj < 16; ++jj)
-          if (tok0 + tile_token(jj, half) >= p.V) acc[jj] = kNegInf;
+      for (int sb = 0; sb < TPW; ++sb) {
+        const int tile = sub + sb;
+        const int tok0 = (item_lo + j) * D::kTok + tile * kTileTokens;
+        if (wave_active && tok0 < p.V) {
+          const unsigned char* base = stage + (j % D::kStages) * D::kStageBytes;
+          u16x8_t a[KS];
+#pragma unroll
+          for (int s = 0; s < KS; ++s)
+            a[s] = *reinterpret_cast<const u16x8_t*>(base + kTileA * sb + 256 * (s >> 3) +
+                                                     a_off[s % D::kAOffs]);
+          float4 uu[4];
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            uu[g] = *reinterpret_cast<const float4*>(base + u_off[sb][g]);
+          f32x16_t acc = {};
+#pragma unroll
+          for (int s = 0; s < NT * KS; ++s) acc = mfma_32x32x16(a[s % KS], e[s], acc);
+          // Epilogue as in the eight-wave path (the same partials bit for bit).
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            acc[4 * g + 0] += uu[g].x;
+            acc[4 * g + 1] += uu[g].y;
+            acc[4 * g + 2] += uu[g].z;
+            acc[4 * g + 3] += uu[g].w;
+          }
+          if (tok0 + kTileTokens > p.V) {
+#pragma unroll
+            for (int jj = 0; jj < 16; ++jj)
+              if (tok0 + tile_token(jj, half) >= p.V) acc[jj] = kNegInf;
+          }
+          float L[16];
+#pragma unroll
+          for (int jj = 0; jj < 16; ++jj) L[jj] = acc[jj] * p.beta;
+          float m = max16(L);
+          m = fmaxf(m, other_half(m, half));
+          float t[16];
+#pragma unroll
+          for (int jj = 0; jj < 16; ++jj) t[jj] = exp_term(L[jj] - m);
+          float sm = (m == kNegInf) ? 0.0f : sum16(t);
+          sm = sm + other_half(sm, half);
+          if (half == 0)
+            pbuf[((j % D::kPartItems) * kDmaTiles + tile) * kDmaGroup + row_own] =
+                make_float2(m, sm);
+        }
       }
-      float L[16];   // the draft temperature scales the logits (beta = 1: unchanged)
-#pragma unroll
-      for (int jj = 0; jj < 16; ++jj) L[jj] = acc[jj] * p.beta;
-      float m = max16(L);
-      m = fmaxf(m, other_half(m, half));
-      float t[16];
-#pragma unroll
-      for (int jj = 0; jj < 16; ++jj) t[jj] = exp_term(L[jj] - m);
-      float sm = (m == kNegInf) ? 0.0f : sum16(t);
-      sm = sm + other_half(sm, half);
-      if (half == 0)
-        pbuf[((j % D::kPartItems) * kDmaTiles + sub) * kDmaGroup + row_own] = make_float2(m, sm);
     }
     lds_barrier();   // stage j % kStages is free for item j + kStages
     if ((j + 1) % D::kPartItems == 0 && j + 1 < n) {
@@ -476,6 +533,15 @@ template <int KS, int NT>
 __global__ __launch_bounds__(kDmaThreads, 1) void markov_step_dma_kernel(StepArgs p) {
   __shared__ DmaLds<KS> lds;
   markov_step_dma<KS, NT>(p, blockIdx.x, gridDim.x, lds);
+}
+
+// The pipelined step with four waves (one per SIMD), each computing both token tiles of an item
+// for its request quarter: 512 registers a lane leave room for the RNN head's three-term bias
+// rows at r = 256 (192 registers), which two waves per SIMD cannot hold.
+template <int KS, int NT>
+__global__ __launch_bounds__(kDmaThreads / 2, 1) void markov_step_dma_wave4_kernel(StepArgs p) {
+  __shared__ DmaLds<KS> lds;
+  markov_step_dma<KS, NT, 2>(p, blockIdx.x, gridDim.x, lds);
 }
 
 // The last draft position's step with the verify planner beside it: workgroup 0 plans (its LDS
@@ -668,6 +734,15 @@ static hipError_t launch_step_dma(const StepArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int KS, int NT>
+static hipError_t launch_step_dma_wave4(const StepArgs& a, hipStream_t s) {
+  const int ngroups = (a.B + kDmaGroup - 1) / kDmaGroup;
+  const int per = a.persistent_wgs / ngroups;
+  const int grid = (per > 0 ? per : 1) * ngroups;
+  launch_kernel(markov_step_dma_wave4_kernel<KS, NT>, dim3(grid), dim3(kDmaThreads / 2), 0, s, a);
+  return hipGetLastError();
+}
+
 template <int KS>
 static hipError_t launch_step_plan(const StepArgs& a, const PlanArgs& pa, hipStream_t s) {
   const int ngroups = (a.B + kDmaGroup - 1) / kDmaGroup;
@@ -702,15 +777,17 @@ static hipError_t launch_step_kind(const StepArgs& a, hipStream_t s) {
   return launch_step_prefetch<KS, NT>(a, s);
 }
 // Bias rows of three bf16 terms (the RNN head) are built for r <= 256; the pipelined step holds
-// them in registers up to r = 128 (at r = 256 they take the register-prefetch kernel, whose
-// LDS holds them).
+// them in registers, with eight waves up to r = 128 and with four (one per SIMD) at r = 256.
 template <int KS>
 static hipError_t launch_step_ks(const StepArgs& a, hipStream_t s) {
   if (a.e_terms == 1) return launch_step_kind<KS, 1>(a, s);
   if constexpr (KS <= 8) {
     if (a.e_terms == kRnnTerms) return launch_step_kind<KS, kRnnTerms>(a, s);
   } else if constexpr (KS == 16) {
-    if (a.e_terms == kRnnTerms) return launch_step_prefetch<KS, kRnnTerms>(a, s);
+    if (a.e_terms == kRnnTerms) {
+      if (a.dbg == nullptr && (a.V & 3) == 0) return launch_step_dma_wave4<KS, kRnnTerms>(a, s);
+      return launch_step_prefetch<KS, kRnnTerms>(a, s);
+    }
   }
   return hipErrorInvalidValue;
 }
