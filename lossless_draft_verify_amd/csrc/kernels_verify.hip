@@ -410,9 +410,12 @@ constexpr int kResThreads = 512;
 constexpr int kResGroup = 64;
 constexpr int kResTiles = 2;
 
-template <int KS>
+// PW: halves of a tile's epilogue each wave takes (1: eight waves, two per tile; 2: four waves,
+// one per tile and SIMD, with room for the RNN head's three-term bias rows at r = 256).
+template <int KS, int PW = 1>
 struct ResStep {
   static constexpr int r = 16 * KS;
+  static constexpr int kThreads = kResThreads / PW;
   static constexpr int kTok = kResTiles * kTileTokens;              // 64 tokens per item
   static constexpr int kW2Chunks = 2 * KS;
   static constexpr int kW2Bytes = kTok * kW2Chunks * 16;
@@ -421,7 +424,7 @@ struct ResStep {
   static constexpr int kStageBytes = kW2Bytes + 2 * kRowBytes;      // W2t | U rows | target rows
   static constexpr int kStages = 2;
   static constexpr int kPartItems = 4;
-  static constexpr int kWaves = kResThreads / 64;
+  static constexpr int kWaves = kThreads / 64;
   static constexpr int kW2Copies = kW2Bytes / 1024 / kWaves;
   static constexpr int kRowCopies = kRowBytes / 1024 / kWaves;
   static constexpr int kCopies = kW2Copies + 2 * kRowCopies;
@@ -433,16 +436,17 @@ struct ResStep {
   static_assert(kResGroup * kW2Chunks * 16 <= kStageBytes, "embedding rows fit in one stage");
 };
 
-template <int KS, bool Greedy, int NT>
-__global__ __launch_bounds__(kResThreads, 1) void residual_dma_kernel(VerifyArgs p) {
-  using D = ResStep<KS>;
+template <int KS, bool Greedy, int NT, int PW>
+__device__ __forceinline__ void residual_dma(const VerifyArgs& p) {
+  using D = ResStep<KS, PW>;
   __shared__ __attribute__((aligned(1024))) unsigned char stage[D::kStages * D::kStageBytes];
   __shared__ double2 pbuf[D::kPartItems * kResTiles * 2 * kResGroup];   // (sum w, sum min)
   __shared__ ResRec rec[kResGroup];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, col = lane & 31;
-  const int sub = (wave >> 1) & 1, rq = wave & 1, part = wave >> 2;
+  const int sub = (wave >> 1) & 1, rq = wave & 1;
+  const int part = (PW == 1) ? (wave >> 2) : 0;   // the wave's (first) half of the tile
   const uint32_t part_sel = part ? kPickB : kPickA;
   const int nres = *p.ws.rcount;
   if (nres <= 0) return;
@@ -473,18 +477,20 @@ __global__ __launch_bounds__(kResThreads, 1) void residual_dma_kernel(VerifyArgs
   auto wait_item = [&]() { wait_copies_upto<D::kW2Copies, 2, D::kRowCopies>(nrow_w); };
 
   const uint32_t stage_addr = lds_addr(stage);
-  uint32_t a_off[D::kAOffs], u_off[2];
+  uint32_t a_off[D::kAOffs], u_off[PW][2];
   {
     const int wrow = 32 * sub + col;
 #pragma unroll
     for (int t = 0; t < D::kAOffs; ++t)
       a_off[t] = 16 * (wrow * D::kW2Chunks + ((2 * t + half) ^ (wrow & D::kW2Swz)));
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int g = 2 * part + h;
-      u_off[h] = D::kW2Bytes +
-                 16 * (row_own * D::kRowChunks + ((8 * sub + 2 * g + half) ^ (row_own & 15)));
-    }
+    for (int pp = 0; pp < PW; ++pp)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int g = 2 * (part + pp) + h;
+        u_off[pp][h] = D::kW2Bytes + 16 * (row_own * D::kRowChunks +
+                                           ((8 * sub + 2 * g + half) ^ (row_own & 15)));
+      }
   }
 
   // This wave's share of item j's copies. Positions past V are clamped (masked later).
@@ -520,7 +526,7 @@ __global__ __launch_bounds__(kResThreads, 1) void residual_dma_kernel(VerifyArgs
   // consecutive tiles of one request.
   auto flush = [&](int j0, int j1) {
     const int per = (j1 - j0) * kResTiles;
-    for (int x = tid; x < gcount * per; x += kResThreads) {
+    for (int x = tid; x < gcount * per; x += D::kThreads) {
       const int row = x / per, tt = x % per;
       const int j = j0 + tt / kResTiles;
       const int tile = (item_lo + j0) * kResTiles + tt;
@@ -587,50 +593,58 @@ __global__ __launch_bounds__(kResThreads, 1) void residual_dma_kernel(VerifyArgs
 #pragma unroll
       for (int s = 0; s < KS; ++s)
         a[s] = *reinterpret_cast<const u16x8_t*>(base + 256 * (s >> 3) + a_off[s % D::kAOffs]);
-      float4 uu[2], tt[2];
+      float4 uu[PW][2], tt[PW][2];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        uu[h] = *reinterpret_cast<const float4*>(base + u_off[h]);
-        tt[h] = *reinterpret_cast<const float4*>(base + u_off[h] + D::kRowBytes);
-      }
+      for (int pp = 0; pp < PW; ++pp)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          uu[pp][h] = *reinterpret_cast<const float4*>(base + u_off[pp][h]);
+          tt[pp][h] = *reinterpret_cast<const float4*>(base + u_off[pp][h] + D::kRowBytes);
+        }
       f32x16_t acc = {};
 #pragma unroll
       for (int s = 0; s < NT * KS; ++s) acc = mfma_32x32x16(a[s % KS], e[s], acc);
-      // This wave's half of the tile (accumulator slot groups 2 part, 2 part + 1), in token order.
-      // Its eight slots are taken by byte permutes (a select here becomes a register-indexing
-      // sequence per term), and only a tile that reaches past V checks its tokens.
-      float Lh[8];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) Lh[q] = pick(acc[q], acc[8 + q], part_sel);
-      double W = 0.0, O = 0.0;
-      auto half_tile = [&](auto checked) {
+      for (int pp = 0; pp < PW; ++pp) {
+        const int pt = part + pp;
+        // This half of the tile (accumulator slot groups 2 pt, 2 pt + 1), in token order. With
+        // eight waves the half is a run-time choice and its slots are taken by byte permutes (a
+        // select here becomes a register-indexing sequence per term); only a tile that reaches
+        // past V checks its tokens.
+        float Lh[8];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int v = tok0 + 8 * (2 * part + h) + 4 * half;
-          const float u4[4] = {uu[h].x, uu[h].y, uu[h].z, uu[h].w};
-          const float t4[4] = {tt[h].x, tt[h].y, tt[h].z, tt[h].w};
+        for (int q = 0; q < 8; ++q)
+          Lh[q] = (PW == 1) ? pick(acc[q], acc[8 + q], part_sel) : acc[8 * pp + q];
+        double W = 0.0, O = 0.0;
+        auto half_tile = [&](auto checked) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            if (!decltype(checked)::value || v + i < p.V) {
-              double w, o;
-              residual_pair(draft_prob_t<Greedy>(u4[i] + Lh[4 * h + i], p.beta, lse_d,
-                                                 v + i == xtok),
-                            t4[i], lse_t, w, o);
-              W += w;
-              O += o;
+          for (int h = 0; h < 2; ++h) {
+            const int v = tok0 + 8 * (2 * pt + h) + 4 * half;
+            const float u4[4] = {uu[pp][h].x, uu[pp][h].y, uu[pp][h].z, uu[pp][h].w};
+            const float t4[4] = {tt[pp][h].x, tt[pp][h].y, tt[pp][h].z, tt[pp][h].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              if (!decltype(checked)::value || v + i < p.V) {
+                double w, o;
+                residual_pair(draft_prob_t<Greedy>(u4[i] + Lh[4 * h + i], p.beta, lse_d,
+                                                   v + i == xtok),
+                              t4[i], lse_t, w, o);
+                W += w;
+                O += o;
+              }
             }
           }
-        }
-      };
-      if (tok0 + kTileTokens <= p.V)
-        half_tile(std::false_type{});
-      else
-        half_tile(std::true_type{});
-      W = W + other_half(W, half);
-      O = O + other_half(O, half);
-      if (half == 0 && row_own < gcount)
-        pbuf[(((j % D::kPartItems) * kResTiles + sub) * 2 + part) * kResGroup + row_own] =
-            make_double2(W, O);
+        };
+        if (tok0 + kTileTokens <= p.V)
+          half_tile(std::false_type{});
+        else
+          half_tile(std::true_type{});
+        W = W + other_half(W, half);
+        O = O + other_half(O, half);
+        if (half == 0 && row_own < gcount)
+          pbuf[(((j % D::kPartItems) * kResTiles + sub) * 2 + pt) * kResGroup + row_own] =
+              make_double2(W, O);
+      }
     }
     lds_barrier();
     if ((j + 1) % D::kPartItems == 0 && j + 1 < n) {
@@ -640,6 +654,19 @@ __global__ __launch_bounds__(kResThreads, 1) void residual_dma_kernel(VerifyArgs
     }
   }
   flush(flushed, n);
+}
+
+template <int KS, bool Greedy, int NT>
+__global__ __launch_bounds__(kResThreads, 1) void residual_dma_kernel(VerifyArgs p) {
+  residual_dma<KS, Greedy, NT, 1>(p);
+}
+
+// Four waves, one per tile and SIMD, each taking both halves of its tile's epilogue in turn (the
+// same half sums as the eight-wave kernel): 512 registers a lane hold the RNN head's three-term
+// bias rows at r = 256.
+template <int KS, bool Greedy, int NT>
+__global__ __launch_bounds__(kResThreads / 2, 1) void residual_dma_wave4_kernel(VerifyArgs p) {
+  residual_dma<KS, Greedy, NT, 2>(p);
 }
 
 template <int KS, int NT>
@@ -827,14 +854,18 @@ hipError_t launch_accept(const VerifyArgs& a, hipStream_t s) {
 template <int KS, bool Greedy, int NT>
 static hipError_t launch_resid_kind(const VerifyArgs& a, hipStream_t s) {
   // The pipelined pass copies 16-byte row chunks (V % 4 == 0) and 1-2 KB of W2t per wave
-  // (128 <= r <= 256) and holds a wave's bias rows in registers (the three terms of the RNN
-  // head only up to r = 128); other shapes take the register-load kernel.
-  if constexpr (KS >= 8 && KS <= 16 && (NT == 1 || KS <= 8)) {
+  // (128 <= r <= 256) and holds a wave's bias rows in registers: eight waves, or four for the
+  // three terms of the RNN head at r = 256; other shapes take the register-load kernel.
+  if constexpr (KS >= 8 && KS <= 16) {
     if ((a.V & 3) == 0) {
       const int groups = (a.B + kResGroup - 1) / kResGroup;
       const int grid = a.persistent_wgs > groups ? a.persistent_wgs : groups;
-      launch_kernel(residual_dma_kernel<KS, Greedy, NT>, dim3(grid), dim3(kResThreads), 0,
-                         s, a);
+      if constexpr (NT == 1 || KS <= 8) {
+        launch_kernel(residual_dma_kernel<KS, Greedy, NT>, dim3(grid), dim3(kResThreads), 0, s, a);
+      } else {
+        launch_kernel(residual_dma_wave4_kernel<KS, Greedy, NT>, dim3(grid), dim3(kResThreads / 2),
+                      0, s, a);
+      }
       return hipGetLastError();
     }
   }
