@@ -166,9 +166,9 @@ def main():
     ap.add_argument("--head", choices=["markov", "rnn"], default="markov",
                     help="serial draft head: the Markov head (eq. 5) or the RNN head (eq. 6)")
     ap.add_argument("--separate-plan", action="store_true",
-                    help="Markov head: launch the confidence head and the planner as calls of "
-                         "their own after the draft (by default one call runs the plan beside "
-                         "the last draft step)")
+                    help="launch the confidence head and the planner as calls of their own "
+                         "after the draft (by default one call runs the plan beside the last "
+                         "draft step)")
     ap.add_argument("--greedy", action="store_true",
                     help="greedy draft (first maximal logit; the verify's residual is p_t "
                          "without the drafted token)")
@@ -225,10 +225,16 @@ def main():
                  **opts)
 
     def round_rnn(s):
-        L.rnn_draft(d, s.U, wts["W1"], wts["W2t"], wts["Wgco"], s.h, s.anchor, s.uniforms,
-                    tokens=tok, q=q, lse=lse, e_rows=e_rows, ws=ws_d, **opts)
-        L.confidence(d, s.h, wts["W1"], wts["w"], s.T, s.anchor, tok, conf=conf)
-        L.plan(d, conf, s.sps, wl.mode, draft_len=dl, row_offsets=ro, stats=st)
+        if args.separate_plan:
+            L.rnn_draft(d, s.U, wts["W1"], wts["W2t"], wts["Wgco"], s.h, s.anchor, s.uniforms,
+                        tokens=tok, q=q, lse=lse, e_rows=e_rows, ws=ws_d, **opts)
+            L.confidence(d, s.h, wts["W1"], wts["w"], s.T, s.anchor, tok, conf=conf)
+            L.plan(d, conf, s.sps, wl.mode, draft_len=dl, row_offsets=ro, stats=st)
+        else:
+            L.rnn_draft_plan(d, s.U, wts["W1"], wts["W2t"], wts["Wgco"], s.h, s.anchor, s.uniforms,
+                             wts["w"], s.T, s.sps, wl.mode, tokens=tok, q=q, lse=lse,
+                             e_rows=e_rows, conf=conf, draft_len=dl, row_offsets=ro, stats=st,
+                             ws=ws_d, **opts)
         L.rnn_verify(d, s.target, ro, dl, s.U, wts["W2t"], e_rows, tok, q, lse, s.uniforms,
                      accept_len=al, next_token=nt, beta_emit=be, flags=fl, ws=ws_v, **opts)
 
@@ -368,7 +374,7 @@ def main():
                    "draft": ("greedy" if args.greedy
                              else f"sampled at temperature {args.temperature:g}"),
                    "head": args.head,
-                   "plan_launch": ("own call" if args.separate_plan or args.head == "rnn"
+                   "plan_launch": ("own call" if args.separate_plan
                                    else "beside the last draft step")},
         "round_us": round_us,
         "graph_rounds_per_s": (round(args.steps / elapsed_graph, 2)

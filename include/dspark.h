@@ -8,8 +8,8 @@
  *   dspark_verify        lossless rejection-sampling verify, residual resample, bonus token
  *   dspark_markov_draft_opts, dspark_verify_opts   the same with a draft temperature or greedy
  *   dspark_rnn_draft, dspark_rnn_verify   the draft and verify with the RNN head of eq. (6)
- *   dspark_markov_draft_plan   draft, confidence and plan of a round in one call, the plan
- *                        computed beside the last position's draft step
+ *   dspark_markov_draft_plan, dspark_rnn_draft_plan   draft, confidence and plan of a round
+ *                        in one call, the plan computed beside the last position's draft step
  *
  * Sources (cited below by tag; each gives the page title and the section or equation):
  *   [V41]  blog.javazero.top, "DeepSeek-V4.1 模型结构（6）：解码，DSpark"
@@ -60,7 +60,7 @@ extern "C" {
 /* Problem sizes. B requests, gamma draft positions, V vocabulary, r Markov rank, d hidden size
  * (d is read only by dspark_confidence). Supported: B >= 1, 1 <= gamma <= 255, 2 <= V <= 2^19,
  * r in {16, 32, 64, 128, 256, 512}, d % 8 == 0, B * (gamma + 1) <= 65535, and for
- * dspark_plan and dspark_markov_draft_plan B * gamma <= 8192. */
+ * dspark_plan and the draft-and-plan calls B * gamma <= 8192. */
 typedef struct dspark_dims {
   int32_t B;
   int32_t gamma;
@@ -337,6 +337,23 @@ DSPARK_API dspark_status dspark_rnn_verify(dspark_dims dims, const float* target
                                            int32_t* next_token, float* beta_emit, uint32_t* flags,
                                            void* ws, size_t ws_bytes,
                                            const dspark_draft_opts* opts, void* stream);
+
+/*
+ * The draft side of one round with the RNN head in a single call: dspark_rnn_draft (without
+ * logits_dbg or force_tokens), dspark_confidence and dspark_plan, with their arguments, checks
+ * and outputs, in the order and with the planner placement of dspark_markov_draft_plan (the
+ * planner beside the last position's step for r in {64, 128, 256} and V % 4 == 0,
+ * B * gamma <= 4096). Passages: those of the three calls. The results are bit-identical to the
+ * three separate calls.
+ *   ws, ws_bytes   the RNN draft workspace (dspark_workspace_bytes(dims, DSPARK_OP_RNN_DRAFT))
+ */
+DSPARK_API dspark_status dspark_rnn_draft_plan(
+    dspark_dims dims, const float* U, const uint16_t* W1, const uint16_t* W2t,
+    const uint16_t* Wgco, const uint16_t* h, const int32_t* anchor, const float* uniforms,
+    const uint16_t* w, const float* T, const double* sps, int32_t sps_len, int32_t mode,
+    float* ring, int32_t round_index, int32_t* tokens, float* q_tok, double* lse, float* e_rows,
+    float* conf, int32_t* draft_len, int32_t* row_offsets, double* stats, void* ws,
+    size_t ws_bytes, const dspark_draft_opts* opts, void* stream);
 
 /*
  * Kernel timing with HIP events (measurement support; not part of the method).

@@ -19,7 +19,7 @@ __all__ = [
     "OP_DRAFT", "OP_CONFIDENCE", "OP_PLAN", "OP_VERIFY", "OP_RNN_DRAFT", "OP_RNN_VERIFY",
     "FLAG_NONFINITE", "FLAG_ZERO_RESIDUAL", "library_path", "load_library", "workspace_bytes",
     "workspace", "markov_draft", "confidence", "plan", "markov_draft_plan", "verify",
-    "rnn_draft", "rnn_verify",
+    "rnn_draft", "rnn_verify", "rnn_draft_plan",
     "profile_begin", "profile_end", "version",
 ]
 
@@ -98,6 +98,10 @@ def load_library():
         lib.dspark_markov_draft_plan.argtypes = (
             [_CDims] + [_P] * 9 + [ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int32] +
             [_P] * 7 + [_P, ctypes.c_size_t, _P, _P])
+        lib.dspark_rnn_draft_plan.restype = ctypes.c_int32
+        lib.dspark_rnn_draft_plan.argtypes = (
+            [_CDims] + [_P] * 10 + [ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int32] +
+            [_P] * 8 + [_P, ctypes.c_size_t, _P, _P])
         lib.dspark_verify.restype = ctypes.c_int32
         lib.dspark_verify.argtypes = [_CDims] + [_P] * 15 + [_P, ctypes.c_size_t, _P]
         lib.dspark_verify_opts.restype = ctypes.c_int32
@@ -354,3 +358,41 @@ def rnn_verify(dims: Dims, target, row_offsets, draft_len, U, W2t, e_rows, token
         _ptr(ws, torch.uint8, None, "ws"), ws.numel(), _opts(temperature, greedy), _stream(stream))
     _check(st, "dspark_rnn_verify")
     return accept_len, next_token, beta_emit, flags
+
+
+def rnn_draft_plan(dims: Dims, U, W1, W2t, Wgco, h, anchor, uniforms, w, T, sps, mode: int, *,
+                   ring=None, round_index: int = 0, tokens=None, q=None, lse=None, e_rows=None,
+                   conf=None, draft_len=None, row_offsets=None, stats=None, ws=None,
+                   temperature: float = 1.0, greedy: bool = False, stream=None):
+    """RNN-head draft, confidence head and plan of a round in one call (dspark_rnn_draft_plan).
+    Returns (tokens, q, lse, e_rows, conf, draft_len, row_offsets, stats)."""
+    B, g, V, r, d = dims.B, dims.gamma, dims.V, dims.r, dims.d
+    dev = U.device
+    tokens = tokens if tokens is not None else torch.empty((B, g), dtype=torch.int32, device=dev)
+    q = q if q is not None else torch.empty((B, g), dtype=torch.float32, device=dev)
+    lse = lse if lse is not None else torch.empty((B, g), dtype=torch.float64, device=dev)
+    e_rows = e_rows if e_rows is not None else torch.empty((B, g, r), dtype=torch.float32, device=dev)
+    conf = conf if conf is not None else torch.empty((B, g), dtype=torch.float32, device=dev)
+    draft_len = draft_len if draft_len is not None else torch.empty(B, dtype=torch.int32, device=dev)
+    row_offsets = (row_offsets if row_offsets is not None
+                   else torch.empty(B + 1, dtype=torch.int32, device=dev))
+    stats = stats if stats is not None else torch.empty(4, dtype=torch.float64, device=dev)
+    ws = ws if ws is not None else workspace(dims, OP_RNN_DRAFT, dev)
+    st = load_library().dspark_rnn_draft_plan(
+        dims.c(), _ptr(U, torch.float32, (B, g, V), "U"), _ptr(W1, torch.bfloat16, (V, r), "W1"),
+        _ptr(W2t, torch.bfloat16, (V, r), "W2t"),
+        _ptr(Wgco, torch.bfloat16, (3 * r, 2 * r + d), "Wgco"),
+        _ptr(h, torch.bfloat16, (B, g, d), "h"), _ptr(anchor, torch.int32, (B,), "anchor"),
+        _ptr(uniforms, torch.float32, (B, g + 1, 3), "uniforms"),
+        _ptr(w, torch.bfloat16, (d + r,), "w"), _ptr(T, torch.float32, (g,), "T"),
+        _ptr(sps, torch.float64, None, "sps"), int(sps.numel()), int(mode),
+        _ptr(ring, torch.float32, (2, B, g), "ring"), int(round_index),
+        _ptr(tokens, torch.int32, (B, g), "tokens"), _ptr(q, torch.float32, (B, g), "q"),
+        _ptr(lse, torch.float64, (B, g), "lse"), _ptr(e_rows, torch.float32, (B, g, r), "e_rows"),
+        _ptr(conf, torch.float32, (B, g), "conf"),
+        _ptr(draft_len, torch.int32, (B,), "draft_len"),
+        _ptr(row_offsets, torch.int32, (B + 1,), "row_offsets"),
+        _ptr(stats, torch.float64, (4,), "stats"), _ptr(ws, torch.uint8, None, "ws"), ws.numel(),
+        _opts(temperature, greedy), _stream(stream))
+    _check(st, "dspark_rnn_draft_plan")
+    return tokens, q, lse, e_rows, conf, draft_len, row_offsets, stats

@@ -414,6 +414,37 @@ dspark_status dspark_rnn_draft(dspark_dims dims, const float* U, const uint16_t*
                     static_cast<hipStream_t>(stream));
 }
 
+dspark_status dspark_rnn_draft_plan(dspark_dims dims, const float* U, const uint16_t* W1,
+                                    const uint16_t* W2t, const uint16_t* Wgco, const uint16_t* h,
+                                    const int32_t* anchor, const float* uniforms,
+                                    const uint16_t* w, const float* T, const double* sps,
+                                    int32_t sps_len, int32_t mode, float* ring,
+                                    int32_t round_index, int32_t* tokens, float* q_tok,
+                                    double* lse, float* e_rows, float* conf, int32_t* draft_len,
+                                    int32_t* row_offsets, double* stats, void* ws,
+                                    size_t ws_bytes, const dspark_draft_opts* opts, void* stream) {
+  if (!U || !W2t || !Wgco || !uniforms || !q_tok || !lse || !e_rows || !ws) return DSPARK_ERR_NULL;
+  dspark_status st = check_confidence(dims, h, W1, w, T, anchor, tokens, conf);
+  if (st != DSPARK_OK) return st;
+  st = check_plan(dims, conf, sps, sps_len, mode, ring, round_index, draft_len, row_offsets, stats);
+  if (st != DSPARK_OK) return st;
+  float beta = 1.0f;
+  int greedy = 0;
+  if (!draft_options(opts, &beta, &greedy)) return DSPARK_ERR_OPTS;
+  if (!rnn_dims_ok(dims)) return DSPARK_ERR_SHAPE;
+  if (!aligned(U, 16) || !aligned(W2t, 16) || !aligned(Wgco, 16) || !aligned(uniforms, 4) ||
+      !aligned(q_tok, 4) || !aligned(lse, 8) || !aligned(e_rows, 4) || !aligned(ws, kAlign))
+    return DSPARK_ERR_ALIGN;
+  if (ws_bytes < rnn_draft_ws(dims, nullptr, nullptr)) return DSPARK_ERR_WORKSPACE;
+  RnnDraftInputs rnn{Wgco, h, e_rows, {}};
+  rnn_draft_ws(dims, ws, &rnn.w);
+  const RoundPlan rp{{dims.B, dims.gamma, dims.r, dims.d, h, W1, w, T, anchor, tokens, conf},
+                     {dims.B, dims.gamma, sps_len, mode, round_index, conf, sps, ring, draft_len,
+                      row_offsets, stats}};
+  return draft_loop(dims, U, W1, W2t, anchor, uniforms, tokens, q_tok, lse, nullptr, nullptr,
+                    rnn.w.draft.part, beta, greedy, &rnn, static_cast<hipStream_t>(stream), &rp);
+}
+
 dspark_status dspark_markov_draft(dspark_dims dims, const float* U, const uint16_t* W1,
                                   const uint16_t* W2t, const int32_t* anchor,
                                   const float* uniforms, int32_t* tokens, float* q_tok,

@@ -550,15 +550,16 @@ __global__ __launch_bounds__(kDmaThreads / 2, 1) void markov_step_dma_wave4_kern
 // the round no time of its own; no workgroup waits for another.
 constexpr int kFusedPlanMax = 4096;   // B * gamma limit of the fused planner
 
-template <int KS>
-__global__ __launch_bounds__(kDmaThreads, 1) void markov_step_plan_kernel(StepArgs p, PlanArgs pa) {
+template <int KS, int NT, int TPW>
+__global__ __launch_bounds__(kDmaThreads / TPW, 1) void markov_step_plan_kernel(StepArgs p,
+                                                                               PlanArgs pa) {
   __shared__ DmaLds<KS> lds;
   static_assert(sizeof(plan::Smem<kFusedPlanMax>) <= sizeof(lds.stage), "planner fits the stages");
   if (blockIdx.x == 0) {
-    plan::run<kDmaThreads>(pa, *reinterpret_cast<plan::Smem<kFusedPlanMax>*>(lds.stage));
+    plan::run<kDmaThreads / TPW>(pa, *reinterpret_cast<plan::Smem<kFusedPlanMax>*>(lds.stage));
     return;
   }
-  markov_step_dma<KS, 1>(p, blockIdx.x - 1, gridDim.x - 1, lds);
+  markov_step_dma<KS, NT, TPW>(p, blockIdx.x - 1, gridDim.x - 1, lds);
 }
 
 // One 1024-thread workgroup per request. Thread t holds a contiguous range of at most 16 tile
@@ -743,12 +744,13 @@ static hipError_t launch_step_dma_wave4(const StepArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int KS>
+template <int KS, int NT, int TPW>
 static hipError_t launch_step_plan(const StepArgs& a, const PlanArgs& pa, hipStream_t s) {
   const int ngroups = (a.B + kDmaGroup - 1) / kDmaGroup;
   const int per = (a.persistent_wgs - 1) / ngroups;
   const int grid = 1 + (per > 0 ? per : 1) * ngroups;
-  launch_kernel(markov_step_plan_kernel<KS>, dim3(grid), dim3(kDmaThreads), 0, s, a, pa);
+  launch_kernel(markov_step_plan_kernel<KS, NT, TPW>, dim3(grid), dim3(kDmaThreads / TPW), 0, s,
+                a, pa);
   return hipGetLastError();
 }
 
@@ -823,16 +825,27 @@ static hipError_t launch_sample_ks(const SampleArgs& a, hipStream_t s) {
 hipError_t launch_markov_step(const StepArgs& a, int r, hipStream_t s) {
   DSPARK_DISPATCH_KS(r, launch_step_ks, a, s)
 }
+// The shapes the pipelined step takes (eight waves; four for the RNN head's three-term bias rows
+// at r = 256).
 bool markov_step_plan_fits(const StepArgs& a, int r, int B, int gamma) {
-  return (r == 64 || r == 128 || r == 256) && a.e_terms == 1 && a.dbg == nullptr &&
-         (a.V & 3) == 0 && static_cast<int64_t>(B) * gamma <= kFusedPlanMax &&
+  return (r == 64 || r == 128 || r == 256) && (a.e_terms == 1 || a.e_terms == kRnnTerms) &&
+         a.dbg == nullptr && (a.V & 3) == 0 &&
+         static_cast<int64_t>(B) * gamma <= kFusedPlanMax &&
          a.persistent_wgs > (B + kDmaGroup - 1) / kDmaGroup;
 }
 hipError_t launch_markov_step_plan(const StepArgs& a, const PlanArgs& pa, int r, hipStream_t s) {
+  if (a.e_terms == kRnnTerms) {
+    switch (r) {
+      case 64: return launch_step_plan<4, kRnnTerms, 1>(a, pa, s);
+      case 128: return launch_step_plan<8, kRnnTerms, 1>(a, pa, s);
+      case 256: return launch_step_plan<16, kRnnTerms, 2>(a, pa, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (r) {
-    case 64: return launch_step_plan<4>(a, pa, s);
-    case 128: return launch_step_plan<8>(a, pa, s);
-    case 256: return launch_step_plan<16>(a, pa, s);
+    case 64: return launch_step_plan<4, 1, 1>(a, pa, s);
+    case 128: return launch_step_plan<8, 1, 1>(a, pa, s);
+    case 256: return launch_step_plan<16, 1, 1>(a, pa, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -1,4 +1,5 @@
-"""The draft-and-plan call (dspark_markov_draft_plan) against the three calls it stands for (the
+"""The draft-and-plan calls (dspark_markov_draft_plan, dspark_rnn_draft_plan) against the three
+calls each stands for (the
 draft, the confidence head and the planner, made one after the other), bit for bit: on the
 shapes where the plan runs on one workgroup of the last draft step's launch (r in {64, 128, 256},
 V % 4 == 0, B * gamma <= 4096) and on those that launch it on its own; in every plan mode, the
@@ -151,3 +152,58 @@ def test_draft_plan_against_the_oracle_planner():
             assert np.allclose(np_(st), o["stats"], rtol=1e-12, atol=0), mode
         else:
             log(f"  flagged planner tie (margin {o['margin']:.1e}), mode {mode}")
+
+
+# The RNN head (eq. (6)): name -> (workload, whether the plan runs beside the last step)
+RNN_CASES = {
+    "rnn-b128-v129280-g5": (W.WORKLOADS["b128-v129280-g5"], True),      # four-wave step, r = 256
+    "rnn-b130-v4100-r128-g3": (_custom("rnn-b130-v4100-r128-g3", seed_id=47, B=130, V=4100, r=128,
+                                       d=64, u_std=3.0, w_std=0.05), True),
+    "rnn-b33-v2052-r64-g4": (_custom("rnn-b33-v2052-r64-g4", seed_id=48, B=33, V=2052, r=64, d=64,
+                                     gamma=4), True),
+    "rnn-b20-v4099-r256-g3": (_custom("rnn-b20-v4099-r256-g3", seed_id=49, B=20, V=4099, r=256,
+                                      d=64), False),                     # V % 4 != 0
+}
+
+
+def _run_rnn_case(wl, fused_expected, mode, temperature=1.0, greedy=False):
+    if wl.sps_kind == "flat":
+        wl = W.scaled(wl, sps_kind="hyperbolic", sps_scale=max(1.0, wl.B * 1.5))
+    d = dims_of(wl)
+    wts = W.weights(wl, DEV)
+    Wgco = W.rnn_weights(wl, DEV)
+    T = W.temperatures(wl).to(DEV)
+    sps_t = torch.tensor(W.sps_table(wl), dtype=torch.float64, device=DEV)
+    inp = W.round_inputs(wl, 0, DEV, with_hidden=True, with_noise=False)
+    opts = dict(temperature=temperature, greedy=greedy)
+    tok, q, lse, e = L.rnn_draft(d, inp["U"], wts["W1"], wts["W2t"], Wgco, inp["h"], inp["anchor"],
+                                 inp["uniforms"], **opts)
+    conf = L.confidence(d, inp["h"], wts["W1"], wts["w"], T, inp["anchor"], tok)
+    dl, ro, st = L.plan(d, conf, sps_t, mode)
+    ref = (tok, q, lse, e, conf, dl, ro, st)
+    L.profile_begin()
+    try:
+        got = L.rnn_draft_plan(d, inp["U"], wts["W1"], wts["W2t"], Wgco, inp["h"], inp["anchor"],
+                               inp["uniforms"], wts["w"], T, sps_t, mode, **opts)
+        torch.cuda.synchronize()
+    finally:
+        prof = L.profile_end()
+    for name, a, b in zip(("tokens", "q", "lse", "e_rows", "conf", "draft_len", "row_offsets",
+                           "stats"), got, ref):
+        _same(a, b, f"{wl.name} mode {mode}: {name}")
+    assert (prof["plan"][0] == 0) == fused_expected, (wl.name, prof["plan"])
+    log(f"  {wl.name}: mode {mode}, fused {fused_expected}")
+
+
+@pytest.mark.parametrize("name", list(RNN_CASES))
+def test_rnn_draft_plan_matches_the_separate_calls(name):
+    wl, fused = RNN_CASES[name]
+    modes = (L.EARLY_STOP,) if wl.V > 32000 else (L.EARLY_STOP, L.FULL_PATH)
+    for mode in modes:
+        _run_rnn_case(wl, fused, mode)
+
+
+@pytest.mark.parametrize("temperature,greedy", [(0.6, False), (1.0, True)])
+def test_rnn_draft_plan_options(temperature, greedy):
+    wl, fused = RNN_CASES["rnn-b130-v4100-r128-g3"]
+    _run_rnn_case(wl, fused, L.EARLY_STOP, temperature=temperature, greedy=greedy)

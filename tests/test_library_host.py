@@ -189,6 +189,26 @@ def test_draft_plan_checks_without_gpu(lib):
     assert call(opts=bad_t) == 8
 
 
+def test_rnn_draft_plan_checks_without_gpu(lib):
+    """dspark_rnn_draft_plan refuses what the RNN draft, confidence and plan calls refuse."""
+    dims = L.Dims(4, 3, 1000, 16, 64)
+    d, P = dims.c(), _p()
+    ws = L.workspace_bytes(dims, L.OP_RNN_DRAFT)
+    sl = 4 * 4 + 1
+
+    def call(dd=d, Wgco=P, e_rows=P, sps_len=sl, mode=1, ws_bytes=ws):
+        return lib.dspark_rnn_draft_plan(dd, P, P, P, Wgco, P, P, P, P, P, P, sps_len, mode, None,
+                                         0, P, P, P, e_rows, P, P, P, None, P, ws_bytes, None,
+                                         None)
+
+    assert call(Wgco=None) == 1
+    assert call(e_rows=None) == 1
+    assert call(dd=L.Dims(4, 3, 1000, 512, 64).c()) == 2     # the RNN head takes r <= 256
+    assert call(sps_len=sl - 1) == 5
+    assert call(mode=3) == 7                                  # LAGGED_TOPK without a ring
+    assert call(ws_bytes=ws - 1) == 4
+
+
 def test_binding_signatures_match_the_header(lib):
     """Every function the binding declares has the header's parameter count and kinds, so a
     marshalled call can never shift its arguments."""
