@@ -184,6 +184,27 @@ __global__ __launch_bounds__(kStateThreads) void rnn_state_kernel(RnnStateArgs p
                     wbase + 1024 * t);
     }
   }
+  // Wave 0's pre-GEMM terms of its (state index, request) pairs, loaded now so that their latency
+  // passes during the dot products (index clamped into the tensor; pairs past B or r unused).
+  const int jl = lane & 31, rp = lane >> 5;          // state index, request pair
+  const int j = j0 + jl;
+  const int N = 3 * r;
+  const size_t M = static_cast<size_t>(p.B) * p.gamma;
+  float pv[2][kRnnPreSplits][3];
+  if (quarter == 0) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const size_t m = static_cast<size_t>(min(b0 + 2 * rp + h, p.B - 1)) * p.gamma + p.k;
+      const int jc = min(j, r - 1);
+#pragma unroll
+      for (int sp = 0; sp < kRnnPreSplits; ++sp) {
+        const float* P = p.P + (sp * M + m) * N;
+        pv[h][sp][0] = P[jc];
+        pv[h][sp][1] = P[r + jc];
+        pv[h][sp][2] = P[2 * r + jc];
+      }
+    }
+  }
   // z of the block's requests: their previous tokens first, then every value's load in flight
   // at once (at most kStateB * 2 * 256 / kStateThreads = 8 per thread) before the LDS stores.
   __shared__ int32_t xs[kStateB];
@@ -208,8 +229,6 @@ __global__ __launch_bounds__(kStateThreads) void rnn_state_kernel(RnnStateArgs p
   }
   wait_copies<0>();
   __syncthreads();
-  const int jl = lane & 31, rp = lane >> 5;          // state index, request pair
-  const int j = j0 + jl;
   const unsigned char* wl = wst + quarter * kStateWaveBytes;
   const double* z0 = zs + (2 * rp) * (2 * r) + i0;
   const double* z1 = z0 + 2 * r;
@@ -245,8 +264,6 @@ __global__ __launch_bounds__(kStateThreads) void rnn_state_kernel(RnnStateArgs p
 #pragma unroll
     for (int t = 0; t < 6; ++t) acc[t] += part[w][t][lane];
   }
-  const int N = 3 * r;
-  const size_t M = static_cast<size_t>(p.B) * p.gamma;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int b = b0 + 2 * rp + h;
@@ -255,10 +272,9 @@ __global__ __launch_bounds__(kStateThreads) void rnn_state_kernel(RnnStateArgs p
     double ag = acc[3 * h], ac = acc[3 * h + 1], ao = acc[3 * h + 2];
 #pragma unroll
     for (int sp = 0; sp < kRnnPreSplits; ++sp) {
-      const float* P = p.P + (sp * M + m) * N;
-      ag += static_cast<double>(P[j]);
-      ac += static_cast<double>(P[r + j]);
-      ao += static_cast<double>(P[2 * r + j]);
+      ag += static_cast<double>(pv[h][sp][0]);
+      ac += static_cast<double>(pv[h][sp][1]);
+      ao += static_cast<double>(pv[h][sp][2]);
     }
     const double gate = 1.0 / (1.0 + exp(-ag));
     const double s_prev = zs[(2 * rp + h) * (2 * r) + j];
