@@ -408,6 +408,7 @@ __global__ __launch_bounds__(kBlock, 2) void residual_partials_kernel(VerifyArgs
 // the tile each (the fp64 exponentials dominate, so eight waves share them).
 constexpr int kResThreads = 512;
 constexpr int kResGroup = 64;
+constexpr int kXcds = 8;          // accelerator complex dies of an MI355X, each with its own L2
 constexpr int kResTiles = 2;
 
 // PW: halves of a tile's epilogue each wave takes (1: eight waves, two per tile; 2: four waves,
@@ -452,8 +453,21 @@ __device__ __forceinline__ void residual_dma(const VerifyArgs& p) {
   if (nres <= 0) return;
   const int ngroups = (nres + kResGroup - 1) / kResGroup;   // <= gridDim.x (launch sizing)
   const int nwg = gridDim.x / ngroups;
-  if (static_cast<int>(blockIdx.x) >= nwg * ngroups) return;
-  const int group = blockIdx.x % ngroups, wg = blockIdx.x / ngroups;
+  const int bid = blockIdx.x;
+  if (bid >= nwg * ngroups) return;
+  // Block -> (group, vocabulary range). Blocks are dispatched round-robin over the XCDs, so
+  // blocks b and b + kXcds share one; with several groups, the groups of one range go to blocks
+  // that share an XCD, and the range's W2t rows come from HBM once and then from that XCD's L2
+  // (a bijection when nwg is a multiple of kXcds; otherwise consecutive blocks).
+  int group, wg;
+  if (ngroups > 1 && nwg % kXcds == 0) {
+    const int xcd = bid % kXcds, slot = bid / kXcds;
+    group = slot % ngroups;
+    wg = (slot / ngroups) * kXcds + xcd;
+  } else {
+    group = bid % ngroups;
+    wg = bid / ngroups;
+  }
   const int gcount = min(kResGroup, nres - group * kResGroup);
   const int nitems = (p.V + D::kTok - 1) / D::kTok;
   const int item_lo = static_cast<int>(static_cast<int64_t>(nitems) * wg / nwg);
