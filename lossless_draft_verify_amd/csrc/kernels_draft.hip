@@ -253,6 +253,7 @@ __global__ __launch_bounds__(kStepThreads, 1) void markov_step_kernel(StepArgs p
 constexpr int kDmaThreads = 512;
 constexpr int kDmaGroup = 128;   // requests per group: 4 waves x 32 per tile
 constexpr int kDmaTiles = 2;     // 32-token tiles per item
+constexpr int kXcds = 8;         // accelerator complex dies of an MI355X, each with its own L2
 
 // TPW: 32-token tiles each wave computes per item (1: eight waves; 2: four waves, each taking
 // both tiles of its request quarter).
@@ -293,7 +294,7 @@ struct DmaLds {
 // The pipelined step as run by workgroup `bid` of `nblk` step workgroups.
 template <int KS, int NT, int TPW = 1>
 __device__ __forceinline__ void markov_step_dma(const StepArgs& p, unsigned bid, unsigned nblk,
-                                                DmaLds<KS>& lds) {
+                                                bool xcd_map, DmaLds<KS>& lds) {
   using D = DmaStep<KS, TPW>;
   unsigned char* stage = lds.stage;
   float2* pbuf = lds.pbuf;
@@ -303,10 +304,22 @@ __device__ __forceinline__ void markov_step_dma(const StepArgs& p, unsigned bid,
   const int half = lane >> 5, col = lane & 31;
   const int sub = wave >> 2, rq = wave & 3;   // (first) tile within the item, request quarter
   // Workgroup w of a group takes a contiguous range of items, so that the partials of one
-  // request that it produces are contiguous in memory (full-line writes).
+  // request that it produces are contiguous in memory (full-line writes). Blocks are dispatched
+  // round-robin over the XCDs (blocks b and b + kXcds share one): when bid is the hardware block
+  // index (xcd_map) and there are several request groups, the groups of one range go to blocks
+  // that share an XCD, so that the range's W2t rows come from HBM once and then from its L2 (a
+  // bijection when nwg is a multiple of kXcds; otherwise consecutive blocks).
   const int ngroups = (p.B + kDmaGroup - 1) / kDmaGroup;
-  const int group = bid % ngroups;
-  const int wg = bid / ngroups, nwg = nblk / ngroups;
+  const int nwg = nblk / ngroups;
+  int group, wg;
+  if (xcd_map && ngroups > 1 && nwg % kXcds == 0) {
+    const int xcd = bid % kXcds, slot = bid / kXcds;
+    group = slot % ngroups;
+    wg = (slot / ngroups) * kXcds + xcd;
+  } else {
+    group = bid % ngroups;
+    wg = bid / ngroups;
+  }
   const int nitems = (p.V + D::kTok - 1) / D::kTok;
   const int item_lo = static_cast<int>(static_cast<int64_t>(nitems) * wg / nwg);
   const int n = static_cast<int>(static_cast<int64_t>(nitems) * (wg + 1) / nwg) - item_lo;
@@ -532,7 +545,7 @@ __device__ __forceinline__ void markov_step_dma(const StepArgs& p, unsigned bid,
 template <int KS, int NT>
 __global__ __launch_bounds__(kDmaThreads, 1) void markov_step_dma_kernel(StepArgs p) {
   __shared__ DmaLds<KS> lds;
-  markov_step_dma<KS, NT>(p, blockIdx.x, gridDim.x, lds);
+  markov_step_dma<KS, NT>(p, blockIdx.x, gridDim.x, true, lds);
 }
 
 // The pipelined step with four waves (one per SIMD), each computing both token tiles of an item
@@ -541,7 +554,7 @@ __global__ __launch_bounds__(kDmaThreads, 1) void markov_step_dma_kernel(StepArg
 template <int KS, int NT>
 __global__ __launch_bounds__(kDmaThreads / 2, 1) void markov_step_dma_wave4_kernel(StepArgs p) {
   __shared__ DmaLds<KS> lds;
-  markov_step_dma<KS, NT, 2>(p, blockIdx.x, gridDim.x, lds);
+  markov_step_dma<KS, NT, 2>(p, blockIdx.x, gridDim.x, true, lds);
 }
 
 // The last draft position's step with the verify planner beside it: workgroup 0 plans (its LDS
@@ -559,7 +572,7 @@ __global__ __launch_bounds__(kDmaThreads / TPW, 1) void markov_step_plan_kernel(
     plan::run<kDmaThreads / TPW>(pa, *reinterpret_cast<plan::Smem<kFusedPlanMax>*>(lds.stage));
     return;
   }
-  markov_step_dma<KS, NT, TPW>(p, blockIdx.x - 1, gridDim.x - 1, lds);
+  markov_step_dma<KS, NT, TPW>(p, blockIdx.x - 1, gridDim.x - 1, false, lds);
 }
 
 // One 1024-thread workgroup per request. Thread t holds a contiguous range of at most 16 tile
