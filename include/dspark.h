@@ -231,7 +231,7 @@ DSPARK_API dspark_status dspark_plan(dspark_dims dims, const float* conf, const 
  * the three separate calls.
  *   ws, ws_bytes   the draft workspace (dspark_workspace_bytes(dims, DSPARK_OP_DRAFT))
  *   opts           nullable; temperature / greedy as in dspark_markov_draft_opts
- * Returns the first failing check of the three calls (nothing is launched then).
+ * A failing check of any of the three calls returns its status, and nothing is launched.
  */
 DSPARK_API dspark_status dspark_markov_draft_plan(
     dspark_dims dims, const float* U, const uint16_t* W1, const uint16_t* W2t,
