@@ -44,6 +44,10 @@ CASES = {
     # pipelined step and pipelined residual at r = 256, d = 320
     "b32-v32000-g7": W.scaled(W.WORKLOADS["b32-v32000-g7"], name="b32-v32000-g7-rnn", seed_id=53,
                               d=320),
+    # pipelined step and residual at r = 128 over two request groups: the groups of one
+    # vocabulary range placed on one XCD, with the three-term bias rows
+    "b130-v4100-r128-g3": _custom("b130-v4100-r128-g3-rnn", seed_id=54, B=130, V=4100, r=128,
+                                  d=64, u_std=3.0, w_std=0.05),
 }
 
 
@@ -134,7 +138,8 @@ def _target(wl, inp, o, draft_len):
 
 
 @pytest.mark.parametrize("opt", list(OPTIONS))
-@pytest.mark.parametrize("name", ["tiny-b4-v1000-g3", "b130-v4099-r256-g3", "b32-v32000-g7"])
+@pytest.mark.parametrize("name", ["tiny-b4-v1000-g3", "b130-v4099-r256-g3", "b32-v32000-g7",
+                                  "b130-v4100-r128-g3"])
 def test_rnn_verify_parity(name, opt):
     """Verify of an RNN draft with ragged lengths: accept lengths and emitted tokens exact
     except flagged near ties, flags exact, beta within the probability tolerance."""
