@@ -98,19 +98,19 @@ __global__ __launch_bounds__(kPreThreads) void rnn_pre_kernel(RnnPreArgs p) {
           base + arow * kPreRowBytes + 16 * (piece ^ (arow & 15)));
       const u16x8_t b = *reinterpret_cast<const u16x8_t*>(
           base + kPreOperandBytes + brow * kPreRowBytes + 16 * (piece ^ (brow & 15)));
-      acc = mfma_32x32x16(in ? a : zero_u16x8(), b, acc);
+      acc = mfma_32x32x16(b, in ? a : zero_u16x8(), acc);   // (rows m) x (outputs n)
     }
 #pragma unroll
     for (int j = 0; j < 16; ++j) acc64[j] += static_cast<double>(acc[j]);
     lds_barrier();   // the stage is free for chunk c + 2
   }
-  const int m = mb + 32 * (wave >> 1) + col;
-  if (m < p.M) {
-    float* out = p.P + (static_cast<size_t>(split) * p.M + m) * N;
+  // Lane col holds output n for the rows m of its half: each store writes two 128-byte row pieces.
+  const int n = nb + 32 * (wave & 1) + col;
+  if (n < N) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const int n = nb + 32 * (wave & 1) + tile_token(j, half);
-      if (n < N) out[n] = static_cast<float>(acc64[j]);
+      const int m = mb + 32 * (wave >> 1) + tile_token(j, half);
+      if (m < p.M) p.P[(static_cast<size_t>(split) * p.M + m) * N + n] = static_cast<float>(acc64[j]);
     }
   }
 }
