@@ -69,6 +69,17 @@ MUTATIONS = [
      "for (int i = 0; i < d; ++i) z[2 * r + i] = bf16_to_double(h_row[i]);",
      "for (int i = 0; i < d && i < r; ++i) z[r + i] = bf16_to_double(h_row[i]);",
      [rp.test_state_path_half_gate_closed_form]),
+    ("lagged capacity by early stop", "const int64_t k_lag = full_path_count(theta_lag, &mg);",
+     "const int64_t k_lag = early_stop_count(theta_lag, &mg);",
+     [pp.test_lagged_capacity_is_a_full_path_search_on_a_two_peak_table]),
+    ("full path keeps the last maximiser", "if (theta[i] > theta[best]) best = i;",
+     "if (theta[i] >= theta[best]) best = i;",
+     [pp.test_full_path_takes_the_first_maximiser_on_a_plateau]),
+    ("bonus drawn from the last drafted row",
+     "const float* row = target + (off + ell) * static_cast<int64_t>(V);",
+     "const float* row = target + (off + ell - 1) * static_cast<int64_t>(V);",
+     [vp.test_bonus_is_drawn_from_the_row_after_the_last_verified_draft,
+      vp.test_two_token_output_exact_grid_with_position_dependent_rows]),
 ]
 
 

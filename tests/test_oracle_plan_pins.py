@@ -235,3 +235,79 @@ def test_lagged_topk_ring_and_capacity():
         rq, _, _ = _sorted_order(a)
         expect = np.bincount(rq[:k_lag], minlength=R)
         assert np.array_equal(p["draft_len"], expect)
+
+
+def _first_argmax_count(c, sps):
+    """Admissions at the first maximiser of Theta along the survival order, written out from the
+    definition ([V41] "目标函数": Theta = tau * SPS(B_tot), tau = R + admitted survivals)."""
+    R = c.shape[0]
+    _, _, a_sorted = _sorted_order(np.cumprod(c.astype(np.float64), axis=1))
+    tau = R + np.concatenate([[0.0], np.cumsum(a_sorted)])
+    theta = tau * sps[R + np.arange(len(tau))]
+    return int(np.argmax(theta)), theta
+
+
+def test_lagged_capacity_is_a_full_path_search_on_a_two_peak_table():
+    """The lagged planner's capacity comes from a search of the whole path, not from early stop
+    ([V41] "阈值随负载变化", [CSDN] 8: the production planner drops early stop because the step
+    time is not unimodal in B). Hand-worked two-peak case, R = 2, gamma = 2:
+    round t-2 confidences [[0.9, 0.9], [0.5, 0.5]] give survivals 0.9, 0.81, 0.5, 0.25 in path
+    order, tau = 2, 2.9, 3.71, 4.21, 4.46, and with SPS(2..6) = 1, 0.6, 0.58, 0.45, 0.44
+    Theta = 2, 1.74, 2.1518, 1.8945, 1.9624: early stop admits 0, the full path 2, so K = 4.
+    Round t's own order (survivals 0.3, 0.06 | 0.95, 0.855) then admits both of request 1."""
+    R, g = 2, 2
+    sps = np.array([1.0, 1.0, 1.0, 0.6, 0.58, 0.45, 0.44])
+    c_lag = np.array([[0.9, 0.9], [0.5, 0.5]], np.float32)
+    c_now = np.array([[0.3, 0.2], [0.95, 0.9]], np.float32)
+    k_np, theta = _first_argmax_count(c_lag, sps)
+    assert np.allclose(theta, [2.0, 1.74, 2.1518, 1.8945, 1.9624], atol=1e-6)
+    assert k_np == 2
+    assert oracle.plan(c_lag, sps, EARLY)["draft_len"].sum() == 0
+    ring = np.zeros((2, R, g), np.float32)
+    ring[0] = c_lag
+    p = oracle.plan(c_now, sps, LAG, ring=ring, round_index=2)
+    assert p["stats"][3] == R + 2
+    assert list(p["draft_len"]) == [0, 2]
+    assert list(p["row_offsets"]) == [0, 1, 4]
+    assert p["stats"][0] == 4
+    assert np.array_equal(ring[0], c_now)
+
+
+def test_full_path_takes_the_first_maximiser_on_a_plateau():
+    """Theta ties exactly along the path (c = 1, SPS(1..4) = 1, 1/2, 1/4, 1/4 gives
+    Theta = 1, 1, 0.75, 1): the full-path search keeps the smallest batch reaching the maximum
+    (the strict comparison of "stop once Theta no longer rises", [V41] "贪心就能解"), so it
+    admits nothing, and so does the lagged capacity read from the same confidences."""
+    c = np.ones((1, 3), np.float32)
+    sps = np.array([1.0, 1.0, 0.5, 0.25, 0.25])
+    k_np, theta = _first_argmax_count(c, sps)
+    assert list(theta) == [1.0, 1.0, 0.75, 1.0] and k_np == 0
+    f = oracle.plan(c, sps, PATH)
+    assert f["draft_len"][0] == 0 and f["stats"][2] == 1.0
+    ring = np.zeros((2, 1, 3), np.float32)
+    ring[1] = c
+    p = oracle.plan(c, sps, LAG, ring=ring, round_index=3)
+    assert p["stats"][3] == 1 and p["draft_len"][0] == 0
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_lagged_capacity_matches_argmax_on_sawtooth_tables(seed):
+    """Random sawtooth and bucketed SPS tables (not unimodal): the lagged capacity equals R plus
+    the first argmax of Theta on the confidences of round t-2, computed here from the
+    definition."""
+    rng = np.random.default_rng(900 + seed)
+    R, g = int(rng.integers(2, 9)), int(rng.integers(1, 6))
+    n = R * (g + 1) + 1
+    x = np.arange(n, dtype=np.float64)
+    if seed % 2:
+        sps = 1.0 / (1.0 + np.floor(x / 4) * rng.uniform(0.3, 1.5)) * (1 + 0.3 * (x % 4 == 3))
+    else:
+        sps = 1.0 / np.ceil((x + 1) / rng.integers(2, 6))
+    c_lag, c_now = _random_conf(rng, R, g), _random_conf(rng, R, g)
+    k_np, _ = _first_argmax_count(c_lag, sps)
+    ring = np.zeros((2, R, g), np.float32)
+    ring[seed % 2] = c_lag
+    p = oracle.plan(c_now, sps, LAG, ring=ring, round_index=2 + seed % 2)
+    assert p["stats"][3] == R + k_np
+    rq, _, _ = _sorted_order(np.cumprod(c_now.astype(np.float64), axis=1))
+    assert np.array_equal(p["draft_len"], np.bincount(rq[:k_np], minlength=R))

@@ -215,3 +215,68 @@ def test_bonus_only_when_all_accepted_and_flags():
     assert list(v["next_token"][:2]) == [V - 1, V - 1]    # 0.99 of a uniform bonus row
     assert v["flags"][2] & oracle.FLAG_NONFINITE
     assert v["accept_len"][2] == 0 and v["next_token"][2] == 0
+
+
+def test_bonus_is_drawn_from_the_row_after_the_last_verified_draft():
+    """When every verified draft is accepted, the extra token comes from the target's
+    distribution at position l+1 ([V41] "投机解码：让小的先猜，大的一次验一串"), i.e. row l of the
+    request's packed rows. Every row is a near point mass on its own token, so reading any
+    other row gives another token. Lengths 3, 1, 2, 0 of gamma = 3 (packed rows)."""
+    B, g, V = 4, 3, 8
+    ell = np.array([3, 1, 2, 0], np.int32)
+    U = np.zeros((B, g, V), np.float32)            # uniform draft
+    W1, W2t = _zeros_w(V)
+    anchor = np.zeros(B, np.int32)
+    u = np.zeros((B, g + 1, 3), np.float32)        # draft token 0; accept whenever p_t(0) > 0
+    u[:, :, 2] = 0.5
+    d = oracle.markov_draft(U, W1, W2t, anchor, u)
+    assert np.all(d["tokens"] == 0)
+    offs = np.concatenate([[0], np.cumsum(1 + ell)]).astype(np.int32)
+    rows, mass_tok = [], []
+    for b in range(B):
+        for k in range(ell[b] + 1):
+            m = 1 + (3 * b + k) % (V - 1)          # never token 0, differs between rows k, k+1
+            row = np.full(V, -1e30, np.float32)
+            row[0] = 0.0                           # p_t(0) = e^-60 > 0: accepted at u = 0
+            row[m] = 60.0
+            rows.append(row)
+            mass_tok.append(m)
+    v = oracle.verify(np.stack(rows), offs, ell, U, W1, W2t, anchor, d["tokens"], d["q"], u)
+    assert list(v["accept_len"]) == list(ell)
+    expect = [mass_tok[offs[b] + ell[b]] for b in range(B)]
+    assert list(v["next_token"]) == expect
+    assert all(mass_tok[offs[b] + ell[b]] != mass_tok[offs[b] + ell[b] - 1]
+               for b in range(B) if ell[b] > 0)
+    assert np.all(v["beta_emit"] == -1.0)
+
+
+def test_two_token_output_exact_grid_with_position_dependent_rows():
+    """gamma = 1, V = 3, exact grid over the four uniforms used (draft, accept, resample,
+    bonus). Target rows differ by position: row 1 is p_1 = (0.2, 0.3, 0.5), the bonus row is
+    T2[x_1] (a table target chain). P(y_1 = a, accepted, y_2 = b) = min(p_d(a), p_1(a)) T2[a][b]
+    and P(y_1 = a, rejected) = max(0, p_1(a) - p_d(a)) ([V41] "投机解码…"; [AIL] 02), so the
+    counts over the 10^4 grid points are exact integers."""
+    n = 10
+    mid = (np.arange(n) + 0.5) / n
+    G = np.stack(np.meshgrid(mid, mid, mid, mid, indexing="ij"), -1).reshape(-1, 4)
+    B, g, V = n ** 4, 1, 3
+    p_d = np.array([0.5, 0.3, 0.2])
+    p_1 = np.array([0.2, 0.3, 0.5])
+    T2 = np.array([[0.6, 0.3, 0.1], [0.1, 0.1, 0.8], [0.3, 0.4, 0.3]])
+    U = np.tile(np.log(p_d).astype(np.float32), (B, g, 1))
+    W1, W2t = _zeros_w(V)
+    anchor = np.zeros(B, np.int32)
+    u = np.zeros((B, g + 1, 3), np.float32)
+    u[:, 0, 0], u[:, 0, 1], u[:, 0, 2], u[:, 1, 2] = G[:, 0], G[:, 1], G[:, 2], G[:, 3]
+    d = oracle.markov_draft(U, W1, W2t, anchor, u)
+    x1 = d["tokens"][:, 0]
+    rows = np.stack([np.tile(np.log(p_1), (B, 1)), np.log(T2[x1])], 1).astype(np.float32)
+    v = oracle.verify(rows.reshape(-1, V), dense_offsets(B, g), np.full(B, g, np.int32), U, W1,
+                      W2t, anchor, d["tokens"], d["q"], u)
+    acc = v["accept_len"] == 1
+    y1 = first_emitted(d["tokens"], v["accept_len"], v["next_token"])
+    joint = np.bincount(y1[acc] * V + v["next_token"][acc], minlength=V * V).reshape(V, V)
+    expect = np.round(B * np.minimum(p_d, p_1)[:, None] * T2).astype(int)
+    assert np.array_equal(joint, expect)
+    rej = np.bincount(y1[~acc], minlength=V)
+    assert np.array_equal(rej, np.round(B * np.maximum(0.0, p_1 - p_d)).astype(int))
