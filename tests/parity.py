@@ -47,6 +47,7 @@ class MismatchCounter:
         self.draws = 0
         self.mismatches = 0
         self.flagged = 0
+        self.worst = 0.0      # largest edge distance of a mismatched draw
 
     def add(self, gpu, ref, margin, tie=NEAR_TIE):
         gpu, ref, margin = np.asarray(gpu), np.asarray(ref), np.asarray(margin)
@@ -58,18 +59,23 @@ class MismatchCounter:
             f"first at {np.argwhere(unflagged)[:5].tolist()}")
         self.draws += bad.size
         self.mismatches += int(bad.sum())
+        if bad.any():
+            self.worst = max(self.worst, float(margin[bad].max()))
         self.flagged += int(flagged.sum())
 
     def rate(self):
         return self.mismatches / max(1, self.draws)
 
     def check_rate(self):
-        assert self.rate() < MAX_MISMATCH_RATE or self.mismatches <= 1, (
+        """Mismatches (all flagged: add() asserts that) under 0.1 % of this counter's draws; a
+        counter of fewer than 1000 draws therefore allows none."""
+        assert self.mismatches < MAX_MISMATCH_RATE * self.draws or self.mismatches == 0, (
             f"{self.what}: mismatch rate {self.rate():.2e} ({self.mismatches}/{self.draws})")
 
     def report(self):
         return (f"{self.what}: draws {self.draws}, mismatches {self.mismatches} "
-                f"({100 * self.rate():.3f} %), flagged {100 * self.flagged / max(1, self.draws):.1f} %")
+                f"({100 * self.rate():.3f} %, within {self.worst:.1e} of an edge), "
+                f"flagged {100 * self.flagged / max(1, self.draws):.1f} %")
 
 
 def gpu_draft(wl, inp, wts, force=None, dbg=False, B=None, temperature=1.0, greedy=False):

@@ -94,6 +94,26 @@ def test_draft_logits_recompute_is_bit_exact():
     assert np.array_equal(ref, g["q"])
 
 
+def test_draft_mismatch_rate_headline_shape():
+    """2 x 10^4 draws at the production drafter's shape (V = 129280, r = 256, W std 0.05):
+    every mismatch must be a flagged near tie, and mismatches must stay under 0.1 % of draws.
+    The report gives how close to a CDF edge the mismatched draws were."""
+    wl = W.scaled(W.WORKLOADS["b128-v129280-g5"], name="rate-r256", seed_id=22, B=1024, d=64)
+    c = MismatchCounter("draft rate V=129280 r=256")
+    wts = W.weights(wl, DEV)
+    for rnd in range(4):
+        inp = W.round_inputs(wl, rnd, DEV, with_hidden=False, with_noise=False)
+        log(f"  round {rnd}: oracle")
+        o = oracle_draft(inp, wts)
+        g = gpu_draft(wl, inp, wts, force=o["tokens"])
+        compare_draft(g, o, c, logits=False)
+        log(f"  round {rnd}: {c.report()}")
+        del inp
+        torch.cuda.empty_cache()
+    assert c.draws >= 20000
+    c.check_rate()
+
+
 def test_draft_mismatch_rate_headline_vocab():
     """2 x 10^4 draws at V = 129280 (r = 16 keeps the oracle fast): every mismatch must be a
     flagged near tie and mismatches must stay under 0.1 % of draws."""
@@ -374,6 +394,66 @@ def _T(a, dt=torch.int32):
     return torch.as_tensor(np.ascontiguousarray(a), dtype=dt, device=DEV)
 
 
+def _compare_chain_round(wl, wts, rec, ring_g, sps_t, temps, cd, ca, ce):
+    """One oracle-driven round of the lagged chain: each entry point gets the oracle's inputs
+    (anchor, drafted tokens, confidences, plan) and is compared with it, the device ring
+    included."""
+    d = dims_of(wl)
+    inp = {k: v.to(DEV) for k, v in rec["inp"].items()}
+    inp["anchor"] = _T(rec["anchor"])
+    o, p, ov = rec["draft"], rec["plan"], rec["verify"]
+    gu = gpu_draft(wl, inp, wts)
+    cd.add(gu["tokens"][:, :1], o["tokens"][:, :1], o["margin"][:, :1])
+    del gu
+    g = gpu_draft(wl, inp, wts, force=o["tokens"], dbg=True)
+    compare_draft(g, o, cd)
+    tok = _T(o["tokens"])
+    cg = L.confidence(d, inp["h"], wts["W1"], wts["w"], temps, inp["anchor"], tok)
+    assert np.abs(np_(cg) - rec["conf"]).max() <= PROB_TOL
+    dl, ro, st = L.plan(d, _T(rec["conf"], torch.float32), sps_t, L.LAGGED_TOPK, ring=ring_g,
+                        round_index=rec["t"])
+    torch.cuda.synchronize()
+    assert np.array_equal(np_(ring_g), rec["ring_after"]), rec["t"]
+    if p["margin"] > PLAN_TIE:
+        assert np.array_equal(np_(dl), p["draft_len"]), rec["t"]
+        assert np.array_equal(np_(ro), p["row_offsets"]), rec["t"]
+        assert np.allclose(np_(st), p["stats"], rtol=1e-12, atol=0), rec["t"]
+    al, nt, be, fl = L.verify(d, _T(rec["target"], torch.float32), _T(p["row_offsets"]),
+                              _T(p["draft_len"]), inp["U"], wts["W1"], wts["W2t"],
+                              inp["anchor"], tok, _T(o["q"], torch.float32), g["lse_t"],
+                              inp["uniforms"])
+    torch.cuda.synchronize()
+    al, nt, be, fl = np_(al), np_(nt), np_(be), np_(fl)
+    ca.add(al, ov["accept_len"], decisive_margin(ov, al, wl.gamma))
+    same = al == ov["accept_len"]
+    ce.add(nt[same], ov["next_token"][same], ov["emit_margin"][same])
+    assert np.array_equal(fl[same].astype(np.uint32), ov["flags"][same])
+    assert np.abs(be[same] - ov["beta_emit"][same]).max() <= PROB_TOL
+    log(f"  round {rec['t']}: B_tot {p['stats'][0]:.0f}, capacity {p['stats'][3]:.0f}, "
+        f"mean accepted {al.mean():.2f}, rejected {int((be >= 0).sum())}")
+
+
+def _oracle_chain(wl, rounds):
+    log(f"[chain] {wl.name}: {rounds} rounds, oracle-driven")
+    wts_cpu = W.weights(wl)
+    wts = {k: v.to(DEV) for k, v in wts_cpu.items()}
+    chain = OracleChain(wl, wts_cpu)
+    state = chain.initial_state()
+    ring_g = torch.zeros((2, wl.B, wl.gamma), dtype=torch.float32, device=DEV)
+    sps_t = _T(W.sps_table(wl), torch.float64)
+    temps = W.temperatures(wl).to(DEV)
+    cd, ca, ce = (MismatchCounter("chain draft"), MismatchCounter("chain accept"),
+                  MismatchCounter("chain emit"))
+    for _ in range(rounds):
+        rec, state = chain.step(state)      # one round at a time: the next needs its anchors
+        _compare_chain_round(wl, wts, rec, ring_g, sps_t, temps, cd, ca, ce)
+        del rec
+        torch.cuda.empty_cache()
+    log(f"  {cd.report()}; {ca.report()}; {ce.report()}")
+    for c in (cd, ca, ce):
+        c.check_rate()
+
+
 def test_lagged_chain_parity():
     """Twenty chained rounds of the lagged planner at a scaled high-load shape (two request
     groups, the second ragged; a vocabulary tail): the oracle drives the chain (next anchor =
@@ -381,52 +461,16 @@ def test_lagged_chain_parity():
     with it, the device confidence ring included."""
     wl = W.scaled(W.WORKLOADS["b512-v129280-g5-lagged"], name="chain-b160-v4100-g5", seed_id=32,
                   B=160, V=4100, d=256, sps_scale=160.0)
-    log(f"[chain] {wl.name}: oracle chain of {wl.rounds} rounds")
-    wts_cpu = W.weights(wl)
-    wts = {k: v.to(DEV) for k, v in wts_cpu.items()}
-    chain = OracleChain(wl, wts_cpu)
-    recs, _ = chain.run(chain.initial_state(), wl.rounds)
-    d = dims_of(wl)
-    ring_g = torch.zeros((2, wl.B, wl.gamma), dtype=torch.float32, device=DEV)
-    sps_t = _T(W.sps_table(wl), torch.float64)
-    temps = W.temperatures(wl).to(DEV)
-    cd, ca, ce = (MismatchCounter("chain draft"), MismatchCounter("chain accept"),
-                  MismatchCounter("chain emit"))
-    for rec in recs:
-        inp = {k: v.to(DEV) for k, v in rec["inp"].items()}
-        inp["anchor"] = _T(rec["anchor"])
-        o, p, ov = rec["draft"], rec["plan"], rec["verify"]
-        gu = gpu_draft(wl, inp, wts)
-        cd.add(gu["tokens"][:, :1], o["tokens"][:, :1], o["margin"][:, :1])
-        g = gpu_draft(wl, inp, wts, force=o["tokens"], dbg=True)
-        compare_draft(g, o, cd)
-        tok = _T(o["tokens"])
-        cg = L.confidence(d, inp["h"], wts["W1"], wts["w"], temps, inp["anchor"], tok)
-        assert np.abs(np_(cg) - rec["conf"]).max() <= PROB_TOL
-        dl, ro, st = L.plan(d, _T(rec["conf"], torch.float32), sps_t, L.LAGGED_TOPK, ring=ring_g,
-                            round_index=rec["t"])
-        torch.cuda.synchronize()
-        assert np.array_equal(np_(ring_g), rec["ring_after"]), rec["t"]
-        if p["margin"] > PLAN_TIE:
-            assert np.array_equal(np_(dl), p["draft_len"]), rec["t"]
-            assert np.array_equal(np_(ro), p["row_offsets"]), rec["t"]
-            assert np.allclose(np_(st), p["stats"], rtol=1e-12, atol=0), rec["t"]
-        al, nt, be, fl = L.verify(d, _T(rec["target"], torch.float32), _T(p["row_offsets"]),
-                                  _T(p["draft_len"]), inp["U"], wts["W1"], wts["W2t"],
-                                  inp["anchor"], tok, _T(o["q"], torch.float32), g["lse_t"],
-                                  inp["uniforms"])
-        torch.cuda.synchronize()
-        al, nt, be, fl = np_(al), np_(nt), np_(be), np_(fl)
-        ca.add(al, ov["accept_len"], decisive_margin(ov, al, wl.gamma))
-        same = al == ov["accept_len"]
-        ce.add(nt[same], ov["next_token"][same], ov["emit_margin"][same])
-        assert np.array_equal(fl[same].astype(np.uint32), ov["flags"][same])
-        assert np.abs(be[same] - ov["beta_emit"][same]).max() <= PROB_TOL
-        log(f"  round {rec['t']}: B_tot {p['stats'][0]:.0f}, capacity {p['stats'][3]:.0f}, "
-            f"mean accepted {al.mean():.2f}")
-    for c in (cd, ca, ce):
-        c.check_rate()
-    log(f"  {cd.report()}; {ca.report()}; {ce.report()}")
+    _oracle_chain(wl, wl.rounds)
+
+
+def test_lagged_chain_full_size_oracle():
+    """The high-load workload at its full size (B = 512, V = 129280, r = 256, d = 5120, steep
+    SPS, lag-2 ring): four chained rounds driven by the oracle, so rounds 2 and 3 plan from the
+    device ring; every entry point is compared with the oracle element by element in the launch
+    configuration the bench uses (four 128-request groups in the draft step with their XCD
+    placement, several 64-request groups in the residual pass)."""
+    _oracle_chain(W.WORKLOADS["b512-v129280-g5-lagged"], 4)
 
 
 def _admission(conf, sps, B, gamma, mode):
