@@ -293,6 +293,32 @@ DSPARK_API dspark_status dspark_verify_opts(dspark_dims dims, const float* targe
                                             const dspark_draft_opts* opts, void* stream);
 
 /*
+ * The verify of dspark_verify_opts for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, and harnesses that forbid hipMalloc. Arguments,
+ * results, checks and kernels are those of dspark_verify_opts, without `ws` / `ws_bytes`: the
+ * scratch space is a fixed array in the library's device memory, DSPARK_NOALLOC_SCRATCH_BYTES
+ * (48 MiB) per GPU, held from the library's first use on that GPU until the process ends.
+ * Sizes whose workspace (dspark_workspace_bytes(dims, DSPARK_OP_VERIFY)) exceeds it return
+ * DSPARK_ERR_WORKSPACE before anything is enqueued; every workload from 4 to 512 requests at
+ * V <= 151936 and gamma <= 15 fits. The call allocates nothing (no hipMalloc, hipFree or
+ * allocating library routine). Every call on one GPU shares that GPU's array and leaves its
+ * contents behind; each call clears what it needs cleared itself. Calls that overlap on one
+ * GPU (concurrent streams or host threads) race on the array and must be serialised by the
+ * caller. DSPARK_ERR_HIP if the array's device address cannot be obtained.
+ */
+#define DSPARK_NOALLOC_SCRATCH_BYTES ((size_t)48 << 20)
+DSPARK_API dspark_status dspark_verify_noalloc(dspark_dims dims, const float* target,
+                                               const int32_t* row_offsets,
+                                               const int32_t* draft_len, const float* U,
+                                               const uint16_t* W1, const uint16_t* W2t,
+                                               const int32_t* anchor, const int32_t* tokens,
+                                               const float* q_tok, const double* lse,
+                                               const float* uniforms, int32_t* accept_len,
+                                               int32_t* next_token, float* beta_emit,
+                                               uint32_t* flags, const dspark_draft_opts* opts,
+                                               void* stream);
+
+/*
  * Draft with the RNN head instead of the Markov head. [CSDN] 4.2, eq. (6); [AIL] "RNN 头（可选）";
  * [V41] "Markov head" (the paper's small-RNN alternative): a recurrent state s summarises the
  * block's prefix. Per request s_0 = 0 and x_0 = anchor[b]; at position k (1-based)

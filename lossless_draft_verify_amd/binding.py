@@ -19,13 +19,14 @@ __all__ = [
     "OP_DRAFT", "OP_CONFIDENCE", "OP_PLAN", "OP_VERIFY", "OP_RNN_DRAFT", "OP_RNN_VERIFY",
     "FLAG_NONFINITE", "FLAG_ZERO_RESIDUAL", "library_path", "load_library", "workspace_bytes",
     "workspace", "markov_draft", "confidence", "plan", "markov_draft_plan", "verify",
-    "rnn_draft", "rnn_verify", "rnn_draft_plan",
+    "rnn_draft", "rnn_verify", "rnn_draft_plan", "verify_noalloc", "NOALLOC_SCRATCH_BYTES",
     "profile_begin", "profile_end", "version",
 ]
 
 FULL_VERIFY, EARLY_STOP, FULL_PATH, LAGGED_TOPK = 0, 1, 2, 3
 OP_DRAFT, OP_CONFIDENCE, OP_PLAN, OP_VERIFY, OP_RNN_DRAFT, OP_RNN_VERIFY = 0, 1, 2, 3, 4, 5
 FLAG_NONFINITE, FLAG_ZERO_RESIDUAL = 1, 2
+NOALLOC_SCRATCH_BYTES = 48 << 20     # DSPARK_NOALLOC_SCRATCH_BYTES
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -106,6 +107,8 @@ def load_library():
         lib.dspark_verify.argtypes = [_CDims] + [_P] * 15 + [_P, ctypes.c_size_t, _P]
         lib.dspark_verify_opts.restype = ctypes.c_int32
         lib.dspark_verify_opts.argtypes = [_CDims] + [_P] * 15 + [_P, ctypes.c_size_t, _P, _P]
+        lib.dspark_verify_noalloc.restype = ctypes.c_int32
+        lib.dspark_verify_noalloc.argtypes = [_CDims] + [_P] * 15 + [_P, _P]
         lib.dspark_rnn_draft.restype = ctypes.c_int32
         lib.dspark_rnn_draft.argtypes = [_CDims] + [_P] * 13 + [_P, ctypes.c_size_t, _P, _P]
         lib.dspark_rnn_verify.restype = ctypes.c_int32
@@ -282,6 +285,31 @@ def verify(dims: Dims, target, row_offsets, draft_len, U, W1, W2t, anchor, token
         _ptr(beta_emit, torch.float32, (B,), "beta_emit"), _ptr(flags, torch.int32, (B,), "flags"),
         _ptr(ws, torch.uint8, None, "ws"), ws.numel(), _opts(temperature, greedy), _stream(stream))
     _check(st, "dspark_verify_opts")
+    return accept_len, next_token, beta_emit, flags
+
+
+def verify_noalloc(dims: Dims, target, row_offsets, draft_len, U, W1, W2t, anchor, tokens, q,
+                   lse, uniforms, *, accept_len, next_token, beta_emit=None, flags=None,
+                   temperature: float = 1.0, greedy: bool = False, stream=None):
+    """The verify on the library's own scratch array (dspark_verify_noalloc): no workspace, and
+    every output is the caller's (nothing is allocated here either). Returns (accept_len,
+    next_token, beta_emit, flags)."""
+    B, g, V, r = dims.B, dims.gamma, dims.V, dims.r
+    if target.dim() != 2 or target.shape[1] != V:
+        raise ValueError("target must be [rows][V]")
+    st = load_library().dspark_verify_noalloc(
+        dims.c(), _ptr(target, torch.float32, None, "target"),
+        _ptr(row_offsets, torch.int32, (B + 1,), "row_offsets"),
+        _ptr(draft_len, torch.int32, (B,), "draft_len"), _ptr(U, torch.float32, (B, g, V), "U"),
+        _ptr(W1, torch.bfloat16, (V, r), "W1"), _ptr(W2t, torch.bfloat16, (V, r), "W2t"),
+        _ptr(anchor, torch.int32, (B,), "anchor"), _ptr(tokens, torch.int32, (B, g), "tokens"),
+        _ptr(q, torch.float32, (B, g), "q"), _ptr(lse, torch.float64, (B, g), "lse"),
+        _ptr(uniforms, torch.float32, (B, g + 1, 3), "uniforms"),
+        _ptr(accept_len, torch.int32, (B,), "accept_len"),
+        _ptr(next_token, torch.int32, (B,), "next_token"),
+        _ptr(beta_emit, torch.float32, (B,), "beta_emit"), _ptr(flags, torch.int32, (B,), "flags"),
+        _opts(temperature, greedy), _stream(stream))
+    _check(st, "dspark_verify_noalloc")
     return accept_len, next_token, beta_emit, flags
 
 

@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "dspark.h"
@@ -326,6 +327,31 @@ dspark_status check_plan(const dspark_dims& dims, const float* conf, const doubl
   return DSPARK_OK;
 }
 
+// Scratch space of dspark_verify_noalloc: a fixed array in device memory, one copy per GPU
+// (each device that loads the library holds its own, until the process ends). Host code never
+// passes the array's name to a kernel: that is a host-side stand-in, not a device address. The
+// device address of the current device's copy comes from hipGetSymbolAddress, once per device,
+// and is kept here.
+constexpr size_t kScratchBytes = DSPARK_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array, or nullptr if HIP cannot give it.
+void* scratch_address() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -558,6 +584,27 @@ dspark_status dspark_verify_opts(dspark_dims dims, const float* target,
   a.greedy = greedy;
   verify_ws(dims, ws, &a.ws);
   return verify_passes(dims, a, static_cast<hipStream_t>(stream));
+}
+
+dspark_status dspark_verify_noalloc(dspark_dims dims, const float* target,
+                                    const int32_t* row_offsets, const int32_t* draft_len,
+                                    const float* U, const uint16_t* W1, const uint16_t* W2t,
+                                    const int32_t* anchor, const int32_t* tokens,
+                                    const float* q_tok, const double* lse, const float* uniforms,
+                                    int32_t* accept_len, int32_t* next_token, float* beta_emit,
+                                    uint32_t* flags, const dspark_draft_opts* opts, void* stream) {
+  // Sizes beyond the scratch array are refused before its address is looked up; the other
+  // checks are those of dspark_verify_opts, which runs the call on the array.
+  if (!dims_ok(dims)) return DSPARK_ERR_SHAPE;
+  if (verify_ws(dims, nullptr, nullptr) > kScratchBytes) return DSPARK_ERR_WORKSPACE;
+  if (!target || !row_offsets || !draft_len || !U || !W1 || !W2t || !anchor || !tokens ||
+      !q_tok || !lse || !uniforms || !accept_len || !next_token)
+    return DSPARK_ERR_NULL;
+  void* ws = scratch_address();
+  if (!ws) return DSPARK_ERR_HIP;
+  return dspark_verify_opts(dims, target, row_offsets, draft_len, U, W1, W2t, anchor, tokens,
+                            q_tok, lse, uniforms, accept_len, next_token, beta_emit, flags, ws,
+                            kScratchBytes, opts, stream);
 }
 
 dspark_status dspark_rnn_verify(dspark_dims dims, const float* target, const int32_t* row_offsets,

@@ -225,3 +225,18 @@ def test_binding_signatures_match_the_header(lib):
             assert _c_kind(c) == _py_kind(py), (name, c, py)
         checked += 1
     assert checked >= 12
+
+
+def test_noalloc_verify_refuses_sizes_beyond_its_scratch(lib):
+    """dspark_verify_noalloc checks the workspace its shape needs against its fixed scratch
+    array on the host, before any HIP call: too large a shape returns DSPARK_ERR_WORKSPACE, a
+    null output DSPARK_ERR_NULL, a bad shape DSPARK_ERR_SHAPE."""
+    P = _p()
+    big = L.Dims(1024, 5, 151936, 256, 8)
+    assert L.workspace_bytes(big, L.OP_VERIFY) > L.NOALLOC_SCRATCH_BYTES
+    args = [P] * 13 + [None, None, None, None]
+    assert lib.dspark_verify_noalloc(big.c(), *args) == 4
+    fits = L.Dims(512, 15, 151936, 256, 8)
+    assert L.workspace_bytes(fits, L.OP_VERIFY) <= L.NOALLOC_SCRATCH_BYTES
+    assert lib.dspark_verify_noalloc(fits.c(), *([P] * 12 + [None] + [None] * 4)) == 1
+    assert lib.dspark_verify_noalloc(L.Dims(4, 3, 1000, 24, 8).c(), *args) == 2
