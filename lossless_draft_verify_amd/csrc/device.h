@@ -57,6 +57,22 @@ __device__ __forceinline__ float exp_term(float x) {
   return __builtin_amdgcn_exp2f(x * 1.44269504088896340736f);
 }
 
+// A probability exp(x - lse) in fp32 from an fp32 logit x and c = lse * log2(e) (fp64, formed
+// once per row). The exponent a = x log2(e) - c is taken in fp64 and split into its nearest
+// integer n and a remainder f in [-1/2, 1/2] (exact in fp64); 2^f comes from the hardware exp2
+// on fp32(f) and 2^n is applied exactly. Rounding f to fp32 moves the result by at most
+// 2^-25 ln 2 relative, so the error is that of the hardware exp2 on [-1/2, 1/2] plus 2e-8,
+// whatever the size of a (no fp32 rounding of a itself). Below 2^-1000 (and for x = -inf or a
+// NaN exponent) the result is 0; it underflows to 0 below 2^-149.
+constexpr double kLog2e64 = 1.4426950408889634073599;
+__device__ __forceinline__ float prob_f32(float x, double c) {
+  double a = __builtin_fma(static_cast<double>(x), kLog2e64, -c);
+  a = (a > -1000.0) ? a : -1000.0;
+  const double n = __builtin_rint(a);
+  const float f = static_cast<float>(a - n);
+  return __builtin_amdgcn_ldexpf(__builtin_amdgcn_exp2f(f), static_cast<int>(n));
+}
+
 // Workgroup barrier for an LDS hand-off that leaves global loads in flight: __syncthreads()
 // carries a workgroup fence, which waits for every outstanding global load before s_barrier
 // and would serialise a software prefetch issued just before it.

@@ -259,21 +259,21 @@ __device__ __forceinline__ int32_t emit_prev(const VerifyArgs& p, int b, int j) 
   return (j == 1) ? p.anchor[b] : p.tokens[static_cast<size_t>(b) * p.gamma + j - 2];
 }
 
-// Draft probability of one token: softmax(beta L) of the position (lse_d its log-sum-exp, beta
-// the draft temperature's multiplier, applied in fp32 as in the draft), or, for a greedy draft,
-// the point mass on the drafted token.
-__device__ __forceinline__ double draft_prob(float L, float beta, double lse_d, bool greedy,
-                                             bool drafted) {
-  return greedy ? (drafted ? 1.0 : 0.0) : exp(static_cast<double>(L * beta) - lse_d);
+// Draft probability of one token in fp32 (prob_f32): softmax(beta L) of the position (cd its
+// log-sum-exp times log2(e), beta the draft temperature's multiplier, applied in fp32 as in the
+// draft), or, for a greedy draft, the point mass on the drafted token.
+__device__ __forceinline__ float draft_prob(float L, float beta, double cd, bool greedy,
+                                            bool drafted) {
+  return greedy ? (drafted ? 1.0f : 0.0f) : prob_f32(L * beta, cd);
 }
 // The same with the kind of draft fixed at compile time (the residual passes, where a run-time
 // select per token is measurable; a greedy pass never reads the draft logits).
 template <bool Greedy>
-__device__ __forceinline__ double draft_prob_t(float L, float beta, double lse_d, bool drafted) {
+__device__ __forceinline__ float draft_prob_t(float L, float beta, double cd, bool drafted) {
   if constexpr (Greedy) {
-    return drafted ? 1.0 : 0.0;
+    return drafted ? 1.0f : 0.0f;
   } else {
-    return exp(static_cast<double>(L * beta) - lse_d);
+    return prob_f32(L * beta, cd);
   }
 }
 
@@ -286,14 +286,20 @@ __device__ __forceinline__ float pick(float a, float b, uint32_t sel) {
   return __uint_as_float(__builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), sel));
 }
 
-// Residual weight and overlap of one token: w = max(0, p_t - p_d), o = min(p_t, p_d), with
-// NaN behaving as in the comparisons written here (a NaN difference gives w = 0).
-__device__ __forceinline__ void residual_pair(double pd, float t, double lse_t, double& w,
-                                              double& o) {
-  const double pt = exp(static_cast<double>(t) - lse_t);
-  const double d = pt - pd;
-  w = (0.0 < d) ? d : 0.0;
+// Residual weight and overlap of one token in fp32: w = max(0, p_t - p_d), o = min(p_t, p_d),
+// with p_t = exp(t - lse_t) from prob_f32 (ct = lse_t log2(e)). Every site that forms these
+// terms (the residual pass, its fallback and the emission's tile walk) calls this, so the walk
+// sees the bits the tile sums were made of.
+__device__ __forceinline__ void residual_pair(float pd, float t, double ct, float& w, float& o) {
+  const float pt = prob_f32(t, ct);
+  const float d = pt - pd;
+  w = (0.0f < d) ? d : 0.0f;
   o = (pd < pt) ? pd : pt;
+}
+
+// Sum of eight fp32 terms as a balanced tree (three rounding levels), widened to fp64.
+__device__ __forceinline__ double sum8(const float (&x)[8]) {
+  return static_cast<double>(((x[0] + x[1]) + (x[2] + x[3])) + ((x[4] + x[5]) + (x[6] + x[7])));
 }
 
 template <int KS, bool Greedy, int NT>
@@ -360,12 +366,12 @@ __global__ __launch_bounds__(kBlock, 2) void residual_partials_kernel(VerifyArgs
           const int j = p.ws.epos[b];
           const float* Urow = p.U + (static_cast<size_t>(b) * p.gamma + j - 1) * p.V;
           const float* trow = p.target + static_cast<size_t>(p.ws.erow[b]) * p.V;
-          const double lse_d = p.lse[static_cast<size_t>(b) * p.gamma + j - 1];
-          const double lse_t = p.ws.erow_lse[b];
+          const double cd = p.lse[static_cast<size_t>(b) * p.gamma + j - 1] * kLog2e64;
+          const double ct = p.ws.erow_lse[b] * kLog2e64;
           const int32_t xtok = p.tokens[static_cast<size_t>(b) * p.gamma + j - 1];
           float L[16];
           tile_logits(acc, Urow, tok0, p.V, half, vec4, L);
-          double W = 0.0, O = 0.0;
+          float w8[2][8], o8[2][8];
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const int v = tok0 + 8 * g + 4 * half;
@@ -373,15 +379,16 @@ __global__ __launch_bounds__(kBlock, 2) void residual_partials_kernel(VerifyArgs
             load4(trow, v, p.V, vec4, t);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              if (v + e < p.V) {
-                double w, o;
-                residual_pair(draft_prob_t<Greedy>(L[4 * g + e], p.beta, lse_d, v + e == xtok),
-                              t[e], lse_t, w, o);
-                W += w;
-                O += o;
-              }
+              float w = 0.0f, o = 0.0f;
+              if (v + e < p.V)
+                residual_pair(draft_prob_t<Greedy>(L[4 * g + e], p.beta, cd, v + e == xtok),
+                              t[e], ct, w, o);
+              w8[g >> 1][4 * (g & 1) + e] = w;
+              o8[g >> 1][4 * (g & 1) + e] = o;
             }
           }
+          double W = sum8(w8[0]) + sum8(w8[1]);
+          double O = sum8(o8[0]) + sum8(o8[1]);
           W = W + lane_xor<32>(W);
           O = O + lane_xor<32>(O);
           if (half == 0) {
@@ -588,7 +595,7 @@ __device__ __forceinline__ void residual_dma(const VerifyArgs& p) {
       e[s] = *reinterpret_cast<const u16x8_t*>(
           eb + 16 * (row_own * D::kW2Chunks + ((2 * s + half) ^ (row_own & D::kW2Swz))));
   }
-  const double lse_d = rec[row_own].lse_d, lse_t = rec[row_own].lse_t;
+  const double cd = rec[row_own].lse_d * kLog2e64, ct = rec[row_own].lse_t * kLog2e64;
   const int32_t xtok = rec[row_own].tok;
   lds_barrier();
   int flushed = 0;
@@ -629,7 +636,7 @@ __device__ __forceinline__ void residual_dma(const VerifyArgs& p) {
 #pragma unroll
         for (int q = 0; q < 8; ++q)
           Lh[q] = (PW == 1) ? pick(acc[q], acc[8 + q], part_sel) : acc[8 * pp + q];
-        double W = 0.0, O = 0.0;
+        float w8[8], o8[8];
         auto half_tile = [&](auto checked) {
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
@@ -638,14 +645,13 @@ __device__ __forceinline__ void residual_dma(const VerifyArgs& p) {
             const float t4[4] = {tt[pp][h].x, tt[pp][h].y, tt[pp][h].z, tt[pp][h].w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              if (!decltype(checked)::value || v + i < p.V) {
-                double w, o;
-                residual_pair(draft_prob_t<Greedy>(u4[i] + Lh[4 * h + i], p.beta, lse_d,
+              float w = 0.0f, o = 0.0f;
+              if (!decltype(checked)::value || v + i < p.V)
+                residual_pair(draft_prob_t<Greedy>(u4[i] + Lh[4 * h + i], p.beta, cd,
                                                    v + i == xtok),
-                              t4[i], lse_t, w, o);
-                W += w;
-                O += o;
-              }
+                              t4[i], ct, w, o);
+              w8[4 * h + i] = w;
+              o8[4 * h + i] = o;
             }
           }
         };
@@ -653,6 +659,7 @@ __device__ __forceinline__ void residual_dma(const VerifyArgs& p) {
           half_tile(std::false_type{});
         else
           half_tile(std::true_type{});
+        double W = sum8(w8), O = sum8(o8);
         W = W + other_half(W, half);
         O = O + other_half(O, half);
         if (half == 0 && row_own < gcount)
@@ -765,15 +772,16 @@ __global__ __launch_bounds__(kBlock) void emit_sample_kernel(VerifyArgs p) {
       recompute_tile_lds<KS, NT>(Es, p.W2t, Urow, tok0, p.V, Ls);
       __builtin_amdgcn_s_waitcnt(0);
       __builtin_amdgcn_wave_barrier();
-      double w = 0.0;
+      float w = 0.0f;
       if (lane < kTileTokens && tok0 + lane < p.V) {
-        double ov;
+        float ov;
         const int32_t xtok = p.tokens[static_cast<size_t>(b) * p.gamma + j - 1];
-        residual_pair(draft_prob(Ls[lane], p.beta, p.lse[static_cast<size_t>(b) * p.gamma + j - 1],
+        residual_pair(draft_prob(Ls[lane], p.beta,
+                                 p.lse[static_cast<size_t>(b) * p.gamma + j - 1] * kLog2e64,
                                  p.greedy, tok0 + lane == xtok),
-                      tv, p.ws.erow_lse[b], w, ov);
+                      tv, p.ws.erow_lse[b] * kLog2e64, w, ov);
       }
-      token = tok0 + walk_tile(w, L.before, L.target, L.take_last != 0);
+      token = tok0 + walk_tile(static_cast<double>(w), L.before, L.target, L.take_last != 0);
     }
   } else if (tid == 0 && p.beta_emit) {
     p.beta_emit[b] = -1.0f;
