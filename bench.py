@@ -10,6 +10,10 @@ each set's own draft logits plus noise, laid out in the planner's packed rows.
 Prints one JSON line. `value` comes from K timed rounds with nothing recorded between launches;
 per-kernel durations (and the roofline of the draft step kernel) come from a second pass of the
 same K rounds with HIP events recorded around every library launch on the launch stream.
+
+`--workload` runs another of the workloads instead (the full-verify ones as draft, plan and
+verify; the lagged one with each input set's confidence ring in its steady state), reported
+the same way under that workload's name.
 """
 import argparse
 import hashlib
@@ -59,13 +63,20 @@ def traffic_from_profiles(launch_units):
     return float(f.group(1))
 
 
+# Round index given to the lagged planner in timed rounds: from round 2 on it reads the ring.
+LAG_ROUND = 2
+
+
 class InputSet:
     def __init__(self, wl, wts, round_index, dev, opts, head="markov"):
         d = L.Dims(wl.B, wl.gamma, wl.V, wl.r, wl.d)
-        inp = W.round_inputs(wl, round_index, dev, with_hidden=True, with_noise=True)
-        self.anchor, self.U, self.h, self.uniforms = inp["anchor"], inp["U"], inp["h"], inp["uniforms"]
+        full = wl.mode == W.FULL_VERIFY
+        inp = W.round_inputs(wl, round_index, dev, with_hidden=not full, with_noise=True)
+        self.anchor, self.U, self.h, self.uniforms = (inp["anchor"], inp["U"], inp.get("h"),
+                                                      inp["uniforms"])
         self.T = W.temperatures(wl).to(dev)
         self.sps = torch.tensor(W.sps_table(wl), dtype=torch.float64, device=dev)
+        self.ring = None
         # Untimed pass: draft with debug logits -> target stand-in = logits + noise; the plan of
         # this pass fixes the packed row layout (the timed rounds recompute the same plan).
         logits = torch.empty_like(self.U)
@@ -75,8 +86,18 @@ class InputSet:
         else:
             tok, q, lse = L.markov_draft(d, self.U, wts["W1"], wts["W2t"], self.anchor,
                                          self.uniforms, logits_dbg=logits, **opts)
-        conf = L.confidence(d, self.h, wts["W1"], wts["w"], self.T, self.anchor, tok)
-        dl, ro, st = L.plan(d, conf, self.sps, wl.mode)
+        if full:
+            dl, ro, st = L.plan(d, None, self.sps, wl.mode)
+        else:
+            conf = L.confidence(d, self.h, wts["W1"], wts["w"], self.T, self.anchor, tok)
+            if wl.mode == W.LAGGED_TOPK:
+                # steady state of the lag ring: the slot a timed round reads holds this set's own
+                # confidences (as two rounds earlier), and the round writes the same values back
+                self.ring = torch.stack([conf, conf]).contiguous()
+                dl, ro, st = L.plan(d, conf, self.sps, wl.mode, ring=self.ring,
+                                    round_index=LAG_ROUND)
+            else:
+                dl, ro, st = L.plan(d, conf, self.sps, wl.mode)
         dense = W.target_dense(logits, inp["U_bonus"], inp["noise"])
         del logits, inp
         self.target = W.pack_rows(dense, dl)
@@ -94,63 +115,106 @@ def algorithmic_bytes(wl, rows, n_res, greedy=False, head="markov"):
     states and the hidden block of Wgco once, the state and embedding blocks of Wgco per step,
     and the fp32 bias vectors written by the draft and read by the verify."""
     B, V, g, r, d = wl.B, wl.V, wl.gamma, wl.r, wl.d
-    draft = g * (4 * B * V + 2 * r * V)
+    draft = g * step_bytes(wl)
     if head == "rnn":
         draft += 2 * B * g * d + 2 * 3 * r * d + g * 2 * 3 * r * 2 * r + 2 * 4 * B * g * r
-    conf = 2 * B * g * d + 2 * (d + r)
-    stats = 4 * rows * V
+    conf = 0 if wl.mode == W.FULL_VERIFY else 2 * B * g * d + 2 * (d + r)
+    return draft + conf + stats_bytes(wl, rows) + residual_bytes(wl, n_res, greedy)
+
+
+def step_bytes(wl):
+    """One draft step: the U slice of the position and W2."""
+    return 4 * wl.B * wl.V + 2 * wl.r * wl.V
+
+
+def stats_bytes(wl, rows):
+    """Target row statistics: every verified row once."""
+    return 4 * rows * wl.V
+
+
+def residual_bytes(wl, n_res, greedy=False):
+    """Residual pass: W2 once plus the U and target rows of each rejected request (the target
+    rows only for a greedy draft, whose draft distribution is a point mass)."""
     if greedy:
-        emit = n_res * 4 * V
-    else:
-        emit = (2 * r * V if n_res > 0 else 0) + n_res * 8 * V
-    return draft + conf + stats + emit
+        return n_res * 4 * wl.V
+    return (2 * wl.r * wl.V if n_res > 0 else 0) + n_res * 8 * wl.V
 
 
-def cpu_baseline(wl, wts, s, threads, opts, head="markov"):
-    """The oracle as it stands, timed on the host on one full round of the same workload."""
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(wl, wts, s, threads, opts, head="markov", reps=3):
+    """The oracle as it stands, timed on the host: `reps` full rounds of the same workload on
+    the same inputs (the median is reported); building the target stand-in is not timed."""
     import oracle
     host = lambda t: t.detach().cpu().numpy()
     bits = W.bf16_bits
     U, W1b, W2b = host(s.U), bits(wts["W1"]), bits(wts["W2t"])
-    anchor, unif, h = host(s.anchor), host(s.uniforms), bits(s.h)
+    anchor, unif = host(s.anchor), host(s.uniforms)
+    h = bits(s.h) if s.h is not None else None
+    Wg = bits(wts["Wgco"]) if head == "rnn" else None
     sps = W.sps_table(wl)
-    t0 = time.perf_counter()
-    if head == "rnn":
-        Wg = bits(wts["Wgco"])
-        o = oracle.rnn_draft(U, W1b, W2b, Wg, h, anchor, unif, want_logits=True, threads=threads,
-                             **opts)
-    else:
-        o = oracle.markov_draft(U, W1b, W2b, anchor, unif, want_logits=True, threads=threads,
-                                **opts)
-    c = oracle.confidence(h, W1b, bits(wts["w"]), W.temperatures(wl).numpy(), anchor, o["tokens"],
-                          threads=threads)
-    p = oracle.plan(c["conf"], sps, wl.mode)
-    t1 = time.perf_counter()
-    # target stand-in (not timed): the oracle's own logits + noise, packed by its own plan
-    noise = host(W.round_inputs(wl, 0, "cuda", with_hidden=False)["noise"])
-    ub = host(W.round_inputs(wl, 0, "cuda", with_hidden=False, with_noise=False)["U_bonus"])
-    dense = np.concatenate([o["logits"], ub[:, None, :]], 1) + noise
-    keep = np.arange(wl.gamma + 1)[None, :] <= p["draft_len"][:, None]
-    target = np.ascontiguousarray(dense[keep], dtype=np.float32)
-    del dense, noise
-    t2 = time.perf_counter()
-    if head == "rnn":
-        oracle.rnn_verify(target, p["row_offsets"], p["draft_len"], U, W1b, W2b, Wg, h, anchor,
+    full = wl.mode == W.FULL_VERIFY
+    target = None
+    secs = []
+    for rep in range(reps):
+        t0 = time.perf_counter()
+        if head == "rnn":
+            o = oracle.rnn_draft(U, W1b, W2b, Wg, h, anchor, unif, want_logits=rep == 0,
+                                 threads=threads, **opts)
+        else:
+            o = oracle.markov_draft(U, W1b, W2b, anchor, unif, want_logits=rep == 0,
+                                    threads=threads, **opts)
+        if full:
+            p = oracle.plan(None, sps, wl.mode, B=wl.B, gamma=wl.gamma)
+        else:
+            c = oracle.confidence(h, W1b, bits(wts["w"]), W.temperatures(wl).numpy(), anchor,
+                                  o["tokens"], threads=threads)
+            if wl.mode == W.LAGGED_TOPK:
+                ring = np.stack([c["conf"], c["conf"]])
+                p = oracle.plan(c["conf"], sps, wl.mode, ring=ring, round_index=LAG_ROUND)
+            else:
+                p = oracle.plan(c["conf"], sps, wl.mode)
+        t1 = time.perf_counter()
+        if target is None:
+            # target stand-in (not timed): the oracle's own logits + noise, packed by its plan
+            inp = W.round_inputs(wl, 0, "cuda", with_hidden=False)
+            dense = np.concatenate([o["logits"], host(inp["U_bonus"])[:, None, :]], 1)
+            dense += host(inp["noise"])
+            del inp
+            keep = np.arange(wl.gamma + 1)[None, :] <= p["draft_len"][:, None]
+            target = np.ascontiguousarray(dense[keep], dtype=np.float32)
+            del dense
+        t2 = time.perf_counter()
+        if head == "rnn":
+            oracle.rnn_verify(target, p["row_offsets"], p["draft_len"], U, W1b, W2b, Wg, h,
+                              anchor, o["tokens"], o["q"], unif, threads=threads, **opts)
+        else:
+            oracle.verify(target, p["row_offsets"], p["draft_len"], U, W1b, W2b, anchor,
                           o["tokens"], o["q"], unif, threads=threads, **opts)
-    else:
-        oracle.verify(target, p["row_offsets"], p["draft_len"], U, W1b, W2b, anchor, o["tokens"],
-                      o["q"], unif, threads=threads, **opts)
-    t3 = time.perf_counter()
-    sec = (t1 - t0) + (t3 - t2)
+        t3 = time.perf_counter()
+        secs.append((t1 - t0) + (t3 - t2))
+    sec = float(np.median(secs))
     return {"value": 1.0 / sec, "unit": "rounds/s", "cores": threads, "kind": "oracle",
-            "sample": f"one full round of {wl.name} (all {wl.B} requests: {head}-head draft, "
-                      f"confidence, "
-                      f"plan, verify; target construction excluded), {sec:.2f} s"}
+            "cpu": cpu_model(),
+            "sample": f"{reps} full rounds of {wl.name} (all {wl.B} requests: {head}-head draft, "
+                      f"{'' if full else 'confidence, '}plan, verify; target construction "
+                      f"excluded), median {sec:.2f} s a round "
+                      f"({', '.join(f'{x:.2f}' for x in secs)})"}
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--workload", choices=sorted(W.WORKLOADS), default=WORKLOAD,
+                    help="workload of the timed rounds (default: the headline one)")
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--sets", type=int, default=3)
@@ -183,7 +247,12 @@ def main():
         sys.exit(2)
 
     dev = "cuda"
-    wl = W.WORKLOADS[WORKLOAD]
+    wl = W.WORKLOADS[args.workload]
+    full = wl.mode == W.FULL_VERIFY
+    if args.head == "rnn" and full:
+        print("the RNN head reads hidden states, which the full-verify workloads do not have",
+              file=sys.stderr)
+        sys.exit(2)
     d = L.Dims(wl.B, wl.gamma, wl.V, wl.r, wl.d)
     L.load_library()
     wts = W.weights(wl, dev)
@@ -209,17 +278,27 @@ def main():
     be = torch.empty(B, dtype=torch.float32, device=dev)
     fl = torch.empty(B, dtype=torch.int32, device=dev)
 
+    lag = dict(ring=None, round_index=0)
+
+    def plan_args(s):
+        return dict(ring=s.ring, round_index=LAG_ROUND) if s.ring is not None else lag
+
     def round_markov(s):
-        if args.separate_plan:
+        if full:
+            L.markov_draft(d, s.U, wts["W1"], wts["W2t"], s.anchor, s.uniforms, tokens=tok, q=q,
+                           lse=lse, ws=ws_d, **opts)
+            L.plan(d, None, s.sps, wl.mode, draft_len=dl, row_offsets=ro, stats=st)
+        elif args.separate_plan:
             L.markov_draft(d, s.U, wts["W1"], wts["W2t"], s.anchor, s.uniforms, tokens=tok, q=q,
                            lse=lse, ws=ws_d, **opts)
             L.confidence(d, s.h, wts["W1"], wts["w"], s.T, s.anchor, tok, conf=conf)
-            L.plan(d, conf, s.sps, wl.mode, draft_len=dl, row_offsets=ro, stats=st)
+            L.plan(d, conf, s.sps, wl.mode, draft_len=dl, row_offsets=ro, stats=st,
+                   **plan_args(s))
         else:
             L.markov_draft_plan(d, s.U, wts["W1"], wts["W2t"], s.anchor, s.uniforms, s.h,
                                 wts["w"], s.T, s.sps, wl.mode, tokens=tok, q=q, lse=lse,
                                 conf=conf, draft_len=dl, row_offsets=ro, stats=st, ws=ws_d,
-                                **opts)
+                                **plan_args(s), **opts)
         L.verify(d, s.target, ro, dl, s.U, wts["W1"], wts["W2t"], s.anchor, tok, q, lse,
                  s.uniforms, accept_len=al, next_token=nt, beta_emit=be, flags=fl, ws=ws_v,
                  **opts)
@@ -229,12 +308,13 @@ def main():
             L.rnn_draft(d, s.U, wts["W1"], wts["W2t"], wts["Wgco"], s.h, s.anchor, s.uniforms,
                         tokens=tok, q=q, lse=lse, e_rows=e_rows, ws=ws_d, **opts)
             L.confidence(d, s.h, wts["W1"], wts["w"], s.T, s.anchor, tok, conf=conf)
-            L.plan(d, conf, s.sps, wl.mode, draft_len=dl, row_offsets=ro, stats=st)
+            L.plan(d, conf, s.sps, wl.mode, draft_len=dl, row_offsets=ro, stats=st,
+                   **plan_args(s))
         else:
             L.rnn_draft_plan(d, s.U, wts["W1"], wts["W2t"], wts["Wgco"], s.h, s.anchor, s.uniforms,
                              wts["w"], s.T, s.sps, wl.mode, tokens=tok, q=q, lse=lse,
                              e_rows=e_rows, conf=conf, draft_len=dl, row_offsets=ro, stats=st,
-                             ws=ws_d, **opts)
+                             ws=ws_d, **plan_args(s), **opts)
         L.rnn_verify(d, s.target, ro, dl, s.U, wts["W2t"], e_rows, tok, q, lse, s.uniforms,
                      accept_len=al, next_token=nt, beta_emit=be, flags=fl, ws=ws_v, **opts)
 
@@ -324,17 +404,38 @@ def main():
     for name, (cnt, ms) in kern.items():
         if cnt:
             kernels[name] = {"launches": cnt, "avg_us": 1e3 * ms / cnt}
+    streaming = {}
+    # algorithmic bytes per launch of each streaming kernel, averaged over the timed rounds
+    per_launch = {
+        "markov_step": step_bytes(wl),
+        "target_stats": float(np.mean([stats_bytes(wl, u["rows"]) for u in used])),
+        "residual_partials": float(np.mean([residual_bytes(wl, u["n_res"], args.greedy)
+                                            for u in used])),
+    }
+    for name, nbytes in per_launch.items():
+        if name in kernels and nbytes > 0:
+            gbs = nbytes / (kernels[name]["avg_us"] * 1e-6) / 1e9
+            streaming[name] = {"bytes_per_launch": round(nbytes), "avg_us": round(kernels[name]["avg_us"], 3),
+                               "achieved_gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
     if "markov_step" in kernels:
-        step_bytes = 4 * wl.B * wl.V + 2 * wl.r * wl.V        # U slice + W2 per launch
+        sb = step_bytes(wl)                                     # U slice + W2 per launch
         avg_s = kernels["markov_step"]["avg_us"] * 1e-6
-        achieved = step_bytes / avg_s / 1e9
-        # the committed counters were taken on the Markov head's step kernel
-        traffic = traffic_from_profiles(1) if args.head == "markov" else None
+        achieved = sb / avg_s / 1e9
+        # the committed counters were taken on the Markov head's step kernel at the headline
+        # workload
+        traffic = (traffic_from_profiles(1) if args.head == "markov" and wl.name == WORKLOAD
+                   else None)
         roofline = {"kernel": "markov_step", "bound": "hbm", "achieved": round(achieved, 1),
                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                     "traffic": traffic, "traffic_unit": "bytes per launch",
-                    "algorithmic_bytes_per_launch": step_bytes,
-                    "avg_launch_us": round(kernels["markov_step"]["avg_us"], 3)}
+                    "algorithmic_bytes_per_launch": sb,
+                    "avg_launch_us": round(kernels["markov_step"]["avg_us"], 3),
+                    "timing": "HIP events recorded with each dispatch (dspark_profile_begin/end), "
+                              "averaged over the K rounds of the kernel-timing pass",
+                    "worst_streaming_kernel": (min(streaming, key=lambda k: streaming[k]["frac"])
+                                               if streaming else None),
+                    "worst_streaming_frac": (min(v["frac"] for v in streaming.values())
+                                             if streaming else None)}
         # the W2 contraction per launch; the RNN head's bias vector enters it as three bf16 terms
         terms = 3 if args.head == "rnn" else 1
         flops = 2.0 * wl.B * wl.r * wl.V * terms
@@ -352,11 +453,17 @@ def main():
 
     base = None
     if not args.no_cpu_baseline:
-        threads = min(16, os.cpu_count() or 1)
+        # every host core this process may run on, up to the 16 one GPU's job gets on the box
+        threads = min(16, len(os.sched_getaffinity(0)) or 1)
         base = cpu_baseline(wl, wts, sets[0], threads, opts, args.head)
 
+    metric = (METRIC if wl.name == WORKLOAD else
+              f"spec rounds/s at B={wl.B},V={wl.V},γ={wl.gamma}; achieved HBM GB/s vs peak")
+    plan_name = {W.FULL_VERIFY: "full_verify", W.EARLY_STOP: "early_stop",
+                 W.FULL_PATH: "full_path", W.LAGGED_TOPK: "lagged_topk"}[wl.mode]
+    sps_name = "flat" if wl.sps_kind == "flat" else f"1/(1+n/{wl.sps_scale:g})"
     out = {
-        "metric": METRIC,
+        "metric": metric,
         "value": round(rounds_per_s, 2),
         "unit": "rounds/s",
         "n_gpus": 1,
@@ -368,13 +475,14 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16 mfma / f32 / f64",
         "data": "synthetic",
-        "config": {"workload": WORKLOAD, "B": wl.B, "V": wl.V, "gamma": wl.gamma, "r": wl.r,
-                   "d": wl.d, "plan": "early_stop", "sps": "1/(1+n/768)", "input_sets": len(sets),
+        "config": {"workload": wl.name, "B": wl.B, "V": wl.V, "gamma": wl.gamma, "r": wl.r,
+                   "d": wl.d, "plan": plan_name, "sps": sps_name, "input_sets": len(sets),
                    "parallelism": "1 GPU", "launch": "eager",
                    "draft": ("greedy" if args.greedy
                              else f"sampled at temperature {args.temperature:g}"),
                    "head": args.head,
-                   "plan_launch": ("own call" if args.separate_plan
+                   "plan_launch": ("own call (full verify: no confidence head)" if full
+                                   else "own call" if args.separate_plan
                                    else "beside the last draft step")},
         "round_us": round_us,
         "graph_rounds_per_s": (round(args.steps / elapsed_graph, 2)
@@ -384,6 +492,7 @@ def main():
         "round_algorithmic_gbs": round(bytes_per_round * rounds_per_s / 1e9, 1),
         "round_hbm_frac": round(bytes_per_round * rounds_per_s / 1e9 / HBM_PEAK_GBS, 4),
         "roofline": roofline,
+        "streaming_kernels": streaming,
         "mfma": mfma,
         "kernels_us": {k: round(v["avg_us"], 2) for k, v in kernels.items()},
         "ms_per_step_with_kernel_events": (round(1e3 * elapsed_ev / args.steps, 4)
