@@ -45,7 +45,7 @@ def _load():
         _lib = ctypes.CDLL(_LIB_PATH)
         for name in ("oracle_markov_draft", "oracle_markov_draft_opts", "oracle_confidence",
                      "oracle_plan", "oracle_verify", "oracle_verify_opts", "oracle_rnn_draft",
-                     "oracle_rnn_verify"):
+                     "oracle_rnn_verify", "oracle_tree_draft", "oracle_tree_verify"):
             getattr(_lib, name).restype = ctypes.c_int
     return _lib
 
@@ -237,4 +237,55 @@ def rnn_verify(target, row_offsets, draft_len, U, W1, W2t, Wgco, h, anchor, toke
                                _ptr(out["accept_margin"]), _ptr(out["emit_margin"]),
                                _ptr(out["resid_mass"]), int(threads))
     _check(rc, "oracle_rnn_verify")
+    return out
+
+
+def tree_candidates(gamma, c, M):
+    """Number of candidate nodes a tree draft expands: c at depth 1, min(M, previous) * c after."""
+    total, width = c, c
+    for _ in range(2, gamma + 1):
+        width = min(M, width) * c
+        total += width
+    return total
+
+
+def tree_draft(U, W1, W2t, anchor, c, M, N, threads=0):
+    """PCTree draft: c children a node, M nodes expanded a depth, N nodes kept.
+    Returns dict(token, depth, parent [B][N] int32, q, path [B][N] f64, logit_margin,
+    path_margin [B] f64); nodes in rank order, parent = rank of the parent (-1: the root)."""
+    lib = _load()
+    U = _c(U, np.float32)
+    B, g, V = U.shape
+    W1, W2t = _bits(W1), _bits(W2t)
+    r = W1.shape[1]
+    out = dict(token=np.zeros((B, N), np.int32), depth=np.zeros((B, N), np.int32),
+               parent=np.zeros((B, N), np.int32), q=np.zeros((B, N), np.float64),
+               path=np.zeros((B, N), np.float64), logit_margin=np.zeros(B, np.float64),
+               path_margin=np.zeros(B, np.float64))
+    rc = lib.oracle_tree_draft(B, g, V, r, int(c), int(M), int(N), _ptr(U), _ptr(W1), _ptr(W2t),
+                               _ptr(_c(anchor, np.int32)), _ptr(out["token"]), _ptr(out["depth"]),
+                               _ptr(out["parent"]), _ptr(out["q"]), _ptr(out["path"]),
+                               _ptr(out["logit_margin"]), _ptr(out["path_margin"]), int(threads))
+    _check(rc, "oracle_tree_draft")
+    return out
+
+
+def tree_verify(target, token, depth, parent, uniforms, threads=0):
+    """Lossless verify of a tree. target [B][N+1][V] f32 (row 0: after the anchor; row 1+n:
+    after node n). Returns dict(accept_len, path [B][gamma], next_token, flags, margin)."""
+    lib = _load()
+    target = _c(target, np.float32)
+    B, n1, V = target.shape
+    N = n1 - 1
+    uniforms = _c(uniforms, np.float32)
+    g = uniforms.shape[1] - 1
+    out = dict(accept_len=np.zeros(B, np.int32), path=np.zeros((B, g), np.int32),
+               next_token=np.zeros(B, np.int32), flags=np.zeros(B, np.uint32),
+               margin=np.zeros(B, np.float64))
+    rc = lib.oracle_tree_verify(B, g, V, N, _ptr(target), _ptr(_c(token, np.int32)),
+                                _ptr(_c(depth, np.int32)), _ptr(_c(parent, np.int32)),
+                                _ptr(uniforms), _ptr(out["accept_len"]), _ptr(out["path"]),
+                                _ptr(out["next_token"]), _ptr(out["flags"]), _ptr(out["margin"]),
+                                int(threads))
+    _check(rc, "oracle_tree_verify")
     return out

@@ -753,3 +753,245 @@ int oracle_rnn_verify(int B, int gamma, int V, int r, int d, const float* target
 }
 
 }  // extern "C"
+
+// ---- PCTree: tree drafting scored by the Markov head, and its lossless verify ----------------
+//
+// [ZDS] "后续工作" (PCTree): the single draft chain becomes a tree. The Markov head already
+// scores every child token under a given parent token, so it picks the candidate children of
+// each parent node directly, and the most likely paths are kept within a fixed verify budget;
+// no retraining and no extra backbone pass. Readings taken where the page is silent:
+//   - The backbone's base logits U_k of a position are shared by every node at that depth (the
+//     backbone runs once); a node's token x scores the next depth's children by
+//     softmax(fp32(U_k + fp32(W1[x] W2))) (eqs. (4), (5)), the root being the anchor.
+//   - A node expands its c best children: the c largest fp32 logits, the smaller id first on a
+//     tie.
+//   - A node's path probability P is the product of the Markov probabilities along its path
+//     (fp64). Depth 1 expands the root; depth k >= 2 expands the M nodes of depth k - 1 with the
+//     largest P (key (-P, index), the index counting a depth's candidates parent by parent in
+//     the expanded order and child by child in rank order).
+//   - The verify budget N keeps the N candidates of all depths with the largest P (key (-P,
+//     depth, index)). A child's P is at most its parent's and the key puts the parent first on a
+//     tie, so the kept set is a tree.
+namespace {
+
+struct TreeCand {
+  double P;        // path probability
+  double q;        // the Markov probability of the token under its parent
+  int depth;       // 1..gamma
+  int idx;         // index within its depth's candidates
+  int parent;      // position of the parent in `all` (-1: the root)
+  int32_t token;
+};
+
+// The c largest logits of L (the smaller id first on a tie), and the smallest gap between two
+// consecutive logits of the c + 1 largest (the decisions that fix the children and their order).
+void top_children(const std::vector<float>& L, int c, std::vector<int32_t>& out, double* gap) {
+  const int V = static_cast<int>(L.size());
+  const int n = std::min(V, c + 1);
+  std::vector<int32_t> ids(V);
+  for (int v = 0; v < V; ++v) ids[v] = v;
+  std::partial_sort(ids.begin(), ids.begin() + n, ids.end(), [&](int32_t a, int32_t b) {
+    if (L[a] != L[b]) return L[a] > L[b];
+    return a < b;
+  });
+  out.assign(ids.begin(), ids.begin() + c);
+  for (int i = 0; i + 1 < n; ++i)
+    *gap = std::min(*gap, static_cast<double>(L[ids[i]]) - static_cast<double>(L[ids[i + 1]]));
+}
+
+// Smallest relative gap between consecutive path probabilities of a ranked list among ranks
+// 0 .. upto (so with upto = the number kept, the boundary with the first one left out counts).
+void rank_gaps(const std::vector<double>& P, int upto, double* gap) {
+  const int n = std::min<int>(static_cast<int>(P.size()), upto + 1);
+  for (int i = 0; i + 1 < n; ++i)
+    if (P[i] > 0.0) *gap = std::min(*gap, (P[i] - P[i + 1]) / P[i]);
+}
+
+}  // namespace
+
+extern "C" {
+
+// Tree draft. U [B][gamma][V] f32, W1/W2t bf16 [V][r], anchor [B]; c children a node, M nodes
+// expanded a depth (depth >= 2), N nodes kept. Outputs per request, nodes in rank order (key
+// (-P, depth, index)): node_token, node_depth (1..gamma), node_parent (rank of the parent node,
+// -1 for the root) [B][N] int32; node_q (the token's Markov probability under its parent) and
+// node_path (P) [B][N] f64. logit_margin / path_margin (nullable, [B]): the smallest logit gap
+// among any expanded node's c + 1 largest logits, and the smallest relative gap between
+// consecutive path probabilities in the depth rankings (up to the M-th) and the final ranking
+// (up to the N-th). Returns 1 on bad sizes (1 <= M <= c <= V, 1 <= N <= the candidate count).
+int oracle_tree_draft(int B, int gamma, int V, int r, int c, int M, int N, const float* U,
+                      const uint16_t* W1, const uint16_t* W2t, const int32_t* anchor,
+                      int32_t* node_token, int32_t* node_depth, int32_t* node_parent,
+                      double* node_q, double* node_path, double* logit_margin,
+                      double* path_margin, int threads) {
+  if (B < 1 || gamma < 1 || V < 2 || r < 1 || c < 1 || M < 1 || M > c || c > V) return 1;
+  int64_t total = c, width = c;
+  for (int k = 2; k <= gamma; ++k) {
+    width = std::min<int64_t>(M, width) * c;
+    total += width;
+  }
+  if (N < 1 || N > total) return 1;
+  parallel_for(B, threads, [&](int64_t b) {
+    double lgap = std::numeric_limits<double>::infinity();
+    double pgap = std::numeric_limits<double>::infinity();
+    std::vector<TreeCand> all;
+    std::vector<int> frontier = {-1};            // positions in `all`; -1 = the root
+    std::vector<float> L;
+    std::vector<double> p;
+    std::vector<int32_t> kids;
+    for (int k = 1; k <= gamma; ++k) {
+      const float* U_row = U + (b * gamma + (k - 1)) * static_cast<int64_t>(V);
+      const size_t first = all.size();
+      for (size_t m = 0; m < frontier.size(); ++m) {
+        const int par = frontier[m];
+        const int32_t x = (par < 0) ? anchor[b] : all[par].token;
+        const double Ppar = (par < 0) ? 1.0 : all[par].P;
+        draft_logits(U_row, W1, W2t, V, r, x, L);
+        softmax_fp64(L.data(), V, p);
+        top_children(L, c, kids, &lgap);
+        for (int i = 0; i < c; ++i) {
+          TreeCand t;
+          t.q = p[kids[i]];
+          t.P = Ppar * t.q;
+          t.depth = k;
+          t.idx = static_cast<int>(m) * c + i;
+          t.parent = par;
+          t.token = kids[i];
+          all.push_back(t);
+        }
+      }
+      if (k == gamma) break;
+      // The M best nodes of this depth are the parents of the next.
+      std::vector<int> order;
+      for (size_t i = first; i < all.size(); ++i) order.push_back(static_cast<int>(i));
+      std::stable_sort(order.begin(), order.end(), [&](int a, int bb) {
+        if (all[a].P != all[bb].P) return all[a].P > all[bb].P;
+        return all[a].idx < all[bb].idx;
+      });
+      std::vector<double> Ps;
+      for (int i : order) Ps.push_back(all[i].P);
+      const int keep = std::min<int>(M, static_cast<int>(order.size()));
+      rank_gaps(Ps, std::min<int>(keep, static_cast<int>(order.size()) - 1), &pgap);
+      frontier.assign(order.begin(), order.begin() + keep);
+    }
+    // The verify budget: the N best candidates of every depth.
+    std::vector<int> rank(all.size());
+    for (size_t i = 0; i < all.size(); ++i) rank[i] = static_cast<int>(i);
+    std::stable_sort(rank.begin(), rank.end(), [&](int a, int bb) {
+      if (all[a].P != all[bb].P) return all[a].P > all[bb].P;
+      if (all[a].depth != all[bb].depth) return all[a].depth < all[bb].depth;
+      return all[a].idx < all[bb].idx;
+    });
+    std::vector<double> Ps;
+    for (int i : rank) Ps.push_back(all[i].P);
+    rank_gaps(Ps, std::min<int>(N, static_cast<int>(rank.size()) - 1), &pgap);
+    std::vector<int> pos_of(all.size(), -1);
+    for (int n = 0; n < N; ++n) pos_of[rank[n]] = n;
+    for (int n = 0; n < N; ++n) {
+      const TreeCand& t = all[rank[n]];
+      const int64_t o = b * static_cast<int64_t>(N) + n;
+      node_token[o] = t.token;
+      node_depth[o] = t.depth;
+      node_parent[o] = (t.parent < 0) ? -1 : pos_of[t.parent];
+      node_q[o] = t.q;
+      node_path[o] = t.P;
+    }
+    if (logit_margin) logit_margin[b] = lgap;
+    if (path_margin) path_margin[b] = pgap;
+  });
+  return 0;
+}
+
+// Lossless verify of a tree. target [B][N + 1][V] f32: row 0 of a request holds the target
+// logits of position 1 (after the anchor), row 1 + n those of the position after node n (its
+// depth + 1), given the node's path. Tree as written by oracle_tree_draft (nodes in rank order;
+// a node's children are the nodes whose parent it is, in rank order).
+// The walk ([V41] "投机解码…": a draft is kept only as far as the target's own draws agree with
+// it; [ZDS] "后续工作"; reading): at the current node (the root first), y is drawn from p_t of
+// its row with u = uniforms[b][depth][2] by the inverse CDF whose order puts the node's
+// children first (in rank order) and then every other token in ascending id. If y is a child,
+// it is accepted and the walk moves to it; otherwise y is the emitted token (a correction, or,
+// at a node without children, the bonus) and the walk stops. Every emitted token is thus a draw
+// from the target's distribution given the accepted path: the tree changes how far the round
+// gets, never the distribution. For one child this is the point-mass rule of a greedy draft
+// (accept with probability p_t(x), else draw from p_t without x), taken with one uniform.
+// Outputs: accept_len [B] (accepted tree tokens), path [B][gamma] (the accepted tokens, -1 past
+// accept_len), next_token [B], flags [B] (NONFINITE when a row the walk read has a non-finite
+// log-sum-exp), margin [B] (nullable: the smallest distance from u to a boundary the walk
+// compared it with).
+int oracle_tree_verify(int B, int gamma, int V, int N, const float* target,
+                       const int32_t* node_token, const int32_t* node_depth,
+                       const int32_t* node_parent, const float* uniforms, int32_t* accept_len,
+                       int32_t* path, int32_t* next_token, uint32_t* flags, double* margin,
+                       int threads) {
+  if (B < 1 || gamma < 1 || V < 2 || N < 1) return 1;
+  parallel_for(B, threads, [&](int64_t b) {
+    const int32_t* tok = node_token + b * static_cast<int64_t>(N);
+    const int32_t* dep = node_depth + b * static_cast<int64_t>(N);
+    const int32_t* par = node_parent + b * static_cast<int64_t>(N);
+    std::vector<double> pt;
+    std::vector<char> excluded(V, 0);
+    double mg = std::numeric_limits<double>::infinity();
+    uint32_t fl = 0;
+    int cur = -1, depth = 0, accepted = 0;
+    int32_t y = 0;
+    for (int k = 0; k < gamma; ++k) path[b * gamma + k] = -1;
+    for (;;) {
+      const float* row = target + (b * static_cast<int64_t>(N + 1) + (cur + 1)) * V;
+      const double lt = softmax_fp64(row, V, pt);
+      if (!std::isfinite(lt)) fl |= ORACLE_FLAG_NONFINITE;
+      const double u = static_cast<double>(uniforms[(b * (gamma + 1) + depth) * 3 + 2]);
+      double S = 0.0;
+      int chosen = -1;
+      std::vector<int32_t> kids;
+      for (int n = 0; n < N; ++n) {
+        if (par[n] != cur) continue;
+        kids.push_back(tok[n]);
+        const double lo = S;
+        S += pt[tok[n]];
+        if (S > u) {
+          mg = std::min(mg, std::min(u - lo, S - u));
+          chosen = n;
+          break;
+        }
+        mg = std::min(mg, u - S);
+      }
+      if (chosen >= 0) {
+        path[b * gamma + accepted] = tok[chosen];
+        ++accepted;
+        cur = chosen;
+        depth = dep[chosen];
+        continue;
+      }
+      // Emission: the first token outside the children whose cumulative mass passes u.
+      for (int32_t x : kids) excluded[x] = 1;
+      double cdf = S;
+      int32_t last_positive = -1;
+      y = -1;
+      for (int v = 0; v < V; ++v) {
+        if (excluded[v]) continue;
+        const double lo = cdf;
+        cdf += pt[v];
+        if (pt[v] > 0.0) last_positive = v;
+        if (u < cdf) {
+          mg = std::min(mg, std::min(u - lo, cdf - u));
+          y = v;
+          break;
+        }
+      }
+      if (y < 0) {
+        mg = 0.0;
+        y = last_positive >= 0 ? last_positive : 0;
+      }
+      for (int32_t x : kids) excluded[x] = 0;
+      break;
+    }
+    accept_len[b] = accepted;
+    next_token[b] = y;
+    if (flags) flags[b] = fl;
+    if (margin) margin[b] = mg;
+  });
+  return 0;
+}
+
+}  // extern "C"

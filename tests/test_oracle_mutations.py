@@ -13,6 +13,7 @@ import test_oracle_draft_options_pins as op
 import test_oracle_draft_pins as dp
 import test_oracle_plan_pins as pp
 import test_oracle_rnn_pins as rp
+import test_oracle_tree_pins as tp
 import test_oracle_verify_pins as vp
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "dspark_oracle.cpp")
@@ -80,6 +81,24 @@ MUTATIONS = [
      "const float* row = target + (off + ell - 1) * static_cast<int64_t>(V);",
      [vp.test_bonus_is_drawn_from_the_row_after_the_last_verified_draft,
       vp.test_two_token_output_exact_grid_with_position_dependent_rows]),
+    ("tree children by the smallest logits", "if (L[a] != L[b]) return L[a] > L[b];",
+     "if (L[a] != L[b]) return L[a] < L[b];",
+     [tp.test_w2_zero_children_are_the_top_c_of_the_base_logits]),
+    ("tree path probability as a sum", "t.P = Ppar * t.q;", "t.P = Ppar + t.q;",
+     [functools.partial(tp.test_kept_nodes_are_the_most_likely_paths_brute_force, 1)]),
+    ("tree expands the least likely nodes", "if (all[a].P != all[bb].P) return all[a].P > all[bb].P;\n        return all[a].idx < all[bb].idx;",
+     "if (all[a].P != all[bb].P) return all[a].P < all[bb].P;\n        return all[a].idx < all[bb].idx;",
+     [functools.partial(tp.test_tree_structure_beam_and_budget, s) for s in range(10)]),
+    ("tree emission re-emits rejected children", "for (int32_t x : kids) excluded[x] = 1;",
+     "for (int32_t x : kids) excluded[x] = 0;",
+     [tp.test_tree_verify_exact_grid_follows_the_target_chain]),
+    ("tree walk reads the root row at every node",
+     "const float* row = target + (b * static_cast<int64_t>(N + 1) + (cur + 1)) * V;",
+     "const float* row = target + (b * static_cast<int64_t>(N + 1)) * V;",
+     [tp.test_tree_verify_exact_grid_follows_the_target_chain]),
+    ("tree walk draws every depth with the first uniform",
+     "uniforms[(b * (gamma + 1) + depth) * 3 + 2]", "uniforms[(b * (gamma + 1)) * 3 + 2]",
+     [tp.test_tree_verify_exact_grid_follows_the_target_chain]),
 ]
 
 
@@ -94,7 +113,8 @@ def test_planted_mistake_is_caught(name, old, new, pins, monkeypatch):
         subprocess.run(["g++", "-O1", "-std=c++17", "-fPIC", "-shared", "-pthread", path, "-o", lib],
                        check=True)
         mutated = ctypes.CDLL(lib)
-        for fn in ("oracle_markov_draft", "oracle_confidence", "oracle_plan", "oracle_verify"):
+        for fn in ("oracle_markov_draft", "oracle_confidence", "oracle_plan", "oracle_verify",
+                   "oracle_tree_draft", "oracle_tree_verify"):
             getattr(mutated, fn).restype = ctypes.c_int
         monkeypatch.setattr(oracle, "_lib", mutated)
         caught = False
