@@ -107,6 +107,38 @@ class InputSet:
         self.draft_len = dl.clone()
 
 
+class TreeInputSet:
+    """Inputs of a PCTree round: base logits, anchors, uniforms, and the target stand-in for
+    the tree the GPU drafts from them (rows after the anchor and after every kept node: base
+    logits of the next position plus the Markov bias of the node's token, plus noise)."""
+
+    def __init__(self, wl, wts, shape, round_index, dev):
+        d = L.Dims(wl.B, wl.gamma, wl.V, wl.r, wl.d)
+        inp = W.round_inputs(wl, round_index, dev, with_hidden=False, with_noise=False)
+        self.anchor, self.U, self.uniforms = inp["anchor"], inp["U"], inp["uniforms"]
+        tok, dep, par, _, _ = L.tree_draft(d, shape, self.U, wts["W1"], wts["W2t"], self.anchor)
+        B, g, N = wl.B, wl.gamma, shape.N
+        prev = torch.cat([self.anchor.long()[:, None], tok.long()], 1)
+        pos = torch.cat([torch.zeros((B, 1), dtype=torch.long, device=dev), dep.long()], 1)
+        W1f, W2f = wts["W1"].float(), wts["W2t"].float()
+        self.target = torch.empty((B, N + 1, wl.V), dtype=torch.float32, device=dev)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(7000 + round_index)
+        for b in range(B):
+            base = torch.where((pos[b] < g)[:, None], self.U[b, pos[b].clamp(max=g - 1)],
+                               inp["U_bonus"][b][None, :])
+            self.target[b] = base + W1f[prev[b]] @ W2f.T
+            self.target[b] += torch.randn((N + 1, wl.V), generator=gen, device=dev) * wl.noise_std(1)
+        del inp
+        torch.cuda.synchronize()
+
+
+def tree_bytes(wl, shape):
+    """Bytes a PCTree round must move: per depth the U slice and W2 (the expanded rows of a
+    request share its U row), then every tree row of the target once."""
+    return wl.gamma * step_bytes(wl) + 4 * wl.B * (shape.N + 1) * wl.V
+
+
 def algorithmic_bytes(wl, rows, n_res, greedy=False, head="markov"):
     """Bytes the method must move in one round (no caching credit): per draft step the U slice
     and W2; the hidden states and confidence weights; every verified target row; for rejected
@@ -233,6 +265,9 @@ def main():
                     help="launch the confidence head and the planner as calls of their own "
                          "after the draft (by default one call runs the plan beside the last "
                          "draft step)")
+    ap.add_argument("--tree", default=None, metavar="c,M,N",
+                    help="PCTree round instead of the chain: c children per node, M nodes "
+                         "expanded per depth, N nodes kept (e.g. 4,4,16)")
     ap.add_argument("--greedy", action="store_true",
                     help="greedy draft (first maximal logit; the verify's residual is p_t "
                          "without the drafted token)")
@@ -248,6 +283,8 @@ def main():
 
     dev = "cuda"
     wl = W.WORKLOADS[args.workload]
+    if args.tree:
+        return tree_main(args, wl, dev)
     full = wl.mode == W.FULL_VERIFY
     if args.head == "rnn" and full:
         print("the RNN head reads hidden states, which the full-verify workloads do not have",
@@ -498,6 +535,87 @@ def main():
         "ms_per_step_with_kernel_events": (round(1e3 * elapsed_ev / args.steps, 4)
                                            if elapsed_ev else None),
         "cpu_baseline": base,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def tree_main(args, wl, dev):
+    """A PCTree round (tree draft + tree verify) timed like the chain's round."""
+    import oracle
+    c, M, N = (int(x) for x in args.tree.split(","))
+    shape = L.TreeShape(c, M, N)
+    d = L.Dims(wl.B, wl.gamma, wl.V, wl.r, wl.d)
+    L.load_library()
+    wts = W.weights(wl, dev)
+    sets = [TreeInputSet(wl, wts, shape, i, dev) for i in range(args.sets)]
+    B, g = wl.B, wl.gamma
+    ws_d = torch.empty(L.tree_workspace_bytes(d, shape, L.OP_TREE_DRAFT), dtype=torch.uint8, device=dev)
+    ws_v = torch.empty(L.tree_workspace_bytes(d, shape, L.OP_TREE_VERIFY), dtype=torch.uint8, device=dev)
+    tok, dep, par = (torch.empty((B, N), dtype=torch.int32, device=dev) for _ in range(3))
+    q, P = (torch.empty((B, N), dtype=torch.float64, device=dev) for _ in range(2))
+    al, nt, fl = (torch.empty(B, dtype=torch.int32, device=dev) for _ in range(3))
+    path = torch.empty((B, g), dtype=torch.int32, device=dev)
+
+    def round_(s):
+        L.tree_draft(d, shape, s.U, wts["W1"], wts["W2t"], s.anchor, node_token=tok,
+                     node_depth=dep, node_parent=par, node_q=q, node_path=P, ws=ws_d)
+        L.tree_verify(d, shape, s.target, tok, par, s.uniforms, accept_len=al, path=path,
+                      next_token=nt, flags=fl, ws=ws_v)
+
+    tokens = []
+    for s in sets:
+        round_(s)
+        torch.cuda.synchronize()
+        tokens.append(int((al + 1).sum().item()))
+    for i in range(args.warmup):
+        round_(sets[i % len(sets)])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        round_(sets[i % len(sets)])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kern = {}
+    if not args.no_kernel_events:
+        L.profile_begin(64 * args.steps)
+        for i in range(args.steps):
+            round_(sets[i % len(sets)])
+        torch.cuda.synchronize()
+        kern = {k: round(1e3 * ms / n, 2) for k, (n, ms) in L.profile_end().items() if n}
+    rps = args.steps / elapsed
+    tpr = float(np.mean([tokens[i % len(sets)] for i in range(args.steps)]))
+    nbytes = tree_bytes(wl, shape)
+    base = None
+    if not args.no_cpu_baseline:
+        threads = min(16, len(os.sched_getaffinity(0)) or 1)
+        s = sets[0]
+        host = lambda t: t.detach().cpu().numpy()
+        U, anc, uni, tgt = host(s.U), host(s.anchor), host(s.uniforms), host(s.target)
+        W1b, W2b = W.bf16_bits(wts["W1"]), W.bf16_bits(wts["W2t"])
+        secs = []
+        for _ in range(3):
+            t1 = time.perf_counter()
+            o = oracle.tree_draft(U, W1b, W2b, anc, c, M, N, threads=threads)
+            oracle.tree_verify(tgt, o["token"], o["depth"], o["parent"], uni, threads=threads)
+            secs.append(time.perf_counter() - t1)
+        sec = float(np.median(secs))
+        base = {"value": 1.0 / sec, "unit": "rounds/s", "cores": threads, "kind": "oracle",
+                "cpu": cpu_model(),
+                "sample": f"3 PCTree rounds of {wl.name} (tree draft c={c} M={M} N={N}, tree "
+                          f"verify; all {B} requests), median {sec:.2f} s a round"}
+    out = {
+        "metric": f"PCTree rounds/s at B={B},V={wl.V},γ={g}; achieved HBM GB/s vs peak",
+        "value": round(rps, 2), "unit": "rounds/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(1e3 * elapsed / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 mfma / f32 / f64", "data": "synthetic",
+        "config": {"workload": wl.name, "B": B, "V": wl.V, "gamma": g, "r": wl.r,
+                   "tree": {"c": c, "M": M, "N": N}, "input_sets": len(sets),
+                   "parallelism": "1 GPU", "launch": "eager"},
+        "tokens_per_round": tpr, "tokens_per_s": round(rps * tpr, 1),
+        "round_algorithmic_gbs": round(nbytes * rps / 1e9, 1),
+        "round_hbm_frac": round(nbytes * rps / 1e9 / HBM_PEAK_GBS, 4),
+        "kernels_us": kern, "cpu_baseline": base,
     }
     print(json.dumps(out), flush=True)
 

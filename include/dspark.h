@@ -10,6 +10,8 @@
  *   dspark_rnn_draft, dspark_rnn_verify   the draft and verify with the RNN head of eq. (6)
  *   dspark_markov_draft_plan, dspark_rnn_draft_plan   draft, confidence and plan of a round
  *                        in one call, the plan computed beside the last position's draft step
+ *   dspark_tree_draft, dspark_tree_verify   PCTree: a draft tree scored by the Markov head
+ *                        within a verify budget, and its lossless verify
  *
  * Sources (cited below by tag; each gives the page title and the section or equation):
  *   [V41]  blog.javazero.top, "DeepSeek-V4.1 模型结构（6）：解码，DSpark"
@@ -94,6 +96,8 @@ typedef int32_t dspark_status;
 #define DSPARK_OP_VERIFY 3
 #define DSPARK_OP_RNN_DRAFT 4
 #define DSPARK_OP_RNN_VERIFY 5
+#define DSPARK_OP_TREE_DRAFT 6   /* sized by dspark_tree_workspace_bytes */
+#define DSPARK_OP_TREE_VERIFY 7
 
 /* Per-request verify flag bits. */
 #define DSPARK_FLAG_NONFINITE 1u     /* a verified target row has a non-finite log-sum-exp */
@@ -291,6 +295,78 @@ DSPARK_API dspark_status dspark_verify_opts(dspark_dims dims, const float* targe
                                             int32_t* next_token, float* beta_emit, uint32_t* flags,
                                             void* ws, size_t ws_bytes,
                                             const dspark_draft_opts* opts, void* stream);
+
+/*
+ * PCTree tree drafting. [ZDS] "后续工作" (PCTree): the draft chain becomes a tree; the Markov
+ * head scores every child token under a parent token, so it picks each parent's candidate
+ * children, and the most likely paths are kept within a fixed verify budget, with no retraining
+ * and no extra backbone pass; [V41] "Markov head" eqs. (4), (5) (the scores).
+ * Per request, with x the token of a node (the anchor at the root) and U_k the base logits of
+ * depth k (shared by every node of the depth):
+ *   - a node of depth k - 1 scores the tokens of depth k by softmax(fp32(U_k + fp32(W1[x] W2)))
+ *     and expands its c best children: the c largest fp32 logits, the smaller id on a tie;
+ *   - a node's path probability P is the product of those probabilities along its path (fp64);
+ *   - depth 1 expands the root; depth k >= 2 expands the M nodes of depth k - 1 with the
+ *     largest P (ties: the earlier candidate, numbering candidates parent by parent and child
+ *     by child in rank order);
+ *   - the N candidates of all depths with the largest P (ties: the smaller depth, then the
+ *     earlier candidate) are kept; they form a tree (a child's P never exceeds its parent's).
+ * Outputs, nodes in that rank order, [B][N] each:
+ *   node_token   int32   the node's token
+ *   node_depth   int32   1..gamma (the token's position)
+ *   node_parent  int32   rank of the parent node, -1 for a child of the root
+ *   node_q       f64     the token's Markov probability under its parent (exp(L - lse))
+ *   node_path    f64     P
+ * U, W1, W2t, anchor as for dspark_markov_draft (no temperature; anchors are clamped into
+ * [0, V)). Shape limits (else DSPARK_ERR_SHAPE): r <= 256, 1 <= M <= c <= 8, M a power of
+ * two, c <= V, c + (gamma - 1) M c <= 1024 candidates, 1 <= N <= min(that, 256), and
+ * ceil(V / 32) <= 32 * (1024 / M). Workspace: dspark_tree_workspace_bytes(dims, shape,
+ * DSPARK_OP_TREE_DRAFT). Precision: the logits are bit-identical to the chain draft's; lse from
+ * the tile partials (fp32 tile sums, fp64 across tiles), probabilities in fp64.
+ */
+typedef struct dspark_tree_shape {
+  int32_t c;   /* children expanded per node */
+  int32_t M;   /* nodes expanded per depth (depth >= 2) */
+  int32_t N;   /* nodes kept: the verify budget */
+} dspark_tree_shape;
+DSPARK_API size_t dspark_tree_workspace_bytes(dspark_dims dims, dspark_tree_shape shape,
+                                              int32_t op);
+DSPARK_API dspark_status dspark_tree_draft(dspark_dims dims, dspark_tree_shape shape,
+                                           const float* U, const uint16_t* W1,
+                                           const uint16_t* W2t, const int32_t* anchor,
+                                           int32_t* node_token, int32_t* node_depth,
+                                           int32_t* node_parent, double* node_q,
+                                           double* node_path, void* ws, size_t ws_bytes,
+                                           void* stream);
+
+/*
+ * Lossless verify of a draft tree. [V41] "投机解码：让小的先猜，大的一次验一串" (a drafted
+ * token is kept only as far as the target's own draw agrees with it; every round emits at least
+ * one token from the target); [ZDS] "后续工作" (PCTree). Rows: target[b][0] holds the target
+ * logits of position 1 (after the anchor), target[b][1 + n] those of the position after kept
+ * node n, given the node's path. The walk: at the current node (the root first, depth 0), y is
+ * drawn from p_t of its row with u = uniforms[b][depth][2], by the inverse CDF whose order puts
+ * the node's children (in rank order) first and then every other token by ascending id. A child
+ * is accepted and the walk moves to it; any other y is emitted (the correction, or at a node
+ * without children the bonus) and the walk stops. Every emitted token is a draw from the
+ * target given the accepted path, so the round is lossless whatever the tree.
+ *   target      [B][N + 1][V] fp32
+ *   node_token, node_parent   [B][N] as written by dspark_tree_draft (clamped into range)
+ *   uniforms    [B][gamma + 1][3] fp32; component 2 of slot depth is used
+ *   accept_len  [B] int32 out: tree tokens accepted (0..gamma)
+ *   path        [B][gamma] int32 out: the accepted tokens, -1 past accept_len
+ *   next_token  [B] int32 out: the emitted token (the next anchor)
+ *   flags       nullable [B] uint32 out: DSPARK_FLAG_NONFINITE when a row the walk read has a
+ *               non-finite log-sum-exp
+ * Shape limits and errors as for dspark_tree_draft; workspace: dspark_tree_workspace_bytes(
+ * dims, shape, DSPARK_OP_TREE_VERIFY).
+ */
+DSPARK_API dspark_status dspark_tree_verify(dspark_dims dims, dspark_tree_shape shape,
+                                            const float* target, const int32_t* node_token,
+                                            const int32_t* node_parent, const float* uniforms,
+                                            int32_t* accept_len, int32_t* path,
+                                            int32_t* next_token, uint32_t* flags, void* ws,
+                                            size_t ws_bytes, void* stream);
 
 /*
  * The verify of dspark_verify_opts for callers that cannot allocate device memory: code under

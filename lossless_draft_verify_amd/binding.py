@@ -20,11 +20,14 @@ __all__ = [
     "FLAG_NONFINITE", "FLAG_ZERO_RESIDUAL", "library_path", "load_library", "workspace_bytes",
     "workspace", "markov_draft", "confidence", "plan", "markov_draft_plan", "verify",
     "rnn_draft", "rnn_verify", "rnn_draft_plan", "verify_noalloc", "NOALLOC_SCRATCH_BYTES",
+    "TreeShape", "OP_TREE_DRAFT", "OP_TREE_VERIFY", "tree_workspace_bytes", "tree_draft",
+    "tree_verify",
     "profile_begin", "profile_end", "version",
 ]
 
 FULL_VERIFY, EARLY_STOP, FULL_PATH, LAGGED_TOPK = 0, 1, 2, 3
 OP_DRAFT, OP_CONFIDENCE, OP_PLAN, OP_VERIFY, OP_RNN_DRAFT, OP_RNN_VERIFY = 0, 1, 2, 3, 4, 5
+OP_TREE_DRAFT, OP_TREE_VERIFY = 6, 7
 FLAG_NONFINITE, FLAG_ZERO_RESIDUAL = 1, 2
 NOALLOC_SCRATCH_BYTES = 48 << 20     # DSPARK_NOALLOC_SCRATCH_BYTES
 
@@ -54,6 +57,21 @@ def _opts(temperature: float, greedy: bool):
     if not greedy and float(temperature) == 1.0:
         return None
     return ctypes.byref(_CDraftOpts(float(temperature), 1 if greedy else 0))
+
+
+class _CTreeShape(ctypes.Structure):
+    _fields_ = [("c", ctypes.c_int32), ("M", ctypes.c_int32), ("N", ctypes.c_int32)]
+
+
+@dataclass(frozen=True)
+class TreeShape:
+    """PCTree shape: c children expanded per node, M nodes expanded per depth, N nodes kept."""
+    c: int
+    M: int
+    N: int
+
+    def c_struct(self) -> _CTreeShape:
+        return _CTreeShape(self.c, self.M, self.N)
 
 
 @dataclass(frozen=True)
@@ -109,6 +127,12 @@ def load_library():
         lib.dspark_verify_opts.argtypes = [_CDims] + [_P] * 15 + [_P, ctypes.c_size_t, _P, _P]
         lib.dspark_verify_noalloc.restype = ctypes.c_int32
         lib.dspark_verify_noalloc.argtypes = [_CDims] + [_P] * 15 + [_P, _P]
+        lib.dspark_tree_workspace_bytes.restype = ctypes.c_size_t
+        lib.dspark_tree_workspace_bytes.argtypes = [_CDims, _CTreeShape, ctypes.c_int32]
+        lib.dspark_tree_draft.restype = ctypes.c_int32
+        lib.dspark_tree_draft.argtypes = [_CDims, _CTreeShape] + [_P] * 9 + [_P, ctypes.c_size_t, _P]
+        lib.dspark_tree_verify.restype = ctypes.c_int32
+        lib.dspark_tree_verify.argtypes = [_CDims, _CTreeShape] + [_P] * 8 + [_P, ctypes.c_size_t, _P]
         lib.dspark_rnn_draft.restype = ctypes.c_int32
         lib.dspark_rnn_draft.argtypes = [_CDims] + [_P] * 13 + [_P, ctypes.c_size_t, _P, _P]
         lib.dspark_rnn_verify.restype = ctypes.c_int32
@@ -424,3 +448,63 @@ def rnn_draft_plan(dims: Dims, U, W1, W2t, Wgco, h, anchor, uniforms, w, T, sps,
         _opts(temperature, greedy), _stream(stream))
     _check(st, "dspark_rnn_draft_plan")
     return tokens, q, lse, e_rows, conf, draft_len, row_offsets, stats
+
+
+def tree_workspace_bytes(dims: Dims, shape: TreeShape, op: int) -> int:
+    n = load_library().dspark_tree_workspace_bytes(dims.c(), shape.c_struct(), op)
+    if n == ctypes.c_size_t(-1).value:
+        raise DsparkError(f"unsupported tree shape {shape} for dims {dims}")
+    return int(n)
+
+
+def tree_draft(dims: Dims, shape: TreeShape, U, W1, W2t, anchor, *, node_token=None,
+               node_depth=None, node_parent=None, node_q=None, node_path=None, ws=None,
+               stream=None):
+    """PCTree draft (dspark_tree_draft). Returns (node_token, node_depth, node_parent, node_q,
+    node_path), each [B][N], nodes in rank order."""
+    B, g, V, r, N = dims.B, dims.gamma, dims.V, dims.r, shape.N
+    dev = U.device
+    i32 = lambda t: t if t is not None else torch.empty((B, N), dtype=torch.int32, device=dev)
+    f64 = lambda t: t if t is not None else torch.empty((B, N), dtype=torch.float64, device=dev)
+    node_token, node_depth, node_parent = i32(node_token), i32(node_depth), i32(node_parent)
+    node_q, node_path = f64(node_q), f64(node_path)
+    if ws is None:
+        ws = torch.empty(tree_workspace_bytes(dims, shape, OP_TREE_DRAFT), dtype=torch.uint8,
+                         device=dev)
+    st = load_library().dspark_tree_draft(
+        dims.c(), shape.c_struct(), _ptr(U, torch.float32, (B, g, V), "U"),
+        _ptr(W1, torch.bfloat16, (V, r), "W1"), _ptr(W2t, torch.bfloat16, (V, r), "W2t"),
+        _ptr(anchor, torch.int32, (B,), "anchor"),
+        _ptr(node_token, torch.int32, (B, N), "node_token"),
+        _ptr(node_depth, torch.int32, (B, N), "node_depth"),
+        _ptr(node_parent, torch.int32, (B, N), "node_parent"),
+        _ptr(node_q, torch.float64, (B, N), "node_q"),
+        _ptr(node_path, torch.float64, (B, N), "node_path"),
+        _ptr(ws, torch.uint8, None, "ws"), ws.numel(), _stream(stream))
+    _check(st, "dspark_tree_draft")
+    return node_token, node_depth, node_parent, node_q, node_path
+
+
+def tree_verify(dims: Dims, shape: TreeShape, target, node_token, node_parent, uniforms, *,
+                accept_len=None, path=None, next_token=None, flags=None, ws=None, stream=None):
+    """Lossless verify of a draft tree (dspark_tree_verify). target [B][N+1][V].
+    Returns (accept_len, path, next_token, flags)."""
+    B, g, V, N = dims.B, dims.gamma, dims.V, shape.N
+    dev = target.device
+    accept_len = accept_len if accept_len is not None else torch.empty(B, dtype=torch.int32, device=dev)
+    path = path if path is not None else torch.empty((B, g), dtype=torch.int32, device=dev)
+    next_token = next_token if next_token is not None else torch.empty(B, dtype=torch.int32, device=dev)
+    flags = flags if flags is not None else torch.empty(B, dtype=torch.int32, device=dev)
+    if ws is None:
+        ws = torch.empty(tree_workspace_bytes(dims, shape, OP_TREE_VERIFY), dtype=torch.uint8,
+                         device=dev)
+    st = load_library().dspark_tree_verify(
+        dims.c(), shape.c_struct(), _ptr(target, torch.float32, (B, N + 1, V), "target"),
+        _ptr(node_token, torch.int32, (B, N), "node_token"),
+        _ptr(node_parent, torch.int32, (B, N), "node_parent"),
+        _ptr(uniforms, torch.float32, (B, g + 1, 3), "uniforms"),
+        _ptr(accept_len, torch.int32, (B,), "accept_len"), _ptr(path, torch.int32, (B, g), "path"),
+        _ptr(next_token, torch.int32, (B,), "next_token"), _ptr(flags, torch.int32, (B,), "flags"),
+        _ptr(ws, torch.uint8, None, "ws"), ws.numel(), _stream(stream))
+    _check(st, "dspark_tree_verify")
+    return accept_len, path, next_token, flags

@@ -17,7 +17,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdspark.so")
 
 SOURCES = ["api.hip", "kernels_draft.hip", "kernels_confidence.hip", "kernels_plan.hip",
-           "kernels_verify.hip", "kernels_rnn.hip"]
+           "kernels_verify.hip", "kernels_rnn.hip", "kernels_tree.hip"]
 
 # -ffp-contract=off: every kernel forms its floating-point results with the same operations, so
 # a sampler that recomputes a tile gets the streaming pass's bits. The packed-fp32 feature is

@@ -152,6 +152,69 @@ size_t rnn_verify_ws(const dspark_dims& d, void* base, VerifyWs* out, uint16_t**
   return off + align_up(static_cast<size_t>(d.B) * d.gamma * kRnnTerms * d.r * sizeof(uint16_t));
 }
 
+// ---- PCTree ------------------------------------------------------------------------------
+// Candidates of a request: c at depth 1, M c at every later depth (M <= c).
+int64_t tree_candidates(const dspark_dims& d, const dspark_tree_shape& t) {
+  return static_cast<int64_t>(t.c) + static_cast<int64_t>(d.gamma - 1) * t.M * t.c;
+}
+bool tree_shape_ok(const dspark_dims& d, const dspark_tree_shape& t) {
+  if (!dims_ok(d) || d.r > 256) return false;
+  if (t.c < 1 || t.c > kTreeMaxChildren || t.c > d.V) return false;
+  if (t.M < 1 || t.M > t.c || (t.M & (t.M - 1)) != 0) return false;
+  const int64_t T = tree_candidates(d, t);
+  if (T > kTreeMaxCand || t.N < 1 || t.N > T || t.N > kTreeMaxNodes) return false;
+  // a select workgroup gives each expanded node 1024 / M threads of at most 32 tile partials
+  if (static_cast<int64_t>(ntiles_of(d.V)) > 32LL * (1024 / t.M)) return false;
+  return static_cast<int64_t>(d.B) * (t.N + 1) <= (1LL << 24);
+}
+struct TreeDraftWs {
+  float2* part;
+  int32_t* ftok[2];
+  double* fP[2];
+  int32_t* fcand[2];
+  TreeCandWs cand;
+};
+size_t tree_draft_ws(const dspark_dims& d, const dspark_tree_shape& t, void* base, TreeDraftWs* out) {
+  const size_t B = d.B, M = t.M, T = static_cast<size_t>(tree_candidates(d, t));
+  char* b = static_cast<char*>(base);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* p = b ? b + off : nullptr;
+    off += align_up(bytes);
+    return p;
+  };
+  TreeDraftWs w;
+  w.part = reinterpret_cast<float2*>(take(B * M * ntiles_of(d.V) * sizeof(float2)));
+  for (int i = 0; i < 2; ++i) {
+    w.ftok[i] = reinterpret_cast<int32_t*>(take(B * M * sizeof(int32_t)));
+    w.fP[i] = reinterpret_cast<double*>(take(B * M * sizeof(double)));
+    w.fcand[i] = reinterpret_cast<int32_t*>(take(B * M * sizeof(int32_t)));
+  }
+  w.cand.tok = reinterpret_cast<int32_t*>(take(B * T * sizeof(int32_t)));
+  w.cand.parent = reinterpret_cast<int32_t*>(take(B * T * sizeof(int32_t)));
+  w.cand.P = reinterpret_cast<double*>(take(B * T * sizeof(double)));
+  w.cand.q = reinterpret_cast<double*>(take(B * T * sizeof(double)));
+  if (out) *out = w;
+  return off;
+}
+// Tree verify: the segment statistics of the B (N + 1) rows (and the target pass's counter).
+size_t tree_verify_ws(const dspark_dims& d, const dspark_tree_shape& t, void* base, VerifyWs* out) {
+  const size_t rows = static_cast<size_t>(d.B) * (t.N + 1), nseg = nseg_of(d.V);
+  char* b = static_cast<char*>(base);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* p = b ? b + off : nullptr;
+    off += align_up(bytes);
+    return p;
+  };
+  VerifyWs w{};
+  w.seg_max = reinterpret_cast<float*>(take(rows * nseg * sizeof(float)));
+  w.seg_sum = reinterpret_cast<double*>(take(rows * nseg * sizeof(double)));
+  w.rcount = reinterpret_cast<int32_t*>(take(sizeof(int32_t)));
+  if (out) *out = w;
+  return off;
+}
+
 // The RNN head needs the hidden states (d a positive multiple of 8) and r <= 256 (the three
 // bf16 terms of a bias row fill at most two 1 KB copies of one wave).
 bool rnn_dims_ok(const dspark_dims& d) { return dims_ok(d) && d.r <= 256 && d.d >= 8 && d.d % 8 == 0; }
@@ -169,12 +232,15 @@ enum KernelId {
   kRnnPre,
   kRnnState,
   kSplitBias,
+  kTreeSelect,
+  kTreeWalk,
   kNumKernels
 };
 const char* const kKernelNames[kNumKernels] = {"markov_step",  "draft_sample", "confidence",
                                                "plan",         "target_stats", "accept",
                                                "residual_partials", "emit_sample",
-                                               "rnn_pre",      "rnn_state",    "split_bias"};
+                                               "rnn_pre",      "rnn_state",    "split_bias",
+                                               "tree_select",  "tree_walk"};
 
 struct Profiler {
   bool armed = false;
@@ -246,7 +312,7 @@ dspark_status draft_loop(const dspark_dims& dims, const float* U, const uint16_t
       RnnStateArgs ra{dims.B,        dims.gamma,       k,          dims.r,
                       dims.d,        rnn->w.P,         rnn->Wgco,  W1,
                       prev,          stride,           k > 0 ? rnn->w.s[(k + 1) & 1] : nullptr,
-                      rnn->w.s[k & 1], rnn->e_rows,    rnn->w.E};
+                      rnn->w.s[k & 1], rnn->e_rows,    rnn->w.E,   dims.V};
       if (timed(kRnnState, s, [&] { return launch_rnn_state(ra, s); }) != hipSuccess)
         return DSPARK_ERR_HIP;
     }
@@ -464,7 +530,7 @@ dspark_status dspark_rnn_draft_plan(dspark_dims dims, const float* U, const uint
   if (ws_bytes < rnn_draft_ws(dims, nullptr, nullptr)) return DSPARK_ERR_WORKSPACE;
   RnnDraftInputs rnn{Wgco, h, e_rows, {}};
   rnn_draft_ws(dims, ws, &rnn.w);
-  const RoundPlan rp{{dims.B, dims.gamma, dims.r, dims.d, h, W1, w, T, anchor, tokens, conf},
+  const RoundPlan rp{{dims.B, dims.gamma, dims.r, dims.d, h, W1, w, T, anchor, tokens, conf, dims.V},
                      {dims.B, dims.gamma, sps_len, mode, round_index, conf, sps, ring, draft_len,
                       row_offsets, stats}};
   return draft_loop(dims, U, W1, W2t, anchor, uniforms, tokens, q_tok, lse, nullptr, nullptr,
@@ -486,7 +552,7 @@ dspark_status dspark_confidence(dspark_dims dims, const uint16_t* h, const uint1
   const dspark_status st = check_confidence(dims, h, W1, w, T, anchor, tokens, conf);
   if (st != DSPARK_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  ConfArgs a{dims.B, dims.gamma, dims.r, dims.d, h, W1, w, T, anchor, tokens, conf};
+  ConfArgs a{dims.B, dims.gamma, dims.r, dims.d, h, W1, w, T, anchor, tokens, conf, dims.V};
   if (timed(kConfidence, s, [&] { return launch_confidence(a, s); }) != hipSuccess)
     return DSPARK_ERR_HIP;
   return DSPARK_OK;
@@ -529,7 +595,7 @@ dspark_status dspark_markov_draft_plan(dspark_dims dims, const float* U, const u
   if (ws_bytes < draft_ws(dims, nullptr, nullptr)) return DSPARK_ERR_WORKSPACE;
   DraftWs dw;
   draft_ws(dims, ws, &dw);
-  const RoundPlan rp{{dims.B, dims.gamma, dims.r, dims.d, h, W1, w, T, anchor, tokens, conf},
+  const RoundPlan rp{{dims.B, dims.gamma, dims.r, dims.d, h, W1, w, T, anchor, tokens, conf, dims.V},
                      {dims.B, dims.gamma, sps_len, mode, round_index, conf, sps, ring, draft_len,
                       row_offsets, stats}};
   return draft_loop(dims, U, W1, W2t, anchor, uniforms, tokens, q_tok, lse, nullptr, nullptr,
@@ -584,6 +650,115 @@ dspark_status dspark_verify_opts(dspark_dims dims, const float* target,
   a.greedy = greedy;
   verify_ws(dims, ws, &a.ws);
   return verify_passes(dims, a, static_cast<hipStream_t>(stream));
+}
+
+size_t dspark_tree_workspace_bytes(dspark_dims dims, dspark_tree_shape shape, int32_t op) {
+  if (!tree_shape_ok(dims, shape)) return static_cast<size_t>(-1);
+  if (op == DSPARK_OP_TREE_DRAFT) return tree_draft_ws(dims, shape, nullptr, nullptr);
+  if (op == DSPARK_OP_TREE_VERIFY) return tree_verify_ws(dims, shape, nullptr, nullptr);
+  return static_cast<size_t>(-1);
+}
+
+dspark_status dspark_tree_draft(dspark_dims dims, dspark_tree_shape shape, const float* U,
+                                const uint16_t* W1, const uint16_t* W2t, const int32_t* anchor,
+                                int32_t* node_token, int32_t* node_depth, int32_t* node_parent,
+                                double* node_q, double* node_path, void* ws, size_t ws_bytes,
+                                void* stream) {
+  if (!U || !W1 || !W2t || !anchor || !node_token || !node_depth || !node_parent || !node_q ||
+      !node_path || !ws)
+    return DSPARK_ERR_NULL;
+  if (!tree_shape_ok(dims, shape)) return DSPARK_ERR_SHAPE;
+  if (!aligned(U, 16) || !aligned(W1, 16) || !aligned(W2t, 16) || !aligned(anchor, 4) ||
+      !aligned(node_token, 4) || !aligned(node_depth, 4) || !aligned(node_parent, 4) ||
+      !aligned(node_q, 8) || !aligned(node_path, 8) || !aligned(ws, kAlign))
+    return DSPARK_ERR_ALIGN;
+  if (ws_bytes < tree_draft_ws(dims, shape, nullptr, nullptr)) return DSPARK_ERR_WORKSPACE;
+  TreeDraftWs w;
+  tree_draft_ws(dims, shape, ws, &w);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int nt = ntiles_of(dims.V);
+  const int cus = compute_units();
+  const int T = static_cast<int>(tree_candidates(dims, shape));
+  int shift = 0;
+  while ((1 << shift) < shape.M) ++shift;
+  for (int k = 0; k < dims.gamma; ++k) {
+    const int rows = (k == 0) ? 1 : shape.M;
+    const int pb = (k + 1) & 1;   // buffer the previous depth's select wrote (k - 1) & 1
+    const int32_t* prev = (k == 0) ? anchor : w.ftok[pb];
+    StepArgs sa{dims.B * rows, dims.V, dims.gamma, k, nt, U, W1, W2t, prev, 1, w.part, nullptr,
+                cus, 1.0f};
+    sa.u_shift = (k == 0) ? 0 : shift;
+    if (timed(kMarkovStep, s, [&] { return launch_markov_step(sa, dims.r, s); }) != hipSuccess)
+      return DSPARK_ERR_HIP;
+    TreeSelectArgs ta{};
+    ta.B = dims.B;
+    ta.V = dims.V;
+    ta.gamma = dims.gamma;
+    ta.k = k;
+    ta.ntiles = nt;
+    ta.c = shape.c;
+    ta.M = shape.M;
+    ta.rows = rows;
+    ta.T = T;
+    ta.cand_base = (k == 0) ? 0 : shape.c + (k - 1) * shape.M * shape.c;
+    ta.U = U;
+    ta.W1 = W1;
+    ta.W2t = W2t;
+    ta.prev = prev;
+    ta.prevP = (k == 0) ? nullptr : w.fP[pb];
+    ta.prevCand = (k == 0) ? nullptr : w.fcand[pb];
+    ta.part = w.part;
+    ta.cand = w.cand;
+    ta.front_tok = w.ftok[k & 1];
+    ta.front_P = w.fP[k & 1];
+    ta.front_cand = w.fcand[k & 1];
+    ta.last = (k == dims.gamma - 1) ? 1 : 0;
+    ta.N = shape.N;
+    ta.node_token = node_token;
+    ta.node_depth = node_depth;
+    ta.node_parent = node_parent;
+    ta.node_q = node_q;
+    ta.node_path = node_path;
+    if (timed(kTreeSelect, s, [&] { return launch_tree_select(ta, dims.r, s); }) != hipSuccess)
+      return DSPARK_ERR_HIP;
+  }
+  return DSPARK_OK;
+}
+
+dspark_status dspark_tree_verify(dspark_dims dims, dspark_tree_shape shape, const float* target,
+                                 const int32_t* node_token, const int32_t* node_parent,
+                                 const float* uniforms, int32_t* accept_len, int32_t* path,
+                                 int32_t* next_token, uint32_t* flags, void* ws, size_t ws_bytes,
+                                 void* stream) {
+  if (!target || !node_token || !node_parent || !uniforms || !accept_len || !path ||
+      !next_token || !ws)
+    return DSPARK_ERR_NULL;
+  if (!tree_shape_ok(dims, shape)) return DSPARK_ERR_SHAPE;
+  if (!aligned(target, 16) || !aligned(node_token, 4) || !aligned(node_parent, 4) ||
+      !aligned(uniforms, 4) || !aligned(accept_len, 4) || !aligned(path, 4) ||
+      !aligned(next_token, 4) || (flags && !aligned(flags, 4)) || !aligned(ws, kAlign))
+    return DSPARK_ERR_ALIGN;
+  if (ws_bytes < tree_verify_ws(dims, shape, nullptr, nullptr)) return DSPARK_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  VerifyArgs a;
+  a.B = dims.B;
+  a.V = dims.V;
+  a.gamma = dims.gamma;
+  a.r = dims.r;
+  a.ntiles = ntiles_of(dims.V);
+  a.nseg = nseg_of(dims.V);
+  a.target = target;
+  a.row_offsets = nullptr;
+  a.dense_rows = dims.B * (shape.N + 1);
+  a.persistent_wgs = compute_units();
+  tree_verify_ws(dims, shape, ws, &a.ws);
+  if (timed(kTargetStats, s, [&] { return launch_target_stats(a, s); }) != hipSuccess)
+    return DSPARK_ERR_HIP;
+  TreeWalkArgs wa{dims.B, dims.V, dims.gamma, shape.N, a.nseg, target, node_token, node_parent,
+                  uniforms, a.ws.seg_max, a.ws.seg_sum, accept_len, path, next_token, flags};
+  if (timed(kTreeWalk, s, [&] { return launch_tree_walk(wa, s); }) != hipSuccess)
+    return DSPARK_ERR_HIP;
+  return DSPARK_OK;
 }
 
 dspark_status dspark_verify_noalloc(dspark_dims dims, const float* target,

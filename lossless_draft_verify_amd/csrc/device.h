@@ -23,6 +23,11 @@ constexpr int kMaxGamma = 255;       // draft positions per request (accept scan
 constexpr int kMaxVocab = 1 << 19;   // a sampler stages one row's tile partials in LDS (8 B each)
 constexpr float kNegInf = -__builtin_inff();
 
+// A token id read from an input, clamped into [0, V): every address formed from a token id stays
+// inside its table whatever the caller passed (the results of a round with such an id are not
+// meaningful, but no access leaves the tensors).
+__device__ __forceinline__ int32_t clamp_token(int32_t x, int V) { return min(max(x, 0), V - 1); }
+
 // One 32x32x16 bf16 MFMA step (fp32 accumulate). Lane l holds A[m = l % 32][k = 8 (l / 32) + i]
 // and B[k = 8 (l / 32) + i][n = l % 32], i = 0..7; the result lane l, slot j holds
 // C[m = 8 (j / 4) + 4 (l / 32) + j % 4][n = l % 32]. In the kernels m indexes tokens and n

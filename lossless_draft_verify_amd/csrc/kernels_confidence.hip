@@ -20,7 +20,8 @@ __global__ __launch_bounds__(kBlock) void confidence_kernel(ConfArgs p) {
   const int idx = blockIdx.x;
   const int b = idx / p.gamma, k = idx % p.gamma;
   const uint16_t* hrow = p.h + static_cast<size_t>(idx) * p.d;
-  const int32_t prevtok = (k == 0) ? p.anchor[b] : p.tokens[static_cast<size_t>(b) * p.gamma + k - 1];
+  const int32_t prevtok = clamp_token(
+      (k == 0) ? p.anchor[b] : p.tokens[static_cast<size_t>(b) * p.gamma + k - 1], p.V);
   constexpr int kBatch = 4;   // pieces of 8 per thread per batch: 8192 elements per batch
   const int nh = p.d / 8;     // hidden-state pieces
   const int ne = p.r / 8;     // embedding-row pieces (<= 64, one per thread)

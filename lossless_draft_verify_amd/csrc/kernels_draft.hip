@@ -69,7 +69,7 @@ struct StepKernel {
 #pragma unroll
     for (int i = 0; i < kURows; ++i) {
       const int b = min(group * BG + i * 16 + (tid >> 5), p.B - 1);
-      const float* row = p.U + (static_cast<size_t>(b) * p.gamma + p.k) * p.V;
+      const float* row = p.U + (static_cast<size_t>(b >> p.u_shift) * p.gamma + p.k) * p.V;
       if (VEC4) {
         u[i] = (v + 3 < p.V) ? *reinterpret_cast<const float4*>(row + v) : make_float4(0.f, 0.f, 0.f, 0.f);
       } else {
@@ -93,7 +93,7 @@ struct StepKernel {
     for (int i = 0; i < kEPieces; ++i) {
       const int c = min(i * kStepThreads + tid, BG * kPR - 1);
       const int b = min(group * BG + c / kPR, p.B - 1);
-      ids[i] = (NT == 1) ? p.prev[static_cast<size_t>(b) * p.prev_stride] : b;
+      ids[i] = (NT == 1) ? clamp_token(p.prev[static_cast<size_t>(b) * p.prev_stride], p.V) : b;
     }
     u16x8_t e[kEPieces];
 #pragma unroll
@@ -368,7 +368,7 @@ __device__ __forceinline__ void markov_step_dma(const StepArgs& p, unsigned bid,
       const int c = (slot % D::kUChunks) ^ (row & 15);
       const int b = min(group * kDmaGroup + row, p.B - 1);
       const int v = min(tok0 + 4 * c, p.V - 4);
-      copy16_to_lds_nt(p.U + (static_cast<size_t>(b) * p.gamma + p.k) * p.V + v,
+      copy16_to_lds_nt(p.U + (static_cast<size_t>(b >> p.u_shift) * p.gamma + p.k) * p.V + v,
                        base + D::kW2Bytes + 1024 * q);
     }
   };
@@ -409,7 +409,8 @@ __device__ __forceinline__ void markov_step_dma(const StepArgs& p, unsigned bid,
         const int slot = 64 * q + lane;
         const int row = slot / D::kW2Chunks;
         const int c = (slot % D::kW2Chunks) ^ (row & D::kW2Swz);
-        copy16_to_lds(p.W1 + static_cast<size_t>(pid[row]) * D::r + 8 * c, ebase + 1024 * q);
+        copy16_to_lds(p.W1 + static_cast<size_t>(clamp_token(pid[row], p.V)) * D::r + 8 * c,
+                      ebase + 1024 * q);
       }
     }
     issue(0);
@@ -620,7 +621,7 @@ __global__ __launch_bounds__(SampleCfg<KS>::kThreads) void draft_sample_kernel(S
   // validity of each partial is applied only after the copy is issued.
   const int per = (nt + kSampleThreads - 1) / kSampleThreads;   // uniform, <= kSamplePer
   const int c0 = min(nt, tid * per), c1 = min(nt, c0 + per);
-  const int32_t prevtok = p.prev[static_cast<size_t>(b) * p.prev_stride];
+  const int32_t prevtok = clamp_token(p.prev[static_cast<size_t>(b) * p.prev_stride], p.V);
   const int32_t forced = p.force ? p.force[out] : 0;   // the token to condition on, if forced
   __shared__ __attribute__((aligned(16))) uint16_t Es[16 * KS * NT];
   float2 v[kSamplePer];

@@ -209,7 +209,7 @@ __global__ __launch_bounds__(kStateThreads) void rnn_state_kernel(RnnStateArgs p
   // at once (at most kStateB * 2 * 256 / kStateThreads = 8 per thread) before the LDS stores.
   __shared__ int32_t xs[kStateB];
   if (tid < kStateB)
-    xs[tid] = p.prev[static_cast<size_t>(min(b0 + tid, p.B - 1)) * p.prev_stride];
+    xs[tid] = clamp_token(p.prev[static_cast<size_t>(min(b0 + tid, p.B - 1)) * p.prev_stride], p.V);
   __syncthreads();
   constexpr int kZPer = kStateB * 2 * 256 / kStateThreads;
   double zv[kZPer];

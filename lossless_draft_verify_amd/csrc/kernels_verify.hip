@@ -61,7 +61,7 @@ __global__ __launch_bounds__(kBlock) void target_stats_kernel(VerifyArgs p) {
   __shared__ double red_d[kBlock / 64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   if (blockIdx.x == 0 && threadIdx.x == 0) *p.ws.rcount = 0;   // residual list (for accept)
-  const int nitems = p.row_offsets[p.B] * p.nseg;
+  const int nitems = (p.dense_rows > 0 ? p.dense_rows : p.row_offsets[p.B]) * p.nseg;
   const bool vec4 = (p.V & 3) == 0;
   int it = blockIdx.x;
   if (it >= nitems) return;
@@ -116,9 +116,9 @@ __global__ __launch_bounds__(kBlock) void accept_kernel(VerifyArgs p) {
   float tx0 = 0.0f, u0 = 0.0f, q0 = 0.0f;
   int32_t x0 = 0;
   double lsed0 = 0.0;
-  const int32_t anc = p.anchor ? p.anchor[b] : 0;   // no anchor for an RNN-head draft
+  const int32_t anc = p.anchor ? clamp_token(p.anchor[b], p.V) : 0;   // none for the RNN head
   if (lane < ell) {
-    x0 = p.tokens[static_cast<size_t>(b) * p.gamma + lane];
+    x0 = clamp_token(p.tokens[static_cast<size_t>(b) * p.gamma + lane], p.V);
     lsed0 = p.lse[static_cast<size_t>(b) * p.gamma + lane];
     u0 = p.uniforms[(static_cast<size_t>(b) * (p.gamma + 1) + lane) * 3 + 1];
     q0 = p.q[static_cast<size_t>(b) * p.gamma + lane];
@@ -200,7 +200,7 @@ __global__ __launch_bounds__(kBlock) void accept_kernel(VerifyArgs p) {
       float tx = tx0, uk = u0, qk = q0;
       if (k0 > 0) {
         const int row = off + k;
-        const int32_t x = p.tokens[static_cast<size_t>(b) * p.gamma + k];
+        const int32_t x = clamp_token(p.tokens[static_cast<size_t>(b) * p.gamma + k], p.V);
         tx = p.target[static_cast<size_t>(row) * p.V + x];
         uk = p.uniforms[(static_cast<size_t>(b) * (p.gamma + 1) + k) * 3 + 1];
         qk = p.q[static_cast<size_t>(b) * p.gamma + k];
@@ -229,7 +229,8 @@ __global__ __launch_bounds__(kBlock) void accept_kernel(VerifyArgs p) {
     const int32_t xr = read_lane(static_cast<int>(x0), last & 63);
     const double ls = read_lane(lsed0, last & 63);
     prev_x = (last == 0) ? anc
-             : (last - 1 < 64 ? xs : p.tokens[static_cast<size_t>(b) * p.gamma + last - 1]);
+             : (last - 1 < 64 ? xs
+                              : clamp_token(p.tokens[static_cast<size_t>(b) * p.gamma + last - 1], p.V));
     xtok = (last < 64) ? xr : p.tokens[static_cast<size_t>(b) * p.gamma + last];
     lse_d = (last < 64) ? ls : p.lse[static_cast<size_t>(b) * p.gamma + last];
   }
@@ -256,7 +257,7 @@ __global__ __launch_bounds__(kBlock) void accept_kernel(VerifyArgs p) {
 
 // Previous token of emission position j (1-based): the anchor for j = 1.
 __device__ __forceinline__ int32_t emit_prev(const VerifyArgs& p, int b, int j) {
-  return (j == 1) ? p.anchor[b] : p.tokens[static_cast<size_t>(b) * p.gamma + j - 2];
+  return clamp_token((j == 1) ? p.anchor[b] : p.tokens[static_cast<size_t>(b) * p.gamma + j - 2], p.V);
 }
 
 // Draft probability of one token in fp32 (prob_f32): softmax(beta L) of the position (cd its

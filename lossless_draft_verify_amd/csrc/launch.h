@@ -23,6 +23,9 @@ struct StepArgs {
   // (b, k) as three bf16 terms, E [B][gamma][3r] (prev unused).
   int e_terms = 1;
   const uint16_t* E = nullptr;
+  // Rows that share a request's base logits: row b reads U row (b >> u_shift) (tree drafting:
+  // the 2^u_shift expanded nodes of one request score their children from the same U_k).
+  int u_shift = 0;
 };
 
 struct SampleArgs {
@@ -53,6 +56,7 @@ struct ConfArgs {
   const int32_t* anchor;
   const int32_t* tokens;
   float* conf;
+  int V;                  // token ids are clamped into [0, V)
 };
 
 struct PlanArgs {
@@ -117,6 +121,57 @@ struct VerifyArgs {
   VerifyWs ws;
   int e_terms = 1;               // bias rows as in StepArgs (3: E [B][gamma][3r], in ws)
   const uint16_t* E = nullptr;
+  int dense_rows = 0;            // > 0: the target pass takes this many rows (no row_offsets)
+};
+
+// PCTree ([ZDS] "后续工作"). Candidates of a request are numbered depth by depth, and within a
+// depth parent by parent (in the order the depth's expanded nodes were ranked) and child by
+// child in rank order; T = c + (gamma - 1) M c of them.
+constexpr int kTreeMaxRows = 8;        // nodes expanded per request and depth (M)
+constexpr int kTreeMaxChildren = 8;    // children per expanded node (c)
+constexpr int kTreeMaxCand = 1024;     // candidates per request over all depths (T)
+constexpr int kTreeMaxNodes = 256;     // kept nodes per request (N)
+struct TreeCandWs {
+  int32_t* tok;      // [B][T]
+  int32_t* parent;   // [B][T] candidate number of the parent (-1: the root)
+  double* P;         // [B][T] path probability
+  double* q;         // [B][T] Markov probability of the token under its parent
+};
+struct TreeSelectArgs {
+  int B, V, gamma, k, ntiles;   // k: 0-based depth (the children sit at position k + 1)
+  int c, M, rows;               // rows: expanded nodes per request at this depth (1 or M)
+  int T, cand_base;             // candidates per request; number of this depth's first one
+  const float* U;
+  const uint16_t* W1;
+  const uint16_t* W2t;
+  const int32_t* prev;          // [B rows] token of each expanded node (the anchor at depth 1)
+  const double* prevP;          // [B rows] its path probability (nullptr: 1)
+  const int32_t* prevCand;      // [B rows] its candidate number (nullptr: the root)
+  const float2* part;           // [B rows][ntiles] the step kernel's partials
+  TreeCandWs cand;
+  int32_t* front_tok;           // [B][M] out: the next depth's expanded nodes (k < gamma - 1)
+  double* front_P;
+  int32_t* front_cand;
+  int last;                     // k == gamma - 1: write the kept nodes instead
+  int N;
+  int32_t* node_token;          // [B][N] out, rank order
+  int32_t* node_depth;
+  int32_t* node_parent;
+  double* node_q;
+  double* node_path;
+};
+struct TreeWalkArgs {
+  int B, V, gamma, N, nseg;
+  const float* target;          // [B][N + 1][V]
+  const int32_t* node_token;    // [B][N]
+  const int32_t* node_parent;   // [B][N]
+  const float* uniforms;        // [B][gamma + 1][3]
+  const float* seg_max;         // [B (N + 1)][nseg]
+  const double* seg_sum;
+  int32_t* accept_len;          // [B]
+  int32_t* path;                // [B][gamma]
+  int32_t* next_token;          // [B]
+  uint32_t* flags;              // nullable [B]
 };
 
 // RNN head, eq. (6). P [kRnnPreSplits][M][3r] = the hidden-state block of Wgco applied to every
@@ -144,6 +199,7 @@ struct RnnStateArgs {
   double* s_out;          // [B][r] s_k
   float* e_out;           // [B][gamma][r] e_k (fp32)
   uint16_t* E;            // [B][gamma][3r] bf16 terms of e_k
+  int V;                  // token ids are clamped into [0, V)
 };
 
 // The bf16 terms of given fp32 bias vectors (the verify of an RNN-head draft): E [n][3r] from
@@ -191,5 +247,7 @@ hipError_t launch_emit_sample(const VerifyArgs& a, hipStream_t s);
 hipError_t launch_rnn_pre(const RnnPreArgs& a, hipStream_t s);
 hipError_t launch_rnn_state(const RnnStateArgs& a, hipStream_t s);
 hipError_t launch_split_bias(const SplitArgs& a, hipStream_t s);
+hipError_t launch_tree_select(const TreeSelectArgs& a, int r, hipStream_t s);
+hipError_t launch_tree_walk(const TreeWalkArgs& a, hipStream_t s);
 
 }  // namespace dspark

@@ -144,6 +144,8 @@ def _c_kind(param):
         return "ptr"
     if t.startswith("dspark_dims"):
         return "dims"
+    if t.startswith("dspark_tree_shape"):
+        return "tree_shape"
     if t.startswith("size_t"):
         return "size_t"
     if t.startswith("int32_t") or t.startswith("dspark_status"):
@@ -154,6 +156,8 @@ def _c_kind(param):
 def _py_kind(t):
     if t is L.binding._CDims:
         return "dims"
+    if t is L.binding._CTreeShape:
+        return "tree_shape"
     if t is ctypes.c_size_t:
         return "size_t"
     if t is ctypes.c_int32:
@@ -240,3 +244,22 @@ def test_noalloc_verify_refuses_sizes_beyond_its_scratch(lib):
     assert L.workspace_bytes(fits, L.OP_VERIFY) <= L.NOALLOC_SCRATCH_BYTES
     assert lib.dspark_verify_noalloc(fits.c(), *([P] * 12 + [None] + [None] * 4)) == 1
     assert lib.dspark_verify_noalloc(L.Dims(4, 3, 1000, 24, 8).c(), *args) == 2
+
+
+def test_tree_shape_checks(lib):
+    """PCTree shape limits are checked on the host: M <= c <= 8, M a power of two, the candidate
+    count and the budget; an unsupported shape sizes no workspace and is refused."""
+    d = L.Dims(16, 5, 129280, 256, 8)
+    ok = L.TreeShape(4, 4, 16)
+    assert L.tree_workspace_bytes(d, ok, L.OP_TREE_DRAFT) > 0
+    assert L.tree_workspace_bytes(d, ok, L.OP_TREE_VERIFY) > 0
+    for bad in (L.TreeShape(4, 8, 16), L.TreeShape(9, 1, 4), L.TreeShape(4, 3, 16),
+                L.TreeShape(4, 4, 0), L.TreeShape(4, 4, 4 + 4 * 16 * 4 + 1)):
+        with pytest.raises(L.DsparkError):
+            L.tree_workspace_bytes(d, bad, L.OP_TREE_DRAFT)
+    P = _p()
+    ws = L.tree_workspace_bytes(d, ok, L.OP_TREE_DRAFT)
+    assert lib.dspark_tree_draft(d.c(), ok.c_struct(), *([P] * 9), P, ws - 1, None) == 4
+    assert lib.dspark_tree_draft(d.c(), L.TreeShape(4, 3, 16).c_struct(), *([P] * 9), P, ws,
+                                 None) == 2
+    assert lib.dspark_tree_verify(d.c(), ok.c_struct(), None, *([P] * 7), P, ws, None) == 1
