@@ -72,7 +72,8 @@ __device__ __forceinline__ double tree_tile_mass(float m, float s, float M) {
   return (m == kNegInf) ? 0.0 : static_cast<double>(exp_term(m - M)) * static_cast<double>(s);
 }
 
-template <int KS>
+// CM: a power of two >= c, the length of each thread's sorted list of best tiles.
+template <int KS, int CM>
 __global__ __launch_bounds__(kTreeThreads) void tree_select_kernel(TreeSelectArgs p) {
   constexpr int r = 16 * KS;
   __shared__ __attribute__((aligned(16))) uint16_t Es[kTreeMaxRows][r];
@@ -107,9 +108,9 @@ __global__ __launch_bounds__(kTreeThreads) void tree_select_kernel(TreeSelectArg
   // the row maximum, as the chain's sampler forms them.
   const float2* part = p.part + static_cast<size_t>(row) * nt;
   float m_thr = kNegInf;
-  uint64_t best[kTreeMaxChildren];
+  uint64_t best[CM];
 #pragma unroll
-  for (int j = 0; j < kTreeMaxChildren; ++j) best[j] = 0;
+  for (int j = 0; j < CM; ++j) best[j] = 0;
   constexpr int kBatch = 8;
   for (int i0 = 0; i0 < kTreePer && G * i0 < nt; i0 += kBatch) {
     float tm[kBatch];
@@ -124,7 +125,7 @@ __global__ __launch_bounds__(kTreeThreads) void tree_select_kernel(TreeSelectArg
       m_thr = fmaxf(m_thr, tm[i]);
       uint64_t key = (t < nt) ? rank_key(tm[i], t) : 0ull;
 #pragma unroll
-      for (int j = 0; j < kTreeMaxChildren; ++j) {
+      for (int j = 0; j < CM; ++j) {
         const uint64_t x = best[j];
         const bool swap = key > x;
         best[j] = swap ? key : x;
@@ -157,14 +158,10 @@ __global__ __launch_bounds__(kTreeThreads) void tree_select_kernel(TreeSelectArg
   for (int w = 0; w < WS; ++w) Z += redd[sub * WS + w];
   const double lse = static_cast<double>(M) + log(Z);
 
-  // The row's c best tiles, one per round (each thread offers its best not yet taken).
-  uint64_t prev_key = ~0ull;
+  // The row's c best tiles, one per round: each thread offers the head of its sorted list, and
+  // the one thread whose head was taken (keys are unique) shifts its list.
   for (int j = 0; j < c; ++j) {
-    uint64_t cand = 0;
-#pragma unroll
-    for (int i = 0; i < kTreeMaxChildren; ++i)
-      if (best[i] < prev_key && best[i] > cand) cand = best[i];
-    cand = wave_max_u64(cand);
+    const uint64_t cand = wave_max_u64(best[0]);
     if (lane == 0) redk[wave] = cand;
     __syncthreads();
     uint64_t kb = 0;
@@ -172,7 +169,10 @@ __global__ __launch_bounds__(kTreeThreads) void tree_select_kernel(TreeSelectArg
       const uint64_t x = redk[sub * WS + w];
       kb = x > kb ? x : kb;
     }
-    prev_key = kb;
+    const bool taken = kb != 0 && best[0] == kb;
+#pragma unroll
+    for (int i = 0; i + 1 < CM; ++i) best[i] = taken ? best[i + 1] : best[i];
+    best[CM - 1] = taken ? 0ull : best[CM - 1];
     if (stid == 0) tile_of[sub][j] = kb ? key_index(kb) : -1;
     __syncthreads();   // redk is rewritten by the next round
   }
@@ -203,15 +203,25 @@ __global__ __launch_bounds__(kTreeThreads) void tree_select_kernel(TreeSelectArg
       }
       keys[i] = key;
     }
-    uint64_t prevk = ~0ull, mine = 0;
-    for (int i = 0; i < c; ++i) {
-      uint64_t best = 0;
+    // sort the lane's four keys (descending), then take heads as above
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (keys[q] < prevk && keys[q] > best) best = keys[q];
-      best = wave_max_u64(best);
-      prevk = best;
-      if (lane == i) mine = best;
+    for (int i = 0; i < 3; ++i)
+#pragma unroll
+      for (int q = 0; q < 3 - i; ++q) {
+        const uint64_t hi = keys[q] > keys[q + 1] ? keys[q] : keys[q + 1];
+        const uint64_t lo = keys[q] > keys[q + 1] ? keys[q + 1] : keys[q];
+        keys[q] = hi;
+        keys[q + 1] = lo;
+      }
+    uint64_t mine = 0;
+    for (int i = 0; i < c; ++i) {
+      const uint64_t kb = wave_max_u64(keys[0]);
+      const bool taken = kb != 0 && keys[0] == kb;
+      keys[0] = taken ? keys[1] : keys[0];
+      keys[1] = taken ? keys[2] : keys[1];
+      keys[2] = taken ? keys[3] : keys[2];
+      keys[3] = taken ? 0ull : keys[3];
+      if (lane == i) mine = kb;
     }
     if (lane < c) {
       const int tok = mine ? key_index(mine) : 0;
@@ -349,41 +359,54 @@ __global__ __launch_bounds__(kWalkThreads) void tree_walk_kernel(TreeWalkArgs p)
   for (int n = tid; n < N; n += kWalkThreads)
     ptn[n] = exp(static_cast<double>(tval[n]) - lse[par[n] + 1]);
   __syncthreads();
-  // 3. The walk: at a node, its children in rank order take the first part of the draw's
-  //    order; a child whose cumulative mass passes u is accepted.
-  if (tid == 0) {
+  // 3. The walk on wave 0: at a node, its children in rank order take the first part of the
+  //    draw's order; the first child whose cumulative mass passes u is accepted. A depth is a
+  //    ballot and a scan over the nodes (64 a batch), the cumulative mass carried across batches.
+  if (wave == 0) {
     int cur = -1, acc = 0;
     uint32_t fl = 0;
     for (;;) {
       if (!isfinite(lse[cur + 1])) fl |= 1u;
       const double u = static_cast<double>(us[acc]);
-      double S = 0.0;
+      double before = 0.0;
       int chosen = -1;
-      for (int n = 0; n < N; ++n) {
-        if (par[n] != cur) continue;
-        S += ptn[n];
-        if (S > u) {
-          chosen = n;
+      for (int i0 = 0; i0 < N; i0 += 64) {
+        const int n = i0 + lane;
+        const bool child = n < N && par[n] == cur;
+        const double inc = before + wave_inclusive_scan(child ? ptn[n] : 0.0, lane);
+        const unsigned long long hit = __ballot(child && inc > u);
+        if (hit) {
+          chosen = i0 + __ffsll(static_cast<long long>(hit)) - 1;
           break;
         }
+        before = read_lane(inc, 63);
       }
       if (chosen < 0 || acc >= p.gamma) break;
-      p.path[static_cast<size_t>(b) * p.gamma + acc] = tok[chosen];
+      if (lane == 0) p.path[static_cast<size_t>(b) * p.gamma + acc] = tok[chosen];
       ++acc;
       cur = chosen;
     }
-    for (int k = acc; k < p.gamma; ++k) p.path[static_cast<size_t>(b) * p.gamma + k] = -1;
+    if (lane == 0)
+      for (int k = acc; k < p.gamma; ++k) p.path[static_cast<size_t>(b) * p.gamma + k] = -1;
+    // the stop node's children (at most c), in rank order: excluded from the emission
     int ne = 0;
-    for (int n = 0; n < N && ne < kTreeMaxChildren; ++n)
-      if (par[n] == cur) {
-        exc[ne] = tok[n];
-        exc_t[ne] = tval[n];
-        ++ne;
+    for (int i0 = 0; i0 < N; i0 += 64) {
+      const int n = i0 + lane;
+      const bool child = n < N && par[n] == cur;
+      const unsigned long long m = __ballot(child);
+      const int pos = ne + __popcll(m & ((1ull << lane) - 1ull));
+      if (child && pos < kTreeMaxChildren) {
+        exc[pos] = tok[n];
+        exc_t[pos] = tval[n];
       }
-    stop_s = cur;
-    acc_s = acc;
-    fl_s = fl;
-    nexc_s = ne;
+      ne += __popcll(m);
+    }
+    if (lane == 0) {
+      stop_s = cur;
+      acc_s = acc;
+      fl_s = fl;
+      nexc_s = min(ne, kTreeMaxChildren);
+    }
   }
   __syncthreads();
   const int stop = stop_s, acc = acc_s, ne = nexc_s;
@@ -478,7 +501,15 @@ __global__ __launch_bounds__(kWalkThreads) void tree_walk_kernel(TreeWalkArgs p)
 
 template <int KS>
 static hipError_t launch_tree_select_ks(const TreeSelectArgs& a, hipStream_t s) {
-  launch_kernel(tree_select_kernel<KS>, dim3(a.B), dim3(kTreeThreads), 0, s, a);
+  if (a.c <= 1) {
+    launch_kernel(tree_select_kernel<KS, 1>, dim3(a.B), dim3(kTreeThreads), 0, s, a);
+  } else if (a.c <= 2) {
+    launch_kernel(tree_select_kernel<KS, 2>, dim3(a.B), dim3(kTreeThreads), 0, s, a);
+  } else if (a.c <= 4) {
+    launch_kernel(tree_select_kernel<KS, 4>, dim3(a.B), dim3(kTreeThreads), 0, s, a);
+  } else {
+    launch_kernel(tree_select_kernel<KS, 8>, dim3(a.B), dim3(kTreeThreads), 0, s, a);
+  }
   return hipGetLastError();
 }
 
