@@ -42,6 +42,10 @@
  *     smallest id v whose cumulative probability (ids in ascending order) exceeds u. The pages
  *     fix only the distribution a draw must follow; this rule makes it reproducible.
  *   - Results are deterministic: two identical calls give bitwise identical outputs.
+ *   - Token ids the caller passes (anchors, forced or drafted tokens, tree node tokens) are
+ *     clamped into [0, V) on the device, and verify lengths into [0, gamma], before any address
+ *     is formed from them: a call with such values reads nothing outside its tensors and gives
+ *     the results of the clamped values (which are then not meaningful).
  */
 #ifndef DSPARK_H_
 #define DSPARK_H_

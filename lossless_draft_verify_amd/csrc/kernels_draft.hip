@@ -622,7 +622,7 @@ __global__ __launch_bounds__(SampleCfg<KS>::kThreads) void draft_sample_kernel(S
   const int per = (nt + kSampleThreads - 1) / kSampleThreads;   // uniform, <= kSamplePer
   const int c0 = min(nt, tid * per), c1 = min(nt, c0 + per);
   const int32_t prevtok = clamp_token(p.prev[static_cast<size_t>(b) * p.prev_stride], p.V);
-  const int32_t forced = p.force ? p.force[out] : 0;   // the token to condition on, if forced
+  const int32_t forced = p.force ? clamp_token(p.force[out], p.V) : 0;   // conditioning token
   __shared__ __attribute__((aligned(16))) uint16_t Es[16 * KS * NT];
   float2 v[kSamplePer];
   auto load_parts = [&](auto n_c) {

@@ -107,7 +107,7 @@ __global__ __launch_bounds__(kBlock) void accept_kernel(VerifyArgs p) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int b = blockIdx.x * (kBlock / 64) + w;
   if (b >= p.B) return;
-  const int ell = p.draft_len[b];
+  const int ell = min(max(p.draft_len[b], 0), p.gamma);   // a length past gamma is clamped
   const int off = p.row_offsets[b];
   uint32_t fl = 0;
   // 0. Everything that needs only (ell, off) goes out first: the accept-test inputs of the first

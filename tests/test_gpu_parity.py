@@ -712,3 +712,54 @@ def test_verify_target_equal_to_draft():
     wl = _custom("b64-v4000-r64-g6-exact", seed_id=93, B=64, V=4000, r=64, gamma=6)
     acc, al = _verify_against_oracle(wl, "b64-v4000-g6 exact target", noise_scale=0.0)
     assert (acc == wl.gamma).mean() >= 0.99 and np.array_equal(acc, al)
+
+
+@pytest.mark.parametrize("name", ["tiny-b4-v1000-g3", "b20-v8192-r256-g2"])
+def test_out_of_range_token_ids_are_clamped(name):
+    """Token ids a caller passes outside [0, V) (anchors, forced draft tokens, the drafted tokens
+    given to the confidence head and the verify) and verify lengths past gamma are clamped on the
+    device: every call gives the same bits as with the clamped values, and no access leaves the
+    tensors."""
+    wl = DRAFT_CASES[name]
+    B, g, V = wl.B, wl.gamma, wl.V
+    d = dims_of(wl)
+    wts = W.weights(wl, DEV)
+    inp = W.round_inputs(wl, 0, DEV, with_hidden=False)
+    raw = torch.tensor([-7, V, V + 100, 5] * ((B + 3) // 4), dtype=torch.int32, device=DEV)[:B]
+    clamped = raw.clamp(0, V - 1).contiguous()
+    run = lambda anc, **kw: [np_(t) for t in L.markov_draft(d, inp["U"], wts["W1"], wts["W2t"],
+                                                             anc, inp["uniforms"], **kw)]
+    for a, b_ in zip(run(raw), run(clamped)):
+        assert np.array_equal(a, b_)
+    force = torch.full((B, g), V + 3, dtype=torch.int32, device=DEV)
+    force[:, ::2] = -2
+    fc = force.clamp(0, V - 1).contiguous()
+    for a, b_ in zip(run(clamped, force_tokens=force), run(clamped, force_tokens=fc)):
+        assert np.array_equal(a, b_)
+    tok, q, lse = L.markov_draft(d, inp["U"], wts["W1"], wts["W2t"], clamped, inp["uniforms"])
+    bad_tok = tok.clone()
+    bad_tok[:, 0] = -1
+    bad_tok[:, -1] = V + 9
+    h = torch.randn((B, g, wl.d), device=DEV).to(torch.bfloat16)
+    temps = W.temperatures(wl).to(DEV)
+    c_raw = L.confidence(d, h, wts["W1"], wts["w"], temps, raw, bad_tok)
+    c_cl = L.confidence(d, h, wts["W1"], wts["w"], temps, clamped, bad_tok.clamp(0, V - 1).contiguous())
+    assert torch.equal(c_raw, c_cl)
+    offs = _T(np.arange(B + 1) * (g + 1))
+    target = torch.randn((B * (g + 1), V), device=DEV)
+    long_len = _T(np.full(B, g + 5))
+    full_len = _T(np.full(B, g))
+    out_raw = L.verify(d, target, offs, long_len, inp["U"], wts["W1"], wts["W2t"], raw, bad_tok,
+                       q, lse, inp["uniforms"])
+    out_cl = L.verify(d, target, offs, full_len, inp["U"], wts["W1"], wts["W2t"], clamped,
+                      bad_tok.clamp(0, V - 1).contiguous(), q, lse, inp["uniforms"])
+    torch.cuda.synchronize()
+    for a, b_ in zip(out_raw, out_cl):
+        assert torch.equal(a, b_)
+    nt = np_(out_raw[1])
+    assert ((nt >= 0) & (nt < V)).all()
+    shape = L.TreeShape(2, 2, 4)
+    ta = [np_(t) for t in L.tree_draft(d, shape, inp["U"], wts["W1"], wts["W2t"], raw)]
+    tb = [np_(t) for t in L.tree_draft(d, shape, inp["U"], wts["W1"], wts["W2t"], clamped)]
+    for a, b_ in zip(ta, tb):
+        assert np.array_equal(a, b_)
