@@ -291,10 +291,47 @@ struct DmaLds {
   __attribute__((aligned(256))) int32_t pid[kDmaGroup];
 };
 
-// The pipelined step as run by workgroup `bid` of `nblk` step workgroups.
+// Workgroup -> (request group, vocabulary range) of the pipelined step. Workgroup w of a group
+// takes a contiguous range of items, so that the partials of one request that it produces are
+// contiguous in memory (full-line writes). Blocks are dispatched round-robin over the XCDs
+// (hardware blocks h and h + kXcds share one): with several request groups, the groups of one
+// range go to blocks that share an XCD, so that the range's W2t rows come from HBM once and then
+// from that XCD's L2. `first` hardware blocks come before the step's (the planner's block of
+// the fused last step); each XCD's step blocks form whole sets of ngroups, and blocks left over
+// take no item (group = -1).
+struct StepMap {
+  int group, wg, nwg;
+};
+__device__ __forceinline__ StepMap step_map(int B, int h, int nblk_hw, int first) {
+  const int ngroups = (B + kDmaGroup - 1) / kDmaGroup;
+  const int nstep = nblk_hw - first;
+  if (ngroups == 1) return StepMap{0, h - first, nstep};
+  if (nstep < kXcds * ngroups) {   // too few blocks for whole sets on every XCD: consecutive
+    const int s = h - first, nwg = nstep / ngroups;
+    return (s < nwg * ngroups) ? StepMap{s % ngroups, s / ngroups, nwg} : StepMap{-1, 0, nwg};
+  }
+  // step blocks on XCD x: hardware blocks first .. nblk_hw - 1 with h % kXcds == x
+  auto on_xcd = [&](int x) {
+    const int lo = (first + kXcds - 1 - x) / kXcds;        // first slot with h >= first
+    const int hi = (nblk_hw - 1 - x + kXcds) / kXcds;      // slots with h < nblk_hw
+    return max(0, hi - lo);
+  };
+  const int x = h % kXcds;
+  const int slot = h / kXcds - (first + kXcds - 1 - x) / kXcds;   // index among x's step blocks
+  int before = 0, total = 0;
+  for (int y = 0; y < kXcds; ++y) {
+    const int ranges = on_xcd(y) / ngroups;
+    if (y < x) before += ranges;
+    total += ranges;
+  }
+  const int ranges_x = on_xcd(x) / ngroups;
+  if (slot >= ranges_x * ngroups) return StepMap{-1, 0, total};
+  return StepMap{slot % ngroups, before + slot / ngroups, total};
+}
+
+// The pipelined step as run by the workgroup that step_map placed at (group, wg of nwg).
 template <int KS, int NT, int TPW = 1>
-__device__ __forceinline__ void markov_step_dma(const StepArgs& p, unsigned bid, unsigned nblk,
-                                                bool xcd_map, DmaLds<KS>& lds) {
+__device__ __forceinline__ void markov_step_dma(const StepArgs& p, StepMap mp, DmaLds<KS>& lds) {
   using D = DmaStep<KS, TPW>;
   unsigned char* stage = lds.stage;
   float2* pbuf = lds.pbuf;
@@ -303,23 +340,8 @@ __device__ __forceinline__ void markov_step_dma(const StepArgs& p, unsigned bid,
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, col = lane & 31;
   const int sub = wave >> 2, rq = wave & 3;   // (first) tile within the item, request quarter
-  // Workgroup w of a group takes a contiguous range of items, so that the partials of one
-  // request that it produces are contiguous in memory (full-line writes). Blocks are dispatched
-  // round-robin over the XCDs (blocks b and b + kXcds share one): when bid is the hardware block
-  // index (xcd_map) and there are several request groups, the groups of one range go to blocks
-  // that share an XCD, so that the range's W2t rows come from HBM once and then from its L2 (a
-  // bijection when nwg is a multiple of kXcds; otherwise consecutive blocks).
-  const int ngroups = (p.B + kDmaGroup - 1) / kDmaGroup;
-  const int nwg = nblk / ngroups;
-  int group, wg;
-  if (xcd_map && ngroups > 1 && nwg % kXcds == 0) {
-    const int xcd = bid % kXcds, slot = bid / kXcds;
-    group = slot % ngroups;
-    wg = (slot / ngroups) * kXcds + xcd;
-  } else {
-    group = bid % ngroups;
-    wg = bid / ngroups;
-  }
+  if (mp.group < 0) return;
+  const int group = mp.group, wg = mp.wg, nwg = mp.nwg;
   const int nitems = (p.V + D::kTok - 1) / D::kTok;
   const int item_lo = static_cast<int>(static_cast<int64_t>(nitems) * wg / nwg);
   const int n = static_cast<int>(static_cast<int64_t>(nitems) * (wg + 1) / nwg) - item_lo;
@@ -546,7 +568,7 @@ __device__ __forceinline__ void markov_step_dma(const StepArgs& p, unsigned bid,
 template <int KS, int NT>
 __global__ __launch_bounds__(kDmaThreads, 1) void markov_step_dma_kernel(StepArgs p) {
   __shared__ DmaLds<KS> lds;
-  markov_step_dma<KS, NT>(p, blockIdx.x, gridDim.x, true, lds);
+  markov_step_dma<KS, NT>(p, step_map(p.B, blockIdx.x, gridDim.x, 0), lds);
 }
 
 // The pipelined step with four waves (one per SIMD), each computing both token tiles of an item
@@ -555,7 +577,7 @@ __global__ __launch_bounds__(kDmaThreads, 1) void markov_step_dma_kernel(StepArg
 template <int KS, int NT>
 __global__ __launch_bounds__(kDmaThreads / 2, 1) void markov_step_dma_wave4_kernel(StepArgs p) {
   __shared__ DmaLds<KS> lds;
-  markov_step_dma<KS, NT, 2>(p, blockIdx.x, gridDim.x, true, lds);
+  markov_step_dma<KS, NT, 2>(p, step_map(p.B, blockIdx.x, gridDim.x, 0), lds);
 }
 
 // The last draft position's step with the verify planner beside it: workgroup 0 plans (its LDS
@@ -573,7 +595,7 @@ __global__ __launch_bounds__(kDmaThreads / TPW, 1) void markov_step_plan_kernel(
     plan::run<kDmaThreads / TPW>(pa, *reinterpret_cast<plan::Smem<kFusedPlanMax>*>(lds.stage));
     return;
   }
-  markov_step_dma<KS, NT, TPW>(p, blockIdx.x - 1, gridDim.x - 1, false, lds);
+  markov_step_dma<KS, NT, TPW>(p, step_map(p.B, blockIdx.x, gridDim.x, 1), lds);
 }
 
 // One 1024-thread workgroup per request. Thread t holds a contiguous range of at most 16 tile
@@ -740,29 +762,29 @@ __global__ __launch_bounds__(SampleCfg<KS>::kThreads) void draft_sample_kernel(S
 
 }  // namespace
 
+// One step workgroup per compute unit (step_map places them), at least one per request group.
+static int step_grid(const StepArgs& a, int first) {
+  const int ngroups = (a.B + kDmaGroup - 1) / kDmaGroup;
+  const int nstep = a.persistent_wgs - first;
+  return first + (nstep > ngroups ? nstep : ngroups);
+}
+
 template <int KS, int NT>
 static hipError_t launch_step_dma(const StepArgs& a, hipStream_t s) {
-  const int ngroups = (a.B + kDmaGroup - 1) / kDmaGroup;
-  const int per = a.persistent_wgs / ngroups;
-  const int grid = (per > 0 ? per : 1) * ngroups;
-  launch_kernel(markov_step_dma_kernel<KS, NT>, dim3(grid), dim3(kDmaThreads), 0, s, a);
+  launch_kernel(markov_step_dma_kernel<KS, NT>, dim3(step_grid(a, 0)), dim3(kDmaThreads), 0, s, a);
   return hipGetLastError();
 }
 
 template <int KS, int NT>
 static hipError_t launch_step_dma_wave4(const StepArgs& a, hipStream_t s) {
-  const int ngroups = (a.B + kDmaGroup - 1) / kDmaGroup;
-  const int per = a.persistent_wgs / ngroups;
-  const int grid = (per > 0 ? per : 1) * ngroups;
-  launch_kernel(markov_step_dma_wave4_kernel<KS, NT>, dim3(grid), dim3(kDmaThreads / 2), 0, s, a);
+  launch_kernel(markov_step_dma_wave4_kernel<KS, NT>, dim3(step_grid(a, 0)), dim3(kDmaThreads / 2),
+                0, s, a);
   return hipGetLastError();
 }
 
 template <int KS, int NT, int TPW>
 static hipError_t launch_step_plan(const StepArgs& a, const PlanArgs& pa, hipStream_t s) {
-  const int ngroups = (a.B + kDmaGroup - 1) / kDmaGroup;
-  const int per = (a.persistent_wgs - 1) / ngroups;
-  const int grid = 1 + (per > 0 ? per : 1) * ngroups;
+  const int grid = step_grid(a, 1);
   launch_kernel(markov_step_plan_kernel<KS, NT, TPW>, dim3(grid), dim3(kDmaThreads / TPW), 0, s,
                 a, pa);
   return hipGetLastError();
