@@ -48,6 +48,12 @@ DRAFT_CASES = {
     "b33-v2052-r64-g4": _custom("b33-v2052-r64-g4", seed_id=16, B=33, V=2052, r=64, gamma=4),
     "b20-v8192-r256-g2": _custom("b20-v8192-r256-g2", seed_id=17, B=20, V=8192, r=256, gamma=2,
                                  u_std=3.0, w_std=0.05),
+    # the 256-request one-tile step (B > 128, r = 256): a ragged second group whose second
+    # wave is partly active, and three groups over the XCD-aware placement
+    "b300-v4100-r256-g3": _custom("b300-v4100-r256-g3", seed_id=23, B=300, V=4100, r=256,
+                                  u_std=3.0, w_std=0.05),
+    "b520-v2052-r256-g2": _custom("b520-v2052-r256-g2", seed_id=24, B=520, V=2052, r=256,
+                                  gamma=2, u_std=3.0, w_std=0.05),
     # the largest vocabulary the library takes (2^19): 16 tiles per sampler thread, the
     # sampler's per-tile masses filling 128 KiB of LDS
     "b3-v524288-r64-g2": _custom("b3-v524288-r64-g2", seed_id=18, B=3, V=1 << 19, r=64, gamma=2),
