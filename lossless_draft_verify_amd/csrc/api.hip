@@ -96,6 +96,7 @@ struct RnnDraftWs {
   float* P;
   double* s[2];
   uint16_t* E;
+  uint16_t* E2;   // the bias terms by MFMA operand, [ceil(B / 32)][gamma][3r / 16][2][32][8]
 };
 size_t rnn_draft_ws(const dspark_dims& d, void* base, RnnDraftWs* out) {
   const size_t M = static_cast<size_t>(d.B) * d.gamma;
@@ -110,11 +111,14 @@ size_t rnn_draft_ws(const dspark_dims& d, void* base, RnnDraftWs* out) {
   char* s0 = take(static_cast<size_t>(d.B) * d.r * sizeof(double));
   char* s1 = take(static_cast<size_t>(d.B) * d.r * sizeof(double));
   char* E = take(M * kRnnTerms * d.r * sizeof(uint16_t));
+  const size_t nblk = (static_cast<size_t>(d.B) + 31) / 32;
+  char* E2 = take(nblk * 32 * d.gamma * kRnnTerms * d.r * sizeof(uint16_t));
   if (out) {
     out->P = reinterpret_cast<float*>(P);
     out->s[0] = reinterpret_cast<double*>(s0);
     out->s[1] = reinterpret_cast<double*>(s1);
     out->E = reinterpret_cast<uint16_t*>(E);
+    out->E2 = reinterpret_cast<uint16_t*>(E2);
   }
   return off;
 }
@@ -312,7 +316,8 @@ dspark_status draft_loop(const dspark_dims& dims, const float* U, const uint16_t
       RnnStateArgs ra{dims.B,        dims.gamma,       k,          dims.r,
                       dims.d,        rnn->w.P,         rnn->Wgco,  W1,
                       prev,          stride,           k > 0 ? rnn->w.s[(k + 1) & 1] : nullptr,
-                      rnn->w.s[k & 1], rnn->e_rows,    rnn->w.E,   dims.V};
+                      rnn->w.s[k & 1], rnn->e_rows,    rnn->w.E,   rnn->w.E2,
+                      dims.V};
       if (timed(kRnnState, s, [&] { return launch_rnn_state(ra, s); }) != hipSuccess)
         return DSPARK_ERR_HIP;
     }
@@ -323,6 +328,7 @@ dspark_status draft_loop(const dspark_dims& dims, const float* U, const uint16_t
     if (rnn) {
       sa.e_terms = pa.e_terms = kRnnTerms;
       sa.E = pa.E = rnn->w.E;
+      sa.E2 = rnn->w.E2;
     }
     if (round_plan && k == dims.gamma - 1) {
       if (timed(kConfidence, s, [&] { return launch_confidence(round_plan->conf, s); }) !=

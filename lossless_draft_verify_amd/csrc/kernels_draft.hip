@@ -255,6 +255,31 @@ constexpr int kDmaGroup = 128;   // requests per group: 4 waves x 32 per tile
 constexpr int kDmaTiles = 2;     // 32-token tiles per item
 constexpr int kXcds = 8;         // accelerator complex dies of an MI355X, each with its own L2
 
+// Bias rows of a wave's 32 requests in MFMA operand form (lane (h, c): k-step s is bf16
+// 16 s + 8 h .. + 8 of request c's row): from the operand layout E2 when the RNN state step wrote
+// it (one contiguous 1 KB a k-step), else from the rows. blk is the wave's 32-request block, row
+// its request within the 128-request group.
+template <int KS, int NT>
+__device__ __forceinline__ void load_bias_operands(const StepArgs& p, int blk, int row, int half,
+                                                   int col, u16x8_t (&e)[NT * KS]) {
+  if (NT > 1 && p.E2) {
+    const int nblk = (p.B + 31) / 32;
+    const uint16_t* src = p.E2 +
+        ((static_cast<size_t>(min(blk, nblk - 1)) * p.gamma + p.k) * (NT * KS) * 2 + half) * 256 +
+        8 * col;
+#pragma unroll
+    for (int s = 0; s < NT * KS; ++s) e[s] = load_u16x8(src + 512 * s);
+    return;
+  }
+  const int b = min((blk / 4) * kDmaGroup + row, p.B - 1);
+  const int32_t prev =
+      (NT == 1) ? clamp_token(p.prev[static_cast<size_t>(b) * p.prev_stride], p.V) : 0;
+  const uint16_t* erow =
+      bias_row<NT>(p.W1, p.E, 16 * KS, prev, static_cast<int64_t>(b) * p.gamma + p.k) + 8 * half;
+#pragma unroll
+  for (int s = 0; s < NT * KS; ++s) e[s] = load_u16x8(erow + 16 * s);
+}
+
 // TPW: 32-token tiles each wave computes per item (1: eight waves; 2: four waves, each taking
 // both tiles of its request quarter).
 template <int KS, int TPW = 1>
@@ -447,11 +472,7 @@ __device__ __forceinline__ void markov_step_dma(const StepArgs& p, StepMap mp, D
     }
     lds_barrier();                              // stage 1 is free for item 1
   } else {
-    const int b = min(group * kDmaGroup + row_own, p.B - 1);
-    const uint16_t* erow =
-        bias_row<NT>(p.W1, p.E, D::r, 0, static_cast<int64_t>(b) * p.gamma + p.k) + 8 * half;
-#pragma unroll
-    for (int s = 0; s < NT * KS; ++s) e[s] = load_u16x8(erow + 16 * s);
+    load_bias_operands<KS, NT>(p, group * kDmaGroup / 32 + rq, row_own, half, col, e);
     __builtin_amdgcn_s_waitcnt(0);
     issue(0);
   }
@@ -571,13 +592,159 @@ __global__ __launch_bounds__(kDmaThreads, 1) void markov_step_dma_kernel(StepArg
   markov_step_dma<KS, NT>(p, step_map(p.B, blockIdx.x, gridDim.x, 0), lds);
 }
 
-// The pipelined step with four waves (one per SIMD), each computing both token tiles of an item
-// for its request quarter: 512 registers a lane leave room for the RNN head's three-term bias
-// rows at r = 256 (192 registers), which two waves per SIMD cannot hold.
+
+// The pipelined step for bias rows held in registers with one wave per SIMD (the RNN head's
+// three-term rows at r = 256): 32-token items in four 32 KB stages, so that three items stream
+// while a wave runs the 48 MFMA k-steps of its tile (with 64-token items in two stages only one
+// item was in flight behind them). Wave w computes the item's tile for request quarter w with
+// the MFMA sequence and epilogue of the other step kernels, so the partials are bit-identical.
+// The bias rows come from the operand layout where the state step wrote it.
+template <int KS>
+struct Deep4Step {
+  static constexpr int r = 16 * KS;
+  static constexpr int kThreads = 256;
+  static constexpr int kWaves = 4;
+  static constexpr int kTok = kTileTokens;                          // one tile per item
+  static constexpr int kW2Chunks = 2 * KS;
+  static constexpr int kW2Bytes = kTok * kW2Chunks * 16;            // 16 KB at r = 256
+  static constexpr int kUChunks = kTok / 4;                         // 8 per U row segment
+  static constexpr int kUBytes = kDmaGroup * kUChunks * 16;         // 16 KB
+  static constexpr int kStageBytes = kW2Bytes + kUBytes;
+  static constexpr int kStages = 4;
+  static constexpr int kPartItems = 16;
+  static constexpr int kW2Copies = kW2Bytes / 1024 / kWaves;
+  static constexpr int kUCopies = kUBytes / 1024 / kWaves;
+  static constexpr int kCopies = kW2Copies + kUCopies;
+  static constexpr int kW2Swz = 15;
+  static_assert(KS == 16, "r = 256");
+  static_assert((kStages - 1) * kCopies <= 63, "vmcnt range");
+};
+
 template <int KS, int NT>
-__global__ __launch_bounds__(kDmaThreads / 2, 1) void markov_step_dma_wave4_kernel(StepArgs p) {
-  __shared__ DmaLds<KS> lds;
-  markov_step_dma<KS, NT, 2>(p, step_map(p.B, blockIdx.x, gridDim.x, 0), lds);
+__global__ __launch_bounds__(256, 1) void markov_step_deep4_kernel(StepArgs p) {
+  using D = Deep4Step<KS>;
+  __shared__ __attribute__((aligned(1024))) unsigned char stage[D::kStages * D::kStageBytes];
+  __shared__ float2 pbuf[D::kPartItems * kDmaGroup];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5, col = lane & 31;
+  const StepMap mp = step_map(p.B, blockIdx.x, gridDim.x, 0);
+  if (mp.group < 0) return;
+  const int group = mp.group;
+  const int nitems = p.ntiles;
+  const int item_lo = static_cast<int>(static_cast<int64_t>(nitems) * mp.wg / mp.nwg);
+  const int n = static_cast<int>(static_cast<int64_t>(nitems) * (mp.wg + 1) / mp.nwg) - item_lo;
+  if (n <= 0) return;
+  const int row_own = 32 * wave + col;
+  const bool wave_active = group * kDmaGroup + 32 * wave < p.B;
+  const uint32_t stage_addr = lds_addr(stage);
+  // A operand (W2t row col, chunk 2s + half) of k-step s at a_off[s % 8] + 256 (s / 8); U chunk
+  // 2g + half of row row_own at u_off[g].
+  uint32_t a_off[8], u_off[4];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) a_off[t] = 16 * (col * D::kW2Chunks + ((2 * t + half) ^ (col & D::kW2Swz)));
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+    u_off[g] = D::kW2Bytes + 16 * (row_own * D::kUChunks + ((2 * g + half) ^ (row_own & 7)));
+
+  // This wave's share of item j's copies into stage j % kStages; rows past V or B are clamped
+  // to the last valid one and masked in the epilogue.
+  auto issue = [&](int j) {
+    const int tok0 = (item_lo + j) * D::kTok;
+    const uint32_t base = stage_addr + (j % D::kStages) * D::kStageBytes;
+#pragma unroll
+    for (int i = 0; i < D::kW2Copies; ++i) {
+      const int q = wave * D::kW2Copies + i;
+      const int slot = 64 * q + lane;
+      const int row = slot / D::kW2Chunks;
+      const int c = (slot % D::kW2Chunks) ^ (row & D::kW2Swz);
+      const int tok = min(tok0 + row, p.V - 1);
+      copy16_to_lds(p.W2t + static_cast<size_t>(tok) * D::r + 8 * c, base + 1024 * q);
+    }
+#pragma unroll
+    for (int i = 0; i < D::kUCopies; ++i) {
+      const int q = wave * D::kUCopies + i;
+      const int slot = 64 * q + lane;
+      const int row = slot / D::kUChunks;
+      const int c = (slot % D::kUChunks) ^ (row & 7);
+      const int b = min(group * kDmaGroup + row, p.B - 1);
+      const int v = min(tok0 + 4 * c, p.V - 4);
+      copy16_to_lds_nt(p.U + (static_cast<size_t>(b >> p.u_shift) * p.gamma + p.k) * p.V + v,
+                       base + D::kW2Bytes + 1024 * q);
+    }
+  };
+  auto flush = [&](int j0, int j1) {
+    const int per = j1 - j0;
+    for (int x = tid; x < kDmaGroup * per; x += D::kThreads) {
+      const int row = x / per, tt = x % per;
+      const int b = group * kDmaGroup + row;
+      if (b < p.B)
+        p.part[static_cast<size_t>(b) * p.ntiles + item_lo + j0 + tt] =
+            pbuf[((j0 + tt) % D::kPartItems) * kDmaGroup + row];
+    }
+  };
+
+  // Prologue: the first kStages - 1 items' copies, then each lane's bias rows (all NT terms)
+  // into registers behind them; all of it is drained before the loop, whose waits then count
+  // copies only.
+#pragma unroll
+  for (int j = 0; j < D::kStages - 1; ++j)
+    if (j < n) issue(j);
+  u16x8_t e[NT * KS];
+  load_bias_operands<KS, NT>(p, group * kDmaGroup / 32 + wave, row_own, half, col, e);
+  __builtin_amdgcn_s_waitcnt(0);
+  int flushed = 0;
+  for (int j = 0; j < n; ++j) {
+    if (j + D::kStages - 1 < n) issue(j + D::kStages - 1);
+    // item j is complete once at most the copies of the items issued after it are in flight
+    wait_copies_upto<0, D::kCopies, D::kStages - 1>(min(D::kStages - 1, n - 1 - j));
+    asm volatile("s_barrier" ::: "memory");
+    const int tok0 = (item_lo + j) * D::kTok;
+    if (wave_active) {
+      const unsigned char* base = stage + (j % D::kStages) * D::kStageBytes;
+      u16x8_t a[KS];
+#pragma unroll
+      for (int s2 = 0; s2 < KS; ++s2)
+        a[s2] = *reinterpret_cast<const u16x8_t*>(base + 256 * (s2 >> 3) + a_off[s2 & 7]);
+      float4 uu[4];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) uu[g] = *reinterpret_cast<const float4*>(base + u_off[g]);
+      f32x16_t acc = {};
+#pragma unroll
+      for (int s2 = 0; s2 < NT * KS; ++s2) acc = mfma_32x32x16(a[s2 % KS], e[s2], acc);
+      // Epilogue as in the other step kernels (the same partials bit for bit).
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        acc[4 * g + 0] += uu[g].x;
+        acc[4 * g + 1] += uu[g].y;
+        acc[4 * g + 2] += uu[g].z;
+        acc[4 * g + 3] += uu[g].w;
+      }
+      if (tok0 + kTileTokens > p.V) {
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj)
+          if (tok0 + tile_token(jj, half) >= p.V) acc[jj] = kNegInf;
+      }
+      float L[16];
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) L[jj] = acc[jj] * p.beta;
+      float m = max16(L);
+      m = fmaxf(m, other_half(m, half));
+      float t[16];
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) t[jj] = exp_term(L[jj] - m);
+      float sm = (m == kNegInf) ? 0.0f : sum16(t);
+      sm = sm + other_half(sm, half);
+      if (half == 0) pbuf[(j % D::kPartItems) * kDmaGroup + row_own] = make_float2(m, sm);
+    }
+    lds_barrier();   // stage j % kStages is free for item j + kStages
+    if ((j + 1) % D::kPartItems == 0 && j + 1 < n) {
+      flush(flushed, j + 1);
+      flushed = j + 1;
+      wait_copies<0>();   // the stores join the counter: drain it so later counts hold copies only
+    }
+  }
+  flush(flushed, n);
 }
 
 // The last draft position's step with the verify planner beside it: workgroup 0 plans (its LDS
@@ -776,9 +943,8 @@ static hipError_t launch_step_dma(const StepArgs& a, hipStream_t s) {
 }
 
 template <int KS, int NT>
-static hipError_t launch_step_dma_wave4(const StepArgs& a, hipStream_t s) {
-  launch_kernel(markov_step_dma_wave4_kernel<KS, NT>, dim3(step_grid(a, 0)), dim3(kDmaThreads / 2),
-                0, s, a);
+static hipError_t launch_step_deep4(const StepArgs& a, hipStream_t s) {
+  launch_kernel(markov_step_deep4_kernel<KS, NT>, dim3(step_grid(a, 0)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -814,8 +980,9 @@ static hipError_t launch_step_kind(const StepArgs& a, hipStream_t s) {
   }
   return launch_step_prefetch<KS, NT>(a, s);
 }
-// Bias rows of three bf16 terms (the RNN head) are built for r <= 256; the pipelined step holds
-// them in registers, with eight waves up to r = 128 and with four (one per SIMD) at r = 256.
+// Bias rows of three bf16 terms (the RNN head) are built for r <= 256; the pipelined steps hold
+// them in registers, with eight waves up to r = 128 and, at r = 256, with four (one per SIMD)
+// over 32-token items in four stages.
 template <int KS>
 static hipError_t launch_step_ks(const StepArgs& a, hipStream_t s) {
   if (a.e_terms == 1) return launch_step_kind<KS, 1>(a, s);
@@ -823,7 +990,7 @@ static hipError_t launch_step_ks(const StepArgs& a, hipStream_t s) {
     if (a.e_terms == kRnnTerms) return launch_step_kind<KS, kRnnTerms>(a, s);
   } else if constexpr (KS == 16) {
     if (a.e_terms == kRnnTerms) {
-      if (a.dbg == nullptr && (a.V & 3) == 0) return launch_step_dma_wave4<KS, kRnnTerms>(a, s);
+      if (a.dbg == nullptr && (a.V & 3) == 0) return launch_step_deep4<KS, kRnnTerms>(a, s);
       return launch_step_prefetch<KS, kRnnTerms>(a, s);
     }
   }

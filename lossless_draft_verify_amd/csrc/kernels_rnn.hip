@@ -158,6 +158,24 @@ __device__ __forceinline__ void split_terms(float e, uint16_t* row, int r) {
   row[2 * r] = bf16_rne(rest2);
 }
 
+// The terms of component j of request b's bias vector at position k, also in the MFMA operand
+// layout of StepArgs::E2 (term t is k-step element t r + j).
+__device__ __forceinline__ void split_terms_operand(float e, uint16_t* E2, int b, int k, int gamma,
+                                                    int j, int r) {
+  static_assert(kRnnTerms == 3, "three terms");
+  const uint16_t t1 = bf16_rne(e);
+  const float rest1 = e - bf16_value(t1);
+  const uint16_t t2 = bf16_rne(rest1);
+  const float rest2 = rest1 - bf16_value(t2);
+  const uint16_t t[3] = {t1, t2, bf16_rne(rest2)};
+  const size_t base = (static_cast<size_t>(b >> 5) * gamma + k) * (kRnnTerms * r / 16);
+#pragma unroll
+  for (int q = 0; q < 3; ++q) {
+    const int i = q * r + j, s = i >> 4, h = (i >> 3) & 1;
+    E2[((base + s) * 2 + h) * 256 + 8 * (b & 31) + (i & 7)] = t[q];
+  }
+}
+
 __global__ __launch_bounds__(kStateThreads) void rnn_state_kernel(RnnStateArgs p) {
   extern __shared__ double zs[];                    // [kStateB][2r]: s_{k-1} | W1[x_{k-1}]
   __shared__ double part[3][6][64];                 // quarters 1..3: (row, request) x lane
@@ -282,6 +300,7 @@ __global__ __launch_bounds__(kStateThreads) void rnn_state_kernel(RnnStateArgs p
     const float e = static_cast<float>(tanh(ao));
     p.e_out[m * r + j] = e;
     split_terms(e, p.E + m * (kRnnTerms * r) + j, r);
+    if (p.E2) split_terms_operand(e, p.E2, b, p.k, p.gamma, j, r);
   }
 }
 

@@ -23,6 +23,10 @@ struct StepArgs {
   // (b, k) as three bf16 terms, E [B][gamma][3r] (prev unused).
   int e_terms = 1;
   const uint16_t* E = nullptr;
+  // The same bias rows by MFMA operand (e_terms = 3; nullable): for each block of 32 requests and
+  // position, k-step s of the 3r / 16, half h and column c hold 8 bf16 at
+  // (((blk * gamma + k) * (3r / 16) + s) * 2 + h) * 256 + 8 c, so a wave's k-step is 1 KB.
+  const uint16_t* E2 = nullptr;
   // Rows that share a request's base logits: row b reads U row (b >> u_shift) (tree drafting:
   // the 2^u_shift expanded nodes of one request score their children from the same U_k).
   int u_shift = 0;
@@ -199,6 +203,7 @@ struct RnnStateArgs {
   double* s_out;          // [B][r] s_k
   float* e_out;           // [B][gamma][r] e_k (fp32)
   uint16_t* E;            // [B][gamma][3r] bf16 terms of e_k
+  uint16_t* E2;           // the same terms by MFMA operand (StepArgs::E2)
   int V;                  // token ids are clamped into [0, V)
 };
 

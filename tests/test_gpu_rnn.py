@@ -48,6 +48,10 @@ CASES = {
     # vocabulary range placed on one XCD, with the three-term bias rows
     "b130-v4100-r128-g3": _custom("b130-v4100-r128-g3-rnn", seed_id=54, B=130, V=4100, r=128,
                                   d=64, u_std=3.0, w_std=0.05),
+    # the four-stage one-tile step at r = 256 over two request groups, the second ragged (two
+    # requests: one wave of four active), and a 4-token tail tile
+    "b130-v4100-r256-g3": _custom("b130-v4100-r256-g3-rnn", seed_id=55, B=130, V=4100, r=256,
+                                  d=64, u_std=3.0, w_std=0.05),
 }
 
 
