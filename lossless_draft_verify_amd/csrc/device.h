@@ -248,6 +248,32 @@ __device__ __forceinline__ int block_min_int(int v, int* red) {
   for (int i = 1; i < NT / 64; ++i) m = min(m, red[i]);
   return m;
 }
+// The same reductions with LDS-only barriers (lds_barrier): global loads and LDS-DMA copies in
+// flight stay in flight through them (a __syncthreads() waits for every one).
+template <int NT>
+__device__ __forceinline__ float block_max_lds(float v, float* red) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  v = wave_max(v);
+  lds_barrier();
+  if (lane == 0) red[w] = v;
+  lds_barrier();
+  float m = red[0];
+#pragma unroll
+  for (int i = 1; i < NT / 64; ++i) m = fmaxf(m, red[i]);
+  return m;
+}
+template <int NT>
+__device__ __forceinline__ int block_min_int_lds(int v, int* red) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  v = wave_min_int(v);
+  lds_barrier();
+  if (lane == 0) red[w] = v;
+  lds_barrier();
+  int m = red[0];
+#pragma unroll
+  for (int i = 1; i < NT / 64; ++i) m = min(m, red[i]);
+  return m;
+}
 // Exclusive scan over the block; returns this thread's exclusive prefix, *total the sum.
 template <int NT>
 __device__ __forceinline__ double block_exclusive_scan(double v, double* red, double* total) {

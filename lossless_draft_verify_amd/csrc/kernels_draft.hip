@@ -280,12 +280,10 @@ __device__ __forceinline__ void load_bias_operands(const StepArgs& p, int blk, i
   for (int s = 0; s < NT * KS; ++s) e[s] = load_u16x8(erow + 16 * s);
 }
 
-// TPW: 32-token tiles each wave computes per item (1: eight waves; 2: four waves, each taking
-// both tiles of its request quarter).
-template <int KS, int TPW = 1>
+template <int KS>
 struct DmaStep {
   static constexpr int r = 16 * KS;
-  static constexpr int kThreads = kDmaThreads / TPW;
+  static constexpr int kThreads = kDmaThreads;
   static constexpr int kTok = kDmaTiles * kTileTokens;              // 64 tokens per item
   static constexpr int kW2Chunks = 2 * KS;                          // 16-byte chunks per row
   static constexpr int kW2Bytes = kTok * kW2Chunks * 16;            // 64 W2t rows
@@ -355,16 +353,16 @@ __device__ __forceinline__ StepMap step_map(int B, int h, int nblk_hw, int first
 }
 
 // The pipelined step as run by the workgroup that step_map placed at (group, wg of nwg).
-template <int KS, int NT, int TPW = 1>
+template <int KS, int NT>
 __device__ __forceinline__ void markov_step_dma(const StepArgs& p, StepMap mp, DmaLds<KS>& lds) {
-  using D = DmaStep<KS, TPW>;
+  using D = DmaStep<KS>;
   unsigned char* stage = lds.stage;
   float2* pbuf = lds.pbuf;
   int32_t* pid = lds.pid;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, col = lane & 31;
-  const int sub = wave >> 2, rq = wave & 3;   // (first) tile within the item, request quarter
+  const int sub = wave >> 2, rq = wave & 3;   // tile within the item, request quarter
   if (mp.group < 0) return;
   const int group = mp.group, wg = mp.wg, nwg = mp.nwg;
   const int nitems = (p.V + D::kTok - 1) / D::kTok;
@@ -375,22 +373,19 @@ __device__ __forceinline__ void markov_step_dma(const StepArgs& p, StepMap mp, D
   const bool wave_active = group * kDmaGroup + 32 * rq < p.B;
 
   // Per-lane LDS offsets: k-step s of the A operand (W2t row 32 sub + col, chunk 2s + half) is
-  // at a_off[s % 8] + 256 (s / 8), plus kTileA for the wave's second tile (the swizzle depends
-  // only on col); U chunk 8 tile + 2g + half of row row_own at u_off[tile - sub][g].
+  // at a_off[s % 8] + 256 (s / 8) (the swizzle depends only on col); U chunk 8 sub + 2g + half of
+  // row row_own at u_off[g].
   const uint32_t stage_addr = lds_addr(stage);
-  constexpr uint32_t kTileA = 16 * kTileTokens * D::kW2Chunks;
-  uint32_t a_off[D::kAOffs], u_off[TPW][4];
+  uint32_t a_off[D::kAOffs], u_off[4];
   {
     const int wrow = 32 * sub + col;
 #pragma unroll
     for (int t = 0; t < D::kAOffs; ++t)
       a_off[t] = 16 * (wrow * D::kW2Chunks + ((2 * t + half) ^ (wrow & D::kW2Swz)));
 #pragma unroll
-    for (int sb = 0; sb < TPW; ++sb)
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-        u_off[sb][g] = D::kW2Bytes + 16 * (row_own * D::kUChunks +
-                                           ((8 * (sub + sb) + 2 * g + half) ^ (row_own & 15)));
+    for (int g = 0; g < 4; ++g)
+      u_off[g] = D::kW2Bytes + 16 * (row_own * D::kUChunks +
+                                     ((8 * sub + 2 * g + half) ^ (row_own & 15)));
   }
 
   // This wave's share of item j's copies into stage j % kStages. Rows past V or B are clamped
@@ -486,95 +481,45 @@ __device__ __forceinline__ void markov_step_dma(const StepArgs& p, StepMap mp, D
     }
     asm volatile("s_barrier" ::: "memory");
 
-    if constexpr (TPW == 1) {
-      const int tok0 = (item_lo + j) * D::kTok + sub * kTileTokens;
-      if (wave_active && tok0 < p.V) {
-        const unsigned char* base = stage + (j % D::kStages) * D::kStageBytes;
-        u16x8_t a[KS];
-  #pragma unroll
-        for (int s = 0; s < KS; ++s)
-          a[s] = *reinterpret_cast<const u16x8_t*>(base + 256 * (s >> 3) + a_off[s % D::kAOffs]);
-        float4 uu[4];
-  #pragma unroll
-        for (int g = 0; g < 4; ++g) uu[g] = *reinterpret_cast<const float4*>(base + u_off[0][g]);
-        f32x16_t acc = {};
-  #pragma unroll
-        for (int s = 0; s < NT * KS; ++s) acc = mfma_32x32x16(a[s % KS], e[s], acc);
-        // Epilogue: L = U + bias, tile max, fp32 sum of exp(L - max) (the order of the
-        // register-prefetch step kernel, so both give the same partials bit for bit).
-  #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          acc[4 * g + 0] += uu[g].x;
-          acc[4 * g + 1] += uu[g].y;
-          acc[4 * g + 2] += uu[g].z;
-          acc[4 * g + 3] += uu[g].w;
-        }
-        if (tok0 + kTileTokens > p.V) {
-  #pragma unroll
-          for (int jj = 0; jj < 16; ++jj)
-            if (tok0 + tile_token(jj, half) >= p.V) acc[jj] = kNegInf;
-        }
-        float L[16];   // the draft temperature scales the logits (beta = 1: unchanged)
-  #pragma unroll
-        for (int jj = 0; jj < 16; ++jj) L[jj] = acc[jj] * p.beta;
-        float m = max16(L);
-        m = fmaxf(m, other_half(m, half));
-        float t[16];
-  #pragma unroll
-        for (int jj = 0; jj < 16; ++jj) t[jj] = exp_term(L[jj] - m);
-        float sm = (m == kNegInf) ? 0.0f : sum16(t);
-        sm = sm + other_half(sm, half);
-        if (half == 0)
-          pbuf[((j % D::kPartItems) * kDmaTiles + sub) * kDmaGroup + row_own] = make_float2(m, sm);
+    const int tok0 = (item_lo + j) * D::kTok + sub * kTileTokens;
+    if (wave_active && tok0 < p.V) {
+      const unsigned char* base = stage + (j % D::kStages) * D::kStageBytes;
+      u16x8_t a[KS];
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        a[s] = *reinterpret_cast<const u16x8_t*>(base + 256 * (s >> 3) + a_off[s % D::kAOffs]);
+      float4 uu[4];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) uu[g] = *reinterpret_cast<const float4*>(base + u_off[g]);
+      f32x16_t acc = {};
+#pragma unroll
+      for (int s = 0; s < NT * KS; ++s) acc = mfma_32x32x16(a[s % KS], e[s], acc);
+      // Epilogue: L = U + bias, tile max, fp32 sum of exp(L - max) (the order of the
+      // register-prefetch step kernel, so both give the same partials bit for bit).
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        acc[4 * g + 0] += uu[g].x;
+        acc[4 * g + 1] += uu[g].y;
+        acc[4 * g + 2] += uu[g].z;
+        acc[4 * g + 3] += uu[g].w;
       }
-    } else {
-      // Four waves: this wave's request quarter over each tile of the item in turn.
+      if (tok0 + kTileTokens > p.V) {
 #pragma unroll
-      for (int sb = 0; sb < TPW; ++sb) {
-        const int tile = sub + sb;
-        const int tok0 = (item_lo + j) * D::kTok + tile * kTileTokens;
-        if (wave_active && tok0 < p.V) {
-          const unsigned char* base = stage + (j % D::kStages) * D::kStageBytes;
-          u16x8_t a[KS];
-#pragma unroll
-          for (int s = 0; s < KS; ++s)
-            a[s] = *reinterpret_cast<const u16x8_t*>(base + kTileA * sb + 256 * (s >> 3) +
-                                                     a_off[s % D::kAOffs]);
-          float4 uu[4];
-#pragma unroll
-          for (int g = 0; g < 4; ++g)
-            uu[g] = *reinterpret_cast<const float4*>(base + u_off[sb][g]);
-          f32x16_t acc = {};
-#pragma unroll
-          for (int s = 0; s < NT * KS; ++s) acc = mfma_32x32x16(a[s % KS], e[s], acc);
-          // Epilogue as in the eight-wave path (the same partials bit for bit).
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            acc[4 * g + 0] += uu[g].x;
-            acc[4 * g + 1] += uu[g].y;
-            acc[4 * g + 2] += uu[g].z;
-            acc[4 * g + 3] += uu[g].w;
-          }
-          if (tok0 + kTileTokens > p.V) {
-#pragma unroll
-            for (int jj = 0; jj < 16; ++jj)
-              if (tok0 + tile_token(jj, half) >= p.V) acc[jj] = kNegInf;
-          }
-          float L[16];
-#pragma unroll
-          for (int jj = 0; jj < 16; ++jj) L[jj] = acc[jj] * p.beta;
-          float m = max16(L);
-          m = fmaxf(m, other_half(m, half));
-          float t[16];
-#pragma unroll
-          for (int jj = 0; jj < 16; ++jj) t[jj] = exp_term(L[jj] - m);
-          float sm = (m == kNegInf) ? 0.0f : sum16(t);
-          sm = sm + other_half(sm, half);
-          if (half == 0)
-            pbuf[((j % D::kPartItems) * kDmaTiles + tile) * kDmaGroup + row_own] =
-                make_float2(m, sm);
-        }
+        for (int jj = 0; jj < 16; ++jj)
+          if (tok0 + tile_token(jj, half) >= p.V) acc[jj] = kNegInf;
       }
+      float L[16];   // the draft temperature scales the logits (beta = 1: unchanged)
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) L[jj] = acc[jj] * p.beta;
+      float m = max16(L);
+      m = fmaxf(m, other_half(m, half));
+      float t[16];
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) t[jj] = exp_term(L[jj] - m);
+      float sm = (m == kNegInf) ? 0.0f : sum16(t);
+      sm = sm + other_half(sm, half);
+      if (half == 0)
+        pbuf[((j % D::kPartItems) * kDmaTiles + sub) * kDmaGroup + row_own] = make_float2(m, sm);
     }
     lds_barrier();   // stage j % kStages is free for item j + kStages
     if ((j + 1) % D::kPartItems == 0 && j + 1 < n) {
@@ -620,15 +565,22 @@ struct Deep4Step {
   static_assert((kStages - 1) * kCopies <= 63, "vmcnt range");
 };
 
-template <int KS, int NT>
-__global__ __launch_bounds__(256, 1) void markov_step_deep4_kernel(StepArgs p) {
+template <int KS>
+struct Deep4Lds {
   using D = Deep4Step<KS>;
-  __shared__ __attribute__((aligned(1024))) unsigned char stage[D::kStages * D::kStageBytes];
-  __shared__ float2 pbuf[D::kPartItems * kDmaGroup];
+  __attribute__((aligned(1024))) unsigned char stage[D::kStages * D::kStageBytes];
+  float2 pbuf[D::kPartItems * kDmaGroup];
+};
+
+template <int KS, int NT>
+__device__ __forceinline__ void markov_step_deep4(const StepArgs& p, StepMap mp,
+                                                  Deep4Lds<KS>& lds) {
+  using D = Deep4Step<KS>;
+  unsigned char* stage = lds.stage;
+  float2* pbuf = lds.pbuf;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, col = lane & 31;
-  const StepMap mp = step_map(p.B, blockIdx.x, gridDim.x, 0);
   if (mp.group < 0) return;
   const int group = mp.group;
   const int nitems = p.ntiles;
@@ -747,22 +699,42 @@ __global__ __launch_bounds__(256, 1) void markov_step_deep4_kernel(StepArgs p) {
   flush(flushed, n);
 }
 
+template <int KS, int NT>
+__global__ __launch_bounds__(256, 1) void markov_step_deep4_kernel(StepArgs p) {
+  __shared__ Deep4Lds<KS> lds;
+  markov_step_deep4<KS, NT>(p, step_map(p.B, blockIdx.x, gridDim.x, 0), lds);
+}
+
+
 // The last draft position's step with the verify planner beside it: workgroup 0 plans (its LDS
 // holds the planner's arrays in place of the copy stages), the others run the step. The plan
 // needs only the confidences, which need only the tokens before the last position, so it costs
 // the round no time of its own; no workgroup waits for another.
 constexpr int kFusedPlanMax = 4096;   // B * gamma limit of the fused planner
 
-template <int KS, int NT, int TPW>
-__global__ __launch_bounds__(kDmaThreads / TPW, 1) void markov_step_plan_kernel(StepArgs p,
+template <int KS, int NT>
+__global__ __launch_bounds__(kDmaThreads, 1) void markov_step_plan_kernel(StepArgs p,
                                                                                PlanArgs pa) {
   __shared__ DmaLds<KS> lds;
   static_assert(sizeof(plan::Smem<kFusedPlanMax>) <= sizeof(lds.stage), "planner fits the stages");
   if (blockIdx.x == 0) {
-    plan::run<kDmaThreads / TPW>(pa, *reinterpret_cast<plan::Smem<kFusedPlanMax>*>(lds.stage));
+    plan::run<kDmaThreads>(pa, *reinterpret_cast<plan::Smem<kFusedPlanMax>*>(lds.stage));
     return;
   }
-  markov_step_dma<KS, NT, TPW>(p, step_map(p.B, blockIdx.x, gridDim.x, 1), lds);
+  markov_step_dma<KS, NT>(p, step_map(p.B, blockIdx.x, gridDim.x, 1), lds);
+}
+
+// The same with the verify planner on workgroup 0 (its arrays in place of the copy stages), for
+// the last position of an RNN-head draft at r = 256.
+template <int KS, int NT>
+__global__ __launch_bounds__(256, 1) void markov_step_deep4_plan_kernel(StepArgs p, PlanArgs pa) {
+  __shared__ Deep4Lds<KS> lds;
+  static_assert(sizeof(plan::Smem<kFusedPlanMax>) <= sizeof(lds.stage), "planner fits the stages");
+  if (blockIdx.x == 0) {
+    plan::run<256>(pa, *reinterpret_cast<plan::Smem<kFusedPlanMax>*>(lds.stage));
+    return;
+  }
+  markov_step_deep4<KS, NT>(p, step_map(p.B, blockIdx.x, gridDim.x, 1), lds);
 }
 
 // One 1024-thread workgroup per request. Thread t holds a contiguous range of at most 16 tile
@@ -812,6 +784,9 @@ __global__ __launch_bounds__(SampleCfg<KS>::kThreads) void draft_sample_kernel(S
   const int c0 = min(nt, tid * per), c1 = min(nt, c0 + per);
   const int32_t prevtok = clamp_token(p.prev[static_cast<size_t>(b) * p.prev_stride], p.V);
   const int32_t forced = p.force ? clamp_token(p.force[out], p.V) : 0;   // conditioning token
+  // The draw's uniform, loaded with the rest at entry (wave 0 reads it after the reductions).
+  const float u_draw = (tid < 64) ? p.uniforms[(static_cast<size_t>(b) * (p.gamma + 1) + p.k) * 3]
+                                  : 0.0f;
   __shared__ __attribute__((aligned(16))) uint16_t Es[16 * KS * NT];
   float2 v[kSamplePer];
   auto load_parts = [&](auto n_c) {
@@ -836,7 +811,7 @@ __global__ __launch_bounds__(SampleCfg<KS>::kThreads) void draft_sample_kernel(S
   float m = kNegInf;
 #pragma unroll
   for (int i = 0; i < kSamplePer; ++i) m = fmaxf(m, v[i].x);
-  const float M = block_max<kSampleThreads>(m, red_f);
+  const float M = block_max_lds<kSampleThreads>(m, red_f);
   int gtile = 0x7fffffff;
   if (p.greedy) {
     // Greedy draft (the partials hold unscaled logits): the first tile whose max is the row max.
@@ -844,7 +819,7 @@ __global__ __launch_bounds__(SampleCfg<KS>::kThreads) void draft_sample_kernel(S
 #pragma unroll
     for (int i = 0; i < kSamplePer; ++i)
       if (i < per && c0 + i < c1 && v[i].x == M) first = min(first, c0 + i);
-    gtile = block_min_int<kSampleThreads>(first, red_i);
+    gtile = block_min_int_lds<kSampleThreads>(first, red_i);
   } else {
     double S = 0.0;
 #pragma unroll
@@ -856,7 +831,7 @@ __global__ __launch_bounds__(SampleCfg<KS>::kThreads) void draft_sample_kernel(S
       }
     }
     ssum[tid] = S;
-    __syncthreads();
+    lds_barrier();   // the embedding-row copy stays in flight (waited for before the recompute)
   }
   if (tid >= 64) return;
   Located L;
@@ -868,8 +843,7 @@ __global__ __launch_bounds__(SampleCfg<KS>::kThreads) void draft_sample_kernel(S
     L.take_last = 0;
     lse = static_cast<double>(M);
   } else {
-    const double u =
-        static_cast<double>(p.uniforms[(static_cast<size_t>(b) * (p.gamma + 1) + p.k) * 3]);
+    const double u = static_cast<double>(u_draw);
     L = wave_locate<kSampleThreads>(
         ssum, nt, per, [u](double Z) { return u * Z; }, [&](int c) { return mass[c]; });
     lse = static_cast<double>(M) + log(L.total);
@@ -948,10 +922,10 @@ static hipError_t launch_step_deep4(const StepArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int KS, int NT, int TPW>
+template <int KS, int NT>
 static hipError_t launch_step_plan(const StepArgs& a, const PlanArgs& pa, hipStream_t s) {
   const int grid = step_grid(a, 1);
-  launch_kernel(markov_step_plan_kernel<KS, NT, TPW>, dim3(grid), dim3(kDmaThreads / TPW), 0, s,
+  launch_kernel(markov_step_plan_kernel<KS, NT>, dim3(grid), dim3(kDmaThreads), 0, s,
                 a, pa);
   return hipGetLastError();
 }
@@ -1028,8 +1002,8 @@ static hipError_t launch_sample_ks(const SampleArgs& a, hipStream_t s) {
 hipError_t launch_markov_step(const StepArgs& a, int r, hipStream_t s) {
   DSPARK_DISPATCH_KS(r, launch_step_ks, a, s)
 }
-// The shapes the pipelined step takes (eight waves; four for the RNN head's three-term bias rows
-// at r = 256).
+// The shapes the pipelined step with the planner beside it takes (eight waves; the four-stage
+// kernel for the RNN head's three-term bias rows at r = 256).
 bool markov_step_plan_fits(const StepArgs& a, int r, int B, int gamma) {
   return (r == 64 || r == 128 || r == 256) && (a.e_terms == 1 || a.e_terms == kRnnTerms) &&
          a.dbg == nullptr && (a.V & 3) == 0 &&
@@ -1039,16 +1013,20 @@ bool markov_step_plan_fits(const StepArgs& a, int r, int B, int gamma) {
 hipError_t launch_markov_step_plan(const StepArgs& a, const PlanArgs& pa, int r, hipStream_t s) {
   if (a.e_terms == kRnnTerms) {
     switch (r) {
-      case 64: return launch_step_plan<4, kRnnTerms, 1>(a, pa, s);
-      case 128: return launch_step_plan<8, kRnnTerms, 1>(a, pa, s);
-      case 256: return launch_step_plan<16, kRnnTerms, 2>(a, pa, s);
+      case 64: return launch_step_plan<4, kRnnTerms>(a, pa, s);
+      case 128: return launch_step_plan<8, kRnnTerms>(a, pa, s);
+      case 256: {
+        launch_kernel(markov_step_deep4_plan_kernel<16, kRnnTerms>, dim3(step_grid(a, 1)), dim3(256),
+                      0, s, a, pa);
+        return hipGetLastError();
+      }
       default: return hipErrorInvalidValue;
     }
   }
   switch (r) {
-    case 64: return launch_step_plan<4, 1, 1>(a, pa, s);
-    case 128: return launch_step_plan<8, 1, 1>(a, pa, s);
-    case 256: return launch_step_plan<16, 1, 1>(a, pa, s);
+    case 64: return launch_step_plan<4, 1>(a, pa, s);
+    case 128: return launch_step_plan<8, 1>(a, pa, s);
+    case 256: return launch_step_plan<16, 1>(a, pa, s);
     default: return hipErrorInvalidValue;
   }
 }
