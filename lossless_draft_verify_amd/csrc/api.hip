@@ -141,6 +141,7 @@ size_t verify_ws(const dspark_dims& d, void* base, VerifyWs* out) {
   w.erow = reinterpret_cast<int32_t*>(take(B * sizeof(int32_t)));
   w.erow_lse = reinterpret_cast<double*>(take(B * sizeof(double)));
   w.eflags = reinterpret_cast<uint32_t*>(take(B * sizeof(uint32_t)));
+  w.eprev = reinterpret_cast<int32_t*>(take(B * sizeof(int32_t)));
   w.rsum = reinterpret_cast<double*>(take(B * nt * sizeof(double)));
   w.rmin = reinterpret_cast<double*>(take(B * nt * sizeof(double)));
   w.rcount = reinterpret_cast<int32_t*>(take(sizeof(int32_t)));

@@ -252,6 +252,7 @@ __global__ __launch_bounds__(kBlock) void accept_kernel(VerifyArgs p) {
     p.ws.erow[b] = off + last;
     p.ws.erow_lse[b] = lse_s[w][last];
     p.ws.eflags[b] = fl;
+    p.ws.eprev[b] = prev_x;
   }
 }
 
@@ -707,31 +708,55 @@ __global__ __launch_bounds__(kBlock) void emit_sample_kernel(VerifyArgs p) {
   const int j = p.ws.epos[b];
   const int erow = p.ws.erow[b];
   uint32_t fl = p.ws.eflags[b];
-  const double u = static_cast<double>(p.uniforms[(static_cast<size_t>(b) * (p.gamma + 1) + j - 1) * 3 + 2]);
+  const int32_t eprev = p.ws.eprev[b];
   const float* trow = p.target + static_cast<size_t>(erow) * p.V;
   bool from_target = (kind == kEmitBonus);
   int token = 0;
+  // The residual tile masses and overlap partials of this request's first batch are loaded
+  // with the records, before the kind is known (a bonus emission does not use them), so that
+  // they do not wait for it; so are the uniform and the inputs of the residual terms of the tile
+  // walk (they need only the position).
+  constexpr int kBatch = 16;
+  const int nt = p.ntiles;
+  const size_t rbase = static_cast<size_t>(b) * nt;
+  double w0[kBatch], ov0[kBatch];
+#pragma unroll
+  for (int i = 0; i < kBatch; ++i) {
+    const int c = min(i * kBlock + tid, nt - 1);
+    w0[i] = p.ws.rsum[rbase + c];
+    ov0[i] = p.ws.rmin[rbase + c];
+  }
+  const size_t pos = static_cast<size_t>(b) * p.gamma + j - 1;
+  const double u = static_cast<double>(p.uniforms[(static_cast<size_t>(b) * (p.gamma + 1) + j - 1) * 3 + 2]);
+  const int32_t xtok = p.tokens[pos];
+  const double lse_d = p.lse[pos], lse_t = p.ws.erow_lse[b];
 
   if (kind == kEmitResidual) {
     // Residual tile masses into LDS (16 loads in flight per thread) with the overlap partials;
-    // the embedding row of the position's previous token is copied into LDS behind them.
-    const size_t base = static_cast<size_t>(b) * p.ntiles;
-    const int nt = p.ntiles;
-    const int32_t prevtok = (NT == 1) ? emit_prev(p, b, j) : 0;
-    constexpr int kBatch = 16;
+    // the embedding row of the position's previous token (accept's record) is copied into LDS
+    // behind them and waited for only before the recompute.
+    const int32_t prevtok = (NT == 1) ? clamp_token(eprev, p.V) : 0;
+    if (tid < 64)
+      copy_row_to_lds<2 * KS * NT>(
+          bias_row<NT>(p.W1, p.E, 16 * KS, prevtok, static_cast<int64_t>(pos)), lds_addr(Es),
+          tid);
     double o = 0.0;
     for (int c0 = 0; c0 < nt; c0 += kBlock * kBatch) {
       double w[kBatch], ov[kBatch];
+      if (c0 == 0) {
 #pragma unroll
-      for (int i = 0; i < kBatch; ++i) {
-        const int c = min(c0 + i * kBlock + tid, nt - 1);
-        w[i] = p.ws.rsum[base + c];
-        ov[i] = p.ws.rmin[base + c];
+        for (int i = 0; i < kBatch; ++i) {
+          w[i] = w0[i];
+          ov[i] = ov0[i];
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) {
+          const int c = min(c0 + i * kBlock + tid, nt - 1);
+          w[i] = p.ws.rsum[rbase + c];
+          ov[i] = p.ws.rmin[rbase + c];
+        }
       }
-      if (c0 == 0 && tid < 64)
-        copy_row_to_lds<2 * KS * NT>(
-            bias_row<NT>(p.W1, p.E, 16 * KS, prevtok, static_cast<int64_t>(b) * p.gamma + j - 1),
-            lds_addr(Es), tid);
 #pragma unroll
       for (int i = 0; i < kBatch; ++i) {
         const int c = c0 + i * kBlock + tid;
@@ -741,14 +766,14 @@ __global__ __launch_bounds__(kBlock) void emit_sample_kernel(VerifyArgs p) {
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
     const int per = (nt + kBlock - 1) / kBlock;   // <= 64 (V <= 2^19)
     const int c0 = min(nt, tid * per), c1 = min(nt, c0 + per);
     double S = 0.0;
     for (int c = c0; c < c1; ++c) S += stage[padded(c)];
     ssum[tid] = S;
     osum[tid] = o;
-    __syncthreads();
+    lds_barrier();
     if (tid < 64) {
       double og = 0.0;
 #pragma unroll
@@ -759,7 +784,7 @@ __global__ __launch_bounds__(kBlock) void emit_sample_kernel(VerifyArgs p) {
           ssum, nt, per, [u](double Z) { return u * Z; }, [&](int c) { return stage[padded(c)]; });
       if (tid == 0) loc = L;
     }
-    __syncthreads();
+    lds_barrier();
     const Located L = loc;
     if (L.chunk < 0) {
       fl |= 2u;
@@ -767,7 +792,7 @@ __global__ __launch_bounds__(kBlock) void emit_sample_kernel(VerifyArgs p) {
     } else {
       if (tid >= 64) return;
       const int tok0 = L.chunk * kTileTokens;
-      const float* Urow = p.U + (static_cast<size_t>(b) * p.gamma + j - 1) * p.V;
+      const float* Urow = p.U + pos * p.V;
       const float tv = (lane < kTileTokens && tok0 + lane < p.V) ? trow[tok0 + lane] : 0.0f;
       wait_copies<0>();   // the embedding row
       recompute_tile_lds<KS, NT>(Es, p.W2t, Urow, tok0, p.V, Ls);
@@ -776,11 +801,8 @@ __global__ __launch_bounds__(kBlock) void emit_sample_kernel(VerifyArgs p) {
       float w = 0.0f;
       if (lane < kTileTokens && tok0 + lane < p.V) {
         float ov;
-        const int32_t xtok = p.tokens[static_cast<size_t>(b) * p.gamma + j - 1];
-        residual_pair(draft_prob(Ls[lane], p.beta,
-                                 p.lse[static_cast<size_t>(b) * p.gamma + j - 1] * kLog2e64,
-                                 p.greedy, tok0 + lane == xtok),
-                      tv, p.ws.erow_lse[b] * kLog2e64, w, ov);
+        residual_pair(draft_prob(Ls[lane], p.beta, lse_d * kLog2e64, p.greedy, tok0 + lane == xtok),
+                      tv, lse_t * kLog2e64, w, ov);
       }
       token = tok0 + walk_tile(static_cast<double>(w), L.before, L.target, L.take_last != 0);
     }

@@ -96,6 +96,7 @@ struct VerifyWs {
   int32_t* erow;     // [B] packed target row of the emission
   double* erow_lse;  // [B] log-sum-exp of that target row
   uint32_t* eflags;  // [B]
+  int32_t* eprev;    // [B] conditioning token of a residual emission's position (its bias row)
   double* rsum;      // [B][ntiles] residual mass per 32-token tile
   double* rmin;      // [B][ntiles] sum of min(p_t, p_d) per tile
   int32_t* rcount;   // [1] residual emissions (zeroed by the target pass, counted by accept)
