@@ -110,14 +110,15 @@ __global__ __launch_bounds__(kBlock) void accept_kernel(VerifyArgs p) {
   const int ell = min(max(p.draft_len[b], 0), p.gamma);   // a length past gamma is clamped
   const int off = p.row_offsets[b];
   uint32_t fl = 0;
-  // 0. Everything that needs only (ell, off) goes out first: the accept-test inputs of the first
-  //    64 positions and, for nseg <= 32, the segment statistics of every verified row; the
-  //    target value of a drafted token waits for the token.
+  // 0. The accept-test inputs of the first 64 positions go out with (ell, off), for every
+  //    drafted position (lanes past ell are masked where they are used); then, needing only those,
+  //    the segment statistics of every verified row (for nseg <= 32) and the target values of
+  //    the drafted tokens.
   float tx0 = 0.0f, u0 = 0.0f, q0 = 0.0f;
   int32_t x0 = 0;
   double lsed0 = 0.0;
   const int32_t anc = p.anchor ? clamp_token(p.anchor[b], p.V) : 0;   // none for the RNN head
-  if (lane < ell) {
+  if (lane < p.gamma) {
     x0 = clamp_token(p.tokens[static_cast<size_t>(b) * p.gamma + lane], p.V);
     lsed0 = p.lse[static_cast<size_t>(b) * p.gamma + lane];
     u0 = p.uniforms[(static_cast<size_t>(b) * (p.gamma + 1) + lane) * 3 + 1];
