@@ -156,7 +156,7 @@ def test_draft_plan_against_the_oracle_planner():
 
 # The RNN head (eq. (6)): name -> (workload, whether the plan runs beside the last step)
 RNN_CASES = {
-    "rnn-b128-v129280-g5": (W.WORKLOADS["b128-v129280-g5"], True),      # four-wave step, r = 256
+    "rnn-b128-v129280-g5": (W.WORKLOADS["b128-v129280-g5"], True),      # four-stage step, r = 256
     "rnn-b130-v4100-r128-g3": (_custom("rnn-b130-v4100-r128-g3", seed_id=47, B=130, V=4100, r=128,
                                        d=64, u_std=3.0, w_std=0.05), True),
     "rnn-b33-v2052-r64-g4": (_custom("rnn-b33-v2052-r64-g4", seed_id=48, B=33, V=2052, r=64, d=64,
