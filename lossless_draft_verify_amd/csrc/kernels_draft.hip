@@ -371,10 +371,20 @@ __device__ __forceinline__ void markov_step_dma(const StepArgs& p, StepMap mp, D
   if (n <= 0) return;
   const int row_own = 32 * rq + col;                    // request row within the group
   const bool wave_active = group * kDmaGroup + 32 * rq < p.B;
+  // Rows that read one U row (u_shift > 0: the expanded nodes of one request) share one copy of
+  // it: the stage holds the group's nd = kDmaGroup >> u_shift distinct U rows, four to a 1 KB
+  // copy, and the copies are spread over the waves (ucopies_w of them per item on this wave).
+  const int ush = p.u_shift;
+  const int u0 = (group * kDmaGroup) >> ush;            // the group's first U row
+  const int nd = max(1, kDmaGroup >> ush);
+  const int ucopies = max(1, nd * D::kUChunks * 16 / 1024);
+  const int uper = __builtin_amdgcn_readfirstlane(max(1, ucopies / D::kWaves));
+  const int ucopies_w = __builtin_amdgcn_readfirstlane(max(0, min(uper, ucopies - wave * uper)));
+  const int urow_own = ((group * kDmaGroup + row_own) >> ush) - u0;   // lane's U row in the stage
 
   // Per-lane LDS offsets: k-step s of the A operand (W2t row 32 sub + col, chunk 2s + half) is
   // at a_off[s % 8] + 256 (s / 8) (the swizzle depends only on col); U chunk 8 sub + 2g + half of
-  // row row_own at u_off[g].
+  // the lane's U row at u_off[g].
   const uint32_t stage_addr = lds_addr(stage);
   uint32_t a_off[D::kAOffs], u_off[4];
   {
@@ -384,9 +394,11 @@ __device__ __forceinline__ void markov_step_dma(const StepArgs& p, StepMap mp, D
       a_off[t] = 16 * (wrow * D::kW2Chunks + ((2 * t + half) ^ (wrow & D::kW2Swz)));
 #pragma unroll
     for (int g = 0; g < 4; ++g)
-      u_off[g] = D::kW2Bytes + 16 * (row_own * D::kUChunks +
-                                     ((8 * sub + 2 * g + half) ^ (row_own & 15)));
+      u_off[g] = D::kW2Bytes + 16 * (urow_own * D::kUChunks +
+                                     ((8 * sub + 2 * g + half) ^ (urow_own & 15)));
   }
+  // Item j is complete once at most the next item's copies (this wave's count) are in flight.
+  auto wait_item = [&]() { wait_copies_upto<D::kW2Copies, 1, D::kUCopies>(ucopies_w); };
 
   // This wave's share of item j's copies into stage j % kStages. Rows past V or B are clamped
   // to the last valid one (all addresses stay inside the tensors); the epilogue masks them.
@@ -404,14 +416,16 @@ __device__ __forceinline__ void markov_step_dma(const StepArgs& p, StepMap mp, D
     }
 #pragma unroll
     for (int i = 0; i < D::kUCopies; ++i) {
-      const int q = wave * D::kUCopies + i;
-      const int slot = 64 * q + lane;
-      const int row = slot / D::kUChunks;
-      const int c = (slot % D::kUChunks) ^ (row & 15);
-      const int b = min(group * kDmaGroup + row, p.B - 1);
-      const int v = min(tok0 + 4 * c, p.V - 4);
-      copy16_to_lds_nt(p.U + (static_cast<size_t>(b >> p.u_shift) * p.gamma + p.k) * p.V + v,
-                       base + D::kW2Bytes + 1024 * q);
+      if (i < ucopies_w) {   // wave-uniform
+        const int q = wave * uper + i;
+        const int slot = 64 * q + lane;
+        const int d = slot / D::kUChunks;               // U row within the stage
+        const int c = (slot % D::kUChunks) ^ (d & 15);
+        const int ub = min(u0 + d, (p.B - 1) >> ush);
+        const int v = min(tok0 + 4 * c, p.V - 4);
+        copy16_to_lds_nt(p.U + (static_cast<size_t>(ub) * p.gamma + p.k) * p.V + v,
+                         __builtin_amdgcn_readfirstlane(base + D::kW2Bytes + 1024 * q));
+      }
     }
   };
 
@@ -456,7 +470,7 @@ __device__ __forceinline__ void markov_step_dma(const StepArgs& p, StepMap mp, D
       }
     }
     issue(0);
-    wait_copies<D::kCopies>();                  // the embedding rows (item 0 may be in flight)
+    wait_item();                                // the embedding rows (item 0 may be in flight)
     asm volatile("s_barrier" ::: "memory");
     {
       const unsigned char* eb = stage + D::kStageBytes;
@@ -475,7 +489,7 @@ __device__ __forceinline__ void markov_step_dma(const StepArgs& p, StepMap mp, D
   for (int j = 0; j < n; ++j) {
     if (j + 1 < n) {
       issue(j + 1);
-      wait_copies<D::kCopies>();
+      wait_item();
     } else {
       wait_copies<0>();
     }
