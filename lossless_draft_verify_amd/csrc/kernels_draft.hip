@@ -429,18 +429,26 @@ __device__ __forceinline__ void markov_step_dma(const StepArgs& p, StepMap mp, D
     }
   };
 
-  // Partials of items j0 .. j1-1 (after a barrier), to global memory by the whole workgroup:
-  // consecutive threads take consecutive tiles of one request, so the stores fill whole lines.
+  // Partials of items j0 .. j1-1 (after a barrier), to global memory by the whole workgroup.
+  // Thread t takes tile slot t % kSlots (item j0 + slot / kDmaTiles) of the rows t / kSlots +
+  // kRowStep i: consecutive threads write consecutive tiles of one request (whole lines), and
+  // all of a thread's LDS reads go out before its stores.
   auto flush = [&](int j0, int j1) {
-    const int per = (j1 - j0) * kDmaTiles;
-    for (int x = tid; x < kDmaGroup * per; x += D::kThreads) {
-      const int row = x / per, tt = x % per;
-      const int j = j0 + tt / kDmaTiles;
-      const int b = group * kDmaGroup + row;
-      const int tile = (item_lo + j0) * kDmaTiles + tt;
-      if (b < p.B && tile < p.ntiles)
-        p.part[static_cast<size_t>(b) * p.ntiles + tile] =
-            pbuf[((j % D::kPartItems) * kDmaTiles + tt % kDmaTiles) * kDmaGroup + row];
+    constexpr int kSlots = D::kPartItems * kDmaTiles;
+    constexpr int kRowStep = D::kThreads / kSlots;
+    static_assert(D::kThreads % kSlots == 0 && kDmaGroup % kRowStep == 0, "flush mapping");
+    const int tt = tid % kSlots, r0 = tid / kSlots;
+    const int j = j0 + tt / kDmaTiles;
+    const int tile = (item_lo + j0) * kDmaTiles + tt;
+    const bool ok = tt < (j1 - j0) * kDmaTiles && tile < p.ntiles;
+    const float2* src = pbuf + ((j % D::kPartItems) * kDmaTiles + tt % kDmaTiles) * kDmaGroup;
+    float2 v[kDmaGroup / kRowStep];
+#pragma unroll
+    for (int i = 0; i < kDmaGroup / kRowStep; ++i) v[i] = src[r0 + kRowStep * i];
+#pragma unroll
+    for (int i = 0; i < kDmaGroup / kRowStep; ++i) {
+      const int b = group * kDmaGroup + r0 + kRowStep * i;
+      if (ok && b < p.B) p.part[static_cast<size_t>(b) * p.ntiles + tile] = v[i];
     }
   };
 
@@ -639,14 +647,21 @@ __device__ __forceinline__ void markov_step_deep4(const StepArgs& p, StepMap mp,
                        base + D::kW2Bytes + 1024 * q);
     }
   };
+  // Partials of items j0 .. j1-1 (one tile each), mapped as in the two-stage kernel's flush.
   auto flush = [&](int j0, int j1) {
-    const int per = j1 - j0;
-    for (int x = tid; x < kDmaGroup * per; x += D::kThreads) {
-      const int row = x / per, tt = x % per;
-      const int b = group * kDmaGroup + row;
-      if (b < p.B)
-        p.part[static_cast<size_t>(b) * p.ntiles + item_lo + j0 + tt] =
-            pbuf[((j0 + tt) % D::kPartItems) * kDmaGroup + row];
+    constexpr int kSlots = D::kPartItems;
+    constexpr int kRowStep = D::kThreads / kSlots;
+    static_assert(D::kThreads % kSlots == 0 && kDmaGroup % kRowStep == 0, "flush mapping");
+    const int tt = tid % kSlots, r0 = tid / kSlots;
+    const bool ok = tt < j1 - j0;
+    const float2* src = pbuf + ((j0 + tt) % D::kPartItems) * kDmaGroup;
+    float2 v[kDmaGroup / kRowStep];
+#pragma unroll
+    for (int i = 0; i < kDmaGroup / kRowStep; ++i) v[i] = src[r0 + kRowStep * i];
+#pragma unroll
+    for (int i = 0; i < kDmaGroup / kRowStep; ++i) {
+      const int b = group * kDmaGroup + r0 + kRowStep * i;
+      if (ok && b < p.B) p.part[static_cast<size_t>(b) * p.ntiles + item_lo + j0 + tt] = v[i];
     }
   };
 

@@ -546,20 +546,34 @@ __device__ __forceinline__ void residual_dma(const VerifyArgs& p) {
     }
   };
 
-  // Tile sums of items j0 .. j1-1 (after a barrier) to rsum / rmin: consecutive threads take
-  // consecutive tiles of one request.
+  // Tile sums of items j0 .. j1-1 (after a barrier) to rsum / rmin: thread t takes tile slot
+  // t % kSlots of the rows t / kSlots + kRowStep i, so consecutive threads write consecutive
+  // tiles of one request, and its LDS reads all go out before its stores.
   auto flush = [&](int j0, int j1) {
-    const int per = (j1 - j0) * kResTiles;
-    for (int x = tid; x < gcount * per; x += D::kThreads) {
-      const int row = x / per, tt = x % per;
-      const int j = j0 + tt / kResTiles;
-      const int tile = (item_lo + j0) * kResTiles + tt;
-      if (tile < p.ntiles) {
-        const int slot = ((j % D::kPartItems) * kResTiles + tt % kResTiles) * 2;
-        const double2 v0 = pbuf[slot * kResGroup + row], v1 = pbuf[(slot + 1) * kResGroup + row];
-        const size_t o = static_cast<size_t>(rec[row].b) * p.ntiles + tile;
-        p.ws.rsum[o] = v0.x + v1.x;
-        p.ws.rmin[o] = v0.y + v1.y;
+    constexpr int kSlots = D::kPartItems * kResTiles;
+    constexpr int kRowStep = D::kThreads / kSlots;
+    constexpr int kPasses = kResGroup / kRowStep;
+    static_assert(D::kThreads % kSlots == 0 && kResGroup % kRowStep == 0, "flush mapping");
+    const int tt = tid % kSlots, r0 = tid / kSlots;   // tile slot, first row
+    const int j = j0 + tt / kResTiles;
+    const int tile = (item_lo + j0) * kResTiles + tt;
+    const bool ok = tt < (j1 - j0) * kResTiles && tile < p.ntiles;
+    const int slot = ((j % D::kPartItems) * kResTiles + tt % kResTiles) * 2;
+    double2 v0[kPasses], v1[kPasses];
+    int rb[kPasses];
+#pragma unroll
+    for (int i = 0; i < kPasses; ++i) {
+      const int row = r0 + kRowStep * i;
+      v0[i] = pbuf[slot * kResGroup + row];
+      v1[i] = pbuf[(slot + 1) * kResGroup + row];
+      rb[i] = rec[row].b;
+    }
+#pragma unroll
+    for (int i = 0; i < kPasses; ++i) {
+      if (ok && r0 + kRowStep * i < gcount) {
+        const size_t o = static_cast<size_t>(rb[i]) * p.ntiles + tile;
+        p.ws.rsum[o] = v0[i].x + v1[i].x;
+        p.ws.rmin[o] = v0[i].y + v1[i].y;
       }
     }
   };
