@@ -49,7 +49,6 @@ bool plan_dims_ok(const dspark_dims& d) {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// Compute units of the current device (cached per device id).
 // Draft options: beta = fp32(1 / temperature) (1 for greedy or no options). False when the
 // temperature is not positive and finite.
 bool draft_options(const dspark_draft_opts* opts, float* beta, int* greedy) {
@@ -66,6 +65,7 @@ bool draft_options(const dspark_draft_opts* opts, float* beta, int* greedy) {
   return true;
 }
 
+// Compute units of the current device (cached per device id).
 int compute_units() {
   static int cached[64] = {0};
   int dev = 0;
@@ -128,8 +128,8 @@ size_t verify_ws(const dspark_dims& d, void* base, VerifyWs* out) {
   const size_t nseg = nseg_of(d.V), nt = ntiles_of(d.V), B = d.B;
   size_t off = 0;
   char* b = static_cast<char*>(base);
-  auto take = [&](size_t bytes) {
-    char* p = b + off;
+  auto take = [&](size_t bytes) {   // a null base only sizes the layout
+    char* p = b ? b + off : nullptr;
     off += align_up(bytes);
     return p;
   };
@@ -153,7 +153,7 @@ size_t verify_ws(const dspark_dims& d, void* base, VerifyWs* out) {
 // Verify of an RNN-head draft: the verify workspace, then the bias rows E [B gamma][3r] bf16.
 size_t rnn_verify_ws(const dspark_dims& d, void* base, VerifyWs* out, uint16_t** E) {
   const size_t off = verify_ws(d, base, out);
-  if (E) *E = reinterpret_cast<uint16_t*>(static_cast<char*>(base) + off);
+  if (E) *E = base ? reinterpret_cast<uint16_t*>(static_cast<char*>(base) + off) : nullptr;
   return off + align_up(static_cast<size_t>(d.B) * d.gamma * kRnnTerms * d.r * sizeof(uint16_t));
 }
 
