@@ -117,19 +117,22 @@ __global__ __launch_bounds__(kPreThreads) void rnn_pre_kernel(RnnPreArgs p) {
 
 // ---- rnn_state: one step of eq. (6) ----------------------------------------------------------
 //
-// Workgroup (block of 32 state indices j, block of 4 requests); its four waves split the 2r
+// Workgroup (block of 16 state indices j, block of 8 requests); its four waves split the 2r
 // columns of z's state and embedding blocks into quarters. Each wave first copies its quarter of
-// the 96 weight rows it needs (rows j, r + j, 2r + j: W_g, W_c, W_o) into its own LDS region by
+// the 48 weight rows it needs (rows j, r + j, 2r + j: W_g, W_c, W_o) into its own LDS region by
 // LDS-DMA loads, all in flight at once (swizzled in 16-byte pieces like the other staged
 // tiles); lane (j, request pair) then forms the six partial dot products with its two requests'
-// z in fp64 (z from LDS, read by 32 lanes at once: broadcasts). Each weight element is read from
-// L2 by 32 request blocks instead of 128 requests. The quarters are summed in fixed order in LDS
-// with the slices of P, then wave 0 applies the gates.
+// z in fp64 (z from LDS, read by 16 lanes at once: broadcasts). Each weight element is read from
+// L2 by 16 request blocks instead of 128 requests. Every quarter's sums go to LDS, and wave w
+// finishes request pair w: the quarters added in quarter order, then the slices of P, then the
+// gates.
 constexpr int kStateThreads = 256;
-constexpr int kStateJ = 32;
-constexpr int kStateB = 4;
-constexpr int kStateRows = 3 * kStateJ;                       // 96 weight rows per workgroup
-constexpr int kStateWaveBytes = kStateRows * (2 * 256 / 4) * 2;   // a quarter at r = 256: 24 KB
+constexpr int kStateJ = 16;
+constexpr int kStateB = 8;
+static_assert(kStateJ * kStateB / 2 == 64 && kStateB / 2 == kStateThreads / 64,
+              "a lane per (state index, request pair); a wave per request pair in the tail");
+constexpr int kStateRows = 3 * kStateJ;                       // 48 weight rows per workgroup
+constexpr int kStateWaveBytes = kStateRows * (2 * 256 / 4) * 2;   // a quarter at r = 256: 12 KB
 
 __device__ __forceinline__ double bf16_to_f64(uint16_t v) {
   return static_cast<double>(__uint_as_float(static_cast<uint32_t>(v) << 16));
@@ -178,7 +181,7 @@ __device__ __forceinline__ void split_terms_operand(float e, uint16_t* E2, int b
 
 __global__ __launch_bounds__(kStateThreads) void rnn_state_kernel(RnnStateArgs p) {
   extern __shared__ double zs[];                    // [kStateB][2r]: s_{k-1} | W1[x_{k-1}]
-  __shared__ double part[3][6][64];                 // quarters 1..3: (row, request) x lane
+  __shared__ double part[4][6][64];                 // every quarter's sums: (row, pair) x lane
   __shared__ __attribute__((aligned(1024))) unsigned char wst[4 * kStateWaveBytes];
   const int tid = threadIdx.x, lane = tid & 63;
   const int quarter = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -188,8 +191,28 @@ __global__ __launch_bounds__(kStateThreads) void rnn_state_kernel(RnnStateArgs p
   const int q = (2 * r) / 4, i0 = quarter * q;       // 2r is a multiple of 32
   const int cpr = q / 8;                             // 16-byte pieces per row: 1, 2, 4, 8 or 16
   const int swz = cpr - 1;
-  // This wave's weight rows (t < 96: block t / 32 of W_g, W_c, W_o, state index t % 32) into
-  // its LDS region, all copies in flight at once.
+  // The previous tokens of the values this thread stages first, straight from memory (no
+  // barrier), then their z loads; the weight copies (this wave's quarter of the rows) and the
+  // tail's pre-GEMM terms go out behind them, so the copies overlap the token round trip's
+  // successor instead of delaying it.
+  constexpr int kZPer = kStateB * 2 * 256 / kStateThreads;
+  int32_t xt[kZPer];
+#pragma unroll
+  for (int u = 0; u < kZPer; ++u) {
+    const int i = tid + u * kStateThreads;
+    const int rb = min(i / (2 * r), kStateB - 1);
+    xt[u] = clamp_token(p.prev[static_cast<size_t>(min(b0 + rb, p.B - 1)) * p.prev_stride], p.V);
+  }
+  double zv[kZPer];
+#pragma unroll
+  for (int u = 0; u < kZPer; ++u) {
+    const int i = tid + u * kStateThreads;
+    const int rb = min(i / (2 * r), kStateB - 1), c = i % (2 * r);
+    const int b = min(b0 + rb, p.B - 1);
+    const double sv = (p.s_in && c < r) ? p.s_in[static_cast<size_t>(b) * r + c] : 0.0;
+    const double ev = bf16_to_f64(p.W1[static_cast<size_t>(xt[u]) * r + (c < r ? 0 : c - r)]);
+    zv[u] = (c < r) ? sv : ev;
+  }
   const uint32_t wbase = lds_addr(wst) + quarter * kStateWaveBytes;
   const int npieces = kStateRows * cpr;
   for (int t = 0; t * 64 < npieces; ++t) {
@@ -202,43 +225,23 @@ __global__ __launch_bounds__(kStateThreads) void rnn_state_kernel(RnnStateArgs p
                     wbase + 1024 * t);
     }
   }
-  // Wave 0's pre-GEMM terms of its (state index, request) pairs, loaded now so that their latency
-  // passes during the dot products (index clamped into the tensor; pairs past B or r unused).
-  const int jl = lane & 31, rp = lane >> 5;          // state index, request pair
-  const int j = j0 + jl;
+  // Tail of wave w: request pair w, lanes 0 .. 2 kStateJ - 1 = (request 2w + th, state index
+  // j0 + tjl); its pre-GEMM terms (index clamped; pairs past B or r unused).
+  const int th = (lane / kStateJ) & 1, tjl = lane % kStateJ;
+  const int tj = j0 + tjl, tb = b0 + 2 * quarter + th;
   const int N = 3 * r;
   const size_t M = static_cast<size_t>(p.B) * p.gamma;
-  float pv[2][kRnnPreSplits][3];
-  if (quarter == 0) {
+  float pv[kRnnPreSplits][3];
+  {
+    const size_t m = static_cast<size_t>(min(tb, p.B - 1)) * p.gamma + p.k;
+    const int jc = min(tj, r - 1);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const size_t m = static_cast<size_t>(min(b0 + 2 * rp + h, p.B - 1)) * p.gamma + p.k;
-      const int jc = min(j, r - 1);
-#pragma unroll
-      for (int sp = 0; sp < kRnnPreSplits; ++sp) {
-        const float* P = p.P + (sp * M + m) * N;
-        pv[h][sp][0] = P[jc];
-        pv[h][sp][1] = P[r + jc];
-        pv[h][sp][2] = P[2 * r + jc];
-      }
+    for (int sp = 0; sp < kRnnPreSplits; ++sp) {
+      const float* P = p.P + (sp * M + m) * N;
+      pv[sp][0] = P[jc];
+      pv[sp][1] = P[r + jc];
+      pv[sp][2] = P[2 * r + jc];
     }
-  }
-  // z of the block's requests: their previous tokens first, then every value's load in flight
-  // at once (at most kStateB * 2 * 256 / kStateThreads = 8 per thread) before the LDS stores.
-  __shared__ int32_t xs[kStateB];
-  if (tid < kStateB)
-    xs[tid] = clamp_token(p.prev[static_cast<size_t>(min(b0 + tid, p.B - 1)) * p.prev_stride], p.V);
-  __syncthreads();
-  constexpr int kZPer = kStateB * 2 * 256 / kStateThreads;
-  double zv[kZPer];
-#pragma unroll
-  for (int u = 0; u < kZPer; ++u) {
-    const int i = tid + u * kStateThreads;
-    const int rb = min(i / (2 * r), kStateB - 1), c = i % (2 * r);
-    const int b = min(b0 + rb, p.B - 1);
-    const double sv = (p.s_in && c < r) ? p.s_in[static_cast<size_t>(b) * r + c] : 0.0;
-    const double ev = bf16_to_f64(p.W1[static_cast<size_t>(xs[rb]) * r + (c < r ? 0 : c - r)]);
-    zv[u] = (c < r) ? sv : ev;
   }
 #pragma unroll
   for (int u = 0; u < kZPer; ++u) {
@@ -247,6 +250,9 @@ __global__ __launch_bounds__(kStateThreads) void rnn_state_kernel(RnnStateArgs p
   }
   wait_copies<0>();
   __syncthreads();
+  // Dot products: lane (state index j0 + jl, request pair rp) over this quarter's inputs, for
+  // the three gate rows and both requests of the pair.
+  const int jl = lane % kStateJ, rp = lane / kStateJ;
   const unsigned char* wl = wst + quarter * kStateWaveBytes;
   const double* z0 = zs + (2 * rp) * (2 * r) + i0;
   const double* z1 = z0 + 2 * r;
@@ -271,37 +277,32 @@ __global__ __launch_bounds__(kStateThreads) void rnn_state_kernel(RnnStateArgs p
       acc[5] = fma(o, zb, acc[5]);
     }
   }
-  if (quarter > 0) {
 #pragma unroll
-    for (int t = 0; t < 6; ++t) part[quarter - 1][t][lane] = acc[t];
-  }
+  for (int t = 0; t < 6; ++t) part[quarter][t][lane] = acc[t];
   __syncthreads();
-  if (quarter != 0 || j >= r) return;
+  if (lane >= 2 * kStateJ || tj >= r || tb >= p.B) return;
+  const int src = quarter * kStateJ + tjl;           // lane (tjl, pair `quarter`) above
+  double ag = part[0][3 * th][src], ac = part[0][3 * th + 1][src], ao = part[0][3 * th + 2][src];
 #pragma unroll
-  for (int w = 0; w < 3; ++w) {
-#pragma unroll
-    for (int t = 0; t < 6; ++t) acc[t] += part[w][t][lane];
+  for (int w = 1; w < 4; ++w) {
+    ag += part[w][3 * th][src];
+    ac += part[w][3 * th + 1][src];
+    ao += part[w][3 * th + 2][src];
   }
+  const size_t m = static_cast<size_t>(tb) * p.gamma + p.k;
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int b = b0 + 2 * rp + h;
-    if (b >= p.B) continue;
-    const size_t m = static_cast<size_t>(b) * p.gamma + p.k;
-    double ag = acc[3 * h], ac = acc[3 * h + 1], ao = acc[3 * h + 2];
-#pragma unroll
-    for (int sp = 0; sp < kRnnPreSplits; ++sp) {
-      ag += static_cast<double>(pv[h][sp][0]);
-      ac += static_cast<double>(pv[h][sp][1]);
-      ao += static_cast<double>(pv[h][sp][2]);
-    }
-    const double gate = 1.0 / (1.0 + exp(-ag));
-    const double s_prev = zs[(2 * rp + h) * (2 * r) + j];
-    p.s_out[static_cast<size_t>(b) * r + j] = gate * s_prev + (1.0 - gate) * tanh(ac);
-    const float e = static_cast<float>(tanh(ao));
-    p.e_out[m * r + j] = e;
-    split_terms(e, p.E + m * (kRnnTerms * r) + j, r);
-    if (p.E2) split_terms_operand(e, p.E2, b, p.k, p.gamma, j, r);
+  for (int sp = 0; sp < kRnnPreSplits; ++sp) {
+    ag += static_cast<double>(pv[sp][0]);
+    ac += static_cast<double>(pv[sp][1]);
+    ao += static_cast<double>(pv[sp][2]);
   }
+  const double gate = 1.0 / (1.0 + exp(-ag));
+  const double s_prev = zs[(2 * quarter + th) * (2 * r) + tj];
+  p.s_out[static_cast<size_t>(tb) * r + tj] = gate * s_prev + (1.0 - gate) * tanh(ac);
+  const float e = static_cast<float>(tanh(ao));
+  p.e_out[m * r + tj] = e;
+  split_terms(e, p.E + m * (kRnnTerms * r) + tj, r);
+  if (p.E2) split_terms_operand(e, p.E2, tb, p.k, p.gamma, tj, r);
 }
 
 __global__ __launch_bounds__(256) void split_bias_kernel(SplitArgs p) {
