@@ -117,22 +117,24 @@ __global__ __launch_bounds__(kPreThreads) void rnn_pre_kernel(RnnPreArgs p) {
 
 // ---- rnn_state: one step of eq. (6) ----------------------------------------------------------
 //
-// Workgroup (block of 16 state indices j, block of 8 requests); its four waves split the 2r
-// columns of z's state and embedding blocks into quarters. Each wave first copies its quarter of
-// the 48 weight rows it needs (rows j, r + j, 2r + j: W_g, W_c, W_o) into its own LDS region by
-// LDS-DMA loads, all in flight at once (swizzled in 16-byte pieces like the other staged
-// tiles); lane (j, request pair) then forms the six partial dot products with its two requests'
-// z in fp64 (z from LDS, read by 16 lanes at once: broadcasts). Each weight element is read from
-// L2 by 16 request blocks instead of 128 requests. Every quarter's sums go to LDS, and wave w
-// finishes request pair w: the quarters added in quarter order, then the slices of P, then the
-// gates.
-constexpr int kStateThreads = 256;
+// Workgroup (block of 16 state indices j, block of 8 requests), eight waves (two per SIMD, so
+// that one's fp64 multiply-adds cover the other's latencies); the waves split the 2r columns of
+// z's state and embedding blocks into eight slices (four at r = 16, the other four waves then
+// add nothing). Each wave first copies its slice of the 48 weight rows it needs (rows j, r + j,
+// 2r + j: W_g, W_c, W_o) into its own LDS region by LDS-DMA loads, all in flight at once
+// (swizzled in 16-byte pieces like the other staged tiles); lane (j, request pair) then forms
+// the six partial dot products with its two requests' z in fp64 (z from LDS, read by 16 lanes at
+// once: broadcasts). Each weight element is read from L2 by 16 request blocks instead of 128
+// requests. Every slice's sums go to LDS, and wave w finishes request w: the slices added in
+// slice order, then the slices of P, then the gates.
+constexpr int kStateThreads = 512;
+constexpr int kStateWaves = kStateThreads / 64;
 constexpr int kStateJ = 16;
 constexpr int kStateB = 8;
-static_assert(kStateJ * kStateB / 2 == 64 && kStateB / 2 == kStateThreads / 64,
-              "a lane per (state index, request pair); a wave per request pair in the tail");
-constexpr int kStateRows = 3 * kStateJ;                       // 48 weight rows per workgroup
-constexpr int kStateWaveBytes = kStateRows * (2 * 256 / 4) * 2;   // a quarter at r = 256: 12 KB
+static_assert(kStateJ * kStateB / 2 == 64 && kStateB == kStateWaves,
+              "a lane per (state index, request pair); a wave per request in the tail");
+constexpr int kStateRows = 3 * kStateJ;                              // 48 weight rows
+constexpr int kStateSliceBytes = kStateRows * (2 * 256 / kStateWaves) * 2;   // r = 256: 6 KB
 
 __device__ __forceinline__ double bf16_to_f64(uint16_t v) {
   return static_cast<double>(__uint_as_float(static_cast<uint32_t>(v) << 16));
@@ -181,20 +183,21 @@ __device__ __forceinline__ void split_terms_operand(float e, uint16_t* E2, int b
 
 __global__ __launch_bounds__(kStateThreads) void rnn_state_kernel(RnnStateArgs p) {
   extern __shared__ double zs[];                    // [kStateB][2r]: s_{k-1} | W1[x_{k-1}]
-  __shared__ double part[4][6][64];                 // every quarter's sums: (row, pair) x lane
-  __shared__ __attribute__((aligned(1024))) unsigned char wst[4 * kStateWaveBytes];
+  __shared__ double part[kStateWaves][6][64];       // every slice's sums: (row, pair) x lane
+  __shared__ __attribute__((aligned(1024))) unsigned char wst[kStateWaves * kStateSliceBytes];
   const int tid = threadIdx.x, lane = tid & 63;
-  const int quarter = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = p.r, nz = 2 * r + p.d;
   const int nj = (r + kStateJ - 1) / kStateJ;
   const int j0 = (blockIdx.x % nj) * kStateJ, b0 = (blockIdx.x / nj) * kStateB;
-  const int q = (2 * r) / 4, i0 = quarter * q;       // 2r is a multiple of 32
-  const int cpr = q / 8;                             // 16-byte pieces per row: 1, 2, 4, 8 or 16
+  const int ns = (2 * r >= 8 * kStateWaves) ? kStateWaves : 4;   // input slices (r = 16: four)
+  const bool active = wave < ns;
+  const int q = (2 * r) / ns, i0 = wave * q;         // q: a multiple of 8 inputs
+  const int cpr = q / 8;                             // 16-byte pieces per row: 1, 2, 4 or 8
   const int swz = cpr - 1;
   // The previous tokens of the values this thread stages first, straight from memory (no
-  // barrier), then their z loads; the weight copies (this wave's quarter of the rows) and the
-  // tail's pre-GEMM terms go out behind them, so the copies overlap the token round trip's
-  // successor instead of delaying it.
+  // barrier), then their z loads; the weight copies (this wave's slice of the rows) and the
+  // tail's pre-GEMM terms go out behind them.
   constexpr int kZPer = kStateB * 2 * 256 / kStateThreads;
   int32_t xt[kZPer];
 #pragma unroll
@@ -213,22 +216,24 @@ __global__ __launch_bounds__(kStateThreads) void rnn_state_kernel(RnnStateArgs p
     const double ev = bf16_to_f64(p.W1[static_cast<size_t>(xt[u]) * r + (c < r ? 0 : c - r)]);
     zv[u] = (c < r) ? sv : ev;
   }
-  const uint32_t wbase = lds_addr(wst) + quarter * kStateWaveBytes;
-  const int npieces = kStateRows * cpr;
-  for (int t = 0; t * 64 < npieces; ++t) {
-    const int slot = 64 * t + lane;
-    if (slot < npieces) {
-      const int row = slot / cpr;
-      const int piece = (slot % cpr) ^ (row & swz);
-      const int jr = min(j0 + row % kStateJ, r - 1);
-      copy16_to_lds(p.Wgco + static_cast<size_t>((row / kStateJ) * r + jr) * nz + i0 + 8 * piece,
-                    wbase + 1024 * t);
+  if (active) {
+    const uint32_t wbase = lds_addr(wst) + wave * kStateSliceBytes;
+    const int npieces = kStateRows * cpr;
+    for (int t = 0; t * 64 < npieces; ++t) {
+      const int slot = 64 * t + lane;
+      if (slot < npieces) {
+        const int row = slot / cpr;
+        const int piece = (slot % cpr) ^ (row & swz);
+        const int jr = min(j0 + row % kStateJ, r - 1);
+        copy16_to_lds(
+            p.Wgco + static_cast<size_t>((row / kStateJ) * r + jr) * nz + i0 + 8 * piece,
+            wbase + 1024 * t);
+      }
     }
   }
-  // Tail of wave w: request pair w, lanes 0 .. 2 kStateJ - 1 = (request 2w + th, state index
-  // j0 + tjl); its pre-GEMM terms (index clamped; pairs past B or r unused).
-  const int th = (lane / kStateJ) & 1, tjl = lane % kStateJ;
-  const int tj = j0 + tjl, tb = b0 + 2 * quarter + th;
+  // Tail of wave w: request b0 + w, lanes 0 .. kStateJ - 1 = state index j0 + lane; its
+  // pre-GEMM terms (index clamped; pairs past B or r unused).
+  const int tj = j0 + lane % kStateJ, tb = b0 + wave;
   const int N = 3 * r;
   const size_t M = static_cast<size_t>(p.B) * p.gamma;
   float pv[kRnnPreSplits][3];
@@ -250,41 +255,45 @@ __global__ __launch_bounds__(kStateThreads) void rnn_state_kernel(RnnStateArgs p
   }
   wait_copies<0>();
   __syncthreads();
-  // Dot products: lane (state index j0 + jl, request pair rp) over this quarter's inputs, for
-  // the three gate rows and both requests of the pair.
+  // Dot products: lane (state index j0 + jl, request pair rp) over this wave's inputs, for the
+  // three gate rows and both requests of the pair.
   const int jl = lane % kStateJ, rp = lane / kStateJ;
-  const unsigned char* wl = wst + quarter * kStateWaveBytes;
-  const double* z0 = zs + (2 * rp) * (2 * r) + i0;
-  const double* z1 = z0 + 2 * r;
   double acc[6] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0};   // (g, c, o) x (request 2rp, 2rp + 1)
-  for (int pc = 0; pc < cpr; ++pc) {
-    u16x8_t w3[3];
+  if (active) {
+    const unsigned char* wl = wst + wave * kStateSliceBytes;
+    const double* z0 = zs + (2 * rp) * (2 * r) + i0;
+    const double* z1 = z0 + 2 * r;
+    for (int pc = 0; pc < cpr; ++pc) {
+      u16x8_t w3[3];
 #pragma unroll
-    for (int m3 = 0; m3 < 3; ++m3) {
-      const int row = m3 * kStateJ + jl;
-      w3[m3] = *reinterpret_cast<const u16x8_t*>(wl + 16 * (row * cpr + (pc ^ (row & swz))));
-    }
+      for (int m3 = 0; m3 < 3; ++m3) {
+        const int row = m3 * kStateJ + jl;
+        w3[m3] = *reinterpret_cast<const u16x8_t*>(wl + 16 * (row * cpr + (pc ^ (row & swz))));
+      }
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const double za = z0[8 * pc + t], zb = z1[8 * pc + t];
-      const double g = bf16_to_f64(w3[0][t]), c = bf16_to_f64(w3[1][t]), o = bf16_to_f64(w3[2][t]);
-      // explicit fused multiply-adds (the build does not contract): one rounding per term
-      acc[0] = fma(g, za, acc[0]);
-      acc[1] = fma(c, za, acc[1]);
-      acc[2] = fma(o, za, acc[2]);
-      acc[3] = fma(g, zb, acc[3]);
-      acc[4] = fma(c, zb, acc[4]);
-      acc[5] = fma(o, zb, acc[5]);
+      for (int t = 0; t < 8; ++t) {
+        const double za = z0[8 * pc + t], zb = z1[8 * pc + t];
+        const double g = bf16_to_f64(w3[0][t]), c = bf16_to_f64(w3[1][t]),
+                     o = bf16_to_f64(w3[2][t]);
+        // explicit fused multiply-adds (the build does not contract): one rounding per term
+        acc[0] = fma(g, za, acc[0]);
+        acc[1] = fma(c, za, acc[1]);
+        acc[2] = fma(o, za, acc[2]);
+        acc[3] = fma(g, zb, acc[3]);
+        acc[4] = fma(c, zb, acc[4]);
+        acc[5] = fma(o, zb, acc[5]);
+      }
     }
   }
 #pragma unroll
-  for (int t = 0; t < 6; ++t) part[quarter][t][lane] = acc[t];
+  for (int t = 0; t < 6; ++t) part[wave][t][lane] = acc[t];
   __syncthreads();
-  if (lane >= 2 * kStateJ || tj >= r || tb >= p.B) return;
-  const int src = quarter * kStateJ + tjl;           // lane (tjl, pair `quarter`) above
+  if (lane >= kStateJ || tj >= r || tb >= p.B) return;
+  const int th = wave & 1;
+  const int src = (wave >> 1) * kStateJ + lane;      // lane (state index, pair wave / 2) above
   double ag = part[0][3 * th][src], ac = part[0][3 * th + 1][src], ao = part[0][3 * th + 2][src];
 #pragma unroll
-  for (int w = 1; w < 4; ++w) {
+  for (int w = 1; w < kStateWaves; ++w) {
     ag += part[w][3 * th][src];
     ac += part[w][3 * th + 1][src];
     ao += part[w][3 * th + 2][src];
@@ -297,7 +306,7 @@ __global__ __launch_bounds__(kStateThreads) void rnn_state_kernel(RnnStateArgs p
     ao += static_cast<double>(pv[sp][2]);
   }
   const double gate = 1.0 / (1.0 + exp(-ag));
-  const double s_prev = zs[(2 * quarter + th) * (2 * r) + tj];
+  const double s_prev = zs[wave * (2 * r) + tj];
   p.s_out[static_cast<size_t>(tb) * r + tj] = gate * s_prev + (1.0 - gate) * tanh(ac);
   const float e = static_cast<float>(tanh(ao));
   p.e_out[m * r + tj] = e;
