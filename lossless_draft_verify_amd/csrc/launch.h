@@ -182,7 +182,7 @@ struct TreeWalkArgs {
 // RNN head, eq. (6). P [kRnnPreSplits][M][3r] = the hidden-state block of Wgco applied to every
 // h_k (M = B gamma rows (b, k)), one part per slice of the hidden dimension (summed in fp64,
 // stored as fp32); computed once per round, off the serial chain.
-constexpr int kRnnPreSplits = 8;
+constexpr int kRnnPreSplits = 4;
 struct RnnPreArgs {
   int M, r, d;
   const uint16_t* h;      // [M][d] bf16
