@@ -236,7 +236,6 @@ enum KernelId {
   kEmitSample,
   kRnnPre,
   kRnnState,
-  kSplitBias,
   kTreeSelect,
   kTreeWalk,
   kNumKernels
@@ -244,7 +243,7 @@ enum KernelId {
 const char* const kKernelNames[kNumKernels] = {"markov_step",  "draft_sample", "confidence",
                                                "plan",         "target_stats", "accept",
                                                "residual_partials", "emit_sample",
-                                               "rnn_pre",      "rnn_state",    "split_bias",
+                                               "rnn_pre",      "rnn_state",
                                                "tree_select",  "tree_walk"};
 
 struct Profiler {
@@ -838,11 +837,9 @@ dspark_status dspark_rnn_verify(dspark_dims dims, const float* target, const int
   rnn_verify_ws(dims, ws, &a.ws, &E);
   a.e_terms = kRnnTerms;
   a.E = E;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  SplitArgs sp{dims.B * dims.gamma, dims.r, e_rows, E};
-  if (timed(kSplitBias, s, [&] { return launch_split_bias(sp, s); }) != hipSuccess)
-    return DSPARK_ERR_HIP;
-  return verify_passes(dims, a, s);
+  a.e_split = e_rows;   // the target pass splits the bias vectors into E
+  a.E_split = E;
+  return verify_passes(dims, a, static_cast<hipStream_t>(stream));
 }
 
 dspark_status dspark_verify(dspark_dims dims, const float* target, const int32_t* row_offsets,

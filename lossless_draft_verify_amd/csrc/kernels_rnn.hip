@@ -6,7 +6,7 @@
 // with s_0 = 0 at the start of every block, the state of size r, no bias terms, and W_g, W_c,
 // W_o stacked by rows into Wgco [3r][2r + d] whose columns follow z (state | embedding | hidden).
 //
-// Three kernels:
+// Two kernels (the verify's target pass splits given bias vectors into the same terms):
 //   rnn_pre     the hidden-state block of Wgco applied to every h_k of the round (one bf16 MFMA
 //               GEMM, B gamma x d x 3r, off the serial chain): P[slice][B gamma][3r], the sums
 //               over kRnnPreSplits slices of the hidden dimension (fp64 sums stored as fp32).
@@ -14,7 +14,6 @@
 //               in fp64, the gates, s_k, and e_k = tanh(a_o), written as fp32 and as three bf16
 //               terms (t1 = RN(e), t2 = RN(e - t1), t3 = RN(e - t1 - t2)) that the bias
 //               contraction of the draft step consumes (their sum is the fp32 e).
-//   split_bias  the same split of given fp32 vectors (the verify of an RNN draft).
 #include <hip/hip_runtime.h>
 
 #include "device.h"
@@ -138,29 +137,6 @@ constexpr int kStateSliceBytes = kStateRows * (2 * 256 / kStateWaves) * 2;   // 
 
 __device__ __forceinline__ double bf16_to_f64(uint16_t v) {
   return static_cast<double>(__uint_as_float(static_cast<uint32_t>(v) << 16));
-}
-
-__device__ __forceinline__ uint16_t bf16_rne(float x) {
-  const uint32_t u = __float_as_uint(x);
-  return static_cast<uint16_t>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);   // x finite
-}
-
-__device__ __forceinline__ float bf16_value(uint16_t v) {
-  return __uint_as_float(static_cast<uint32_t>(v) << 16);
-}
-
-// The bf16 terms of a bias component, written to row[0], row[r], row[2r]: t1 = RN(e),
-// t2 = RN(e - t1), t3 = RN(e - t1 - t2). Each difference is exact in fp32 (every term takes the
-// leading 8 bits of what remains), so t1 + t2 + t3 = e for every finite fp32 e in (-1, 1).
-__device__ __forceinline__ void split_terms(float e, uint16_t* row, int r) {
-  static_assert(kRnnTerms == 3, "three terms");
-  const uint16_t t1 = bf16_rne(e);
-  const float rest1 = e - bf16_value(t1);
-  const uint16_t t2 = bf16_rne(rest1);
-  const float rest2 = rest1 - bf16_value(t2);
-  row[0] = t1;
-  row[r] = t2;
-  row[2 * r] = bf16_rne(rest2);
 }
 
 // The terms of component j of request b's bias vector at position k, also in the MFMA operand
@@ -314,14 +290,6 @@ __global__ __launch_bounds__(kStateThreads) void rnn_state_kernel(RnnStateArgs p
   if (p.E2) split_terms_operand(e, p.E2, tb, p.k, p.gamma, tj, r);
 }
 
-__global__ __launch_bounds__(256) void split_bias_kernel(SplitArgs p) {
-  const size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
-  const size_t n = static_cast<size_t>(p.n) * p.r;
-  if (i >= n) return;
-  const size_t m = i / p.r, j = i % p.r;
-  split_terms(p.e[i], p.E + m * (kRnnTerms * p.r) + j, p.r);
-}
-
 }  // namespace
 
 hipError_t launch_rnn_pre(const RnnPreArgs& a, hipStream_t s) {
@@ -338,12 +306,5 @@ hipError_t launch_rnn_state(const RnnStateArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_split_bias(const SplitArgs& a, hipStream_t s) {
-  const size_t n = static_cast<size_t>(a.n) * a.r;
-  if (n == 0) return hipSuccess;
-  launch_kernel(split_bias_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0,
-                     s, a);
-  return hipGetLastError();
-}
 
 }  // namespace dspark

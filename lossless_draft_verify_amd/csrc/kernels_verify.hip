@@ -62,12 +62,21 @@ __global__ __launch_bounds__(kBlock) void target_stats_kernel(VerifyArgs p) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   if (blockIdx.x == 0 && threadIdx.x == 0) *p.ws.rcount = 0;   // residual list (for accept)
   const int nitems = (p.dense_rows > 0 ? p.dense_rows : p.row_offsets[p.B]) * p.nseg;
+  // The RNN head's bias terms for the later passes (a grid-strided share per thread): the first
+  // value goes out with the row count, and the split runs while the first segment is loading.
+  const int nsplit = p.e_split ? p.B * p.gamma * p.r : 0;
+  const int i0 = blockIdx.x * kBlock + threadIdx.x;
+  const float e0 = (i0 < nsplit) ? p.e_split[i0] : 0.0f;
   const bool vec4 = (p.V & 3) == 0;
   int it = blockIdx.x;
-  if (it >= nitems) return;
   float x[16], y[16];
-  load_segment(p.target + static_cast<size_t>(it / p.nseg) * p.V, (it % p.nseg) * kSegTokens, p.V,
-               vec4, x);
+  if (it < nitems)
+    load_segment(p.target + static_cast<size_t>(it / p.nseg) * p.V, (it % p.nseg) * kSegTokens,
+                 p.V, vec4, x);
+  for (int i = i0; i < nsplit; i += gridDim.x * kBlock)
+    split_terms(i == i0 ? e0 : p.e_split[i],
+                p.E_split + static_cast<size_t>(i / p.r) * (kRnnTerms * p.r) + i % p.r, p.r);
+  if (it >= nitems) return;
   for (; it < nitems; it += gridDim.x) {
     const int nxt = it + gridDim.x;
     if (nxt < nitems)

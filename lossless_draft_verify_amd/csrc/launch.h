@@ -127,6 +127,10 @@ struct VerifyArgs {
   int e_terms = 1;               // bias rows as in StepArgs (3: E [B][gamma][3r], in ws)
   const uint16_t* E = nullptr;
   int dense_rows = 0;            // > 0: the target pass takes this many rows (no row_offsets)
+  // Nullable: fp32 bias vectors e [B gamma][r] whose bf16 terms the target pass writes to
+  // E_split [B gamma][3r] (the E above) before the passes that read them.
+  const float* e_split = nullptr;
+  uint16_t* E_split = nullptr;
 };
 
 // PCTree ([ZDS] "后续工作"). Candidates of a request are numbered depth by depth, and within a
@@ -208,13 +212,6 @@ struct RnnStateArgs {
   int V;                  // token ids are clamped into [0, V)
 };
 
-// The bf16 terms of given fp32 bias vectors (the verify of an RNN-head draft): E [n][3r] from
-// e [n][r], the same split the state step writes.
-struct SplitArgs {
-  int n, r;
-  const float* e;
-  uint16_t* E;
-};
 
 // Kernel timing: the event pair the next launch records with its dispatch (hipExtLaunchKernel
 // start and stop events, taken by the command processor around the kernel itself), or none.
@@ -252,7 +249,6 @@ hipError_t launch_residual_partials(const VerifyArgs& a, hipStream_t s);
 hipError_t launch_emit_sample(const VerifyArgs& a, hipStream_t s);
 hipError_t launch_rnn_pre(const RnnPreArgs& a, hipStream_t s);
 hipError_t launch_rnn_state(const RnnStateArgs& a, hipStream_t s);
-hipError_t launch_split_bias(const SplitArgs& a, hipStream_t s);
 hipError_t launch_tree_select(const TreeSelectArgs& a, int r, hipStream_t s);
 hipError_t launch_tree_walk(const TreeWalkArgs& a, hipStream_t s);
 

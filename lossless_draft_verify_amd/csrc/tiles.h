@@ -89,6 +89,29 @@ __device__ __forceinline__ const uint16_t* bias_row(const uint16_t* W1, const ui
   }
 }
 
+__device__ __forceinline__ uint16_t bf16_rne(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return static_cast<uint16_t>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);   // x finite
+}
+
+__device__ __forceinline__ float bf16_value(uint16_t v) {
+  return __uint_as_float(static_cast<uint32_t>(v) << 16);
+}
+
+// The bf16 terms of a bias component, written to row[0], row[r], row[2r]: t1 = RN(e),
+// t2 = RN(e - t1), t3 = RN(e - t1 - t2). Each difference is exact in fp32 (every term takes the
+// leading 8 bits of what remains), so t1 + t2 + t3 = e for every finite fp32 e in (-1, 1).
+__device__ __forceinline__ void split_terms(float e, uint16_t* row, int r) {
+  static_assert(kRnnTerms == 3, "three terms");
+  const uint16_t t1 = bf16_rne(e);
+  const float rest1 = e - bf16_value(t1);
+  const uint16_t t2 = bf16_rne(rest1);
+  const float rest2 = rest1 - bf16_value(t2);
+  row[0] = t1;
+  row[r] = t2;
+  row[2 * r] = bf16_rne(rest2);
+}
+
 // Recompute the logits of one 32-token tile for one request with exactly the instruction
 // sequence of the streaming draft step (same k order: the NT terms in turn, each over the r
 // columns; same operands; the request sits in every MFMA column, and column placement does not
