@@ -353,7 +353,7 @@ __device__ __forceinline__ StepMap step_map(int B, int h, int nblk_hw, int first
 }
 
 // The pipelined step as run by the workgroup that step_map placed at (group, wg of nwg).
-template <int KS, int NT>
+template <int KS, int NT, bool kUShared = false>
 __device__ __forceinline__ void markov_step_dma(const StepArgs& p, StepMap mp, DmaLds<KS>& lds) {
   using D = DmaStep<KS>;
   unsigned char* stage = lds.stage;
@@ -371,15 +371,19 @@ __device__ __forceinline__ void markov_step_dma(const StepArgs& p, StepMap mp, D
   if (n <= 0) return;
   const int row_own = 32 * rq + col;                    // request row within the group
   const bool wave_active = group * kDmaGroup + 32 * rq < p.B;
-  // Rows that read one U row (u_shift > 0: the expanded nodes of one request) share one copy of
-  // it: the stage holds the group's nd = kDmaGroup >> u_shift distinct U rows, four to a 1 KB
-  // copy, and the copies are spread over the waves (ucopies_w of them per item on this wave).
-  const int ush = p.u_shift;
+  // kUShared (u_shift > 0: the expanded nodes of one request read one U row): the rows that
+  // share a U row share one copy of it; the stage holds the group's nd = kDmaGroup >> u_shift
+  // distinct U rows, four to a 1 KB copy, and the copies are spread over the waves (ucopies_w of
+  // them per item on this wave). Otherwise every row has its own U row, kUCopies per wave.
+  const int ush = kUShared ? p.u_shift : 0;
   const int u0 = (group * kDmaGroup) >> ush;            // the group's first U row
   const int nd = max(1, kDmaGroup >> ush);
   const int ucopies = max(1, nd * D::kUChunks * 16 / 1024);
-  const int uper = __builtin_amdgcn_readfirstlane(max(1, ucopies / D::kWaves));
-  const int ucopies_w = __builtin_amdgcn_readfirstlane(max(0, min(uper, ucopies - wave * uper)));
+  const int uper =
+      kUShared ? __builtin_amdgcn_readfirstlane(max(1, ucopies / D::kWaves)) : D::kUCopies;
+  const int ucopies_w =
+      kUShared ? __builtin_amdgcn_readfirstlane(max(0, min(uper, ucopies - wave * uper)))
+               : D::kUCopies;
   const int urow_own = ((group * kDmaGroup + row_own) >> ush) - u0;   // lane's U row in the stage
 
   // Per-lane LDS offsets: k-step s of the A operand (W2t row 32 sub + col, chunk 2s + half) is
@@ -398,7 +402,12 @@ __device__ __forceinline__ void markov_step_dma(const StepArgs& p, StepMap mp, D
                                      ((8 * sub + 2 * g + half) ^ (urow_own & 15)));
   }
   // Item j is complete once at most the next item's copies (this wave's count) are in flight.
-  auto wait_item = [&]() { wait_copies_upto<D::kW2Copies, 1, D::kUCopies>(ucopies_w); };
+  auto wait_item = [&]() {
+    if constexpr (kUShared)
+      wait_copies_upto<D::kW2Copies, 1, D::kUCopies>(ucopies_w);
+    else
+      wait_copies<D::kCopies>();
+  };
 
   // This wave's share of item j's copies into stage j % kStages. Rows past V or B are clamped
   // to the last valid one (all addresses stay inside the tensors); the epilogue masks them.
@@ -416,39 +425,65 @@ __device__ __forceinline__ void markov_step_dma(const StepArgs& p, StepMap mp, D
     }
 #pragma unroll
     for (int i = 0; i < D::kUCopies; ++i) {
-      if (i < ucopies_w) {   // wave-uniform
-        const int q = wave * uper + i;
+      if constexpr (kUShared) {
+        if (i < ucopies_w) {   // wave-uniform
+          const int q = wave * uper + i;
+          const int slot = 64 * q + lane;
+          const int d = slot / D::kUChunks;             // U row within the stage
+          const int c = (slot % D::kUChunks) ^ (d & 15);
+          const int ub = min(u0 + d, (p.B - 1) >> ush);
+          const int v = min(tok0 + 4 * c, p.V - 4);
+          copy16_to_lds_nt(p.U + (static_cast<size_t>(ub) * p.gamma + p.k) * p.V + v,
+                           __builtin_amdgcn_readfirstlane(base + D::kW2Bytes + 1024 * q));
+        }
+      } else {
+        const int q = wave * D::kUCopies + i;
         const int slot = 64 * q + lane;
-        const int d = slot / D::kUChunks;               // U row within the stage
-        const int c = (slot % D::kUChunks) ^ (d & 15);
-        const int ub = min(u0 + d, (p.B - 1) >> ush);
+        const int row = slot / D::kUChunks;
+        const int c = (slot % D::kUChunks) ^ (row & 15);
+        const int b = min(group * kDmaGroup + row, p.B - 1);
         const int v = min(tok0 + 4 * c, p.V - 4);
-        copy16_to_lds_nt(p.U + (static_cast<size_t>(ub) * p.gamma + p.k) * p.V + v,
-                         __builtin_amdgcn_readfirstlane(base + D::kW2Bytes + 1024 * q));
+        copy16_to_lds_nt(p.U + (static_cast<size_t>(b) * p.gamma + p.k) * p.V + v,
+                         base + D::kW2Bytes + 1024 * q);
       }
     }
   };
 
   // Partials of items j0 .. j1-1 (after a barrier), to global memory by the whole workgroup.
-  // Thread t takes tile slot t % kSlots (item j0 + slot / kDmaTiles) of the rows t / kSlots +
-  // kRowStep i: consecutive threads write consecutive tiles of one request (whole lines), and
-  // all of a thread's LDS reads go out before its stores.
-  auto flush = [&](int j0, int j1) {
-    constexpr int kSlots = D::kPartItems * kDmaTiles;
+  // With kSlots the power of two at or above their tile count, thread t takes tile slot
+  // t % kSlots (item j0 + slot / kDmaTiles) of the rows t / kSlots + kRowStep i: consecutive
+  // threads write consecutive tiles of one request (whole lines), and all of a thread's LDS reads
+  // go out before its stores.
+  auto flush_slots = [&](int j0, int j1, auto slots_c) {
+    constexpr int kSlots = decltype(slots_c)::value;
     constexpr int kRowStep = D::kThreads / kSlots;
-    static_assert(D::kThreads % kSlots == 0 && kDmaGroup % kRowStep == 0, "flush mapping");
+    constexpr int kPasses = (kDmaGroup + kRowStep - 1) / kRowStep;
+    static_assert(D::kThreads % kSlots == 0 && kSlots <= D::kPartItems * kDmaTiles, "flush mapping");
     const int tt = tid % kSlots, r0 = tid / kSlots;
     const int j = j0 + tt / kDmaTiles;
     const int tile = (item_lo + j0) * kDmaTiles + tt;
     const bool ok = tt < (j1 - j0) * kDmaTiles && tile < p.ntiles;
     const float2* src = pbuf + ((j % D::kPartItems) * kDmaTiles + tt % kDmaTiles) * kDmaGroup;
-    float2 v[kDmaGroup / kRowStep];
+    float2 v[kPasses];
 #pragma unroll
-    for (int i = 0; i < kDmaGroup / kRowStep; ++i) v[i] = src[r0 + kRowStep * i];
+    for (int i = 0; i < kPasses; ++i) v[i] = src[min(r0 + kRowStep * i, kDmaGroup - 1)];
 #pragma unroll
-    for (int i = 0; i < kDmaGroup / kRowStep; ++i) {
-      const int b = group * kDmaGroup + r0 + kRowStep * i;
-      if (ok && b < p.B) p.part[static_cast<size_t>(b) * p.ntiles + tile] = v[i];
+    for (int i = 0; i < kPasses; ++i) {
+      const int row = r0 + kRowStep * i;
+      const int b = group * kDmaGroup + row;
+      if (ok && row < kDmaGroup && b < p.B) p.part[static_cast<size_t>(b) * p.ntiles + tile] = v[i];
+    }
+  };
+  auto flush = [&](int j0, int j1) {
+    const int per = (j1 - j0) * kDmaTiles;   // uniform
+    if (per <= 2) {
+      flush_slots(j0, j1, std::integral_constant<int, 2>{});
+    } else if (per <= 4) {
+      flush_slots(j0, j1, std::integral_constant<int, 4>{});
+    } else if (per <= 8) {
+      flush_slots(j0, j1, std::integral_constant<int, 8>{});
+    } else {
+      flush_slots(j0, j1, std::integral_constant<int, D::kPartItems * kDmaTiles>{});
     }
   };
 
@@ -553,10 +588,10 @@ __device__ __forceinline__ void markov_step_dma(const StepArgs& p, StepMap mp, D
   flush(flushed, n);
 }
 
-template <int KS, int NT>
+template <int KS, int NT, bool kUShared>
 __global__ __launch_bounds__(kDmaThreads, 1) void markov_step_dma_kernel(StepArgs p) {
   __shared__ DmaLds<KS> lds;
-  markov_step_dma<KS, NT>(p, step_map(p.B, blockIdx.x, gridDim.x, 0), lds);
+  markov_step_dma<KS, NT, kUShared>(p, step_map(p.B, blockIdx.x, gridDim.x, 0), lds);
 }
 
 
@@ -648,20 +683,35 @@ __device__ __forceinline__ void markov_step_deep4(const StepArgs& p, StepMap mp,
     }
   };
   // Partials of items j0 .. j1-1 (one tile each), mapped as in the two-stage kernel's flush.
-  auto flush = [&](int j0, int j1) {
-    constexpr int kSlots = D::kPartItems;
+  auto flush_slots = [&](int j0, int j1, auto slots_c) {
+    constexpr int kSlots = decltype(slots_c)::value;
     constexpr int kRowStep = D::kThreads / kSlots;
-    static_assert(D::kThreads % kSlots == 0 && kDmaGroup % kRowStep == 0, "flush mapping");
+    constexpr int kPasses = (kDmaGroup + kRowStep - 1) / kRowStep;
+    static_assert(D::kThreads % kSlots == 0 && kSlots <= D::kPartItems, "flush mapping");
     const int tt = tid % kSlots, r0 = tid / kSlots;
     const bool ok = tt < j1 - j0;
     const float2* src = pbuf + ((j0 + tt) % D::kPartItems) * kDmaGroup;
-    float2 v[kDmaGroup / kRowStep];
+    float2 v[kPasses];
 #pragma unroll
-    for (int i = 0; i < kDmaGroup / kRowStep; ++i) v[i] = src[r0 + kRowStep * i];
+    for (int i = 0; i < kPasses; ++i) v[i] = src[min(r0 + kRowStep * i, kDmaGroup - 1)];
 #pragma unroll
-    for (int i = 0; i < kDmaGroup / kRowStep; ++i) {
-      const int b = group * kDmaGroup + r0 + kRowStep * i;
-      if (ok && b < p.B) p.part[static_cast<size_t>(b) * p.ntiles + item_lo + j0 + tt] = v[i];
+    for (int i = 0; i < kPasses; ++i) {
+      const int row = r0 + kRowStep * i;
+      const int b = group * kDmaGroup + row;
+      if (ok && row < kDmaGroup && b < p.B)
+        p.part[static_cast<size_t>(b) * p.ntiles + item_lo + j0 + tt] = v[i];
+    }
+  };
+  auto flush = [&](int j0, int j1) {
+    const int per = j1 - j0;   // uniform
+    if (per <= 2) {
+      flush_slots(j0, j1, std::integral_constant<int, 2>{});
+    } else if (per <= 4) {
+      flush_slots(j0, j1, std::integral_constant<int, 4>{});
+    } else if (per <= 8) {
+      flush_slots(j0, j1, std::integral_constant<int, 8>{});
+    } else {
+      flush_slots(j0, j1, std::integral_constant<int, D::kPartItems>{});
     }
   };
 
@@ -941,7 +991,13 @@ static int step_grid(const StepArgs& a, int first) {
 
 template <int KS, int NT>
 static hipError_t launch_step_dma(const StepArgs& a, hipStream_t s) {
-  launch_kernel(markov_step_dma_kernel<KS, NT>, dim3(step_grid(a, 0)), dim3(kDmaThreads), 0, s, a);
+  // Tree depths past the first read one U row per request for several rows (u_shift > 0).
+  if (a.u_shift > 0)
+    launch_kernel(markov_step_dma_kernel<KS, NT, true>, dim3(step_grid(a, 0)), dim3(kDmaThreads), 0,
+                  s, a);
+  else
+    launch_kernel(markov_step_dma_kernel<KS, NT, false>, dim3(step_grid(a, 0)), dim3(kDmaThreads),
+                  0, s, a);
   return hipGetLastError();
 }
 

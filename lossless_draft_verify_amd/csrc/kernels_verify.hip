@@ -18,6 +18,8 @@
 //                      target row into w = max(0, p_t - p_d) and min(p_t, p_d), summed per tile
 //   emit_sample        one workgroup per request: inverse-CDF draw from the residual tiles, or
 //                      from the target row's segments for a bonus (or a zero-mass residual)
+#include <type_traits>
+
 #include "device.h"
 #include "launch.h"
 #include "dma.h"
@@ -56,27 +58,35 @@ __device__ __forceinline__ void load_segment(const float* __restrict__ trow, int
   }
 }
 
+template <bool kSplit>
 __global__ __launch_bounds__(kBlock) void target_stats_kernel(VerifyArgs p) {
   __shared__ float red_f[kBlock / 64];
   __shared__ double red_d[kBlock / 64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   if (blockIdx.x == 0 && threadIdx.x == 0) *p.ws.rcount = 0;   // residual list (for accept)
   const int nitems = (p.dense_rows > 0 ? p.dense_rows : p.row_offsets[p.B]) * p.nseg;
-  // The RNN head's bias terms for the later passes (a grid-strided share per thread): the first
-  // value goes out with the row count, and the split runs while the first segment is loading.
-  const int nsplit = p.e_split ? p.B * p.gamma * p.r : 0;
-  const int i0 = blockIdx.x * kBlock + threadIdx.x;
-  const float e0 = (i0 < nsplit) ? p.e_split[i0] : 0.0f;
   const bool vec4 = (p.V & 3) == 0;
   int it = blockIdx.x;
   float x[16], y[16];
-  if (it < nitems)
+  if constexpr (kSplit) {
+    // The RNN head's bias terms for the later passes (a grid-strided share per thread): the
+    // first value goes out with the row count, and the split runs while the first segment is
+    // loading.
+    const int nsplit = p.B * p.gamma * p.r;
+    const int i0 = blockIdx.x * kBlock + threadIdx.x;
+    const float e0 = (i0 < nsplit) ? p.e_split[i0] : 0.0f;
+    if (it < nitems)
+      load_segment(p.target + static_cast<size_t>(it / p.nseg) * p.V, (it % p.nseg) * kSegTokens,
+                   p.V, vec4, x);
+    for (int i = i0; i < nsplit; i += gridDim.x * kBlock)
+      split_terms(i == i0 ? e0 : p.e_split[i],
+                  p.E_split + static_cast<size_t>(i / p.r) * (kRnnTerms * p.r) + i % p.r, p.r);
+    if (it >= nitems) return;
+  } else {
+    if (it >= nitems) return;
     load_segment(p.target + static_cast<size_t>(it / p.nseg) * p.V, (it % p.nseg) * kSegTokens,
                  p.V, vec4, x);
-  for (int i = i0; i < nsplit; i += gridDim.x * kBlock)
-    split_terms(i == i0 ? e0 : p.e_split[i],
-                p.E_split + static_cast<size_t>(i / p.r) * (kRnnTerms * p.r) + i % p.r, p.r);
-  if (it >= nitems) return;
+  }
   for (; it < nitems; it += gridDim.x) {
     const int nxt = it + gridDim.x;
     if (nxt < nitems)
@@ -555,14 +565,15 @@ __device__ __forceinline__ void residual_dma(const VerifyArgs& p) {
     }
   };
 
-  // Tile sums of items j0 .. j1-1 (after a barrier) to rsum / rmin: thread t takes tile slot
-  // t % kSlots of the rows t / kSlots + kRowStep i, so consecutive threads write consecutive
-  // tiles of one request, and its LDS reads all go out before its stores.
-  auto flush = [&](int j0, int j1) {
-    constexpr int kSlots = D::kPartItems * kResTiles;
+  // Tile sums of items j0 .. j1-1 (after a barrier) to rsum / rmin: with kSlots the power of two
+  // at or above their tile count, thread t takes tile slot t % kSlots of the rows t / kSlots +
+  // kRowStep i, so consecutive threads write consecutive tiles of one request, and its LDS reads
+  // all go out before its stores.
+  auto flush_slots = [&](int j0, int j1, auto slots_c) {
+    constexpr int kSlots = decltype(slots_c)::value;
     constexpr int kRowStep = D::kThreads / kSlots;
-    constexpr int kPasses = kResGroup / kRowStep;
-    static_assert(D::kThreads % kSlots == 0 && kResGroup % kRowStep == 0, "flush mapping");
+    constexpr int kPasses = (kResGroup + kRowStep - 1) / kRowStep;
+    static_assert(D::kThreads % kSlots == 0 && kSlots <= D::kPartItems * kResTiles, "flush mapping");
     const int tt = tid % kSlots, r0 = tid / kSlots;   // tile slot, first row
     const int j = j0 + tt / kResTiles;
     const int tile = (item_lo + j0) * kResTiles + tt;
@@ -572,7 +583,7 @@ __device__ __forceinline__ void residual_dma(const VerifyArgs& p) {
     int rb[kPasses];
 #pragma unroll
     for (int i = 0; i < kPasses; ++i) {
-      const int row = r0 + kRowStep * i;
+      const int row = min(r0 + kRowStep * i, kResGroup - 1);
       v0[i] = pbuf[slot * kResGroup + row];
       v1[i] = pbuf[(slot + 1) * kResGroup + row];
       rb[i] = rec[row].b;
@@ -584,6 +595,16 @@ __device__ __forceinline__ void residual_dma(const VerifyArgs& p) {
         p.ws.rsum[o] = v0[i].x + v1[i].x;
         p.ws.rmin[o] = v0[i].y + v1[i].y;
       }
+    }
+  };
+  auto flush = [&](int j0, int j1) {
+    const int per = (j1 - j0) * kResTiles;   // uniform
+    if (per <= 2) {
+      flush_slots(j0, j1, std::integral_constant<int, 2>{});
+    } else if (per <= 4) {
+      flush_slots(j0, j1, std::integral_constant<int, 4>{});
+    } else {
+      flush_slots(j0, j1, std::integral_constant<int, D::kPartItems * kResTiles>{});
     }
   };
 
@@ -909,8 +930,11 @@ __global__ __launch_bounds__(kBlock) void emit_sample_kernel(VerifyArgs p) {
 }  // namespace
 
 hipError_t launch_target_stats(const VerifyArgs& a, hipStream_t s) {
-  launch_kernel(target_stats_kernel, dim3(a.persistent_wgs * kStatsBlocksPerCU), dim3(kBlock),
-                     0, s, a);
+  const dim3 grid(a.persistent_wgs * kStatsBlocksPerCU);
+  if (a.e_split)
+    launch_kernel(target_stats_kernel<true>, grid, dim3(kBlock), 0, s, a);
+  else
+    launch_kernel(target_stats_kernel<false>, grid, dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }
 
