@@ -172,8 +172,10 @@ struct StepKernel {
           if (v < p.V) p.dbg[drow + v] = acc[nt][j];
         }
       }
+      if (p.beta != 1.0f) {   // beta = 1: unchanged, no multiply
 #pragma unroll
-      for (int j = 0; j < 16; ++j) acc[nt][j] *= p.beta;
+        for (int j = 0; j < 16; ++j) acc[nt][j] *= p.beta;
+      }
       float L[16];
 #pragma unroll
       for (int j = 0; j < 16; ++j) L[j] = acc[nt][j];
@@ -565,9 +567,14 @@ __device__ __forceinline__ void markov_step_dma(const StepArgs& p, StepMap mp, D
         for (int jj = 0; jj < 16; ++jj)
           if (tok0 + tile_token(jj, half) >= p.V) acc[jj] = kNegInf;
       }
-      float L[16];   // the draft temperature scales the logits (beta = 1: unchanged)
+      float L[16];   // the draft temperature scales the logits (beta = 1: unchanged, no multiply)
+      if (p.beta != 1.0f) {
 #pragma unroll
-      for (int jj = 0; jj < 16; ++jj) L[jj] = acc[jj] * p.beta;
+        for (int jj = 0; jj < 16; ++jj) L[jj] = acc[jj] * p.beta;
+      } else {
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) L[jj] = acc[jj];
+      }
       float m = max16(L);
       m = fmaxf(m, other_half(m, half));
       float t[16];
@@ -756,9 +763,14 @@ __device__ __forceinline__ void markov_step_deep4(const StepArgs& p, StepMap mp,
         for (int jj = 0; jj < 16; ++jj)
           if (tok0 + tile_token(jj, half) >= p.V) acc[jj] = kNegInf;
       }
-      float L[16];
+      float L[16];   // beta = 1: unchanged, no multiply
+      if (p.beta != 1.0f) {
 #pragma unroll
-      for (int jj = 0; jj < 16; ++jj) L[jj] = acc[jj] * p.beta;
+        for (int jj = 0; jj < 16; ++jj) L[jj] = acc[jj] * p.beta;
+      } else {
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) L[jj] = acc[jj];
+      }
       float m = max16(L);
       m = fmaxf(m, other_half(m, half));
       float t[16];
