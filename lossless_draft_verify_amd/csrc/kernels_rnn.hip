@@ -306,5 +306,4 @@ hipError_t launch_rnn_state(const RnnStateArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-
 }  // namespace dspark

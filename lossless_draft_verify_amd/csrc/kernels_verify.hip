@@ -10,7 +10,8 @@
 // Kernels, in stream order (no host synchronisation; grids are sized for the largest plan and
 // read the actual row count from row_offsets[B] on the device):
 //   target_stats       every verified target row, 4096-token segments: segment max and fp64 sum
-//                      of exp(t - segment max)
+//                      of exp(t - segment max); for an RNN-head draft it also splits the given
+//                      fp32 bias vectors into their three bf16 terms for the later passes
 //   accept             one wave per request: row log-sum-exp from the segments, left-to-right
 //                      accept test u * q < p_t(x), emission kind / position / row
 //   residual_partials  requests that rejected: the draft logits of the rejected position are

@@ -1,6 +1,7 @@
 // MFMA tile helpers shared by the draft step, the draft sampler and the residual kernels. All
 // of them form a token tile's logits with the same instruction sequence, so a sampler that
-// recomputes one tile reproduces the streaming pass bit for bit.
+// recomputes one tile reproduces the streaming pass bit for bit. Also the bias rows' layout and
+// the split of an RNN bias component into its three bf16 terms.
 #pragma once
 
 #include "device.h"
