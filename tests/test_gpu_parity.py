@@ -54,6 +54,9 @@ DRAFT_CASES = {
                                   u_std=3.0, w_std=0.05),
     "b520-v2052-r256-g2": _custom("b520-v2052-r256-g2", seed_id=24, B=520, V=2052, r=256,
                                   gamma=2, u_std=3.0, w_std=0.05),
+    # three or four 64-token items per step workgroup: the partials flush with eight tile slots
+    "b64-v57344-r256-g3": _custom("b64-v57344-r256-g3", seed_id=25, B=64, V=57344, r=256,
+                                  gamma=3, u_std=3.0, w_std=0.05),
     # the largest vocabulary the library takes (2^19): 16 tiles per sampler thread, the
     # sampler's per-tile masses filling 128 KiB of LDS
     "b3-v524288-r64-g2": _custom("b3-v524288-r64-g2", seed_id=18, B=3, V=1 << 19, r=64, gamma=2),
