@@ -262,7 +262,9 @@ DSPARK_API dspark_status dspark_markov_draft_plan(
  *   First reject at k: next_token ~ max(0, p_t - p_d) / sum, p_d the draft distribution of
  *   position k recomputed from U, W1, W2t and x_{k-1} (uniforms[b][k-1][2]); all accepted:
  *   next_token ~ p_t of row draft_len[b] (uniforms[b][draft_len[b]][2]).
- *   target      [row_offsets[B]][V] fp32 (device-resident; sized for the plan's rows)
+ *   target      [row_offsets[B]][V] fp32 (device-resident; sized for the plan's rows, of which
+ *               there are at least B: each request verifies 1 + draft_len[b] >= 1 rows, and
+ *               rows 0..B-1 may be read before row_offsets[B] is)
  *   row_offsets [B+1], draft_len [B] int32 (as written by dspark_plan)
  *   U, W1, W2t, anchor, tokens, q_tok, lse, uniforms: as given to / written by the draft
  *   accept_len  [B] int32   out: number of drafted tokens accepted (0..draft_len[b]); the

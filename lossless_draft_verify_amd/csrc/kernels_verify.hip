@@ -32,89 +32,140 @@ namespace {
 
 // Target row statistics, one 256-thread block per (row, 4096-token segment) work item on a
 // grid-stride loop over the rows the plan produced (read on the device). Each thread holds 16
-// values; the next item's loads are issued before the current item is reduced, and the block
-// reductions use LDS-only barriers, so those loads stay in flight through them.
+// values of an item in one of two register buffers; the next item's loads go into the other
+// buffer before the current one is reduced, and the block reductions use LDS-only barriers, so
+// those loads stay in flight through them. The vector-memory counter is in-order, so the loop
+// is written for the compiler's wait placement: the loop is unrolled over the two buffers (no
+// copy between them waits for a load), the next item's loads are issued on every pass (past the
+// last item they read one line at the row start), and each item's statistics are kept in LDS
+// and written when the block is done (a store between two loads would be waited for with them).
 constexpr int kStatsBlocksPerCU = 8;
+constexpr int kStatsKept = kBlock;   // statistics held in LDS between writes
 
 // The row is read once per round: non-temporal loads, so that it displaces less of the W2
-// columns the residual pass reads next.
-__device__ __forceinline__ void load_segment(const float* __restrict__ trow, int t0, int V,
-                                             bool vec4, float (&x)[16]) {
+// columns the residual pass reads next. With V % 4 == 0 the four 16-byte loads are unguarded
+// (addresses past the row are clamped to its last four values, and the reduction masks them),
+// so they go out back to back; a guarded fallback writing the same registers would make the
+// compiler wait for each load before issuing the next.
+template <bool kVec4>
+__device__ __forceinline__ void issue_segment(const VerifyArgs& p, int it, bool live,
+                                              float (&x)[16]) {
   typedef float nt_f4 __attribute__((ext_vector_type(4)));
+  const float* __restrict__ trow = p.target + static_cast<size_t>(it / p.nseg) * p.V;
+  const int t0 = (it % p.nseg) * kSegTokens;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int v = t0 + 1024 * i + 4 * threadIdx.x;
-    float o[4];
-    if (vec4 && v + 3 < V) {
-      const nt_f4 t = __builtin_nontemporal_load(reinterpret_cast<const nt_f4*>(trow + v));
-      o[0] = t.x;
-      o[1] = t.y;
-      o[2] = t.z;
-      o[3] = t.w;
+    if constexpr (kVec4) {
+      const float* src = live ? trow + min(v, p.V - 4) : p.target;
+      const nt_f4 t = __builtin_nontemporal_load(reinterpret_cast<const nt_f4*>(src));
+      x[4 * i + 0] = t.x;
+      x[4 * i + 1] = t.y;
+      x[4 * i + 2] = t.z;
+      x[4 * i + 3] = t.w;
     } else {
-      load4(trow, v, V, vec4, o);
-    }
+      float o[4];
+      load4(live ? trow : p.target, live ? v : 0, p.V, false, o);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) x[4 * i + e] = (v + e < V) ? o[e] : kNegInf;
+      for (int e = 0; e < 4; ++e) x[4 * i + e] = o[e];
+    }
   }
 }
 
-template <bool kSplit>
+// Segment max and fp64 sum of exp(t - max) of item `it` (values past the row end are -inf), to
+// LDS slot `slot`.
+__device__ __forceinline__ void reduce_segment(const VerifyArgs& p, int it, float (&x)[16],
+                                               float* red_f, double* red_d, float* kept_m,
+                                               double* kept_s, int slot) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int t0 = (it % p.nseg) * kSegTokens;
+  if (t0 + kSegTokens > p.V) {   // a row's last, partial segment (uniform over the block)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (t0 + 1024 * i + 4 * static_cast<int>(threadIdx.x) + e >= p.V) x[4 * i + e] = kNegInf;
+  }
+  float m = max16(x);
+  m = wave_max(m);
+  lds_barrier();
+  if (lane == 0) red_f[w] = m;
+  lds_barrier();
+  m = fmaxf(fmaxf(red_f[0], red_f[1]), fmaxf(red_f[2], red_f[3]));
+  double s = 0.0;
+  if (m != kNegInf) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) s += static_cast<double>(exp_term(x[j] - m));
+  }
+  s = wave_sum(s);
+  if (lane == 0) red_d[w] = s;
+  lds_barrier();
+  if (threadIdx.x == 0) {
+    kept_m[slot] = m;
+    kept_s[slot] = (red_d[0] + red_d[1]) + (red_d[2] + red_d[3]);
+  }
+}
+
+template <bool kSplit, bool kVec4>
 __global__ __launch_bounds__(kBlock) void target_stats_kernel(VerifyArgs p) {
   __shared__ float red_f[kBlock / 64];
   __shared__ double red_d[kBlock / 64];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  __shared__ float kept_m[kStatsKept];
+  __shared__ double kept_s[kStatsKept];
   if (blockIdx.x == 0 && threadIdx.x == 0) *p.ws.rcount = 0;   // residual list (for accept)
-  const int nitems = (p.dense_rows > 0 ? p.dense_rows : p.row_offsets[p.B]) * p.nseg;
-  const bool vec4 = (p.V & 3) == 0;
+  const int G = gridDim.x;
+  // Every request verifies at least one row, so rows 0 .. B-1 exist whatever the plan (the
+  // row count is at least B): a first item among them goes out right behind the row count's
+  // load, and that load's round trip no longer precedes the stream. Only a block whose first
+  // item lies past them (a grid larger than B * nseg items) waits for the count first.
+  const int rows = p.dense_rows > 0 ? p.dense_rows : p.row_offsets[p.B];
   int it = blockIdx.x;
-  float x[16], y[16];
+  if (it >= p.B * p.nseg && it >= rows * p.nseg) return;
+  float xa[16], xb[16];
   if constexpr (kSplit) {
     // The RNN head's bias terms for the later passes (a grid-strided share per thread): the
-    // first value goes out with the row count, and the split runs while the first segment is
-    // loading.
+    // first value goes out with the first segment, and the split runs while it is loading.
     const int nsplit = p.B * p.gamma * p.r;
     const int i0 = blockIdx.x * kBlock + threadIdx.x;
     const float e0 = (i0 < nsplit) ? p.e_split[i0] : 0.0f;
-    if (it < nitems)
-      load_segment(p.target + static_cast<size_t>(it / p.nseg) * p.V, (it % p.nseg) * kSegTokens,
-                   p.V, vec4, x);
+    issue_segment<kVec4>(p, it, true, xa);
     for (int i = i0; i < nsplit; i += gridDim.x * kBlock)
       split_terms(i == i0 ? e0 : p.e_split[i],
                   p.E_split + static_cast<size_t>(i / p.r) * (kRnnTerms * p.r) + i % p.r, p.r);
-    if (it >= nitems) return;
   } else {
-    if (it >= nitems) return;
-    load_segment(p.target + static_cast<size_t>(it / p.nseg) * p.V, (it % p.nseg) * kSegTokens,
-                 p.V, vec4, x);
+    issue_segment<kVec4>(p, it, true, xa);
   }
-  for (; it < nitems; it += gridDim.x) {
-    const int nxt = it + gridDim.x;
-    if (nxt < nitems)
-      load_segment(p.target + static_cast<size_t>(nxt / p.nseg) * p.V, (nxt % p.nseg) * kSegTokens,
-                   p.V, vec4, y);
-    float m = max16(x);
-    m = wave_max(m);
+  const int nitems = rows * p.nseg;
+  // Item k of this block is it0 + k G; its statistics go to output item it0 + k G too (the
+  // item number is the (row, segment) offset of the output arrays).
+  const int it0 = it;
+  int k = 0;
+  auto write_kept = [&](int k0, int cnt) {
     lds_barrier();
-    if (lane == 0) red_f[w] = m;
-    lds_barrier();
-    m = fmaxf(fmaxf(red_f[0], red_f[1]), fmaxf(red_f[2], red_f[3]));
-    double s = 0.0;
-    if (m != kNegInf) {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) s += static_cast<double>(exp_term(x[j] - m));
+    if (static_cast<int>(threadIdx.x) < cnt) {
+      const size_t o = static_cast<size_t>(it0) + static_cast<size_t>(k0 + threadIdx.x) * G;
+      p.ws.seg_max[o] = kept_m[threadIdx.x];
+      p.ws.seg_sum[o] = kept_s[threadIdx.x];
     }
-    s = wave_sum(s);
-    if (lane == 0) red_d[w] = s;
     lds_barrier();
-    if (threadIdx.x == 0) {
-      const size_t o = static_cast<size_t>(it / p.nseg) * p.nseg + it % p.nseg;
-      p.ws.seg_max[o] = m;
-      p.ws.seg_sum[o] = (red_d[0] + red_d[1]) + (red_d[2] + red_d[3]);
-    }
-#pragma unroll
-    for (int j = 0; j < 16; ++j) x[j] = y[j];
+    // Drained here (once per kStatsKept items), so that the loop's own waits need not count
+    // these stores: the compiler would otherwise wait for them, and for every load, at the top
+    // of each pass.
+    __builtin_amdgcn_s_waitcnt(0);
+  };
+  auto step = [&](float (&cur)[16], float (&nxt)[16]) {
+    issue_segment<kVec4>(p, it + G, it + G < nitems, nxt);
+    reduce_segment(p, it, cur, red_f, red_d, kept_m, kept_s, k % kStatsKept);
+    if (++k % kStatsKept == 0) write_kept(k - kStatsKept, kStatsKept);
+    it += G;
+  };
+  while (true) {
+    step(xa, xb);
+    if (it >= nitems) break;
+    step(xb, xa);
+    if (it >= nitems) break;
   }
+  if (k % kStatsKept) write_kept(k - k % kStatsKept, k % kStatsKept);
 }
 
 // One wave per request. The log-sum-exp of all its verified rows and the accept-test inputs of
@@ -932,10 +983,18 @@ __global__ __launch_bounds__(kBlock) void emit_sample_kernel(VerifyArgs p) {
 
 hipError_t launch_target_stats(const VerifyArgs& a, hipStream_t s) {
   const dim3 grid(a.persistent_wgs * kStatsBlocksPerCU);
-  if (a.e_split)
-    launch_kernel(target_stats_kernel<true>, grid, dim3(kBlock), 0, s, a);
-  else
-    launch_kernel(target_stats_kernel<false>, grid, dim3(kBlock), 0, s, a);
+  const bool vec4 = (a.V & 3) == 0;
+  if (a.e_split) {
+    if (vec4)
+      launch_kernel(target_stats_kernel<true, true>, grid, dim3(kBlock), 0, s, a);
+    else
+      launch_kernel(target_stats_kernel<true, false>, grid, dim3(kBlock), 0, s, a);
+  } else {
+    if (vec4)
+      launch_kernel(target_stats_kernel<false, true>, grid, dim3(kBlock), 0, s, a);
+    else
+      launch_kernel(target_stats_kernel<false, false>, grid, dim3(kBlock), 0, s, a);
+  }
   return hipGetLastError();
 }
 
