@@ -465,16 +465,16 @@ __global__ __launch_bounds__(kWalkThreads) void tree_walk_kernel(TreeWalkArgs p)
     const float sm = seg_m;
     const bool vec4 = (V & 3) == 0;
     double Sum = 0.0;
+    float x16[16];
+    load16(trow, t0 + 16 * tid, V, vec4, x16);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float x4[4];
-      load4(trow, t0 + 16 * tid + 4 * i, V, vec4, x4);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int ch = 16 * tid + 4 * i + e;
         bool skip = ch >= n;
         for (int x = 0; x < ne; ++x) skip = skip || (exc[x] == t0 + ch);
-        const double ms = skip ? 0.0 : static_cast<double>(exp_term(x4[e] - sm));
+        const double ms = skip ? 0.0 : static_cast<double>(exp_term(x16[4 * i + e] - sm));
         stage[padded(ch)] = ms;
         Sum += ms;
       }

@@ -112,15 +112,16 @@ __global__ __launch_bounds__(kBlock) void target_stats_kernel(VerifyArgs p) {
   __shared__ double red_d[kBlock / 64];
   __shared__ float kept_m[kStatsKept];
   __shared__ double kept_s[kStatsKept];
-  if (blockIdx.x == 0 && threadIdx.x == 0) *p.ws.rcount = 0;   // residual list (for accept)
   const int G = gridDim.x;
   // Every request verifies at least one row, so rows 0 .. B-1 exist whatever the plan (the
-  // row count is at least B): a first item among them goes out right behind the row count's
-  // load, and that load's round trip no longer precedes the stream. Only a block whose first
-  // item lies past them (a grid larger than B * nseg items) waits for the count first.
-  const int rows = p.dense_rows > 0 ? p.dense_rows : p.row_offsets[p.B];
+  // row count is at least B): a first item among them goes out before the row count is read,
+  // and that load's round trip no longer precedes the stream. Only a block whose first item
+  // lies past them (a grid larger than B * nseg items) reads the count first.
+  auto row_count = [&]() { return p.dense_rows > 0 ? p.dense_rows : p.row_offsets[p.B]; };
   int it = blockIdx.x;
-  if (it >= p.B * p.nseg && it >= rows * p.nseg) return;
+  if (it >= p.B * p.nseg) {
+    if (it >= row_count() * p.nseg) return;
+  }
   float xa[16], xb[16];
   if constexpr (kSplit) {
     // The RNN head's bias terms for the later passes (a grid-strided share per thread): the
@@ -135,7 +136,7 @@ __global__ __launch_bounds__(kBlock) void target_stats_kernel(VerifyArgs p) {
   } else {
     issue_segment<kVec4>(p, it, true, xa);
   }
-  const int nitems = rows * p.nseg;
+  const int nitems = row_count() * p.nseg;
   // Item k of this block is it0 + k G; its statistics go to output item it0 + k G too (the
   // item number is the (row, segment) offset of the output arrays).
   const int it0 = it;
@@ -155,6 +156,7 @@ __global__ __launch_bounds__(kBlock) void target_stats_kernel(VerifyArgs p) {
   };
   auto step = [&](float (&cur)[16], float (&nxt)[16]) {
     issue_segment<kVec4>(p, it + G, it + G < nitems, nxt);
+    __builtin_amdgcn_sched_barrier(0);   // the loads stay ahead of the reduction's first wait
     reduce_segment(p, it, cur, red_f, red_d, kept_m, kept_s, k % kStatsKept);
     if (++k % kStatsKept == 0) write_kept(k - kStatsKept, kStatsKept);
     it += G;
@@ -166,6 +168,10 @@ __global__ __launch_bounds__(kBlock) void target_stats_kernel(VerifyArgs p) {
     if (it >= nitems) break;
   }
   if (k % kStatsKept) write_kept(k - k % kStatsKept, k % kStatsKept);
+  // The residual list starts empty (accept appends to it). Written last: with no store ahead of
+  // them, the row-count reads are known unclobbered and go through the scalar cache, so waiting
+  // for the count does not wait for the segment loads issued before it.
+  if (blockIdx.x == 0 && threadIdx.x == 0) *p.ws.rcount = 0;
 }
 
 // One wave per request. The log-sum-exp of all its verified rows and the accept-test inputs of
@@ -950,14 +956,14 @@ __global__ __launch_bounds__(kBlock) void emit_sample_kernel(VerifyArgs p) {
       const float sm = seg_m;
       const bool vec4 = (p.V & 3) == 0;
       double Sum = 0.0;
+      float x16[16];
+      load16(trow, t0 + 16 * tid, p.V, vec4, x16);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float x4[4];
-        load4(trow, t0 + 16 * tid + 4 * i, p.V, vec4, x4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int c = 16 * tid + 4 * i + e;
-          const double ms = (c < n) ? static_cast<double>(exp_term(x4[e] - sm)) : 0.0;
+          const double ms = (c < n) ? static_cast<double>(exp_term(x16[4 * i + e] - sm)) : 0.0;
           stage[padded(c)] = ms;
           Sum += ms;
         }

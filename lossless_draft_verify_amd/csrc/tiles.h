@@ -46,6 +46,28 @@ __device__ __forceinline__ void load4(const float* __restrict__ row, int v, int 
   }
 }
 
+// Sixteen consecutive values row[v0 .. v0 + 15] (v0 a multiple of 4). With V % 4 == 0 the four
+// 16-byte loads are unguarded, addresses past the row clamped to its last four values (the
+// caller ignores those entries), so all four go out before the first is used: a guarded fallback
+// in the same branch would make each load wait for the one before it. Otherwise per-element
+// guarded loads (0 past V).
+__device__ __forceinline__ void load16(const float* __restrict__ row, int v0, int V, bool vec4,
+                                       float (&x)[16]) {
+  if (vec4) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 t = *reinterpret_cast<const float4*>(row + min(v0 + 4 * i, V - 4));
+      x[4 * i + 0] = t.x;
+      x[4 * i + 1] = t.y;
+      x[4 * i + 2] = t.z;
+      x[4 * i + 3] = t.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x[i] = (v0 + i < V) ? row[v0 + i] : 0.0f;
+  }
+}
+
 // Logits of the 16 accumulator slots a lane holds: L = U + bias (fp32 add), -inf past V.
 __device__ __forceinline__ void tile_logits(const f32x16_t& acc, const float* __restrict__ Urow,
                                             int tok0, int V, int half, bool vec4, float (&L)[16]) {
