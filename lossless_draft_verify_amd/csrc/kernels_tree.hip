@@ -113,12 +113,14 @@ __global__ __launch_bounds__(kTreeThreads) void tree_select_kernel(TreeSelectArg
   for (int j = 0; j < CM; ++j) best[j] = 0;
   constexpr int kBatch = 8;
   for (int i0 = 0; i0 < kTreePer && G * i0 < nt; i0 += kBatch) {
+    // Loads at clamped indices, unconditionally, and the range applied afterwards: a guarded
+    // load per element would make each one wait for the one before it.
     float tm[kBatch];
 #pragma unroll
-    for (int i = 0; i < kBatch; ++i) {
-      const int t = stid + G * (i0 + i);
-      tm[i] = (t < nt) ? part[t].x : kNegInf;
-    }
+    for (int i = 0; i < kBatch; ++i) tm[i] = part[min(stid + G * (i0 + i), nt - 1)].x;
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i)
+      if (stid + G * (i0 + i) >= nt) tm[i] = kNegInf;
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
       const int t = stid + G * (i0 + i);
@@ -144,10 +146,10 @@ __global__ __launch_bounds__(kTreeThreads) void tree_select_kernel(TreeSelectArg
   for (int i0 = 0; i0 < kTreePer && G * i0 < nt; i0 += kBatch) {
     float2 pv[kBatch];
 #pragma unroll
-    for (int i = 0; i < kBatch; ++i) {
-      const int t = stid + G * (i0 + i);
-      pv[i] = (t < nt) ? part[t] : make_float2(kNegInf, 0.0f);
-    }
+    for (int i = 0; i < kBatch; ++i) pv[i] = part[min(stid + G * (i0 + i), nt - 1)];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i)
+      if (stid + G * (i0 + i) >= nt) pv[i] = make_float2(kNegInf, 0.0f);
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) z += tree_tile_mass(pv[i].x, pv[i].y, M);
   }
