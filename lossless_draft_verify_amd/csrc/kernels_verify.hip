@@ -39,7 +39,8 @@ namespace {
 // copy between them waits for a load), the next item's loads are issued on every pass (past the
 // last item they read one line at the row start), and each item's statistics are kept in LDS
 // and written when the block is done (a store between two loads would be waited for with them).
-constexpr int kStatsBlocksPerCU = 8;
+constexpr int kStatsBlocksPerCU = 8;        // up to 1023 rows
+constexpr int kStatsBlocksPerCULarge = 4;   // 1024 rows and more
 constexpr int kStatsKept = kBlock;   // statistics held in LDS between writes
 
 // The row is read once per round: non-temporal loads, so that it displaces less of the W2
@@ -988,7 +989,14 @@ __global__ __launch_bounds__(kBlock) void emit_sample_kernel(VerifyArgs p) {
 }  // namespace
 
 hipError_t launch_target_stats(const VerifyArgs& a, hipStream_t s) {
-  const dim3 grid(a.persistent_wgs * kStatsBlocksPerCU);
+  // Blocks per CU by the largest row count the call can have (the plan's actual count is read on
+  // the device): 8 for up to 1023 rows, where the launch's fixed cost dominates, and 4 from 1024
+  // rows on, where the steady stream is faster with fewer segment loads in flight (b128-v151936-g15
+  // target_stats over 2048 rows: 193.7 us at 4, 195.2 at 6, 206.1 at 8; over 334 rows at
+  // b128-v129280-g5: 29.1, 28.6 and 28.2 us).
+  const long max_rows = a.dense_rows > 0 ? a.dense_rows : static_cast<long>(a.B) * (a.gamma + 1);
+  const int per_cu = (max_rows >= 1024) ? kStatsBlocksPerCULarge : kStatsBlocksPerCU;
+  const dim3 grid(a.persistent_wgs * per_cu);
   const bool vec4 = (a.V & 3) == 0;
   if (a.e_split) {
     if (vec4)
