@@ -173,13 +173,22 @@ def residual_bytes(wl, n_res, greedy=False):
 
 
 def cpu_model():
+    """The host CPU as /proc/cpuinfo names it, with its family and model numbers (a virtual
+    machine may report only a generic name: family 26 is AMD's Zen 5 generation, EPYC 9005)."""
+    info = {}
     try:
         for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
+            if ":" in line:
+                k, v = (x.strip() for x in line.split(":", 1))
+                info.setdefault(k, v)
     except OSError:
-        pass
-    return "unknown"
+        return "unknown"
+    name = info.get("model name", "unknown")
+    extra = [f"family {info['cpu family']} model {info['model']}"] if "cpu family" in info else []
+    if "hypervisor" in info.get("flags", "").split():
+        extra.append("virtual machine")
+    extra.append(f"{os.cpu_count()} logical CPUs visible")
+    return f"{name} ({', '.join(extra)})"
 
 
 def cpu_baseline(wl, wts, s, threads, opts, head="markov", reps=3):
