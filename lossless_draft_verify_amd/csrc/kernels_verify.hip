@@ -41,7 +41,9 @@ namespace {
 // and written when the block is done (a store between two loads would be waited for with them).
 constexpr int kStatsBlocksPerCU = 8;        // up to 1023 rows
 constexpr int kStatsBlocksPerCULarge = 4;   // 1024 rows and more
-constexpr int kStatsKept = kBlock;   // statistics held in LDS between writes
+// Statistics held in LDS between writes: 64 items, so that the in-loop write runs for long row
+// sets (b128-v151936-g15 and the PCTree rows give a block 68-76 items) as well as at the end.
+constexpr int kStatsKept = 64;
 
 // The row is read once per round: non-temporal loads, so that it displaces less of the W2
 // columns the residual pass reads next. With V % 4 == 0 the four 16-byte loads are unguarded
