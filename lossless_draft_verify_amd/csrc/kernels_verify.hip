@@ -183,7 +183,8 @@ __global__ __launch_bounds__(kBlock) void target_stats_kernel(VerifyArgs p) {
 constexpr int kAcceptRows = 16;    // rows reduced per batch (one batch when gamma < 16)
 
 __global__ __launch_bounds__(kBlock) void accept_kernel(VerifyArgs p) {
-  __shared__ double lse_s[kBlock / 64][kMaxGamma + 1];
+  __shared__ double lse_s[kBlock / 64][kMaxGamma + 1];   // each row's sum z, then its lse
+  __shared__ float lse_m[kBlock / 64][kMaxGamma + 1];    // each row's max M
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int b = blockIdx.x * (kBlock / 64) + w;
   if (b >= p.B) return;
@@ -240,7 +241,10 @@ __global__ __launch_bounds__(kBlock) void accept_kernel(VerifyArgs p) {
         z += lane_xor<2>(z);
         z += lane_xor<1>(z);
         const int row = r0 + 2 * pr + half;
-        if (sgi == 0 && row <= ell) lse_s[w][row] = static_cast<double>(M) + log(z);
+        if (sgi == 0 && row <= ell) {
+          lse_s[w][row] = z;
+          lse_m[w][row] = M;
+        }
       }
     }
   } else {
@@ -266,10 +270,17 @@ __global__ __launch_bounds__(kBlock) void accept_kernel(VerifyArgs p) {
         if (r0 + r > ell) break;
         const float M = wave_max(fmaxf(mx[r][0], mx[r][1]));
         const double z = wave_sum(partial_mass(mx[r][0], sg[r][0], M) + partial_mass(mx[r][1], sg[r][1], M));
-        if (lane == 0) lse_s[w][r0 + r] = static_cast<double>(M) + log(z);
+        if (lane == 0) {
+          lse_s[w][r0 + r] = z;
+          lse_m[w][r0 + r] = M;
+        }
       }
     }
   }
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_wave_barrier();
+  // The rows' log-sum-exps M + log z, one row a lane (the fp64 log once for up to 64 rows).
+  for (int r = lane; r <= ell; r += 64) lse_s[w][r] = static_cast<double>(lse_m[w][r]) + log(lse_s[w][r]);
   __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_wave_barrier();
   // 2. accept tests, 64 positions per batch: lane k tests position k0 + k + 1.
