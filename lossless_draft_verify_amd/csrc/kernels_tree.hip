@@ -298,7 +298,8 @@ __global__ __launch_bounds__(kWalkThreads) void tree_walk_kernel(TreeWalkArgs p)
   extern __shared__ double stage[];   // padded: segment masses, then one segment's terms
   __shared__ int tok[kTreeMaxNodes], par[kTreeMaxNodes];
   __shared__ float tval[kTreeMaxNodes];
-  __shared__ double lse[kTreeMaxNodes + 1];
+  __shared__ double lse[kTreeMaxNodes + 1];     // each row's sum z, then its lse
+  __shared__ float lse_m[kTreeMaxNodes + 1];    // each row's max M
   __shared__ double ptn[kTreeMaxNodes];
   __shared__ float us[kMaxGamma + 1];
   __shared__ double ssum[kWalkThreads];
@@ -354,9 +355,15 @@ __global__ __launch_bounds__(kWalkThreads) void tree_walk_kernel(TreeWalkArgs p)
       const float Mr = wave_max(fmaxf(ms[j][0], ms[j][1]));
       const double zr =
           wave_sum(partial_mass(ms[j][0], sg[j][0], Mr) + partial_mass(ms[j][1], sg[j][1], Mr));
-      if (lane == 0) lse[rr] = static_cast<double>(Mr) + log(zr);
+      if (lane == 0) {
+        lse[rr] = zr;
+        lse_m[rr] = Mr;
+      }
     }
   }
+  __syncthreads();
+  // The rows' log-sum-exps M + log z, one row a thread (the fp64 log in one pass).
+  for (int rr = tid; rr <= N; rr += kWalkThreads) lse[rr] = static_cast<double>(lse_m[rr]) + log(lse[rr]);
   __syncthreads();
   for (int n = tid; n < N; n += kWalkThreads)
     ptn[n] = exp(static_cast<double>(tval[n]) - lse[par[n] + 1]);
