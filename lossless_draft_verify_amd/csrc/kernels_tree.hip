@@ -77,7 +77,7 @@ template <int KS, int CM>
 __global__ __launch_bounds__(kTreeThreads) void tree_select_kernel(TreeSelectArgs p) {
   constexpr int r = 16 * KS;
   __shared__ __attribute__((aligned(16))) uint16_t Es[kTreeMaxRows][r];
-  __shared__ unsigned long long redk[kTreeThreads / 64];
+  __shared__ unsigned long long redk[kTreeThreads / 64][kTreeMaxChildren];
   __shared__ float redf[kTreeThreads / 64];
   __shared__ double redd[kTreeThreads / 64];
   __shared__ float Lt[kTreeMaxRows][kTreeMaxChildren][kTileTokens];
@@ -160,23 +160,36 @@ __global__ __launch_bounds__(kTreeThreads) void tree_select_kernel(TreeSelectArg
   for (int w = 0; w < WS; ++w) Z += redd[sub * WS + w];
   const double lse = static_cast<double>(M) + log(Z);
 
-  // The row's c best tiles, one per round: each thread offers the head of its sorted list, and
-  // the one thread whose head was taken (keys are unique) shifts its list.
+  // The row's c best tiles. Each wave first takes its own c best, one per round: every lane
+  // offers the head of its sorted list, and the one lane whose head was taken (keys are unique)
+  // shifts its list. The row's first wave then takes the c best of its waves' WS c (<= 128,
+  // two a lane), the same set in the same order as c rounds over the whole row.
   for (int j = 0; j < c; ++j) {
-    const uint64_t cand = wave_max_u64(best[0]);
-    if (lane == 0) redk[wave] = cand;
-    __syncthreads();
-    uint64_t kb = 0;
-    for (int w = 0; w < WS; ++w) {
-      const uint64_t x = redk[sub * WS + w];
-      kb = x > kb ? x : kb;
-    }
+    const uint64_t kb = wave_max_u64(best[0]);
     const bool taken = kb != 0 && best[0] == kb;
 #pragma unroll
     for (int i = 0; i + 1 < CM; ++i) best[i] = taken ? best[i + 1] : best[i];
     best[CM - 1] = taken ? 0ull : best[CM - 1];
-    if (stid == 0) tile_of[sub][j] = kb ? key_index(kb) : -1;
-    __syncthreads();   // redk is rewritten by the next round
+    if (lane == 0) redk[wave][j] = kb;
+  }
+  __syncthreads();
+  if (wsub == 0) {
+    const int nc = WS * c;
+    const int f0 = lane, f1 = lane + 64;
+    uint64_t k0 = (f0 < nc) ? redk[sub * WS + f0 / c][f0 % c] : 0ull;
+    uint64_t k1 = (f1 < nc) ? redk[sub * WS + f1 / c][f1 % c] : 0ull;
+    if (k1 > k0) {
+      const uint64_t t = k0;
+      k0 = k1;
+      k1 = t;
+    }
+    for (int j = 0; j < c; ++j) {
+      const uint64_t kb = wave_max_u64(k0);
+      const bool taken = kb != 0 && k0 == kb;
+      k0 = taken ? k1 : k0;
+      k1 = taken ? 0ull : k1;
+      if (lane == 0) tile_of[sub][j] = kb ? key_index(kb) : -1;
+    }
   }
 
   // Recompute those tiles with the step's instruction sequence.
