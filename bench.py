@@ -286,7 +286,7 @@ def main():
         sys.exit(2)
     opts = {"temperature": args.temperature, "greedy": args.greedy}
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build runs on a single MI355X and has no "
+        print("bench.py measures one GPU: the library runs on a single MI355X and has no "
               "multi-GPU path; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 

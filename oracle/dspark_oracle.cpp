@@ -84,7 +84,7 @@ double softmax_fp64(const float* logits, int V, std::vector<double>& p) {
 }
 
 // Inverse-CDF draw over token ids in ascending order: the first v with CDF(v) > u.
-// Reading: the pages fix only the distribution a draw must follow; this build fixes the rule
+// Reading: the pages fix only the distribution a draw must follow; the oracle fixes the rule
 // "ascending token id, strict >, u in [0,1)" so that results are reproducible bit for bit.
 // If rounding leaves no edge above u, the last token with positive probability is taken.
 // *margin receives the distance from u to the nearer edge of the chosen token's interval.
