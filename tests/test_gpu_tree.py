@@ -125,3 +125,47 @@ def test_tree_draft_is_deterministic_and_rows_share_base_logits():
     b = [np_(t) for t in L.tree_draft(d, shape, inp["U"], wts["W1"], wts["W2t"], inp["anchor"])]
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
+
+
+def test_tree_full_size_sampled_requests():
+    """The PCTree round in the launch configuration the benchmark times (B = 128, V = 129280,
+    r = 256, gamma = 5, c = 4, M = 4, N = 16; depths 2-5 expand 512 rows, four 128-row groups),
+    checked against the oracle on six requests spread over those groups: a request's tree and
+    walk depend only on its own rows. The verify walks the oracle's tree for those requests (the
+    GPU's own tree for the rest), over target rows built along each tree's paths."""
+    wl, shape = W.WORKLOADS["b128-v129280-g5"], L.TreeShape(4, 4, 16)
+    B, g, V, N = wl.B, wl.gamma, wl.V, shape.N
+    idx = np.array([0, 31, 45, 64, 101, 127])
+    log(f"[tree full size] B {B} V {V} c4 m4 n16, oracle on requests {idx.tolist()}")
+    d = L.Dims(B, g, V, wl.r, wl.d)
+    wts = W.weights(wl, DEV)
+    inp = W.round_inputs(wl, 0, DEV, with_hidden=False, with_noise=False)
+    tok, dep, par, q, P = (np_(t) for t in L.tree_draft(d, shape, inp["U"], wts["W1"],
+                                                         wts["W2t"], inp["anchor"]))
+    o = oracle.tree_draft(np_(inp["U"])[idx], bits(wts["W1"]), bits(wts["W2t"]),
+                          np_(inp["anchor"])[idx], shape.c, shape.M, N)
+    flagged = (o["logit_margin"] < TREE_TIE) | (o["path_margin"] < TREE_TIE)
+    same = ((tok[idx] == o["token"]).all(1) & (dep[idx] == o["depth"]).all(1)
+            & (par[idx] == o["parent"]).all(1))
+    assert not (~same & ~flagged).any(), f"unflagged mismatches at {idx[~same & ~flagged]}"
+    if same.any():
+        assert np.abs(q[idx][same] - o["q"][same]).max() <= PROB_TOL
+        assert (np.abs(P[idx][same] - o["path"][same]) <= PROB_TOL * o["depth"][same]).all()
+    log(f"  draft: {int(same.sum())}/{len(idx)} sampled trees equal, {int(flagged.sum())} flagged")
+    tok_v, dep_v, par_v = tok.copy(), dep.copy(), par.copy()
+    tok_v[idx], dep_v[idx], par_v[idx] = o["token"], o["depth"], o["parent"]
+    target = _tree_target(wl, inp, wts, tok_v, dep_v, N)
+    T = lambda a: torch.as_tensor(np.ascontiguousarray(a), dtype=torch.int32, device=DEV)
+    al, path, nt, fl = (np_(t) for t in L.tree_verify(d, shape, target, T(tok_v), T(par_v),
+                                                      inp["uniforms"]))
+    ov = oracle.tree_verify(np_(target[torch.as_tensor(idx, device=DEV)]), o["token"], o["depth"],
+                            o["parent"], np_(inp["uniforms"])[idx])
+    del target
+    c = MismatchCounter("tree walk full size")
+    walk_same = ((al[idx] == ov["accept_len"]) & (path[idx] == ov["path"]).all(1)
+                 & (nt[idx] == ov["next_token"]))
+    c.add(walk_same, np.ones(len(idx), bool), ov["margin"])
+    assert np.array_equal(fl[idx].astype(np.uint32), ov["flags"])
+    assert ((al >= 0) & (al <= g)).all() and ((nt >= 0) & (nt < V)).all()
+    log(f"  verify: accepted {al[idx].tolist()}; {c.report()}")
+    c.check_rate()
