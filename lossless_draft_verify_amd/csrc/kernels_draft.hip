@@ -838,20 +838,25 @@ __global__ __launch_bounds__(256, 1) void markov_step_deep4_plan_kernel(StepArgs
 // scaled by the draft temperature as in the step kernel; a greedy draft instead takes the first
 // maximal logit (the first tile whose max is the row max, then its first lane holding it).
 // r = 512 takes 512 threads: its 32-step tile recompute needs more than 128 registers a lane.
-template <int KS>
+// kHalf: 512 threads at r <= 256 for batches past 256 requests, up to 16 tiles a thread
+// (V <= 262144). The kernel holds more than 64 registers a lane, so a CU takes 16 of its waves:
+// one 1024-thread workgroup, or two of 512, and B = 512 then runs in one round of workgroups
+// instead of two.
+template <int KS, bool kHalf = false>
 struct SampleCfg {
-  static constexpr int kThreads = (KS >= 32) ? 512 : 1024;
-  static constexpr int kPer = kMaxVocab / kTileTokens / kThreads;   // tiles per thread, at most
+  static constexpr int kThreads = (KS >= 32 || kHalf) ? 512 : 1024;
+  static constexpr int kPer = kHalf ? 16 : kMaxVocab / kTileTokens / kThreads;   // tiles a thread
 };
+constexpr int kHalfSampleMinB = 257;
 
 __device__ __forceinline__ double tile_mass(float m, float s, float M) {
   return (m == kNegInf) ? 0.0 : static_cast<double>(exp_term(m - M)) * static_cast<double>(s);
 }
 
-template <int KS, int NT>
-__global__ __launch_bounds__(SampleCfg<KS>::kThreads) void draft_sample_kernel(SampleArgs p) {
-  constexpr int kSampleThreads = SampleCfg<KS>::kThreads;
-  constexpr int kSamplePer = SampleCfg<KS>::kPer;
+template <int KS, int NT, bool kHalf = false>
+__global__ __launch_bounds__((SampleCfg<KS, kHalf>::kThreads)) void draft_sample_kernel(SampleArgs p) {
+  constexpr int kSampleThreads = SampleCfg<KS, kHalf>::kThreads;
+  constexpr int kSamplePer = SampleCfg<KS, kHalf>::kPer;
   __shared__ float red_f[kSampleThreads / 64];
   __shared__ int red_i[kSampleThreads / 64];
   __shared__ double ssum[kSampleThreads];
@@ -1070,6 +1075,21 @@ static hipError_t launch_step_ks(const StepArgs& a, hipStream_t s) {
 template <int KS>
 static hipError_t launch_sample_ks(const SampleArgs& a, hipStream_t s) {
   const size_t lds = static_cast<size_t>(a.ntiles) * sizeof(double);
+  if constexpr (KS <= 16) {
+    constexpr int kHalfThreads = SampleCfg<KS, true>::kThreads;
+    if (a.B >= kHalfSampleMinB && a.ntiles <= kHalfThreads * SampleCfg<KS, true>::kPer) {
+      if (a.e_terms == 1) {
+        launch_kernel(draft_sample_kernel<KS, 1, true>, dim3(a.B), dim3(kHalfThreads), lds, s, a);
+        return hipGetLastError();
+      }
+      if (a.e_terms == kRnnTerms) {
+        launch_kernel(draft_sample_kernel<KS, kRnnTerms, true>, dim3(a.B), dim3(kHalfThreads), lds,
+                      s, a);
+        return hipGetLastError();
+      }
+      return hipErrorInvalidValue;
+    }
+  }
   if (a.e_terms == 1) {
     launch_kernel(draft_sample_kernel<KS, 1>, dim3(a.B), dim3(SampleCfg<KS>::kThreads), lds,
                        s, a);
