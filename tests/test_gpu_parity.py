@@ -48,6 +48,9 @@ DRAFT_CASES = {
     "b33-v2052-r64-g4": _custom("b33-v2052-r64-g4", seed_id=16, B=33, V=2052, r=64, gamma=4),
     "b20-v8192-r256-g2": _custom("b20-v8192-r256-g2", seed_id=17, B=20, V=8192, r=256, gamma=2,
                                  u_std=3.0, w_std=0.05),
+    # three request groups (the third ragged) and the 512-thread sampler of batches past 256
+    "b300-v4100-r256-g3": _custom("b300-v4100-r256-g3", seed_id=18, B=300, V=4100, r=256, d=64,
+                                  u_std=3.0, w_std=0.05),
     # the 256-request one-tile step (B > 128, r = 256): a ragged second group whose second
     # wave is partly active, and three groups over the XCD-aware placement
     "b300-v4100-r256-g3": _custom("b300-v4100-r256-g3", seed_id=23, B=300, V=4100, r=256,

@@ -52,6 +52,10 @@ CASES = {
     # requests: one wave of four active), and a 4-token tail tile
     "b130-v4100-r256-g3": _custom("b130-v4100-r256-g3-rnn", seed_id=55, B=130, V=4100, r=256,
                                   d=64, u_std=3.0, w_std=0.05),
+    # the four-stage step over three request groups (the third ragged) and the 512-thread
+    # sampler of batches past 256, with the three-term bias rows
+    "b300-v4100-r256-g3": _custom("b300-v4100-r256-g3-rnn", seed_id=56, B=300, V=4100, r=256,
+                                  d=64, u_std=3.0, w_std=0.05),
 }
 
 
